@@ -1,0 +1,8 @@
+"""Float64 CPU oracle of the REINFORCE Zero learner hot path.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the package smoke check and
+the benchmark's CPU-baseline leg, never by the product path.  It shares no code
+with the HIP kernels.  See reinforce_zero.py for the definitions and sources.
+"""
+from .reinforce_zero import *  # noqa: F401,F403
+from .reinforce_zero import __all__  # noqa: F401

@@ -1,0 +1,387 @@
+"""Pins of the float64 oracle to facts fixed outside itself.
+
+Each test checks the oracle against something it does not compute the same
+way: closed forms, a library routine the oracle does not call (SciPy,
+torch.log_softmax), brute force with Python loops, central finite differences,
+the exact-enumeration importance-sampling identities of the REINFORCE Zero
+project page ("The full IS correction"), and hand-derived worked cases under
+tests/golden/.  A plausible slip anywhere in the oracle (a dropped term, a
+flipped sign, a transposed operand, a wrong average) fails at least one test.
+"""
+import json
+import math
+import pathlib
+from fractions import Fraction
+
+import numpy as np
+import pytest
+from scipy.special import log_softmax as sp_log_softmax
+from scipy.special import logsumexp as sp_logsumexp
+
+import oracle as O
+
+GOLDEN = pathlib.Path(__file__).parent / "golden"
+
+
+def _frac(s):
+    return float(Fraction(s))
+
+
+def _rng(seed):
+    return np.random.default_rng(np.random.PCG64(seed))
+
+
+def _small_problem(seed, B=4, H=8, V=16, lo=2, hi=6, masked=True, sigma=0.3,
+                   group_size=2):
+    rng = _rng(seed)
+    lengths = rng.integers(lo, hi + 1, size=B)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    N = int(cu[-1])
+    mask = np.ones(N, dtype=np.uint8)
+    if masked:
+        mask[rng.random(N) < 0.3] = 0
+        mask[cu[:-1]] = 1   # every response keeps a valid row
+    hidden = rng.standard_normal((N, H))
+    W = 0.5 * rng.standard_normal((V, H))
+    tokens = rng.integers(0, V, size=N)
+    rewards = rng.random(B)
+    group_ids = np.arange(B) // group_size
+    logpi, _ = O.token_logprobs(hidden, W, tokens)
+    logmu = logpi + sigma * rng.standard_normal(N)
+    return dict(hidden=hidden, W=W, tokens=tokens, mask=mask, cu=cu,
+                rewards=rewards, group_ids=group_ids, logmu=logmu)
+
+
+def _loss_of(p, hidden, W):
+    logpi_all, _ = O.token_logprobs(hidden, W, p["tokens"])
+    logpi = np.where(p["mask"] != 0, logpi_all, 0.0)
+    return O.loss_stage(logpi, p["logmu"], p["mask"], p["cu"], p["rewards"],
+                        p["group_ids"])["loss"]
+
+
+# ------------------------------------------------------------ input decode
+def test_bf16_decode_exact():
+    bits = np.array([0x3F80, 0xC000, 0x3F81, 0x0000, 0x8000, 0x7F7F, 0x0001],
+                    dtype=np.uint16)
+    got = O.decode_bf16(bits)
+    want = [1.0, -2.0, 1.0 + 2.0 ** -7, 0.0, -0.0,
+            (2 - 2.0 ** -7) * 2.0 ** 127, 2.0 ** -133]
+    assert got.tolist() == want
+
+
+# --------------------------------------------------------- logits/logsoftmax
+@pytest.mark.parametrize("V", [1024, 151936])
+def test_zero_head_gives_uniform_policy(V):
+    """W = 0: every logit is 0, so log pi = -ln V exactly."""
+    hidden = _rng(1).standard_normal((3, 4))
+    W = np.zeros((V, 4))
+    tokens = np.array([0, V // 2, V - 1])
+    logpi, lse = O.token_logprobs(hidden, W, tokens)
+    assert np.allclose(logpi, -math.log(V), rtol=0, atol=1e-12)
+    assert np.allclose(lse, math.log(V), rtol=0, atol=1e-12)
+
+
+def test_onehot_hidden_selects_head_column():
+    """hidden = e_k gives z = W[:, k]; compare with SciPy's log_softmax."""
+    rng = _rng(2)
+    V, H = 37, 5
+    W = rng.standard_normal((V, H))
+    for k in range(H):
+        hidden = np.zeros((V, H))
+        hidden[:, k] = 1.0
+        tokens = np.arange(V)
+        logpi, lse = O.token_logprobs(hidden, W, tokens)
+        ref = sp_log_softmax(W[:, k])
+        assert np.allclose(logpi, ref, rtol=0, atol=1e-13)
+        assert np.allclose(lse, sp_logsumexp(W[:, k]), rtol=0, atol=1e-13)
+
+
+def test_two_class_closed_form():
+    """V = 2: log pi(0) = -log(1 + exp(z1 - z0))."""
+    rng = _rng(3)
+    hidden = rng.standard_normal((50, 6))
+    W = 3.0 * rng.standard_normal((2, 6))
+    z = np.array([[sum(hidden[t, h] * W[v, h] for h in range(6)) for v in range(2)]
+                  for t in range(50)])
+    for a in (0, 1):
+        logpi, _ = O.token_logprobs(hidden, W, np.full(50, a))
+        want = -np.log1p(np.exp(z[:, 1 - a] - z[:, a]))
+        assert np.allclose(logpi, want, rtol=0, atol=1e-13)
+
+
+def test_probabilities_sum_to_one():
+    rng = _rng(4)
+    V, H = 64, 7
+    hidden = rng.standard_normal((5, H))
+    W = rng.standard_normal((V, H))
+    tot = np.zeros(5)
+    for a in range(V):
+        lp, _ = O.token_logprobs(hidden, W, np.full(5, a))
+        tot += np.exp(lp)
+    assert np.allclose(tot, 1.0, rtol=0, atol=1e-13)
+
+
+def test_gather_brute_force_python_loops():
+    rng = _rng(5)
+    N, H, V = 6, 4, 9
+    hidden = rng.standard_normal((N, H))
+    W = rng.standard_normal((V, H))
+    tokens = rng.integers(0, V, size=N)
+    logpi, lse = O.token_logprobs(hidden, W, tokens, row_chunk=4)
+    for t in range(N):
+        z = [math.fsum(hidden[t, h] * W[v, h] for h in range(H)) for v in range(V)]
+        m = max(z)
+        l = m + math.log(math.fsum(math.exp(x - m) for x in z))
+        assert abs(lse[t] - l) < 1e-13
+        assert abs(logpi[t] - (z[tokens[t]] - l)) < 1e-13
+
+
+def test_log_softmax_against_torch_f64():
+    torch = pytest.importorskip("torch")
+    rng = _rng(6)
+    hidden = rng.standard_normal((40, 16))
+    W = 0.3 * rng.standard_normal((300, 16))
+    tokens = rng.integers(0, 300, size=40)
+    logpi, _ = O.token_logprobs(hidden, W, tokens, row_chunk=7)
+    z = torch.from_numpy(hidden) @ torch.from_numpy(W).T
+    ref = torch.log_softmax(z, dim=1)[torch.arange(40), torch.from_numpy(tokens)]
+    assert np.allclose(logpi, ref.numpy(), rtol=0, atol=1e-12)
+
+
+def test_large_logits_do_not_overflow():
+    hidden = np.array([[1000.0, -1000.0]])
+    W = np.array([[1.0, 0.0], [0.0, 1.0], [0.5, 0.0]])
+    logpi, lse = O.token_logprobs(hidden, W, np.array([2]))
+    z = np.array([1000.0, -1000.0, 500.0])
+    assert np.isfinite(logpi).all()
+    assert abs(lse[0] - sp_logsumexp(z)) < 1e-9
+    assert abs(logpi[0] - (500.0 - sp_logsumexp(z))) < 1e-9
+
+
+# -------------------------------------------------------------- advantages
+def test_group_advantages_sum_to_zero_per_group():
+    rng = _rng(7)
+    rewards = rng.integers(0, 2, size=64).astype(np.float64)
+    groups = rng.permutation(np.arange(64) // 8)
+    A = O.group_mean_advantages(rewards, groups)
+    for g in range(8):
+        assert abs(A[groups == g].sum()) < 1e-15
+    rewards = rng.random(64)
+    A = O.group_mean_advantages(rewards, groups)
+    for g in range(8):
+        assert abs(A[groups == g].sum()) < 1e-14
+
+
+def test_advantage_values_hand_case():
+    A = O.group_mean_advantages(np.array([1.0, 0.0, 0.5, 0.25, 3.0]),
+                                np.array([3, 3, 9, 9, 1]))
+    assert A.tolist() == [0.5, -0.5, 0.125, -0.125, 0.0]
+
+
+def test_equal_rewards_give_zero_loss_and_gradient():
+    p = _small_problem(8)
+    p["rewards"] = np.full_like(p["rewards"], 0.7)
+    out = O.reinforce_zero_fwd_bwd(p["hidden"], p["W"], p["tokens"], p["logmu"],
+                                   p["mask"], p["cu"], p["rewards"], p["group_ids"])
+    assert out["loss"] == 0.0
+    assert not out["d_hidden"].any() and not out["d_lm_head"].any()
+
+
+# --------------------------------------------------------- the loss itself
+def test_two_level_mean_golden():
+    g = json.loads((GOLDEN / "two_level_mean.json").read_text())
+    cu = np.array(g["cu_rows"])
+    mask = np.array(g["mask"], dtype=np.uint8)
+    w = np.array(g["weights"])
+    logmu = np.zeros(len(w))
+    logpi = np.log(w)      # so that log pi - log mu = ln w
+    st = O.loss_stage(logpi, logmu, mask, cu, np.array(g["rewards"]),
+                      np.array(g["group_ids"]))
+    e = g["expected"]
+    assert st["adv"].tolist() == [_frac(a) for a in e["adv"]]
+    assert st["T"].tolist() == e["T"]
+    assert abs(st["loss"] - _frac(e["loss"])) < 1e-15
+    assert abs(st["loss"] - _frac(e["flat_token_mean_loss_for_contrast"])) > 0.1
+    assert np.allclose(st["coef"], [_frac(c) for c in e["coef"]], rtol=0, atol=1e-15)
+    assert abs(st["d3"] - (7 / 8 - math.log(2) / 2)) < 1e-15
+    assert abs(st["kl"] - (-math.log(2) / 2)) < 1e-15
+
+
+def test_T_counts_valid_rows_not_length():
+    cu = np.array([0, 4, 6])
+    mask = np.array([1, 0, 0, 1, 1, 1], dtype=np.uint8)
+    assert O.valid_token_counts(cu, mask).tolist() == [2, 2]
+
+
+def test_response_without_valid_tokens_contributes_nothing():
+    cu = np.array([0, 2, 4, 5])
+    mask = np.array([1, 1, 0, 0, 1], dtype=np.uint8)
+    logpi = np.array([-1.0, -2.0, -3.0, -4.0, -0.5])
+    logmu = logpi - np.array([0.1, -0.2, 5.0, 5.0, 0.3])
+    rewards = np.array([1.0, 0.0, 0.0])
+    groups = np.array([0, 0, 1])
+    st = O.loss_stage(logpi, logmu, mask, cu, rewards, groups)
+    # B = 3 still divides; response 1 (T = 0) adds nothing; response 2 has A = 0
+    want = -(1 / 3) * (0.5 * (math.exp(0.1) + math.exp(-0.2)) / 2)
+    assert abs(st["loss"] - want) < 1e-15
+    assert st["coef"][2] == 0.0 and st["coef"][3] == 0.0
+
+
+# ------------------------------------------------------------- diagnostics
+def test_unit_weights_give_exact_zero_diagnostics():
+    rng = _rng(9)
+    logpi = -rng.random(1000) * 12
+    d3, kl = O.diagnostics(logpi, logpi.copy())
+    assert d3 == 0.0 and kl == 0.0
+
+
+def test_empty_valid_set_gives_nan():
+    d3, kl = O.diagnostics(np.zeros(3), np.zeros(3), np.zeros(3, dtype=np.uint8))
+    assert math.isnan(d3) and math.isnan(kl)
+
+
+def test_lag_noise_closed_form():
+    g = json.loads((GOLDEN / "lag_noise_d3.json").read_text())
+    n = 1_000_000
+    for case in g["cases"]:
+        sigma = case["sigma"]
+        rng = _rng(11)
+        logpi = -12.0 + rng.standard_normal(n)
+        logmu = logpi + sigma * rng.standard_normal(n)
+        d3, kl = O.diagnostics(logpi, logmu)
+        se_d3 = sigma ** 2 / math.sqrt(2 * n)
+        assert abs(d3 - case["expected_d3"]) < 5 * se_d3
+        assert abs(kl) < 5 * sigma / math.sqrt(n)
+
+
+# ---------------------------------------------------------------- gradient
+def _fd_check(p, seed):
+    out = O.reinforce_zero_fwd_bwd(p["hidden"], p["W"], p["tokens"], p["logmu"],
+                                   p["mask"], p["cu"], p["rewards"], p["group_ids"])
+    rng = _rng(seed)
+    eps = 1e-6
+    for name, arr, grad in (("hidden", p["hidden"], out["d_hidden"]),
+                            ("W", p["W"], out["d_lm_head"])):
+        scale = np.abs(grad).max()
+        flat = rng.choice(arr.size, size=min(64, arr.size), replace=False)
+        for f in flat:
+            idx = np.unravel_index(f, arr.shape)
+            plus, minus = arr.copy(), arr.copy()
+            plus[idx] += eps
+            minus[idx] -= eps
+            if name == "hidden":
+                fd = (_loss_of(p, plus, p["W"]) - _loss_of(p, minus, p["W"])) / (2 * eps)
+            else:
+                fd = (_loss_of(p, p["hidden"], plus) - _loss_of(p, p["hidden"], minus)) / (2 * eps)
+            assert abs(fd - grad[idx]) <= 1e-6 * scale + 1e-6 * abs(grad[idx]), (name, idx)
+    # random directions through both inputs at once
+    for _ in range(4):
+        dh = rng.standard_normal(p["hidden"].shape)
+        dw = rng.standard_normal(p["W"].shape)
+        fd = (_loss_of(p, p["hidden"] + eps * dh, p["W"] + eps * dw)
+              - _loss_of(p, p["hidden"] - eps * dh, p["W"] - eps * dw)) / (2 * eps)
+        an = float((out["d_hidden"] * dh).sum() + (out["d_lm_head"] * dw).sum())
+        assert abs(fd - an) <= 1e-6 * max(1e-12, abs(an)) + 1e-9
+
+
+@pytest.mark.parametrize("seed", [21, 22])
+def test_finite_difference_gradients(seed):
+    _fd_check(_small_problem(seed), seed + 100)
+
+
+def test_finite_difference_gradients_unmasked_single_group():
+    _fd_check(_small_problem(23, masked=False, group_size=4), 123)
+
+
+def test_unit_weights_gradient_is_plain_reinforce():
+    """log mu := log pi makes w = 1; the IS loss's gradient must then equal the
+    gradient of the plain REINFORCE surrogate
+    J = -(1/B) sum_i (A_i / T_i) sum_t log pi_t, taken by finite differences."""
+    p = _small_problem(24)
+    logpi_all, _ = O.token_logprobs(p["hidden"], p["W"], p["tokens"])
+    p["logmu"] = np.where(p["mask"] != 0, logpi_all, 0.0)
+    out = O.reinforce_zero_fwd_bwd(p["hidden"], p["W"], p["tokens"], p["logmu"],
+                                   p["mask"], p["cu"], p["rewards"], p["group_ids"])
+    assert out["d3"] == 0.0 and out["kl"] == 0.0
+    assert abs(out["loss"] + np.sum(out["adv"]) / len(p["rewards"])) < 1e-15
+    B = len(p["rewards"])
+    A = out["adv"]
+    T = out["T"]
+
+    def surrogate(hidden, W):
+        lp, _ = O.token_logprobs(hidden, W, p["tokens"])
+        tot = 0.0
+        for i in range(B):
+            rows = range(p["cu"][i], p["cu"][i + 1])
+            tot += A[i] / T[i] * sum(lp[t] for t in rows if p["mask"][t])
+        return -tot / B
+
+    rng = _rng(124)
+    eps = 1e-6
+    for _ in range(6):
+        dh = rng.standard_normal(p["hidden"].shape)
+        dw = rng.standard_normal(p["W"].shape)
+        fd = (surrogate(p["hidden"] + eps * dh, p["W"] + eps * dw)
+              - surrogate(p["hidden"] - eps * dh, p["W"] - eps * dw)) / (2 * eps)
+        an = float((out["d_hidden"] * dh).sum() + (out["d_lm_head"] * dw).sum())
+        assert abs(fd - an) <= 1e-6 * abs(an) + 1e-10
+
+
+def test_masked_rows_do_not_affect_loss_or_gradients():
+    p = _small_problem(25)
+    base = O.reinforce_zero_fwd_bwd(p["hidden"], p["W"], p["tokens"], p["logmu"],
+                                    p["mask"], p["cu"], p["rewards"], p["group_ids"])
+    q = dict(p)
+    m0 = p["mask"] == 0
+    assert m0.any()
+    rng = _rng(26)
+    q["hidden"] = p["hidden"].copy()
+    q["hidden"][m0] = rng.standard_normal((int(m0.sum()), p["hidden"].shape[1]))
+    q["logmu"] = p["logmu"].copy()
+    q["logmu"][m0] = -50.0
+    q["tokens"] = p["tokens"].copy()
+    q["tokens"][m0] = 0
+    other = O.reinforce_zero_fwd_bwd(q["hidden"], q["W"], q["tokens"], q["logmu"],
+                                     q["mask"], q["cu"], q["rewards"], q["group_ids"])
+    assert base["loss"] == other["loss"]
+    assert np.array_equal(base["d_lm_head"], other["d_lm_head"])
+    assert not base["d_hidden"][m0].any() and not base["logpi"][m0].any()
+
+
+# ------------------------------------------- exact-enumeration IS identities
+def test_importance_sampling_identities_by_enumeration():
+    """'The full IS correction' on the REINFORCE Zero project page: at a fixed
+    history with sampler q = mu and target p = pi, E_q[w s] = 0 and
+    E_q[w A s] = Cov_p(A, s) = E_p[A s], where s = grad_z log pi.  A batch of
+    single-token responses whose token multiset is exactly mu turns the batch
+    means into these expectations, with no sampling error."""
+    mu = np.array([0.5, 0.25, 0.125, 0.125])
+    tokens = np.array([0, 0, 0, 0, 1, 1, 2, 3])       # multiset reproduces mu
+    reward_of = np.array([1.0, 0.0, 0.5, 1.0])
+    z = np.array([0.3, -0.1, 0.7, 0.0])
+    W = z[:, None]                                     # H = 1, hidden = [1]
+    hidden = np.ones((8, 1))
+    B = 8
+    logmu = np.log(mu[tokens])
+    mask = np.ones(8, dtype=np.uint8)
+    cu = np.arange(9)
+    rewards = reward_of[tokens]
+    groups = np.zeros(8, dtype=np.int64)
+    out = O.reinforce_zero_fwd_bwd(hidden, W, tokens, logmu, mask, cu, rewards, groups)
+
+    pi = np.exp(z) / np.exp(z).sum()
+    score = np.eye(4) - pi                     # row a: grad_z log pi(a)
+    # E_q[w s] = sum_a mu(a) (pi(a)/mu(a)) s(a) = sum_a pi(a) s(a) = 0
+    w = np.exp(O.log_ratio(out["logpi"], logmu))
+    assert np.allclose((w[:, None] * score[tokens]).mean(axis=0), 0.0, atol=1e-15)
+    # the loss gradient wrt the shared logits is -(1/B) sum_i A_i w_i s(a_i)
+    # and dW[:, 0] collects it (hidden = 1); it must equal -E_p[A s].
+    rbar = (mu * reward_of).sum()
+    target = (pi[:, None] * (reward_of - rbar)[:, None] * score).sum(axis=0)
+    assert np.allclose(-out["d_lm_head"][:, 0], target, rtol=0, atol=1e-14)
+    # D3 = E_mu[w - 1 - log w] = KL(mu || pi) exactly, and so is the k1 KL
+    kl_exact = float((mu * np.log(mu / pi)).sum())
+    assert abs(out["d3"] - kl_exact) < 1e-15
+    assert abs(out["kl"] - kl_exact) < 1e-15
+    assert kl_exact > 0.0
+    assert B == len(rewards)
