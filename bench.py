@@ -1,0 +1,186 @@
+"""Benchmark: one REINFORCE Zero learner step (logprobs + IS loss + gradients)
+per step on the Qwen3-4B tool-use shape, on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one rz_reinforce_zero_fwd_bwd call over the whole synthetic batch
+(inputs already resident in HBM).  Prints ONE JSON line with the throughput
+in valid tokens/s, the fraction of bf16 MFMA peak on the algorithmic
+6 H V FLOP per valid token, the roofline of the dominant kernel (its
+launches timed live with HIP events on the call's stream), and the float64
+oracle timed on a bounded sample on the host cores.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tokens/s fused logprob+IS-loss fwd/bwd (Qwen3-4B shape); % MFMA peak"
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA
+HBM_GBS = 8000.0
+GEMM_KERNELS = ("fwd_logits_gemm", "bwd_dz_gemm", "bwd_dh_gemm", "bwd_dw_gemm")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def behaviour_logprobs(torch, hidden, head, tokens, rows=2048):
+    """Stand-in rollout policy (plain torch fp32 on the GPU) that places
+    log mu near log pi; it is input preparation, never timed or compared."""
+    Wf = head.float().t().contiguous()
+    out = torch.empty(hidden.shape[0], dtype=torch.float32, device=hidden.device)
+    for r0 in range(0, hidden.shape[0], rows):
+        r1 = min(hidden.shape[0], r0 + rows)
+        lp = torch.log_softmax(hidden[r0:r1].float() @ Wf, dim=1)
+        out[r0:r1] = lp.gather(1, tokens[r0:r1].long()[:, None])[:, 0]
+    del Wf
+    return out
+
+
+def cpu_baseline(b, logmu, max_valid):
+    """The float64 oracle, as it stands, on the first responses of the same
+    workload up to `max_valid` valid rows at the full H and V."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = None
+    cores = len(os.sched_getaffinity(0))
+    valid = np.flatnonzero(b.mask != 0)
+    n_keep = int(valid[max_valid - 1]) + 1 if len(valid) > max_valid else b.N
+    cu = b.cu_rows.astype(np.int64)
+    nb = int(np.searchsorted(cu, n_keep, side="left"))
+    cu_s = cu[: nb + 1].copy()
+    cu_s[nb] = n_keep
+    hidden = O.to_f64(b.hidden[:n_keep], b.dtype)
+    head = O.to_f64(b.lm_head, b.dtype)
+    t0 = time.perf_counter()
+    out = O.reinforce_zero_fwd_bwd(hidden, head, b.tokens[:n_keep],
+                                   logmu[:n_keep].astype(np.float64),
+                                   b.mask[:n_keep], cu_s, b.rewards[:nb],
+                                   b.group_ids[:nb])
+    dt = time.perf_counter() - t0
+    nv = int(np.count_nonzero(b.mask[:n_keep]))
+    assert np.isfinite(out["loss"])
+    return {"value": nv / dt, "unit": "tokens/s", "cores": blas_threads or cores,
+            "kind": "oracle",
+            "sample": (f"first {nb} responses, {nv} valid of {n_keep} rows of "
+                       f"{b.name} at full H={b.H}, V={b.V}; float64 NumPy "
+                       f"fwd+loss+bwd, {dt:.1f} s on {cores} host cores "
+                       f"(BLAS threads {blas_threads})")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="qwen3_4b_tool")
+    ap.add_argument("--cpu-valid", type=int, default=1024,
+                    help="valid rows in the oracle's CPU-baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(this path has no multi-GPU mode)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import invariant_token_logprobs_amd as rz
+    from invariant_token_logprobs_amd import synth
+
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    b = synth.make_workload(args.workload)
+    log(f"workload {b.name}: N={b.N} B={b.B} valid={b.n_valid} H={b.H} V={b.V} "
+        f"({time.time() - t0:.1f}s to draw)")
+
+    def up(x, bf16=False):
+        t = torch.from_numpy(np.ascontiguousarray(x.view(np.int16) if bf16 else x))
+        return (t.view(torch.bfloat16) if bf16 else t).to(dev)
+
+    isbf = b.dtype == "bf16"
+    hidden, head = up(b.hidden, isbf), up(b.lm_head, isbf)
+    tokens = up(b.tokens)
+    mu_ref = behaviour_logprobs(torch, hidden, head, tokens)
+    logmu = synth.make_logmu(mu_ref.cpu().numpy(), b.sigma, b.noise_seed)
+    del mu_ref
+    torch.cuda.empty_cache()
+    args_dev = [hidden, head, tokens, up(logmu), up(b.mask), up(b.cu_rows),
+                up(b.rewards), up(b.group_ids)]
+    ws = rz.Workspace()
+    outs = {}
+    step = lambda: rz.reinforce_zero_fwd_bwd(*args_dev, workspace=ws, outputs=outs)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    rz.timing_enable(True)
+    rz.timing_read(reset=True)
+    torch.cuda.synchronize()
+    ts = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    te = time.perf_counter()
+    kt = rz.timing_read(reset=True)
+    rz.timing_enable(False)
+    loss = float(outs["loss"].cpu()[0])
+    assert np.isfinite(loss), "non-finite loss"
+
+    ms = (te - ts) * 1e3 / args.steps
+    nv = b.n_valid
+    value = nv * args.steps / (te - ts)
+    flop_alg = 6.0 * b.H * b.V * nv
+    peak = PEAK_TFLOPS[b.dtype]
+    mfma_frac = flop_alg / (ms * 1e-3) / (peak * 1e12)
+
+    # dominant kernel and its roofline (per-launch average, live HIP events)
+    kms = {k: v[0] / args.steps for k, v in kt.items() if v[1]}
+    dom = max(GEMM_KERNELS, key=lambda k: kt[k][0])
+    tot_ms, launches = kt[dom]
+    avg_ms = tot_ms / launches
+    flop_per_launch = 2.0 * b.H * b.V * nv * args.steps / launches
+    achieved = flop_per_launch / (avg_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": None, "avg_launch_ms": round(avg_ms, 4),
+                "launches_per_step": launches // args.steps}
+    log("per-step kernel ms: " + ", ".join(f"{k}={v:.2f}" for k, v in
+                                            sorted(kms.items(), key=lambda x: -x[1])))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the float64 oracle on a bounded sample ...")
+        cpu = cpu_baseline(b, logmu, args.cpu_valid)
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": b.dtype, "data": "synthetic",
+        "config": {"workload": b.name, "hidden": b.H, "vocab": b.V,
+                   "responses": b.B, "rows": b.N, "valid_tokens": nv,
+                   "masked_frac": round(1 - nv / b.N, 4), "lag_sigma": b.sigma},
+        "mfma_peak_frac_algorithmic": round(mfma_frac, 4),
+        "executed_flop_per_valid_token": 8.0 * b.H * b.V,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernel_ms_per_step": {k: round(v, 3) for k, v in kms.items()},
+        "loss": loss,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

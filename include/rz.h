@@ -1,0 +1,189 @@
+/*
+ * rz.h -- C ABI of librz: batch-invariant per-token logprobs and the
+ * REINFORCE Zero importance-sampling loss on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (sources are cited by page title and section):
+ *
+ *  - log pi_theta(a_t | h_t): the learner's logprob of each sampled token,
+ *    through a linear LM head (z = h W^T, W laid out [V, H], no bias,
+ *    temperature 1), a log-softmax over the whole vocabulary and a gather.
+ *    ("REINFORCE Zero" project page, section 02, "A minimal REINFORCE
+ *    objective": pi_theta(a_it | h_it); the head itself is a reading, the
+ *    pages never spell it out.)  The result for a row is bit-identical for
+ *    the same (hidden row, W, token) whatever the number of rows, the row
+ *    offset, the other rows in the batch or the entry point that computed
+ *    it: the trainer-inference invariance the pages turn on (project page
+ *    section 02 "Remove kernel mismatch"; vLLM blog "Zero mismatch, simple
+ *    async RL", section 5, "diff 0").
+ *
+ *  - the unclipped token-level IS-REINFORCE loss (vLLM blog section 4, loss
+ *    equation; project page "A minimal REINFORCE objective"):
+ *        L = -(1/B) sum_i (1/T_i) sum_{valid t in i} A_i * w_t,
+ *        w_t = exp(log pi_t - log mu_t)   (no clipping, no filtering),
+ *        A_i = r_i - mean of r over the group of i,
+ *        T_i = number of valid (mask = 1) rows of response i,
+ *    and its gradient through the numerator pi_theta only, with respect to
+ *    the hidden states and the LM-head weights.
+ *
+ *  - the diagnostics D3 = mean over valid tokens of (w - 1 - log w)
+ *    (vLLM blog section 3) and the sampled rollout-to-learner KL, read as
+ *    the k1 estimate mean(log mu - log pi) (vLLM blog section 4).
+ *
+ * Conventions shared by every entry point:
+ *  - All array arguments are DEVICE pointers owned by the caller, row-major
+ *    and contiguous.  The library never allocates, frees or synchronises: it
+ *    enqueues work on `stream` (a hipStream_t; NULL = the null stream) and
+ *    outputs are valid once the stream reaches that point.
+ *  - Scratch memory is a caller-provided device workspace of at least
+ *    rz_workspace_bytes(...) bytes, 256-byte aligned.  Its contents on entry
+ *    do not matter and on return are unspecified.
+ *  - hidden and lm_head are fp32 (RZ_DTYPE_F32) or bfloat16 (RZ_DTYPE_BF16);
+ *    every other floating-point array is fp32.  Arithmetic accumulates in
+ *    fp32 (reductions over tokens in fp64).
+ *  - Argument errors that the host can see return a negative rz_status
+ *    before any HIP call (so they are testable without a GPU).  n_rows = 0
+ *    is a valid no-op.
+ *  - Errors only the device can see set bits in *err_flag (a device int32,
+ *    may be NULL; bits are OR-ed in, never cleared) and turn the affected
+ *    outputs into NaN; the call still completes normally.
+ *  - The library keeps no state between calls except the optional kernel
+ *    timer (rz_timing_*), which is process-global and not thread-safe.
+ */
+#ifndef RZ_H_
+#define RZ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RZ_OK = 0,
+  RZ_ERR_INVALID_ARG = -1, /* null required pointer, bad size or count     */
+  RZ_ERR_UNSUPPORTED = -2, /* unknown dtype, H not a multiple of 64, ...    */
+  RZ_ERR_WORKSPACE = -3,   /* workspace NULL, misaligned or too small      */
+  RZ_ERR_HIP = -4          /* a HIP launch or event call failed            */
+} rz_status;
+
+typedef enum { RZ_DTYPE_F32 = 0, RZ_DTYPE_BF16 = 1 } rz_dtype;
+
+typedef enum {
+  RZ_OP_TOKEN_LOGPROBS = 0,
+  RZ_OP_FWD_BWD = 1,
+  RZ_OP_DIAGNOSTICS = 2
+} rz_op;
+
+/* device-side error bits written to *err_flag */
+#define RZ_DEVERR_TOKEN 1   /* a token id outside [0, V): its logprob is NaN  */
+#define RZ_DEVERR_GROUP 2   /* a group id outside [0, n_resp): loss/adv NaN    */
+#define RZ_DEVERR_CU_ROWS 4 /* cu_rows not 0..n_rows monotone: loss/adv NaN   */
+
+/* Limits checked on the host. */
+#define RZ_MAX_ROWS ((int64_t)1 << 30)
+#define RZ_MAX_VOCAB (1 << 24)
+#define RZ_MAX_HIDDEN 32768
+
+/* Bytes of workspace an entry point needs for the given sizes; 0 when the
+ * sizes are themselves invalid (the call would return an error anyway).
+ * For RZ_OP_DIAGNOSTICS only n_rows is read. */
+size_t rz_workspace_bytes(rz_op op, int64_t n_rows, int32_t n_resp, int32_t H,
+                          int32_t V, rz_dtype dt);
+
+/* Static description of an error code. Never NULL. */
+const char* rz_status_string(rz_status s);
+
+/*
+ * rz_token_logprobs -- the rollout-shaped (or learner-shaped) forward.
+ *
+ *   hidden   [n_rows, H]  dt      final hidden state of each history h_t
+ *   lm_head  [V, H]       dt      LM-head weights W
+ *   tokens   [n_rows]     int32   sampled token a_t of each row
+ *   logprobs [n_rows]     fp32    out: log pi(a_t | h_t)
+ *   lse      [n_rows]     fp32    out, may be NULL: log sum_v exp(z[t, v])
+ *   err_flag              int32   may be NULL; RZ_DEVERR_TOKEN on bad tokens
+ *
+ * H must be a multiple of 64.  Rows are independent; the row's result does
+ * not depend on n_rows, on its position or on the other rows.
+ */
+rz_status rz_token_logprobs(const void* hidden, const void* lm_head,
+                            const int32_t* tokens, int64_t n_rows, int32_t H,
+                            int32_t V, rz_dtype dt, float* logprobs,
+                            float* lse, int32_t* err_flag, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
+ * rz_reinforce_zero_fwd_bwd -- one learner step of the hot path.
+ *
+ *   hidden    [n_rows, H]  dt     final hidden states, responses packed
+ *   lm_head   [V, H]       dt     LM-head weights
+ *   tokens    [n_rows]     int32  sampled tokens (the caller has applied the
+ *                                 next-token shift: row t predicts tokens[t])
+ *   logmu     [n_rows]     fp32   recorded behaviour logprob log mu of tokens[t]
+ *   mask      [n_rows]     uint8  1 = valid action token, 0 = masked row
+ *   cu_rows   [n_resp + 1] int32  response i owns rows [cu_rows[i], cu_rows[i+1]);
+ *                                 cu_rows[0] = 0, cu_rows[n_resp] = n_rows
+ *   rewards   [n_resp]     fp32   scalar reward r_i
+ *   group_ids [n_resp]     int32  group of response i, in [0, n_resp)
+ *
+ *   logprobs  [n_rows]     fp32 out: log pi on valid rows, 0 on masked rows
+ *   loss      [1]          fp32 out: L (above)
+ *   d_hidden  [n_rows, H]  fp32 out: dL/dhidden; zero rows where mask = 0
+ *   d_lm_head [V, H]       fp32 out: dL/dW, overwritten (not accumulated)
+ *   diag      [2]          fp32 out, may be NULL: {D3, KL} over valid rows,
+ *                               bit-identical to rz_diagnostics(logprobs,
+ *                               logmu, mask) on this call's outputs
+ *   adv       [n_resp]     fp32 out, may be NULL: A_i
+ *
+ * A response with T_i = 0 adds nothing to L or the gradients; B = n_resp
+ * still counts it.  No clipping is applied anywhere: a large log-ratio gives
+ * an infinite weight and loss, as the method prescribes.
+ * Device-detected faults: RZ_DEVERR_TOKEN (that row's logprob is NaN, and so
+ * are the loss and gradients it feeds), RZ_DEVERR_GROUP and RZ_DEVERR_CU_ROWS
+ * (loss, adv and the gradients are NaN).
+ * Determinism: every output is identical run to run for identical inputs;
+ * logprobs rows are additionally batch-invariant as in rz_token_logprobs.
+ */
+rz_status rz_reinforce_zero_fwd_bwd(
+    const void* hidden, const void* lm_head, const int32_t* tokens,
+    const float* logmu, const uint8_t* mask, const int32_t* cu_rows,
+    const float* rewards, const int32_t* group_ids, int64_t n_rows,
+    int32_t n_resp, int32_t H, int32_t V, rz_dtype dt, float* logprobs,
+    float* loss, float* d_hidden, float* d_lm_head, float* diag, float* adv,
+    int32_t* err_flag, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * rz_diagnostics -- D3 and the k1 rollout-to-learner KL.
+ *
+ *   logpi [n] fp32, logmu [n] fp32, mask [n] uint8 (may be NULL = all valid)
+ *   diag  [2] fp32 out: {mean(expm1(d) - d), mean(-d)} over valid entries,
+ *         d = logpi - logmu; NaN for both when no entry is valid.
+ *
+ * The reduction order depends only on n, so the result is a pure function
+ * of (logpi, logmu, mask, n).
+ */
+rz_status rz_diagnostics(const float* logpi, const float* logmu,
+                         const uint8_t* mask, int64_t n, float* diag,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
+ * Kernel timer (measurement support).  While enabled, every kernel launch of
+ * the entry points above is bracketed by a pair of HIP events on the call's
+ * stream.  rz_timing_read waits for those events, adds each launch's elapsed
+ * time to its kernel's total, and copies totals (milliseconds) and launch
+ * counts for kernels 0 .. rz_timing_num_kernels()-1; reset != 0 clears them.
+ * Enabling creates the events (host-side driver objects, no device memory);
+ * disabling destroys them.  Not thread-safe.
+ */
+rz_status rz_timing_enable(int on);
+int rz_timing_num_kernels(void);
+const char* rz_timing_kernel_name(int k);
+rz_status rz_timing_read(double* total_ms, int64_t* launches, int reset);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RZ_H_ */

@@ -1,0 +1,14 @@
+"""Batch-invariant token logprobs and the REINFORCE Zero IS loss on MI355X.
+
+The compute lives in the HIP library ``librz.so`` (C ABI declared in
+``include/rz.h``); the functions here only marshal torch tensors into it.
+Importing the package does not load the library; the first call does, and it
+raises if the library has not been built.
+"""
+from .binding import (  # noqa: F401
+    EXPORTS, RZ_DEVERR_CU_ROWS, RZ_DEVERR_GROUP, RZ_DEVERR_TOKEN,
+    RZ_DTYPE_BF16, RZ_DTYPE_F32, RZ_OP_DIAGNOSTICS, RZ_OP_FWD_BWD,
+    RZ_OP_TOKEN_LOGPROBS, RzError, Workspace, diagnostics, library_path,
+    load_library, reinforce_zero_fwd_bwd, timing_enable, timing_read,
+    token_logprobs, workspace_bytes,
+)

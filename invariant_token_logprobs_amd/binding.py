@@ -1,0 +1,271 @@
+"""ctypes binding of librz (C ABI in include/rz.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of librz.so.  torch supplies device memory and the stream; the
+functions take torch tensors already on the GPU and return torch tensors.
+There is no fallback: if the library is missing or the GPU is absent, the
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+RZ_DTYPE_F32 = 0
+RZ_DTYPE_BF16 = 1
+RZ_OP_TOKEN_LOGPROBS = 0
+RZ_OP_FWD_BWD = 1
+RZ_OP_DIAGNOSTICS = 2
+
+RZ_DEVERR_TOKEN = 1
+RZ_DEVERR_GROUP = 2
+RZ_DEVERR_CU_ROWS = 4
+
+_STATUS = {0: "RZ_OK", -1: "RZ_ERR_INVALID_ARG", -2: "RZ_ERR_UNSUPPORTED",
+           -3: "RZ_ERR_WORKSPACE", -4: "RZ_ERR_HIP"}
+
+EXPORTS = [
+    "rz_workspace_bytes", "rz_status_string", "rz_token_logprobs",
+    "rz_reinforce_zero_fwd_bwd", "rz_diagnostics", "rz_timing_enable",
+    "rz_timing_num_kernels", "rz_timing_kernel_name", "rz_timing_read",
+]
+
+
+class RzError(RuntimeError):
+    def __init__(self, msg, status=None):
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "librz.so")
+
+
+def load_library():
+    """Load librz.so and declare its signatures (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RzError(f"{path} is not built; run "
+                      "`python -m invariant_token_logprobs_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.rz_workspace_bytes.argtypes = [ctypes.c_int, i64, i32, i32, i32, ctypes.c_int]
+    lib.rz_workspace_bytes.restype = sz
+    lib.rz_status_string.argtypes = [ctypes.c_int]
+    lib.rz_status_string.restype = ctypes.c_char_p
+    lib.rz_token_logprobs.argtypes = [vp, vp, vp, i64, i32, i32, ctypes.c_int,
+                                      vp, vp, vp, vp, sz, vp]
+    lib.rz_token_logprobs.restype = ctypes.c_int
+    lib.rz_reinforce_zero_fwd_bwd.argtypes = [
+        vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, ctypes.c_int,
+        vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.rz_reinforce_zero_fwd_bwd.restype = ctypes.c_int
+    lib.rz_diagnostics.argtypes = [vp, vp, vp, i64, vp, vp, sz, vp]
+    lib.rz_diagnostics.restype = ctypes.c_int
+    lib.rz_timing_enable.argtypes = [ctypes.c_int]
+    lib.rz_timing_enable.restype = ctypes.c_int
+    lib.rz_timing_num_kernels.argtypes = []
+    lib.rz_timing_num_kernels.restype = ctypes.c_int
+    lib.rz_timing_kernel_name.argtypes = [ctypes.c_int]
+    lib.rz_timing_kernel_name.restype = ctypes.c_char_p
+    lib.rz_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double),
+                                   ctypes.POINTER(ctypes.c_int64), ctypes.c_int]
+    lib.rz_timing_read.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        lib = load_library()
+        msg = lib.rz_status_string(status).decode()
+        raise RzError(f"{what}: {_STATUS.get(status, status)} ({msg})", status)
+
+
+# ------------------------------------------------------------ marshalling
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return RZ_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return RZ_DTYPE_BF16
+    raise RzError(f"hidden / lm_head must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtype, ndim=None, device=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise RzError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise RzError(f"{name} must live on the GPU")
+    if dtype is not None and t.dtype != dtype:
+        raise RzError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise RzError(f"{name} must have {ndim} dims, got {t.dim()}")
+    if not t.is_contiguous():
+        raise RzError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise RzError(f"{name} is on {t.device}, expected {device}")
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class Workspace:
+    """A grow-only device byte buffer reused across calls on one device."""
+
+    def __init__(self, device=None):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes: int, device):
+        torch = _torch()
+        if nbytes == 0:
+            return None
+        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
+            self.buf = None
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        return self.buf
+
+
+_default_ws = {}
+
+
+def _workspace(ws: Optional[Workspace], nbytes: int, device):
+    if ws is None:
+        ws = _default_ws.setdefault(str(device), Workspace())
+    return ws.get(nbytes, device)
+
+
+def workspace_bytes(op: int, n_rows: int, n_resp: int, H: int, V: int,
+                    dtype_code: int) -> int:
+    return int(load_library().rz_workspace_bytes(op, n_rows, n_resp, H, V,
+                                                 dtype_code))
+
+
+# ------------------------------------------------------------ entry points
+def token_logprobs(hidden, lm_head, tokens, *, want_lse: bool = False,
+                   err_flag=None, workspace: Optional[Workspace] = None,
+                   stream=None, out=None):
+    """log pi(tokens[t] | hidden[t]) for every row (rz_token_logprobs)."""
+    torch = _torch()
+    lib = load_library()
+    dt = _dtype_code(hidden)
+    _need(hidden, "hidden", None, 2)
+    dev = hidden.device
+    _need(lm_head, "lm_head", hidden.dtype, 2, dev)
+    _need(tokens, "tokens", torch.int32, 1, dev)
+    N, H = hidden.shape
+    V = lm_head.shape[0]
+    if lm_head.shape[1] != H or tokens.shape[0] != N:
+        raise RzError("shape mismatch between hidden, lm_head and tokens")
+    logprobs = out if out is not None else torch.empty(N, dtype=torch.float32, device=dev)
+    lse = torch.empty(N, dtype=torch.float32, device=dev) if want_lse else None
+    nbytes = workspace_bytes(RZ_OP_TOKEN_LOGPROBS, N, 1, H, V, dt)
+    ws = _workspace(workspace, nbytes, dev)
+    _check(lib.rz_token_logprobs(_ptr(hidden), _ptr(lm_head), _ptr(tokens), N, H,
+                                 V, dt, _ptr(logprobs), _ptr(lse), _ptr(err_flag),
+                                 _ptr(ws), nbytes, _stream(stream)),
+           "rz_token_logprobs")
+    return (logprobs, lse) if want_lse else logprobs
+
+
+def reinforce_zero_fwd_bwd(hidden, lm_head, tokens, logmu, mask, cu_rows,
+                           rewards, group_ids, *, err_flag=None,
+                           workspace: Optional[Workspace] = None, stream=None,
+                           outputs: Optional[dict] = None):
+    """One learner step (rz_reinforce_zero_fwd_bwd).  Returns a dict with
+    logprobs, loss, d_hidden, d_lm_head, diag (D3, KL) and adv."""
+    torch = _torch()
+    lib = load_library()
+    dt = _dtype_code(hidden)
+    _need(hidden, "hidden", None, 2)
+    dev = hidden.device
+    _need(lm_head, "lm_head", hidden.dtype, 2, dev)
+    _need(tokens, "tokens", torch.int32, 1, dev)
+    _need(logmu, "logmu", torch.float32, 1, dev)
+    _need(mask, "mask", torch.uint8, 1, dev)
+    _need(cu_rows, "cu_rows", torch.int32, 1, dev)
+    _need(rewards, "rewards", torch.float32, 1, dev)
+    _need(group_ids, "group_ids", torch.int32, 1, dev)
+    N, H = hidden.shape
+    V = lm_head.shape[0]
+    B = rewards.shape[0]
+    if (lm_head.shape[1] != H or tokens.shape[0] != N or logmu.shape[0] != N
+            or mask.shape[0] != N or cu_rows.shape[0] != B + 1
+            or group_ids.shape[0] != B):
+        raise RzError("shape mismatch between the fwd_bwd arguments")
+    o = outputs if outputs is not None else {}
+    f32 = torch.float32
+    if "logprobs" not in o:
+        o["logprobs"] = torch.empty(N, dtype=f32, device=dev)
+        o["loss"] = torch.empty(1, dtype=f32, device=dev)
+        o["d_hidden"] = torch.empty((N, H), dtype=f32, device=dev)
+        o["d_lm_head"] = torch.empty((V, H), dtype=f32, device=dev)
+        o["diag"] = torch.empty(2, dtype=f32, device=dev)
+        o["adv"] = torch.empty(B, dtype=f32, device=dev)
+    nbytes = workspace_bytes(RZ_OP_FWD_BWD, N, B, H, V, dt)
+    ws = _workspace(workspace, nbytes, dev)
+    _check(lib.rz_reinforce_zero_fwd_bwd(
+        _ptr(hidden), _ptr(lm_head), _ptr(tokens), _ptr(logmu), _ptr(mask),
+        _ptr(cu_rows), _ptr(rewards), _ptr(group_ids), N, B, H, V, dt,
+        _ptr(o["logprobs"]), _ptr(o["loss"]), _ptr(o["d_hidden"]),
+        _ptr(o["d_lm_head"]), _ptr(o["diag"]), _ptr(o["adv"]), _ptr(err_flag),
+        _ptr(ws), nbytes, _stream(stream)), "rz_reinforce_zero_fwd_bwd")
+    return o
+
+
+def diagnostics(logpi, logmu, mask=None, *, workspace: Optional[Workspace] = None,
+                stream=None, out=None):
+    """(D3, KL) over the valid entries (rz_diagnostics)."""
+    torch = _torch()
+    lib = load_library()
+    _need(logpi, "logpi", torch.float32, 1)
+    dev = logpi.device
+    _need(logmu, "logmu", torch.float32, 1, dev)
+    if mask is not None:
+        _need(mask, "mask", torch.uint8, 1, dev)
+    n = logpi.shape[0]
+    if logmu.shape[0] != n or (mask is not None and mask.shape[0] != n):
+        raise RzError("shape mismatch between logpi, logmu and mask")
+    diag = out if out is not None else torch.empty(2, dtype=torch.float32, device=dev)
+    nbytes = workspace_bytes(RZ_OP_DIAGNOSTICS, n, 1, 64, 1, 0)
+    ws = _workspace(workspace, nbytes, dev)
+    _check(lib.rz_diagnostics(_ptr(logpi), _ptr(logmu), _ptr(mask), n, _ptr(diag),
+                              _ptr(ws), nbytes, _stream(stream)), "rz_diagnostics")
+    return diag
+
+
+# ------------------------------------------------------------ kernel timer
+def timing_enable(on: bool = True):
+    _check(load_library().rz_timing_enable(1 if on else 0), "rz_timing_enable")
+
+
+def timing_read(reset: bool = True) -> dict:
+    """{kernel name: (total ms, launches)} accumulated since the last reset."""
+    lib = load_library()
+    n = lib.rz_timing_num_kernels()
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    _check(lib.rz_timing_read(ms, cnt, 1 if reset else 0), "rz_timing_read")
+    return {lib.rz_timing_kernel_name(k).decode(): (ms[k], cnt[k])
+            for k in range(n)}

@@ -1,0 +1,83 @@
+"""Build librz.so (the HIP kernels and the C ABI) in-tree for gfx950.
+
+    python -m invariant_token_logprobs_amd.build [-v]
+
+Every translation unit is compiled with hipcc for gfx950 only, with the
+packed-fp32 target feature disabled (the compiler still vectorises ordinary
+float code; it just may not emit v_pk_{add,mul,fma}_f32), and linked into
+invariant_token_logprobs_amd/librz.so next to this file.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "librz.so")
+SOURCES = ["rz_kernels.hip", "rz_api.hip"]
+
+ARCH = "gfx950"
+FLAGS = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-ffp-contract=fast",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-result",
+    f"-I{INCLUDE}",
+    f"-I{CSRC}",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"),
+                 "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found; the HIP library cannot be built")
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                         text=True)
+    out = "\n".join(l for l in res.stdout.splitlines()
+                    if "packed-fp32-ops" not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"command failed ({res.returncode}): {' '.join(cmd)}\n{out}")
+    if verbose and out.strip():
+        print(out, flush=True)
+
+
+def build(verbose: bool = False) -> str:
+    cc = hipcc()
+    tmp = tempfile.mkdtemp(prefix="rz_build_")
+    try:
+        objs = []
+        cmds = []
+        for src in SOURCES:
+            obj = os.path.join(tmp, src.replace(".hip", ".o"))
+            objs.append(obj)
+            cmds.append([cc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+            list(ex.map(lambda c: _run(c, verbose), cmds))
+        out_tmp = LIB + ".tmp"
+        _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out_tmp,
+              *objs], verbose)
+        os.replace(out_tmp, LIB)
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

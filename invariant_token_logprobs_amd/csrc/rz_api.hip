@@ -1,0 +1,384 @@
+// rz_api.hip -- the C ABI of librz (declared in include/rz.h): host-side
+// argument checks, workspace layout and the launch sequence of each entry
+// point on the caller's stream.  No allocation, no host synchronisation.
+#include <stdint.h>
+#include <string.h>
+
+#include <vector>
+
+#include "../../include/rz.h"
+#include "rz_internal.h"
+
+namespace rz {
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kChunkRows = 32768;  // backward token chunk (a multiple of 256)
+constexpr int kVocabTile = 256;
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+inline size_t esize(rz_dtype dt) { return dt == RZ_DTYPE_BF16 ? 2 : 4; }
+
+// Bump allocator over the caller's workspace; with base == nullptr it only
+// measures.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  template <typename P>
+  P* take(size_t bytes) {
+    P* p = base ? reinterpret_cast<P*>(base + off) : nullptr;
+    off += align_up(bytes);
+    return p;
+  }
+};
+
+bool dims_ok(int32_t H, int32_t V, rz_dtype dt) {
+  return (dt == RZ_DTYPE_F32 || dt == RZ_DTYPE_BF16) && H > 0 &&
+         H <= RZ_MAX_HIDDEN && (H % 64) == 0 && V > 0 && V <= RZ_MAX_VOCAB;
+}
+
+int chunk_rows(int64_t n) {
+  const int64_t c = round_up(n > 0 ? n : 1, 256);
+  return (int)(c < kChunkRows ? c : kChunkRows);
+}
+
+// ---- token_logprobs layout ----
+struct TlpWs {
+  float2* partials;
+  float* ztgt;
+};
+size_t carve_tlp(Carver& c, int64_t n, int32_t V, TlpWs* w) {
+  const int nt = (int)((V + kVocabTile - 1) / kVocabTile);
+  TlpWs t;
+  t.partials = c.take<float2>(sizeof(float2) * (size_t)nt * (size_t)n);
+  t.ztgt = c.take<float>(sizeof(float) * (size_t)n);
+  if (w) *w = t;
+  return c.off;
+}
+
+// ---- fwd_bwd layout ----
+struct FbWs {
+  int* nvalid;
+  int* bad_cu;
+  int* blk;
+  int* idx;
+  int* tokv;
+  int* respv;
+  float2* partials;
+  float* ztgt;
+  float* lse_v;
+  float* logpi_v;
+  float* coef;
+  int* T;
+  double* S;
+  int* gcnt;
+  double* gsum;
+  double* fcoef;
+  float* diag_tmp;
+  void* diag_part;
+  void* WT;
+  void* hT;
+  void* dz;
+  void* dzT;
+  int* counts;
+  int* cursor;
+  int* offsets;
+  int* sorted;
+};
+size_t carve_fb(Carver& c, int64_t n, int32_t B, int32_t H, int32_t V,
+                rz_dtype dt, FbWs* w) {
+  const int nt = (int)((V + kVocabTile - 1) / kVocabTile);
+  const int64_t Vpad = round_up(V, 64);
+  const int C = chunk_rows(n);
+  const size_t es = esize(dt);
+  FbWs t;
+  t.nvalid = c.take<int>(sizeof(int));
+  t.bad_cu = c.take<int>(sizeof(int));
+  t.blk = c.take<int>(sizeof(int) * (size_t)((n + 1023) / 1024 + 1));
+  t.idx = c.take<int>(sizeof(int) * (size_t)n);
+  t.tokv = c.take<int>(sizeof(int) * (size_t)n);
+  t.respv = c.take<int>(sizeof(int) * (size_t)n);
+  t.partials = c.take<float2>(sizeof(float2) * (size_t)nt * (size_t)n);
+  t.ztgt = c.take<float>(sizeof(float) * (size_t)n);
+  t.lse_v = c.take<float>(sizeof(float) * (size_t)n);
+  t.logpi_v = c.take<float>(sizeof(float) * (size_t)n);
+  t.coef = c.take<float>(sizeof(float) * (size_t)n);
+  t.T = c.take<int>(sizeof(int) * (size_t)B);
+  t.S = c.take<double>(sizeof(double) * (size_t)B);
+  t.gcnt = c.take<int>(sizeof(int) * (size_t)B);
+  t.gsum = c.take<double>(sizeof(double) * (size_t)B);
+  t.fcoef = c.take<double>(sizeof(double) * (size_t)B);
+  t.diag_tmp = c.take<float>(2 * sizeof(float));
+  t.diag_part = c.take<char>(diag_partials_bytes(n));
+  t.WT = c.take<char>(es * (size_t)H * (size_t)Vpad);
+  t.hT = c.take<char>(es * (size_t)H * (size_t)C);
+  t.dz = c.take<char>(es * (size_t)C * (size_t)Vpad);
+  t.dzT = c.take<char>(es * (size_t)Vpad * (size_t)C);
+  t.counts = c.take<int>(sizeof(int) * (size_t)V);
+  t.cursor = c.take<int>(sizeof(int) * (size_t)V);
+  t.offsets = c.take<int>(sizeof(int) * ((size_t)V + 1));
+  t.sorted = c.take<int>(sizeof(int) * (size_t)n);
+  if (w) *w = t;
+  return c.off;
+}
+
+rz_status ws_check(void* ws, size_t have, size_t need) {
+  if (need == 0) return RZ_OK;
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0 || have < need)
+    return RZ_ERR_WORKSPACE;
+  return RZ_OK;
+}
+
+#define RZ_TRY(expr)                                  \
+  do {                                                \
+    hipError_t e_ = (expr);                           \
+    if (e_ != hipSuccess) return RZ_ERR_HIP;          \
+  } while (0)
+
+// ---- kernel timer ----
+struct TimerState {
+  bool on = false;
+  struct Pending {
+    int k;
+    hipEvent_t a, b;
+  };
+  std::vector<Pending> pending;
+  std::vector<hipEvent_t> pool;
+  double total[K_NUM_KERNELS] = {};
+  int64_t count[K_NUM_KERNELS] = {};
+  hipEvent_t cur_a = nullptr;
+};
+TimerState g_timer;
+
+hipEvent_t take_event() {
+  if (!g_timer.pool.empty()) {
+    hipEvent_t e = g_timer.pool.back();
+    g_timer.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+}  // namespace
+
+bool Timer::on() { return g_timer.on; }
+
+void Timer::before(int, hipStream_t s) {
+  if (!g_timer.on) return;
+  g_timer.cur_a = take_event();
+  if (g_timer.cur_a) (void)hipEventRecord(g_timer.cur_a, s);
+}
+
+hipError_t Timer::after(int k, hipStream_t s) {
+  if (!g_timer.on || !g_timer.cur_a) return hipSuccess;
+  hipEvent_t b = take_event();
+  if (!b) return hipErrorOutOfMemory;
+  hipError_t e = hipEventRecord(b, s);
+  g_timer.pending.push_back({k, g_timer.cur_a, b});
+  g_timer.cur_a = nullptr;
+  return e;
+}
+
+}  // namespace rz
+
+using namespace rz;
+
+extern "C" {
+
+const char* rz_status_string(rz_status s) {
+  switch (s) {
+    case RZ_OK: return "ok";
+    case RZ_ERR_INVALID_ARG: return "invalid argument";
+    case RZ_ERR_UNSUPPORTED: return "unsupported dtype or size";
+    case RZ_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case RZ_ERR_HIP: return "HIP launch or event failure";
+  }
+  return "unknown status";
+}
+
+size_t rz_workspace_bytes(rz_op op, int64_t n_rows, int32_t n_resp, int32_t H,
+                          int32_t V, rz_dtype dt) {
+  if (n_rows < 0 || n_rows > RZ_MAX_ROWS) return 0;
+  Carver c{nullptr};
+  switch (op) {
+    case RZ_OP_TOKEN_LOGPROBS:
+      if (!dims_ok(H, V, dt)) return 0;
+      return n_rows == 0 ? 0 : carve_tlp(c, n_rows, V, nullptr);
+    case RZ_OP_FWD_BWD:
+      if (!dims_ok(H, V, dt) || n_resp < 1) return 0;
+      return carve_fb(c, n_rows, n_resp, H, V, dt, nullptr);
+    case RZ_OP_DIAGNOSTICS:
+      return align_up(diag_partials_bytes(n_rows));
+  }
+  return 0;
+}
+
+rz_status rz_token_logprobs(const void* hidden, const void* lm_head,
+                            const int32_t* tokens, int64_t n_rows, int32_t H,
+                            int32_t V, rz_dtype dt, float* logprobs,
+                            float* lse, int32_t* err_flag, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (n_rows < 0 || n_rows > RZ_MAX_ROWS) return RZ_ERR_INVALID_ARG;
+  if (dt != RZ_DTYPE_F32 && dt != RZ_DTYPE_BF16) return RZ_ERR_UNSUPPORTED;
+  if (H <= 0 || V <= 0) return RZ_ERR_INVALID_ARG;
+  if (!dims_ok(H, V, dt)) return RZ_ERR_UNSUPPORTED;
+  if (n_rows == 0) return RZ_OK;
+  if (!hidden || !lm_head || !tokens || !logprobs) return RZ_ERR_INVALID_ARG;
+  Carver meas{nullptr};
+  const size_t need = carve_tlp(meas, n_rows, V, nullptr);
+  rz_status st = ws_check(workspace, workspace_bytes, need);
+  if (st != RZ_OK) return st;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  Carver c{reinterpret_cast<char*>(workspace)};
+  TlpWs w;
+  carve_tlp(c, n_rows, V, &w);
+  const int nt = (V + kVocabTile - 1) / kVocabTile;
+  DevRows rows{nullptr, 0, (int)n_rows};
+  RZ_TRY(launch_fwd_logits(dt, hidden, (int64_t)H * esize(dt), nullptr, rows,
+                           lm_head, H, V, tokens, w.partials, n_rows, w.ztgt,
+                           s));
+  RZ_TRY(launch_lse_merge(w.partials, n_rows, nt, rows, w.ztgt, tokens, V,
+                          lse, logprobs, nullptr, nullptr, err_flag, s));
+  return RZ_OK;
+}
+
+rz_status rz_diagnostics(const float* logpi, const float* logmu,
+                         const uint8_t* mask, int64_t n, float* diag,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  if (n < 0 || n > RZ_MAX_ROWS) return RZ_ERR_INVALID_ARG;
+  if (!diag) return RZ_ERR_INVALID_ARG;
+  if (n > 0 && (!logpi || !logmu)) return RZ_ERR_INVALID_ARG;
+  const size_t need = align_up(diag_partials_bytes(n));
+  rz_status st = ws_check(workspace, workspace_bytes, need);
+  if (st != RZ_OK) return st;
+  RZ_TRY(launch_diagnostics(logpi, logmu, mask, n, workspace, diag,
+                            reinterpret_cast<hipStream_t>(stream)));
+  return RZ_OK;
+}
+
+rz_status rz_reinforce_zero_fwd_bwd(
+    const void* hidden, const void* lm_head, const int32_t* tokens,
+    const float* logmu, const uint8_t* mask, const int32_t* cu_rows,
+    const float* rewards, const int32_t* group_ids, int64_t n_rows,
+    int32_t n_resp, int32_t H, int32_t V, rz_dtype dt, float* logprobs,
+    float* loss, float* d_hidden, float* d_lm_head, float* diag, float* adv,
+    int32_t* err_flag, void* workspace, size_t workspace_bytes, void* stream) {
+  if (n_rows < 0 || n_rows > RZ_MAX_ROWS) return RZ_ERR_INVALID_ARG;
+  if (n_resp < 1 || n_resp > (1 << 24)) return RZ_ERR_INVALID_ARG;
+  if (dt != RZ_DTYPE_F32 && dt != RZ_DTYPE_BF16) return RZ_ERR_UNSUPPORTED;
+  if (H <= 0 || V <= 0) return RZ_ERR_INVALID_ARG;
+  if (!dims_ok(H, V, dt)) return RZ_ERR_UNSUPPORTED;
+  if (!lm_head || !cu_rows || !rewards || !group_ids || !loss || !d_lm_head)
+    return RZ_ERR_INVALID_ARG;
+  if (n_rows > 0 && (!hidden || !tokens || !logmu || !mask || !logprobs ||
+                     !d_hidden))
+    return RZ_ERR_INVALID_ARG;
+  Carver meas{nullptr};
+  const size_t need = carve_fb(meas, n_rows, n_resp, H, V, dt, nullptr);
+  rz_status st = ws_check(workspace, workspace_bytes, need);
+  if (st != RZ_OK) return st;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  Carver c{reinterpret_cast<char*>(workspace)};
+  FbWs w;
+  carve_fb(c, n_rows, n_resp, H, V, dt, &w);
+  const int64_t N = n_rows;
+  const int nt = (V + kVocabTile - 1) / kVocabTile;
+  const int Vpad = (int)round_up(V, 64);
+  const int C = chunk_rows(N);
+  const size_t es = esize(dt);
+  const int64_t lda = (int64_t)H * es;
+
+  // a0: valid-row list (device count), cu_rows validation
+  RZ_TRY(launch_mask_compact(mask, N, tokens, cu_rows, n_resp, w.blk,
+                             w.nvalid, w.bad_cu, w.idx, w.tokv, w.respv,
+                             err_flag, s));
+  // a1-a3: logits GEMM with the log-softmax epilogue, ordered merge
+  DevRows vrows{w.nvalid, 0, (int)N};
+  if (N > 0) {
+    RZ_TRY(launch_fwd_logits(dt, hidden, lda, w.idx, vrows, lm_head, H, V,
+                             w.tokv, w.partials, N, w.ztgt, s));
+    RZ_TRY(launch_lse_merge(w.partials, N, nt, vrows, w.ztgt, w.tokv, V,
+                            w.lse_v, w.logpi_v, w.idx, logprobs, err_flag, s));
+    RZ_TRY(launch_rows_finalize(mask, N, H, logprobs, d_hidden, s));
+  }
+  // a4-a5: weights, T_i, advantages, loss, per-token coefficients
+  RZ_TRY(launch_loss(mask, logprobs, logmu, N, cu_rows, rewards, group_ids,
+                     n_resp, w.bad_cu, w.T, w.S, w.gcnt, w.gsum, w.fcoef, adv,
+                     loss, err_flag, s));
+  if (N > 0)
+    RZ_TRY(launch_coef(w.nvalid, N, w.logpi_v, logmu, w.idx, w.respv,
+                       w.fcoef, w.coef, s));
+  // a6: diagnostics over this call's outputs (same kernels as rz_diagnostics)
+  RZ_TRY(launch_diagnostics(logprobs, logmu, mask, N, w.diag_part,
+                            diag ? diag : w.diag_tmp, s));
+  // a7-a9: backward in token chunks of C valid rows
+  RZ_TRY(launch_transpose(dt, K_TRANSPOSE_W, lm_head, H, nullptr,
+                          DevRows{nullptr, 0, V}, Vpad, H, w.WT, Vpad, s));
+  const int64_t nchunks = N > 0 ? (N + C - 1) / C : 1;
+  for (int64_t k = 0; k < nchunks; ++k) {
+    DevRows crow{w.nvalid, k * C, C};
+    if (N > 0) {
+      RZ_TRY(launch_transpose(dt, K_TRANSPOSE_H, hidden, H, w.idx, crow, C, H,
+                              w.hT, C, s));
+      RZ_TRY(launch_bwd_dz(dt, hidden, lda, w.idx, crow, lm_head, H, V, Vpad,
+                           w.lse_v, w.coef, w.dz, Vpad, w.dzT, C, s));
+      RZ_TRY(launch_bwd_dh(dt, w.dz, Vpad, crow, w.WT, Vpad, H, V, Vpad,
+                           w.idx, w.tokv, w.coef, lm_head, d_hidden, s));
+    }
+    RZ_TRY(launch_bwd_dw(dt, w.dzT, C, N > 0 ? crow : DevRows{nullptr, 0, 0},
+                         w.hT, C, H, V, d_lm_head, k == 0, s));
+  }
+  RZ_TRY(launch_dw_fix(dt, w.nvalid, N, w.tokv, w.idx, w.coef, hidden, H, V,
+                       w.counts, w.cursor, w.offsets, w.sorted, d_lm_head, s));
+  return RZ_OK;
+}
+
+rz_status rz_timing_enable(int on) {
+  if (on) {
+    g_timer.on = true;
+    return RZ_OK;
+  }
+  g_timer.on = false;
+  for (auto& p : g_timer.pending) {
+    (void)hipEventDestroy(p.a);
+    (void)hipEventDestroy(p.b);
+  }
+  g_timer.pending.clear();
+  for (auto e : g_timer.pool) (void)hipEventDestroy(e);
+  g_timer.pool.clear();
+  return RZ_OK;
+}
+
+int rz_timing_num_kernels(void) { return K_NUM_KERNELS; }
+
+const char* rz_timing_kernel_name(int k) { return kernel_name(k); }
+
+rz_status rz_timing_read(double* total_ms, int64_t* launches, int reset) {
+  for (auto& p : g_timer.pending) {
+    if (hipEventSynchronize(p.b) != hipSuccess) return RZ_ERR_HIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, p.a, p.b) != hipSuccess) return RZ_ERR_HIP;
+    g_timer.total[p.k] += ms;
+    g_timer.count[p.k] += 1;
+    g_timer.pool.push_back(p.a);
+    g_timer.pool.push_back(p.b);
+  }
+  g_timer.pending.clear();
+  for (int k = 0; k < K_NUM_KERNELS; ++k) {
+    if (total_ms) total_ms[k] = g_timer.total[k];
+    if (launches) launches[k] = g_timer.count[k];
+    if (reset) {
+      g_timer.total[k] = 0.0;
+      g_timer.count[k] = 0;
+    }
+  }
+  return RZ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,230 @@
+// rz_gemm.h -- the one MFMA tile engine behind every contraction of the path.
+//
+// C[m, n] = sum_k A[m, k] * B[n, k] with both operands K-contiguous ("NT"),
+// computed by one fixed 256 x 256 output tile per workgroup, K consumed in
+// fixed 128-byte stages (64 bf16 or 32 fp32 values) from k = 0 upwards, no
+// split-K.  The instruction sequence that produces C[m, n] is the same for
+// every m and n, and does not depend on M: the basis of the batch-invariant
+// logprobs (the trainer-inference invariance of the REINFORCE Zero project
+// page, section 02 "Remove kernel mismatch").
+//
+// Layout of the work (gfx950, CDNA4):
+//  * 256 threads = 4 wave64s in a 2 x 2 grid, each wave owning a 128 x 128
+//    sub-tile = 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 (fp32 inputs use
+//    v_mfma_f32_32x32x2_f32, four per 16-byte fragment);
+//  * A and B stages are staged global -> registers -> LDS, double-buffered
+//    (2 x 64 KB), with a 16-byte-chunk XOR swizzle (chunk ^ (row & 7)) so
+//    both the stage stores and the fragment reads are bank-conflict free;
+//  * the next stage's global loads are issued before the current stage's
+//    MFMAs so their latency hides behind the matrix work;
+//  * workgroups are numbered XCD-aware: the dispatcher places workgroup i on
+//    XCD i % 8, so logical tiles are renumbered to give each XCD a
+//    contiguous range, and within it tiles are walked in groups of tile-rows
+//    so the co-resident workgroups of one XCD share A and B stages in its L2.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rz {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kBM = 256;          // tile rows (M)
+constexpr int kBN = 256;          // tile columns (N)
+constexpr int kRowBytes = 128;    // K bytes per stage row
+constexpr int kThreads = 256;
+constexpr int kTM = 4;            // 32 x 32 blocks per wave along M
+constexpr int kTN = 4;            // ... along N
+constexpr int kOperandBytes = kBM * kRowBytes;      // 32 KB
+constexpr int kStageBytes = 2 * kOperandBytes;      // A + B
+constexpr int kLdsBytes = 2 * kStageBytes;          // double buffer, 128 KB
+constexpr int kGroupM = 8;        // tile-rows walked together per XCD
+
+template <typename T>
+struct Stage {
+  static constexpr int kK = kRowBytes / (int)sizeof(T);  // K values per stage
+};
+
+constexpr float kLog2e = 1.4426950408889634f;  // log2(e), for exp via exp2
+
+__device__ __forceinline__ float exp_approx(float x) {
+  // e^x = 2^(x log2 e); v_exp_f32 evaluates 2^y
+  return __builtin_amdgcn_exp2f(x * kLog2e);
+}
+
+// One 16-byte fragment step of the MFMA pipe: 32x32x16 for bf16 ...
+__device__ __forceinline__ void mfma_step(f32x16& acc, u32x4 a, u32x4 b,
+                                          const bf16*) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+      __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc, 0, 0,
+      0);
+}
+// ... or four 32x32x2 steps for fp32 (lane half h holds k = 4h .. 4h+3 of the
+// 8-value slice; both operands use the same mapping, so the K sum is exact).
+// The whole 16-byte vector is reinterpreted first: bit-casting single vector
+// elements is miscompiled by this toolchain (every element reads lane 0).
+__device__ __forceinline__ void mfma_step(f32x16& acc, u32x4 a, u32x4 b,
+                                          const float*) {
+  const f32x4 af = __builtin_bit_cast(f32x4, a);
+  const f32x4 bf = __builtin_bit_cast(f32x4, b);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(af[j], bf[j], acc, 0, 0, 0);
+}
+
+// Rows of a launch whose count may live on the device (valid-row count).
+struct RowCount {
+  const int* count;  // device count of rows in the whole list (nullable)
+  int64_t base;      // first list position covered by this launch
+  int cap;           // rows of this launch when count is null; upper bound
+  __device__ __forceinline__ int get() const {
+    if (!count) return cap;
+    const int64_t r = (int64_t)(*count) - base;
+    return r <= 0 ? 0 : (r < cap ? (int)r : cap);
+  }
+};
+
+struct TileCoord {
+  int tm, tn;
+};
+
+// XCD-aware, grouped tile order.  Bijective on [0, mt * nt).
+__device__ __forceinline__ TileCoord map_tile(int bid, int nblk, int mt,
+                                              int nt) {
+  const int per = nblk >> 3, rem = nblk & 7;
+  const int x = bid & 7, local = bid >> 3;
+  const int logical = x * per + (x < rem ? x : rem) + local;
+  const int width = kGroupM * nt;
+  const int g = logical / width;
+  const int first = g * kGroupM;
+  const int gm = (mt - first) < kGroupM ? (mt - first) : kGroupM;
+  const int in = logical - g * width;
+  return {first + in % gm, in / gm};
+}
+
+// Position of accumulator register r of block (mi, ni) inside the 256 x 256
+// tile, for v_mfma_*_32x32 output: lane l holds column l % 32 and rows
+// 8 * (r / 4) + 4 * (l / 32) + (r % 4) of its 32 x 32 block.
+__device__ __forceinline__ int acc_row(int wm, int mi, int r, int lane) {
+  return wm * 128 + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+__device__ __forceinline__ int acc_col(int wn, int ni, int lane) {
+  return wn * 128 + ni * 32 + (lane & 31);
+}
+
+struct GemmOperands {
+  const char* A;        // A[m, :] row base is A + row(m) * lda
+  int64_t lda;          // bytes
+  const int* a_rows;    // optional gather: row(m) = a_rows[a_base + m]
+  int64_t a_base;       // else row(m) = a_base + m
+  const char* B;        // B[n, :] row base is B + n * ldb
+  int64_t ldb;          // bytes
+  int N;                // rows of B (columns of C)
+};
+
+// Accumulate acc over K stages [0, nk) for the tile at (m0, n0).  Rows of A
+// at or past M (and rows of B at or past N) are read from row M-1 (N-1) so
+// every load stays in bounds; their results are discarded by the epilogue.
+// Leaves the LDS free (all waves past the last barrier) on return.
+template <typename T>
+__device__ __forceinline__ void gemm_mainloop(const GemmOperands& op, int M,
+                                              int m0, int n0, int nk,
+                                              f32x16 (&acc)[kTM][kTN],
+                                              char* lds) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wid = tid >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+
+#pragma unroll
+  for (int mi = 0; mi < kTM; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < kTN; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+  if (nk <= 0) return;
+
+  // global -> register assignment: chunk (tid & 7) of rows (tid >> 3) + 32 i
+  const int gchunk = tid & 7;
+  const int grow = tid >> 3;
+  const char* aptr[8];
+  const char* bptr[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    int m = m0 + grow + 32 * i;
+    m = m < M ? m : M - 1;
+    const int64_t prow = op.a_rows ? (int64_t)op.a_rows[op.a_base + m]
+                                   : op.a_base + m;
+    aptr[i] = op.A + prow * op.lda + gchunk * 16;
+    int n = n0 + grow + 32 * i;
+    n = n < op.N ? n : op.N - 1;
+    bptr[i] = op.B + (int64_t)n * op.ldb + gchunk * 16;
+  }
+  // every stored row r has r & 7 == grow & 7
+  const int st_off = grow * kRowBytes + ((gchunk ^ (grow & 7)) << 4);
+
+  // fragment read offsets: row (block base + lane % 32), chunk 2 s + lane / 32
+  int a_off[kTM], b_off[kTN];
+#pragma unroll
+  for (int mi = 0; mi < kTM; ++mi)
+    a_off[mi] = (wm * 128 + mi * 32 + (lane & 31)) * kRowBytes;
+#pragma unroll
+  for (int ni = 0; ni < kTN; ++ni)
+    b_off[ni] = (wn * 128 + ni * 32 + (lane & 31)) * kRowBytes;
+  int c_off[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) c_off[s] = ((2 * s + (lane >> 5)) ^ (lane & 7)) << 4;
+
+  u32x4 ra[8], rb[8];
+  auto gload = [&](int kt) {
+    const int64_t k = (int64_t)kt * kRowBytes;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ra[i] = *reinterpret_cast<const u32x4*>(aptr[i] + k);
+      rb[i] = *reinterpret_cast<const u32x4*>(bptr[i] + k);
+    }
+  };
+  auto sstore = [&](int stage) {
+    char* sa = lds + stage * kStageBytes;
+    char* sb = sa + kOperandBytes;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      *reinterpret_cast<u32x4*>(sa + st_off + i * 32 * kRowBytes) = ra[i];
+      *reinterpret_cast<u32x4*>(sb + st_off + i * 32 * kRowBytes) = rb[i];
+    }
+  };
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+    const char* sa = lds + cur * kStageBytes;
+    const char* sb = sa + kOperandBytes;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 fa[kTM], fb[kTN];
+#pragma unroll
+      for (int mi = 0; mi < kTM; ++mi)
+        fa[mi] = *reinterpret_cast<const u32x4*>(sa + a_off[mi] + c_off[s]);
+#pragma unroll
+      for (int ni = 0; ni < kTN; ++ni)
+        fb[ni] = *reinterpret_cast<const u32x4*>(sb + b_off[ni] + c_off[s]);
+#pragma unroll
+      for (int mi = 0; mi < kTM; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < kTN; ++ni)
+          mfma_step(acc[mi][ni], fa[mi], fb[ni], (const T*)nullptr);
+    }
+    if (kt + 1 < nk) sstore(cur ^ 1);
+    __syncthreads();
+  }
+}
+
+}  // namespace rz

@@ -1,0 +1,105 @@
+// rz_internal.h -- launchers shared by the kernel and API translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rz {
+
+// Kernel classes, in the order the timer reports them.
+enum KernelId {
+  K_MASK_COUNT = 0,
+  K_MASK_SCAN,
+  K_MASK_SCATTER,
+  K_FWD_LOGITS,      // bi_lmhead_gemm with the fused log-softmax epilogue
+  K_LSE_MERGE,       // bi_logsoftmax_gather merge
+  K_ROWS_FINALIZE,
+  K_RESP_SUMS,       // rz_loss: per-response reductions
+  K_LOSS_FINALIZE,   // rz_loss: groups, advantages, loss
+  K_COEF,
+  K_DIAG_PARTIAL,    // rz_diagnostics
+  K_DIAG_FINAL,
+  K_TRANSPOSE_W,
+  K_TRANSPOSE_H,
+  K_BWD_DZ,          // recompute GEMM with the dlogits epilogue
+  K_BWD_DH,          // dHidden GEMM
+  K_BWD_DW,          // dW GEMM
+  K_FILL,
+  K_TOK_HIST,
+  K_SCAN,
+  K_TOK_SCATTER,
+  K_BUCKET_SORT,
+  K_DW_FIX,
+  K_NUM_KERNELS
+};
+
+const char* kernel_name(int k);
+
+// Brackets launches with events when the timer is on.
+struct Timer {
+  static bool on();
+  static void before(int k, hipStream_t s);
+  static hipError_t after(int k, hipStream_t s);
+};
+
+// Device counts live in the workspace; a null pointer means "use cap".
+struct DevRows {
+  const int* count;
+  int64_t base;
+  int cap;
+};
+
+// ---- launchers (return the launch status) ----
+hipError_t launch_fwd_logits(int dt, const void* hidden, int64_t lda_bytes,
+                             const int* a_rows, DevRows rows,
+                             const void* lm_head, int H, int V,
+                             const int* row_tokens, float2* partials,
+                             int64_t ldp, float* ztgt, hipStream_t s);
+hipError_t launch_lse_merge(const float2* partials, int64_t ldp, int nt,
+                            DevRows rows, const float* ztgt,
+                            const int* row_tokens, int V, float* lse_out,
+                            float* logpi_out, const int* scatter_idx,
+                            float* logprobs_rows, int* err, hipStream_t s);
+hipError_t launch_mask_compact(const uint8_t* mask, int64_t n,
+                               const int* tokens, const int* cu, int B,
+                               int* blk, int* nvalid, int* bad_cu, int* idx,
+                               int* tokv, int* respv, int* err, hipStream_t s);
+hipError_t launch_rows_finalize(const uint8_t* mask, int64_t n, int H,
+                                float* logprobs, float* d_hidden,
+                                hipStream_t s);
+hipError_t launch_loss(const uint8_t* mask, const float* logprobs,
+                       const float* logmu, int64_t n, const int* cu,
+                       const float* rewards, const int* gid, int B,
+                       const int* bad_cu, int* T, double* S, int* gcnt,
+                       double* gsum, double* fcoef, float* adv, float* loss,
+                       int* err, hipStream_t s);
+hipError_t launch_coef(const int* nvalid, int64_t cap, const float* logpi_v,
+                       const float* logmu, const int* idx, const int* respv,
+                       const double* fcoef, float* coef, hipStream_t s);
+size_t diag_partials_bytes(int64_t n);
+hipError_t launch_diagnostics(const float* logpi, const float* logmu,
+                              const uint8_t* mask, int64_t n, void* partials,
+                              float* diag, hipStream_t s);
+hipError_t launch_transpose(int dt, int kid, const void* in, int64_t ld_in,
+                            const int* rowmap, DevRows rows, int rows_pad,
+                            int cols, void* out, int64_t ld_out,
+                            hipStream_t s);
+hipError_t launch_bwd_dz(int dt, const void* hidden, int64_t lda_bytes,
+                         const int* idx, DevRows rows, const void* lm_head,
+                         int H, int V, int Vpad, const float* lse_v,
+                         const float* coef, void* dz, int64_t ldz, void* dzT,
+                         int64_t ldzt, hipStream_t s);
+hipError_t launch_bwd_dh(int dt, const void* dz, int64_t ldz, DevRows rows,
+                         const void* WT, int64_t ldwt, int H, int V, int Vpad,
+                         const int* idx, const int* tokv, const float* coef,
+                         const void* lm_head, float* d_hidden, hipStream_t s);
+hipError_t launch_bwd_dw(int dt, const void* dzT, int64_t ldzt, DevRows krows,
+                         const void* hT, int64_t ldht, int H, int V,
+                         float* d_lm_head, int first, hipStream_t s);
+hipError_t launch_dw_fix(int dt, const int* nvalid, int64_t cap,
+                         const int* tokv, const int* idx, const float* coef,
+                         const void* hidden, int H, int V, int* counts,
+                         int* cursor, int* offsets, int* sorted,
+                         float* d_lm_head, hipStream_t s);
+
+}  // namespace rz

@@ -1,0 +1,1112 @@
+// rz_kernels.hip -- the HIP kernels of the REINFORCE Zero learner hot path.
+//
+// Sources (page title and section): the REINFORCE Zero project page
+// ("hujian.website"), section 02 "A minimal REINFORCE objective" (loss,
+// T_i, gradient through the numerator); the vLLM blog "Zero mismatch, simple
+// async RL" (zh translation), sections 2-4 (w = pi / mu unclipped, group-mean
+// advantage, D3, rollout-to-learner KL) and section 5 ("diff 0": bitwise
+// identical logprobs between rollout and trainer).
+#include <math.h>
+
+#include "rz_gemm.h"
+#include "rz_internal.h"
+
+#define RZ_GEMM_ATTR \
+  __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+
+namespace rz {
+
+namespace {
+
+constexpr float kNegInf = -__builtin_inff();
+
+struct MaxOp {
+  static __device__ __forceinline__ float apply(float a, float b) {
+    return fmaxf(a, b);
+  }
+};
+struct SumOp {
+  static __device__ __forceinline__ float apply(float a, float b) {
+    return a + b;
+  }
+};
+
+// Reduce 16 per-lane row values (the rows of one 32 x 32 block held by this
+// lane) across the 32 lanes of its half-wave: recursive halving over lane
+// bits 4, 3, 2, 1, then an exchange over bit 0.  Afterwards lane l holds the
+// reduction of row r = (l % 32) / 2 in v[0] (both lanes of a pair agree).
+// The tree is the same for every row (a + b == b + a), so a row's result
+// does not depend on its position in the tile.
+template <class Op>
+__device__ __forceinline__ void reduce_scatter16(float (&v)[16], int lane) {
+#pragma unroll
+  for (int step = 0; step < 4; ++step) {
+    const int mask = 16 >> step;
+    const int half = 8 >> step;
+    const bool upper = (lane & mask) != 0;
+#pragma unroll
+    for (int i = 0; i < half; ++i) {
+      const float send = upper ? v[i] : v[half + i];
+      const float keep = upper ? v[half + i] : v[i];
+      const float recv = __shfl_xor(send, mask, 64);
+      v[i] = Op::apply(keep, recv);
+    }
+  }
+  v[0] = Op::apply(v[0], __shfl_xor(v[0], 1, 64));
+}
+
+__device__ __forceinline__ RowCount to_rc(const DevRows& r) {
+  return RowCount{r.count, r.base, r.cap};
+}
+
+template <typename T>
+__device__ __forceinline__ float load_f(const T* p) {
+  return (float)(*p);
+}
+
+template <typename T>
+__device__ __forceinline__ T from_f(float x) {
+  return (T)x;
+}
+
+}  // namespace
+
+// ===================================================================
+// bi_lmhead_gemm (forward): z = h W^T on one 256 x 256 tile, with the
+// log-softmax partials and the sampled-token gather fused in the epilogue.
+// Per (row, vocab tile) it writes m = max_v z and s = sum_v exp(z - m) over
+// the tile's columns (pad columns >= V excluded), and z[a_t] when the row's
+// token falls in the tile.  Nothing of the logits leaves the chip.
+// ===================================================================
+struct FwdArgs {
+  GemmOperands op;
+  DevRows rows;
+  const int* row_tokens;  // token of list position p
+  int V, nk, mt, nt;
+  float2* partials;       // [nt][ldp] by list position
+  int64_t ldp;
+  float* ztgt;            // [positions]
+};
+
+template <typename T>
+__global__ RZ_GEMM_ATTR void k_fwd_logits(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  const RowCount rc = to_rc(a.rows);
+  const int M = rc.get();
+  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, a.mt, a.nt);
+  const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
+  if (m0 >= M) return;
+
+  f32x16 acc[kTM][kTN];
+  gemm_mainloop<T>(a.op, M, m0, n0, a.nk, acc, lds);
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+  float* red = reinterpret_cast<float*>(lds);  // [2][256]
+  float* rowm = red + 512;                     // [256]
+  int* rtok = reinterpret_cast<int*>(rowm + 256);
+  {
+    const int m = m0 + tid;
+    rtok[tid] = m < M ? a.row_tokens[rc.base + m] : -1;
+  }
+  const int colbase = n0 + wn * 128 + (lane & 31);
+  const bool tail = n0 + kBN > a.V;
+
+  // row of the tile that this lane owns after a 16-row reduce-scatter
+  const int rown = (lane & 31) >> 1;
+#pragma unroll
+  for (int mi = 0; mi < kTM; ++mi) {
+    float v[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int ni = 0; ni < kTN; ++ni) {
+        const float x = (!tail || colbase + ni * 32 < a.V) ? acc[mi][ni][r]
+                                                          : kNegInf;
+        mx = fmaxf(mx, x);
+      }
+      v[r] = mx;
+    }
+    reduce_scatter16<MaxOp>(v, lane);
+    if ((lane & 1) == 0) red[wn * 256 + acc_row(wm, mi, rown, lane)] = v[0];
+  }
+  __syncthreads();
+  rowm[tid] = fmaxf(red[tid], red[256 + tid]);
+  __syncthreads();
+
+#pragma unroll
+  for (int mi = 0; mi < kTM; ++mi) {
+    float v[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float mrow = rowm[acc_row(wm, mi, r, lane)];
+      float s = 0.f;
+#pragma unroll
+      for (int ni = 0; ni < kTN; ++ni) {
+        const float e = exp_approx(acc[mi][ni][r] - mrow);
+        s += (!tail || colbase + ni * 32 < a.V) ? e : 0.f;
+      }
+      v[r] = s;
+    }
+    reduce_scatter16<SumOp>(v, lane);
+    if ((lane & 1) == 0) red[wn * 256 + acc_row(wm, mi, rown, lane)] = v[0];
+  }
+  __syncthreads();
+  {
+    const int m = m0 + tid;
+    if (m < M) {
+      const float s = red[tid] + red[256 + tid];
+      a.partials[(int64_t)tc.tn * a.ldp + rc.base + m] =
+          make_float2(rowm[tid], s);
+    }
+  }
+  // sampled-token gather: the lane holding column a_t of row t stores z
+#pragma unroll
+  for (int mi = 0; mi < kTM; ++mi)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = acc_row(wm, mi, r, lane);
+      const int u = rtok[row] - colbase;
+      if (((u & 31) == 0) && ((unsigned)u < 128u)) {
+        const int ni = u >> 5;
+        const float z = ni == 0 ? acc[mi][0][r]
+                        : ni == 1 ? acc[mi][1][r]
+                        : ni == 2 ? acc[mi][2][r]
+                                  : acc[mi][3][r];
+        a.ztgt[rc.base + m0 + row] = z;
+      }
+    }
+}
+
+// ===================================================================
+// bi_logsoftmax_gather merge: per row, fold the vocab-tile partials in
+// ascending tile order, (m, s) <- (m', s e^(m - m') + s_j e^(m_j - m')),
+// then lse = m + log s and log pi = z[a_t] - lse.  The fold order depends
+// only on V, never on the number of rows.
+// ===================================================================
+__global__ __launch_bounds__(256) void k_lse_merge(
+    const float2* __restrict__ partials, int64_t ldp, int nt, DevRows rows,
+    const float* __restrict__ ztgt, const int* __restrict__ row_tokens, int V,
+    float* lse_out, float* logpi_out, const int* scatter_idx,
+    float* logprobs_rows, int* err) {
+  const RowCount rc = to_rc(rows);
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  if (p >= rc.get()) return;
+  const int64_t pos = rc.base + p;
+  float m = kNegInf, s = 0.f;
+  for (int t = 0; t < nt; ++t) {
+    const float2 ms = partials[(int64_t)t * ldp + pos];
+    const float mn = fmaxf(m, ms.x);
+    s = s * exp_approx(m - mn) + ms.y * exp_approx(ms.x - mn);
+    m = mn;
+  }
+  const float lse = m + logf(s);
+  const int tok = row_tokens[pos];
+  float lp;
+  if (tok >= 0 && tok < V) {
+    lp = ztgt[pos] - lse;
+  } else {
+    lp = __builtin_nanf("");
+    if (err) atomicOr(err, 1);
+  }
+  if (lse_out) lse_out[pos] = lse;
+  if (logpi_out) logpi_out[pos] = lp;
+  if (scatter_idx) logprobs_rows[scatter_idx[pos]] = lp;
+}
+
+// ===================================================================
+// Valid-row compaction (T_i counts valid action tokens): stable ascending
+// list of rows with mask = 1, their tokens and their responses.
+// ===================================================================
+constexpr int kCompactRows = 1024;
+
+__device__ __forceinline__ int block_excl_scan256(int x, int* sh, int* total) {
+  // Hillis-Steele over 256 threads (exact integer arithmetic)
+  const int tid = threadIdx.x;
+  sh[tid] = x;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int y = tid >= off ? sh[tid - off] : 0;
+    __syncthreads();
+    sh[tid] += y;
+    __syncthreads();
+  }
+  const int incl = sh[tid];
+  if (total) *total = sh[255];
+  __syncthreads();
+  return incl - x;
+}
+
+__global__ __launch_bounds__(256) void k_mask_count(const uint8_t* mask,
+                                                    int64_t n, int* blk) {
+  __shared__ int sh[256];
+  const int64_t base = (int64_t)blockIdx.x * kCompactRows + threadIdx.x * 4;
+  int c = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (base + i < n) c += mask[base + i] != 0;
+  int total;
+  block_excl_scan256(c, sh, &total);
+  if (threadIdx.x == 0) blk[blockIdx.x] = total;
+}
+
+__global__ __launch_bounds__(1024) void k_mask_scan(int* blk, int nblk,
+                                                    const int* cu, int B,
+                                                    int64_t n, int* nvalid,
+                                                    int* bad_cu, int* err) {
+  __shared__ int sh[1024];
+  const int tid = threadIdx.x;
+  const int per = (nblk + 1023) / 1024;
+  const int lo = tid * per, hi = min(nblk, lo + per);
+  int sum = 0;
+  for (int i = lo; i < hi; ++i) sum += blk[i];
+  sh[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int y = tid >= off ? sh[tid - off] : 0;
+    __syncthreads();
+    sh[tid] += y;
+    __syncthreads();
+  }
+  int run = sh[tid] - sum;
+  for (int i = lo; i < hi; ++i) {
+    const int c = blk[i];
+    blk[i] = run;
+    run += c;
+  }
+  if (tid == 1023) *nvalid = sh[1023];
+  // cu_rows must run 0 = cu[0] <= cu[1] <= ... <= cu[B] = n
+  __shared__ int bad;
+  if (tid == 0) bad = (cu[0] != 0) || ((int64_t)cu[B] != n);
+  __syncthreads();
+  for (int i = tid; i < B; i += 1024)
+    if (cu[i] > cu[i + 1]) bad = 1;
+  __syncthreads();
+  if (tid == 0) {
+    *bad_cu = bad;
+    if (bad && err) atomicOr(err, 4);
+  }
+}
+
+__device__ __forceinline__ int response_of(const int* cu, int B, int64_t row) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)cu[mid] <= row) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(256) void k_mask_scatter(
+    const uint8_t* mask, int64_t n, const int* blk_off, const int* tokens,
+    const int* cu, int B, int* idx, int* tokv, int* respv) {
+  __shared__ int sh[256];
+  const int64_t base = (int64_t)blockIdx.x * kCompactRows + threadIdx.x * 4;
+  uint8_t mk[4];
+  int c = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    mk[i] = (base + i < n) ? (mask[base + i] != 0) : 0;
+    c += mk[i];
+  }
+  int pos = blk_off[blockIdx.x] + block_excl_scan256(c, sh, nullptr);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (mk[i]) {
+      const int64_t row = base + i;
+      idx[pos] = (int)row;
+      tokv[pos] = tokens[row];
+      respv[pos] = response_of(cu, B, row);
+      ++pos;
+    }
+}
+
+// Masked rows: log pi reported as 0 and a zero gradient row.
+__global__ __launch_bounds__(256) void k_rows_finalize(const uint8_t* mask,
+                                                       int64_t n, int H,
+                                                       float* logprobs,
+                                                       float* d_hidden) {
+  const int64_t row = blockIdx.x;
+  if (row >= n || mask[row] != 0) return;
+  if (threadIdx.x == 0) logprobs[row] = 0.f;
+  float4* d = reinterpret_cast<float4*>(d_hidden + row * (int64_t)H);
+  for (int i = threadIdx.x; i < H / 4; i += 256) d[i] = make_float4(0, 0, 0, 0);
+}
+
+// ===================================================================
+// rz_loss.  Per response i (one workgroup): T_i = sum of mask, S_i = sum of
+// w_t = exp(log pi_t - log mu_t) over valid rows (no clipping), summed in
+// fp64 in a fixed order (per-thread strided partials, then a fixed tree).
+// ===================================================================
+__device__ __forceinline__ double block_sum_d(double x, double* sh) {
+  const int tid = threadIdx.x;
+  sh[tid] = x;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (tid < off) sh[tid] += sh[tid + off];
+    __syncthreads();
+  }
+  const double r = sh[0];
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ int block_sum_i(int x, int* sh) {
+  const int tid = threadIdx.x;
+  sh[tid] = x;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (tid < off) sh[tid] += sh[tid + off];
+    __syncthreads();
+  }
+  const int r = sh[0];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(256) void k_resp_sums(const uint8_t* mask,
+                                                   const float* logprobs,
+                                                   const float* logmu,
+                                                   int64_t n, const int* cu,
+                                                   int* T, double* S) {
+  __shared__ double shd[256];
+  __shared__ int shi[256];
+  const int i = blockIdx.x;
+  int64_t lo = cu[i], hi = cu[i + 1];
+  lo = lo < 0 ? 0 : (lo > n ? n : lo);
+  hi = hi < lo ? lo : (hi > n ? n : hi);
+  double s = 0.0;
+  int c = 0;
+  for (int64_t t = lo + threadIdx.x; t < hi; t += 256) {
+    if (mask[t]) {
+      s += (double)expf(logprobs[t] - logmu[t]);
+      ++c;
+    }
+  }
+  const double ss = block_sum_d(s, shd);
+  const int cc = block_sum_i(c, shi);
+  if (threadIdx.x == 0) {
+    S[i] = ss;
+    T[i] = cc;
+  }
+}
+
+// Groups, advantages A_i = r_i - mean of r over the group (ascending i),
+// the per-response factor A_i / (B T_i) and L = -(1/B) sum_i A_i S_i / T_i.
+__global__ __launch_bounds__(256) void k_loss_finalize(
+    const float* rewards, const int* gid, int B, const int* T, const double* S,
+    const int* bad_cu, int* gcnt, double* gsum, double* fcoef, float* adv,
+    float* loss, int* err) {
+  __shared__ double shd[256];
+  __shared__ int bad;
+  const int tid = threadIdx.x;
+  if (tid == 0) bad = *bad_cu;
+  __syncthreads();
+  for (int g = tid; g < B; g += 256) {
+    int c = 0;
+    double r = 0.0;
+    for (int j = 0; j < B; ++j)
+      if (gid[j] == g) {
+        ++c;
+        r += (double)rewards[j];
+      }
+    gcnt[g] = c;
+    gsum[g] = r;
+  }
+  for (int i = tid; i < B; i += 256)
+    if (gid[i] < 0 || gid[i] >= B) atomicOr(&bad, 2);
+  __syncthreads();
+  const double qnan = __builtin_nan("");
+  double part = 0.0;
+  for (int i = tid; i < B; i += 256) {
+    const int g = gid[i];
+    double A = qnan, f = qnan, term = qnan;
+    if (!bad) {
+      A = (double)rewards[i] - gsum[g] / (double)gcnt[g];
+      f = T[i] > 0 ? A / ((double)B * (double)T[i]) : 0.0;
+      term = T[i] > 0 ? A * S[i] / (double)T[i] : 0.0;
+    }
+    fcoef[i] = f;
+    if (adv) adv[i] = (float)A;
+    part += term;
+  }
+  const double tot = block_sum_d(part, shd);
+  if (tid == 0) {
+    *loss = (float)(-tot / (double)B);
+    if (err && (bad & 2)) atomicOr(err, 2);
+  }
+}
+
+// c_t = A_i w_t / (B T_i): minus the derivative of L by log pi_t (the
+// gradient flows through the numerator pi_theta only).
+__global__ __launch_bounds__(256) void k_coef(DevRows rows,
+                                              const float* logpi_v,
+                                              const float* logmu,
+                                              const int* idx,
+                                              const int* respv,
+                                              const double* fcoef,
+                                              float* coef) {
+  const RowCount rc = to_rc(rows);
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  if (p >= rc.get()) return;
+  const float w = expf(logpi_v[p] - logmu[idx[p]]);
+  coef[p] = (float)(fcoef[respv[p]] * (double)w);
+}
+
+// ===================================================================
+// rz_diagnostics: D3 = mean(expm1(d) - d), KL = mean(-d), d = log pi - log mu
+// over valid entries.  Fixed 2048-entry chunks, each reduced by one fixed
+// tree, then one fixed tree over the chunks: the order depends only on n.
+// ===================================================================
+constexpr int kDiagChunk = 2048;
+struct DiagPartial {
+  double d3, kl;
+  long long cnt;
+};
+
+__global__ __launch_bounds__(256) void k_diag_partial(const float* logpi,
+                                                      const float* logmu,
+                                                      const uint8_t* mask,
+                                                      int64_t n,
+                                                      DiagPartial* out) {
+  __shared__ double shd[256];
+  __shared__ int shi[256];
+  const int64_t base = (int64_t)blockIdx.x * kDiagChunk;
+  double d3 = 0.0, kl = 0.0;
+  int c = 0;
+#pragma unroll
+  for (int i = 0; i < kDiagChunk / 256; ++i) {
+    const int64_t t = base + threadIdx.x + 256 * i;
+    if (t < n && (!mask || mask[t])) {
+      const double d = (double)logpi[t] - (double)logmu[t];
+      d3 += expm1(d) - d;
+      kl += -d;
+      ++c;
+    }
+  }
+  d3 = block_sum_d(d3, shd);
+  kl = block_sum_d(kl, shd);
+  c = block_sum_i(c, shi);
+  if (threadIdx.x == 0) out[blockIdx.x] = DiagPartial{d3, kl, c};
+}
+
+__global__ __launch_bounds__(256) void k_diag_final(const DiagPartial* in,
+                                                    int nchunk, float* diag) {
+  __shared__ double shd[256];
+  __shared__ long long shl[256];
+  double d3 = 0.0, kl = 0.0;
+  long long c = 0;
+  for (int i = threadIdx.x; i < nchunk; i += 256) {
+    d3 += in[i].d3;
+    kl += in[i].kl;
+    c += in[i].cnt;
+  }
+  d3 = block_sum_d(d3, shd);
+  kl = block_sum_d(kl, shd);
+  shl[threadIdx.x] = c;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (threadIdx.x < off) shl[threadIdx.x] += shl[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const long long cnt = shl[0];
+    const float qnan = __builtin_nanf("");
+    diag[0] = cnt ? (float)(d3 / (double)cnt) : qnan;
+    diag[1] = cnt ? (float)(kl / (double)cnt) : qnan;
+  }
+}
+
+// ===================================================================
+// Transposes feeding the backward GEMMs their K-contiguous operands:
+// out[c, r] = in[row(r), c] for r < rows, 0 for rows <= r < rows_pad.
+// ===================================================================
+template <typename T>
+__global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ in,
+                                                   int64_t ld_in,
+                                                   const int* rowmap,
+                                                   DevRows rows, int rows_pad,
+                                                   int cols, T* __restrict__ out,
+                                                   int64_t ld_out) {
+  __shared__ T tile[64][65];
+  const RowCount rc = to_rc(rows);
+  const int R = rc.get();
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  if (r0 >= rows_pad) return;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int rr = ty; rr < 64; rr += 4) {
+    const int r = r0 + rr;
+    T val = from_f<T>(0.f);
+    if (r < R) {
+      const int64_t pr = rowmap ? (int64_t)rowmap[rc.base + r] : rc.base + r;
+      val = in[pr * ld_in + c0 + tx];
+    }
+    tile[rr][tx] = val;
+  }
+  __syncthreads();
+  for (int cc = ty; cc < 64; cc += 4)
+    if (c0 + cc < cols) out[(int64_t)(c0 + cc) * ld_out + r0 + tx] = tile[tx][cc];
+}
+
+// ===================================================================
+// Backward, part 1: recompute the logits tile (same engine, same K order
+// as the forward) and emit dlogits = c_t * softmax(z)_v for v < V, as the
+// token-major dz [C, Vpad] (A operand of dHidden) and the vocab-major
+// dz^T [Vpad, C] (A operand of dW).  The one-hot part -c_t [v == a_t] is
+// applied exactly in fp32 by the dHidden epilogue and the dW fix-up.
+// ===================================================================
+template <typename T>
+struct DzArgs {
+  GemmOperands op;
+  DevRows rows;
+  const float* lse;
+  const float* coef;
+  int V, Vpad, nk, mt, nt;
+  T* dz;
+  int64_t ldz;
+  T* dzT;
+  int64_t ldzt;
+};
+
+template <typename T>
+__global__ RZ_GEMM_ATTR void k_bwd_dz(DzArgs<T> a) {
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  const RowCount rc = to_rc(a.rows);
+  const int M = rc.get();
+  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, a.mt, a.nt);
+  const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
+  if (m0 >= M) return;
+
+  f32x16 acc[kTM][kTN];
+  gemm_mainloop<T>(a.op, M, m0, n0, a.nk, acc, lds);
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+  float* slse = reinterpret_cast<float*>(lds);
+  float* scoef = slse + 256;
+  {
+    const int m = m0 + tid;
+    slse[tid] = m < M ? a.lse[rc.base + m] : 0.f;
+    scoef[tid] = m < M ? a.coef[rc.base + m] : 0.f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int mi = 0; mi < kTM; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < kTN; ++ni) {
+      const int col = n0 + acc_col(wn, ni, lane);
+      if (col >= a.Vpad) continue;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        T q[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = r4 * 4 + j;
+          const int row = acc_row(wm, mi, r, lane);
+          float val = 0.f;
+          if (m0 + row < M && col < a.V)
+            val = scoef[row] * exp_approx(acc[mi][ni][r] - slse[row]);
+          q[j] = from_f<T>(val);
+          a.dz[(int64_t)(m0 + row) * a.ldz + col] = q[j];
+        }
+        const int row0 = acc_row(wm, mi, r4 * 4, lane);
+        T* dst = a.dzT + (int64_t)col * a.ldzt + m0 + row0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dst[j] = q[j];
+      }
+    }
+}
+
+// ===================================================================
+// Backward, part 2: dHidden = dz W (K = Vpad in fixed order) minus the
+// exact one-hot term c_t W[a_t, :], scattered to the rows' positions.
+// ===================================================================
+template <typename T>
+struct DhArgs {
+  GemmOperands op;
+  DevRows rows;
+  const int* idx;
+  const int* tokv;
+  const float* coef;
+  const T* W;
+  int H, V, nk, mt, nt;
+  float* dh;
+};
+
+template <typename T>
+__global__ RZ_GEMM_ATTR void k_bwd_dh(DhArgs<T> a) {
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  const RowCount rc = to_rc(a.rows);
+  const int M = rc.get();
+  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, a.mt, a.nt);
+  const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
+  if (m0 >= M) return;
+
+  f32x16 acc[kTM][kTN];
+  gemm_mainloop<T>(a.op, M, m0, n0, a.nk, acc, lds);
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+  int* sidx = reinterpret_cast<int*>(lds);
+  int* stok = sidx + 256;
+  float* scoef = reinterpret_cast<float*>(stok + 256);
+  {
+    const int m = m0 + tid;
+    const int64_t p = rc.base + m;
+    sidx[tid] = m < M ? a.idx[p] : 0;
+    int tk = m < M ? a.tokv[p] : 0;
+    stok[tid] = (tk >= 0 && tk < a.V) ? tk : 0;
+    scoef[tid] = m < M ? a.coef[p] : 0.f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int mi = 0; mi < kTM; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < kTN; ++ni) {
+      const int h = n0 + acc_col(wn, ni, lane);
+      if (h >= a.H) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = acc_row(wm, mi, r, lane);
+        if (m0 + row < M) {
+          const float w = load_f(a.W + (int64_t)stok[row] * a.H + h);
+          a.dh[(int64_t)sidx[row] * a.H + h] = acc[mi][ni][r] - scoef[row] * w;
+        }
+      }
+    }
+}
+
+// ===================================================================
+// Backward, part 3: dW (+)= dz^T h over this chunk's tokens (K in fixed
+// order); chunks are accumulated in order, the first one overwrites.
+// ===================================================================
+struct DwArgs {
+  GemmOperands op;
+  DevRows krows;
+  int V, H, kstage, mt, nt, first;
+  float* dw;
+};
+
+template <typename T>
+__global__ RZ_GEMM_ATTR void k_bwd_dw(DwArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  const int K = to_rc(a.krows).get();
+  const int nk = (K + a.kstage - 1) / a.kstage;
+  if (nk == 0 && !a.first) return;
+  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, a.mt, a.nt);
+  const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
+
+  f32x16 acc[kTM][kTN];
+  gemm_mainloop<T>(a.op, a.V, m0, n0, nk, acc, lds);
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+#pragma unroll
+  for (int mi = 0; mi < kTM; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < kTN; ++ni) {
+      const int h = n0 + acc_col(wn, ni, lane);
+      if (h >= a.H) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int v = m0 + acc_row(wm, mi, r, lane);
+        if (v < a.V) {
+          float* p = a.dw + (int64_t)v * a.H + h;
+          *p = a.first ? acc[mi][ni][r] : *p + acc[mi][ni][r];
+        }
+      }
+    }
+}
+
+// ===================================================================
+// dW one-hot fix-up: dW[v, :] -= sum over valid t with a_t = v, in
+// ascending t, of c_t h_t.  Tokens are bucketed by a counting sort whose
+// buckets are then ordered by position, so the sum order is fixed.
+// ===================================================================
+__global__ __launch_bounds__(256) void k_fill_i32(int* p, int64_t n, int v) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+__global__ __launch_bounds__(256) void k_tok_hist(DevRows rows,
+                                                  const int* tokv, int V,
+                                                  int* counts) {
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  if (p >= to_rc(rows).get()) return;
+  const int t = tokv[p];
+  if (t >= 0 && t < V) atomicAdd(&counts[t], 1);
+}
+
+__global__ __launch_bounds__(1024) void k_scan_excl(const int* counts, int n,
+                                                    int* offsets) {
+  __shared__ int sh[1024];
+  const int tid = threadIdx.x;
+  const int per = (n + 1023) / 1024;
+  const int lo = tid * per, hi = min(n, lo + per);
+  int sum = 0;
+  for (int i = lo; i < hi; ++i) sum += counts[i];
+  sh[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int y = tid >= off ? sh[tid - off] : 0;
+    __syncthreads();
+    sh[tid] += y;
+    __syncthreads();
+  }
+  int run = sh[tid] - sum;
+  for (int i = lo; i < hi; ++i) {
+    offsets[i] = run;
+    run += counts[i];
+  }
+  if (tid == 1023) offsets[n] = sh[1023];
+}
+
+__global__ __launch_bounds__(256) void k_tok_scatter(DevRows rows,
+                                                     const int* tokv, int V,
+                                                     const int* offsets,
+                                                     int* cursor,
+                                                     int* sorted) {
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  if (p >= to_rc(rows).get()) return;
+  const int t = tokv[p];
+  if (t < 0 || t >= V) return;
+  sorted[offsets[t] + atomicAdd(&cursor[t], 1)] = p;
+}
+
+__global__ __launch_bounds__(256) void k_bucket_sort(const int* offsets, int V,
+                                                     int* sorted) {
+  const int v = blockIdx.x * 256 + threadIdx.x;
+  if (v >= V) return;
+  const int lo = offsets[v], hi = offsets[v + 1];
+  for (int i = lo + 1; i < hi; ++i) {
+    const int x = sorted[i];
+    int j = i - 1;
+    while (j >= lo && sorted[j] > x) {
+      sorted[j + 1] = sorted[j];
+      --j;
+    }
+    sorted[j + 1] = x;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_dw_fix(const int* offsets,
+                                                const int* sorted,
+                                                const int* idx,
+                                                const float* coef,
+                                                const T* hidden, int H,
+                                                float* dw) {
+  const int v = blockIdx.x;
+  const int lo = offsets[v], hi = offsets[v + 1];
+  if (lo == hi) return;
+  for (int h = threadIdx.x; h < H; h += 256) {
+    float acc = 0.f;
+    for (int q = lo; q < hi; ++q) {
+      const int p = sorted[q];
+      acc += coef[p] * load_f(hidden + (int64_t)idx[p] * H + h);
+    }
+    dw[(int64_t)v * H + h] -= acc;
+  }
+}
+
+// ===================================================================
+// launchers
+// ===================================================================
+namespace {
+
+template <typename F>
+hipError_t timed(int kid, hipStream_t s, F&& launch) {
+  Timer::before(kid, s);
+  launch();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return Timer::after(kid, s);
+}
+
+inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+}  // namespace
+
+const char* kernel_name(int k) {
+  static const char* names[K_NUM_KERNELS] = {
+      "mask_count",   "mask_scan",    "mask_scatter", "fwd_logits_gemm",
+      "lse_merge",    "rows_finalize", "resp_sums",   "loss_finalize",
+      "coef",         "diag_partial", "diag_final",   "transpose_w",
+      "transpose_h",  "bwd_dz_gemm",  "bwd_dh_gemm",  "bwd_dw_gemm",
+      "fill",         "tok_hist",     "scan",         "tok_scatter",
+      "bucket_sort",  "dw_fix"};
+  return (k >= 0 && k < K_NUM_KERNELS) ? names[k] : "?";
+}
+
+hipError_t launch_fwd_logits(int dt, const void* hidden, int64_t lda_bytes,
+                             const int* a_rows, DevRows rows,
+                             const void* lm_head, int H, int V,
+                             const int* row_tokens, float2* partials,
+                             int64_t ldp, float* ztgt, hipStream_t s) {
+  FwdArgs a;
+  a.op = GemmOperands{(const char*)hidden, lda_bytes, a_rows, rows.base,
+                      (const char*)lm_head, (int64_t)H * (dt ? 2 : 4), V};
+  a.rows = rows;
+  a.row_tokens = row_tokens;
+  a.V = V;
+  a.nk = H / (dt ? Stage<bf16>::kK : Stage<float>::kK);
+  a.mt = cdiv(rows.cap, kBM);
+  a.nt = cdiv(V, kBN);
+  a.partials = partials;
+  a.ldp = ldp;
+  a.ztgt = ztgt;
+  const int nblk = a.mt * a.nt;
+  return timed(K_FWD_LOGITS, s, [&] {
+    if (dt) k_fwd_logits<bf16><<<nblk, kThreads, 0, s>>>(a);
+    else k_fwd_logits<float><<<nblk, kThreads, 0, s>>>(a);
+  });
+}
+
+hipError_t launch_lse_merge(const float2* partials, int64_t ldp, int nt,
+                            DevRows rows, const float* ztgt,
+                            const int* row_tokens, int V, float* lse_out,
+                            float* logpi_out, const int* scatter_idx,
+                            float* logprobs_rows, int* err, hipStream_t s) {
+  return timed(K_LSE_MERGE, s, [&] {
+    k_lse_merge<<<cdiv(rows.cap, 256), 256, 0, s>>>(
+        partials, ldp, nt, rows, ztgt, row_tokens, V, lse_out, logpi_out,
+        scatter_idx, logprobs_rows, err);
+  });
+}
+
+hipError_t launch_mask_compact(const uint8_t* mask, int64_t n,
+                               const int* tokens, const int* cu, int B,
+                               int* blk, int* nvalid, int* bad_cu, int* idx,
+                               int* tokv, int* respv, int* err,
+                               hipStream_t s) {
+  const int nblk = cdiv(n, kCompactRows);
+  hipError_t e = hipSuccess;
+  if (nblk > 0) {
+    e = timed(K_MASK_COUNT, s, [&] {
+      k_mask_count<<<nblk, 256, 0, s>>>(mask, n, blk);
+    });
+    if (e != hipSuccess) return e;
+  }
+  e = timed(K_MASK_SCAN, s, [&] {
+    k_mask_scan<<<1, 1024, 0, s>>>(blk, nblk, cu, B, n, nvalid, bad_cu, err);
+  });
+  if (e != hipSuccess || nblk == 0) return e;
+  return timed(K_MASK_SCATTER, s, [&] {
+    k_mask_scatter<<<nblk, 256, 0, s>>>(mask, n, blk, tokens, cu, B, idx,
+                                        tokv, respv);
+  });
+}
+
+hipError_t launch_rows_finalize(const uint8_t* mask, int64_t n, int H,
+                                float* logprobs, float* d_hidden,
+                                hipStream_t s) {
+  return timed(K_ROWS_FINALIZE, s, [&] {
+    k_rows_finalize<<<(unsigned)n, 256, 0, s>>>(mask, n, H, logprobs,
+                                                 d_hidden);
+  });
+}
+
+hipError_t launch_loss(const uint8_t* mask, const float* logprobs,
+                       const float* logmu, int64_t n, const int* cu,
+                       const float* rewards, const int* gid, int B,
+                       const int* bad_cu, int* T, double* S, int* gcnt,
+                       double* gsum, double* fcoef, float* adv, float* loss,
+                       int* err, hipStream_t s) {
+  hipError_t e = timed(K_RESP_SUMS, s, [&] {
+    k_resp_sums<<<B, 256, 0, s>>>(mask, logprobs, logmu, n, cu, T, S);
+  });
+  if (e != hipSuccess) return e;
+  return timed(K_LOSS_FINALIZE, s, [&] {
+    k_loss_finalize<<<1, 256, 0, s>>>(rewards, gid, B, T, S, bad_cu, gcnt,
+                                      gsum, fcoef, adv, loss, err);
+  });
+}
+
+hipError_t launch_coef(const int* nvalid, int64_t cap, const float* logpi_v,
+                       const float* logmu, const int* idx, const int* respv,
+                       const double* fcoef, float* coef, hipStream_t s) {
+  DevRows rows{nvalid, 0, (int)cap};
+  return timed(K_COEF, s, [&] {
+    k_coef<<<cdiv(cap, 256), 256, 0, s>>>(rows, logpi_v, logmu, idx, respv,
+                                          fcoef, coef);
+  });
+}
+
+size_t diag_partials_bytes(int64_t n) {
+  return (size_t)(n > 0 ? cdiv(n, kDiagChunk) : 1) * sizeof(DiagPartial);
+}
+
+hipError_t launch_diagnostics(const float* logpi, const float* logmu,
+                              const uint8_t* mask, int64_t n, void* partials,
+                              float* diag, hipStream_t s) {
+  const int nchunk = cdiv(n, kDiagChunk);
+  DiagPartial* p = reinterpret_cast<DiagPartial*>(partials);
+  hipError_t e = hipSuccess;
+  if (nchunk > 0) {
+    e = timed(K_DIAG_PARTIAL, s, [&] {
+      k_diag_partial<<<nchunk, 256, 0, s>>>(logpi, logmu, mask, n, p);
+    });
+    if (e != hipSuccess) return e;
+  }
+  return timed(K_DIAG_FINAL, s, [&] {
+    k_diag_final<<<1, 256, 0, s>>>(p, nchunk, diag);
+  });
+}
+
+hipError_t launch_transpose(int dt, int kid, const void* in, int64_t ld_in,
+                            const int* rowmap, DevRows rows, int rows_pad,
+                            int cols, void* out, int64_t ld_out,
+                            hipStream_t s) {
+  dim3 grid(cdiv(rows_pad, 64), cdiv(cols, 64));
+  return timed(kid, s, [&] {
+    if (dt)
+      k_transpose<bf16><<<grid, 256, 0, s>>>((const bf16*)in, ld_in, rowmap,
+                                             rows, rows_pad, cols, (bf16*)out,
+                                             ld_out);
+    else
+      k_transpose<float><<<grid, 256, 0, s>>>((const float*)in, ld_in,
+                                              rowmap, rows, rows_pad, cols,
+                                              (float*)out, ld_out);
+  });
+}
+
+template <typename T>
+static hipError_t launch_bwd_dz_t(const void* hidden, int64_t lda_bytes,
+                                  const int* idx, DevRows rows,
+                                  const void* lm_head, int H, int V, int Vpad,
+                                  const float* lse_v, const float* coef,
+                                  void* dz, int64_t ldz, void* dzT,
+                                  int64_t ldzt, hipStream_t s) {
+  DzArgs<T> a;
+  a.op = GemmOperands{(const char*)hidden, lda_bytes, idx, rows.base,
+                      (const char*)lm_head, (int64_t)H * (int64_t)sizeof(T), V};
+  a.rows = rows;
+  a.lse = lse_v;
+  a.coef = coef;
+  a.V = V;
+  a.Vpad = Vpad;
+  a.nk = H / Stage<T>::kK;
+  a.mt = cdiv(rows.cap, kBM);
+  a.nt = cdiv(V, kBN);
+  a.dz = (T*)dz;
+  a.ldz = ldz;
+  a.dzT = (T*)dzT;
+  a.ldzt = ldzt;
+  return timed(K_BWD_DZ, s, [&] {
+    k_bwd_dz<T><<<a.mt * a.nt, kThreads, 0, s>>>(a);
+  });
+}
+
+hipError_t launch_bwd_dz(int dt, const void* hidden, int64_t lda_bytes,
+                         const int* idx, DevRows rows, const void* lm_head,
+                         int H, int V, int Vpad, const float* lse_v,
+                         const float* coef, void* dz, int64_t ldz, void* dzT,
+                         int64_t ldzt, hipStream_t s) {
+  return dt ? launch_bwd_dz_t<bf16>(hidden, lda_bytes, idx, rows, lm_head, H,
+                                    V, Vpad, lse_v, coef, dz, ldz, dzT, ldzt, s)
+            : launch_bwd_dz_t<float>(hidden, lda_bytes, idx, rows, lm_head, H,
+                                     V, Vpad, lse_v, coef, dz, ldz, dzT, ldzt,
+                                     s);
+}
+
+template <typename T>
+static hipError_t launch_bwd_dh_t(const void* dz, int64_t ldz, DevRows rows,
+                                  const void* WT, int64_t ldwt, int H, int V,
+                                  int Vpad, const int* idx, const int* tokv,
+                                  const float* coef, const void* lm_head,
+                                  float* d_hidden, hipStream_t s) {
+  DhArgs<T> a;
+  a.op = GemmOperands{(const char*)dz, ldz * (int64_t)sizeof(T), nullptr,
+                      rows.base * 0, (const char*)WT,
+                      ldwt * (int64_t)sizeof(T), H};
+  a.rows = rows;
+  a.idx = idx;
+  a.tokv = tokv;
+  a.coef = coef;
+  a.W = (const T*)lm_head;
+  a.H = H;
+  a.V = V;
+  a.nk = Vpad / Stage<T>::kK;
+  a.mt = cdiv(rows.cap, kBM);
+  a.nt = cdiv(H, kBN);
+  a.dh = d_hidden;
+  return timed(K_BWD_DH, s, [&] {
+    k_bwd_dh<T><<<a.mt * a.nt, kThreads, 0, s>>>(a);
+  });
+}
+
+hipError_t launch_bwd_dh(int dt, const void* dz, int64_t ldz, DevRows rows,
+                         const void* WT, int64_t ldwt, int H, int V, int Vpad,
+                         const int* idx, const int* tokv, const float* coef,
+                         const void* lm_head, float* d_hidden, hipStream_t s) {
+  return dt ? launch_bwd_dh_t<bf16>(dz, ldz, rows, WT, ldwt, H, V, Vpad, idx,
+                                    tokv, coef, lm_head, d_hidden, s)
+            : launch_bwd_dh_t<float>(dz, ldz, rows, WT, ldwt, H, V, Vpad, idx,
+                                     tokv, coef, lm_head, d_hidden, s);
+}
+
+hipError_t launch_bwd_dw(int dt, const void* dzT, int64_t ldzt, DevRows krows,
+                         const void* hT, int64_t ldht, int H, int V,
+                         float* d_lm_head, int first, hipStream_t s) {
+  const int esz = dt ? 2 : 4;
+  DwArgs a;
+  a.op = GemmOperands{(const char*)dzT, ldzt * esz, nullptr, 0,
+                      (const char*)hT, ldht * esz, H};
+  a.krows = krows;
+  a.V = V;
+  a.H = H;
+  a.kstage = dt ? Stage<bf16>::kK : Stage<float>::kK;
+  a.mt = cdiv(V, kBM);
+  a.nt = cdiv(H, kBN);
+  a.first = first;
+  a.dw = d_lm_head;
+  return timed(K_BWD_DW, s, [&] {
+    if (dt) k_bwd_dw<bf16><<<a.mt * a.nt, kThreads, 0, s>>>(a);
+    else k_bwd_dw<float><<<a.mt * a.nt, kThreads, 0, s>>>(a);
+  });
+}
+
+hipError_t launch_dw_fix(int dt, const int* nvalid, int64_t cap,
+                         const int* tokv, const int* idx, const float* coef,
+                         const void* hidden, int H, int V, int* counts,
+                         int* cursor, int* offsets, int* sorted,
+                         float* d_lm_head, hipStream_t s) {
+  DevRows rows{nvalid, 0, (int)cap};
+  hipError_t e = timed(K_FILL, s, [&] {
+    k_fill_i32<<<cdiv(V, 256), 256, 0, s>>>(counts, V, 0);
+    k_fill_i32<<<cdiv(V, 256), 256, 0, s>>>(cursor, V, 0);
+  });
+  if (e != hipSuccess) return e;
+  if (cap > 0) {
+    e = timed(K_TOK_HIST, s, [&] {
+      k_tok_hist<<<cdiv(cap, 256), 256, 0, s>>>(rows, tokv, V, counts);
+    });
+    if (e != hipSuccess) return e;
+  }
+  e = timed(K_SCAN, s, [&] {
+    k_scan_excl<<<1, 1024, 0, s>>>(counts, V, offsets);
+  });
+  if (e != hipSuccess) return e;
+  if (cap > 0) {
+    e = timed(K_TOK_SCATTER, s, [&] {
+      k_tok_scatter<<<cdiv(cap, 256), 256, 0, s>>>(rows, tokv, V, offsets,
+                                                   cursor, sorted);
+    });
+    if (e != hipSuccess) return e;
+  }
+  e = timed(K_BUCKET_SORT, s, [&] {
+    k_bucket_sort<<<cdiv(V, 256), 256, 0, s>>>(offsets, V, sorted);
+  });
+  if (e != hipSuccess) return e;
+  return timed(K_DW_FIX, s, [&] {
+    if (dt)
+      k_dw_fix<bf16><<<V, 256, 0, s>>>(offsets, sorted, idx, coef,
+                                       (const bf16*)hidden, H, d_lm_head);
+    else
+      k_dw_fix<float><<<V, 256, 0, s>>>(offsets, sorted, idx, coef,
+                                        (const float*)hidden, H, d_lm_head);
+  });
+}
+
+}  // namespace rz

@@ -1,0 +1,204 @@
+"""Shared helpers of the GPU tests: host arrays -> device tensors, the
+tolerances, and the stand-in behaviour policy used to draw log mu.
+
+Tolerances (per element, |gpu - oracle| <= atol + rtol * |oracle|):
+* logprobs: bf16 rtol 2e-3 / atol 1e-4, fp32 rtol 1e-5 / atol 1e-5;
+* gradients (values near 1e-8, so a fixed atol would be vacuous):
+  atol = 1e-4 * max|oracle| (bf16) or 1e-5 * max|oracle| (fp32), plus the
+  normwise ||gpu - oracle|| / ||oracle|| <= rtol;
+* scalars: the loss, D3 and KL are sums of many terms whose inputs
+  (the logprobs) already carry the logprob tolerance, so their tolerance is
+  propagated from it: |dL| <= sum_i |A_i| / (B T_i) sum_t w_t tol_t,
+  |dKL| <= mean tol_t, |dD3| <= mean |w_t - 1| tol_t, plus rtol * |value|.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+from invariant_token_logprobs_amd import synth
+
+TOL = {"bf16": dict(rtol=2e-3, atol=1e-4, gscale=1e-4),
+       "f32": dict(rtol=1e-5, atol=1e-5, gscale=1e-5)}
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def device():
+    torch = torch_mod()
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test run without a GPU")
+    return torch.device("cuda:0")
+
+
+def say(*a):
+    print("[gpu-test]", *a, flush=True)
+
+
+def mat_to_dev(x: np.ndarray, dtype: str):
+    torch = torch_mod()
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(device())
+
+
+def vec_to_dev(x: np.ndarray):
+    torch = torch_mod()
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device())
+
+
+def batch_to_dev(b: synth.Batch, logmu: np.ndarray) -> dict:
+    return dict(hidden=mat_to_dev(b.hidden, b.dtype),
+                lm_head=mat_to_dev(b.lm_head, b.dtype),
+                tokens=vec_to_dev(b.tokens.astype(np.int32)),
+                logmu=vec_to_dev(logmu.astype(np.float32)),
+                mask=vec_to_dev(b.mask.astype(np.uint8)),
+                cu_rows=vec_to_dev(b.cu_rows.astype(np.int32)),
+                rewards=vec_to_dev(b.rewards.astype(np.float32)),
+                group_ids=vec_to_dev(b.group_ids.astype(np.int32)))
+
+
+def host(t) -> np.ndarray:
+    return t.detach().cpu().numpy()
+
+
+def behaviour_logprobs_torch(hidden, lm_head, tokens, rows_per_chunk=2048):
+    """Stand-in rollout policy for drawing log mu at sizes the oracle cannot
+    finish: a plain torch fp32 log-softmax on the GPU (an independent third
+    implementation, never our kernels).  Only used to place log mu near
+    log pi; nothing is compared against it."""
+    torch = torch_mod()
+    Wf = lm_head.float().t().contiguous()
+    out = torch.empty(hidden.shape[0], dtype=torch.float32, device=hidden.device)
+    for r0 in range(0, hidden.shape[0], rows_per_chunk):
+        r1 = min(hidden.shape[0], r0 + rows_per_chunk)
+        z = hidden[r0:r1].float() @ Wf
+        lp = torch.log_softmax(z, dim=1)
+        out[r0:r1] = lp.gather(1, tokens[r0:r1].long()[:, None])[:, 0]
+    del Wf
+    return out
+
+
+def assert_close(got, want, rtol, atol, what):
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    err = np.abs(got - want)
+    bound = atol + rtol * np.abs(want)
+    bad = ~(err <= bound)
+    if bad.any():
+        i = np.flatnonzero(bad.ravel())[:5]
+        raise AssertionError(
+            f"{what}: {bad.sum()} of {bad.size} outside tolerance; first "
+            f"{i.tolist()} got {got.ravel()[i].tolist()} want {want.ravel()[i].tolist()}")
+
+
+def assert_grad_close(got, want, dtype, what):
+    t = TOL[dtype]
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    scale = float(np.abs(want).max()) if want.size else 0.0
+    assert_close(got, want, t["rtol"], t["gscale"] * scale, what)
+    nw = np.linalg.norm(want)
+    if nw > 0:
+        rel = np.linalg.norm(got - want) / nw
+        assert rel <= t["rtol"], f"{what}: normwise relative error {rel:.3e}"
+
+
+def scalar_tols(ref: dict, mask, cu_rows, dtype):
+    """Propagated absolute tolerances of (loss, D3, KL) from the logprob
+    tolerance, evaluated on the oracle's values."""
+    t = TOL[dtype]
+    valid = np.asarray(mask) != 0
+    lp = ref["logpi"]
+    tol = t["atol"] + t["rtol"] * np.abs(lp)
+    w = ref["w"]
+    B = len(cu_rows) - 1
+    T = ref["T"]
+    A = ref["adv"]
+    loss_tol = 0.0
+    for i in range(B):
+        if T[i] == 0:
+            continue
+        rows = slice(cu_rows[i], cu_rows[i + 1])
+        loss_tol += abs(A[i]) / (B * T[i]) * float(np.sum((w[rows] * tol[rows])[valid[rows]]))
+    nv = max(1, int(valid.sum()))
+    kl_tol = float(np.sum(tol[valid])) / nv
+    d3_tol = float(np.sum((np.abs(w - 1) * tol)[valid])) / nv
+    return loss_tol, d3_tol, kl_tol
+
+
+def oracle_full(b: synth.Batch, logmu):
+    return O.reinforce_zero_fwd_bwd(
+        O.to_f64(b.hidden, b.dtype), O.to_f64(b.lm_head, b.dtype), b.tokens,
+        np.asarray(logmu, np.float64), b.mask, b.cu_rows, b.rewards,
+        b.group_ids)
+
+
+def logmu_from_oracle(b: synth.Batch):
+    logpi, _ = O.token_logprobs(O.to_f64(b.hidden, b.dtype),
+                                O.to_f64(b.lm_head, b.dtype), b.tokens)
+    return synth.make_logmu(logpi, b.sigma, b.noise_seed)
+
+
+def small_batch(*, N_resp=6, group_size=3, H=256, V=1000, lo=40, hi=200,
+                dtype="bf16", masked=0.3, seed=7, sigma=0.05,
+                rewards="uniform", shuffle_groups=True) -> synth.Batch:
+    """A seeded batch at oracle-friendly sizes with ragged tails."""
+    rng = np.random.default_rng(np.random.PCG64(seed))
+    lengths = rng.integers(lo, hi + 1, size=N_resp)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    N = int(cu[-1])
+    mask = np.ones(N, dtype=np.uint8)
+    if masked > 0:
+        mask[rng.random(N) < masked] = 0
+        mask[cu[:-1]] = 1
+    if rewards == "uniform":
+        r = rng.random(N_resp, dtype=np.float32)
+    else:
+        r = rng.integers(0, 2, size=N_resp).astype(np.float32)
+    gids = (np.arange(N_resp) // group_size).astype(np.int32)
+    if shuffle_groups:
+        gids = rng.permutation(gids).astype(np.int32)
+    hidden, tokens = synth.random_rows(N, H, V, dtype, seed + 1)
+    head = synth.random_lm_head(V, H, dtype, seed + 2)
+    return synth.Batch("small", dtype, H, V, hidden, head, tokens, mask, cu, r,
+                       gids, sigma, seed + 3)
+
+
+def run_fwd_bwd(d: dict, err=None, workspace=None):
+    import invariant_token_logprobs_amd as rz
+    out = rz.reinforce_zero_fwd_bwd(d["hidden"], d["lm_head"], d["tokens"],
+                                    d["logmu"], d["mask"], d["cu_rows"],
+                                    d["rewards"], d["group_ids"], err_flag=err,
+                                    workspace=workspace)
+    torch_mod().cuda.synchronize()
+    return out
+
+
+def compare_full(out: dict, ref: dict, b: synth.Batch, what: str):
+    """Element-by-element comparison of every fwd_bwd output."""
+    t = TOL[b.dtype]
+    valid = b.mask != 0
+    lp = host(out["logprobs"])
+    assert np.all(lp[~valid] == 0.0), f"{what}: masked logprobs not 0"
+    assert_close(lp[valid], ref["logpi"][valid], t["rtol"], t["atol"],
+                 f"{what} logprobs")
+    assert_close(host(out["adv"]), ref["adv"], 1e-6, 1e-7, f"{what} adv")
+    lt, dt3, dkl = scalar_tols(ref, b.mask, b.cu_rows, b.dtype)
+    diag = host(out["diag"])
+    assert_close([float(host(out["loss"])[0])], [ref["loss"]], t["rtol"], 1e-7 + lt,
+                 f"{what} loss")
+    assert_close([diag[0]], [ref["d3"]], t["rtol"], 1e-7 + dt3, f"{what} D3")
+    assert_close([diag[1]], [ref["kl"]], t["rtol"], 1e-7 + dkl, f"{what} KL")
+    dh = host(out["d_hidden"])
+    assert np.all(dh[~valid] == 0.0), f"{what}: masked d_hidden rows not 0"
+    assert_grad_close(dh, ref["d_hidden"], b.dtype, f"{what} d_hidden")
+    assert_grad_close(host(out["d_lm_head"]), ref["d_lm_head"], b.dtype,
+                      f"{what} d_lm_head")

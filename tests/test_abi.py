@@ -1,0 +1,141 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/rz.h declares, and rejects bad host-visible arguments with the
+documented status before making any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import invariant_token_logprobs_amd as rz
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rz.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+F32, BF16 = rz.RZ_DTYPE_F32, rz.RZ_DTYPE_BF16
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(rz.library_path()):
+        pytest.fail("librz.so is not built (python -m invariant_token_logprobs_amd.build)")
+    return rz.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rz_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("rz_token_logprobs", "rz_reinforce_zero_fwd_bwd", "rz_diagnostics",
+              "rz_workspace_bytes", "rz_status_string"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert sorted(rz.EXPORTS) == declared_functions()
+
+
+def test_status_strings(lib):
+    for code in (OK, INVALID, UNSUPPORTED, WORKSPACE, -4, 17):
+        assert lib.rz_status_string(code)
+
+
+# fake device pointers: never dereferenced, the calls must fail before HIP
+P = ctypes.c_void_p(0x1000)
+NULL = None
+
+
+def tlp(lib, hidden=P, head=P, tokens=P, n=4, H=64, V=10, dt=BF16, out=P,
+        ws=P, ws_bytes=0):
+    return lib.rz_token_logprobs(hidden, head, tokens, n, H, V, dt, out, NULL,
+                                 NULL, ws, ws_bytes, NULL)
+
+
+def test_token_logprobs_argument_errors(lib):
+    assert tlp(lib, n=-1) == INVALID
+    assert tlp(lib, H=0) == INVALID
+    assert tlp(lib, V=0) == INVALID
+    assert tlp(lib, H=96) == UNSUPPORTED          # not a multiple of 64
+    assert tlp(lib, dt=7) == UNSUPPORTED
+    assert tlp(lib, V=1 << 25) == UNSUPPORTED
+    assert tlp(lib, hidden=NULL) == INVALID
+    assert tlp(lib, tokens=NULL) == INVALID
+    assert tlp(lib, out=NULL) == INVALID
+    assert tlp(lib, ws=NULL, ws_bytes=1 << 30) == WORKSPACE
+    need = lib.rz_workspace_bytes(0, 4, 1, 64, 10, BF16)
+    assert need > 0
+    assert tlp(lib, ws_bytes=need - 1) == WORKSPACE
+    assert tlp(lib, ws=ctypes.c_void_p(0x1001), ws_bytes=need) == WORKSPACE
+    assert tlp(lib, n=0) == OK                    # empty call: no work at all
+
+
+def fb(lib, n=8, B=2, H=64, V=10, dt=F32, ws=P, ws_bytes=0, **null):
+    args = dict(hidden=P, head=P, tokens=P, logmu=P, mask=P, cu=P, rewards=P,
+                gid=P, logprobs=P, loss=P, dh=P, dw=P)
+    for k in null:
+        args[k] = NULL
+    a = args
+    return lib.rz_reinforce_zero_fwd_bwd(
+        a["hidden"], a["head"], a["tokens"], a["logmu"], a["mask"], a["cu"],
+        a["rewards"], a["gid"], n, B, H, V, dt, a["logprobs"], a["loss"],
+        a["dh"], a["dw"], NULL, NULL, NULL, ws, ws_bytes, NULL)
+
+
+def test_fwd_bwd_argument_errors(lib):
+    assert fb(lib, n=-5) == INVALID
+    assert fb(lib, B=0) == INVALID
+    assert fb(lib, H=-64) == INVALID
+    assert fb(lib, H=100) == UNSUPPORTED
+    assert fb(lib, dt=3) == UNSUPPORTED
+    for name in ("hidden", "head", "tokens", "logmu", "mask", "cu", "rewards",
+                 "gid", "logprobs", "loss", "dh", "dw"):
+        assert fb(lib, **{name: True}) == INVALID, name
+    need = lib.rz_workspace_bytes(1, 8, 2, 64, 10, F32)
+    assert need > 0
+    assert fb(lib, ws=NULL, ws_bytes=need) == WORKSPACE
+    assert fb(lib, ws_bytes=need - 1) == WORKSPACE
+
+
+def test_diagnostics_argument_errors(lib):
+    f = lib.rz_diagnostics
+    assert f(P, P, NULL, -1, P, P, 1 << 20, NULL) == INVALID
+    assert f(P, P, NULL, 10, NULL, P, 1 << 20, NULL) == INVALID
+    assert f(NULL, P, NULL, 10, P, P, 1 << 20, NULL) == INVALID
+    assert f(P, P, NULL, 10, P, NULL, 0, NULL) == WORKSPACE
+
+
+def test_workspace_sizes(lib):
+    ws = lib.rz_workspace_bytes
+    assert ws(0, -1, 1, 64, 10, F32) == 0
+    assert ws(0, 10, 1, 65, 10, F32) == 0
+    assert ws(1, 10, 0, 64, 10, F32) == 0
+    assert ws(0, 0, 1, 64, 10, F32) == 0
+    a = ws(1, 1000, 4, 256, 1024, F32)
+    b = ws(1, 2000, 4, 256, 1024, F32)
+    assert 0 < a < b
+    assert ws(1, 1000, 4, 256, 1024, BF16) < a
+    for op in (0, 1, 2):
+        assert ws(op, 12345, 7, 2560, 151936, BF16) % 256 == 0
+    # the headline tool-use workload fits comfortably in one MI355X's HBM
+    assert ws(1, 295658, 32, 2560, 151936, BF16) < 40 * 2 ** 30
+
+
+def test_timer_without_gpu_work(lib):
+    rz.timing_enable(True)
+    t = rz.timing_read()
+    assert "fwd_logits_gemm" in t and all(v == (0.0, 0) for v in t.values())
+    rz.timing_enable(False)
+
+
+def test_binding_rejects_host_tensors():
+    torch = pytest.importorskip("torch")
+    h = torch.zeros(4, 64)
+    with pytest.raises(rz.RzError):
+        rz.token_logprobs(h, torch.zeros(10, 64), torch.zeros(4, dtype=torch.int32))

@@ -1,0 +1,175 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Small cases compare every output element by element; they span several
+256 x 256 tiles with ragged row and vocab tails, masked rows, shuffled group
+ids, a response without valid tokens and the multi-chunk backward.  At the
+full workload sizes (in the launch configuration the benchmark times) the
+oracle computes sampled rows one by one, and the rest is checked through
+properties that hold at any size.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+from invariant_token_logprobs_amd import synth
+import invariant_token_logprobs_amd as rz
+
+from gpu_util import (TOL, assert_close, assert_grad_close, batch_to_dev,
+                      behaviour_logprobs_torch, compare_full, device, host,
+                      logmu_from_oracle, mat_to_dev, oracle_full, run_fwd_bwd,
+                      say, small_batch, torch_mod, vec_to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(b, what):
+    say(what, f"N={b.N} B={b.B} H={b.H} V={b.V} dtype={b.dtype} valid={b.n_valid}")
+    logmu = logmu_from_oracle(b)
+    out = run_fwd_bwd(batch_to_dev(b, logmu))
+    ref = oracle_full(b, logmu)
+    compare_full(out, ref, b, what)
+
+
+def test_tiny_workload_full_parity():
+    _case(synth.make_workload("tiny"), "tiny")
+
+
+def test_tiny_workload_masked_full_parity():
+    b = synth.make_workload("tiny")
+    rng = np.random.default_rng(np.random.PCG64(99))
+    b.mask[rng.random(b.N) < 0.35] = 0
+    b.mask[b.cu_rows[:-1]] = 1
+    b.mask[b.cu_rows[3]:b.cu_rows[4]] = 0          # response 3: T_i = 0
+    _case(b, "tiny-masked")
+
+
+def test_tiny_token_logprobs():
+    b = synth.make_workload("tiny")
+    say("tiny token_logprobs")
+    lp, lse = rz.token_logprobs(mat_to_dev(b.hidden, "f32"),
+                                mat_to_dev(b.lm_head, "f32"),
+                                vec_to_dev(b.tokens), want_lse=True)
+    ref_lp, ref_lse = O.token_logprobs(O.to_f64(b.hidden, "f32"),
+                                       O.to_f64(b.lm_head, "f32"), b.tokens)
+    t = TOL["f32"]
+    assert_close(host(lp), ref_lp, t["rtol"], t["atol"], "tiny logprobs")
+    assert_close(host(lse), ref_lse, t["rtol"], t["atol"], "tiny lse")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ragged_tiles_full_parity(dtype):
+    # 6 responses, ~700 rows (3 row tiles, ragged), V = 1000 (ragged vocab tile)
+    _case(small_batch(dtype=dtype, seed=11), f"ragged-{dtype}")
+
+
+def test_bernoulli_rewards_singleton_group():
+    b = small_batch(N_resp=5, group_size=2, dtype="bf16", seed=12,
+                    rewards="bernoulli", V=777, H=128)
+    b.group_ids[:] = np.array([0, 1, 0, 1, 2], dtype=np.int32)  # group 2 is a singleton
+    _case(b, "bernoulli-singleton")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_multi_chunk_backward(dtype):
+    # more valid rows than one backward chunk (32768): dW accumulates chunks
+    b = small_batch(N_resp=8, group_size=4, H=64, V=300, lo=4500, hi=6500,
+                    dtype=dtype, masked=0.2, seed=13)
+    assert b.n_valid > 32768
+    _case(b, f"multichunk-{dtype}")
+
+
+def test_qwen3_4b_truncated_full_parity():
+    """The headline tool-use shape at its full H = 2560, V = 151936, on the
+    first responses up to 1024 valid rows, every output compared."""
+    b = synth.make_workload("qwen3_4b_tool", max_valid=1024)
+    _case(b, "qwen3-4b-truncated")
+
+
+# ----------------------------------------------------------- full sizes
+def _full_size(name, n_sample_rows=512, n_sample_grad=16):
+    torch = torch_mod()
+    b = synth.make_workload(name)
+    say(f"{name}: N={b.N} B={b.B} valid={b.n_valid}")
+    d = batch_to_dev(b, np.zeros(b.N, np.float32))
+    mu_ref = behaviour_logprobs_torch(d["hidden"], d["lm_head"], d["tokens"])
+    logmu = synth.make_logmu(host(mu_ref), b.sigma, b.noise_seed)
+    del mu_ref
+    d["logmu"] = vec_to_dev(logmu)
+    out = run_fwd_bwd(d)
+    t = TOL[b.dtype]
+    valid = b.mask != 0
+    vidx = np.flatnonzero(valid)
+    rng = np.random.default_rng(np.random.PCG64(4242))
+    hidden64 = None
+
+    # sampled logprobs against the oracle, row by row
+    rows = np.sort(rng.choice(vidx, size=min(n_sample_rows, len(vidx)), replace=False))
+    W64 = O.to_f64(b.lm_head, b.dtype)
+    h64 = O.to_f64(b.hidden[rows], b.dtype)
+    ref_lp, ref_lse = O.token_logprobs(h64, W64, b.tokens[rows])
+    lp = host(out["logprobs"])
+    assert_close(lp[rows], ref_lp, t["rtol"], t["atol"], f"{name} sampled logprobs")
+    assert np.all(lp[~valid] == 0.0)
+
+    # advantages and T_i depend only on the inputs
+    A = O.group_mean_advantages(b.rewards, b.group_ids)
+    T = O.valid_token_counts(b.cu_rows, b.mask)
+    assert_close(host(out["adv"]), A, 1e-6, 1e-7, f"{name} adv")
+
+    # sampled d_hidden rows: c_t from the oracle's own log pi for that row
+    grows = rows[:n_sample_grad]
+    resp = np.searchsorted(b.cu_rows, grows, side="right") - 1
+    lp_g = ref_lp[:n_sample_grad]
+    w = np.exp(lp_g - logmu[grows].astype(np.float64))
+    c = A[resp] * w / (b.B * T[resp])
+    dh_ref, _ = O.backward(h64[:n_sample_grad], W64, b.tokens[grows],
+                           ref_lse[:n_sample_grad], c)
+    dh = host(out["d_hidden"][torch.from_numpy(grows).to(device())])
+    assert_grad_close(dh, dh_ref, b.dtype, f"{name} sampled d_hidden")
+    mrows = np.flatnonzero(~valid)[:64]
+    if mrows.size:
+        assert not host(out["d_hidden"][torch.from_numpy(mrows).to(device())]).any()
+
+    # properties of the whole-batch outputs
+    diag = host(out["diag"])
+    diag2 = host(rz.diagnostics(out["logprobs"], d["logmu"], d["mask"]))
+    assert np.array_equal(diag, diag2), "fwd_bwd diag != rz_diagnostics"
+    nv = len(vidx)
+    e_d3 = math.expm1(b.sigma ** 2 / 2)
+    assert abs(diag[0] - e_d3) < 6 * b.sigma ** 2 / math.sqrt(2 * nv) + 3 * t["rtol"] * e_d3, (diag, e_d3)
+    assert abs(diag[1]) < 6 * b.sigma / math.sqrt(nv), diag
+    # loss is the two-level mean of the weights of the returned logprobs
+    wgpu = np.exp(lp.astype(np.float64) - logmu.astype(np.float64))
+    L = 0.0
+    for i in range(b.B):
+        r = slice(b.cu_rows[i], b.cu_rows[i + 1])
+        if T[i]:
+            L += A[i] * float(np.sum(wgpu[r][valid[r]])) / T[i]
+    L = -L / b.B
+    scale = sum(abs(A[i]) for i in range(b.B)) / b.B * 2
+    assert abs(float(host(out["loss"])[0]) - L) <= 1e-5 * scale, (host(out["loss"]), L)
+    # dW: every column sums to zero (sum_v p = 1), and <dW, W> = <dH, h>
+    dW = out["d_lm_head"]
+    dH = out["d_hidden"]
+    colsum = dW.double().sum(dim=0)
+    colabs = dW.double().abs().sum(dim=0)
+    assert float((colsum.abs() / colabs.clamp_min(1e-30)).max()) < 1e-3
+    lhs = float((dW.double() * d["lm_head"].double()).sum())
+    rhs = float((dH.double() * d["hidden"].double()).sum())
+    assert abs(lhs - rhs) <= 2e-3 * max(abs(lhs), abs(rhs)) + 1e-9, (lhs, rhs)
+    del out, d
+    torch.cuda.empty_cache()
+
+
+def test_qwen3_4b_full_size_sampled():
+    _full_size("qwen3_4b_tool")
+
+
+def test_r1_distill_1p5b_full_size_sampled():
+    _full_size("r1_distill_1p5b", n_sample_rows=256, n_sample_grad=8)
+
+
+def test_qwen3_30b_full_size_sampled():
+    _full_size("qwen3_30b_a3b", n_sample_rows=256, n_sample_grad=8)
