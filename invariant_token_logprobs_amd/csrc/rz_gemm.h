@@ -13,8 +13,8 @@
 //    sub-tile = 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 (fp32 inputs use
 //    v_mfma_f32_32x32x2_f32, four per 16-byte fragment);
 //  * A and B stages are staged global -> registers -> LDS, double-buffered
-//    (2 x 64 KB), with a 16-byte-chunk XOR swizzle (chunk ^ (row & 7)) so
-//    both the stage stores and the fragment reads are bank-conflict free;
+//    (2 x 64 KB), with a 16-byte-chunk XOR swizzle (see swz) so both the
+//    stage stores and the fragment reads are bank-conflict free;
 //  * the next stage's global loads are issued before the current stage's
 //    MFMAs so their latency hides behind the matrix work;
 //  * workgroups are numbered XCD-aware: the dispatcher places workgroup i on
@@ -118,6 +118,8 @@ __device__ __forceinline__ int acc_col(int wn, int ni, int lane) {
   return wn * 128 + ni * 32 + (lane & 31);
 }
 
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
 struct GemmOperands {
   const char* A;        // A[m, :] row base is A + row(m) * lda
   int64_t lda;          // bytes
@@ -165,8 +167,12 @@ __device__ __forceinline__ void gemm_mainloop(const GemmOperands& op, int M,
     n = n < op.N ? n : op.N - 1;
     bptr[i] = op.B + (int64_t)n * op.ldb + gchunk * 16;
   }
-  // every stored row r has r & 7 == grow & 7
-  const int st_off = grow * kRowBytes + ((gchunk ^ (grow & 7)) << 4);
+  // 16-byte chunk c of LDS row r lives at chunk c ^ swz(r), swz(r) =
+  // (r & 7) ^ ((r >> 3) & 1): any 8 consecutive rows (a 128-byte bank line)
+  // and the same-parity rows of any 16 (a 256-byte line) get distinct
+  // chunks, so fragment reads and stage stores are bank-conflict free.
+  // Every row this thread stores has the same low 4 bits as grow.
+  const int st_off = grow * kRowBytes + ((gchunk ^ swz(grow)) << 4);
 
   // fragment read offsets: row (block base + lane % 32), chunk 2 s + lane / 32
   int a_off[kTM], b_off[kTN];
@@ -178,7 +184,8 @@ __device__ __forceinline__ void gemm_mainloop(const GemmOperands& op, int M,
     b_off[ni] = (wn * 128 + ni * 32 + (lane & 31)) * kRowBytes;
   int c_off[4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) c_off[s] = ((2 * s + (lane >> 5)) ^ (lane & 7)) << 4;
+  for (int s = 0; s < 4; ++s)
+    c_off[s] = ((2 * s + (lane >> 5)) ^ swz(lane & 31)) << 4;
 
   u32x4 ra[8], rb[8];
   auto gload = [&](int kt) {
@@ -198,32 +205,52 @@ __device__ __forceinline__ void gemm_mainloop(const GemmOperands& op, int M,
       *reinterpret_cast<u32x4*>(sb + st_off + i * 32 * kRowBytes) = rb[i];
     }
   };
-
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const char* sa = lds + cur * kStageBytes;
+  // fragments of two consecutive 16-byte K steps (register double buffer)
+  u32x4 fa[2][kTM], fb[2][kTN];
+  auto lread = [&](int buf, int stage, int s) {
+    const char* sa = lds + stage * kStageBytes;
     const char* sb = sa + kOperandBytes;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      u32x4 fa[kTM], fb[kTN];
+    for (int mi = 0; mi < kTM; ++mi)
+      fa[buf][mi] = *reinterpret_cast<const u32x4*>(sa + a_off[mi] + c_off[s]);
 #pragma unroll
-      for (int mi = 0; mi < kTM; ++mi)
-        fa[mi] = *reinterpret_cast<const u32x4*>(sa + a_off[mi] + c_off[s]);
+    for (int ni = 0; ni < kTN; ++ni)
+      fb[buf][ni] = *reinterpret_cast<const u32x4*>(sb + b_off[ni] + c_off[s]);
+  };
+  auto mma = [&](int buf) {
+#pragma unroll
+    for (int mi = 0; mi < kTM; ++mi)
 #pragma unroll
       for (int ni = 0; ni < kTN; ++ni)
-        fb[ni] = *reinterpret_cast<const u32x4*>(sb + b_off[ni] + c_off[s]);
-#pragma unroll
-      for (int mi = 0; mi < kTM; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < kTN; ++ni)
-          mfma_step(acc[mi][ni], fa[mi], fb[ni], (const T*)nullptr);
-    }
+        mfma_step(acc[mi][ni], fa[buf][mi], fb[buf][ni], (const T*)nullptr);
+  };
+
+  // Schedule per K stage kt (stage buffer cur = kt & 1):
+  //   step s: read the fragments of step s + 1, then issue step s's MFMAs;
+  //   after step 2's reads: store stage kt + 1 (fetched one stage earlier)
+  //   into the other buffer, then fetch stage kt + 2 into registers;
+  //   barrier; read step 0 of stage kt + 1.
+  // The other buffer was last read before the previous barrier, so the
+  // store cannot race with a slower wave.  The MFMA order per accumulator
+  // is k = 0, 1, 2, ... exactly as in a plain loop.
+  gload(0);
+  sstore(0);
+  if (nk > 1) gload(1);
+  __syncthreads();
+  lread(0, 0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    lread(1, cur, 1);
+    mma(0);
+    lread(0, cur, 2);
+    mma(1);
+    lread(1, cur, 3);
     if (kt + 1 < nk) sstore(cur ^ 1);
+    if (kt + 2 < nk) gload(kt + 2);
+    mma(0);
+    mma(1);
     __syncthreads();
+    if (kt + 1 < nk) lread(0, cur ^ 1, 0);
   }
 }
 

@@ -20,25 +20,26 @@ namespace {
 
 constexpr float kNegInf = -__builtin_inff();
 
-struct MaxOp {
-  static __device__ __forceinline__ float apply(float a, float b) {
-    return fmaxf(a, b);
-  }
-};
-struct SumOp {
-  static __device__ __forceinline__ float apply(float a, float b) {
-    return a + b;
-  }
-};
+// (max, sum-exp) pairs: (m1, s1) + (m2, s2) = (M, s1 e^(m1-M) + s2 e^(m2-M)),
+// M = max(m1, m2).  The two operands are first put in a canonical order
+// (larger max first, ties by larger sum), so the value is the same whichever
+// lane evaluates it and however the compiler contracts the arithmetic; the
+// tree of reduce_scatter16_ms then gives every row the same result wherever
+// it sits in the tile.  Masked columns carry m = kMaskedLogit (finite), never
+// -inf, so no (-inf) - (-inf) appears.
+constexpr float kMaskedLogit = -1.0e30f;
 
-// Reduce 16 per-lane row values (the rows of one 32 x 32 block held by this
-// lane) across the 32 lanes of its half-wave: recursive halving over lane
-// bits 4, 3, 2, 1, then an exchange over bit 0.  Afterwards lane l holds the
-// reduction of row r = (l % 32) / 2 in v[0] (both lanes of a pair agree).
-// The tree is the same for every row (a + b == b + a), so a row's result
-// does not depend on its position in the tile.
-template <class Op>
-__device__ __forceinline__ void reduce_scatter16(float (&v)[16], int lane) {
+__device__ __forceinline__ void ms_combine(float& m, float& s, float m2,
+                                           float s2) {
+  const bool sw = (m2 > m) || (m2 == m && s2 > s);
+  const float ma = sw ? m2 : m, sa = sw ? s2 : s;
+  const float mb = sw ? m : m2, sb = sw ? s : s2;
+  s = sa + sb * exp_approx(mb - ma);
+  m = ma;
+}
+
+__device__ __forceinline__ void reduce_scatter16_ms(float (&m)[16],
+                                                    float (&s)[16], int lane) {
 #pragma unroll
   for (int step = 0; step < 4; ++step) {
     const int mask = 16 >> step;
@@ -46,13 +47,16 @@ __device__ __forceinline__ void reduce_scatter16(float (&v)[16], int lane) {
     const bool upper = (lane & mask) != 0;
 #pragma unroll
     for (int i = 0; i < half; ++i) {
-      const float send = upper ? v[i] : v[half + i];
-      const float keep = upper ? v[half + i] : v[i];
-      const float recv = __shfl_xor(send, mask, 64);
-      v[i] = Op::apply(keep, recv);
+      const float sm = upper ? m[i] : m[half + i];
+      const float ss = upper ? s[i] : s[half + i];
+      float km = upper ? m[half + i] : m[i];
+      float ks = upper ? s[half + i] : s[i];
+      ms_combine(km, ks, __shfl_xor(sm, mask, 64), __shfl_xor(ss, mask, 64));
+      m[i] = km;
+      s[i] = ks;
     }
   }
-  v[0] = Op::apply(v[0], __shfl_xor(v[0], 1, 64));
+  ms_combine(m[0], s[0], __shfl_xor(m[0], 1, 64), __shfl_xor(s[0], 1, 64));
 }
 
 __device__ __forceinline__ RowCount to_rc(const DevRows& r) {
@@ -102,81 +106,67 @@ __global__ RZ_GEMM_ATTR void k_fwd_logits(FwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
-  float* red = reinterpret_cast<float*>(lds);  // [2][256]
-  float* rowm = red + 512;                     // [256]
-  int* rtok = reinterpret_cast<int*>(rowm + 256);
+  // LDS after the main loop: per-wave (m, s) of its 128 rows, tile tokens
+  float2* wstat = reinterpret_cast<float2*>(lds);            // [4][128]
+  int* rtok = reinterpret_cast<int*>(lds + 4 * 128 * 8);     // [256]
   {
     const int m = m0 + tid;
     rtok[tid] = m < M ? a.row_tokens[rc.base + m] : -1;
   }
+  __syncthreads();
   const int colbase = n0 + wn * 128 + (lane & 31);
-  const bool tail = n0 + kBN > a.V;
+  const int half = lane >> 5;
+  const int rown = (lane & 31) >> 1;  // row owned after the reduce-scatter
+  bool cvalid[kTN];
+#pragma unroll
+  for (int ni = 0; ni < kTN; ++ni) cvalid[ni] = colbase + ni * 32 < a.V;
 
-  // row of the tile that this lane owns after a 16-row reduce-scatter
-  const int rown = (lane & 31) >> 1;
+  // One pass over the accumulators: per row, this lane folds its 4 columns
+  // into (max, sum exp(z - max)) and stores z[a_t] if it holds column a_t;
+  // the 32 lanes of a half-wave then combine their pairs (128 columns).
 #pragma unroll
   for (int mi = 0; mi < kTM; ++mi) {
-    float v[16];
+    float vm[16], vs[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float mx = kNegInf;
+      float x[kTN];
+      float mx = kMaskedLogit;
 #pragma unroll
       for (int ni = 0; ni < kTN; ++ni) {
-        const float x = (!tail || colbase + ni * 32 < a.V) ? acc[mi][ni][r]
-                                                          : kNegInf;
-        mx = fmaxf(mx, x);
+        x[ni] = cvalid[ni] ? acc[mi][ni][r] : kMaskedLogit;
+        mx = fmaxf(mx, x[ni]);
       }
-      v[r] = mx;
-    }
-    reduce_scatter16<MaxOp>(v, lane);
-    if ((lane & 1) == 0) red[wn * 256 + acc_row(wm, mi, rown, lane)] = v[0];
-  }
-  __syncthreads();
-  rowm[tid] = fmaxf(red[tid], red[256 + tid]);
-  __syncthreads();
-
+      float sm = 0.f;
 #pragma unroll
-  for (int mi = 0; mi < kTM; ++mi) {
-    float v[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float mrow = rowm[acc_row(wm, mi, r, lane)];
-      float s = 0.f;
-#pragma unroll
-      for (int ni = 0; ni < kTN; ++ni) {
-        const float e = exp_approx(acc[mi][ni][r] - mrow);
-        s += (!tail || colbase + ni * 32 < a.V) ? e : 0.f;
-      }
-      v[r] = s;
-    }
-    reduce_scatter16<SumOp>(v, lane);
-    if ((lane & 1) == 0) red[wn * 256 + acc_row(wm, mi, rown, lane)] = v[0];
-  }
-  __syncthreads();
-  {
-    const int m = m0 + tid;
-    if (m < M) {
-      const float s = red[tid] + red[256 + tid];
-      a.partials[(int64_t)tc.tn * a.ldp + rc.base + m] =
-          make_float2(rowm[tid], s);
-    }
-  }
-  // sampled-token gather: the lane holding column a_t of row t stores z
-#pragma unroll
-  for (int mi = 0; mi < kTM; ++mi)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
+      for (int ni = 0; ni < kTN; ++ni) sm += exp_approx(x[ni] - mx);
+      vm[r] = mx;
+      vs[r] = sm;
       const int row = acc_row(wm, mi, r, lane);
       const int u = rtok[row] - colbase;
       if (((u & 31) == 0) && ((unsigned)u < 128u)) {
         const int ni = u >> 5;
-        const float z = ni == 0 ? acc[mi][0][r]
-                        : ni == 1 ? acc[mi][1][r]
-                        : ni == 2 ? acc[mi][2][r]
-                                  : acc[mi][3][r];
-        a.ztgt[rc.base + m0 + row] = z;
+        a.ztgt[rc.base + m0 + row] =
+            ni == 0 ? x[0] : ni == 1 ? x[1] : ni == 2 ? x[2] : x[3];
       }
     }
+    reduce_scatter16_ms(vm, vs, lane);
+    if ((lane & 1) == 0) {
+      const int lrow = mi * 32 + 8 * (rown >> 2) + 4 * half + (rown & 3);
+      wstat[wid * 128 + lrow] = make_float2(vm[0], vs[0]);
+    }
+  }
+  __syncthreads();
+  // merge the two column halves of each row in a fixed order
+  {
+    const int m = m0 + tid;
+    if (m < M) {
+      const int w0 = (tid >> 7) * 2, lr = tid & 127;
+      const float2 p0 = wstat[w0 * 128 + lr], p1 = wstat[(w0 + 1) * 128 + lr];
+      float mm = p0.x, ss = p0.y;
+      ms_combine(mm, ss, p1.x, p1.y);
+      a.partials[(int64_t)tc.tn * a.ldp + rc.base + m] = make_float2(mm, ss);
+    }
+  }
 }
 
 // ===================================================================
@@ -706,15 +696,20 @@ __global__ RZ_GEMM_ATTR void k_bwd_dw(DwArgs a) {
   for (int mi = 0; mi < kTM; ++mi)
 #pragma unroll
     for (int ni = 0; ni < kTN; ++ni) {
+      // one 32 x 32 block at a time keeps the in-flight loads bounded
+      __builtin_amdgcn_sched_barrier(0);
       const int h = n0 + acc_col(wn, ni, lane);
       if (h >= a.H) continue;
+      float prev[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int v = m0 + acc_row(wm, mi, r, lane);
-        if (v < a.V) {
-          float* p = a.dw + (int64_t)v * a.H + h;
-          *p = a.first ? acc[mi][ni][r] : *p + acc[mi][ni][r];
-        }
+        prev[r] = (!a.first && v < a.V) ? a.dw[(int64_t)v * a.H + h] : 0.f;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int v = m0 + acc_row(wm, mi, r, lane);
+        if (v < a.V) a.dw[(int64_t)v * a.H + h] = prev[r] + acc[mi][ni][r];
       }
     }
 }
