@@ -12,11 +12,13 @@
 //  * 256 threads = 4 wave64s in a 2 x 2 grid, each wave owning a 128 x 128
 //    sub-tile = 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 (fp32 inputs use
 //    v_mfma_f32_32x32x2_f32, four per 16-byte fragment);
-//  * A and B stages are staged global -> registers -> LDS, double-buffered
-//    (2 x 64 KB), with a 16-byte-chunk XOR swizzle (see swz) so both the
-//    stage stores and the fragment reads are bank-conflict free;
-//  * the next stage's global loads are issued before the current stage's
-//    MFMAs so their latency hides behind the matrix work;
+//  * A and B stages go straight from global memory into LDS
+//    (global_load_lds_dwordx4, no register round trip), double-buffered
+//    (2 x 64 KB), with a 16-byte-chunk XOR swizzle (see swz) so the fragment
+//    reads are bank-conflict free;
+//  * stage kt + 1 is in flight while stage kt feeds the MFMAs, and the
+//    fragments of the next 16-byte K step are read while the current
+//    step's MFMAs run;
 //  * workgroups are numbered XCD-aware: the dispatcher places workgroup i on
 //    XCD i % 8, so logical tiles are renumbered to give each XCD a
 //    contiguous range, and within it tiles are walked in groups of tile-rows
@@ -151,29 +153,6 @@ __device__ __forceinline__ void gemm_mainloop(const GemmOperands& op, int M,
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
   if (nk <= 0) return;
 
-  // global -> register assignment: chunk (tid & 7) of rows (tid >> 3) + 32 i
-  const int gchunk = tid & 7;
-  const int grow = tid >> 3;
-  const char* aptr[8];
-  const char* bptr[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    int m = m0 + grow + 32 * i;
-    m = m < M ? m : M - 1;
-    const int64_t prow = op.a_rows ? (int64_t)op.a_rows[op.a_base + m]
-                                   : op.a_base + m;
-    aptr[i] = op.A + prow * op.lda + gchunk * 16;
-    int n = n0 + grow + 32 * i;
-    n = n < op.N ? n : op.N - 1;
-    bptr[i] = op.B + (int64_t)n * op.ldb + gchunk * 16;
-  }
-  // 16-byte chunk c of LDS row r lives at chunk c ^ swz(r), swz(r) =
-  // (r & 7) ^ ((r >> 3) & 1): any 8 consecutive rows (a 128-byte bank line)
-  // and the same-parity rows of any 16 (a 256-byte line) get distinct
-  // chunks, so fragment reads and stage stores are bank-conflict free.
-  // Every row this thread stores has the same low 4 bits as grow.
-  const int st_off = grow * kRowBytes + ((gchunk ^ swz(grow)) << 4);
-
   // fragment read offsets: row (block base + lane % 32), chunk 2 s + lane / 32
   int a_off[kTM], b_off[kTN];
 #pragma unroll
@@ -182,27 +161,49 @@ __device__ __forceinline__ void gemm_mainloop(const GemmOperands& op, int M,
 #pragma unroll
   for (int ni = 0; ni < kTN; ++ni)
     b_off[ni] = (wn * 128 + ni * 32 + (lane & 31)) * kRowBytes;
+  // 16-byte chunk c of LDS row r lives at chunk c ^ swz(r), swz(r) =
+  // (r & 7) ^ ((r >> 3) & 1): any 8 consecutive rows (a 128-byte bank line)
+  // and the same-parity rows of any 16 (a 256-byte line) get distinct
+  // chunks, so the fragment reads are bank-conflict free.
   int c_off[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s)
     c_off[s] = ((2 * s + (lane >> 5)) ^ swz(lane & 31)) << 4;
 
-  u32x4 ra[8], rb[8];
-  auto gload = [&](int kt) {
-    const int64_t k = (int64_t)kt * kRowBytes;
+  // Global -> LDS without a register round trip: global_load_lds_dwordx4
+  // writes lane l's 16 bytes at (LDS base + 16 l).  Wave w fills rows
+  // [64 w, 64 w + 64) of each operand, 8 rows per instruction; lane l lands
+  // in row l / 8 at physical chunk l % 8, so it fetches the logical chunk
+  // (l % 8) ^ swz(row) that the swizzle places there.
+  typedef __attribute__((address_space(3))) void* lds_ptr_t;
+  const int wu = __builtin_amdgcn_readfirstlane(wid);
+  const char* ga[8];
+  const char* gb[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      ra[i] = *reinterpret_cast<const u32x4*>(aptr[i] + k);
-      rb[i] = *reinterpret_cast<const u32x4*>(bptr[i] + k);
-    }
-  };
-  auto sstore = [&](int stage) {
-    char* sa = lds + stage * kStageBytes;
+  for (int i = 0; i < 8; ++i) {
+    const int r = wu * 64 + 8 * i + (lane >> 3);
+    const int c = (lane & 7) ^ swz(r);
+    int m = m0 + r;
+    m = m < M ? m : M - 1;
+    const int64_t prow = op.a_rows ? (int64_t)op.a_rows[op.a_base + m]
+                                   : op.a_base + m;
+    ga[i] = op.A + prow * op.lda + c * 16;
+    int n = n0 + r;
+    n = n < op.N ? n : op.N - 1;
+    gb[i] = op.B + (int64_t)n * op.ldb + c * 16;
+  }
+  auto dload = [&](int kt, int stage) {
+    const int64_t k = (int64_t)kt * kRowBytes;
+    char* sa = lds + stage * kStageBytes + wu * 64 * kRowBytes;
     char* sb = sa + kOperandBytes;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      *reinterpret_cast<u32x4*>(sa + st_off + i * 32 * kRowBytes) = ra[i];
-      *reinterpret_cast<u32x4*>(sb + st_off + i * 32 * kRowBytes) = rb[i];
+      __builtin_amdgcn_global_load_lds(ga[i] + k,
+                                       (lds_ptr_t)(sa + i * 8 * kRowBytes), 16,
+                                       0, 0);
+      __builtin_amdgcn_global_load_lds(gb[i] + k,
+                                       (lds_ptr_t)(sb + i * 8 * kRowBytes), 16,
+                                       0, 0);
     }
   };
   // fragments of two consecutive 16-byte K steps (register double buffer)
@@ -225,18 +226,17 @@ __device__ __forceinline__ void gemm_mainloop(const GemmOperands& op, int M,
         mfma_step(acc[mi][ni], fa[buf][mi], fb[buf][ni], (const T*)nullptr);
   };
 
-  // Schedule per K stage kt (stage buffer cur = kt & 1):
-  //   step s: read the fragments of step s + 1, then issue step s's MFMAs;
-  //   after step 2's reads: store stage kt + 1 (fetched one stage earlier)
-  //   into the other buffer, then fetch stage kt + 2 into registers;
-  //   barrier; read step 0 of stage kt + 1.
-  // The other buffer was last read before the previous barrier, so the
-  // store cannot race with a slower wave.  The MFMA order per accumulator
-  // is k = 0, 1, 2, ... exactly as in a plain loop.
-  gload(0);
-  sstore(0);
-  if (nk > 1) gload(1);
+  // Schedule: stage kt lives in LDS buffer kt & 1.  While stage kt is
+  // consumed (four 16-byte K steps, the fragments of step s + 1 read while
+  // step s's MFMAs run), stage kt + 1 is landing in the other buffer.  At
+  // the end of the stage every wave waits for its own loads (vmcnt(0)),
+  // the barrier makes stage kt + 1 complete and buffer kt & 1 free, and
+  // stage kt + 2 is requested into it.  The MFMA order per accumulator is
+  // k = 0, 1, 2, ... exactly as in a plain loop.
+  dload(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  if (nk > 1) dload(1, 1);
   lread(0, 0, 0);
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
@@ -245,11 +245,11 @@ __device__ __forceinline__ void gemm_mainloop(const GemmOperands& op, int M,
     lread(0, cur, 2);
     mma(1);
     lread(1, cur, 3);
-    if (kt + 1 < nk) sstore(cur ^ 1);
-    if (kt + 2 < nk) gload(kt + 2);
     mma(0);
     mma(1);
+    if (kt + 1 < nk) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    if (kt + 2 < nk) dload(kt + 2, cur);
     if (kt + 1 < nk) lread(0, cur ^ 1, 0);
   }
 }

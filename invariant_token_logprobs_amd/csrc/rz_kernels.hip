@@ -97,9 +97,12 @@ __global__ RZ_GEMM_ATTR void k_fwd_logits(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
   const RowCount rc = to_rc(a.rows);
   const int M = rc.get();
-  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, a.mt, a.nt);
+  // Only the tiles of the M rows present are numbered (M may be a device
+  // count below the launch bound), so the active tiles spread over all XCDs.
+  const int mt = (M + kBM - 1) / kBM;
+  if ((int)blockIdx.x >= mt * a.nt) return;
+  const TileCoord tc = map_tile(blockIdx.x, mt * a.nt, mt, a.nt);
   const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
-  if (m0 >= M) return;
 
   f32x16 acc[kTM][kTN];
   gemm_mainloop<T>(a.op, M, m0, n0, a.nk, acc, lds);
@@ -564,9 +567,12 @@ __global__ RZ_GEMM_ATTR void k_bwd_dz(DzArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
   const RowCount rc = to_rc(a.rows);
   const int M = rc.get();
-  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, a.mt, a.nt);
+  // Only the tiles of the M rows present are numbered (M may be a device
+  // count below the launch bound), so the active tiles spread over all XCDs.
+  const int mt = (M + kBM - 1) / kBM;
+  if ((int)blockIdx.x >= mt * a.nt) return;
+  const TileCoord tc = map_tile(blockIdx.x, mt * a.nt, mt, a.nt);
   const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
-  if (m0 >= M) return;
 
   f32x16 acc[kTM][kTN];
   gemm_mainloop<T>(a.op, M, m0, n0, a.nk, acc, lds);
@@ -629,9 +635,12 @@ __global__ RZ_GEMM_ATTR void k_bwd_dh(DhArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
   const RowCount rc = to_rc(a.rows);
   const int M = rc.get();
-  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, a.mt, a.nt);
+  // Only the tiles of the M rows present are numbered (M may be a device
+  // count below the launch bound), so the active tiles spread over all XCDs.
+  const int mt = (M + kBM - 1) / kBM;
+  if ((int)blockIdx.x >= mt * a.nt) return;
+  const TileCoord tc = map_tile(blockIdx.x, mt * a.nt, mt, a.nt);
   const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
-  if (m0 >= M) return;
 
   f32x16 acc[kTM][kTN];
   gemm_mainloop<T>(a.op, M, m0, n0, a.nk, acc, lds);
