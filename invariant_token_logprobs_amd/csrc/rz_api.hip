@@ -75,6 +75,7 @@ struct FbWs {
   int* gcnt;
   double* gsum;
   double* fcoef;
+  double* Ad;
   float* diag_tmp;
   void* diag_part;
   void* WT;
@@ -109,6 +110,7 @@ size_t carve_fb(Carver& c, int64_t n, int32_t B, int32_t H, int32_t V,
   t.gcnt = c.take<int>(sizeof(int) * (size_t)B);
   t.gsum = c.take<double>(sizeof(double) * (size_t)B);
   t.fcoef = c.take<double>(sizeof(double) * (size_t)B);
+  t.Ad = c.take<double>(sizeof(double) * (size_t)B);
   t.diag_tmp = c.take<float>(2 * sizeof(float));
   t.diag_part = c.take<char>(diag_partials_bytes(n));
   t.WT = c.take<char>(es * (size_t)H * (size_t)Vpad);
@@ -240,7 +242,7 @@ rz_status rz_token_logprobs(const void* hidden, const void* lm_head,
   DevRows rows{nullptr, 0, (int)n_rows};
   RZ_TRY(launch_fwd_logits(dt, hidden, (int64_t)H * esize(dt), nullptr, rows,
                            lm_head, H, V, tokens, w.partials, n_rows, w.ztgt,
-                           s));
+                           nullptr, 0, 0, s));
   RZ_TRY(launch_lse_merge(w.partials, n_rows, nt, rows, w.ztgt, tokens, V,
                           lse, logprobs, nullptr, nullptr, err_flag, s));
   return RZ_OK;
@@ -298,42 +300,47 @@ rz_status rz_reinforce_zero_fwd_bwd(
   RZ_TRY(launch_mask_compact(mask, N, tokens, cu_rows, n_resp, w.blk,
                              w.nvalid, w.bad_cu, w.idx, w.tokv, w.respv,
                              err_flag, s));
-  // a1-a3: logits GEMM with the log-softmax epilogue, ordered merge
-  DevRows vrows{w.nvalid, 0, (int)N};
-  if (N > 0) {
-    RZ_TRY(launch_fwd_logits(dt, hidden, lda, w.idx, vrows, lm_head, H, V,
-                             w.tokv, w.partials, N, w.ztgt, s));
-    RZ_TRY(launch_lse_merge(w.partials, N, nt, vrows, w.ztgt, w.tokv, V,
-                            w.lse_v, w.logpi_v, w.idx, logprobs, err_flag, s));
-    RZ_TRY(launch_rows_finalize(mask, N, H, logprobs, d_hidden, s));
-  }
-  // a4-a5: weights, T_i, advantages, loss, per-token coefficients
-  RZ_TRY(launch_loss(mask, logprobs, logmu, N, cu_rows, rewards, group_ids,
-                     n_resp, w.bad_cu, w.T, w.S, w.gcnt, w.gsum, w.fcoef, adv,
-                     loss, err_flag, s));
-  if (N > 0)
-    RZ_TRY(launch_coef(w.nvalid, N, w.logpi_v, logmu, w.idx, w.respv,
-                       w.fcoef, w.coef, s));
-  // a6: diagnostics over this call's outputs (same kernels as rz_diagnostics)
-  RZ_TRY(launch_diagnostics(logprobs, logmu, mask, N, w.diag_part,
-                            diag ? diag : w.diag_tmp, s));
-  // a7-a9: backward in token chunks of C valid rows
+  // a5 (inputs only): T_i, group means, A_i and the factors A_i / (B T_i)
+  RZ_TRY(launch_advantages(mask, N, cu_rows, rewards, group_ids, n_resp,
+                           w.bad_cu, w.T, w.gcnt, w.gsum, w.Ad, w.fcoef, adv,
+                           err_flag, s));
   RZ_TRY(launch_transpose(dt, K_TRANSPOSE_W, lm_head, H, nullptr,
                           DevRows{nullptr, 0, V}, Vpad, H, w.WT, Vpad, s));
+  // a1-a4, a7-a9 in chunks of C valid rows (the count lives on the device;
+  // chunks past it do no work):
+  //   logits GEMM + log-softmax epilogue, also storing exp(z - m_tile);
+  //   ordered merge -> lse, log pi; c_t; dz = c_t e^(m_tile - lse) exp(...);
+  //   dHidden GEMM; dW GEMM accumulated over chunks in order.
   const int64_t nchunks = N > 0 ? (N + C - 1) / C : 1;
   for (int64_t k = 0; k < nchunks; ++k) {
     DevRows crow{w.nvalid, k * C, C};
     if (N > 0) {
+      RZ_TRY(launch_fwd_logits(dt, hidden, lda, w.idx, crow, lm_head, H, V,
+                               w.tokv, w.partials, N, w.ztgt, w.dz, Vpad, Vpad,
+                               s));
+      RZ_TRY(launch_lse_merge(w.partials, N, nt, crow, w.ztgt, w.tokv, V,
+                              w.lse_v, w.logpi_v, w.idx, logprobs, err_flag,
+                              s));
+      RZ_TRY(launch_coef(crow, w.logpi_v, logmu, w.idx, w.respv, w.fcoef,
+                         w.coef, s));
+      RZ_TRY(launch_dz_scale(dt, w.dz, Vpad, w.dzT, C, crow, w.partials, N,
+                             w.lse_v, w.coef, Vpad, s));
       RZ_TRY(launch_transpose(dt, K_TRANSPOSE_H, hidden, H, w.idx, crow, C, H,
                               w.hT, C, s));
-      RZ_TRY(launch_bwd_dz(dt, hidden, lda, w.idx, crow, lm_head, H, V, Vpad,
-                           w.lse_v, w.coef, w.dz, Vpad, w.dzT, C, s));
       RZ_TRY(launch_bwd_dh(dt, w.dz, Vpad, crow, w.WT, Vpad, H, V, Vpad,
                            w.idx, w.tokv, w.coef, lm_head, d_hidden, s));
     }
     RZ_TRY(launch_bwd_dw(dt, w.dzT, C, N > 0 ? crow : DevRows{nullptr, 0, 0},
                          w.hT, C, H, V, d_lm_head, k == 0, s));
   }
+  if (N > 0) RZ_TRY(launch_rows_finalize(mask, N, H, logprobs, d_hidden, s));
+  // a5: S_i from this call's logprobs, then L
+  RZ_TRY(launch_loss_value(mask, logprobs, logmu, N, cu_rows, n_resp, w.T,
+                           w.Ad, w.S, loss, s));
+  // a6: diagnostics over this call's outputs (same kernels as rz_diagnostics)
+  RZ_TRY(launch_diagnostics(logprobs, logmu, mask, N, w.diag_part,
+                            diag ? diag : w.diag_tmp, s));
+  // a9: exact one-hot part of dW
   RZ_TRY(launch_dw_fix(dt, w.nvalid, N, w.tokv, w.idx, w.coef, hidden, H, V,
                        w.counts, w.cursor, w.offsets, w.sorted, d_lm_head, s));
   return RZ_OK;

@@ -11,17 +11,19 @@ enum KernelId {
   K_MASK_COUNT = 0,
   K_MASK_SCAN,
   K_MASK_SCATTER,
+  K_RESP_COUNTS,     // rz_loss: T_i
+  K_ADVANTAGES,      // rz_loss: groups, A_i, per-response factors
   K_FWD_LOGITS,      // bi_lmhead_gemm with the fused log-softmax epilogue
   K_LSE_MERGE,       // bi_logsoftmax_gather merge
   K_ROWS_FINALIZE,
-  K_RESP_SUMS,       // rz_loss: per-response reductions
-  K_LOSS_FINALIZE,   // rz_loss: groups, advantages, loss
   K_COEF,
+  K_DZ_SCALE,        // dlogits from the forward's stored exp(z - m_tile)
+  K_RESP_SUMS,       // rz_loss: S_i
+  K_LOSS_VALUE,      // rz_loss: L
   K_DIAG_PARTIAL,    // rz_diagnostics
   K_DIAG_FINAL,
   K_TRANSPOSE_W,
   K_TRANSPOSE_H,
-  K_BWD_DZ,          // recompute GEMM with the dlogits epilogue
   K_BWD_DH,          // dHidden GEMM
   K_BWD_DW,          // dW GEMM
   K_FILL,
@@ -54,7 +56,8 @@ hipError_t launch_fwd_logits(int dt, const void* hidden, int64_t lda_bytes,
                              const int* a_rows, DevRows rows,
                              const void* lm_head, int H, int V,
                              const int* row_tokens, float2* partials,
-                             int64_t ldp, float* ztgt, hipStream_t s);
+                             int64_t ldp, float* ztgt, void* e, int64_t lde,
+                             int Vpad, hipStream_t s);
 hipError_t launch_lse_merge(const float2* partials, int64_t ldp, int nt,
                             DevRows rows, const float* ztgt,
                             const int* row_tokens, int V, float* lse_out,
@@ -67,15 +70,18 @@ hipError_t launch_mask_compact(const uint8_t* mask, int64_t n,
 hipError_t launch_rows_finalize(const uint8_t* mask, int64_t n, int H,
                                 float* logprobs, float* d_hidden,
                                 hipStream_t s);
-hipError_t launch_loss(const uint8_t* mask, const float* logprobs,
-                       const float* logmu, int64_t n, const int* cu,
-                       const float* rewards, const int* gid, int B,
-                       const int* bad_cu, int* T, double* S, int* gcnt,
-                       double* gsum, double* fcoef, float* adv, float* loss,
-                       int* err, hipStream_t s);
-hipError_t launch_coef(const int* nvalid, int64_t cap, const float* logpi_v,
-                       const float* logmu, const int* idx, const int* respv,
-                       const double* fcoef, float* coef, hipStream_t s);
+hipError_t launch_advantages(const uint8_t* mask, int64_t n, const int* cu,
+                             const float* rewards, const int* gid, int B,
+                             const int* bad_cu, int* T, int* gcnt, double* gsum,
+                             double* Ad, double* fcoef, float* adv, int* err,
+                             hipStream_t s);
+hipError_t launch_loss_value(const uint8_t* mask, const float* logprobs,
+                             const float* logmu, int64_t n, const int* cu,
+                             int B, const int* T, const double* Ad, double* S,
+                             float* loss, hipStream_t s);
+hipError_t launch_coef(DevRows rows, const float* logpi_v, const float* logmu,
+                       const int* idx, const int* respv, const double* fcoef,
+                       float* coef, hipStream_t s);
 size_t diag_partials_bytes(int64_t n);
 hipError_t launch_diagnostics(const float* logpi, const float* logmu,
                               const uint8_t* mask, int64_t n, void* partials,
@@ -84,11 +90,10 @@ hipError_t launch_transpose(int dt, int kid, const void* in, int64_t ld_in,
                             const int* rowmap, DevRows rows, int rows_pad,
                             int cols, void* out, int64_t ld_out,
                             hipStream_t s);
-hipError_t launch_bwd_dz(int dt, const void* hidden, int64_t lda_bytes,
-                         const int* idx, DevRows rows, const void* lm_head,
-                         int H, int V, int Vpad, const float* lse_v,
-                         const float* coef, void* dz, int64_t ldz, void* dzT,
-                         int64_t ldzt, hipStream_t s);
+hipError_t launch_dz_scale(int dt, void* dz, int64_t ldz, void* dzT,
+                           int64_t ldzt, DevRows rows, const float2* partials,
+                           int64_t ldp, const float* lse, const float* coef,
+                           int Vpad, hipStream_t s);
 hipError_t launch_bwd_dh(int dt, const void* dz, int64_t ldz, DevRows rows,
                          const void* WT, int64_t ldwt, int H, int V, int Vpad,
                          const int* idx, const int* tokv, const float* coef,

@@ -38,24 +38,31 @@ __device__ __forceinline__ void ms_combine(float& m, float& s, float m2,
   m = ma;
 }
 
+// One halving step of the reduce-scatter, element I of HALF: written with
+// compile-time indices (template recursion, no loop variable), so the
+// lane-dependent choice between two elements stays a register select
+// instead of becoming a dynamically indexed (scratch) array access.
+template <int I, int HALF, int MASK>
+__device__ __forceinline__ void rs_elems(float (&m)[16], float (&s)[16],
+                                         bool upper) {
+  if constexpr (I < HALF) {
+    const float sm = upper ? m[I] : m[HALF + I];
+    const float ss = upper ? s[I] : s[HALF + I];
+    float km = upper ? m[HALF + I] : m[I];
+    float ks = upper ? s[HALF + I] : s[I];
+    ms_combine(km, ks, __shfl_xor(sm, MASK, 64), __shfl_xor(ss, MASK, 64));
+    m[I] = km;
+    s[I] = ks;
+    rs_elems<I + 1, HALF, MASK>(m, s, upper);
+  }
+}
+
 __device__ __forceinline__ void reduce_scatter16_ms(float (&m)[16],
                                                     float (&s)[16], int lane) {
-#pragma unroll
-  for (int step = 0; step < 4; ++step) {
-    const int mask = 16 >> step;
-    const int half = 8 >> step;
-    const bool upper = (lane & mask) != 0;
-#pragma unroll
-    for (int i = 0; i < half; ++i) {
-      const float sm = upper ? m[i] : m[half + i];
-      const float ss = upper ? s[i] : s[half + i];
-      float km = upper ? m[half + i] : m[i];
-      float ks = upper ? s[half + i] : s[i];
-      ms_combine(km, ks, __shfl_xor(sm, mask, 64), __shfl_xor(ss, mask, 64));
-      m[i] = km;
-      s[i] = ks;
-    }
-  }
+  rs_elems<0, 8, 16>(m, s, (lane & 16) != 0);
+  rs_elems<0, 4, 8>(m, s, (lane & 8) != 0);
+  rs_elems<0, 2, 4>(m, s, (lane & 4) != 0);
+  rs_elems<0, 1, 2>(m, s, (lane & 2) != 0);
   ms_combine(m[0], s[0], __shfl_xor(m[0], 1, 64), __shfl_xor(s[0], 1, 64));
 }
 
@@ -86,15 +93,33 @@ struct FwdArgs {
   GemmOperands op;
   DevRows rows;
   const int* row_tokens;  // token of list position p
-  int V, nk, mt, nt;
+  int V, Vpad, nk, mt, nt;
   float2* partials;       // [nt][ldp] by list position
   int64_t ldp;
   float* ztgt;            // [positions]
+  void* e;                // learner call only: exp(z - m_tile) [rows][lde]
+  int64_t lde;
 };
 
-template <typename T>
+// Staging of one 256 x 256 bf16 tile row-major in LDS for coalesced stores:
+// row R, column c at byte R * 512 + ((c / 8) ^ (R & 4)) * 16 + (c % 8) * 2.
+// The chunk swizzle puts the two rows one store instruction writes (R and
+// R + 4) into different bank groups.
+__device__ __forceinline__ int stage_off(int R, int c) {
+  return R * 512 + (((c >> 3) ^ (R & 4)) << 4) + ((c & 7) << 1);
+}
+
+// Storage type of e = exp(z - m_tile) in (0, 1]: fp16 for bf16 inputs (an
+// 11-bit significand at the same two bytes, so that e's rounding adds a
+// quarter of the bf16 rounding the dlogits already carry), fp32 otherwise.
+template <typename T> struct EStore { typedef float type; };
+template <> struct EStore<bf16> { typedef _Float16 type; };
+
+template <typename T, bool kStoreE>
 __global__ RZ_GEMM_ATTR void k_fwd_logits(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  // [0, 128 KB): main-loop stages, then (learner call) the e tile;
+  // then per-wave (m, s), the tile's tokens and its row maxima
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes + 6144];
   const RowCount rc = to_rc(a.rows);
   const int M = rc.get();
   // Only the tiles of the M rows present are numbered (M may be a device
@@ -109,9 +134,9 @@ __global__ RZ_GEMM_ATTR void k_fwd_logits(FwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
-  // LDS after the main loop: per-wave (m, s) of its 128 rows, tile tokens
-  float2* wstat = reinterpret_cast<float2*>(lds);            // [4][128]
-  int* rtok = reinterpret_cast<int*>(lds + 4 * 128 * 8);     // [256]
+  float2* wstat = reinterpret_cast<float2*>(lds + kLdsBytes);        // [4][128]
+  int* rtok = reinterpret_cast<int*>(lds + kLdsBytes + 4096);        // [256]
+  float* rmax = reinterpret_cast<float*>(lds + kLdsBytes + 5120);    // [256]
   {
     const int m = m0 + tid;
     rtok[tid] = m < M ? a.row_tokens[rc.base + m] : -1;
@@ -162,12 +187,63 @@ __global__ RZ_GEMM_ATTR void k_fwd_logits(FwdArgs a) {
   // merge the two column halves of each row in a fixed order
   {
     const int m = m0 + tid;
-    if (m < M) {
-      const int w0 = (tid >> 7) * 2, lr = tid & 127;
-      const float2 p0 = wstat[w0 * 128 + lr], p1 = wstat[(w0 + 1) * 128 + lr];
-      float mm = p0.x, ss = p0.y;
-      ms_combine(mm, ss, p1.x, p1.y);
+    const int w0 = (tid >> 7) * 2, lr = tid & 127;
+    const float2 p0 = wstat[w0 * 128 + lr], p1 = wstat[(w0 + 1) * 128 + lr];
+    float mm = p0.x, ss = p0.y;
+    ms_combine(mm, ss, p1.x, p1.y);
+    if (m < M)
       a.partials[(int64_t)tc.tn * a.ldp + rc.base + m] = make_float2(mm, ss);
+    rmax[tid] = mm;
+  }
+  if constexpr (kStoreE) {
+    // e = exp(z - m_tile) with the tile max just stored in the partials;
+    // the backward rescales it to dlogits once lse is known.  Zero for
+    // columns >= V and rows >= M.
+    __syncthreads();
+    typedef typename EStore<T>::type E;
+    E* e = reinterpret_cast<E*>(a.e);
+    if constexpr (sizeof(T) == 2) {
+      char* tile = lds;
+#pragma unroll
+      for (int mi = 0; mi < kTM; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < kTN; ++ni) {
+          const int lc = acc_col(wn, ni, lane);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int R = acc_row(wm, mi, r, lane);
+            const float v = (cvalid[ni] && m0 + R < M)
+                                ? exp_approx(acc[mi][ni][r] - rmax[R])
+                                : 0.f;
+            *reinterpret_cast<E*>(tile + stage_off(R, lc)) = (E)v;
+          }
+        }
+      __syncthreads();
+      // 16-byte row chunks: 32 lanes cover one 512-byte tile row
+#pragma unroll 4
+      for (int it = 0; it < 32; ++it) {
+        const int idx = it * 256 + tid;
+        const int R = idx >> 5, k = idx & 31;
+        const int col = n0 + k * 8;
+        if (m0 + R < M && col < a.Vpad)
+          *reinterpret_cast<u32x4*>(e + (int64_t)(m0 + R) * a.lde + col) =
+              *reinterpret_cast<const u32x4*>(tile + stage_off(R, k * 8));
+      }
+    } else {
+#pragma unroll
+      for (int mi = 0; mi < kTM; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < kTN; ++ni) {
+          const int col = colbase + ni * 32;
+          if (col >= a.Vpad) continue;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int R = acc_row(wm, mi, r, lane);
+            if (m0 + R >= M) continue;
+            e[(int64_t)(m0 + R) * a.lde + col] =
+                cvalid[ni] ? (E)exp_approx(acc[mi][ni][r] - rmax[R]) : (E)0.f;
+          }
+        }
     }
   }
 }
@@ -358,40 +434,28 @@ __device__ __forceinline__ int block_sum_i(int x, int* sh) {
   return r;
 }
 
-__global__ __launch_bounds__(256) void k_resp_sums(const uint8_t* mask,
-                                                   const float* logprobs,
-                                                   const float* logmu,
-                                                   int64_t n, const int* cu,
-                                                   int* T, double* S) {
-  __shared__ double shd[256];
+// T_i: valid rows of response i (cu_rows clamped to [0, n] so that a bad
+// cu_rows cannot send the reads out of bounds; it is flagged separately).
+__global__ __launch_bounds__(256) void k_resp_counts(const uint8_t* mask,
+                                                     int64_t n, const int* cu,
+                                                     int* T) {
   __shared__ int shi[256];
   const int i = blockIdx.x;
   int64_t lo = cu[i], hi = cu[i + 1];
   lo = lo < 0 ? 0 : (lo > n ? n : lo);
   hi = hi < lo ? lo : (hi > n ? n : hi);
-  double s = 0.0;
   int c = 0;
-  for (int64_t t = lo + threadIdx.x; t < hi; t += 256) {
-    if (mask[t]) {
-      s += (double)expf(logprobs[t] - logmu[t]);
-      ++c;
-    }
-  }
-  const double ss = block_sum_d(s, shd);
-  const int cc = block_sum_i(c, shi);
-  if (threadIdx.x == 0) {
-    S[i] = ss;
-    T[i] = cc;
-  }
+  for (int64_t t = lo + threadIdx.x; t < hi; t += 256) c += mask[t] != 0;
+  c = block_sum_i(c, shi);
+  if (threadIdx.x == 0) T[i] = c;
 }
 
-// Groups, advantages A_i = r_i - mean of r over the group (ascending i),
-// the per-response factor A_i / (B T_i) and L = -(1/B) sum_i A_i S_i / T_i.
-__global__ __launch_bounds__(256) void k_loss_finalize(
-    const float* rewards, const int* gid, int B, const int* T, const double* S,
-    const int* bad_cu, int* gcnt, double* gsum, double* fcoef, float* adv,
-    float* loss, int* err) {
-  __shared__ double shd[256];
+// Groups and advantages: A_i = r_i - mean of r over the group of i (sums in
+// ascending i, fp64), and the per-response factor A_i / (B T_i) of c_t.
+__global__ __launch_bounds__(256) void k_advantages(
+    const float* rewards, const int* gid, int B, const int* T,
+    const int* bad_cu, int* gcnt, double* gsum, double* Ad, double* fcoef,
+    float* adv, int* err) {
   __shared__ int bad;
   const int tid = threadIdx.x;
   if (tid == 0) bad = *bad_cu;
@@ -411,24 +475,51 @@ __global__ __launch_bounds__(256) void k_loss_finalize(
     if (gid[i] < 0 || gid[i] >= B) atomicOr(&bad, 2);
   __syncthreads();
   const double qnan = __builtin_nan("");
-  double part = 0.0;
   for (int i = tid; i < B; i += 256) {
-    const int g = gid[i];
-    double A = qnan, f = qnan, term = qnan;
+    double A = qnan, f = qnan;
     if (!bad) {
+      const int g = gid[i];
       A = (double)rewards[i] - gsum[g] / (double)gcnt[g];
       f = T[i] > 0 ? A / ((double)B * (double)T[i]) : 0.0;
-      term = T[i] > 0 ? A * S[i] / (double)T[i] : 0.0;
     }
+    Ad[i] = A;
     fcoef[i] = f;
     if (adv) adv[i] = (float)A;
-    part += term;
   }
-  const double tot = block_sum_d(part, shd);
-  if (tid == 0) {
-    *loss = (float)(-tot / (double)B);
-    if (err && (bad & 2)) atomicOr(err, 2);
-  }
+  if (tid == 0 && err && (bad & 2)) atomicOr(err, 2);
+}
+
+// S_i = sum of w_t = exp(log pi_t - log mu_t) over the valid rows of
+// response i (no clipping), fp64, per-thread strided partials then a fixed
+// tree: the order depends only on the response's rows.
+__global__ __launch_bounds__(256) void k_resp_sums(const uint8_t* mask,
+                                                   const float* logprobs,
+                                                   const float* logmu,
+                                                   int64_t n, const int* cu,
+                                                   double* S) {
+  __shared__ double shd[256];
+  const int i = blockIdx.x;
+  int64_t lo = cu[i], hi = cu[i + 1];
+  lo = lo < 0 ? 0 : (lo > n ? n : lo);
+  hi = hi < lo ? lo : (hi > n ? n : hi);
+  double s = 0.0;
+  for (int64_t t = lo + threadIdx.x; t < hi; t += 256)
+    if (mask[t]) s += (double)expf(logprobs[t] - logmu[t]);
+  s = block_sum_d(s, shd);
+  if (threadIdx.x == 0) S[i] = s;
+}
+
+// L = -(1/B) sum_i [T_i > 0] A_i S_i / T_i, a fixed tree over responses.
+__global__ __launch_bounds__(256) void k_loss_value(const double* Ad,
+                                                    const int* T,
+                                                    const double* S, int B,
+                                                    float* loss) {
+  __shared__ double shd[256];
+  double part = 0.0;
+  for (int i = threadIdx.x; i < B; i += 256)
+    part += T[i] > 0 ? Ad[i] * S[i] / (double)T[i] : 0.0;
+  part = block_sum_d(part, shd);
+  if (threadIdx.x == 0) *loss = (float)(-part / (double)B);
 }
 
 // c_t = A_i w_t / (B T_i): minus the derivative of L by log pi_t (the
@@ -441,8 +532,9 @@ __global__ __launch_bounds__(256) void k_coef(DevRows rows,
                                               const double* fcoef,
                                               float* coef) {
   const RowCount rc = to_rc(rows);
-  const int p = blockIdx.x * 256 + threadIdx.x;
-  if (p >= rc.get()) return;
+  const int q = blockIdx.x * 256 + threadIdx.x;
+  if (q >= rc.get()) return;
+  const int64_t p = rc.base + q;
   const float w = expf(logpi_v[p] - logmu[idx[p]]);
   coef[p] = (float)(fcoef[respv[p]] * (double)w);
 }
@@ -543,75 +635,45 @@ __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ in,
 }
 
 // ===================================================================
-// Backward, part 1: recompute the logits tile (same engine, same K order
-// as the forward) and emit dlogits = c_t * softmax(z)_v for v < V, as the
-// token-major dz [C, Vpad] (A operand of dHidden) and the vocab-major
-// dz^T [Vpad, C] (A operand of dW).  The one-hot part -c_t [v == a_t] is
-// applied exactly in fp32 by the dHidden epilogue and the dW fix-up.
+// Backward, part 1: dlogits.  The forward of the learner call stored
+// e[t, v] = exp(z[t, v] - m_tile(t, j)) (EStore type, in the dz buffer) for
+// the vocab tile j holding v; with
+// lse_t known, dz[t, v] = c_t * exp(m_tile(t, j) - lse_t) * e[t, v] is the
+// softmax part of dL/dz (the one-hot part -c_t [v == a_t] is applied exactly
+// in fp32 by the dHidden epilogue and the dW fix-up).  The kernel rescales
+// e in place into the token-major dz [C, Vpad] (A operand of dHidden) and
+// writes the vocab-major dz^T [Vpad, C] (A operand of dW) through an LDS
+// transpose.  Rows at or past the chunk's count become zero columns of dz^T.
 // ===================================================================
 template <typename T>
-struct DzArgs {
-  GemmOperands op;
-  DevRows rows;
-  const float* lse;
-  const float* coef;
-  int V, Vpad, nk, mt, nt;
-  T* dz;
-  int64_t ldz;
-  T* dzT;
-  int64_t ldzt;
-};
-
-template <typename T>
-__global__ RZ_GEMM_ATTR void k_bwd_dz(DzArgs<T> a) {
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
-  const RowCount rc = to_rc(a.rows);
-  const int M = rc.get();
-  // Only the tiles of the M rows present are numbered (M may be a device
-  // count below the launch bound), so the active tiles spread over all XCDs.
-  const int mt = (M + kBM - 1) / kBM;
-  if ((int)blockIdx.x >= mt * a.nt) return;
-  const TileCoord tc = map_tile(blockIdx.x, mt * a.nt, mt, a.nt);
-  const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
-
-  f32x16 acc[kTM][kTN];
-  gemm_mainloop<T>(a.op, M, m0, n0, a.nk, acc, lds);
-
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
-  float* slse = reinterpret_cast<float*>(lds);
-  float* scoef = slse + 256;
-  {
-    const int m = m0 + tid;
-    slse[tid] = m < M ? a.lse[rc.base + m] : 0.f;
-    scoef[tid] = m < M ? a.coef[rc.base + m] : 0.f;
+__global__ __launch_bounds__(256) void k_dz_scale(
+    T* __restrict__ dz, int64_t ldz, T* __restrict__ dzT, int64_t ldzt,
+    DevRows rows, const float2* __restrict__ partials, int64_t ldp,
+    const float* __restrict__ lse, const float* __restrict__ coef, int Vpad) {
+  __shared__ T tile[64][66];
+  const RowCount rc = to_rc(rows);
+  const int R = rc.get();
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  if (r0 >= ((R + 63) & ~63) || c0 >= Vpad) return;
+  const int j = c0 / kBN;  // the 64-column block lies in vocab tile j
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int rr = ty; rr < 64; rr += 4) {
+    const int t = r0 + rr;
+    T y = (T)0.f;
+    if (t < R) {
+      const int64_t pos = rc.base + t;
+      const float sc =
+          coef[pos] * exp_approx(partials[(int64_t)j * ldp + pos].x - lse[pos]);
+      T* p = dz + (int64_t)t * ldz + c0 + tx;
+      typedef typename EStore<T>::type E;
+      y = (T)(sc * (float)(*reinterpret_cast<const E*>(p)));
+      *p = y;
+    }
+    tile[rr][tx] = y;
   }
   __syncthreads();
-#pragma unroll
-  for (int mi = 0; mi < kTM; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < kTN; ++ni) {
-      const int col = n0 + acc_col(wn, ni, lane);
-      if (col >= a.Vpad) continue;
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        T q[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = r4 * 4 + j;
-          const int row = acc_row(wm, mi, r, lane);
-          float val = 0.f;
-          if (m0 + row < M && col < a.V)
-            val = scoef[row] * exp_approx(acc[mi][ni][r] - slse[row]);
-          q[j] = from_f<T>(val);
-          a.dz[(int64_t)(m0 + row) * a.ldz + col] = q[j];
-        }
-        const int row0 = acc_row(wm, mi, r4 * 4, lane);
-        T* dst = a.dzT + (int64_t)col * a.ldzt + m0 + row0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) dst[j] = q[j];
-      }
-    }
+  for (int cc = ty; cc < 64; cc += 4)
+    dzT[(int64_t)(c0 + cc) * ldzt + r0 + tx] = tile[tx][cc];
 }
 
 // ===================================================================
@@ -834,12 +896,12 @@ inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 const char* kernel_name(int k) {
   static const char* names[K_NUM_KERNELS] = {
-      "mask_count",   "mask_scan",    "mask_scatter", "fwd_logits_gemm",
-      "lse_merge",    "rows_finalize", "resp_sums",   "loss_finalize",
-      "coef",         "diag_partial", "diag_final",   "transpose_w",
-      "transpose_h",  "bwd_dz_gemm",  "bwd_dh_gemm",  "bwd_dw_gemm",
-      "fill",         "tok_hist",     "scan",         "tok_scatter",
-      "bucket_sort",  "dw_fix"};
+      "mask_count",  "mask_scan",   "mask_scatter", "resp_counts",
+      "advantages",  "fwd_logits_gemm", "lse_merge", "rows_finalize",
+      "coef",        "dz_scale",    "resp_sums",    "loss_value",
+      "diag_partial", "diag_final", "transpose_w",  "transpose_h",
+      "bwd_dh_gemm", "bwd_dw_gemm", "fill",         "tok_hist",
+      "scan",        "tok_scatter", "bucket_sort",  "dw_fix"};
   return (k >= 0 && k < K_NUM_KERNELS) ? names[k] : "?";
 }
 
@@ -847,23 +909,32 @@ hipError_t launch_fwd_logits(int dt, const void* hidden, int64_t lda_bytes,
                              const int* a_rows, DevRows rows,
                              const void* lm_head, int H, int V,
                              const int* row_tokens, float2* partials,
-                             int64_t ldp, float* ztgt, hipStream_t s) {
+                             int64_t ldp, float* ztgt, void* e, int64_t lde,
+                             int Vpad, hipStream_t s) {
   FwdArgs a;
   a.op = GemmOperands{(const char*)hidden, lda_bytes, a_rows, rows.base,
                       (const char*)lm_head, (int64_t)H * (dt ? 2 : 4), V};
   a.rows = rows;
   a.row_tokens = row_tokens;
   a.V = V;
+  a.Vpad = Vpad;
   a.nk = H / (dt ? Stage<bf16>::kK : Stage<float>::kK);
   a.mt = cdiv(rows.cap, kBM);
   a.nt = cdiv(V, kBN);
   a.partials = partials;
   a.ldp = ldp;
   a.ztgt = ztgt;
+  a.e = e;
+  a.lde = lde;
   const int nblk = a.mt * a.nt;
   return timed(K_FWD_LOGITS, s, [&] {
-    if (dt) k_fwd_logits<bf16><<<nblk, kThreads, 0, s>>>(a);
-    else k_fwd_logits<float><<<nblk, kThreads, 0, s>>>(a);
+    if (dt) {
+      if (e) k_fwd_logits<bf16, true><<<nblk, kThreads, 0, s>>>(a);
+      else k_fwd_logits<bf16, false><<<nblk, kThreads, 0, s>>>(a);
+    } else {
+      if (e) k_fwd_logits<float, true><<<nblk, kThreads, 0, s>>>(a);
+      else k_fwd_logits<float, false><<<nblk, kThreads, 0, s>>>(a);
+    }
   });
 }
 
@@ -911,29 +982,40 @@ hipError_t launch_rows_finalize(const uint8_t* mask, int64_t n, int H,
   });
 }
 
-hipError_t launch_loss(const uint8_t* mask, const float* logprobs,
-                       const float* logmu, int64_t n, const int* cu,
-                       const float* rewards, const int* gid, int B,
-                       const int* bad_cu, int* T, double* S, int* gcnt,
-                       double* gsum, double* fcoef, float* adv, float* loss,
-                       int* err, hipStream_t s) {
-  hipError_t e = timed(K_RESP_SUMS, s, [&] {
-    k_resp_sums<<<B, 256, 0, s>>>(mask, logprobs, logmu, n, cu, T, S);
+hipError_t launch_advantages(const uint8_t* mask, int64_t n, const int* cu,
+                             const float* rewards, const int* gid, int B,
+                             const int* bad_cu, int* T, int* gcnt, double* gsum,
+                             double* Ad, double* fcoef, float* adv, int* err,
+                             hipStream_t s) {
+  hipError_t e = timed(K_RESP_COUNTS, s, [&] {
+    k_resp_counts<<<B, 256, 0, s>>>(mask, n, cu, T);
   });
   if (e != hipSuccess) return e;
-  return timed(K_LOSS_FINALIZE, s, [&] {
-    k_loss_finalize<<<1, 256, 0, s>>>(rewards, gid, B, T, S, bad_cu, gcnt,
-                                      gsum, fcoef, adv, loss, err);
+  return timed(K_ADVANTAGES, s, [&] {
+    k_advantages<<<1, 256, 0, s>>>(rewards, gid, B, T, bad_cu, gcnt, gsum, Ad,
+                                   fcoef, adv, err);
   });
 }
 
-hipError_t launch_coef(const int* nvalid, int64_t cap, const float* logpi_v,
-                       const float* logmu, const int* idx, const int* respv,
-                       const double* fcoef, float* coef, hipStream_t s) {
-  DevRows rows{nvalid, 0, (int)cap};
+hipError_t launch_loss_value(const uint8_t* mask, const float* logprobs,
+                             const float* logmu, int64_t n, const int* cu,
+                             int B, const int* T, const double* Ad, double* S,
+                             float* loss, hipStream_t s) {
+  hipError_t e = timed(K_RESP_SUMS, s, [&] {
+    k_resp_sums<<<B, 256, 0, s>>>(mask, logprobs, logmu, n, cu, S);
+  });
+  if (e != hipSuccess) return e;
+  return timed(K_LOSS_VALUE, s, [&] {
+    k_loss_value<<<1, 256, 0, s>>>(Ad, T, S, B, loss);
+  });
+}
+
+hipError_t launch_coef(DevRows rows, const float* logpi_v, const float* logmu,
+                       const int* idx, const int* respv, const double* fcoef,
+                       float* coef, hipStream_t s) {
   return timed(K_COEF, s, [&] {
-    k_coef<<<cdiv(cap, 256), 256, 0, s>>>(rows, logpi_v, logmu, idx, respv,
-                                          fcoef, coef);
+    k_coef<<<cdiv(rows.cap, 256), 256, 0, s>>>(rows, logpi_v, logmu, idx,
+                                               respv, fcoef, coef);
   });
 }
 
@@ -975,43 +1057,21 @@ hipError_t launch_transpose(int dt, int kid, const void* in, int64_t ld_in,
   });
 }
 
-template <typename T>
-static hipError_t launch_bwd_dz_t(const void* hidden, int64_t lda_bytes,
-                                  const int* idx, DevRows rows,
-                                  const void* lm_head, int H, int V, int Vpad,
-                                  const float* lse_v, const float* coef,
-                                  void* dz, int64_t ldz, void* dzT,
-                                  int64_t ldzt, hipStream_t s) {
-  DzArgs<T> a;
-  a.op = GemmOperands{(const char*)hidden, lda_bytes, idx, rows.base,
-                      (const char*)lm_head, (int64_t)H * (int64_t)sizeof(T), V};
-  a.rows = rows;
-  a.lse = lse_v;
-  a.coef = coef;
-  a.V = V;
-  a.Vpad = Vpad;
-  a.nk = H / Stage<T>::kK;
-  a.mt = cdiv(rows.cap, kBM);
-  a.nt = cdiv(V, kBN);
-  a.dz = (T*)dz;
-  a.ldz = ldz;
-  a.dzT = (T*)dzT;
-  a.ldzt = ldzt;
-  return timed(K_BWD_DZ, s, [&] {
-    k_bwd_dz<T><<<a.mt * a.nt, kThreads, 0, s>>>(a);
+hipError_t launch_dz_scale(int dt, void* dz, int64_t ldz, void* dzT,
+                           int64_t ldzt, DevRows rows, const float2* partials,
+                           int64_t ldp, const float* lse, const float* coef,
+                           int Vpad, hipStream_t s) {
+  dim3 grid(cdiv(rows.cap, 64), cdiv(Vpad, 64));
+  return timed(K_DZ_SCALE, s, [&] {
+    if (dt)
+      k_dz_scale<bf16><<<grid, 256, 0, s>>>((bf16*)dz, ldz, (bf16*)dzT, ldzt,
+                                            rows, partials, ldp, lse, coef,
+                                            Vpad);
+    else
+      k_dz_scale<float><<<grid, 256, 0, s>>>((float*)dz, ldz, (float*)dzT,
+                                             ldzt, rows, partials, ldp, lse,
+                                             coef, Vpad);
   });
-}
-
-hipError_t launch_bwd_dz(int dt, const void* hidden, int64_t lda_bytes,
-                         const int* idx, DevRows rows, const void* lm_head,
-                         int H, int V, int Vpad, const float* lse_v,
-                         const float* coef, void* dz, int64_t ldz, void* dzT,
-                         int64_t ldzt, hipStream_t s) {
-  return dt ? launch_bwd_dz_t<bf16>(hidden, lda_bytes, idx, rows, lm_head, H,
-                                    V, Vpad, lse_v, coef, dz, ldz, dzT, ldzt, s)
-            : launch_bwd_dz_t<float>(hidden, lda_bytes, idx, rows, lm_head, H,
-                                     V, Vpad, lse_v, coef, dz, ldz, dzT, ldzt,
-                                     s);
 }
 
 template <typename T>
