@@ -650,30 +650,57 @@ __global__ __launch_bounds__(256) void k_dz_scale(
     T* __restrict__ dz, int64_t ldz, T* __restrict__ dzT, int64_t ldzt,
     DevRows rows, const float2* __restrict__ partials, int64_t ldp,
     const float* __restrict__ lse, const float* __restrict__ coef, int Vpad) {
-  __shared__ T tile[64][66];
+  typedef typename EStore<T>::type E;
+  constexpr int kVec = 16 / (int)sizeof(T);           // values per 16 bytes
+  constexpr int kRowChunks = kBN / kVec;              // 16-byte chunks per row
+  __shared__ __attribute__((aligned(16))) T tile[64][kBN + 8];
+  __shared__ float sc[64];
   const RowCount rc = to_rc(rows);
   const int R = rc.get();
-  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
-  if (r0 >= ((R + 63) & ~63) || c0 >= Vpad) return;
-  const int j = c0 / kBN;  // the 64-column block lies in vocab tile j
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int rr = ty; rr < 64; rr += 4) {
-    const int t = r0 + rr;
-    T y = (T)0.f;
+  const int r0 = blockIdx.x * 64, j = blockIdx.y, c0 = j * kBN;
+  if (r0 >= ((R + 63) & ~63)) return;
+  const int tid = threadIdx.x;
+  // one scale per row of this vocab tile: c_t exp(m_tile(t, j) - lse_t)
+  if (tid < 64) {
+    const int t = r0 + tid;
+    float v = 0.f;
     if (t < R) {
       const int64_t pos = rc.base + t;
-      const float sc =
-          coef[pos] * exp_approx(partials[(int64_t)j * ldp + pos].x - lse[pos]);
-      T* p = dz + (int64_t)t * ldz + c0 + tx;
-      typedef typename EStore<T>::type E;
-      y = (T)(sc * (float)(*reinterpret_cast<const E*>(p)));
-      *p = y;
+      v = coef[pos] * exp_approx(partials[(int64_t)j * ldp + pos].x - lse[pos]);
     }
-    tile[rr][tx] = y;
+    sc[tid] = v;
   }
   __syncthreads();
-  for (int cc = ty; cc < 64; cc += 4)
-    dzT[(int64_t)(c0 + cc) * ldzt + r0 + tx] = tile[tx][cc];
+  // rescale e -> dz in place, 16 bytes at a time; rows at or past R are zero
+  for (int c = tid; c < 64 * kRowChunks; c += 256) {
+    const int rr = c / kRowChunks, k = c % kRowChunks;
+    const int t = r0 + rr, col = c0 + k * kVec;
+    T y[kVec];
+    if (t < R && col < Vpad) {
+      T* p = dz + (int64_t)t * ldz + col;
+      E x[kVec];
+      *reinterpret_cast<u32x4*>(x) = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+      for (int q = 0; q < kVec; ++q) y[q] = (T)(sc[rr] * (float)x[q]);
+      *reinterpret_cast<u32x4*>(p) = *reinterpret_cast<const u32x4*>(y);
+    } else {
+#pragma unroll
+      for (int q = 0; q < kVec; ++q) y[q] = (T)0.f;
+    }
+    *reinterpret_cast<u32x4*>(&tile[rr][k * kVec]) = *reinterpret_cast<const u32x4*>(y);
+  }
+  __syncthreads();
+  // dz^T: each 16-byte chunk holds kVec consecutive tokens of one vocab
+  // column; lanes walk consecutive columns (conflict-free LDS reads)
+  for (int c = tid; c < kBN * (64 / kVec); c += 256) {
+    const int v = c % kBN, tq = c / kBN;
+    if (c0 + v >= Vpad) continue;
+    T y[kVec];
+#pragma unroll
+    for (int q = 0; q < kVec; ++q) y[q] = tile[tq * kVec + q][v];
+    *reinterpret_cast<u32x4*>(dzT + (int64_t)(c0 + v) * ldzt + r0 + tq * kVec) =
+        *reinterpret_cast<const u32x4*>(y);
+  }
 }
 
 // ===================================================================
@@ -1061,7 +1088,7 @@ hipError_t launch_dz_scale(int dt, void* dz, int64_t ldz, void* dzT,
                            int64_t ldzt, DevRows rows, const float2* partials,
                            int64_t ldp, const float* lse, const float* coef,
                            int Vpad, hipStream_t s) {
-  dim3 grid(cdiv(rows.cap, 64), cdiv(Vpad, 64));
+  dim3 grid(cdiv(rows.cap, 64), cdiv(Vpad, kBN));
   return timed(K_DZ_SCALE, s, [&] {
     if (dt)
       k_dz_scale<bf16><<<grid, 256, 0, s>>>((bf16*)dz, ldz, (bf16*)dzT, ldzt,
