@@ -87,6 +87,9 @@ def main():
     ap.add_argument("--cpu-valid", type=int, default=1024,
                     help="valid rows in the oracle's CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, run one plain 1 GiB device "
+                         "copy so a counter run can scale its byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -158,6 +161,15 @@ def main():
                 "launches_per_step": launches // args.steps}
     log("per-step kernel ms: " + ", ".join(f"{k}={v:.2f}" for k, v in
                                             sorted(kms.items(), key=lambda x: -x[1])))
+
+    if args.copy_calibration:
+        x = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        torch.cuda.synchronize()
+        y.copy_(x)
+        torch.cuda.synchronize()
+        log("copy calibration: 1 GiB read + 1 GiB written by one copy kernel")
+        del x, y
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -192,19 +192,19 @@ __device__ __forceinline__ void gemm_mainloop(const GemmOperands& op, int M,
     n = n < op.N ? n : op.N - 1;
     gb[i] = op.B + (int64_t)n * op.ldb + c * 16;
   }
-  auto dload = [&](int kt, int stage) {
+  // load j of a stage: j < 8 fills A rows 8 j + [0, 8) of this wave's 64,
+  // j >= 8 the same rows of B
+  auto dma1 = [&](int kt, int stage, int j) {
     const int64_t k = (int64_t)kt * kRowBytes;
     char* sa = lds + stage * kStageBytes + wu * 64 * kRowBytes;
-    char* sb = sa + kOperandBytes;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_global_load_lds(ga[i] + k,
-                                       (lds_ptr_t)(sa + i * 8 * kRowBytes), 16,
+    if (j < 8)
+      __builtin_amdgcn_global_load_lds(ga[j] + k,
+                                       (lds_ptr_t)(sa + j * 8 * kRowBytes), 16,
                                        0, 0);
-      __builtin_amdgcn_global_load_lds(gb[i] + k,
-                                       (lds_ptr_t)(sb + i * 8 * kRowBytes), 16,
-                                       0, 0);
-    }
+    else
+      __builtin_amdgcn_global_load_lds(
+          gb[j - 8] + k,
+          (lds_ptr_t)(sa + kOperandBytes + (j - 8) * 8 * kRowBytes), 16, 0, 0);
   };
   // fragments of two consecutive 16-byte K steps (register double buffer)
   u32x4 fa[2][kTM], fb[2][kTN];
@@ -218,40 +218,68 @@ __device__ __forceinline__ void gemm_mainloop(const GemmOperands& op, int M,
     for (int ni = 0; ni < kTN; ++ni)
       fb[buf][ni] = *reinterpret_cast<const u32x4*>(sb + b_off[ni] + c_off[s]);
   };
-  auto mma = [&](int buf) {
+  // block q = 4 mi + ni of one K step
+  auto mm1 = [&](int buf, int q) {
+    mfma_step(acc[q / kTN][q % kTN], fa[buf][q / kTN], fb[buf][q % kTN],
+              (const T*)nullptr);
+  };
+  auto mmr = [&](int buf, int lo, int hi) {
 #pragma unroll
-    for (int mi = 0; mi < kTM; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < kTN; ++ni)
-        mfma_step(acc[mi][ni], fa[buf][mi], fb[buf][ni], (const T*)nullptr);
+    for (int q = lo; q < hi; ++q) mm1(buf, q);
   };
 
-  // Schedule: stage kt lives in LDS buffer kt & 1.  While stage kt is
-  // consumed (four 16-byte K steps, the fragments of step s + 1 read while
-  // step s's MFMAs run), stage kt + 1 is landing in the other buffer.  At
-  // the end of the stage every wave waits for its own loads (vmcnt(0)),
-  // the barrier makes stage kt + 1 complete and buffer kt & 1 free, and
-  // stage kt + 2 is requested into it.  The MFMA order per accumulator is
-  // k = 0, 1, 2, ... exactly as in a plain loop.
-  dload(0, 0);
+  // Schedule: stage kt lives in LDS buffer kt & 1 and is consumed as four
+  // 16-byte K steps s, each a phase of 16 MFMAs on fragments read during
+  // the previous phase.  A phase starts with one MFMA, which needs the
+  // previous phase's reads, and only then issues the next step's reads, so
+  // the LDS wait before it never covers reads that were just issued.
+  // Stage kt + 1's sixteen loads go out one per MFMA: eight right after the
+  // barrier that frees its buffer (among the last eight MFMAs of stage
+  // kt - 1) and eight in the first phase of stage kt; a burst of loads
+  // stalls the in-order wave and drains the MFMA pipe.  Before the barrier
+  // that ends stage kt, each wave waits for its own loads (vmcnt(0)), so the
+  // barrier makes stage kt + 1 complete in LDS and buffer kt & 1 free.
+  // sched_barrier(0) pins this order against the scheduler.  The MFMA
+  // order per accumulator is k = 0, 1, 2, ... exactly as in a plain loop.
+#define RZ_SB() __builtin_amdgcn_sched_barrier(0)
+#pragma unroll
+  for (int j = 0; j < 16; ++j) dma1(0, 0, j);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (nk > 1) dload(1, 1);
+  if (nk > 1) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dma1(1, 1, j);
+  }
   lread(0, 0, 0);
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    lread(1, cur, 1);
-    mma(0);
-    lread(0, cur, 2);
-    mma(1);
-    lread(1, cur, 3);
-    mma(0);
-    mma(1);
-    if (kt + 1 < nk) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const bool nx = kt + 1 < nk, nx2 = kt + 2 < nk;
+    RZ_SB(); mm1(0, 0); RZ_SB(); lread(1, cur, 1); RZ_SB();
+#pragma unroll
+    for (int q = 1; q < 16; ++q) {
+      mm1(0, q);
+      RZ_SB();
+      if (q <= 8 && nx) dma1(kt + 1, cur ^ 1, 7 + q);
+      RZ_SB();
+    }
+    mm1(1, 0); RZ_SB(); lread(0, cur, 2); RZ_SB(); mmr(1, 1, 16); RZ_SB();
+    mm1(0, 0); RZ_SB(); lread(1, cur, 3); RZ_SB(); mmr(0, 1, 16); RZ_SB();
+    mmr(1, 0, 8);
+    RZ_SB();
+    if (nx) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (kt + 2 < nk) dload(kt + 2, cur);
-    if (kt + 1 < nk) lread(0, cur ^ 1, 0);
+    RZ_SB();
+    if (nx) lread(0, cur ^ 1, 0);
+    RZ_SB();
+#pragma unroll
+    for (int q = 8; q < 16; ++q) {
+      mm1(1, q);
+      RZ_SB();
+      if (nx2) dma1(kt + 2, cur, q - 8);
+      RZ_SB();
+    }
   }
+#undef RZ_SB
 }
 
 }  // namespace rz
