@@ -136,7 +136,13 @@ struct GemmOperands {
 // at or past M (and rows of B at or past N) are read from row M-1 (N-1) so
 // every load stays in bounds; their results are discarded by the epilogue.
 // Leaves the LDS free (all waves past the last barrier) on return.
-template <typename T>
+//
+// kSwap = true issues each MFMA with the operands exchanged, which computes
+// the same products but leaves the transposed block in the accumulators:
+// lane l then holds row l % 32 of its 32 x 32 block (an A row) and registers
+// r hold columns 8 (r / 4) + 4 (l / 32) + (r % 4), i.e. every lane owns
+// four runs of four consecutive B rows of one A row.
+template <typename T, bool kSwap = false>
 __device__ __forceinline__ void gemm_mainloop(const GemmOperands& op, int M,
                                               int m0, int n0, int nk,
                                               f32x16 (&acc)[kTM][kTN],
@@ -220,8 +226,12 @@ __device__ __forceinline__ void gemm_mainloop(const GemmOperands& op, int M,
   };
   // block q = 4 mi + ni of one K step
   auto mm1 = [&](int buf, int q) {
-    mfma_step(acc[q / kTN][q % kTN], fa[buf][q / kTN], fb[buf][q % kTN],
-              (const T*)nullptr);
+    if constexpr (kSwap)
+      mfma_step(acc[q / kTN][q % kTN], fb[buf][q % kTN], fa[buf][q / kTN],
+                (const T*)nullptr);
+    else
+      mfma_step(acc[q / kTN][q % kTN], fa[buf][q / kTN], fb[buf][q % kTN],
+                (const T*)nullptr);
   };
   auto mmr = [&](int buf, int lo, int hi) {
 #pragma unroll

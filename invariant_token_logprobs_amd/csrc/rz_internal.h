@@ -32,6 +32,7 @@ enum KernelId {
   K_TOK_SCATTER,
   K_BUCKET_SORT,
   K_DW_FIX,
+  K_TARGET_LOGIT,    // z[t, a_t] for the gather
   K_NUM_KERNELS
 };
 

@@ -20,51 +20,9 @@ namespace {
 
 constexpr float kNegInf = -__builtin_inff();
 
-// (max, sum-exp) pairs: (m1, s1) + (m2, s2) = (M, s1 e^(m1-M) + s2 e^(m2-M)),
-// M = max(m1, m2).  The two operands are first put in a canonical order
-// (larger max first, ties by larger sum), so the value is the same whichever
-// lane evaluates it and however the compiler contracts the arithmetic; the
-// tree of reduce_scatter16_ms then gives every row the same result wherever
-// it sits in the tile.  Masked columns carry m = kMaskedLogit (finite), never
-// -inf, so no (-inf) - (-inf) appears.
+// Logits of vocabulary columns >= V inside the last vocab tile: finite, so
+// the row maximum stays finite and no (-inf) - (-inf) can appear.
 constexpr float kMaskedLogit = -1.0e30f;
-
-__device__ __forceinline__ void ms_combine(float& m, float& s, float m2,
-                                           float s2) {
-  const bool sw = (m2 > m) || (m2 == m && s2 > s);
-  const float ma = sw ? m2 : m, sa = sw ? s2 : s;
-  const float mb = sw ? m : m2, sb = sw ? s : s2;
-  s = sa + sb * exp_approx(mb - ma);
-  m = ma;
-}
-
-// One halving step of the reduce-scatter, element I of HALF: written with
-// compile-time indices (template recursion, no loop variable), so the
-// lane-dependent choice between two elements stays a register select
-// instead of becoming a dynamically indexed (scratch) array access.
-template <int I, int HALF, int MASK>
-__device__ __forceinline__ void rs_elems(float (&m)[16], float (&s)[16],
-                                         bool upper) {
-  if constexpr (I < HALF) {
-    const float sm = upper ? m[I] : m[HALF + I];
-    const float ss = upper ? s[I] : s[HALF + I];
-    float km = upper ? m[HALF + I] : m[I];
-    float ks = upper ? s[HALF + I] : s[I];
-    ms_combine(km, ks, __shfl_xor(sm, MASK, 64), __shfl_xor(ss, MASK, 64));
-    m[I] = km;
-    s[I] = ks;
-    rs_elems<I + 1, HALF, MASK>(m, s, upper);
-  }
-}
-
-__device__ __forceinline__ void reduce_scatter16_ms(float (&m)[16],
-                                                    float (&s)[16], int lane) {
-  rs_elems<0, 8, 16>(m, s, (lane & 16) != 0);
-  rs_elems<0, 4, 8>(m, s, (lane & 8) != 0);
-  rs_elems<0, 2, 4>(m, s, (lane & 4) != 0);
-  rs_elems<0, 1, 2>(m, s, (lane & 2) != 0);
-  ms_combine(m[0], s[0], __shfl_xor(m[0], 1, 64), __shfl_xor(s[0], 1, 64));
-}
 
 __device__ __forceinline__ RowCount to_rc(const DevRows& r) {
   return RowCount{r.count, r.base, r.cap};
@@ -92,34 +50,49 @@ __device__ __forceinline__ T from_f(float x) {
 struct FwdArgs {
   GemmOperands op;
   DevRows rows;
-  const int* row_tokens;  // token of list position p
   int V, Vpad, nk, mt, nt;
   float2* partials;       // [nt][ldp] by list position
   int64_t ldp;
-  float* ztgt;            // [positions]
   void* e;                // learner call only: exp(z - m_tile) [rows][lde]
   int64_t lde;
 };
-
-// Staging of one 256 x 256 bf16 tile row-major in LDS for coalesced stores:
-// row R, column c at byte R * 512 + ((c / 8) ^ (R & 4)) * 16 + (c % 8) * 2.
-// The chunk swizzle puts the two rows one store instruction writes (R and
-// R + 4) into different bank groups.
-__device__ __forceinline__ int stage_off(int R, int c) {
-  return R * 512 + (((c >> 3) ^ (R & 4)) << 4) + ((c & 7) << 1);
-}
 
 // Storage type of e = exp(z - m_tile) in (0, 1]: fp16 for bf16 inputs (an
 // 11-bit significand at the same two bytes, so that e's rounding adds a
 // quarter of the bf16 rounding the dlogits already carry), fp32 otherwise.
 template <typename T> struct EStore { typedef float type; };
 template <> struct EStore<bf16> { typedef _Float16 type; };
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+template <bool B> struct BoolC { static constexpr bool value = B; };
 
+// LDS staging of a 256 x 256 fp16 e tile, 512 bytes per row, for coalesced
+// 16-byte stores.  The 16-byte chunk k of row R sits at chunk k ^ (R % 32):
+// the 8-byte writes of one instruction (32 rows, one chunk) then hit every
+// bank exactly twice, and a row read back by 32 lanes is a permutation of
+// its own 512 bytes.
+__device__ __forceinline__ int e_stage_off(int R, int k) {
+  return R * 512 + ((k ^ (R & 31)) << 4);
+}
+
+// bi_lmhead_gemm + the log-softmax statistics of one 256 x 256 logits tile
+// (vocab tile j = tn): per row t, m_tile = max_v z[t, v] and
+// s_tile = sum_v exp(z[t, v] - m_tile), written to partials[j][t]; on the
+// learner call also e = exp(z - m_tile) for the backward.
+//
+// The MFMAs run with swapped operands (see gemm_mainloop), so each lane
+// holds one row t and, per 32 x 32 block, four runs of four consecutive
+// vocabulary columns.  Row statistics are then in-lane folds over 64 values
+// per block, one exchange with lane l ^ 32 and one combine of the two
+// column-half waves through LDS, each in a fixed order that depends only on
+// the column, never on the row's position or the batch: the per-row result
+// is the same in every launch (batch invariance).  The maximum is exact in
+// any order, so it is taken first over the whole tile; one exp per element
+// then serves both s_tile and e.
 template <typename T, bool kStoreE>
 __global__ RZ_GEMM_ATTR void k_fwd_logits(FwdArgs a) {
-  // [0, 128 KB): main-loop stages, then (learner call) the e tile;
-  // then per-wave (m, s), the tile's tokens and its row maxima
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes + 6144];
+  // [0, 128 KB): main-loop stages, then (learner call, bf16) the e tile;
+  // then the per-wave row maxima and row sums [2][256] each
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes + 4096];
   const RowCount rc = to_rc(a.rows);
   const int M = rc.get();
   // Only the tiles of the M rows present are numbered (M may be a device
@@ -130,122 +103,151 @@ __global__ RZ_GEMM_ATTR void k_fwd_logits(FwdArgs a) {
   const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
 
   f32x16 acc[kTM][kTN];
-  gemm_mainloop<T>(a.op, M, m0, n0, a.nk, acc, lds);
+  gemm_mainloop<T, true>(a.op, M, m0, n0, a.nk, acc, lds);
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
-  float2* wstat = reinterpret_cast<float2*>(lds + kLdsBytes);        // [4][128]
-  int* rtok = reinterpret_cast<int*>(lds + kLdsBytes + 4096);        // [256]
-  float* rmax = reinterpret_cast<float*>(lds + kLdsBytes + 5120);    // [256]
-  {
-    const int m = m0 + tid;
-    rtok[tid] = m < M ? a.row_tokens[rc.base + m] : -1;
-  }
-  __syncthreads();
-  const int colbase = n0 + wn * 128 + (lane & 31);
-  const int half = lane >> 5;
-  const int rown = (lane & 31) >> 1;  // row owned after the reduce-scatter
-  bool cvalid[kTN];
-#pragma unroll
-  for (int ni = 0; ni < kTN; ++ni) cvalid[ni] = colbase + ni * 32 < a.V;
+  const int half = lane >> 5, l32 = lane & 31;
+  float* wmax = reinterpret_cast<float*>(lds + kLdsBytes);         // [2][256]
+  float* wsum = reinterpret_cast<float*>(lds + kLdsBytes + 2048);  // [2][256]
+  // column of register r in block ni: cbase + 32 ni + 8 (r / 4) + (r % 4)
+  const int cbase = n0 + wn * 128 + 4 * half;
 
-  // One pass over the accumulators: per row, this lane folds its 4 columns
-  // into (max, sum exp(z - max)) and stores z[a_t] if it holds column a_t;
-  // the 32 lanes of a half-wave then combine their pairs (128 columns).
+  // Tile row maxima.  Columns >= V (last vocab tile only) hold a copy of
+  // column V - 1 (the main loop reads B rows >= N from row N - 1), which
+  // cannot change a maximum, so no mask is needed here.
+  float rm[kTM];
 #pragma unroll
   for (int mi = 0; mi < kTM; ++mi) {
-    float vm[16], vs[16];
+    float mx = acc[mi][0][0];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float x[kTN];
-      float mx = kMaskedLogit;
+    for (int ni = 0; ni < kTN; ++ni)
 #pragma unroll
-      for (int ni = 0; ni < kTN; ++ni) {
-        x[ni] = cvalid[ni] ? acc[mi][ni][r] : kMaskedLogit;
-        mx = fmaxf(mx, x[ni]);
-      }
-      float sm = 0.f;
-#pragma unroll
-      for (int ni = 0; ni < kTN; ++ni) sm += exp_approx(x[ni] - mx);
-      vm[r] = mx;
-      vs[r] = sm;
-      const int row = acc_row(wm, mi, r, lane);
-      const int u = rtok[row] - colbase;
-      if (((u & 31) == 0) && ((unsigned)u < 128u)) {
-        const int ni = u >> 5;
-        a.ztgt[rc.base + m0 + row] =
-            ni == 0 ? x[0] : ni == 1 ? x[1] : ni == 2 ? x[2] : x[3];
-      }
-    }
-    reduce_scatter16_ms(vm, vs, lane);
-    if ((lane & 1) == 0) {
-      const int lrow = mi * 32 + 8 * (rown >> 2) + 4 * half + (rown & 3);
-      wstat[wid * 128 + lrow] = make_float2(vm[0], vs[0]);
-    }
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[mi][ni][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (half == 0) wmax[wn * 256 + wm * 128 + mi * 32 + l32] = mx;
   }
   __syncthreads();
-  // merge the two column halves of each row in a fixed order
+#pragma unroll
+  for (int mi = 0; mi < kTM; ++mi) {
+    const int R = wm * 128 + mi * 32 + l32;
+    rm[mi] = fmaxf(wmax[R], wmax[256 + R]);
+  }
+
+  // e = exp(z - m_tile) once per element, 0 for columns >= V; row sums in a
+  // fixed order
+  typedef typename EStore<T>::type E;
+  E* e = reinterpret_cast<E*>(a.e);
+  auto pass2 = [&](auto full_c) {
+    constexpr bool kFull = decltype(full_c)::value;
+#pragma unroll
+    for (int mi = 0; mi < kTM; ++mi) {
+      const int R = wm * 128 + mi * 32 + l32;
+      const bool rvalid = m0 + R < M;
+      float s = 0.f;
+#pragma unroll
+      for (int ni = 0; ni < kTN; ++ni)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c0 = cbase + ni * 32 + 8 * q;  // multiple of 4
+          float ev[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            ev[j] = exp_approx(acc[mi][ni][4 * q + j] - rm[mi]);
+            if constexpr (!kFull) ev[j] = c0 + j < a.V ? ev[j] : 0.f;
+            s += ev[j];
+          }
+          if constexpr (kStoreE) {
+            if constexpr (sizeof(T) == 2) {
+              const f16x4 hv = {(_Float16)ev[0], (_Float16)ev[1],
+                                (_Float16)ev[2], (_Float16)ev[3]};
+              *reinterpret_cast<u32x2*>(
+                  lds + e_stage_off(R, wn * 16 + ni * 4 + q) + half * 8) =
+                  __builtin_bit_cast(u32x2, hv);
+            } else {
+              if (rvalid && c0 < a.Vpad)
+                *reinterpret_cast<f32x4*>(e + (int64_t)(m0 + R) * a.lde + c0) =
+                    f32x4{ev[0], ev[1], ev[2], ev[3]};
+            }
+          }
+        }
+      // the wave's 128 columns: lower column half first
+      const float so = __shfl_xor(s, 32, 64);
+      if (half == 0) wsum[wn * 256 + R] = s + so;
+    }
+  };
+  if (n0 + kBN <= a.V) pass2(BoolC<true>{});
+  else pass2(BoolC<false>{});
+  __syncthreads();
   {
     const int m = m0 + tid;
-    const int w0 = (tid >> 7) * 2, lr = tid & 127;
-    const float2 p0 = wstat[w0 * 128 + lr], p1 = wstat[(w0 + 1) * 128 + lr];
-    float mm = p0.x, ss = p0.y;
-    ms_combine(mm, ss, p1.x, p1.y);
     if (m < M)
-      a.partials[(int64_t)tc.tn * a.ldp + rc.base + m] = make_float2(mm, ss);
-    rmax[tid] = mm;
+      a.partials[(int64_t)tc.tn * a.ldp + rc.base + m] =
+          make_float2(fmaxf(wmax[tid], wmax[256 + tid]), wsum[tid] + wsum[256 + tid]);
   }
-  if constexpr (kStoreE) {
-    // e = exp(z - m_tile) with the tile max just stored in the partials;
-    // the backward rescales it to dlogits once lse is known.  Zero for
-    // columns >= V and rows >= M.
-    __syncthreads();
-    typedef typename EStore<T>::type E;
-    E* e = reinterpret_cast<E*>(a.e);
-    if constexpr (sizeof(T) == 2) {
-      char* tile = lds;
-#pragma unroll
-      for (int mi = 0; mi < kTM; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < kTN; ++ni) {
-          const int lc = acc_col(wn, ni, lane);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int R = acc_row(wm, mi, r, lane);
-            const float v = (cvalid[ni] && m0 + R < M)
-                                ? exp_approx(acc[mi][ni][r] - rmax[R])
-                                : 0.f;
-            *reinterpret_cast<E*>(tile + stage_off(R, lc)) = (E)v;
-          }
-        }
-      __syncthreads();
-      // 16-byte row chunks: 32 lanes cover one 512-byte tile row
+  if constexpr (kStoreE && sizeof(T) == 2) {
+    // 16-byte row chunks: 32 lanes cover one 512-byte tile row.  Columns
+    // >= V hold 0; rows >= M and columns >= Vpad are not stored.
 #pragma unroll 4
-      for (int it = 0; it < 32; ++it) {
-        const int idx = it * 256 + tid;
-        const int R = idx >> 5, k = idx & 31;
-        const int col = n0 + k * 8;
-        if (m0 + R < M && col < a.Vpad)
-          *reinterpret_cast<u32x4*>(e + (int64_t)(m0 + R) * a.lde + col) =
-              *reinterpret_cast<const u32x4*>(tile + stage_off(R, k * 8));
-      }
-    } else {
-#pragma unroll
-      for (int mi = 0; mi < kTM; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < kTN; ++ni) {
-          const int col = colbase + ni * 32;
-          if (col >= a.Vpad) continue;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int R = acc_row(wm, mi, r, lane);
-            if (m0 + R >= M) continue;
-            e[(int64_t)(m0 + R) * a.lde + col] =
-                cvalid[ni] ? (E)exp_approx(acc[mi][ni][r] - rmax[R]) : (E)0.f;
-          }
-        }
+    for (int it = 0; it < 32; ++it) {
+      const int idx = it * 256 + tid;
+      const int R = idx >> 5, k = idx & 31;
+      const int col = n0 + k * 8;
+      if (m0 + R < M && col < a.Vpad)
+        *reinterpret_cast<u32x4*>(e + (int64_t)(m0 + R) * a.lde + col) =
+            *reinterpret_cast<const u32x4*>(lds + e_stage_off(R, k));
     }
   }
+}
+
+// z[t, a_t] = <hidden[t], W[a_t]> for every listed row: one wave per row,
+// lane l folding 16-byte chunks l, l + 64, ... in ascending order (fp32
+// FMA), then a fixed xor butterfly across the wave.  Per-row work in a fixed
+// order, so the value does not depend on the batch.  Rows with a token
+// outside [0, V) are skipped (the merge flags them and writes NaN).
+template <typename T>
+__global__ __launch_bounds__(256) void k_target_logit(
+    const char* __restrict__ hidden, int64_t lda, const int* __restrict__ a_rows,
+    DevRows rows, const char* __restrict__ lm_head, int H, int V,
+    const int* __restrict__ row_tokens, float* __restrict__ ztgt) {
+  const RowCount rc = to_rc(rows);
+  const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (p >= rc.get()) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t pos = rc.base + p;
+  const int tok = row_tokens[pos];
+  if (tok < 0 || tok >= V) return;
+  const int64_t hrow = a_rows ? (int64_t)a_rows[pos] : pos;
+  const char* hp = hidden + hrow * lda;
+  const char* wp = lm_head + (int64_t)tok * H * (int64_t)sizeof(T);
+  const int nch = H * (int)sizeof(T) / 16;
+  float acc = 0.f;
+  for (int c = lane; c < nch; c += 64) {
+    const u32x4 hv = *reinterpret_cast<const u32x4*>(hp + (int64_t)c * 16);
+    const u32x4 wv = *reinterpret_cast<const u32x4*>(wp + (int64_t)c * 16);
+    // whole-vector bit casts only: casting single vector elements is
+    // miscompiled by this toolchain
+    if constexpr (sizeof(T) == 2) {
+      const u32x4 hi_mask = {0xffff0000u, 0xffff0000u, 0xffff0000u, 0xffff0000u};
+      const f32x4 hl = __builtin_bit_cast(f32x4, hv << 16);
+      const f32x4 wl = __builtin_bit_cast(f32x4, wv << 16);
+      const f32x4 hh = __builtin_bit_cast(f32x4, hv & hi_mask);
+      const f32x4 wh = __builtin_bit_cast(f32x4, wv & hi_mask);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc = fmaf(hl[j], wl[j], acc);   // element 2 j
+        acc = fmaf(hh[j], wh[j], acc);   // element 2 j + 1
+      }
+    } else {
+      const f32x4 hf = __builtin_bit_cast(f32x4, hv);
+      const f32x4 wf = __builtin_bit_cast(f32x4, wv);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc = fmaf(hf[j], wf[j], acc);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  if (lane == 0) ztgt[pos] = acc;
 }
 
 // ===================================================================
@@ -928,7 +930,8 @@ const char* kernel_name(int k) {
       "coef",        "dz_scale",    "resp_sums",    "loss_value",
       "diag_partial", "diag_final", "transpose_w",  "transpose_h",
       "bwd_dh_gemm", "bwd_dw_gemm", "fill",         "tok_hist",
-      "scan",        "tok_scatter", "bucket_sort",  "dw_fix"};
+      "scan",        "tok_scatter", "bucket_sort",  "dw_fix",
+      "target_logit"};
   return (k >= 0 && k < K_NUM_KERNELS) ? names[k] : "?";
 }
 
@@ -938,11 +941,21 @@ hipError_t launch_fwd_logits(int dt, const void* hidden, int64_t lda_bytes,
                              const int* row_tokens, float2* partials,
                              int64_t ldp, float* ztgt, void* e, int64_t lde,
                              int Vpad, hipStream_t s) {
+  hipError_t err = timed(K_TARGET_LOGIT, s, [&] {
+    if (dt)
+      k_target_logit<bf16><<<cdiv(rows.cap, 4), 256, 0, s>>>(
+          (const char*)hidden, lda_bytes, a_rows, rows, (const char*)lm_head,
+          H, V, row_tokens, ztgt);
+    else
+      k_target_logit<float><<<cdiv(rows.cap, 4), 256, 0, s>>>(
+          (const char*)hidden, lda_bytes, a_rows, rows, (const char*)lm_head,
+          H, V, row_tokens, ztgt);
+  });
+  if (err != hipSuccess) return err;
   FwdArgs a;
   a.op = GemmOperands{(const char*)hidden, lda_bytes, a_rows, rows.base,
                       (const char*)lm_head, (int64_t)H * (dt ? 2 : 4), V};
   a.rows = rows;
-  a.row_tokens = row_tokens;
   a.V = V;
   a.Vpad = Vpad;
   a.nk = H / (dt ? Stage<bf16>::kK : Stage<float>::kK);
@@ -950,7 +963,6 @@ hipError_t launch_fwd_logits(int dt, const void* hidden, int64_t lda_bytes,
   a.nt = cdiv(V, kBN);
   a.partials = partials;
   a.ldp = ldp;
-  a.ztgt = ztgt;
   a.e = e;
   a.lde = lde;
   const int nblk = a.mt * a.nt;
