@@ -644,8 +644,14 @@ __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ in,
 // softmax part of dL/dz (the one-hot part -c_t [v == a_t] is applied exactly
 // in fp32 by the dHidden epilogue and the dW fix-up).  The kernel rescales
 // e in place into the token-major dz [C, Vpad] (A operand of dHidden) and
-// writes the vocab-major dz^T [Vpad, C] (A operand of dW) through an LDS
-// transpose.  Rows at or past the chunk's count become zero columns of dz^T.
+// writes the vocab-major dz^T [Vpad, C] (A operand of dW).  Rows at or past
+// the chunk's count become zero columns of dz^T.
+//
+// Each lane owns a kVec x kVec block (kVec = values per 16 bytes): it reads
+// kVec 16-byte row pieces, writes them back rescaled, transposes the block
+// in registers and writes kVec 16-byte column pieces.  Lanes are laid out so
+// that eight of them (bf16) cover one 128-byte line of a dz row and of a
+// dz^T row alike; no LDS round trip.
 // ===================================================================
 template <typename T>
 __global__ __launch_bounds__(256) void k_dz_scale(
@@ -653,15 +659,18 @@ __global__ __launch_bounds__(256) void k_dz_scale(
     DevRows rows, const float2* __restrict__ partials, int64_t ldp,
     const float* __restrict__ lse, const float* __restrict__ coef, int Vpad) {
   typedef typename EStore<T>::type E;
-  constexpr int kVec = 16 / (int)sizeof(T);           // values per 16 bytes
-  constexpr int kRowChunks = kBN / kVec;              // 16-byte chunks per row
-  __shared__ __attribute__((aligned(16))) T tile[64][kBN + 8];
+  constexpr int kVec = 16 / (int)sizeof(T);       // 8 (bf16) or 4 (fp32)
+  constexpr int kG = 64 / kVec;                   // row blocks per wave
+  constexpr int kWaveCols = (64 / kG) * kVec;     // 64 (bf16) or 16 (fp32)
+  constexpr int kBlockCols = 4 * kWaveCols;       // within one vocab tile
   __shared__ float sc[64];
   const RowCount rc = to_rc(rows);
   const int R = rc.get();
-  const int r0 = blockIdx.x * 64, j = blockIdx.y, c0 = j * kBN;
+  const int r0 = blockIdx.x * 64;
   if (r0 >= ((R + 63) & ~63)) return;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int cblk = blockIdx.y * kBlockCols;
+  const int j = cblk / kBN;
   // one scale per row of this vocab tile: c_t exp(m_tile(t, j) - lse_t)
   if (tid < 64) {
     const int t = r0 + tid;
@@ -673,35 +682,61 @@ __global__ __launch_bounds__(256) void k_dz_scale(
     sc[tid] = v;
   }
   __syncthreads();
-  // rescale e -> dz in place, 16 bytes at a time; rows at or past R are zero
-  for (int c = tid; c < 64 * kRowChunks; c += 256) {
-    const int rr = c / kRowChunks, k = c % kRowChunks;
-    const int t = r0 + rr, col = c0 + k * kVec;
-    T y[kVec];
-    if (t < R && col < Vpad) {
-      T* p = dz + (int64_t)t * ldz + col;
-      E x[kVec];
-      *reinterpret_cast<u32x4*>(x) = *reinterpret_cast<const u32x4*>(p);
+  const int cw = cblk + wid * kWaveCols;
+  if (cw >= Vpad) return;  // Vpad is a multiple of 64: whole waves drop out
+  const int tr = (lane % kG) * kVec;             // first row of the block
+  const int col = cw + (lane / kG) * kVec;       // first column
+  if constexpr (sizeof(T) == 2) {
+    uint32_t y[8][4];  // y[i]: row tr + i, columns col .. col + 7 (bf16 pairs)
 #pragma unroll
-      for (int q = 0; q < kVec; ++q) y[q] = (T)(sc[rr] * (float)x[q]);
-      *reinterpret_cast<u32x4*>(p) = *reinterpret_cast<const u32x4*>(y);
-    } else {
+    for (int i = 0; i < 8; ++i) {
+      const int t = r0 + tr + i;
+      if (t < R) {
+        T* p = dz + (int64_t)t * ldz + col;
+        typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+        const f16x8 x = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(p));
+        const float f = sc[tr + i];
 #pragma unroll
-      for (int q = 0; q < kVec; ++q) y[q] = (T)0.f;
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t lo = __builtin_bit_cast(uint16_t, (T)(f * (float)x[2 * w]));
+          const uint32_t hi = __builtin_bit_cast(uint16_t, (T)(f * (float)x[2 * w + 1]));
+          y[i][w] = lo | (hi << 16);
+        }
+        *reinterpret_cast<u32x4*>(p) = u32x4{y[i][0], y[i][1], y[i][2], y[i][3]};
+      } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) y[i][w] = 0u;
+      }
     }
-    *reinterpret_cast<u32x4*>(&tile[rr][k * kVec]) = *reinterpret_cast<const u32x4*>(y);
-  }
-  __syncthreads();
-  // dz^T: each 16-byte chunk holds kVec consecutive tokens of one vocab
-  // column; lanes walk consecutive columns (conflict-free LDS reads)
-  for (int c = tid; c < kBN * (64 / kVec); c += 256) {
-    const int v = c % kBN, tq = c / kBN;
-    if (c0 + v >= Vpad) continue;
-    T y[kVec];
+    // column q of the block: rows tr .. tr + 7 of vocab column col + q
 #pragma unroll
-    for (int q = 0; q < kVec; ++q) y[q] = tile[tq * kVec + q][v];
-    *reinterpret_cast<u32x4*>(dzT + (int64_t)(c0 + v) * ldzt + r0 + tq * kVec) =
-        *reinterpret_cast<const u32x4*>(y);
+    for (int q = 0; q < 8; ++q) {
+      const int sh = (q & 1) * 16;
+      uint32_t o[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        o[w] = ((y[2 * w][q >> 1] >> sh) & 0xffffu) |
+               (((y[2 * w + 1][q >> 1] >> sh) & 0xffffu) << 16);
+      *reinterpret_cast<u32x4*>(dzT + (int64_t)(col + q) * ldzt + r0 + tr) =
+          u32x4{o[0], o[1], o[2], o[3]};
+    }
+  } else {
+    f32x4 y[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = r0 + tr + i;
+      if (t < R) {
+        T* p = dz + (int64_t)t * ldz + col;
+        y[i] = sc[tr + i] * *reinterpret_cast<const f32x4*>(p);
+        *reinterpret_cast<f32x4*>(p) = y[i];
+      } else {
+        y[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<f32x4*>(dzT + (int64_t)(col + q) * ldzt + r0 + tr) =
+          f32x4{y[0][q], y[1][q], y[2][q], y[3][q]};
   }
 }
 
@@ -1100,7 +1135,8 @@ hipError_t launch_dz_scale(int dt, void* dz, int64_t ldz, void* dzT,
                            int64_t ldzt, DevRows rows, const float2* partials,
                            int64_t ldp, const float* lse, const float* coef,
                            int Vpad, hipStream_t s) {
-  dim3 grid(cdiv(rows.cap, 64), cdiv(Vpad, kBN));
+  // 64 rows x (4 waves x 64 bf16 or 16 fp32 columns) per workgroup
+  dim3 grid(cdiv(rows.cap, 64), cdiv(Vpad, dt ? 256 : 64));
   return timed(K_DZ_SCALE, s, [&] {
     if (dt)
       k_dz_scale<bf16><<<grid, 256, 0, s>>>((bf16*)dz, ldz, (bf16*)dzT, ldzt,
