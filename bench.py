@@ -26,6 +26,33 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA
 HBM_GBS = 8000.0
 GEMM_KERNELS = ("fwd_logits_gemm", "bwd_dh_gemm", "bwd_dw_gemm")
 
+# HBM bytes per launch of the GEMM kernels at the Qwen3-4B tool-use shape,
+# from two rocprofv3 counter runs of this script (FETCH_SIZE x 2.0 and
+# WRITE_SIZE x 1.0, the factors a plain 1 GiB copy reads on the same
+# counters), averaged over one step's chunk launches.  Valid only for the
+# kernel sources they were taken from.  Derivation and commands:
+# profiles/gemm_traffic_qwen3_4b_tool.md.
+COUNTER_TRAFFIC = {
+    "workload": "qwen3_4b_tool",
+    "sources_sha256": "0ce813f05ad5efe3f36ebda50dd4228629fed38fe114fc36cbbd412cf766490c",
+    "bytes_per_launch": {"fwd_logits_gemm": 29643375790,
+                         "bwd_dh_gemm": 25122281172,
+                         "bwd_dw_gemm": 32028791703},
+}
+
+
+def kernel_sources_sha256():
+    """Fingerprint of the HIP sources; counter figures taken from an older
+    build of the kernels no longer describe them."""
+    import hashlib
+    d = os.path.join(ROOT, "invariant_token_logprobs_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
@@ -155,9 +182,15 @@ def main():
     avg_ms = tot_ms / launches
     flop_per_launch = 2.0 * b.H * b.V * nv * args.steps / launches
     achieved = flop_per_launch / (avg_ms * 1e-3) / 1e12
+    traffic = None
+    if (b.name == COUNTER_TRAFFIC["workload"]
+            and kernel_sources_sha256() == COUNTER_TRAFFIC["sources_sha256"]):
+        traffic = COUNTER_TRAFFIC["bytes_per_launch"].get(dom)
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": None, "avg_launch_ms": round(avg_ms, 4),
+                "traffic": traffic,
+                "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                "avg_launch_ms": round(avg_ms, 4),
                 "launches_per_step": launches // args.steps}
     log("per-step kernel ms: " + ", ".join(f"{k}={v:.2f}" for k, v in
                                             sorted(kms.items(), key=lambda x: -x[1])))
