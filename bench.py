@@ -111,7 +111,7 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="qwen3_4b_tool")
-    ap.add_argument("--cpu-valid", type=int, default=1024,
+    ap.add_argument("--cpu-valid", type=int, default=3072,
                     help="valid rows in the oracle's CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -157,12 +157,17 @@ def main():
 
     rz.timing_enable(True)
     rz.timing_read(reset=True)
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     ts = time.perf_counter()
-    for _ in range(args.steps):
+    evs[0].record(stream)
+    for i in range(args.steps):
         step()
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     te = time.perf_counter()
+    step_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
     kt = rz.timing_read(reset=True)
     rz.timing_enable(False)
     loss = float(outs["loss"].cpu()[0])
@@ -217,6 +222,9 @@ def main():
         "config": {"workload": b.name, "hidden": b.H, "vocab": b.V,
                    "responses": b.B, "rows": b.N, "valid_tokens": nv,
                    "masked_frac": round(1 - nv / b.N, 4), "lag_sigma": b.sigma},
+        "rows_per_s": round(b.N * args.steps / (te - ts), 1),
+        "step_ms_median": round(float(np.median(step_ms)), 3),
+        "step_ms_min": round(float(np.min(step_ms)), 3),
         "mfma_peak_frac_algorithmic": round(mfma_frac, 4),
         "executed_flop_per_valid_token": 6.0 * b.H * b.V,
         "roofline": roofline,
