@@ -116,7 +116,9 @@ size_t carve_fb(Carver& c, int64_t n, int32_t B, int32_t H, int32_t V,
   t.WT = c.take<char>(es * (size_t)H * (size_t)Vpad);
   t.hT = c.take<char>(es * (size_t)H * (size_t)C);
   t.dz = c.take<char>(es * (size_t)C * (size_t)Vpad);
-  t.dzT = c.take<char>(es * (size_t)Vpad * (size_t)C);
+  // dz^T only for fp32 (bf16 dW reads dz through transposing LDS reads)
+  t.dzT = dt == RZ_DTYPE_F32 ? c.take<char>(es * (size_t)Vpad * (size_t)C)
+                             : nullptr;
   t.counts = c.take<int>(sizeof(int) * (size_t)V);
   t.cursor = c.take<int>(sizeof(int) * (size_t)V);
   t.offsets = c.take<int>(sizeof(int) * ((size_t)V + 1));
@@ -330,8 +332,10 @@ rz_status rz_reinforce_zero_fwd_bwd(
       RZ_TRY(launch_bwd_dh(dt, w.dz, Vpad, crow, w.WT, Vpad, H, V, Vpad,
                            w.idx, w.tokv, w.coef, lm_head, d_hidden, s));
     }
-    RZ_TRY(launch_bwd_dw(dt, w.dzT, C, N > 0 ? crow : DevRows{nullptr, 0, 0},
-                         w.hT, C, H, V, d_lm_head, k == 0, s));
+    const bool kmaj = dt == RZ_DTYPE_BF16;
+    RZ_TRY(launch_bwd_dw(dt, kmaj ? w.dz : w.dzT, kmaj ? Vpad : C,
+                         N > 0 ? crow : DevRows{nullptr, 0, 0}, w.hT, C, H, V,
+                         Vpad, d_lm_head, k == 0, s));
   }
   if (N > 0) RZ_TRY(launch_rows_finalize(mask, N, H, logprobs, d_hidden, s));
   // a5: S_i from this call's logprobs, then L

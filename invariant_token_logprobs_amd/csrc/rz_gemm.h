@@ -137,16 +137,23 @@ struct GemmOperands {
 // every load stays in bounds; their results are discarded by the epilogue.
 // Leaves the LDS free (all waves past the last barrier) on return.
 //
+// kTransA = true (16-bit values only) takes A stored K-major instead:
+// A[m, k] at A + k * lda + 2 m, i.e. rows of the memory matrix are K and
+// M is contiguous.  A stage is then 64 K-rows x 512 bytes in LDS, and the
+// MFMA fragments come out of gfx950's transposing LDS read
+// (ds_read_b64_tr_b16, see lread), so no transposed copy of A is needed.
+//
 // kSwap = true issues each MFMA with the operands exchanged, which computes
 // the same products but leaves the transposed block in the accumulators:
 // lane l then holds row l % 32 of its 32 x 32 block (an A row) and registers
 // r hold columns 8 (r / 4) + 4 (l / 32) + (r % 4), i.e. every lane owns
 // four runs of four consecutive B rows of one A row.
-template <typename T, bool kSwap = false>
+template <typename T, bool kSwap = false, bool kTransA = false>
 __device__ __forceinline__ void gemm_mainloop(const GemmOperands& op, int M,
                                               int m0, int n0, int nk,
                                               f32x16 (&acc)[kTM][kTN],
                                               char* lds) {
+  static_assert(!kTransA || sizeof(T) == 2, "K-major A needs 16-bit values");
   const int tid = threadIdx.x;
   const int lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
@@ -191,9 +198,22 @@ __device__ __forceinline__ void gemm_mainloop(const GemmOperands& op, int M,
     const int c = (lane & 7) ^ swz(r);
     int m = m0 + r;
     m = m < M ? m : M - 1;
-    const int64_t prow = op.a_rows ? (int64_t)op.a_rows[op.a_base + m]
-                                   : op.a_base + m;
-    ga[i] = op.A + prow * op.lda + c * 16;
+    if constexpr (kTransA) {
+      // K-major A: instruction i of wave wu fills K-rows 2 (8 wu + i) and
+      // 2 (8 wu + i) + 1 of the stage (512 bytes each, lane / 32 picks the
+      // row); lane % 32 is the physical 16-byte chunk, which holds logical
+      // chunk (lane % 32) ^ 4 (row % 4), i.e. columns m0 + 8 chunk .. + 7.
+      // Columns past M - 8 read the last 8 (discarded by the epilogue).
+      const int kr = 2 * (wu * 8 + i) + (lane >> 5);
+      const int lc = (lane & 31) ^ (4 * (kr & 3));
+      int mm = m0 + 8 * lc;
+      mm = mm <= M - 8 ? mm : M - 8;
+      ga[i] = op.A + (int64_t)kr * op.lda + (int64_t)mm * 2;
+    } else {
+      const int64_t prow = op.a_rows ? (int64_t)op.a_rows[op.a_base + m]
+                                     : op.a_base + m;
+      ga[i] = op.A + prow * op.lda + c * 16;
+    }
     int n = n0 + r;
     n = n < op.N ? n : op.N - 1;
     gb[i] = op.B + (int64_t)n * op.ldb + c * 16;
@@ -202,9 +222,11 @@ __device__ __forceinline__ void gemm_mainloop(const GemmOperands& op, int M,
   // j >= 8 the same rows of B
   auto dma1 = [&](int kt, int stage, int j) {
     const int64_t k = (int64_t)kt * kRowBytes;
+    // a K-major A stage advances by 64 rows, a K-contiguous one by 128 bytes
+    const int64_t ka = kTransA ? (int64_t)kt * 64 * op.lda : k;
     char* sa = lds + stage * kStageBytes + wu * 64 * kRowBytes;
     if (j < 8)
-      __builtin_amdgcn_global_load_lds(ga[j] + k,
+      __builtin_amdgcn_global_load_lds(ga[j] + ka,
                                        (lds_ptr_t)(sa + j * 8 * kRowBytes), 16,
                                        0, 0);
     else
@@ -212,14 +234,57 @@ __device__ __forceinline__ void gemm_mainloop(const GemmOperands& op, int M,
           gb[j - 8] + k,
           (lds_ptr_t)(sa + kOperandBytes + (j - 8) * 8 * kRowBytes), 16, 0, 0);
   };
+  // K-major A: ds_read_b64_tr_b16 works on groups of 16 lanes; lane q of
+  // a group names 8 bytes (4 values) at K-row q / 4 of a 4-row slab and
+  // columns 4 (q % 4) .. + 3, and lane 4 a + b of the group receives column
+  // 4 a + b of all four rows -- four consecutive K values of one M row, the
+  // MFMA A-operand layout.  Group g of the wave covers the 16 columns
+  // 16 (g % 2) .. of the 32-row block and K-rows 8 (g / 2) + 4 r .. of the
+  // step; two reads (r = 0, 1) make the 8 values of one fragment.  The
+  // XOR of the chunk with 4 (row % 4) puts the 8 rows one read touches in
+  // four different 64-byte bank groups (two rows each, the minimum for
+  // 512 bytes).
+  int a_tr[kTM][2];
+  if constexpr (kTransA) {
+    const int g = lane >> 4, q = lane & 15;
+    const int X = 4 * (q >> 2);
+#pragma unroll
+    for (int mi = 0; mi < kTM; ++mi)
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int kq = 8 * (g >> 1) + 4 * r + (q >> 2);
+        const int mloc = wm * 128 + mi * 32 + 16 * (g & 1) + 4 * (q & 3);
+        a_tr[mi][r] = kq * 512 + (((mloc >> 3) ^ X) << 4) + (mloc & 7) * 2;
+      }
+  }
+  typedef __attribute__((address_space(3))) const char* lds_cptr_t;
   // fragments of two consecutive 16-byte K steps (register double buffer)
   u32x4 fa[2][kTM], fb[2][kTN];
   auto lread = [&](int buf, int stage, int s) {
     const char* sa = lds + stage * kStageBytes;
     const char* sb = sa + kOperandBytes;
+    if constexpr (kTransA) {
+      // Issued by hand: the compiler waits for every outstanding LDS-DMA
+      // load (vmcnt(0)) before its own form of this read.  The B reads
+      // below are issued after these ("memory" keeps them there) and LDS
+      // reads retire in order, so the lgkmcnt wait the compiler places
+      // before the first MFMA that uses B also covers these.
 #pragma unroll
-    for (int mi = 0; mi < kTM; ++mi)
-      fa[buf][mi] = *reinterpret_cast<const u32x4*>(sa + a_off[mi] + c_off[s]);
+      for (int mi = 0; mi < kTM; ++mi) {
+        const uint32_t p0 = (uint32_t)(uintptr_t)(lds_cptr_t)(sa + a_tr[mi][0]);
+        const uint32_t p1 = (uint32_t)(uintptr_t)(lds_cptr_t)(sa + a_tr[mi][1]);
+        u32x2 lo, hi;
+        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                     : "=v"(lo) : "v"(p0), "i"(s * 8192) : "memory");
+        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                     : "=v"(hi) : "v"(p1), "i"(s * 8192) : "memory");
+        fa[buf][mi] = u32x4{lo.x, lo.y, hi.x, hi.y};
+      }
+    } else {
+#pragma unroll
+      for (int mi = 0; mi < kTM; ++mi)
+        fa[buf][mi] = *reinterpret_cast<const u32x4*>(sa + a_off[mi] + c_off[s]);
+    }
 #pragma unroll
     for (int ni = 0; ni < kTN; ++ni)
       fb[buf][ni] = *reinterpret_cast<const u32x4*>(sb + b_off[ni] + c_off[s]);

@@ -99,8 +99,10 @@ hipError_t launch_bwd_dh(int dt, const void* dz, int64_t ldz, DevRows rows,
                          const void* WT, int64_t ldwt, int H, int V, int Vpad,
                          const int* idx, const int* tokv, const float* coef,
                          const void* lm_head, float* d_hidden, hipStream_t s);
-hipError_t launch_bwd_dw(int dt, const void* dzT, int64_t ldzt, DevRows krows,
-                         const void* hT, int64_t ldht, int H, int V,
+// bf16: dz = dz [C][Vpad] (ld = Vpad), read K-major; fp32: dz = dz^T
+// [Vpad][C] (ld = C)
+hipError_t launch_bwd_dw(int dt, const void* dz, int64_t ld, DevRows krows,
+                         const void* hT, int64_t ldht, int H, int V, int Vpad,
                          float* d_lm_head, int first, hipStream_t s);
 hipError_t launch_dw_fix(int dt, const int* nvalid, int64_t cap,
                          const int* tokv, const int* idx, const float* coef,

@@ -643,15 +643,17 @@ __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ in,
 // lse_t known, dz[t, v] = c_t * exp(m_tile(t, j) - lse_t) * e[t, v] is the
 // softmax part of dL/dz (the one-hot part -c_t [v == a_t] is applied exactly
 // in fp32 by the dHidden epilogue and the dW fix-up).  The kernel rescales
-// e in place into the token-major dz [C, Vpad] (A operand of dHidden) and
-// writes the vocab-major dz^T [Vpad, C] (A operand of dW).  Rows at or past
-// the chunk's count become zero columns of dz^T.
+// e in place into the token-major dz [C, Vpad], the A operand of dHidden and
+// (bf16, read K-major) of dW.  fp32 has no transposing LDS read, so there
+// the kernel also writes the vocab-major dz^T [Vpad, C] for dW.  Rows from
+// the chunk's count up to the next multiple of 64 (the last K stage of dW)
+// become zero rows of dz (bf16) or zero columns of dz^T (fp32).
 //
 // Each lane owns a kVec x kVec block (kVec = values per 16 bytes): it reads
-// kVec 16-byte row pieces, writes them back rescaled, transposes the block
-// in registers and writes kVec 16-byte column pieces.  Lanes are laid out so
-// that eight of them (bf16) cover one 128-byte line of a dz row and of a
-// dz^T row alike; no LDS round trip.
+// kVec 16-byte row pieces and writes them back rescaled; for fp32 it then
+// transposes the block in registers and writes kVec 16-byte column pieces
+// of dz^T.  Eight lanes (bf16) cover one 128-byte line of a dz row; no LDS
+// round trip.
 // ===================================================================
 template <typename T>
 __global__ __launch_bounds__(256) void k_dz_scale(
@@ -704,21 +706,8 @@ __global__ __launch_bounds__(256) void k_dz_scale(
         }
         *reinterpret_cast<u32x4*>(p) = u32x4{y[i][0], y[i][1], y[i][2], y[i][3]};
       } else {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) y[i][w] = 0u;
+        *reinterpret_cast<u32x4*>(dz + (int64_t)t * ldz + col) = u32x4{0u, 0u, 0u, 0u};
       }
-    }
-    // column q of the block: rows tr .. tr + 7 of vocab column col + q
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int sh = (q & 1) * 16;
-      uint32_t o[4];
-#pragma unroll
-      for (int w = 0; w < 4; ++w)
-        o[w] = ((y[2 * w][q >> 1] >> sh) & 0xffffu) |
-               (((y[2 * w + 1][q >> 1] >> sh) & 0xffffu) << 16);
-      *reinterpret_cast<u32x4*>(dzT + (int64_t)(col + q) * ldzt + r0 + tr) =
-          u32x4{o[0], o[1], o[2], o[3]};
     }
   } else {
     f32x4 y[4];
@@ -807,9 +796,9 @@ __global__ RZ_GEMM_ATTR void k_bwd_dh(DhArgs<T> a) {
 // order); chunks are accumulated in order, the first one overwrites.
 // ===================================================================
 struct DwArgs {
-  GemmOperands op;
+  GemmOperands op;  // bf16: A = dz [K rows][Vpad], K-major; fp32: A = dz^T
   DevRows krows;
-  int V, H, kstage, mt, nt, first;
+  int V, H, amax, kstage, mt, nt, first;  // amax: A columns (bf16) / rows
   float* dw;
 };
 
@@ -823,7 +812,9 @@ __global__ RZ_GEMM_ATTR void k_bwd_dw(DwArgs a) {
   const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
 
   f32x16 acc[kTM][kTN];
-  gemm_mainloop<T>(a.op, a.V, m0, n0, nk, acc, lds);
+  // bf16 reads dz itself through transposing LDS reads; fp32 has no such
+  // read and takes the transposed copy dz^T
+  gemm_mainloop<T, false, sizeof(T) == 2>(a.op, a.amax, m0, n0, nk, acc, lds);
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
@@ -1185,16 +1176,17 @@ hipError_t launch_bwd_dh(int dt, const void* dz, int64_t ldz, DevRows rows,
                                      tokv, coef, lm_head, d_hidden, s);
 }
 
-hipError_t launch_bwd_dw(int dt, const void* dzT, int64_t ldzt, DevRows krows,
-                         const void* hT, int64_t ldht, int H, int V,
+hipError_t launch_bwd_dw(int dt, const void* dz, int64_t ld, DevRows krows,
+                         const void* hT, int64_t ldht, int H, int V, int Vpad,
                          float* d_lm_head, int first, hipStream_t s) {
   const int esz = dt ? 2 : 4;
   DwArgs a;
-  a.op = GemmOperands{(const char*)dzT, ldzt * esz, nullptr, 0,
+  a.op = GemmOperands{(const char*)dz, ld * esz, nullptr, 0,
                       (const char*)hT, ldht * esz, H};
   a.krows = krows;
   a.V = V;
   a.H = H;
+  a.amax = dt ? Vpad : V;
   a.kstage = dt ? Stage<bf16>::kK : Stage<float>::kK;
   a.mt = cdiv(V, kBM);
   a.nt = cdiv(H, kBN);
