@@ -34,10 +34,10 @@ GEMM_KERNELS = ("fwd_logits_gemm", "bwd_dh_gemm", "bwd_dw_gemm")
 # profiles/gemm_traffic_qwen3_4b_tool.md.
 COUNTER_TRAFFIC = {
     "workload": "qwen3_4b_tool",
-    "sources_sha256": "0ce813f05ad5efe3f36ebda50dd4228629fed38fe114fc36cbbd412cf766490c",
-    "bytes_per_launch": {"fwd_logits_gemm": 29643375790,
-                         "bwd_dh_gemm": 25122281172,
-                         "bwd_dw_gemm": 32028791703},
+    "sources_sha256": "69a51442f59aac74a9b52984e2b9a7bbc22111ccfaa555db3f977d159e6787ca",
+    "bytes_per_launch": {"fwd_logits_gemm": 28401980603,
+                         "bwd_dh_gemm": 24612960644,
+                         "bwd_dw_gemm": 28300835319},
 }
 
 
