@@ -144,6 +144,8 @@ __global__ RZ_GEMM_ATTR void k_fwd_logits(FwdArgs a) {
     for (int mi = 0; mi < kTM; ++mi) {
       const int R = wm * 128 + mi * 32 + l32;
       const bool rvalid = m0 + R < M;
+      // exp(z - m) = 2^(z log2 e - m log2 e): one FMA per element
+      const float nm = -rm[mi] * kLog2e;
       float s = 0.f;
 #pragma unroll
       for (int ni = 0; ni < kTN; ++ni)
@@ -153,7 +155,7 @@ __global__ RZ_GEMM_ATTR void k_fwd_logits(FwdArgs a) {
           float ev[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            ev[j] = exp_approx(acc[mi][ni][4 * q + j] - rm[mi]);
+            ev[j] = __builtin_amdgcn_exp2f(fmaf(acc[mi][ni][4 * q + j], kLog2e, nm));
             if constexpr (!kFull) ev[j] = c0 + j < a.V ? ev[j] : 0.f;
             s += ev[j];
           }
@@ -251,28 +253,47 @@ __global__ __launch_bounds__(256) void k_target_logit(
 }
 
 // ===================================================================
-// bi_logsoftmax_gather merge: per row, fold the vocab-tile partials in
-// ascending tile order, (m, s) <- (m', s e^(m - m') + s_j e^(m_j - m')),
-// then lse = m + log s and log pi = z[a_t] - lse.  The fold order depends
-// only on V, never on the number of rows.
+// bi_logsoftmax_gather merge: per row, eight lanes fold the vocab-tile
+// partials, lane q the tiles q, q + 8, q + 16, ... in ascending order, with
+// (m, s) <- (m', s e^(m - m') + s_j e^(m_j - m')); the eight pairs are then
+// folded the same way in the order q = 0 .. 7.  lse = m + log s and
+// log pi = z[a_t] - lse.  The fold order depends only on V, never on the
+// number of rows or the row's position.
 // ===================================================================
+__device__ __forceinline__ void ms_fold(float& m, float& s, float mj,
+                                        float sj) {
+  const float mn = fmaxf(m, mj);
+  s = s * exp_approx(m - mn) + sj * exp_approx(mj - mn);
+  m = mn;
+}
+
 __global__ __launch_bounds__(256) void k_lse_merge(
     const float2* __restrict__ partials, int64_t ldp, int nt, DevRows rows,
     const float* __restrict__ ztgt, const int* __restrict__ row_tokens, int V,
     float* lse_out, float* logpi_out, const int* scatter_idx,
     float* logprobs_rows, int* err) {
   const RowCount rc = to_rc(rows);
-  const int p = blockIdx.x * 256 + threadIdx.x;
-  if (p >= rc.get()) return;
-  const int64_t pos = rc.base + p;
+  const int p = blockIdx.x * 32 + (threadIdx.x >> 3);
+  const int q = threadIdx.x & 7;
+  // every lane of a row's group of eight stays to the shuffles
+  const bool live = p < rc.get();
+  const int64_t pos = rc.base + (live ? p : 0);
   float m = kNegInf, s = 0.f;
-  for (int t = 0; t < nt; ++t) {
-    const float2 ms = partials[(int64_t)t * ldp + pos];
-    const float mn = fmaxf(m, ms.x);
-    s = s * exp_approx(m - mn) + ms.y * exp_approx(ms.x - mn);
-    m = mn;
+  if (live)
+    for (int t = q; t < nt; t += 8) {
+      const float2 ms = partials[(int64_t)t * ldp + pos];
+      ms_fold(m, s, ms.x, ms.y);
+    }
+  float M = kNegInf, S = 0.f;
+  const int g0 = threadIdx.x & ~7;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float mj = __shfl(m, g0 + j, 64);
+    const float sj = __shfl(s, g0 + j, 64);
+    if (mj != kNegInf) ms_fold(M, S, mj, sj);  // lanes with no tile hold (-inf, 0)
   }
-  const float lse = m + logf(s);
+  if (!live || q != 0) return;
+  const float lse = M + logf(S);
   const int tok = row_tokens[pos];
   float lp;
   if (tok >= 0 && tok < V) {
@@ -607,8 +628,14 @@ __global__ __launch_bounds__(256) void k_diag_final(const DiagPartial* in,
 
 // ===================================================================
 // Transposes feeding the backward GEMMs their K-contiguous operands:
-// out[c, r] = in[row(r), c] for r < rows, 0 for rows <= r < rows_pad.
+// out[c, r] = in[row(r), c] for r < rows, and 0 for rows <= r < the row
+// count rounded up to 64 (the last K stage a GEMM reads; never past
+// rows_pad).
 // ===================================================================
+// Each lane moves a kVec x kVec block (kVec = values per 16 bytes): kVec
+// 16-byte row pieces in, a transpose in registers, kVec 16-byte column
+// pieces out.  Eight lanes (bf16) cover one 128-byte line on either side.
+// rows_pad and cols are multiples of 64.
 template <typename T>
 __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ in,
                                                    int64_t ld_in,
@@ -616,24 +643,47 @@ __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ in,
                                                    DevRows rows, int rows_pad,
                                                    int cols, T* __restrict__ out,
                                                    int64_t ld_out) {
-  __shared__ T tile[64][65];
+  constexpr int kVec = 16 / (int)sizeof(T);       // 8 (bf16) or 4 (fp32)
+  constexpr int kG = 64 / kVec;                   // row blocks per wave
+  constexpr int kWaveCols = (64 / kG) * kVec;     // 64 (bf16) or 16 (fp32)
   const RowCount rc = to_rc(rows);
   const int R = rc.get();
-  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
-  if (r0 >= rows_pad) return;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int rr = ty; rr < 64; rr += 4) {
-    const int r = r0 + rr;
-    T val = from_f<T>(0.f);
+  const int r0 = blockIdx.x * 64;
+  if (r0 >= rows_pad || r0 >= ((R + 63) & ~63)) return;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int cw = blockIdx.y * (4 * kWaveCols) + wid * kWaveCols;
+  if (cw >= cols) return;
+  const int tr = (lane % kG) * kVec;          // first row of the block
+  const int col = cw + (lane / kG) * kVec;    // first column
+  u32x4 x[kVec];
+#pragma unroll
+  for (int i = 0; i < kVec; ++i) {
+    const int r = r0 + tr + i;
+    x[i] = u32x4{0u, 0u, 0u, 0u};
     if (r < R) {
       const int64_t pr = rowmap ? (int64_t)rowmap[rc.base + r] : rc.base + r;
-      val = in[pr * ld_in + c0 + tx];
+      x[i] = *reinterpret_cast<const u32x4*>(in + pr * ld_in + col);
     }
-    tile[rr][tx] = val;
   }
-  __syncthreads();
-  for (int cc = ty; cc < 64; cc += 4)
-    if (c0 + cc < cols) out[(int64_t)(c0 + cc) * ld_out + r0 + tx] = tile[tx][cc];
+  if constexpr (sizeof(T) == 2) {
+    // column q: the q-th 16-bit value of the 8 row pieces
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int sh = (q & 1) * 16;
+      uint32_t o[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        o[w] = ((x[2 * w][q >> 1] >> sh) & 0xffffu) |
+               (((x[2 * w + 1][q >> 1] >> sh) & 0xffffu) << 16);
+      *reinterpret_cast<u32x4*>(out + (int64_t)(col + q) * ld_out + r0 + tr) =
+          u32x4{o[0], o[1], o[2], o[3]};
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<u32x4*>(out + (int64_t)(col + q) * ld_out + r0 + tr) =
+          u32x4{x[0][q], x[1][q], x[2][q], x[3][q]};
+  }
 }
 
 // ===================================================================
@@ -1009,7 +1059,7 @@ hipError_t launch_lse_merge(const float2* partials, int64_t ldp, int nt,
                             float* logpi_out, const int* scatter_idx,
                             float* logprobs_rows, int* err, hipStream_t s) {
   return timed(K_LSE_MERGE, s, [&] {
-    k_lse_merge<<<cdiv(rows.cap, 256), 256, 0, s>>>(
+    k_lse_merge<<<cdiv(rows.cap, 32), 256, 0, s>>>(
         partials, ldp, nt, rows, ztgt, row_tokens, V, lse_out, logpi_out,
         scatter_idx, logprobs_rows, err);
   });
@@ -1109,7 +1159,8 @@ hipError_t launch_transpose(int dt, int kid, const void* in, int64_t ld_in,
                             const int* rowmap, DevRows rows, int rows_pad,
                             int cols, void* out, int64_t ld_out,
                             hipStream_t s) {
-  dim3 grid(cdiv(rows_pad, 64), cdiv(cols, 64));
+  // 64 rows x (4 waves x 64 bf16 or 16 fp32 columns) per workgroup
+  dim3 grid(cdiv(rows_pad, 64), cdiv(cols, dt ? 256 : 64));
   return timed(kid, s, [&] {
     if (dt)
       k_transpose<bf16><<<grid, 256, 0, s>>>((const bf16*)in, ld_in, rowmap,
