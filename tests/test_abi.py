@@ -139,3 +139,27 @@ def test_binding_rejects_host_tensors():
     h = torch.zeros(4, 64)
     with pytest.raises(rz.RzError):
         rz.token_logprobs(h, torch.zeros(10, 64), torch.zeros(4, dtype=torch.int32))
+
+
+def test_product_path_never_loads_the_oracle():
+    """The package, its binding and the input generators work without the
+    oracle: importing them (and calling every binding entry that needs no
+    GPU) must not pull oracle/ in, and no package source imports it."""
+    import pathlib
+    import subprocess
+    import sys
+    code = (
+        "import sys\n"
+        "import invariant_token_logprobs_amd as rz\n"
+        "from invariant_token_logprobs_amd import synth, binding\n"
+        "rz.load_library(); rz.workspace_bytes(rz.RZ_OP_FWD_BWD, 64, 2, 64, 100, rz.RZ_DTYPE_BF16)\n"
+        "synth.make_workload('tiny')\n"
+        "assert not any(m == 'oracle' or m.startswith('oracle.') for m in sys.modules), "
+        "sorted(m for m in sys.modules if 'oracle' in m)\n")
+    root = pathlib.Path(__file__).resolve().parents[1]
+    res = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True,
+                         text=True, timeout=300)
+    assert res.returncode == 0, res.stderr[-2000:]
+    for src in (root / "invariant_token_logprobs_amd").rglob("*.py"):
+        text = src.read_text()
+        assert "import oracle" not in text and "from oracle" not in text, src
