@@ -2,7 +2,12 @@
 
 TEST INFRASTRUCTURE ONLY: imported by the tests, the package smoke check and
 the benchmark's CPU-baseline leg, never by the product path.  It shares no code
-with the HIP kernels.  See reinforce_zero.py for the definitions and sources.
+with the HIP kernels.  See reinforce_zero.py (learner path) and
+rollout_sampler.py (rollout-side draw) for the definitions and sources.
 """
 from .reinforce_zero import *  # noqa: F401,F403
-from .reinforce_zero import __all__  # noqa: F401
+from .rollout_sampler import *  # noqa: F401,F403
+from .reinforce_zero import __all__ as _rz_all
+from .rollout_sampler import __all__ as _rs_all
+
+__all__ = list(_rz_all) + list(_rs_all)

@@ -385,3 +385,97 @@ def test_importance_sampling_identities_by_enumeration():
     assert abs(out["kl"] - kl_exact) < 1e-15
     assert kl_exact > 0.0
     assert B == len(rewards)
+
+
+# ------------------------------------------------------- rollout-side sampler
+# Published known-answer vectors of Philox4x32-10 (Salmon, Moraes, Dror and
+# Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011; the
+# known-answer file of its reference implementation): counter, key, output.
+PHILOX_KAT = [
+    ([0x00000000] * 4, [0x00000000] * 2,
+     [0x6627e8d5, 0xe169c58d, 0xbc57ac4c, 0x9b00dbd8]),
+    ([0xffffffff] * 4, [0xffffffff] * 2,
+     [0x408f276d, 0x41c83b0e, 0xa20bc7c6, 0x6d5451fd]),
+    ([0x243f6a88, 0x85a308d3, 0x13198a2e, 0x03707344], [0xa4093822, 0x299f31d0],
+     [0xd16cfe09, 0x94fdcceb, 0x5001e420, 0x24126ea1]),
+]
+
+
+@pytest.mark.parametrize("ctr,key,want", PHILOX_KAT)
+def test_philox_known_answers(ctr, key, want):
+    got = O.philox4x32_10(np.array(ctr, dtype=np.uint64), np.array(key, dtype=np.uint64))
+    assert [int(x) for x in got] == want
+
+
+def test_philox_batches_like_single_calls():
+    rng = np.random.default_rng(5)
+    ctr = rng.integers(0, 2 ** 32, size=(7, 4), dtype=np.uint64)
+    key = np.array([0x12345678, 0x9abcdef0], dtype=np.uint64)
+    batch = O.philox4x32_10(ctr, key)
+    for i in range(7):
+        assert np.array_equal(batch[i], O.philox4x32_10(ctr[i], key))
+
+
+def test_gumbel_uniforms_range_moments_and_layout():
+    ids = np.arange(200, dtype=np.int64)
+    u = O.gumbel_uniforms(7, ids, 1000)
+    assert u.shape == (200, 1000)
+    assert u.min() > 0.0 and u.max() < 1.0
+    # mean 1/2 and variance 1/12 of U(0, 1): 2e5 draws, standard errors
+    # 6.5e-4 and 1.9e-4; the bounds are ~8 standard errors
+    assert abs(u.mean() - 0.5) < 5e-3
+    assert abs(u.var() - 1.0 / 12.0) < 1.5e-3
+    # word v % 4 of counter v // 4: four consecutive columns share a call
+    x = O.philox4x32_10(np.array([2, 13, 0, 0], dtype=np.uint64),
+                        np.array([7, 0], dtype=np.uint64))
+    assert np.array_equal(np.round(u[13, 8:12] * 2.0 ** 32 - 0.5), x.astype(np.float64))
+    # the high word of the id and the seed's high word both enter
+    hi = O.gumbel_uniforms(7, np.array([13 + (1 << 32)]), 1000)
+    assert not np.array_equal(hi[0], u[13])
+    assert not np.array_equal(O.gumbel_uniforms(7 + (1 << 32), ids[:1], 1000)[0], u[0])
+
+
+def test_sampler_frequencies_match_softmax():
+    """Gumbel-max draws over many row ids follow softmax(z): chi-square of
+    60000 draws over 6 classes (5 degrees of freedom; 30 is far past the
+    0.01% point, so a correct sampler passes for any seed with certainty
+    in practice, and a biased one fails)."""
+    z = np.array([0.3, -1.2, 2.0, 0.0, 0.5, -0.7])
+    n = 60000
+    hidden = np.tile(z, (n, 1))
+    tokens, logmu, gap = O.sample_tokens(hidden, np.eye(6), np.arange(n), seed=11,
+                                         row_chunk=4096)
+    p = np.exp(z - z.max())
+    p /= p.sum()
+    counts = np.bincount(tokens, minlength=6)
+    chi2 = float(((counts - n * p) ** 2 / (n * p)).sum())
+    assert chi2 < 30.0, (chi2, counts, n * p)
+    assert np.allclose(logmu, np.log(p)[tokens], rtol=0, atol=1e-12)
+    assert np.all(gap >= 0.0)
+
+
+def test_sampler_draw_depends_on_row_id_not_batch():
+    rng = np.random.default_rng(3)
+    H, V = 8, 50
+    W = rng.normal(size=(V, H))
+    hidden = rng.normal(size=(12, H))
+    ids = rng.integers(0, 2 ** 40, size=12)
+    tok, lmu, _ = O.sample_tokens(hidden, W, ids, seed=99)
+    perm = rng.permutation(12)
+    tok_p, lmu_p, _ = O.sample_tokens(hidden[perm], W, ids[perm], seed=99)
+    assert np.array_equal(tok_p, tok[perm])
+    assert np.array_equal(lmu_p, lmu[perm])
+    # each row alone gives the same draw (its log mu only to rounding: the
+    # float64 matrix product itself varies with the batch shape in its last
+    # bits), and the record is the learner's log pi
+    for i in range(12):
+        t1, l1, _ = O.sample_tokens(hidden[i:i + 1], W, ids[i:i + 1], seed=99)
+        assert t1[0] == tok[i] and abs(l1[0] - lmu[i]) < 1e-12
+    logpi, _ = O.token_logprobs(hidden, W, tok)
+    assert np.allclose(logpi, lmu, rtol=0, atol=1e-12)
+    # brute force: the argmax of z + g, smallest index on ties
+    u = O.gumbel_uniforms(99, ids, V)
+    score = hidden @ W.T - np.log(-np.log(u))
+    for i in range(12):
+        best = max(range(V), key=lambda v: (score[i, v], -v))
+        assert best == tok[i]
