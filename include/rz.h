@@ -72,7 +72,8 @@ typedef enum { RZ_DTYPE_F32 = 0, RZ_DTYPE_BF16 = 1 } rz_dtype;
 typedef enum {
   RZ_OP_TOKEN_LOGPROBS = 0,
   RZ_OP_FWD_BWD = 1,
-  RZ_OP_DIAGNOSTICS = 2
+  RZ_OP_DIAGNOSTICS = 2,
+  RZ_OP_SAMPLE = 3
 } rz_op;
 
 /* device-side error bits written to *err_flag */
@@ -152,6 +153,38 @@ rz_status rz_reinforce_zero_fwd_bwd(
     int32_t n_resp, int32_t H, int32_t V, rz_dtype dt, float* logprobs,
     float* loss, float* d_hidden, float* d_lm_head, float* diag, float* adv,
     int32_t* err_flag, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * rz_sample_tokens -- the rollout side: draw each row's token and record
+ * its logprob ("Zero mismatch, simple async RL", vLLM blog, section 4
+ * "Recipe" item 2: the rollout records the logprob of every token it
+ * samples; section 5: "diff 0", rollout and trainer compute bit-identical
+ * logprobs for every sampled token).
+ *
+ *   hidden   [n_rows, H]  dt      final hidden state of each history h_t
+ *   lm_head  [V, H]       dt      LM-head weights W
+ *   row_ids  [n_rows]     uint64  a caller-chosen identity of each row
+ *   seed                  uint64  key of the draw
+ *   tokens   [n_rows]     int32   out: a_t
+ *   logmu    [n_rows]     fp32    out: log pi(a_t | h_t), the record
+ *   lse      [n_rows]     fp32    out, may be NULL: log sum_v exp(z[t, v])
+ *
+ * The draw is from softmax(z_t) at temperature 1 by the Gumbel-max rule:
+ * a_t = argmax_v z[t, v] - log(-log u[t, v]), ties to the smaller v, with
+ * u = (x + 1/2) 2^-32 and x = word v % 4 of Philox4x32-10 (Salmon et al.,
+ * "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011) at counter
+ * (v / 4, id low word, id high word, 0) and key (seed low word, seed high
+ * word).  A row's token depends on (seed, its id, hidden, W) only, not on
+ * n_rows or the other rows.  logmu and lse are computed by the kernels of
+ * rz_token_logprobs, so logmu is bit-identical to rz_token_logprobs(hidden,
+ * lm_head, tokens) at the same weights.  H must be a multiple of 64.
+ */
+rz_status rz_sample_tokens(const void* hidden, const void* lm_head,
+                           const uint64_t* row_ids, int64_t n_rows, int32_t H,
+                           int32_t V, rz_dtype dt, uint64_t seed,
+                           int32_t* tokens, float* logmu, float* lse,
+                           void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /*
  * rz_diagnostics -- D3 and the k1 rollout-to-learner KL.

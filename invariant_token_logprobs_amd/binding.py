@@ -17,6 +17,7 @@ RZ_DTYPE_BF16 = 1
 RZ_OP_TOKEN_LOGPROBS = 0
 RZ_OP_FWD_BWD = 1
 RZ_OP_DIAGNOSTICS = 2
+RZ_OP_SAMPLE = 3
 
 RZ_DEVERR_TOKEN = 1
 RZ_DEVERR_GROUP = 2
@@ -27,8 +28,9 @@ _STATUS = {0: "RZ_OK", -1: "RZ_ERR_INVALID_ARG", -2: "RZ_ERR_UNSUPPORTED",
 
 EXPORTS = [
     "rz_workspace_bytes", "rz_status_string", "rz_token_logprobs",
-    "rz_reinforce_zero_fwd_bwd", "rz_diagnostics", "rz_timing_enable",
-    "rz_timing_num_kernels", "rz_timing_kernel_name", "rz_timing_read",
+    "rz_reinforce_zero_fwd_bwd", "rz_diagnostics", "rz_sample_tokens",
+    "rz_timing_enable", "rz_timing_num_kernels", "rz_timing_kernel_name",
+    "rz_timing_read",
 ]
 
 
@@ -69,6 +71,9 @@ def load_library():
     lib.rz_reinforce_zero_fwd_bwd.restype = ctypes.c_int
     lib.rz_diagnostics.argtypes = [vp, vp, vp, i64, vp, vp, sz, vp]
     lib.rz_diagnostics.restype = ctypes.c_int
+    lib.rz_sample_tokens.argtypes = [vp, vp, vp, i64, i32, i32, ctypes.c_int,
+                                     ctypes.c_uint64, vp, vp, vp, vp, sz, vp]
+    lib.rz_sample_tokens.restype = ctypes.c_int
     lib.rz_timing_enable.argtypes = [ctypes.c_int]
     lib.rz_timing_enable.restype = ctypes.c_int
     lib.rz_timing_num_kernels.argtypes = []
@@ -187,6 +192,39 @@ def token_logprobs(hidden, lm_head, tokens, *, want_lse: bool = False,
                                  _ptr(ws), nbytes, _stream(stream)),
            "rz_token_logprobs")
     return (logprobs, lse) if want_lse else logprobs
+
+
+def sample_tokens(hidden, lm_head, row_ids, seed: int, *, want_lse: bool = False,
+                  workspace: Optional[Workspace] = None, stream=None):
+    """Draw each row's token and record its logprob (rz_sample_tokens).
+
+    row_ids: int64 tensor [n_rows], each row's identity (its bits are the
+    uint64 id of the draw); seed: 0 <= seed < 2**64.  Returns (tokens int32,
+    logmu float32[, lse float32])."""
+    torch = _torch()
+    lib = load_library()
+    dt = _dtype_code(hidden)
+    _need(hidden, "hidden", None, 2)
+    dev = hidden.device
+    _need(lm_head, "lm_head", hidden.dtype, 2, dev)
+    _need(row_ids, "row_ids", torch.int64, 1, dev)
+    N, H = hidden.shape
+    V = lm_head.shape[0]
+    if lm_head.shape[1] != H or row_ids.shape[0] != N:
+        raise RzError("shape mismatch between hidden, lm_head and row_ids")
+    if not 0 <= int(seed) < 2 ** 64:
+        raise RzError("seed must be in [0, 2**64)")
+    tokens = torch.empty(N, dtype=torch.int32, device=dev)
+    logmu = torch.empty(N, dtype=torch.float32, device=dev)
+    lse = torch.empty(N, dtype=torch.float32, device=dev) if want_lse else None
+    nbytes = workspace_bytes(RZ_OP_SAMPLE, N, 1, H, V, dt)
+    ws = _workspace(workspace, nbytes, dev)
+    _check(lib.rz_sample_tokens(_ptr(hidden), _ptr(lm_head), _ptr(row_ids), N, H,
+                                V, dt, ctypes.c_uint64(int(seed)), _ptr(tokens),
+                                _ptr(logmu), _ptr(lse), _ptr(ws), nbytes,
+                                _stream(stream)),
+           "rz_sample_tokens")
+    return (tokens, logmu, lse) if want_lse else (tokens, logmu)
 
 
 def reinforce_zero_fwd_bwd(hidden, lm_head, tokens, logmu, mask, cu_rows,

@@ -57,6 +57,22 @@ size_t carve_tlp(Carver& c, int64_t n, int32_t V, TlpWs* w) {
   return c.off;
 }
 
+// ---- sample layout ----
+struct SmpWs {
+  float2* partials;
+  float2* cand;
+  float* ztgt;
+};
+size_t carve_smp(Carver& c, int64_t n, int32_t V, SmpWs* w) {
+  const int nt = (int)((V + kVocabTile - 1) / kVocabTile);
+  SmpWs t;
+  t.partials = c.take<float2>(sizeof(float2) * (size_t)nt * (size_t)n);
+  t.cand = c.take<float2>(sizeof(float2) * (size_t)nt * (size_t)n);
+  t.ztgt = c.take<float>(sizeof(float) * (size_t)n);
+  if (w) *w = t;
+  return c.off;
+}
+
 // ---- fwd_bwd layout ----
 struct FbWs {
   int* nvalid;
@@ -216,8 +232,47 @@ size_t rz_workspace_bytes(rz_op op, int64_t n_rows, int32_t n_resp, int32_t H,
       return carve_fb(c, n_rows, n_resp, H, V, dt, nullptr);
     case RZ_OP_DIAGNOSTICS:
       return align_up(diag_partials_bytes(n_rows));
+    case RZ_OP_SAMPLE:
+      if (!dims_ok(H, V, dt)) return 0;
+      return n_rows == 0 ? 0 : carve_smp(c, n_rows, V, nullptr);
   }
   return 0;
+}
+
+rz_status rz_sample_tokens(const void* hidden, const void* lm_head,
+                           const uint64_t* row_ids, int64_t n_rows, int32_t H,
+                           int32_t V, rz_dtype dt, uint64_t seed,
+                           int32_t* tokens, float* logmu, float* lse,
+                           void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  if (n_rows < 0 || n_rows > RZ_MAX_ROWS) return RZ_ERR_INVALID_ARG;
+  if (dt != RZ_DTYPE_F32 && dt != RZ_DTYPE_BF16) return RZ_ERR_UNSUPPORTED;
+  if (H <= 0 || V <= 0) return RZ_ERR_INVALID_ARG;
+  if (!dims_ok(H, V, dt)) return RZ_ERR_UNSUPPORTED;
+  if (n_rows == 0) return RZ_OK;
+  if (!hidden || !lm_head || !row_ids || !tokens || !logmu)
+    return RZ_ERR_INVALID_ARG;
+  Carver meas{nullptr};
+  const size_t need = carve_smp(meas, n_rows, V, nullptr);
+  rz_status st = ws_check(workspace, workspace_bytes, need);
+  if (st != RZ_OK) return st;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  Carver c{reinterpret_cast<char*>(workspace)};
+  SmpWs w;
+  carve_smp(c, n_rows, V, &w);
+  const int nt = (V + kVocabTile - 1) / kVocabTile;
+  DevRows rows{nullptr, 0, (int)n_rows};
+  // the logits GEMM with the draw in its epilogue, then the draw's merge
+  RZ_TRY(launch_fwd_sample(dt, hidden, n_rows, lm_head, H, V, row_ids, seed,
+                           w.partials, w.cand, n_rows, s));
+  RZ_TRY(launch_draw_merge(w.cand, n_rows, nt, n_rows, tokens, s));
+  // the record: rz_token_logprobs' own target and merge kernels
+  RZ_TRY(launch_target_logit(dt, hidden, (int64_t)H * esize(dt), nullptr,
+                             rows, lm_head, H, V, tokens, w.ztgt, s));
+  RZ_TRY(launch_lse_merge(w.partials, n_rows, nt, rows, w.ztgt, tokens, V,
+                          lse, logmu, nullptr, nullptr, nullptr, s));
+  return RZ_OK;
 }
 
 rz_status rz_token_logprobs(const void* hidden, const void* lm_head,

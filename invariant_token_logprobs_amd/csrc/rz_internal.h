@@ -33,6 +33,8 @@ enum KernelId {
   K_BUCKET_SORT,
   K_DW_FIX,
   K_TARGET_LOGIT,    // z[t, a_t] for the gather
+  K_FWD_SAMPLE,      // rollout-side logits GEMM with the draw in the epilogue
+  K_DRAW_MERGE,      // per-row best draw over the vocab tiles
   K_NUM_KERNELS
 };
 
@@ -59,6 +61,18 @@ hipError_t launch_fwd_logits(int dt, const void* hidden, int64_t lda_bytes,
                              const int* row_tokens, float2* partials,
                              int64_t ldp, float* ztgt, void* e, int64_t lde,
                              int Vpad, hipStream_t s);
+hipError_t launch_target_logit(int dt, const void* hidden, int64_t lda_bytes,
+                               const int* a_rows, DevRows rows,
+                               const void* lm_head, int H, int V,
+                               const int* row_tokens, float* ztgt,
+                               hipStream_t s);
+hipError_t launch_fwd_sample(int dt, const void* hidden, int64_t n,
+                             const void* lm_head, int H, int V,
+                             const uint64_t* row_ids, uint64_t seed,
+                             float2* partials, float2* cand, int64_t ldp,
+                             hipStream_t s);
+hipError_t launch_draw_merge(const float2* cand, int64_t ldp, int nt, int64_t n,
+                             int* tokens, hipStream_t s);
 hipError_t launch_lse_merge(const float2* partials, int64_t ldp, int nt,
                             DevRows rows, const float* ztgt,
                             const int* row_tokens, int V, float* lse_out,

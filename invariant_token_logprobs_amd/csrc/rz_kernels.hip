@@ -55,6 +55,9 @@ struct FwdArgs {
   int64_t ldp;
   void* e;                // learner call only: exp(z - m_tile) [rows][lde]
   int64_t lde;
+  const uint64_t* row_ids;  // sampling call only: the rows' identities
+  uint64_t seed;
+  float2* cand;           // sampling call only: [nt][ldp] (best z + g, index)
 };
 
 // Storage type of e = exp(z - m_tile) in (0, 1]: fp16 for bf16 inputs (an
@@ -74,6 +77,60 @@ __device__ __forceinline__ int e_stage_off(int R, int k) {
   return R * 512 + ((k ^ (R & 31)) << 4);
 }
 
+// ---- the rollout-side draw ----
+// Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers:
+// As Easy as 1, 2, 3", SC 2011): ten rounds of two 32 x 32 -> 64-bit
+// products on counter words 0 and 2, the halves and the key XORed into the
+// next counter; the key grows by fixed Weyl increments between rounds.
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1,
+                                              uint32_t c2, uint32_t c3,
+                                              uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
+    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+  }
+  return u32x4{c0, c1, c2, c3};
+}
+
+constexpr float kLn2 = 0.69314718055994531f;
+constexpr float kTwoM32 = 2.3283064365386963e-10f;  // 2^-32
+
+// Gumbel noise g = -ln(-ln u) of u = (x + 1/2) 2^-32.  The largest g come
+// from u near 1, so E = -ln u is taken from w = 1 - u (exact from the
+// integer) there: a short series for small w, else Kahan's form
+// -ln(y) w / (1 - y) with y = 1 - w rounded, which cancels y's rounding.
+__device__ __forceinline__ float gumbel_of_bits(uint32_t x) {
+  float E;
+  if (x < 0x80000000u) {
+    const float u = ((float)x + 0.5f) * kTwoM32;
+    E = -__builtin_amdgcn_logf(u) * kLn2;
+  } else {
+    const float w = ((float)(0xFFFFFFFFu - x) + 0.5f) * kTwoM32;  // 1 - u
+    if (w < 0.015625f) {
+      E = w * (1.f + w * (0.5f + w * (1.f / 3.f + w * (0.25f + w * 0.2f))));
+    } else {
+      const float y = 1.f - w;
+      E = -__builtin_amdgcn_logf(y) * kLn2 * (w / (1.f - y));
+    }
+  }
+  return -__builtin_amdgcn_logf(E) * kLn2;
+}
+
+// (score, index) order of the draw: larger score first, then smaller index
+__device__ __forceinline__ bool draw_better(float s, int v, float bs, int bv) {
+  return s > bs || (s == bs && v < bv);
+}
+
 // bi_lmhead_gemm + the log-softmax statistics of one 256 x 256 logits tile
 // (vocab tile j = tn): per row t, m_tile = max_v z[t, v] and
 // s_tile = sum_v exp(z[t, v] - m_tile), written to partials[j][t]; on the
@@ -88,11 +145,12 @@ __device__ __forceinline__ int e_stage_off(int R, int k) {
 // is the same in every launch (batch invariance).  The maximum is exact in
 // any order, so it is taken first over the whole tile; one exp per element
 // then serves both s_tile and e.
-template <typename T, bool kStoreE>
+template <typename T, bool kStoreE, bool kSample = false>
 __global__ RZ_GEMM_ATTR void k_fwd_logits(FwdArgs a) {
   // [0, 128 KB): main-loop stages, then (learner call, bf16) the e tile;
-  // then the per-wave row maxima and row sums [2][256] each
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes + 4096];
+  // then the per-wave row maxima and row sums [2][256] each; then (sampling
+  // call) the per-wave best draw and its index [2][256] each
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes + (kSample ? 8192 : 4096)];
   const RowCount rc = to_rc(a.rows);
   const int M = rc.get();
   // Only the tiles of the M rows present are numbered (M may be a device
@@ -180,6 +238,61 @@ __global__ RZ_GEMM_ATTR void k_fwd_logits(FwdArgs a) {
   };
   if (n0 + kBN <= a.V) pass2(BoolC<true>{});
   else pass2(BoolC<false>{});
+  if constexpr (kSample) {
+    // The draw: per row, the best z + g over the tile's columns < V (see
+    // gumbel_of_bits; counter (v / 4, id_lo, id_hi, 0), key = the seed, word
+    // v % 4), under draw_better's total order, so the order in which lanes
+    // and waves meet does not matter.
+    float* wbs = reinterpret_cast<float*>(lds + kLdsBytes + 4096);   // [2][256]
+    int* wbv = reinterpret_cast<int*>(lds + kLdsBytes + 6144);       // [2][256]
+    const uint32_t k0 = (uint32_t)a.seed, k1 = (uint32_t)(a.seed >> 32);
+#pragma unroll
+    for (int mi = 0; mi < kTM; ++mi) {
+      const int R = wm * 128 + mi * 32 + l32;
+      const uint64_t id = m0 + R < M ? a.row_ids[rc.base + m0 + R] : 0;
+      float bs = -__builtin_inff();
+      int bv = 0x7fffffff;
+#pragma unroll
+      for (int ni = 0; ni < kTN; ++ni)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c0 = cbase + ni * 32 + 8 * q;  // multiple of 4
+          const u32x4 x = philox4x32_10((uint32_t)c0 >> 2, (uint32_t)id,
+                                        (uint32_t)(id >> 32), 0u, k0, k1);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int v = c0 + j;
+            const float sc = acc[mi][ni][4 * q + j] + gumbel_of_bits(x[j]);
+            if (v < a.V && draw_better(sc, v, bs, bv)) {
+              bs = sc;
+              bv = v;
+            }
+          }
+        }
+      const float os = __shfl_xor(bs, 32, 64);
+      const int ov = __shfl_xor(bv, 32, 64);
+      if (draw_better(os, ov, bs, bv)) {
+        bs = os;
+        bv = ov;
+      }
+      if (half == 0) {
+        wbs[wn * 256 + R] = bs;
+        wbv[wn * 256 + R] = bv;
+      }
+    }
+    __syncthreads();
+    const int m = m0 + tid;
+    if (m < M) {
+      float bs = wbs[tid];
+      int bv = wbv[tid];
+      if (draw_better(wbs[256 + tid], wbv[256 + tid], bs, bv)) {
+        bs = wbs[256 + tid];
+        bv = wbv[256 + tid];
+      }
+      a.cand[(int64_t)tc.tn * a.ldp + rc.base + m] =
+          make_float2(bs, __builtin_bit_cast(float, bv));
+    }
+  }
   __syncthreads();
   {
     const int m = m0 + tid;
@@ -305,6 +418,38 @@ __global__ __launch_bounds__(256) void k_lse_merge(
   if (lse_out) lse_out[pos] = lse;
   if (logpi_out) logpi_out[pos] = lp;
   if (scatter_idx) logprobs_rows[scatter_idx[pos]] = lp;
+}
+
+// The draw's merge: per row, the best (score, index) over the vocab tiles
+// under draw_better's total order (lanes take tiles q, q + 8, ...; any
+// meeting order gives the same winner).
+__global__ __launch_bounds__(256) void k_draw_merge(
+    const float2* __restrict__ cand, int64_t ldp, int nt, int64_t n,
+    int* __restrict__ tokens) {
+  const int64_t p = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+  const int q = threadIdx.x & 7;
+  const bool live = p < n;
+  float bs = -__builtin_inff();
+  int bv = 0x7fffffff;
+  if (live)
+    for (int t = q; t < nt; t += 8) {
+      const float2 c = cand[(int64_t)t * ldp + p];
+      const int v = __builtin_bit_cast(int, c.y);
+      if (draw_better(c.x, v, bs, bv)) {
+        bs = c.x;
+        bv = v;
+      }
+    }
+#pragma unroll
+  for (int o = 4; o >= 1; o >>= 1) {
+    const float os = __shfl_xor(bs, o, 64);
+    const int ov = __shfl_xor(bv, o, 64);
+    if (draw_better(os, ov, bs, bv)) {
+      bs = os;
+      bv = ov;
+    }
+  }
+  if (live && q == 0) tokens[p] = bv;
 }
 
 // ===================================================================
@@ -1007,8 +1152,58 @@ const char* kernel_name(int k) {
       "diag_partial", "diag_final", "transpose_w",  "transpose_h",
       "bwd_dh_gemm", "bwd_dw_gemm", "fill",         "tok_hist",
       "scan",        "tok_scatter", "bucket_sort",  "dw_fix",
-      "target_logit"};
+      "target_logit", "fwd_sample_gemm", "draw_merge"};
   return (k >= 0 && k < K_NUM_KERNELS) ? names[k] : "?";
+}
+
+hipError_t launch_target_logit(int dt, const void* hidden, int64_t lda_bytes,
+                               const int* a_rows, DevRows rows,
+                               const void* lm_head, int H, int V,
+                               const int* row_tokens, float* ztgt,
+                               hipStream_t s) {
+  return timed(K_TARGET_LOGIT, s, [&] {
+    if (dt)
+      k_target_logit<bf16><<<cdiv(rows.cap, 4), 256, 0, s>>>(
+          (const char*)hidden, lda_bytes, a_rows, rows, (const char*)lm_head,
+          H, V, row_tokens, ztgt);
+    else
+      k_target_logit<float><<<cdiv(rows.cap, 4), 256, 0, s>>>(
+          (const char*)hidden, lda_bytes, a_rows, rows, (const char*)lm_head,
+          H, V, row_tokens, ztgt);
+  });
+}
+
+hipError_t launch_fwd_sample(int dt, const void* hidden, int64_t n,
+                             const void* lm_head, int H, int V,
+                             const uint64_t* row_ids, uint64_t seed,
+                             float2* partials, float2* cand, int64_t ldp,
+                             hipStream_t s) {
+  FwdArgs a{};
+  a.op = GemmOperands{(const char*)hidden, (int64_t)H * (dt ? 2 : 4), nullptr,
+                      0, (const char*)lm_head, (int64_t)H * (dt ? 2 : 4), V};
+  a.rows = DevRows{nullptr, 0, (int)n};
+  a.V = V;
+  a.Vpad = V;
+  a.nk = H / (dt ? Stage<bf16>::kK : Stage<float>::kK);
+  a.mt = cdiv(n, kBM);
+  a.nt = cdiv(V, kBN);
+  a.partials = partials;
+  a.ldp = ldp;
+  a.row_ids = row_ids;
+  a.seed = seed;
+  a.cand = cand;
+  const int nblk = a.mt * a.nt;
+  return timed(K_FWD_SAMPLE, s, [&] {
+    if (dt) k_fwd_logits<bf16, false, true><<<nblk, kThreads, 0, s>>>(a);
+    else k_fwd_logits<float, false, true><<<nblk, kThreads, 0, s>>>(a);
+  });
+}
+
+hipError_t launch_draw_merge(const float2* cand, int64_t ldp, int nt, int64_t n,
+                             int* tokens, hipStream_t s) {
+  return timed(K_DRAW_MERGE, s, [&] {
+    k_draw_merge<<<cdiv(n, 32), 256, 0, s>>>(cand, ldp, nt, n, tokens);
+  });
 }
 
 hipError_t launch_fwd_logits(int dt, const void* hidden, int64_t lda_bytes,
@@ -1028,7 +1223,7 @@ hipError_t launch_fwd_logits(int dt, const void* hidden, int64_t lda_bytes,
           H, V, row_tokens, ztgt);
   });
   if (err != hipSuccess) return err;
-  FwdArgs a;
+  FwdArgs a{};
   a.op = GemmOperands{(const char*)hidden, lda_bytes, a_rows, rows.base,
                       (const char*)lm_head, (int64_t)H * (dt ? 2 : 4), V};
   a.rows = rows;

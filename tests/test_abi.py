@@ -163,3 +163,32 @@ def test_product_path_never_loads_the_oracle():
     for src in (root / "invariant_token_logprobs_amd").rglob("*.py"):
         text = src.read_text()
         assert "import oracle" not in text and "from oracle" not in text, src
+
+
+def smp(lib, n=4, H=64, V=10, dt=BF16, seed=1, ws=P, ws_bytes=0, **null):
+    args = dict(hidden=P, head=P, ids=P, tokens=P, logmu=P)
+    for k in null:
+        args[k] = NULL
+    a = args
+    return lib.rz_sample_tokens(a["hidden"], a["head"], a["ids"], n, H, V, dt,
+                                ctypes.c_uint64(seed), a["tokens"], a["logmu"],
+                                NULL, ws, ws_bytes, NULL)
+
+
+def test_sample_tokens_argument_errors(lib):
+    assert smp(lib, n=-1) == INVALID
+    assert smp(lib, H=0) == INVALID
+    assert smp(lib, V=0) == INVALID
+    assert smp(lib, H=96) == UNSUPPORTED
+    assert smp(lib, dt=5) == UNSUPPORTED
+    for name in ("hidden", "head", "ids", "tokens", "logmu"):
+        assert smp(lib, **{name: True}) == INVALID, name
+    need = lib.rz_workspace_bytes(rz.RZ_OP_SAMPLE, 4, 1, 64, 10, BF16)
+    assert need > 0 and need % 256 == 0
+    assert smp(lib, ws=NULL, ws_bytes=need) == WORKSPACE
+    assert smp(lib, ws_bytes=need - 1) == WORKSPACE
+    assert smp(lib, n=0) == OK
+    # two vocab-tile tables (statistics, draw) and the target logits
+    nt = (151936 + 255) // 256
+    big = lib.rz_workspace_bytes(rz.RZ_OP_SAMPLE, 4096, 1, 2560, 151936, BF16)
+    assert big >= 2 * 8 * nt * 4096 + 4 * 4096
