@@ -105,6 +105,73 @@ def cpu_baseline(b, logmu, max_valid):
                        f"(BLAS threads {blas_threads})")}
 
 
+def bench_sample(args, torch, rz, synth, dev):
+    """The rollout-side draw at decode size: rz_sample_tokens on
+    --sample-rows live rows at the Qwen3-4B head (H 2560, V 151936, bf16)."""
+    H, V, M = 2560, 151936, args.sample_rows
+    hid, _ = synth.random_rows(M, H, V, "bf16", 3001)
+    head = synth.random_lm_head(V, H, "bf16", 3002)
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x.view(np.int16))).view(
+        torch.bfloat16).to(dev)
+    hidden, W = up(hid), up(head)
+    ids = torch.arange(M, dtype=torch.int64, device=dev)
+    ws = rz.Workspace()
+    seed = 0x5EED
+    for _ in range(args.warmup):
+        rz.sample_tokens(hidden, W, ids, seed, workspace=ws)
+    torch.cuda.synchronize()
+    rz.timing_enable(True)
+    rz.timing_read(reset=True)
+    torch.cuda.synchronize()
+    ts = time.perf_counter()
+    for _ in range(args.steps):
+        tok, logmu = rz.sample_tokens(hidden, W, ids, seed, workspace=ws)
+    torch.cuda.synchronize()
+    te = time.perf_counter()
+    kt = rz.timing_read(reset=True)
+    rz.timing_enable(False)
+    ms = (te - ts) * 1e3 / args.steps
+    assert bool(torch.isfinite(logmu).all()), "non-finite record"
+    gemm_ms, launches = kt["fwd_sample_gemm"]
+    avg = gemm_ms / launches
+    flop = 2.0 * M * H * V
+    w_bytes = 2.0 * V * H
+    achieved = flop / (avg * 1e-3) / 1e12
+    kms = {k: v[0] / args.steps for k, v in kt.items() if v[1]}
+    log("per-call kernel ms: " + ", ".join(f"{k}={v:.3f}" for k, v in
+                                           sorted(kms.items(), key=lambda x: -x[1])))
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle as O
+        n_cpu = 16
+        t0 = time.perf_counter()
+        O.sample_tokens(O.to_f64(hid[:n_cpu], "bf16"), O.to_f64(head, "bf16"),
+                        np.arange(n_cpu), seed, row_chunk=n_cpu)
+        dt = time.perf_counter() - t0
+        cpu = {"value": n_cpu / dt, "unit": "tokens/s",
+               "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+               "sample": f"first {n_cpu} rows at full H={H}, V={V}; float64 NumPy "
+                         f"logits + Philox noise + draw + record, {dt:.1f} s "
+                         "(includes decoding W to float64)"}
+    line = {
+        "metric": "sampled tokens/s (rollout draw + recorded logprob, Qwen3-4B head)",
+        "value": round(M * args.steps / (te - ts), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "rollout_draw_qwen3_4b_head", "hidden": H, "vocab": V,
+                   "rows": M},
+        "roofline": {"bound": "mfma", "kernel": "fwd_sample_gemm",
+                     "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"],
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
+                     "traffic": None, "avg_launch_ms": round(avg, 4),
+                     "w_read_TBps": round(w_bytes / (avg * 1e-3) / 1e12, 3)},
+        "cpu_baseline": cpu,
+        "kernel_ms_per_step": {k: round(v, 4) for k, v in kms.items()},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -114,6 +181,11 @@ def main():
     ap.add_argument("--cpu-valid", type=int, default=3072,
                     help="valid rows in the oracle's CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=("learner", "sample"), default="learner",
+                    help="learner: the fused fwd/bwd step (the headline); "
+                         "sample: the rollout-side draw + record at decode size")
+    ap.add_argument("--sample-rows", type=int, default=1024,
+                    help="live rows of the rollout batch in --mode sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run one plain 1 GiB device "
                          "copy so a counter run can scale its byte counters")
@@ -128,6 +200,8 @@ def main():
     from invariant_token_logprobs_amd import synth
 
     dev = torch.device("cuda:0")
+    if args.mode == "sample":
+        return bench_sample(args, torch, rz, synth, dev)
     t0 = time.time()
     b = synth.make_workload(args.workload)
     log(f"workload {b.name}: N={b.N} B={b.B} valid={b.n_valid} H={b.H} V={b.V} "

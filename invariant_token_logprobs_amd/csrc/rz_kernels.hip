@@ -67,6 +67,16 @@ template <typename T> struct EStore { typedef float type; };
 template <> struct EStore<bf16> { typedef _Float16 type; };
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 template <bool B> struct BoolC { static constexpr bool value = B; };
+template <int I> struct IntC { static constexpr int value = I; };
+// f(IntC<I>{}) for I = B .. E - 1: indices stay compile-time constants
+// whatever the unroller decides about a loop this large
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(IntC<B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 // LDS staging of a 256 x 256 fp16 e tile, 512 bytes per row, for coalesced
 // 16-byte stores.  The 16-byte chunk k of row R sits at chunk k ^ (R % 32):
@@ -85,7 +95,10 @@ __device__ __forceinline__ int e_stage_off(int R, int k) {
 __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1,
                                               uint32_t c2, uint32_t c3,
                                               uint32_t k0, uint32_t k1) {
-#pragma unroll
+  // kept rolled: fully unrolled at every call site of the draw's epilogue
+  // it stops the enclosing loops from unrolling, and the accumulators they
+  // index would move to scratch memory
+#pragma unroll 1
   for (int r = 0; r < 10; ++r) {
     if (r) {
       k0 += 0x9E3779B9u;
@@ -246,29 +259,27 @@ __global__ RZ_GEMM_ATTR void k_fwd_logits(FwdArgs a) {
     float* wbs = reinterpret_cast<float*>(lds + kLdsBytes + 4096);   // [2][256]
     int* wbv = reinterpret_cast<int*>(lds + kLdsBytes + 6144);       // [2][256]
     const uint32_t k0 = (uint32_t)a.seed, k1 = (uint32_t)(a.seed >> 32);
-#pragma unroll
-    for (int mi = 0; mi < kTM; ++mi) {
+    static_for<0, kTM>([&](auto mi_c) {
+      constexpr int mi = decltype(mi_c)::value;
       const int R = wm * 128 + mi * 32 + l32;
       const uint64_t id = m0 + R < M ? a.row_ids[rc.base + m0 + R] : 0;
       float bs = -__builtin_inff();
       int bv = 0x7fffffff;
-#pragma unroll
-      for (int ni = 0; ni < kTN; ++ni)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int c0 = cbase + ni * 32 + 8 * q;  // multiple of 4
-          const u32x4 x = philox4x32_10((uint32_t)c0 >> 2, (uint32_t)id,
-                                        (uint32_t)(id >> 32), 0u, k0, k1);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int v = c0 + j;
-            const float sc = acc[mi][ni][4 * q + j] + gumbel_of_bits(x[j]);
-            if (v < a.V && draw_better(sc, v, bs, bv)) {
-              bs = sc;
-              bv = v;
-            }
+      static_for<0, kTN * 4>([&](auto nq_c) {
+        constexpr int ni = decltype(nq_c)::value / 4, q = decltype(nq_c)::value % 4;
+        const int c0 = cbase + ni * 32 + 8 * q;  // multiple of 4
+        const u32x4 x = philox4x32_10((uint32_t)c0 >> 2, (uint32_t)id,
+                                      (uint32_t)(id >> 32), 0u, k0, k1);
+        static_for<0, 4>([&](auto j_c) {
+          constexpr int j = decltype(j_c)::value;
+          const int v = c0 + j;
+          const float sc = acc[mi][ni][4 * q + j] + gumbel_of_bits(x[j]);
+          if (v < a.V && draw_better(sc, v, bs, bv)) {
+            bs = sc;
+            bv = v;
           }
-        }
+        });
+      });
       const float os = __shfl_xor(bs, 32, 64);
       const int ov = __shfl_xor(bv, 32, 64);
       if (draw_better(os, ov, bs, bv)) {
@@ -279,7 +290,7 @@ __global__ RZ_GEMM_ATTR void k_fwd_logits(FwdArgs a) {
         wbs[wn * 256 + R] = bs;
         wbv[wn * 256 + R] = bv;
       }
-    }
+    });
     __syncthreads();
     const int m = m0 + tid;
     if (m < M) {
