@@ -213,6 +213,9 @@ __global__ RZ_GEMM_ATTR void k_fwd_logits(FwdArgs a) {
     constexpr bool kFull = decltype(full_c)::value;
 #pragma unroll
     for (int mi = 0; mi < kTM; ++mi) {
+      // a 32-row block wholly past the row count: nothing to compute
+      // (uniform across the wave; its rows are never read back)
+      if (m0 + wm * 128 + mi * 32 >= M) continue;
       const int R = wm * 128 + mi * 32 + l32;
       const bool rvalid = m0 + R < M;
       // exp(z - m) = 2^(z log2 e - m log2 e): one FMA per element
@@ -261,6 +264,7 @@ __global__ RZ_GEMM_ATTR void k_fwd_logits(FwdArgs a) {
     const uint32_t k0 = (uint32_t)a.seed, k1 = (uint32_t)(a.seed >> 32);
     static_for<0, kTM>([&](auto mi_c) {
       constexpr int mi = decltype(mi_c)::value;
+      if (m0 + wm * 128 + mi * 32 >= M) return;  // block past the row count
       const int R = wm * 128 + mi * 32 + l32;
       const uint64_t id = m0 + R < M ? a.row_ids[rc.base + m0 + R] : 0;
       float bs = -__builtin_inff();
