@@ -34,10 +34,10 @@ GEMM_KERNELS = ("fwd_logits_gemm", "bwd_dh_gemm", "bwd_dw_gemm")
 # profiles/gemm_traffic_qwen3_4b_tool.md.
 COUNTER_TRAFFIC = {
     "workload": "qwen3_4b_tool",
-    "sources_sha256": "69a51442f59aac74a9b52984e2b9a7bbc22111ccfaa555db3f977d159e6787ca",
-    "bytes_per_launch": {"fwd_logits_gemm": 28401980603,
-                         "bwd_dh_gemm": 24612960644,
-                         "bwd_dw_gemm": 28300835319},
+    "sources_sha256": "2458ee7d0d5e1c09dd47db69d0095d2d853ad398e73ed532645ddbc410c04e9f",
+    "bytes_per_launch": {"fwd_logits_gemm": 30714717981,
+                         "bwd_dh_gemm": 24369720363,
+                         "bwd_dw_gemm": 28226607009},
 }
 
 
