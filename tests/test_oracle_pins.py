@@ -479,3 +479,55 @@ def test_sampler_draw_depends_on_row_id_not_batch():
     for i in range(12):
         best = max(range(V), key=lambda v: (score[i, v], -v))
         assert best == tok[i]
+
+
+# ------------------------------------------------------ run-level diagnostics
+def test_grad_norms_hand_case_and_identities():
+    dh = np.array([[3.0, 0.0], [0.0, 4.0]])
+    dw = np.array([[1.0, 2.0, 2.0]])
+    assert O.grad_norms(dh, dw) == (5.0, 3.0)
+    rng = np.random.default_rng(4)
+    a = rng.normal(size=(37, 11))
+    b = rng.normal(size=(5, 11))
+    na, nb = O.grad_norms(a, b)
+    # a library norm of a different formulation (scipy's BLAS nrm2 path)
+    import scipy.linalg
+    assert abs(na - scipy.linalg.norm(a)) < 1e-12 * na
+    # permutation and scaling identities
+    assert abs(O.grad_norms(a[::-1], b)[0] - na) < 1e-12 * na
+    assert abs(O.grad_norms(a, 3.0 * b)[1] - 3.0 * nb) < 1e-12 * nb
+
+
+def test_response_diagnostics_hand_case():
+    # two responses: rows 0-2 (row 1 masked) and rows 3-4; a third with no
+    # valid row
+    logpi = np.array([-1.0, -5.0, -2.0, -0.5, -0.5, -3.0])
+    logmu = np.array([-1.5, -1.0, -2.0, -0.5, -1.0, -3.0])
+    mask = np.array([1, 0, 1, 1, 1, 0], dtype=np.uint8)
+    cu = np.array([0, 3, 5, 6])
+    d3, kl = O.response_diagnostics(logpi, logmu, mask, cu)
+    f = lambda d: math.expm1(d) - d
+    assert abs(d3[0] - (f(0.5) + f(0.0)) / 2) < 1e-15
+    assert abs(kl[0] - (-0.5 + 0.0) / 2) < 1e-15
+    assert abs(d3[1] - (f(0.0) + f(0.5)) / 2) < 1e-15
+    assert abs(kl[1] - (0.0 - 0.5) / 2) < 1e-15
+    assert np.isnan(d3[2]) and np.isnan(kl[2])
+    # the token-weighted mean of per-response values is the flat step value
+    flat_d3, flat_kl = O.diagnostics(logpi, logmu, mask)
+    counts = np.array([2, 2])
+    assert abs((counts * d3[:2]).sum() / counts.sum() - flat_d3) < 1e-15
+    assert abs((counts * kl[:2]).sum() / counts.sum() - flat_kl) < 1e-15
+
+
+def test_run_summary_hand_case():
+    d3 = [0.1, 0.2, 0.15, 3.0, 0.1]          # median 0.15, one spike
+    kl = [1.0, 2.0, 3.0, 10.0, 20.0, 30.0]   # window 3: medians 2 and 20
+    g = [0.5, 38.27, 1.0]
+    s = O.run_summary(d3, kl, g, window=3)
+    assert s["d3_peak"] == 3.0 and s["d3_median"] == 0.15
+    assert abs(s["d3_peak_over_median"] - 20.0) < 1e-12
+    assert s["kl_median_first"] == 2.0 and s["kl_median_last"] == 20.0
+    assert s["kl_median_ratio"] == 10.0
+    assert s["grad_norm_max"] == 38.27
+    # even count: the mean of the two middle values
+    assert O.run_summary([1.0, 2.0, 4.0, 8.0], [1.0], [0.0])["d3_median"] == 3.0
