@@ -73,7 +73,8 @@ typedef enum {
   RZ_OP_TOKEN_LOGPROBS = 0,
   RZ_OP_FWD_BWD = 1,
   RZ_OP_DIAGNOSTICS = 2,
-  RZ_OP_SAMPLE = 3
+  RZ_OP_SAMPLE = 3,
+  RZ_OP_GRAD_NORMS = 4
 } rz_op;
 
 /* device-side error bits written to *err_flag */
@@ -88,7 +89,9 @@ typedef enum {
 
 /* Bytes of workspace an entry point needs for the given sizes; 0 when the
  * sizes are themselves invalid (the call would return an error anyway).
- * For RZ_OP_DIAGNOSTICS only n_rows is read. */
+ * For RZ_OP_DIAGNOSTICS only n_rows is read; for RZ_OP_GRAD_NORMS, n_rows,
+ * H and V (dt is ignored).  rz_response_diagnostics and rz_run_summary need
+ * no workspace. */
 size_t rz_workspace_bytes(rz_op op, int64_t n_rows, int32_t n_resp, int32_t H,
                           int32_t V, rz_dtype dt);
 
@@ -200,6 +203,72 @@ rz_status rz_diagnostics(const float* logpi, const float* logmu,
                          const uint8_t* mask, int64_t n, float* diag,
                          void* workspace, size_t workspace_bytes,
                          void* stream);
+
+/*
+ * Run-level diagnostics ("Zero mismatch, simple async RL", vLLM blog,
+ * section 3 and Figure 1: the per-update D3 over a run, its peak against its
+ * median; section 4 "What happens without alignment": the median
+ * rollout-to-learner KL over the first and the last 1,000 updates and the
+ * largest gradient norm before clipping.  "REINFORCE Zero" project page,
+ * section 01, Figure 2: batch-averaged D3, peak over median.)
+ *
+ * rz_grad_norms -- L2 norms of this path's two gradients.
+ *
+ *   d_hidden  [n_rows, H] fp32  dL/dhidden (device, 16-byte aligned; may be
+ *                               NULL when n_rows = 0)
+ *   d_lm_head [V, H]      fp32  dL/dW (device, 16-byte aligned)
+ *   norms     [2]         fp32  out (device): {||d_hidden||_2, ||d_lm_head||_2}
+ *
+ * Sums of squares are taken in float64 over fixed chunks of 16384 values
+ * and then over the chunks in a fixed tree, so the result is a pure
+ * function of the inputs and their sizes.  Workspace:
+ * rz_workspace_bytes(RZ_OP_GRAD_NORMS, n_rows, 0, H, V, 0).
+ */
+rz_status rz_grad_norms(const float* d_hidden, int64_t n_rows, int32_t H,
+                        const float* d_lm_head, int32_t V, float* norms,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * rz_response_diagnostics -- D3 and KL of each response (rz_diagnostics
+ * restricted to one response's valid rows).
+ *
+ *   logpi, logmu [n_rows] fp32, mask [n_rows] uint8 (may be NULL = all
+ *   valid), cu_rows [n_resp + 1] int32 as in rz_reinforce_zero_fwd_bwd
+ *   (all device).
+ *   d3, kl [n_resp] fp32 out (device): mean(expm1(d) - d) and mean(-d) over
+ *   response i's valid rows, d = logpi - logmu, accumulated in float64 in a
+ *   fixed order; NaN for a response with no valid row.
+ *   err_flag int32, may be NULL: RZ_DEVERR_CU_ROWS is or-ed in when a
+ *   response's range is not an ordered range inside [0, n_rows), or
+ *   cu_rows[0] != 0 or cu_rows[n_resp] != n_rows; such responses read NaN.
+ *
+ * No workspace.  n_resp = 0 is a no-op.
+ */
+rz_status rz_response_diagnostics(const float* logpi, const float* logmu,
+                                  const uint8_t* mask, const int32_t* cu_rows,
+                                  int64_t n_rows, int32_t n_resp, float* d3,
+                                  float* kl, int32_t* err_flag, void* stream);
+
+/*
+ * rz_run_summary -- the run-level view over per-step records (host memory,
+ * host code; no GPU work).
+ *
+ *   d3, kl, grad_norm [n_steps] fp32 host arrays of per-step values in
+ *   step order; any may be NULL, which makes its outputs NaN.
+ *   window            steps in each KL window (>= 1; a run shorter than
+ *                     the window uses all its steps for both).
+ *   out [7] float64 host: {D3 peak, D3 median, D3 peak / median, median KL
+ *   over the first `window` steps, median KL over the last `window` steps,
+ *   last / first, largest gradient norm}.
+ *
+ * The median of an even count is the mean of the two middle values.  An
+ * array holding a NaN gives NaN for its statistics; quotients follow IEEE
+ * division (a zero median, as in a run with D3 = 0 at every step, gives
+ * inf or NaN).  n_steps = 0 gives NaN throughout.
+ */
+rz_status rz_run_summary(const float* d3, const float* kl,
+                         const float* grad_norm, int64_t n_steps,
+                         int32_t window, double* out);
 
 /*
  * Kernel timer (measurement support).  While enabled, every kernel launch of

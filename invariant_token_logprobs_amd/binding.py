@@ -18,6 +18,7 @@ RZ_OP_TOKEN_LOGPROBS = 0
 RZ_OP_FWD_BWD = 1
 RZ_OP_DIAGNOSTICS = 2
 RZ_OP_SAMPLE = 3
+RZ_OP_GRAD_NORMS = 4
 
 RZ_DEVERR_TOKEN = 1
 RZ_DEVERR_GROUP = 2
@@ -29,6 +30,7 @@ _STATUS = {0: "RZ_OK", -1: "RZ_ERR_INVALID_ARG", -2: "RZ_ERR_UNSUPPORTED",
 EXPORTS = [
     "rz_workspace_bytes", "rz_status_string", "rz_token_logprobs",
     "rz_reinforce_zero_fwd_bwd", "rz_diagnostics", "rz_sample_tokens",
+    "rz_grad_norms", "rz_response_diagnostics", "rz_run_summary",
     "rz_timing_enable", "rz_timing_num_kernels", "rz_timing_kernel_name",
     "rz_timing_read",
 ]
@@ -74,6 +76,14 @@ def load_library():
     lib.rz_sample_tokens.argtypes = [vp, vp, vp, i64, i32, i32, ctypes.c_int,
                                      ctypes.c_uint64, vp, vp, vp, vp, sz, vp]
     lib.rz_sample_tokens.restype = ctypes.c_int
+    lib.rz_grad_norms.argtypes = [vp, i64, i32, vp, i32, vp, vp, sz, vp]
+    lib.rz_grad_norms.restype = ctypes.c_int
+    lib.rz_response_diagnostics.argtypes = [vp, vp, vp, vp, i64, i32, vp, vp,
+                                            vp, vp]
+    lib.rz_response_diagnostics.restype = ctypes.c_int
+    lib.rz_run_summary.argtypes = [vp, vp, vp, i64, i32,
+                                   ctypes.POINTER(ctypes.c_double)]
+    lib.rz_run_summary.restype = ctypes.c_int
     lib.rz_timing_enable.argtypes = [ctypes.c_int]
     lib.rz_timing_enable.restype = ctypes.c_int
     lib.rz_timing_num_kernels.argtypes = []
@@ -291,6 +301,112 @@ def diagnostics(logpi, logmu, mask=None, *, workspace: Optional[Workspace] = Non
     _check(lib.rz_diagnostics(_ptr(logpi), _ptr(logmu), _ptr(mask), n, _ptr(diag),
                               _ptr(ws), nbytes, _stream(stream)), "rz_diagnostics")
     return diag
+
+
+# ------------------------------------------------------- run-level diagnostics
+def grad_norms(d_hidden, d_lm_head, *, workspace: Optional[Workspace] = None,
+               stream=None, out=None):
+    """(||d_hidden||_2, ||d_lm_head||_2) as a float32 device tensor [2]
+    (rz_grad_norms)."""
+    torch = _torch()
+    lib = load_library()
+    _need(d_lm_head, "d_lm_head", torch.float32, 2)
+    dev = d_lm_head.device
+    _need(d_hidden, "d_hidden", torch.float32, 2, dev)
+    N, H = d_hidden.shape
+    V = d_lm_head.shape[0]
+    if d_lm_head.shape[1] != H:
+        raise RzError("d_hidden and d_lm_head disagree on H")
+    norms = out if out is not None else torch.empty(2, dtype=torch.float32, device=dev)
+    nbytes = workspace_bytes(RZ_OP_GRAD_NORMS, N, 0, H, V, 0)
+    ws = _workspace(workspace, nbytes, dev)
+    _check(lib.rz_grad_norms(_ptr(d_hidden), N, H, _ptr(d_lm_head), V,
+                             _ptr(norms), _ptr(ws), nbytes, _stream(stream)),
+           "rz_grad_norms")
+    return norms
+
+
+def response_diagnostics(logpi, logmu, mask, cu_rows, *, err_flag=None,
+                         stream=None):
+    """Per-response (D3, KL), two float32 device tensors [n_resp]
+    (rz_response_diagnostics); mask may be None (all rows valid)."""
+    torch = _torch()
+    lib = load_library()
+    _need(logpi, "logpi", torch.float32, 1)
+    dev = logpi.device
+    _need(logmu, "logmu", torch.float32, 1, dev)
+    _need(cu_rows, "cu_rows", torch.int32, 1, dev)
+    if mask is not None:
+        _need(mask, "mask", torch.uint8, 1, dev)
+    n = logpi.shape[0]
+    B = cu_rows.shape[0] - 1
+    if B < 0 or logmu.shape[0] != n or (mask is not None and mask.shape[0] != n):
+        raise RzError("shape mismatch between logpi, logmu, mask and cu_rows")
+    d3 = torch.empty(B, dtype=torch.float32, device=dev)
+    kl = torch.empty(B, dtype=torch.float32, device=dev)
+    _check(lib.rz_response_diagnostics(_ptr(logpi), _ptr(logmu), _ptr(mask),
+                                       _ptr(cu_rows), n, B, _ptr(d3), _ptr(kl),
+                                       _ptr(err_flag), _stream(stream)),
+           "rz_response_diagnostics")
+    return d3, kl
+
+
+RUN_SUMMARY_KEYS = ("d3_peak", "d3_median", "d3_peak_over_median",
+                    "kl_median_first", "kl_median_last", "kl_median_ratio",
+                    "grad_norm_max")
+
+
+def run_summary(d3_steps, kl_steps, grad_norm_steps, window: int = 1000) -> dict:
+    """Run-level view over per-step host values (rz_run_summary): sequences
+    of floats (or None) in step order, all of the same length."""
+    import numpy as np
+    lib = load_library()
+    arrs = [None if a is None else np.ascontiguousarray(a, dtype=np.float32)
+            for a in (d3_steps, kl_steps, grad_norm_steps)]
+    lens = {a.shape[0] for a in arrs if a is not None}
+    if len(lens) > 1 or any(a is not None and a.ndim != 1 for a in arrs):
+        raise RzError("per-step arrays must be 1-D and of one length")
+    n = lens.pop() if lens else 0
+    out = (ctypes.c_double * 7)()
+    ptrs = [None if a is None else ctypes.c_void_p(a.ctypes.data) for a in arrs]
+    _check(lib.rz_run_summary(*ptrs, n, int(window), out), "rz_run_summary")
+    return dict(zip(RUN_SUMMARY_KEYS, list(out)))
+
+
+class RunTracker:
+    """Per-step D3, KL and gradient norm of a training run, kept on the GPU
+    until a summary is asked for (one copy to the host then, none per step).
+
+    record(diag, grad_norm): diag is the [2] (D3, KL) output of
+    reinforce_zero_fwd_bwd or diagnostics; grad_norm a one-element tensor,
+    e.g. grad_norms(...)[1:] for this path's parameter gradient or the
+    trainer's global norm before clipping."""
+
+    def __init__(self, device, window: int = 1000, capacity: int = 4096):
+        torch = _torch()
+        self.window = int(window)
+        self.n = 0
+        self.buf = torch.empty((max(1, capacity), 3), dtype=torch.float32,
+                               device=device)
+
+    def record(self, diag, grad_norm):
+        torch = _torch()
+        if self.n == self.buf.shape[0]:
+            grown = torch.empty((2 * self.n, 3), dtype=torch.float32,
+                                device=self.buf.device)
+            grown[: self.n].copy_(self.buf)
+            self.buf = grown
+        self.buf[self.n, 0:2].copy_(diag.reshape(2))
+        self.buf[self.n, 2:3].copy_(grad_norm.reshape(1))
+        self.n += 1
+
+    def values(self):
+        """(d3, kl, grad_norm) per step as host float32 arrays."""
+        h = self.buf[: self.n].cpu().numpy()
+        return h[:, 0].copy(), h[:, 1].copy(), h[:, 2].copy()
+
+    def summary(self) -> dict:
+        return run_summary(*self.values(), window=self.window)
 
 
 # ------------------------------------------------------------ kernel timer

@@ -1,9 +1,11 @@
 // rz_api.hip -- the C ABI of librz (declared in include/rz.h): host-side
 // argument checks, workspace layout and the launch sequence of each entry
 // point on the caller's stream.  No allocation, no host synchronisation.
+#include <math.h>
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "../../include/rz.h"
@@ -69,6 +71,20 @@ size_t carve_smp(Carver& c, int64_t n, int32_t V, SmpWs* w) {
   t.partials = c.take<float2>(sizeof(float2) * (size_t)nt * (size_t)n);
   t.cand = c.take<float2>(sizeof(float2) * (size_t)nt * (size_t)n);
   t.ztgt = c.take<float>(sizeof(float) * (size_t)n);
+  if (w) *w = t;
+  return c.off;
+}
+
+// ---- grad_norms layout: float64 chunk sums of each gradient ----
+constexpr int64_t kMaxNormElems = (int64_t)1 << 36;  // 256 GiB of fp32
+struct GnWs {
+  double* ph;
+  double* pw;
+};
+size_t carve_gn(Carver& c, int64_t n, int32_t H, int32_t V, GnWs* w) {
+  GnWs t;
+  t.ph = c.take<double>(sizeof(double) * (norm_partials(n * H) + 1));
+  t.pw = c.take<double>(sizeof(double) * (norm_partials((int64_t)V * H) + 1));
   if (w) *w = t;
   return c.off;
 }
@@ -235,8 +251,52 @@ size_t rz_workspace_bytes(rz_op op, int64_t n_rows, int32_t n_resp, int32_t H,
     case RZ_OP_SAMPLE:
       if (!dims_ok(H, V, dt)) return 0;
       return n_rows == 0 ? 0 : carve_smp(c, n_rows, V, nullptr);
+    case RZ_OP_GRAD_NORMS:
+      if (H <= 0 || H > RZ_MAX_HIDDEN || V <= 0 || V > RZ_MAX_VOCAB) return 0;
+      return carve_gn(c, n_rows, H, V, nullptr);
   }
   return 0;
+}
+
+rz_status rz_grad_norms(const float* d_hidden, int64_t n_rows, int32_t H,
+                        const float* d_lm_head, int32_t V, float* norms,
+                        void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (n_rows < 0 || n_rows > RZ_MAX_ROWS) return RZ_ERR_INVALID_ARG;
+  if (H <= 0 || H > RZ_MAX_HIDDEN || V <= 0 || V > RZ_MAX_VOCAB)
+    return RZ_ERR_INVALID_ARG;
+  if (!norms || !d_lm_head || (n_rows > 0 && !d_hidden))
+    return RZ_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(d_hidden) |
+       reinterpret_cast<uintptr_t>(d_lm_head)) & 15)
+    return RZ_ERR_INVALID_ARG;
+  if (n_rows * H > kMaxNormElems || (int64_t)V * H > kMaxNormElems)
+    return RZ_ERR_INVALID_ARG;
+  Carver meas{nullptr};
+  const size_t need = carve_gn(meas, n_rows, H, V, nullptr);
+  rz_status st = ws_check(workspace, workspace_bytes, need);
+  if (st != RZ_OK) return st;
+  Carver c{reinterpret_cast<char*>(workspace)};
+  GnWs w;
+  carve_gn(c, n_rows, H, V, &w);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  RZ_TRY(launch_grad_norm(d_hidden, n_rows * H, w.ph, norms, s));
+  RZ_TRY(launch_grad_norm(d_lm_head, (int64_t)V * H, w.pw, norms + 1, s));
+  return RZ_OK;
+}
+
+rz_status rz_response_diagnostics(const float* logpi, const float* logmu,
+                                  const uint8_t* mask, const int32_t* cu_rows,
+                                  int64_t n_rows, int32_t n_resp, float* d3,
+                                  float* kl, int32_t* err_flag, void* stream) {
+  if (n_rows < 0 || n_rows > RZ_MAX_ROWS) return RZ_ERR_INVALID_ARG;
+  if (n_resp < 0 || n_resp > (1 << 24)) return RZ_ERR_INVALID_ARG;
+  if (n_resp == 0) return RZ_OK;
+  if (!cu_rows || !d3 || !kl || (n_rows > 0 && (!logpi || !logmu)))
+    return RZ_ERR_INVALID_ARG;
+  RZ_TRY(launch_resp_diag(logpi, logmu, mask, cu_rows, n_resp, n_rows, d3, kl,
+                          err_flag, reinterpret_cast<hipStream_t>(stream)));
+  return RZ_OK;
 }
 
 rz_status rz_sample_tokens(const void* hidden, const void* lm_head,
@@ -402,6 +462,45 @@ rz_status rz_reinforce_zero_fwd_bwd(
   // a9: exact one-hot part of dW
   RZ_TRY(launch_dw_fix(dt, w.nvalid, N, w.tokv, w.idx, w.coef, hidden, H, V,
                        w.counts, w.cursor, w.offsets, w.sorted, d_lm_head, s));
+  return RZ_OK;
+}
+
+rz_status rz_run_summary(const float* d3, const float* kl,
+                         const float* grad_norm, int64_t n_steps,
+                         int32_t window, double* out) {
+  if (!out || n_steps < 0 || window < 1) return RZ_ERR_INVALID_ARG;
+  const double qnan = NAN;
+  // median of x[lo, hi), the mean of the two middle values for an even count;
+  // NaN when the range is empty or holds a NaN
+  auto median = [&](const float* x, int64_t lo, int64_t hi) {
+    if (!x || hi <= lo) return qnan;
+    std::vector<double> v(x + lo, x + hi);
+    for (double e : v)
+      if (e != e) return qnan;
+    const size_t m = v.size() / 2;
+    std::nth_element(v.begin(), v.begin() + m, v.end());
+    const double upper = v[m];
+    if (v.size() % 2) return upper;
+    const double lower = *std::max_element(v.begin(), v.begin() + m);
+    return 0.5 * (lower + upper);
+  };
+  auto maximum = [&](const float* x) {
+    if (!x || n_steps == 0) return qnan;
+    double m = -INFINITY;
+    for (int64_t i = 0; i < n_steps; ++i) {
+      if (x[i] != x[i]) return qnan;
+      m = std::max(m, (double)x[i]);
+    }
+    return m;
+  };
+  const int64_t w = std::min<int64_t>(window, n_steps);
+  out[0] = maximum(d3);
+  out[1] = median(d3, 0, n_steps);
+  out[2] = out[0] / out[1];
+  out[3] = median(kl, 0, w);
+  out[4] = median(kl, n_steps - w, n_steps);
+  out[5] = out[4] / out[3];
+  out[6] = maximum(grad_norm);
   return RZ_OK;
 }
 

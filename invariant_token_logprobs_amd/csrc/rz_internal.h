@@ -35,6 +35,8 @@ enum KernelId {
   K_TARGET_LOGIT,    // z[t, a_t] for the gather
   K_FWD_SAMPLE,      // rollout-side logits GEMM with the draw in the epilogue
   K_DRAW_MERGE,      // per-row best draw over the vocab tiles
+  K_GRAD_NORM,       // run-level: gradient L2 norms
+  K_RESP_DIAG,       // run-level: per-response D3 and KL
   K_NUM_KERNELS
 };
 
@@ -73,6 +75,13 @@ hipError_t launch_fwd_sample(int dt, const void* hidden, int64_t n,
                              hipStream_t s);
 hipError_t launch_draw_merge(const float2* cand, int64_t ldp, int nt, int64_t n,
                              int* tokens, hipStream_t s);
+size_t norm_partials(int64_t n);
+hipError_t launch_grad_norm(const float* x, int64_t n, double* partials,
+                            float* norm, hipStream_t s);
+hipError_t launch_resp_diag(const float* logpi, const float* logmu,
+                            const uint8_t* mask, const int* cu, int B,
+                            int64_t n, float* d3, float* kl, int* err,
+                            hipStream_t s);
 hipError_t launch_lse_merge(const float2* partials, int64_t ldp, int nt,
                             DevRows rows, const float* ztgt,
                             const int* row_tokens, int V, float* lse_out,

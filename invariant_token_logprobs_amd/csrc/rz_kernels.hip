@@ -787,6 +787,81 @@ __global__ __launch_bounds__(256) void k_diag_final(const DiagPartial* in,
 }
 
 // ===================================================================
+// Run-level diagnostics ([P2] section 4 "What happens without alignment":
+// the largest gradient norm; [P2] section 3, Figure 1: D3 per update).
+// Gradient norms: sums of squares in float64 over fixed 16384-value chunks
+// (each a fixed tree), then one fixed tree over the chunks.
+// ===================================================================
+constexpr int kNormChunk = 16384;
+
+__global__ __launch_bounds__(256) void k_sumsq_partial(const float* __restrict__ x,
+                                                       int64_t n, double* out) {
+  __shared__ double shd[256];
+  const int64_t base = (int64_t)blockIdx.x * kNormChunk;
+  double acc = 0.0;
+#pragma unroll 4
+  for (int i = 0; i < kNormChunk / 1024; ++i) {
+    const int64_t t = base + 4 * ((int64_t)i * 256 + threadIdx.x);
+    if (t + 3 < n) {  // x is 16-byte aligned
+      const f32x4 v = *reinterpret_cast<const f32x4*>(x + t);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc += (double)v[j] * (double)v[j];
+    } else {
+      for (int j = 0; j < 4; ++j)
+        if (t + j < n) acc += (double)x[t + j] * (double)x[t + j];
+    }
+  }
+  acc = block_sum_d(acc, shd);
+  if (threadIdx.x == 0) out[blockIdx.x] = acc;
+}
+
+__global__ __launch_bounds__(256) void k_sumsq_final(const double* in, int nchunk,
+                                                     float* norm) {
+  __shared__ double shd[256];
+  double acc = 0.0;
+  for (int i = threadIdx.x; i < nchunk; i += 256) acc += in[i];
+  acc = block_sum_d(acc, shd);
+  if (threadIdx.x == 0) *norm = (float)sqrt(acc);
+}
+
+// Per-response D3 and KL: one wave per response, lane l takes its rows
+// l, l + 64, ... in order (float64), then a fixed xor tree; NaN for a
+// response without valid rows or with a bad cu_rows range.
+__global__ __launch_bounds__(256) void k_resp_diag(
+    const float* __restrict__ logpi, const float* __restrict__ logmu,
+    const uint8_t* __restrict__ mask, const int* __restrict__ cu, int B,
+    int64_t n, float* d3_out, float* kl_out, int* err) {
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (i >= B) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t r0 = cu[i], r1 = cu[i + 1];
+  const bool bad = r0 < 0 || r1 < r0 || r1 > n || (i == 0 && r0 != 0) ||
+                   (i == B - 1 && r1 != n);
+  double d3 = 0.0, kl = 0.0;
+  int c = 0;
+  if (!bad)
+    for (int64_t t = r0 + lane; t < r1; t += 64) {
+      if (mask && !mask[t]) continue;
+      const double d = (double)logpi[t] - (double)logmu[t];
+      d3 += expm1(d) - d;
+      kl += -d;
+      ++c;
+    }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    d3 += __shfl_xor(d3, o, 64);
+    kl += __shfl_xor(kl, o, 64);
+    c += __shfl_xor(c, o, 64);
+  }
+  if (lane == 0) {
+    const float qnan = __builtin_nanf("");
+    d3_out[i] = (!bad && c) ? (float)(d3 / c) : qnan;
+    kl_out[i] = (!bad && c) ? (float)(kl / c) : qnan;
+    if (bad && err) atomicOr(err, 4);
+  }
+}
+
+// ===================================================================
 // Transposes feeding the backward GEMMs their K-contiguous operands:
 // out[c, r] = in[row(r), c] for r < rows, and 0 for rows <= r < the row
 // count rounded up to 64 (the last K stage a GEMM reads; never past
@@ -1167,7 +1242,8 @@ const char* kernel_name(int k) {
       "diag_partial", "diag_final", "transpose_w",  "transpose_h",
       "bwd_dh_gemm", "bwd_dw_gemm", "fill",         "tok_hist",
       "scan",        "tok_scatter", "bucket_sort",  "dw_fix",
-      "target_logit", "fwd_sample_gemm", "draw_merge"};
+      "target_logit", "fwd_sample_gemm", "draw_merge", "grad_norm",
+      "resp_diag"};
   return (k >= 0 && k < K_NUM_KERNELS) ? names[k] : "?";
 }
 
@@ -1362,6 +1438,33 @@ hipError_t launch_diagnostics(const float* logpi, const float* logmu,
   }
   return timed(K_DIAG_FINAL, s, [&] {
     k_diag_final<<<1, 256, 0, s>>>(p, nchunk, diag);
+  });
+}
+
+size_t norm_partials(int64_t n) { return (size_t)cdiv(n, kNormChunk); }
+
+hipError_t launch_grad_norm(const float* x, int64_t n, double* partials,
+                            float* norm, hipStream_t s) {
+  const int nchunk = (int)norm_partials(n);
+  hipError_t e = hipSuccess;
+  if (nchunk > 0) {
+    e = timed(K_GRAD_NORM, s, [&] {
+      k_sumsq_partial<<<nchunk, 256, 0, s>>>(x, n, partials);
+    });
+    if (e != hipSuccess) return e;
+  }
+  return timed(K_GRAD_NORM, s, [&] {
+    k_sumsq_final<<<1, 256, 0, s>>>(partials, nchunk, norm);
+  });
+}
+
+hipError_t launch_resp_diag(const float* logpi, const float* logmu,
+                            const uint8_t* mask, const int* cu, int B,
+                            int64_t n, float* d3, float* kl, int* err,
+                            hipStream_t s) {
+  return timed(K_RESP_DIAG, s, [&] {
+    k_resp_diag<<<cdiv(B, 4), 256, 0, s>>>(logpi, logmu, mask, cu, B, n, d3,
+                                           kl, err);
   });
 }
 

@@ -25,7 +25,8 @@ Readings:
 * Run level: over the recorded steps, D3 peak / median; the median KL of the
   first and of the last `window` steps and their ratio; the largest gradient
   norm.  The median is the usual one (mean of the two middle values for an
-  even count).
+  even count).  Quotients are IEEE divisions (a zero median gives inf or
+  NaN); a NaN step value makes its statistics NaN.
 
 Parity status: pinned by tests/test_oracle_pins.py (hand cases, a library
 norm on a tiny array, permutation and scaling identities).
@@ -73,15 +74,19 @@ def run_summary(d3_steps, kl_steps, grad_norm_steps, window: int = 1000):
     kl = np.asarray(kl_steps, np.float64)
     g = np.asarray(grad_norm_steps, np.float64)
     w = min(window, len(kl))
-    first = float(np.median(kl[:w])) if w else np.nan
-    last = float(np.median(kl[-w:])) if w else np.nan
-    med = float(np.median(d3)) if len(d3) else np.nan
+    first = np.float64(np.median(kl[:w])) if w else np.float64(np.nan)
+    last = np.float64(np.median(kl[-w:])) if w else np.float64(np.nan)
+    peak = np.float64(np.max(d3)) if len(d3) else np.float64(np.nan)
+    med = np.float64(np.median(d3)) if len(d3) else np.float64(np.nan)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        # IEEE quotients: a run with D3 = 0 at every step has a zero median
+        ratio_d3, ratio_kl = peak / med, last / first
     return {
-        "d3_peak": float(np.max(d3)) if len(d3) else np.nan,
-        "d3_median": med,
-        "d3_peak_over_median": float(np.max(d3)) / med if len(d3) else np.nan,
-        "kl_median_first": first,
-        "kl_median_last": last,
-        "kl_median_ratio": last / first if w else np.nan,
+        "d3_peak": float(peak),
+        "d3_median": float(med),
+        "d3_peak_over_median": float(ratio_d3),
+        "kl_median_first": float(first),
+        "kl_median_last": float(last),
+        "kl_median_ratio": float(ratio_kl),
         "grad_norm_max": float(np.max(g)) if len(g) else np.nan,
     }

@@ -192,3 +192,69 @@ def test_sample_tokens_argument_errors(lib):
     nt = (151936 + 255) // 256
     big = lib.rz_workspace_bytes(rz.RZ_OP_SAMPLE, 4096, 1, 2560, 151936, BF16)
     assert big >= 2 * 8 * nt * 4096 + 4 * 4096
+
+
+# ----------------------------------------------------- run-level diagnostics
+def test_grad_norms_argument_errors(lib):
+    ws_need = rz.workspace_bytes(rz.RZ_OP_GRAD_NORMS, 100, 0, 64, 1000, 0)
+    assert ws_need > 0
+    assert rz.workspace_bytes(rz.RZ_OP_GRAD_NORMS, 100, 0, 0, 1000, 0) == 0
+    out = P
+    def gn(dh=P, n=100, H=64, dw=P, V=1000, o=out, ws=P, wsb=ws_need):
+        return lib.rz_grad_norms(dh, n, H, dw, V, o, ws, wsb, NULL)
+    assert gn(n=-1) == INVALID
+    assert gn(H=0) == INVALID
+    assert gn(V=0) == INVALID
+    assert gn(o=NULL) == INVALID
+    assert gn(dw=NULL) == INVALID
+    assert gn(dh=NULL) == INVALID
+    assert gn(dh=ctypes.c_void_p(0x1004)) == INVALID       # not 16-byte aligned
+    assert gn(ws=NULL) == WORKSPACE
+    assert gn(wsb=ws_need - 1) == WORKSPACE
+    assert gn(ws=ctypes.c_void_p(0x1010)) == WORKSPACE     # not 256-byte aligned
+
+
+def test_response_diagnostics_argument_errors(lib):
+    def rd(lp=P, lm=P, cu=P, n=10, B=2, d3=P, kl=P):
+        return lib.rz_response_diagnostics(lp, lm, NULL, cu, n, B, d3, kl, NULL, NULL)
+    assert rd(n=-1) == INVALID
+    assert rd(B=-1) == INVALID
+    assert rd(B=0) == OK                                     # no-op, no launch
+    assert rd(cu=NULL) == INVALID
+    assert rd(d3=NULL) == INVALID
+    assert rd(kl=NULL) == INVALID
+    assert rd(lp=NULL) == INVALID
+
+
+def test_run_summary_matches_the_oracle():
+    """rz_run_summary is host code: exact agreement with the oracle on the
+    same float32 values (odd and even counts, windows longer than the run,
+    zero medians, NaN steps, missing arrays)."""
+    import numpy as np
+    import oracle as O
+    rng = np.random.default_rng(12)
+    cases = []
+    for n in (1, 2, 3, 10, 999, 1000, 2501):
+        d3 = rng.gamma(0.5, 1e-3, size=n).astype(np.float32)
+        kl = rng.normal(1e-4, 1e-3, size=n).astype(np.float32)
+        g = rng.lognormal(0.0, 1.0, size=n).astype(np.float32)
+        for window in (1, 7, 1000):
+            cases.append((d3, kl, g, window))
+    z = np.zeros(6, np.float32)
+    cases.append((z, z, z, 3))
+    cases.append((np.array([0.1, np.nan, 0.3], np.float32),
+                  np.array([1.0, 2.0, 4.0], np.float32),
+                  np.array([np.nan, 1.0, 2.0], np.float32), 2))
+    for d3, kl, g, window in cases:
+        got = rz.run_summary(d3, kl, g, window)
+        want = O.run_summary(d3.astype(np.float64), kl.astype(np.float64),
+                             g.astype(np.float64), window)
+        for k in rz.RUN_SUMMARY_KEYS:
+            a, b = got[k], want[k]
+            assert (np.isnan(a) and np.isnan(b)) or a == b, (len(d3), window, k, a, b)
+    empty = rz.run_summary(None, None, None)
+    assert all(np.isnan(v) for v in empty.values())
+    with pytest.raises(rz.RzError):
+        rz.run_summary([1.0], [1.0], [1.0], window=0)
+    with pytest.raises(rz.RzError):
+        rz.run_summary([1.0, 2.0], [1.0], [1.0])

@@ -531,3 +531,16 @@ def test_run_summary_hand_case():
     assert s["grad_norm_max"] == 38.27
     # even count: the mean of the two middle values
     assert O.run_summary([1.0, 2.0, 4.0, 8.0], [1.0], [0.0])["d3_median"] == 3.0
+    # a run at diff 0 has D3 = 0 at every step: the quotient is IEEE 0/0
+    z = O.run_summary([0.0, 0.0, 0.0], [0.0, 0.0], [1.0], window=1)
+    assert z["d3_peak"] == 0.0 and np.isnan(z["d3_peak_over_median"])
+    assert np.isnan(z["kl_median_ratio"])
+    assert O.run_summary([0.0, 0.0, 2.0], [1.0], [1.0])["d3_peak_over_median"] == np.inf
+    # a NaN step value (a step without valid tokens) poisons its statistics
+    n = O.run_summary([0.1, np.nan, 0.2], [1.0, 2.0], [3.0, np.nan], window=1)
+    assert np.isnan(n["d3_peak"]) and np.isnan(n["d3_median"])
+    assert n["kl_median_first"] == 1.0 and n["kl_median_last"] == 2.0
+    assert np.isnan(n["grad_norm_max"])
+    # a window longer than the run takes all of it for both medians
+    w = O.run_summary([1.0], [3.0, 1.0, 2.0], [0.0], window=1000)
+    assert w["kl_median_first"] == w["kl_median_last"] == 2.0
