@@ -2,6 +2,7 @@
 per step on the Qwen3-4B tool-use shape, on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--mode learner|sample|diag]
 
 A step is one rz_reinforce_zero_fwd_bwd call over the whole synthetic batch
 (inputs already resident in HBM).  Prints ONE JSON line with the throughput
@@ -105,6 +106,18 @@ def cpu_baseline(b, logmu, max_valid):
                        f"(BLAS threads {blas_threads})")}
 
 
+def copy_calibration(torch, dev):
+    """One plain 1 GiB device copy, so a counter run can scale its byte
+    counters by what they read for a known transfer."""
+    x = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    y.copy_(x)
+    torch.cuda.synchronize()
+    log("copy calibration: 1 GiB read + 1 GiB written by one copy kernel")
+    del x, y
+
+
 def bench_sample(args, torch, rz, synth, dev):
     """The rollout-side draw at decode size: rz_sample_tokens on
     --sample-rows live rows at the Qwen3-4B head (H 2560, V 151936, bf16)."""
@@ -172,6 +185,99 @@ def bench_sample(args, torch, rz, synth, dev):
     print(json.dumps(line), flush=True)
 
 
+def bench_diag(args, torch, rz, synth, dev):
+    """Run-level diagnostics over one learner step's outputs at the step's
+    shape: rz_grad_norms over dL/dhidden [N, H] and dL/dW [V, H] (fp32),
+    rz_response_diagnostics and rz_diagnostics over the N rows, and the
+    tracker's per-step record.  Inputs are seeded synthetic values of those
+    shapes (the step's own outputs are not needed to time a reduction)."""
+    wl = synth.WORKLOADS[args.workload]
+    _, lengths, mask_np, _, _ = synth.workload_layout(args.workload)
+    H, V = wl.H, wl.V
+    N, B = int(lengths.sum()), len(lengths)
+    cu_np = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    g = torch.Generator(device=dev)
+    g.manual_seed(4001)
+    dh = torch.randn((N, H), generator=g, device=dev) * 1e-4
+    dw = torch.randn((V, H), generator=g, device=dev) * 1e-6
+    rng = np.random.default_rng(4002)
+    lp_np = -rng.exponential(2.0, size=N).astype(np.float32)
+    lm_np = (lp_np + rng.normal(0.0, wl.sigma, size=N)).astype(np.float32)
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    logpi, logmu, mask, cu = up(lp_np), up(lm_np), up(mask_np), up(cu_np)
+    ws = rz.Workspace()
+    norms = torch.empty(2, dtype=torch.float32, device=dev)
+    diag = torch.empty(2, dtype=torch.float32, device=dev)
+    tracker = rz.RunTracker(dev, capacity=args.steps + args.warmup + 1)
+
+    def step():
+        rz.grad_norms(dh, dw, workspace=ws, out=norms)
+        d3, kl = rz.response_diagnostics(logpi, logmu, mask, cu)
+        rz.diagnostics(logpi, logmu, mask, workspace=ws, out=diag)
+        tracker.record(diag, norms[1:])
+        return d3, kl
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    rz.timing_enable(True)
+    rz.timing_read(reset=True)
+    torch.cuda.synchronize()
+    ts = time.perf_counter()
+    for _ in range(args.steps):
+        d3, kl = step()
+    torch.cuda.synchronize()
+    te = time.perf_counter()
+    kt = rz.timing_read(reset=True)
+    rz.timing_enable(False)
+    summary = tracker.summary()
+    assert np.isfinite(summary["grad_norm_max"]), "non-finite norm"
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
+    ms = (te - ts) * 1e3 / args.steps
+    tot_ms, launches = kt["grad_norm"]
+    grad_bytes = 4.0 * (N * H + V * H)          # each gradient read once
+    per_launch = grad_bytes * args.steps / launches
+    achieved = per_launch / (tot_ms / launches * 1e-3) / 1e9
+    kms = {k: v[0] / args.steps for k, v in kt.items() if v[1]}
+    log("per-pass kernel ms: " + ", ".join(f"{k}={v:.4f}" for k, v in
+                                           sorted(kms.items(), key=lambda x: -x[1])))
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle as O
+        h_dh = dh.cpu().numpy()
+        h_dw = dw.cpu().numpy()
+        t0 = time.perf_counter()
+        O.grad_norms(h_dh, h_dw)
+        O.response_diagnostics(lp_np, lm_np, mask_np, cu_np)
+        O.diagnostics(lp_np, lm_np, mask_np)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(1.0 / dt, 4), "unit": "passes/s",
+               "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+               "sample": f"one whole pass (N={N}, B={B}, H={H}, V={V}): float64 "
+                         f"NumPy norms + per-response and step D3/KL, {dt:.2f} s "
+                         "(host copies excluded)"}
+    line = {
+        "metric": "run-level diagnostic passes/s (gradient norms + per-response "
+                  "and step D3/KL + tracker record, Qwen3-4B step shape)",
+        "value": round(args.steps / (te - ts), 2), "unit": "passes/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+        "config": {"workload": f"run_diagnostics_{args.workload}", "hidden": H,
+                   "vocab": V, "rows": N, "responses": B},
+        "roofline": {"bound": "hbm", "kernel": "grad_norm",
+                     "achieved": round(achieved, 1), "peak": HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_GBS, 4),
+                     "traffic": None,
+                     "avg_launch_ms": round(tot_ms / launches, 4),
+                     "launches_per_step": launches // args.steps},
+        "cpu_baseline": cpu,
+        "kernel_ms_per_step": {k: round(v, 4) for k, v in kms.items()},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -181,9 +287,11 @@ def main():
     ap.add_argument("--cpu-valid", type=int, default=3072,
                     help="valid rows in the oracle's CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=("learner", "sample"), default="learner",
+    ap.add_argument("--mode", choices=("learner", "sample", "diag"),
+                    default="learner",
                     help="learner: the fused fwd/bwd step (the headline); "
-                         "sample: the rollout-side draw + record at decode size")
+                         "sample: the rollout-side draw + record at decode size; "
+                         "diag: the run-level diagnostics over a step's outputs")
     ap.add_argument("--sample-rows", type=int, default=1024,
                     help="live rows of the rollout batch in --mode sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -202,6 +310,8 @@ def main():
     dev = torch.device("cuda:0")
     if args.mode == "sample":
         return bench_sample(args, torch, rz, synth, dev)
+    if args.mode == "diag":
+        return bench_diag(args, torch, rz, synth, dev)
     t0 = time.time()
     b = synth.make_workload(args.workload)
     log(f"workload {b.name}: N={b.N} B={b.B} valid={b.n_valid} H={b.H} V={b.V} "
@@ -275,13 +385,7 @@ def main():
                                             sorted(kms.items(), key=lambda x: -x[1])))
 
     if args.copy_calibration:
-        x = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-        y = torch.empty_like(x)
-        torch.cuda.synchronize()
-        y.copy_(x)
-        torch.cuda.synchronize()
-        log("copy calibration: 1 GiB read + 1 GiB written by one copy kernel")
-        del x, y
+        copy_calibration(torch, dev)
 
     cpu = None
     if not args.no_cpu_baseline:

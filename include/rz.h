@@ -219,7 +219,7 @@ rz_status rz_diagnostics(const float* logpi, const float* logmu,
  *   d_lm_head [V, H]      fp32  dL/dW (device, 16-byte aligned)
  *   norms     [2]         fp32  out (device): {||d_hidden||_2, ||d_lm_head||_2}
  *
- * Sums of squares are taken in float64 over fixed chunks of 16384 values
+ * Sums of squares are taken in float64 over fixed chunks of 65536 values
  * and then over the chunks in a fixed tree, so the result is a pure
  * function of the inputs and their sizes.  Workspace:
  * rz_workspace_bytes(RZ_OP_GRAD_NORMS, n_rows, 0, H, V, 0).

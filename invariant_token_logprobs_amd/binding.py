@@ -406,7 +406,13 @@ class RunTracker:
         return h[:, 0].copy(), h[:, 1].copy(), h[:, 2].copy()
 
     def summary(self) -> dict:
-        return run_summary(*self.values(), window=self.window)
+        """rz_run_summary over the recorded steps, plus the count of
+        sequences a gate rejected: always 0, since this loss has no gate
+        (every valid token of every response enters it, unclipped)."""
+        out = run_summary(*self.values(), window=self.window)
+        out["steps"] = self.n
+        out["rejected_sequences"] = 0
+        return out
 
 
 # ------------------------------------------------------------ kernel timer

@@ -35,7 +35,8 @@ enum KernelId {
   K_TARGET_LOGIT,    // z[t, a_t] for the gather
   K_FWD_SAMPLE,      // rollout-side logits GEMM with the draw in the epilogue
   K_DRAW_MERGE,      // per-row best draw over the vocab tiles
-  K_GRAD_NORM,       // run-level: gradient L2 norms
+  K_GRAD_NORM,       // run-level: float64 sums of squares per chunk
+  K_GRAD_NORM_FINAL, // run-level: fixed tree over the chunks, sqrt
   K_RESP_DIAG,       // run-level: per-response D3 and KL
   K_NUM_KERNELS
 };

@@ -789,71 +789,112 @@ __global__ __launch_bounds__(256) void k_diag_final(const DiagPartial* in,
 // ===================================================================
 // Run-level diagnostics ([P2] section 4 "What happens without alignment":
 // the largest gradient norm; [P2] section 3, Figure 1: D3 per update).
-// Gradient norms: sums of squares in float64 over fixed 16384-value chunks
-// (each a fixed tree), then one fixed tree over the chunks.
 // ===================================================================
-constexpr int kNormChunk = 16384;
+// Sum over a 1024-thread block in a fixed order: an xor tree inside each
+// wave (every lane ends with the same bits), then the 16 wave sums in
+// ascending wave order.  sh holds 16 doubles.
+template <typename T>
+__device__ __forceinline__ T block1024_sum(T x, T* sh) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = x;
+  __syncthreads();
+  T r = sh[0];
+#pragma unroll
+  for (int w = 1; w < 16; ++w) r += sh[w];
+  __syncthreads();
+  return r;
+}
+
+// Gradient norms: sums of squares in float64 over fixed chunks of
+// kNormChunk values (thread t takes 16-byte groups t, t + 256, ... of its
+// chunk in order, then a 256-wide fixed tree), then one fixed tree over the
+// chunks.
+constexpr int kNormChunk = 65536;
+constexpr int kNormBatch = 8;  // 16-byte loads in flight per thread
 
 __global__ __launch_bounds__(256) void k_sumsq_partial(const float* __restrict__ x,
                                                        int64_t n, double* out) {
   __shared__ double shd[256];
   const int64_t base = (int64_t)blockIdx.x * kNormChunk;
   double acc = 0.0;
-#pragma unroll 4
-  for (int i = 0; i < kNormChunk / 1024; ++i) {
-    const int64_t t = base + 4 * ((int64_t)i * 256 + threadIdx.x);
-    if (t + 3 < n) {  // x is 16-byte aligned
-      const f32x4 v = *reinterpret_cast<const f32x4*>(x + t);
+  if (base + kNormChunk <= n) {  // whole chunk (x is 16-byte aligned)
+    const f32x4* p = reinterpret_cast<const f32x4*>(x + base) + threadIdx.x;
+    for (int i = 0; i < kNormChunk / 1024; i += kNormBatch) {
+      f32x4 v[kNormBatch];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc += (double)v[j] * (double)v[j];
-    } else {
-      for (int j = 0; j < 4; ++j)
-        if (t + j < n) acc += (double)x[t + j] * (double)x[t + j];
+      for (int j = 0; j < kNormBatch; ++j) v[j] = __builtin_nontemporal_load(p + (i + j) * 256);
+#pragma unroll
+      for (int j = 0; j < kNormBatch; ++j)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc += (double)v[j][k] * (double)v[j][k];
+    }
+  } else {  // the tail chunk: same order, element-guarded
+    for (int i = 0; i < kNormChunk / 1024; ++i) {
+      const int64_t t = base + 4 * ((int64_t)i * 256 + threadIdx.x);
+      for (int k = 0; k < 4; ++k)
+        if (t + k < n) acc += (double)x[t + k] * (double)x[t + k];
     }
   }
   acc = block_sum_d(acc, shd);
   if (threadIdx.x == 0) out[blockIdx.x] = acc;
 }
 
-__global__ __launch_bounds__(256) void k_sumsq_final(const double* in, int nchunk,
-                                                     float* norm) {
-  __shared__ double shd[256];
+__global__ __launch_bounds__(1024) void k_sumsq_final(const double* in, int nchunk,
+                                                      float* norm) {
+  __shared__ double shd[16];
   double acc = 0.0;
-  for (int i = threadIdx.x; i < nchunk; i += 256) acc += in[i];
-  acc = block_sum_d(acc, shd);
+  for (int i = threadIdx.x; i < nchunk; i += 1024) acc += in[i];
+  acc = block1024_sum(acc, shd);
   if (threadIdx.x == 0) *norm = (float)sqrt(acc);
 }
 
-// Per-response D3 and KL: one wave per response, lane l takes its rows
-// l, l + 64, ... in order (float64), then a fixed xor tree; NaN for a
-// response without valid rows or with a bad cu_rows range.
-__global__ __launch_bounds__(256) void k_resp_diag(
+// Per-response D3 and KL: one 1024-thread workgroup per response; thread t
+// takes rows r0 + t, r0 + t + 1024, ... in order (float64; rows are loaded
+// kRespBatch at a time), then block1024_sum.  The order is fixed relative to
+// the response's first row, so a response's values do not depend on where it
+// sits in the batch.  NaN for a response without valid rows or with a bad
+// cu_rows range.
+constexpr int kRespBatch = 8;
+
+__global__ __launch_bounds__(1024) void k_resp_diag(
     const float* __restrict__ logpi, const float* __restrict__ logmu,
     const uint8_t* __restrict__ mask, const int* __restrict__ cu, int B,
     int64_t n, float* d3_out, float* kl_out, int* err) {
-  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (i >= B) return;
-  const int lane = threadIdx.x & 63;
+  __shared__ double shd[16];
+  __shared__ int shc[16];
+  const int i = blockIdx.x;
   const int64_t r0 = cu[i], r1 = cu[i + 1];
   const bool bad = r0 < 0 || r1 < r0 || r1 > n || (i == 0 && r0 != 0) ||
                    (i == B - 1 && r1 != n);
   double d3 = 0.0, kl = 0.0;
   int c = 0;
-  if (!bad)
-    for (int64_t t = r0 + lane; t < r1; t += 64) {
-      if (mask && !mask[t]) continue;
-      const double d = (double)logpi[t] - (double)logmu[t];
-      d3 += expm1(d) - d;
-      kl += -d;
-      ++c;
-    }
+  if (!bad) {
+    for (int64_t t0 = r0 + threadIdx.x; t0 < r1; t0 += 1024 * kRespBatch) {
+      float a[kRespBatch], m[kRespBatch];
+      bool v[kRespBatch];
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    d3 += __shfl_xor(d3, o, 64);
-    kl += __shfl_xor(kl, o, 64);
-    c += __shfl_xor(c, o, 64);
+      for (int j = 0; j < kRespBatch; ++j) {
+        const int64_t t = t0 + (int64_t)j * 1024;
+        v[j] = t < r1;
+        a[j] = v[j] ? logpi[t] : 0.f;
+        m[j] = v[j] ? logmu[t] : 0.f;
+        if (v[j] && mask) v[j] = mask[t] != 0;
+      }
+#pragma unroll
+      for (int j = 0; j < kRespBatch; ++j)
+        if (v[j]) {
+          const double d = (double)a[j] - (double)m[j];
+          d3 += expm1(d) - d;
+          kl += -d;
+          ++c;
+        }
+    }
   }
-  if (lane == 0) {
+  d3 = block1024_sum(d3, shd);
+  kl = block1024_sum(kl, shd);
+  c = block1024_sum(c, shc);
+  if (threadIdx.x == 0) {
     const float qnan = __builtin_nanf("");
     d3_out[i] = (!bad && c) ? (float)(d3 / c) : qnan;
     kl_out[i] = (!bad && c) ? (float)(kl / c) : qnan;
@@ -1243,7 +1284,7 @@ const char* kernel_name(int k) {
       "bwd_dh_gemm", "bwd_dw_gemm", "fill",         "tok_hist",
       "scan",        "tok_scatter", "bucket_sort",  "dw_fix",
       "target_logit", "fwd_sample_gemm", "draw_merge", "grad_norm",
-      "resp_diag"};
+      "grad_norm_final", "resp_diag"};
   return (k >= 0 && k < K_NUM_KERNELS) ? names[k] : "?";
 }
 
@@ -1453,8 +1494,8 @@ hipError_t launch_grad_norm(const float* x, int64_t n, double* partials,
     });
     if (e != hipSuccess) return e;
   }
-  return timed(K_GRAD_NORM, s, [&] {
-    k_sumsq_final<<<1, 256, 0, s>>>(partials, nchunk, norm);
+  return timed(K_GRAD_NORM_FINAL, s, [&] {
+    k_sumsq_final<<<1, 1024, 0, s>>>(partials, nchunk, norm);
   });
 }
 
@@ -1463,8 +1504,7 @@ hipError_t launch_resp_diag(const float* logpi, const float* logmu,
                             int64_t n, float* d3, float* kl, int* err,
                             hipStream_t s) {
   return timed(K_RESP_DIAG, s, [&] {
-    k_resp_diag<<<cdiv(B, 4), 256, 0, s>>>(logpi, logmu, mask, cu, B, n, d3,
-                                           kl, err);
+    k_resp_diag<<<B, 1024, 0, s>>>(logpi, logmu, mask, cu, B, n, d3, kl, err);
   });
 }
 

@@ -33,7 +33,7 @@ def _norms(dh, dw):
 @pytest.mark.parametrize("N,H,V", [(1000, 320, 3001), (0, 64, 7), (3, 37, 5),
                                    (129, 2560, 1)])
 def test_grad_norms_parity(N, H, V):
-    """Several 16384-value chunks with a ragged tail, an empty d_hidden, H
+    """Several 65536-value chunks with a ragged tail, an empty d_hidden, H
     not a multiple of 4 (the scalar tail path), a one-row d_lm_head."""
     rng = np.random.default_rng(N + 7 * H + V)
     dh = (rng.standard_normal((N, H)) * 1e-3).astype(np.float32)
@@ -189,5 +189,6 @@ def test_run_tracker_matches_the_oracle():
                          g.astype(np.float64), window=1000)
     for k, v in want.items():
         assert got[k] == v, (k, got[k], v)
+    assert got["steps"] == steps and got["rejected_sequences"] == 0
     del dev_vals
     torch.cuda.empty_cache()
