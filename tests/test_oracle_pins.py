@@ -544,3 +544,106 @@ def test_run_summary_hand_case():
     # a window longer than the run takes all of it for both medians
     w = O.run_summary([1.0], [3.0, 1.0, 2.0], [0.0], window=1000)
     assert w["kl_median_first"] == w["kl_median_last"] == 2.0
+
+
+# ------------------------------------------------------------ MX-format head
+def test_e2m1_values_of_the_specification():
+    # OCP MX v1.0: E2M1 magnitudes 0, 0.5 (the subnormal), 1 (smallest
+    # normal), 1.5, 2, 3, 4, 6 (largest); bit 3 is the sign
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    got = O.decode_e2m1(np.arange(16))
+    assert got[:8].tolist() == mags
+    assert (-got[8:]).tolist() == mags
+    assert math.copysign(1.0, got[8]) == -1.0          # code 8 is -0
+
+
+def test_e4m3_against_the_specification_and_torch():
+    import torch
+    codes = np.arange(256)
+    got = O.decode_e4m3(codes)
+    ref = torch.from_numpy(codes.astype(np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert np.flatnonzero(np.isnan(got)).tolist() == [0x7F, 0xFF]
+    # listed values: largest normal 448, smallest normal 2^-6, largest
+    # subnormal 0.875 * 2^-6, smallest subnormal 2^-9
+    assert got[0x7E] == 448.0 and got[0x08] == 2.0 ** -6
+    assert got[0x07] == 0.875 * 2.0 ** -6 and got[0x01] == 2.0 ** -9
+    assert got[0xFE] == -448.0
+
+
+def test_e8m0_against_torch():
+    import torch
+    codes = np.arange(256)
+    got = O.decode_e8m0(codes)
+    ref = torch.from_numpy(codes.astype(np.uint8)).view(torch.float8_e8m0fnu).double().numpy()
+    assert np.isnan(got[255]) and np.isnan(ref[255])
+    assert np.array_equal(got[:255], ref[:255])
+    assert got[127] == 1.0 and got[0] == 2.0 ** -127 and got[254] == 2.0 ** 127
+
+
+def test_unpack_fp4_nibble_order():
+    codes = O.unpack_fp4(np.array([[0x21, 0xF8]], dtype=np.uint8))
+    assert codes.tolist() == [[1, 2, 8, 15]]
+    assert O.decode_e2m1(codes).tolist() == [[0.5, 1.0, -0.0, -6.0]]
+
+
+def test_dequantize_head_blocks_and_invalid_scales():
+    # two rows, H = 64: two blocks per row with their own scales
+    V, H = 2, 64
+    codes = np.full((V, H), 0x38, dtype=np.uint8)        # E4M3 1.0
+    codes[1, 40] = 0x7F                                   # a NaN code
+    scales = np.array([[127 + 3, 127 - 2], [127 + 120, 127 - 124]], dtype=np.uint8)
+    W = O.dequantize_head(codes, scales, "mxfp8")
+    assert np.all(W[0, :32] == 8.0) and np.all(W[0, 32:] == 0.25)
+    assert np.all(np.isnan(W[1, :32]))                    # s = 120 > 119
+    assert np.all(W[1, 32:40] == 2.0 ** -124) and np.isnan(W[1, 40])
+    # E2M1: the NaN scale code and s = 126 > 125 are invalid, s = -127 valid
+    packed = np.full((V, H // 2), 0x77, dtype=np.uint8)   # 6.0, 6.0
+    sc4 = np.array([[255, 127 + 125], [127 + 126, 0]], dtype=np.uint8)
+    W4 = O.dequantize_head(packed, sc4, "mxfp4")
+    assert np.all(np.isnan(W4[0, :32])) and np.all(W4[0, 32:] == 6.0 * 2.0 ** 125)
+    assert np.all(np.isnan(W4[1, :32])) and np.all(W4[1, 32:] == 6.0 * 2.0 ** -127)
+
+
+def test_valid_dequantized_values_are_bfloat16_numbers():
+    """The reading's exactness claim, checked by brute force: every element
+    code at every valid scale (the range ends included) round-trips through
+    bfloat16 unchanged, and one step past each end does not for some code."""
+    import torch
+
+    def exact(v):
+        t = torch.from_numpy(v)
+        return bool(torch.equal(t.to(torch.bfloat16).double(), t))
+
+    for fmt, vals in (("mxfp4", O.decode_e2m1(np.arange(16))),
+                      ("mxfp8", O.decode_e4m3(np.arange(256)))):
+        vals = vals[~np.isnan(vals)]
+        lo, hi = O.scale_range(fmt)
+        for s in range(lo, hi + 1):
+            assert exact(vals * 2.0 ** s), (fmt, s)
+        assert not exact(vals * 2.0 ** (hi + 1)), fmt
+        if lo > -127:
+            assert not exact(vals * 2.0 ** (lo - 1)), fmt
+
+
+def test_token_logprobs_mx_is_the_bf16_head_definition():
+    rng = np.random.default_rng(3)
+    V, H, n = 40, 64, 5
+    codes = rng.integers(0, 256, size=(V, H // 2), dtype=np.uint8)
+    scales = rng.integers(120, 125, size=(V, H // 32), dtype=np.uint8)
+    hidden = rng.normal(size=(n, H))
+    tok = rng.integers(0, V, size=n)
+    lp, lse = O.token_logprobs_mx(hidden, codes, scales, "mxfp4", tok)
+    # brute force from the decoded table, element by element
+    W = np.zeros((V, H))
+    table = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    for v in range(V):
+        for k in range(H):
+            b = int(codes[v, k // 2])
+            c = (b & 0xF) if k % 2 == 0 else (b >> 4)
+            W[v, k] = (-1 if c & 8 else 1) * table[c & 7] * 2.0 ** (int(scales[v, k // 32]) - 127)
+    z = hidden @ W.T
+    want = z[np.arange(n), tok] - np.log(np.exp(z - z.max(1, keepdims=True)).sum(1)) - z.max(1)
+    assert np.allclose(lp, want, rtol=0, atol=1e-12)
