@@ -77,10 +77,17 @@ typedef enum {
   RZ_OP_GRAD_NORMS = 4
 } rz_op;
 
+/* element format of an MX-format LM head (OCP Microscaling Formats v1.0) */
+typedef enum {
+  RZ_MX_FP4 = 0, /* MXFP4: E2M1 elements, two per byte (low nibble first) */
+  RZ_MX_FP8 = 1  /* MXFP8: E4M3 elements, one per byte                     */
+} rz_mx_format;
+
 /* device-side error bits written to *err_flag */
 #define RZ_DEVERR_TOKEN 1   /* a token id outside [0, V): its logprob is NaN  */
 #define RZ_DEVERR_GROUP 2   /* a group id outside [0, n_resp): loss/adv NaN    */
 #define RZ_DEVERR_CU_ROWS 4 /* cu_rows not 0..n_rows monotone: loss/adv NaN   */
+#define RZ_DEVERR_MX_SCALE 8 /* an MX block scale outside the exact range     */
 
 /* Limits checked on the host. */
 #define RZ_MAX_ROWS ((int64_t)1 << 30)
@@ -203,6 +210,34 @@ rz_status rz_diagnostics(const float* logpi, const float* logmu,
                          const uint8_t* mask, int64_t n, float* diag,
                          void* workspace, size_t workspace_bytes,
                          void* stream);
+
+/*
+ * rz_dequantize_head -- an LM head stored at release precision, as MX
+ * blocks, expanded to the bfloat16 head every other entry point takes
+ * ("Zero mismatch, simple async RL", vLLM blog: the aligned path keeps
+ * release precision, FP8 and MXFP4 weights included, with zero mismatch
+ * between rollout and trainer).
+ *
+ *   codes   RZ_MX_FP4: [V, H / 2] bytes, element 2j of a row in the low
+ *           nibble of byte j; RZ_MX_FP8: [V, H] bytes (device, 16-byte aligned)
+ *   scales  [V, H / 32] E8M0 bytes: block b of row v covers elements
+ *           32 b .. 32 b + 31 and scales them by 2^(scales[v, b] - 127)
+ *   lm_head [V, H] bf16 out (device, 16-byte aligned)
+ *   err_flag int32, may be NULL: RZ_DEVERR_MX_SCALE is or-ed in when a block
+ *           scale is the NaN code 255 or outside the exact range below
+ *
+ * Element values follow the OCP Microscaling Formats v1.0 encodings (E2M1:
+ * bias 1, largest 6; E4M3: bias 7, largest 448, S.1111.111 NaN).  With scale
+ * 2^s every value of a block is exactly a bfloat16 number when s <= 125
+ * (E2M1) or -124 <= s <= 119 (E4M3); such blocks are converted with no
+ * rounding, so running the bf16 entry points on the output is the MX head
+ * itself, and rollout and learner calls on it agree bit for bit.  Blocks
+ * outside the range are written as NaN; an E4M3 NaN code gives a NaN value.
+ * H must be a multiple of 32 (the GEMM entry points need 64).  No workspace.
+ */
+rz_status rz_dequantize_head(const uint8_t* codes, const uint8_t* scales,
+                             int32_t V, int32_t H, rz_mx_format fmt,
+                             void* lm_head, int32_t* err_flag, void* stream);
 
 /*
  * Run-level diagnostics ("Zero mismatch, simple async RL", vLLM blog,

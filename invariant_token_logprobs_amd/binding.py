@@ -23,6 +23,9 @@ RZ_OP_GRAD_NORMS = 4
 RZ_DEVERR_TOKEN = 1
 RZ_DEVERR_GROUP = 2
 RZ_DEVERR_CU_ROWS = 4
+RZ_DEVERR_MX_SCALE = 8
+
+RZ_MX_FORMATS = {"mxfp4": 0, "mxfp8": 1}
 
 _STATUS = {0: "RZ_OK", -1: "RZ_ERR_INVALID_ARG", -2: "RZ_ERR_UNSUPPORTED",
            -3: "RZ_ERR_WORKSPACE", -4: "RZ_ERR_HIP"}
@@ -31,6 +34,7 @@ EXPORTS = [
     "rz_workspace_bytes", "rz_status_string", "rz_token_logprobs",
     "rz_reinforce_zero_fwd_bwd", "rz_diagnostics", "rz_sample_tokens",
     "rz_grad_norms", "rz_response_diagnostics", "rz_run_summary",
+    "rz_dequantize_head",
     "rz_timing_enable", "rz_timing_num_kernels", "rz_timing_kernel_name",
     "rz_timing_read",
 ]
@@ -84,6 +88,8 @@ def load_library():
     lib.rz_run_summary.argtypes = [vp, vp, vp, i64, i32,
                                    ctypes.POINTER(ctypes.c_double)]
     lib.rz_run_summary.restype = ctypes.c_int
+    lib.rz_dequantize_head.argtypes = [vp, vp, i32, i32, ctypes.c_int, vp, vp, vp]
+    lib.rz_dequantize_head.restype = ctypes.c_int
     lib.rz_timing_enable.argtypes = [ctypes.c_int]
     lib.rz_timing_enable.restype = ctypes.c_int
     lib.rz_timing_num_kernels.argtypes = []
@@ -301,6 +307,31 @@ def diagnostics(logpi, logmu, mask=None, *, workspace: Optional[Workspace] = Non
     _check(lib.rz_diagnostics(_ptr(logpi), _ptr(logmu), _ptr(mask), n, _ptr(diag),
                               _ptr(ws), nbytes, _stream(stream)), "rz_diagnostics")
     return diag
+
+
+# ------------------------------------------------------------ MX-format head
+def dequantize_head(codes, scales, fmt: str, *, err_flag=None, stream=None,
+                    out=None):
+    """The bf16 head [V, H] of an MX-format head (rz_dequantize_head).
+
+    codes: uint8 [V, H/2] (fmt "mxfp4", two E2M1 codes per byte, low nibble
+    first) or [V, H] ("mxfp8", E4M3); scales: uint8 [V, H/32] E8M0."""
+    torch = _torch()
+    lib = load_library()
+    if fmt not in RZ_MX_FORMATS:
+        raise RzError(f"fmt must be one of {sorted(RZ_MX_FORMATS)}, got {fmt!r}")
+    _need(codes, "codes", torch.uint8, 2)
+    dev = codes.device
+    _need(scales, "scales", torch.uint8, 2, dev)
+    V = codes.shape[0]
+    H = codes.shape[1] * (2 if fmt == "mxfp4" else 1)
+    if tuple(scales.shape) != (V, H // 32) or H % 32:
+        raise RzError(f"scales must be [V, H/32] = [{V}, {H // 32}] with H % 32 == 0")
+    W = out if out is not None else torch.empty((V, H), dtype=torch.bfloat16, device=dev)
+    _check(lib.rz_dequantize_head(_ptr(codes), _ptr(scales), V, H,
+                                  RZ_MX_FORMATS[fmt], _ptr(W), _ptr(err_flag),
+                                  _stream(stream)), "rz_dequantize_head")
+    return W
 
 
 # ------------------------------------------------------- run-level diagnostics

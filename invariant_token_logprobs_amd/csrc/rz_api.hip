@@ -285,6 +285,21 @@ rz_status rz_grad_norms(const float* d_hidden, int64_t n_rows, int32_t H,
   return RZ_OK;
 }
 
+rz_status rz_dequantize_head(const uint8_t* codes, const uint8_t* scales,
+                             int32_t V, int32_t H, rz_mx_format fmt,
+                             void* lm_head, int32_t* err_flag, void* stream) {
+  if (fmt != RZ_MX_FP4 && fmt != RZ_MX_FP8) return RZ_ERR_UNSUPPORTED;
+  if (V <= 0 || V > RZ_MAX_VOCAB || H <= 0 || H > RZ_MAX_HIDDEN || H % 32)
+    return RZ_ERR_INVALID_ARG;
+  if (!codes || !scales || !lm_head) return RZ_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(codes) | reinterpret_cast<uintptr_t>(lm_head)) & 15)
+    return RZ_ERR_INVALID_ARG;
+  RZ_TRY(launch_mx_dequant(fmt == RZ_MX_FP4 ? 0 : 1, codes, scales,
+                           (int64_t)V * (H / 32), lm_head, err_flag,
+                           reinterpret_cast<hipStream_t>(stream)));
+  return RZ_OK;
+}
+
 rz_status rz_response_diagnostics(const float* logpi, const float* logmu,
                                   const uint8_t* mask, const int32_t* cu_rows,
                                   int64_t n_rows, int32_t n_resp, float* d3,

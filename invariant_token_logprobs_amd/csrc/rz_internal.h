@@ -38,6 +38,7 @@ enum KernelId {
   K_GRAD_NORM,       // run-level: float64 sums of squares per chunk
   K_GRAD_NORM_FINAL, // run-level: fixed tree over the chunks, sqrt
   K_RESP_DIAG,       // run-level: per-response D3 and KL
+  K_MX_DEQUANT,      // MX-format head -> bf16
   K_NUM_KERNELS
 };
 
@@ -76,6 +77,8 @@ hipError_t launch_fwd_sample(int dt, const void* hidden, int64_t n,
                              hipStream_t s);
 hipError_t launch_draw_merge(const float2* cand, int64_t ldp, int nt, int64_t n,
                              int* tokens, hipStream_t s);
+hipError_t launch_mx_dequant(int fmt, const uint8_t* codes, const uint8_t* scales,
+                             int64_t nblk, void* out, int* err, hipStream_t s);
 size_t norm_partials(int64_t n);
 hipError_t launch_grad_norm(const float* x, int64_t n, double* partials,
                             float* norm, hipStream_t s);

@@ -903,6 +903,69 @@ __global__ __launch_bounds__(1024) void k_resp_diag(
 }
 
 // ===================================================================
+// MX-format head -> bfloat16 ("Zero mismatch, simple async RL", vLLM blog:
+// the aligned path keeps release precision, FP8 and MXFP4 weights included).
+// Encodings of the OCP Microscaling Formats v1.0: E2M1 and E4M3 elements,
+// one E8M0 scale 2^(code - 127) per 32 consecutive values along H.  Each
+// value is built directly as a bf16 bit pattern with integer operations; the
+// scale range checked per block makes every value of the block exactly a
+// bf16 number (normal or subnormal), so nothing is rounded.
+// ===================================================================
+// k * 2^q as bf16 bits (0 <= k < 16; exact by the caller's range check).
+__device__ __forceinline__ uint32_t mx_bf16_bits(uint32_t k, int q, uint32_t sign) {
+  if (k == 0) return sign;
+  const int p = 31 - __builtin_clz(k);
+  const int e = q + p;
+  if (e >= -126) return sign | ((uint32_t)(e + 127) << 7) | ((k << (7 - p)) & 0x7Fu);
+  return sign | (k << (q + 133));  // subnormal: k 2^q = m 2^-133
+}
+
+template <int kFmt>  // 0: E2M1 (two codes per byte), 1: E4M3
+__global__ __launch_bounds__(256) void k_mx_dequant(const uint8_t* __restrict__ codes,
+                                                    const uint8_t* __restrict__ scales,
+                                                    int64_t nblk, uint32_t* __restrict__ out,
+                                                    int* err) {
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (b >= nblk) return;
+  const int sc = scales[b];
+  const int s = sc - 127;
+  const bool ok = sc != 255 && (kFmt == 0 ? s <= 125 : (s >= -124 && s <= 119));
+  uint32_t w[16];  // 32 bf16 values, element 2j in the low half of w[j]
+  if constexpr (kFmt == 0) {
+    const u32x4 c = *reinterpret_cast<const u32x4*>(codes + b * 16);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const uint32_t x = (c[j >> 3] >> (4 * (j & 7))) & 0xFu;  // bits 4j.. of the block
+      const uint32_t e = (x >> 1) & 3u, m = x & 1u;
+      const uint32_t v = mx_bf16_bits(e ? 2u + m : m, (e ? (int)e - 2 : -1) + s,
+                                      (x & 8u) << 12);
+      w[j >> 1] = (j & 1) ? (w[j >> 1] | (v << 16)) : v;
+    }
+  } else {
+    const u32x4 c0 = *reinterpret_cast<const u32x4*>(codes + b * 32);
+    const u32x4 c1 = *reinterpret_cast<const u32x4*>(codes + b * 32 + 16);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const uint32_t word = j < 16 ? c0[j >> 2] : c1[(j - 16) >> 2];
+      const uint32_t x = (word >> (8 * (j & 3))) & 0xFFu;
+      const uint32_t e = (x >> 3) & 15u, m = x & 7u;
+      uint32_t v = mx_bf16_bits(e ? 8u + m : m, (e ? (int)e - 10 : -9) + s,
+                                (x & 0x80u) << 8);
+      if (e == 15u && m == 7u) v = 0x7FC0u;  // the E4M3 NaN code
+      w[j >> 1] = (j & 1) ? (w[j >> 1] | (v << 16)) : v;
+    }
+  }
+  if (!ok) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) w[j] = 0x7FC07FC0u;
+    if (err) atomicOr(err, 8);
+  }
+  u32x4* o = reinterpret_cast<u32x4*>(out + b * 16);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = u32x4{w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]};
+}
+
+// ===================================================================
 // Transposes feeding the backward GEMMs their K-contiguous operands:
 // out[c, r] = in[row(r), c] for r < rows, and 0 for rows <= r < the row
 // count rounded up to 64 (the last K stage a GEMM reads; never past
@@ -1284,7 +1347,7 @@ const char* kernel_name(int k) {
       "bwd_dh_gemm", "bwd_dw_gemm", "fill",         "tok_hist",
       "scan",        "tok_scatter", "bucket_sort",  "dw_fix",
       "target_logit", "fwd_sample_gemm", "draw_merge", "grad_norm",
-      "grad_norm_final", "resp_diag"};
+      "grad_norm_final", "resp_diag", "mx_dequant"};
   return (k >= 0 && k < K_NUM_KERNELS) ? names[k] : "?";
 }
 
@@ -1479,6 +1542,19 @@ hipError_t launch_diagnostics(const float* logpi, const float* logmu,
   }
   return timed(K_DIAG_FINAL, s, [&] {
     k_diag_final<<<1, 256, 0, s>>>(p, nchunk, diag);
+  });
+}
+
+hipError_t launch_mx_dequant(int fmt, const uint8_t* codes, const uint8_t* scales,
+                             int64_t nblk, void* out, int* err, hipStream_t s) {
+  if (nblk == 0) return hipSuccess;
+  const int64_t grid = cdiv(nblk, 256);
+  uint32_t* o = reinterpret_cast<uint32_t*>(out);
+  return timed(K_MX_DEQUANT, s, [&] {
+    if (fmt == 0)
+      k_mx_dequant<0><<<grid, 256, 0, s>>>(codes, scales, nblk, o, err);
+    else
+      k_mx_dequant<1><<<grid, 256, 0, s>>>(codes, scales, nblk, o, err);
   });
 }
 

@@ -229,3 +229,33 @@ def random_rows(n: int, H: int, V: int, dtype: str, seed: int):
 def random_lm_head(V: int, H: int, dtype: str, seed: int) -> np.ndarray:
     rng = np.random.default_rng(np.random.PCG64(seed))
     return _normal(rng, (V, H), 0.02, dtype)
+
+
+def random_mx_head(V: int, H: int, fmt: str, seed: int, scale_code: int = 121):
+    """A release-precision head in MX storage, drawn directly as codes.
+
+    Element codes: a random sign and a magnitude code drawn with weights
+    falling off with the code (small magnitudes most common, as in a head
+    quantized from a bell-shaped distribution); E4M3 magnitude codes span
+    0x00 .. 0x7E (never the NaN code).  Scales: E8M0 code scale_code +
+    {-1, 0, +1} per 32-value block (121 = 2^-6, so values stay near 0.02).
+    Returns (codes, scales) as uint8 arrays: codes [V, H/2] packed two per
+    byte (low nibble first) for "mxfp4", [V, H] for "mxfp8"; scales
+    [V, H/32].
+    """
+    rng = np.random.default_rng(np.random.PCG64(seed))
+    if fmt == "mxfp4":
+        p = np.array([4, 4, 3, 3, 2, 2, 1, 1], dtype=np.float64)
+        mag = rng.choice(8, size=(V, H), p=p / p.sum()).astype(np.uint8)
+        elem = mag | (rng.integers(0, 2, size=(V, H), dtype=np.uint8) << 3)
+        codes = (elem[:, 0::2] | (elem[:, 1::2] << 4)).astype(np.uint8)
+    elif fmt == "mxfp8":
+        # exponent field weighted toward the middle, mantissa uniform
+        pe = np.array([1, 1, 2, 3, 4, 5, 6, 6, 5, 3, 1, .5, 0, 0, 0, 0])
+        e = rng.choice(16, size=(V, H), p=pe / pe.sum()).astype(np.uint8)
+        m = rng.integers(0, 8, size=(V, H), dtype=np.uint8)
+        codes = ((e << 3) | m | (rng.integers(0, 2, size=(V, H), dtype=np.uint8) << 7)).astype(np.uint8)
+    else:
+        raise ValueError(fmt)
+    scales = (scale_code + rng.integers(-1, 2, size=(V, H // 32))).astype(np.uint8)
+    return codes, scales

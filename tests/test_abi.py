@@ -258,3 +258,29 @@ def test_run_summary_matches_the_oracle():
         rz.run_summary([1.0], [1.0], [1.0], window=0)
     with pytest.raises(rz.RzError):
         rz.run_summary([1.0, 2.0], [1.0], [1.0])
+
+
+def test_dequantize_head_argument_errors(lib):
+    def dq(codes=P, scales=P, V=10, H=64, fmt=0, out=P):
+        return lib.rz_dequantize_head(codes, scales, V, H, fmt, out, NULL, NULL)
+    assert dq(fmt=2) == UNSUPPORTED
+    assert dq(V=0) == INVALID
+    assert dq(H=48) == INVALID                         # not a multiple of 32
+    assert dq(H=0) == INVALID
+    assert dq(codes=NULL) == INVALID
+    assert dq(scales=NULL) == INVALID
+    assert dq(out=NULL) == INVALID
+    assert dq(codes=ctypes.c_void_p(0x1008)) == INVALID   # not 16-byte aligned
+    assert dq(out=ctypes.c_void_p(0x1002)) == INVALID
+
+
+def test_random_mx_head_is_valid_storage():
+    """The generator's heads decode (oracle) to finite weights near 0.02."""
+    import numpy as np
+    import oracle as O
+    from invariant_token_logprobs_amd import synth
+    for fmt in ("mxfp4", "mxfp8"):
+        codes, scales = synth.random_mx_head(64, 128, fmt, 5)
+        W = O.dequantize_head(codes, scales, fmt)
+        assert W.shape == (64, 128) and np.isfinite(W).all()
+        assert 0.003 < W.std() < 0.1, (fmt, W.std())

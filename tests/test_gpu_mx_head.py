@@ -1,0 +1,122 @@
+"""The release-precision head on the GPU: rz_dequantize_head against the
+float64 oracle (oracle/mx_head.py), bit for bit, and the logprob path run
+on its output against the oracle's token_logprobs_mx.
+
+Dequantization is exact by construction (every valid value is a bfloat16
+number), so the bf16 head must equal the oracle's float64 decode exactly,
+signed zeros included, with NaN exactly where the oracle has NaN.  The
+logprobs then carry the bf16 head's tolerance (rtol 2e-3, atol 1e-4), and
+rollout records on the dequantized head equal learner logprobs bit for bit.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from gpu_util import TOL, assert_close, host, mat_to_dev, say, torch_mod, vec_to_dev
+from invariant_token_logprobs_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _dequant(codes, scales, fmt, err=None):
+    import invariant_token_logprobs_amd as rz
+    torch = torch_mod()
+    W = rz.dequantize_head(vec_to_dev(codes), vec_to_dev(scales), fmt, err_flag=err)
+    torch.cuda.synchronize()
+    return W
+
+
+def _bf16_to_f64(W):
+    torch = torch_mod()
+    return W.to(torch.float64).cpu().numpy()
+
+
+def _assert_exact(got, want, what):
+    nan_g, nan_w = np.isnan(got), np.isnan(want)
+    assert np.array_equal(nan_g, nan_w), (what, np.argwhere(nan_g != nan_w)[:5])
+    ok = ~nan_w
+    assert np.array_equal(got[ok], want[ok]), what
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(want[ok])), what
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
+def test_dequantize_every_code_at_every_scale(fmt):
+    """Row r has scale code r (0 .. 255, the invalid ones included) and holds
+    every element code of the format; a NaN-free head leaves the flag clear."""
+    torch = torch_mod()
+    if fmt == "mxfp4":
+        H = 64
+        elem = np.tile(np.arange(16, dtype=np.uint8), (256, H // 16))
+        codes = (elem[:, 0::2] | (elem[:, 1::2] << 4)).astype(np.uint8)
+    else:
+        H = 256
+        codes = np.tile(np.arange(256, dtype=np.uint8), (256, 1))
+    scales = np.repeat(np.arange(256, dtype=np.uint8)[:, None], H // 32, axis=1)
+    say("dequant exhaustive", fmt)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    W = _dequant(codes, scales, fmt, err)
+    _assert_exact(_bf16_to_f64(W), O.dequantize_head(codes, scales, fmt), fmt)
+    assert int(host(err)[0]) == 8
+    lo, hi = O.scale_range(fmt)
+    valid = np.arange(127 + lo, 127 + hi + 1)
+    err.zero_()
+    W = _dequant(codes[valid], scales[valid], fmt, err)
+    _assert_exact(_bf16_to_f64(W), O.dequantize_head(codes[valid], scales[valid], fmt),
+                  fmt + " valid rows")
+    assert int(host(err)[0]) == 0
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
+def test_mx_head_logprobs_and_diff0(fmt):
+    """A random MX head (V = 1000: three full vocab tiles and a ragged one),
+    300 rows: the dequantized head is the oracle's exactly, the logprobs
+    match token_logprobs_mx, and the rollout draw on it records exactly the
+    learner's logprobs."""
+    import invariant_token_logprobs_amd as rz
+    torch = torch_mod()
+    V, H, n = 1000, 256, 300
+    codes, scales = synth.random_mx_head(V, H, fmt, 41)
+    hid, tok = synth.random_rows(n, H, V, "bf16", 42)
+    say("mx head parity", fmt)
+    W = _dequant(codes, scales, fmt)
+    W64 = O.dequantize_head(codes, scales, fmt)
+    _assert_exact(_bf16_to_f64(W), W64, fmt)
+    hidden = mat_to_dev(hid, "bf16")
+    lp, lse = rz.token_logprobs(hidden, W, vec_to_dev(tok), want_lse=True)
+    want_lp, want_lse = O.token_logprobs_mx(O.to_f64(hid, "bf16"), codes, scales,
+                                            fmt, tok)
+    t = TOL["bf16"]
+    assert_close(host(lp), want_lp, t["rtol"], t["atol"], f"{fmt} logprobs")
+    assert_close(host(lse), want_lse, t["rtol"], t["atol"], f"{fmt} lse")
+    ids = vec_to_dev(np.arange(n, dtype=np.int64) * 7919)
+    tokens, logmu = rz.sample_tokens(hidden, W, ids, 0xABCDEF)
+    lp2 = rz.token_logprobs(hidden, W, tokens)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(logmu).view(np.uint32), host(lp2).view(np.uint32))
+
+
+def test_mx_qwen3_4b_head_mxfp4():
+    """The Qwen3-4B head shape [151936, 2560] in MXFP4: 512 sampled rows of
+    the dequantized head equal the oracle's decode exactly; 48 rows'
+    logprobs over the full vocabulary match the oracle."""
+    import invariant_token_logprobs_amd as rz
+    torch = torch_mod()
+    V, H = 151936, 2560
+    codes, scales = synth.random_mx_head(V, H, "mxfp4", 77)
+    say("mx qwen3-4b head: dequant")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    W = _dequant(codes, scales, "mxfp4", err)
+    assert int(host(err)[0]) == 0
+    rows = np.sort(np.random.default_rng(78).choice(V, size=512, replace=False))
+    rows[-1] = V - 1
+    got = W[torch.from_numpy(rows).to("cuda:0")].to(torch.float64).cpu().numpy()
+    _assert_exact(got, O.dequantize_head(codes[rows], scales[rows], "mxfp4"), "rows")
+    say("mx qwen3-4b head: logprobs")
+    hid, tok = synth.random_rows(48, H, V, "bf16", 79)
+    lp = rz.token_logprobs(mat_to_dev(hid, "bf16"), W, vec_to_dev(tok))
+    torch.cuda.synchronize()
+    want, _ = O.token_logprobs_mx(O.to_f64(hid, "bf16"), codes, scales, "mxfp4", tok)
+    t = TOL["bf16"]
+    assert_close(host(lp), want, t["rtol"], t["atol"], "qwen3-4b mxfp4 logprobs")
+    del W
+    torch.cuda.empty_cache()
