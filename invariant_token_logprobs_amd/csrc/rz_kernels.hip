@@ -104,13 +104,15 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1,
       k0 += 0x9E3779B9u;
       k1 += 0xBB67AE85u;
     }
-    const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
-    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
-    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    // one 64-bit product gives both halves (v_mad_u64_u32)
+    const uint64_t p0 = (uint64_t)c0 * 0xD2511F53u;
+    const uint64_t p1 = (uint64_t)c2 * 0xCD9E8D57u;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
     c0 = n0;
-    c1 = lo1;
+    c1 = (uint32_t)p1;
     c2 = n2;
-    c3 = lo0;
+    c3 = (uint32_t)p0;
   }
   return u32x4{c0, c1, c2, c3};
 }
@@ -122,20 +124,17 @@ constexpr float kTwoM32 = 2.3283064365386963e-10f;  // 2^-32
 // from u near 1, so E = -ln u is taken from w = 1 - u (exact from the
 // integer) there: a short series for small w, else Kahan's form
 // -ln(y) w / (1 - y) with y = 1 - w rounded, which cancels y's rounding.
+// Every lane evaluates all three forms and selects (no divergent branches;
+// the discarded forms may be inf or NaN).
 __device__ __forceinline__ float gumbel_of_bits(uint32_t x) {
-  float E;
-  if (x < 0x80000000u) {
-    const float u = ((float)x + 0.5f) * kTwoM32;
-    E = -__builtin_amdgcn_logf(u) * kLn2;
-  } else {
-    const float w = ((float)(0xFFFFFFFFu - x) + 0.5f) * kTwoM32;  // 1 - u
-    if (w < 0.015625f) {
-      E = w * (1.f + w * (0.5f + w * (1.f / 3.f + w * (0.25f + w * 0.2f))));
-    } else {
-      const float y = 1.f - w;
-      E = -__builtin_amdgcn_logf(y) * kLn2 * (w / (1.f - y));
-    }
-  }
+  const bool low = x < 0x80000000u;
+  const float u = ((float)x + 0.5f) * kTwoM32;
+  const float w = ((float)(~x) + 0.5f) * kTwoM32;  // 1 - u for the upper half
+  const float y = 1.f - w;
+  const float L = -__builtin_amdgcn_logf(low ? u : y) * kLn2;
+  const float kahan = L * (w * __builtin_amdgcn_rcpf(1.f - y));
+  const float series = w * (1.f + w * (0.5f + w * (1.f / 3.f + w * (0.25f + w * 0.2f))));
+  const float E = low ? L : (w < 0.015625f ? series : kahan);
   return -__builtin_amdgcn_logf(E) * kLn2;
 }
 
@@ -274,14 +273,16 @@ __global__ RZ_GEMM_ATTR void k_fwd_logits(FwdArgs a) {
         const int c0 = cbase + ni * 32 + 8 * q;  // multiple of 4
         const u32x4 x = philox4x32_10((uint32_t)c0 >> 2, (uint32_t)id,
                                       (uint32_t)(id >> 32), 0u, k0, k1);
+        // a lane meets its columns in increasing order, so a strict > keeps
+        // the smallest index among equal scores (draw_better's order)
         static_for<0, 4>([&](auto j_c) {
           constexpr int j = decltype(j_c)::value;
           const int v = c0 + j;
-          const float sc = acc[mi][ni][4 * q + j] + gumbel_of_bits(x[j]);
-          if (v < a.V && draw_better(sc, v, bs, bv)) {
-            bs = sc;
-            bv = v;
-          }
+          float sc = acc[mi][ni][4 * q + j] + gumbel_of_bits(x[j]);
+          sc = v < a.V ? sc : -__builtin_inff();
+          const bool take = sc > bs;
+          bs = take ? sc : bs;
+          bv = take ? v : bv;
         });
       });
       const float os = __shfl_xor(bs, 32, 64);
