@@ -2,7 +2,7 @@
 per step on the Qwen3-4B tool-use shape, on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--mode learner|sample|diag]
+                    [--mode learner|sample|diag|mx]
 
 A step is one rz_reinforce_zero_fwd_bwd call over the whole synthetic batch
 (inputs already resident in HBM).  Prints ONE JSON line with the throughput
@@ -278,6 +278,68 @@ def bench_diag(args, torch, rz, synth, dev):
     print(json.dumps(line), flush=True)
 
 
+def bench_mx(args, torch, rz, synth, dev):
+    """The release-precision head: rz_dequantize_head expanding the Qwen3-4B
+    head (V 151936, H 2560) from --mx-format storage to bf16."""
+    H, V, fmt = 2560, 151936, args.mx_format
+    t0 = time.time()
+    codes_np, scales_np = synth.random_mx_head(V, H, fmt, 5001)
+    log(f"{fmt} head drawn ({time.time() - t0:.1f}s)")
+    codes = torch.from_numpy(codes_np).to(dev)
+    scales = torch.from_numpy(scales_np).to(dev)
+    W = torch.empty((V, H), dtype=torch.bfloat16, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    run = lambda: rz.dequantize_head(codes, scales, fmt, err_flag=err, out=W)
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    rz.timing_enable(True)
+    rz.timing_read(reset=True)
+    torch.cuda.synchronize()
+    ts = time.perf_counter()
+    for _ in range(args.steps):
+        run()
+    torch.cuda.synchronize()
+    te = time.perf_counter()
+    kt = rz.timing_read(reset=True)
+    rz.timing_enable(False)
+    assert int(err.cpu()[0]) == 0, "invalid block scales in the synthetic head"
+    tot_ms, launches = kt["mx_dequant"]
+    avg = tot_ms / launches
+    nbytes = codes_np.nbytes + scales_np.nbytes + 2.0 * V * H
+    achieved = nbytes / (avg * 1e-3) / 1e9
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle as O
+        rows = 16384
+        t0 = time.perf_counter()
+        O.dequantize_head(codes_np[:rows], scales_np[:rows], fmt)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(rows / V / dt, 4), "unit": "heads/s",
+               "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+               "sample": f"first {rows} of {V} rows at H={H}; float64 NumPy "
+                         f"decode, {dt:.2f} s, scaled to the whole head"}
+    line = {
+        "metric": f"MX head expansions/s ({fmt} -> bf16, Qwen3-4B head)",
+        "value": round(args.steps / (te - ts), 2), "unit": "heads/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round((te - ts) * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "u8", "data": "synthetic",
+        "config": {"workload": f"mx_dequant_{fmt}_qwen3_4b_head", "hidden": H,
+                   "vocab": V, "format": fmt},
+        "roofline": {"bound": "hbm", "kernel": "mx_dequant",
+                     "achieved": round(achieved, 1), "peak": HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_GBS, 4),
+                     "traffic": None, "avg_launch_ms": round(avg, 4),
+                     "bytes_per_launch": int(nbytes)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -287,11 +349,14 @@ def main():
     ap.add_argument("--cpu-valid", type=int, default=3072,
                     help="valid rows in the oracle's CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=("learner", "sample", "diag"),
+    ap.add_argument("--mode", choices=("learner", "sample", "diag", "mx"),
                     default="learner",
                     help="learner: the fused fwd/bwd step (the headline); "
                          "sample: the rollout-side draw + record at decode size; "
-                         "diag: the run-level diagnostics over a step's outputs")
+                         "diag: the run-level diagnostics over a step's outputs; "
+                         "mx: expanding an MX-format head to bf16")
+    ap.add_argument("--mx-format", choices=("mxfp4", "mxfp8"), default="mxfp4",
+                    help="element format of the head in --mode mx")
     ap.add_argument("--sample-rows", type=int, default=1024,
                     help="live rows of the rollout batch in --mode sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -312,6 +377,8 @@ def main():
         return bench_sample(args, torch, rz, synth, dev)
     if args.mode == "diag":
         return bench_diag(args, torch, rz, synth, dev)
+    if args.mode == "mx":
+        return bench_mx(args, torch, rz, synth, dev)
     t0 = time.time()
     b = synth.make_workload(args.workload)
     log(f"workload {b.name}: N={b.N} B={b.B} valid={b.n_valid} H={b.H} V={b.V} "

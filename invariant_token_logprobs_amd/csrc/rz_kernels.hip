@@ -389,6 +389,8 @@ __global__ __launch_bounds__(256) void k_target_logit(
 // log pi = z[a_t] - lse.  The fold order depends only on V, never on the
 // number of rows or the row's position.
 // ===================================================================
+constexpr int kMergeBatch = 8;  // tile partials loaded ahead per lane
+
 __device__ __forceinline__ void ms_fold(float& m, float& s, float mj,
                                         float sj) {
   const float mn = fmaxf(m, mj);
@@ -409,9 +411,17 @@ __global__ __launch_bounds__(256) void k_lse_merge(
   const int64_t pos = rc.base + (live ? p : 0);
   float m = kNegInf, s = 0.f;
   if (live)
-    for (int t = q; t < nt; t += 8) {
-      const float2 ms = partials[(int64_t)t * ldp + pos];
-      ms_fold(m, s, ms.x, ms.y);
+    for (int t0 = q; t0 < nt; t0 += 8 * kMergeBatch) {
+      // loads issued kMergeBatch at a time, folded in the same order
+      float2 ms[kMergeBatch];
+#pragma unroll
+      for (int j = 0; j < kMergeBatch; ++j) {
+        const int t = t0 + 8 * j;
+        if (t < nt) ms[j] = partials[(int64_t)t * ldp + pos];
+      }
+#pragma unroll
+      for (int j = 0; j < kMergeBatch; ++j)
+        if (t0 + 8 * j < nt) ms_fold(m, s, ms[j].x, ms[j].y);
     }
   float M = kNegInf, S = 0.f;
   const int g0 = threadIdx.x & ~7;
@@ -448,12 +458,20 @@ __global__ __launch_bounds__(256) void k_draw_merge(
   float bs = -__builtin_inff();
   int bv = 0x7fffffff;
   if (live)
-    for (int t = q; t < nt; t += 8) {
-      const float2 c = cand[(int64_t)t * ldp + p];
-      const int v = __builtin_bit_cast(int, c.y);
-      if (draw_better(c.x, v, bs, bv)) {
-        bs = c.x;
-        bv = v;
+    for (int t0 = q; t0 < nt; t0 += 8 * kMergeBatch) {
+      float2 c[kMergeBatch];
+#pragma unroll
+      for (int j = 0; j < kMergeBatch; ++j) {
+        const int t = t0 + 8 * j;
+        if (t < nt) c[j] = cand[(int64_t)t * ldp + p];
+      }
+#pragma unroll
+      for (int j = 0; j < kMergeBatch; ++j) {
+        const int v = __builtin_bit_cast(int, c[j].y);
+        if (t0 + 8 * j < nt && draw_better(c[j].x, v, bs, bv)) {
+          bs = c[j].x;
+          bv = v;
+        }
       }
     }
 #pragma unroll
@@ -921,49 +939,95 @@ __device__ __forceinline__ uint32_t mx_bf16_bits(uint32_t k, int q, uint32_t sig
   return sign | (k << (q + 133));  // subnormal: k 2^q = m 2^-133
 }
 
+// Shorter exact forms for blocks whose values are all normal bf16 numbers
+// (or zero).  E2M1 magnitudes 0.5, 1, 1.5, 2, 3, 4, 6 (codes 1..7) are the
+// bf16 patterns 0x3EC0 + 0x40 m + 0x40 [m > 1]; the scale adds s to the
+// exponent field, valid for -125 <= s <= 125.
+__device__ __forceinline__ uint32_t e2m1_bf16_normal(uint32_t x, uint32_t sbias) {
+  const uint32_t m3 = x & 7u;
+  const uint32_t mag = 0x3EC0u + (m3 << 6) + (m3 > 1u ? 0x40u : 0u) + sbias;
+  return (m3 ? mag : 0u) | ((x & 8u) << 12);
+}
+// E4M3: a normal code (exponent field e >= 1) (1 + m/8) 2^(e-7) 2^s is the
+// bf16 pattern (x & 0x7F) << 4 plus (120 + s) << 7; a subnormal code m 2^-9
+// 2^s is made exactly in fp32 (3 significant bits), whose top half is the
+// bf16 number.  Valid for -117 <= s <= 119, where both stay normal.
+__device__ __forceinline__ uint32_t e4m3_bf16_normal(uint32_t x, int s, uint32_t ebias) {
+  const uint32_t x7 = x & 0x7Fu;
+  const uint32_t sub = __builtin_bit_cast(uint32_t, __builtin_ldexpf((float)x7, s - 9)) >> 16;
+  const uint32_t mag = x7 >= 8u ? (x7 << 4) + ebias : sub;
+  return x7 == 0x7Fu ? 0x7FC0u : (mag | ((x & 0x80u) << 8));
+}
+
+// A wave expands 64 consecutive blocks (4 KB of bf16) with every load and
+// store instruction covering one contiguous span: in step j = 0..3, lane l
+// takes the 8 values 8 (l % 4) .. + 7 of block 16 j + l / 4, reading their
+// 4 (E2M1) or 8 (E4M3) code bytes and writing 16 bytes at 1 KB j + 16 l.
 template <int kFmt>  // 0: E2M1 (two codes per byte), 1: E4M3
 __global__ __launch_bounds__(256) void k_mx_dequant(const uint8_t* __restrict__ codes,
                                                     const uint8_t* __restrict__ scales,
                                                     int64_t nblk, uint32_t* __restrict__ out,
                                                     int* err) {
-  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (b >= nblk) return;
-  const int sc = scales[b];
-  const int s = sc - 127;
-  const bool ok = sc != 255 && (kFmt == 0 ? s <= 125 : (s >= -124 && s <= 119));
-  uint32_t w[16];  // 32 bf16 values, element 2j in the low half of w[j]
-  if constexpr (kFmt == 0) {
-    const u32x4 c = *reinterpret_cast<const u32x4*>(codes + b * 16);
+  const int lane = threadIdx.x & 63;
+  const int64_t wbase = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 64;
+  bool bad = false;
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const uint32_t x = (c[j >> 3] >> (4 * (j & 7))) & 0xFu;  // bits 4j.. of the block
-      const uint32_t e = (x >> 1) & 3u, m = x & 1u;
-      const uint32_t v = mx_bf16_bits(e ? 2u + m : m, (e ? (int)e - 2 : -1) + s,
-                                      (x & 8u) << 12);
-      w[j >> 1] = (j & 1) ? (w[j >> 1] | (v << 16)) : v;
+  for (int j = 0; j < 4; ++j) {
+    const int64_t b = wbase + 16 * j + (lane >> 2);
+    if (b >= nblk) break;
+    const int part = lane & 3;  // values 8 part .. 8 part + 7 of block b
+    const int sc = scales[b];
+    const int s = sc - 127;
+    const bool ok = sc != 255 && (kFmt == 0 ? s <= 125 : (s >= -124 && s <= 119));
+    uint32_t w[4];  // 8 bf16 values, value 2i in the low half of w[i]
+    if constexpr (kFmt == 0) {
+      const uint32_t c = *reinterpret_cast<const uint32_t*>(codes + b * 16 + 4 * part);
+      if (s >= -125) {
+        const uint32_t sbias = (uint32_t)s << 7;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t v = e2m1_bf16_normal((c >> (4 * i)) & 0xFu, sbias);
+          w[i >> 1] = (i & 1) ? (w[i >> 1] | (v << 16)) : v;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t x = (c >> (4 * i)) & 0xFu;  // low nibble first
+          const uint32_t e = (x >> 1) & 3u, m = x & 1u;
+          const uint32_t v = mx_bf16_bits(e ? 2u + m : m, (e ? (int)e - 2 : -1) + s,
+                                          (x & 8u) << 12);
+          w[i >> 1] = (i & 1) ? (w[i >> 1] | (v << 16)) : v;
+        }
+      }
+    } else {
+      const u32x2 c = *reinterpret_cast<const u32x2*>(codes + b * 32 + 8 * part);
+      if (s >= -117 && s <= 119) {
+        const uint32_t ebias = (uint32_t)(120 + s) << 7;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t v = e4m3_bf16_normal((c[i >> 2] >> (8 * (i & 3))) & 0xFFu, s, ebias);
+          w[i >> 1] = (i & 1) ? (w[i >> 1] | (v << 16)) : v;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t x = (c[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+          const uint32_t e = (x >> 3) & 15u, m = x & 7u;
+          uint32_t v = mx_bf16_bits(e ? 8u + m : m, (e ? (int)e - 10 : -9) + s,
+                                    (x & 0x80u) << 8);
+          if (e == 15u && m == 7u) v = 0x7FC0u;  // the E4M3 NaN code
+          w[i >> 1] = (i & 1) ? (w[i >> 1] | (v << 16)) : v;
+        }
+      }
     }
-  } else {
-    const u32x4 c0 = *reinterpret_cast<const u32x4*>(codes + b * 32);
-    const u32x4 c1 = *reinterpret_cast<const u32x4*>(codes + b * 32 + 16);
+    if (!ok) {
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const uint32_t word = j < 16 ? c0[j >> 2] : c1[(j - 16) >> 2];
-      const uint32_t x = (word >> (8 * (j & 3))) & 0xFFu;
-      const uint32_t e = (x >> 3) & 15u, m = x & 7u;
-      uint32_t v = mx_bf16_bits(e ? 8u + m : m, (e ? (int)e - 10 : -9) + s,
-                                (x & 0x80u) << 8);
-      if (e == 15u && m == 7u) v = 0x7FC0u;  // the E4M3 NaN code
-      w[j >> 1] = (j & 1) ? (w[j >> 1] | (v << 16)) : v;
+      for (int i = 0; i < 4; ++i) w[i] = 0x7FC07FC0u;
+      bad = true;
     }
+    *reinterpret_cast<u32x4*>(out + b * 16 + 4 * part) = u32x4{w[0], w[1], w[2], w[3]};
   }
-  if (!ok) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) w[j] = 0x7FC07FC0u;
-    if (err) atomicOr(err, 8);
-  }
-  u32x4* o = reinterpret_cast<u32x4*>(out + b * 16);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) o[j] = u32x4{w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]};
+  if (bad && err) atomicOr(err, 8);
 }
 
 // ===================================================================
@@ -1549,7 +1613,7 @@ hipError_t launch_diagnostics(const float* logpi, const float* logmu,
 hipError_t launch_mx_dequant(int fmt, const uint8_t* codes, const uint8_t* scales,
                              int64_t nblk, void* out, int* err, hipStream_t s) {
   if (nblk == 0) return hipSuccess;
-  const int64_t grid = cdiv(nblk, 256);
+  const int64_t grid = cdiv(nblk, 256);  // 4 waves x 64 blocks per workgroup
   uint32_t* o = reinterpret_cast<uint32_t*>(out);
   return timed(K_MX_DEQUANT, s, [&] {
     if (fmt == 0)
