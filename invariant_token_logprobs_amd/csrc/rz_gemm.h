@@ -47,6 +47,11 @@ constexpr int kOperandBytes = kBM * kRowBytes;      // 32 KB
 constexpr int kStageBytes = 2 * kOperandBytes;      // A + B
 constexpr int kLdsBytes = 2 * kStageBytes;          // double buffer, 128 KB
 constexpr int kGroupM = 8;        // tile-rows walked together per XCD
+// the 64-row tile (gemm_mainloop_rows64)
+constexpr int kBM64 = 64;
+constexpr int kOperandBytesA64 = kBM64 * kRowBytes;              // 8 KB
+constexpr int kStageBytes64 = kOperandBytesA64 + kOperandBytes;  // 40 KB
+constexpr int kLdsBytes64 = 2 * kStageBytes64;                   // 80 KB
 
 template <typename T>
 struct Stage {
@@ -355,6 +360,107 @@ __device__ __forceinline__ void gemm_mainloop(const GemmOperands& op, int M,
     }
   }
 #undef RZ_SB
+}
+
+// The 64-row tile for small row counts (the rollout at decode size): each
+// wave owns one 32-row block (wm) and the four 32-column blocks of its column
+// half (wn), and issues each MFMA with swapped operands on fragments taken
+// from the same swizzled LDS layout and K steps as gemm_mainloop<T, true>,
+// so every 32 x 32 block's accumulators are bit-identical to that tile's.
+// A stage is 64 A rows and 256 B rows (40 KB); stage kt + 1 streams in
+// (global_load_lds_dwordx4: two loads for A and eight for B per wave) while
+// stage kt feeds the MFMAs; each stage ends with every wave's loads complete
+// and a barrier.  At these row counts the B stream (the head W, read once
+// per vocab tile) bounds the kernel, not the MFMAs.  Rows of A at or past M
+// (B rows past N) read row M - 1 (N - 1), as in gemm_mainloop.  Leaves the
+// LDS free on return.
+template <typename T>
+__device__ __forceinline__ void gemm_mainloop_rows64(const GemmOperands& op, int M,
+                                                     int m0, int n0, int nk,
+                                                     f32x16 (&acc)[1][kTN],
+                                                     char* lds) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wid = tid >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+#pragma unroll
+  for (int ni = 0; ni < kTN; ++ni)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[0][ni][r] = 0.f;
+  if (nk <= 0) return;
+
+  const int a_off = (wm * 32 + (lane & 31)) * kRowBytes;
+  int b_off[kTN];
+#pragma unroll
+  for (int ni = 0; ni < kTN; ++ni)
+    b_off[ni] = (wn * 128 + ni * 32 + (lane & 31)) * kRowBytes;
+  int c_off[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    c_off[s] = ((2 * s + (lane >> 5)) ^ swz(lane & 31)) << 4;
+
+  // load i of wave wu fills 8 rows (lane / 8 picks the row, lane % 8 the
+  // physical chunk, which holds logical chunk (lane % 8) ^ swz(row)):
+  // A rows 16 wu + 8 i (i < 2), B rows 64 wu + 8 i (i < 8)
+  typedef __attribute__((address_space(3))) void* lds_ptr_t;
+  const int wu = __builtin_amdgcn_readfirstlane(wid);
+  const char* ga[2];
+  const char* gb[8];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = wu * 16 + 8 * i + (lane >> 3);
+    const int c = (lane & 7) ^ swz(r);
+    int m = m0 + r;
+    m = m < M ? m : M - 1;
+    const int64_t prow = op.a_rows ? (int64_t)op.a_rows[op.a_base + m] : op.a_base + m;
+    ga[i] = op.A + prow * op.lda + c * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = wu * 64 + 8 * i + (lane >> 3);
+    const int c = (lane & 7) ^ swz(r);
+    int n = n0 + r;
+    n = n < op.N ? n : op.N - 1;
+    gb[i] = op.B + (int64_t)n * op.ldb + c * 16;
+  }
+  auto dma = [&](int kt, int stage) {
+    const int64_t k = (int64_t)kt * kRowBytes;
+    char* sa = lds + stage * kStageBytes64;
+    char* sb = sa + kOperandBytesA64;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_global_load_lds(ga[i] + k,
+                                       (lds_ptr_t)(sa + (wu * 16 + 8 * i) * kRowBytes),
+                                       16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_global_load_lds(gb[i] + k,
+                                       (lds_ptr_t)(sb + (wu * 64 + 8 * i) * kRowBytes),
+                                       16, 0, 0);
+  };
+
+  dma(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    // buffer cur ^ 1 was drained by the barrier that ended stage kt - 1
+    if (kt + 1 < nk) dma(kt + 1, cur ^ 1);
+    const char* sa = lds + cur * kStageBytes64;
+    const char* sb = sa + kOperandBytesA64;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const u32x4 fa = *reinterpret_cast<const u32x4*>(sa + a_off + c_off[s]);
+      u32x4 fb[kTN];
+#pragma unroll
+      for (int ni = 0; ni < kTN; ++ni)
+        fb[ni] = *reinterpret_cast<const u32x4*>(sb + b_off[ni] + c_off[s]);
+#pragma unroll
+      for (int ni = 0; ni < kTN; ++ni)
+        mfma_step(acc[0][ni], fb[ni], fa, (const T*)nullptr);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
 }
 
 }  // namespace rz

@@ -20,6 +20,10 @@ namespace {
 
 constexpr float kNegInf = -__builtin_inff();
 
+// Row counts up to which the forward of rz_token_logprobs and
+// rz_sample_tokens runs on the 64-row tile.
+constexpr int kRows64Max = 256;
+
 // Logits of vocabulary columns >= V inside the last vocab tile: finite, so
 // the row maximum stays finite and no (-inf) - (-inf) can appear.
 constexpr float kMaskedLogit = -1.0e30f;
@@ -157,51 +161,62 @@ __device__ __forceinline__ bool draw_better(float s, int v, float bs, int bv) {
 // is the same in every launch (batch invariance).  The maximum is exact in
 // any order, so it is taken first over the whole tile; one exp per element
 // then serves both s_tile and e.
-template <typename T, bool kStoreE, bool kSample = false>
-__global__ RZ_GEMM_ATTR void k_fwd_logits(FwdArgs a) {
-  // [0, 128 KB): main-loop stages, then (learner call, bf16) the e tile;
-  // then the per-wave row maxima and row sums [2][256] each; then (sampling
-  // call) the per-wave best draw and its index [2][256] each
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes + (kSample ? 8192 : 4096)];
+//
+// TM = 32-row blocks per wave along M: kTM (the 256-row tile) or 1 (the
+// 64-row tile for small row counts).  Both run the same MFMA per 32 x 32
+// block in the same K order and the same per-row folds below, so a row's
+// statistics and draw are bit-identical whichever tile computes them.
+template <typename T, bool kStoreE, bool kSample, int TM>
+__device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
+  static_assert(TM == kTM || (TM == 1 && !kStoreE), "64-row tile: no e output");
+  constexpr int BM = 64 * TM;  // tile rows
+  constexpr int RW = 32 * TM;  // rows per wave
+  // epilogue arrays [2][BM] each: row maxima, row sums and (sampling call)
+  // the best draw and its index; after the e tile (256-row tile) or over
+  // the drained stage buffers (64-row tile)
+  constexpr int kEpi = TM == kTM ? kLdsBytes : 0;
   const RowCount rc = to_rc(a.rows);
   const int M = rc.get();
   // Only the tiles of the M rows present are numbered (M may be a device
   // count below the launch bound), so the active tiles spread over all XCDs.
-  const int mt = (M + kBM - 1) / kBM;
+  const int mt = (M + BM - 1) / BM;
   if ((int)blockIdx.x >= mt * a.nt) return;
   const TileCoord tc = map_tile(blockIdx.x, mt * a.nt, mt, a.nt);
-  const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
+  const int m0 = tc.tm * BM, n0 = tc.tn * kBN;
 
-  f32x16 acc[kTM][kTN];
-  gemm_mainloop<T, true>(a.op, M, m0, n0, a.nk, acc, lds);
+  f32x16 acc[TM][kTN];
+  if constexpr (TM == kTM)
+    gemm_mainloop<T, true>(a.op, M, m0, n0, a.nk, acc, lds);
+  else
+    gemm_mainloop_rows64<T>(a.op, M, m0, n0, a.nk, acc, lds);
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
   const int half = lane >> 5, l32 = lane & 31;
-  float* wmax = reinterpret_cast<float*>(lds + kLdsBytes);         // [2][256]
-  float* wsum = reinterpret_cast<float*>(lds + kLdsBytes + 2048);  // [2][256]
+  float* wmax = reinterpret_cast<float*>(lds + kEpi);           // [2][BM]
+  float* wsum = reinterpret_cast<float*>(lds + kEpi + 8 * BM);  // [2][BM]
   // column of register r in block ni: cbase + 32 ni + 8 (r / 4) + (r % 4)
   const int cbase = n0 + wn * 128 + 4 * half;
 
   // Tile row maxima.  Columns >= V (last vocab tile only) hold a copy of
   // column V - 1 (the main loop reads B rows >= N from row N - 1), which
   // cannot change a maximum, so no mask is needed here.
-  float rm[kTM];
+  float rm[TM];
 #pragma unroll
-  for (int mi = 0; mi < kTM; ++mi) {
+  for (int mi = 0; mi < TM; ++mi) {
     float mx = acc[mi][0][0];
 #pragma unroll
     for (int ni = 0; ni < kTN; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[mi][ni][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    if (half == 0) wmax[wn * 256 + wm * 128 + mi * 32 + l32] = mx;
+    if (half == 0) wmax[wn * BM + wm * RW + mi * 32 + l32] = mx;
   }
   __syncthreads();
 #pragma unroll
-  for (int mi = 0; mi < kTM; ++mi) {
-    const int R = wm * 128 + mi * 32 + l32;
-    rm[mi] = fmaxf(wmax[R], wmax[256 + R]);
+  for (int mi = 0; mi < TM; ++mi) {
+    const int R = wm * RW + mi * 32 + l32;
+    rm[mi] = fmaxf(wmax[R], wmax[BM + R]);
   }
 
   // e = exp(z - m_tile) once per element, 0 for columns >= V; row sums in a
@@ -211,11 +226,11 @@ __global__ RZ_GEMM_ATTR void k_fwd_logits(FwdArgs a) {
   auto pass2 = [&](auto full_c) {
     constexpr bool kFull = decltype(full_c)::value;
 #pragma unroll
-    for (int mi = 0; mi < kTM; ++mi) {
+    for (int mi = 0; mi < TM; ++mi) {
       // a 32-row block wholly past the row count: nothing to compute
       // (uniform across the wave; its rows are never read back)
-      if (m0 + wm * 128 + mi * 32 >= M) continue;
-      const int R = wm * 128 + mi * 32 + l32;
+      if (m0 + wm * RW + mi * 32 >= M) continue;
+      const int R = wm * RW + mi * 32 + l32;
       const bool rvalid = m0 + R < M;
       // exp(z - m) = 2^(z log2 e - m log2 e): one FMA per element
       const float nm = -rm[mi] * kLog2e;
@@ -248,7 +263,7 @@ __global__ RZ_GEMM_ATTR void k_fwd_logits(FwdArgs a) {
         }
       // the wave's 128 columns: lower column half first
       const float so = __shfl_xor(s, 32, 64);
-      if (half == 0) wsum[wn * 256 + R] = s + so;
+      if (half == 0) wsum[wn * BM + R] = s + so;
     }
   };
   if (n0 + kBN <= a.V) pass2(BoolC<true>{});
@@ -258,13 +273,13 @@ __global__ RZ_GEMM_ATTR void k_fwd_logits(FwdArgs a) {
     // gumbel_of_bits; counter (v / 4, id_lo, id_hi, 0), key = the seed, word
     // v % 4), under draw_better's total order, so the order in which lanes
     // and waves meet does not matter.
-    float* wbs = reinterpret_cast<float*>(lds + kLdsBytes + 4096);   // [2][256]
-    int* wbv = reinterpret_cast<int*>(lds + kLdsBytes + 6144);       // [2][256]
+    float* wbs = reinterpret_cast<float*>(lds + kEpi + 16 * BM);  // [2][BM]
+    int* wbv = reinterpret_cast<int*>(lds + kEpi + 24 * BM);      // [2][BM]
     const uint32_t k0 = (uint32_t)a.seed, k1 = (uint32_t)(a.seed >> 32);
-    static_for<0, kTM>([&](auto mi_c) {
+    static_for<0, TM>([&](auto mi_c) {
       constexpr int mi = decltype(mi_c)::value;
-      if (m0 + wm * 128 + mi * 32 >= M) return;  // block past the row count
-      const int R = wm * 128 + mi * 32 + l32;
+      if (m0 + wm * RW + mi * 32 >= M) return;  // block past the row count
+      const int R = wm * RW + mi * 32 + l32;
       const uint64_t id = m0 + R < M ? a.row_ids[rc.base + m0 + R] : 0;
       float bs = -__builtin_inff();
       int bv = 0x7fffffff;
@@ -292,18 +307,18 @@ __global__ RZ_GEMM_ATTR void k_fwd_logits(FwdArgs a) {
         bv = ov;
       }
       if (half == 0) {
-        wbs[wn * 256 + R] = bs;
-        wbv[wn * 256 + R] = bv;
+        wbs[wn * BM + R] = bs;
+        wbv[wn * BM + R] = bv;
       }
     });
     __syncthreads();
     const int m = m0 + tid;
-    if (m < M) {
+    if (tid < BM && m < M) {
       float bs = wbs[tid];
       int bv = wbv[tid];
-      if (draw_better(wbs[256 + tid], wbv[256 + tid], bs, bv)) {
-        bs = wbs[256 + tid];
-        bv = wbv[256 + tid];
+      if (draw_better(wbs[BM + tid], wbv[BM + tid], bs, bv)) {
+        bs = wbs[BM + tid];
+        bv = wbv[BM + tid];
       }
       a.cand[(int64_t)tc.tn * a.ldp + rc.base + m] =
           make_float2(bs, __builtin_bit_cast(float, bv));
@@ -312,9 +327,9 @@ __global__ RZ_GEMM_ATTR void k_fwd_logits(FwdArgs a) {
   __syncthreads();
   {
     const int m = m0 + tid;
-    if (m < M)
+    if (tid < BM && m < M)
       a.partials[(int64_t)tc.tn * a.ldp + rc.base + m] =
-          make_float2(fmaxf(wmax[tid], wmax[256 + tid]), wsum[tid] + wsum[256 + tid]);
+          make_float2(fmaxf(wmax[tid], wmax[BM + tid]), wsum[tid] + wsum[BM + tid]);
   }
   if constexpr (kStoreE && sizeof(T) == 2) {
     // 16-byte row chunks: 32 lanes cover one 512-byte tile row.  Columns
@@ -329,6 +344,24 @@ __global__ RZ_GEMM_ATTR void k_fwd_logits(FwdArgs a) {
             *reinterpret_cast<const u32x4*>(lds + e_stage_off(R, k));
     }
   }
+}
+
+template <typename T, bool kStoreE, bool kSample = false>
+__global__ RZ_GEMM_ATTR void k_fwd_logits(FwdArgs a) {
+  // [0, 128 KB): main-loop stages, then (learner call, bf16) the e tile;
+  // then the epilogue arrays, [2][256] floats each
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes + (kSample ? 8192 : 4096)];
+  fwd_logits_body<T, kStoreE, kSample, kTM>(a, lds);
+}
+
+// The 64-row tile: 80 KB of LDS and a quarter of the accumulators, so two
+// workgroups share a CU; for row counts where the 256-row tile would mostly
+// compute rows that are not there.
+template <typename T, bool kSample>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_fwd_logits64(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes64];
+  fwd_logits_body<T, false, kSample, 1>(a, lds);
 }
 
 // z[t, a_t] = <hidden[t], W[a_t]> for every listed row: one wave per row,
@@ -925,38 +958,39 @@ __global__ __launch_bounds__(1024) void k_resp_diag(
 // MX-format head -> bfloat16 ("Zero mismatch, simple async RL", vLLM blog:
 // the aligned path keeps release precision, FP8 and MXFP4 weights included).
 // Encodings of the OCP Microscaling Formats v1.0: E2M1 and E4M3 elements,
-// one E8M0 scale 2^(code - 127) per 32 consecutive values along H.  Each
-// value is built directly as a bf16 bit pattern with integer operations; the
-// scale range checked per block makes every value of the block exactly a
+// one E8M0 scale 2^(code - 127) per 32 consecutive values along H.  The
+// scale range checked per block makes every value of a valid block exactly a
 // bf16 number (normal or subnormal), so nothing is rounded.
 // ===================================================================
-// k * 2^q as bf16 bits (0 <= k < 16; exact by the caller's range check).
-__device__ __forceinline__ uint32_t mx_bf16_bits(uint32_t k, int q, uint32_t sign) {
-  if (k == 0) return sign;
-  const int p = 31 - __builtin_clz(k);
-  const int e = q + p;
-  if (e >= -126) return sign | ((uint32_t)(e + 127) << 7) | ((k << (7 - p)) & 0x7Fu);
-  return sign | (k << (q + 133));  // subnormal: k 2^q = m 2^-133
+// Valid blocks go through gfx950's scaled conversions
+// (v_cvt_scalef32_pk_bf16_fp4 / _fp8: two codes times a float scale to two
+// bf16 values, low nibble / low byte first), which an exhaustive check over
+// every code at every E8M0 scale found exact wherever the result is a bf16
+// number -- the whole valid range, subnormal results included.  The scale
+// 2^s is the float with exponent field s + 127 (2^-127: the subnormal
+// 0x00400000).
+__device__ __forceinline__ float e8m0_scale(int code) {
+  return __builtin_bit_cast(float, code == 0 ? 0x00400000u : (uint32_t)code << 23);
 }
 
-// Shorter exact forms for blocks whose values are all normal bf16 numbers
-// (or zero).  E2M1 magnitudes 0.5, 1, 1.5, 2, 3, 4, 6 (codes 1..7) are the
-// bf16 patterns 0x3EC0 + 0x40 m + 0x40 [m > 1]; the scale adds s to the
-// exponent field, valid for -125 <= s <= 125.
-__device__ __forceinline__ uint32_t e2m1_bf16_normal(uint32_t x, uint32_t sbias) {
-  const uint32_t m3 = x & 7u;
-  const uint32_t mag = 0x3EC0u + (m3 << 6) + (m3 > 1u ? 0x40u : 0u) + sbias;
-  return (m3 ? mag : 0u) | ((x & 8u) << 12);
+// 8 E2M1 codes (4 bytes, low nibble first) -> 8 bf16 values
+__device__ __forceinline__ u32x4 fp4x8_to_bf16(uint32_t c, float sc) {
+  return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 0)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 1)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 2)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 3))};
 }
-// E4M3: a normal code (exponent field e >= 1) (1 + m/8) 2^(e-7) 2^s is the
-// bf16 pattern (x & 0x7F) << 4 plus (120 + s) << 7; a subnormal code m 2^-9
-// 2^s is made exactly in fp32 (3 significant bits), whose top half is the
-// bf16 number.  Valid for -117 <= s <= 119, where both stay normal.
-__device__ __forceinline__ uint32_t e4m3_bf16_normal(uint32_t x, int s, uint32_t ebias) {
-  const uint32_t x7 = x & 0x7Fu;
-  const uint32_t sub = __builtin_bit_cast(uint32_t, __builtin_ldexpf((float)x7, s - 9)) >> 16;
-  const uint32_t mag = x7 >= 8u ? (x7 << 4) + ebias : sub;
-  return x7 == 0x7Fu ? 0x7FC0u : (mag | ((x & 0x80u) << 8));
+// 8 E4M3 codes (8 bytes, low byte first) -> 8 bf16 values
+__device__ __forceinline__ u32x4 fp8x8_to_bf16(u32x2 c, float sc) {
+  return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, sc, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, sc, true)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, sc, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, sc, true))};
+}
+
+__device__ __forceinline__ bool mx_scale_ok(int fmt, int code) {
+  const int s = code - 127;
+  return code != 255 && (fmt == 0 ? s <= 125 : (s >= -124 && s <= 119));
 }
 
 // A wave expands 64 consecutive blocks (4 KB of bf16) with every load and
@@ -977,49 +1011,17 @@ __global__ __launch_bounds__(256) void k_mx_dequant(const uint8_t* __restrict__ 
     if (b >= nblk) break;
     const int part = lane & 3;  // values 8 part .. 8 part + 7 of block b
     const int sc = scales[b];
-    const int s = sc - 127;
-    const bool ok = sc != 255 && (kFmt == 0 ? s <= 125 : (s >= -124 && s <= 119));
+    const bool ok = mx_scale_ok(kFmt, sc);
     uint32_t w[4];  // 8 bf16 values, value 2i in the low half of w[i]
-    if constexpr (kFmt == 0) {
-      const uint32_t c = *reinterpret_cast<const uint32_t*>(codes + b * 16 + 4 * part);
-      if (s >= -125) {
-        const uint32_t sbias = (uint32_t)s << 7;
+    u32x4 v;
+    if constexpr (kFmt == 0)
+      v = fp4x8_to_bf16(*reinterpret_cast<const uint32_t*>(codes + b * 16 + 4 * part),
+                        e8m0_scale(sc));
+    else
+      v = fp8x8_to_bf16(*reinterpret_cast<const u32x2*>(codes + b * 32 + 8 * part),
+                        e8m0_scale(sc));
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t v = e2m1_bf16_normal((c >> (4 * i)) & 0xFu, sbias);
-          w[i >> 1] = (i & 1) ? (w[i >> 1] | (v << 16)) : v;
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t x = (c >> (4 * i)) & 0xFu;  // low nibble first
-          const uint32_t e = (x >> 1) & 3u, m = x & 1u;
-          const uint32_t v = mx_bf16_bits(e ? 2u + m : m, (e ? (int)e - 2 : -1) + s,
-                                          (x & 8u) << 12);
-          w[i >> 1] = (i & 1) ? (w[i >> 1] | (v << 16)) : v;
-        }
-      }
-    } else {
-      const u32x2 c = *reinterpret_cast<const u32x2*>(codes + b * 32 + 8 * part);
-      if (s >= -117 && s <= 119) {
-        const uint32_t ebias = (uint32_t)(120 + s) << 7;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t v = e4m3_bf16_normal((c[i >> 2] >> (8 * (i & 3))) & 0xFFu, s, ebias);
-          w[i >> 1] = (i & 1) ? (w[i >> 1] | (v << 16)) : v;
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t x = (c[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-          const uint32_t e = (x >> 3) & 15u, m = x & 7u;
-          uint32_t v = mx_bf16_bits(e ? 8u + m : m, (e ? (int)e - 10 : -9) + s,
-                                    (x & 0x80u) << 8);
-          if (e == 15u && m == 7u) v = 0x7FC0u;  // the E4M3 NaN code
-          w[i >> 1] = (i & 1) ? (w[i >> 1] | (v << 16)) : v;
-        }
-      }
-    }
+    for (int i = 0; i < 4; ++i) w[i] = v[i];
     if (!ok) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) w[i] = 0x7FC07FC0u;
@@ -1445,7 +1447,8 @@ hipError_t launch_fwd_sample(int dt, const void* hidden, int64_t n,
   a.V = V;
   a.Vpad = V;
   a.nk = H / (dt ? Stage<bf16>::kK : Stage<float>::kK);
-  a.mt = cdiv(n, kBM);
+  const bool small = n <= kRows64Max;
+  a.mt = cdiv(n, small ? kBM64 : kBM);
   a.nt = cdiv(V, kBN);
   a.partials = partials;
   a.ldp = ldp;
@@ -1454,8 +1457,13 @@ hipError_t launch_fwd_sample(int dt, const void* hidden, int64_t n,
   a.cand = cand;
   const int nblk = a.mt * a.nt;
   return timed(K_FWD_SAMPLE, s, [&] {
-    if (dt) k_fwd_logits<bf16, false, true><<<nblk, kThreads, 0, s>>>(a);
-    else k_fwd_logits<float, false, true><<<nblk, kThreads, 0, s>>>(a);
+    if (small) {
+      if (dt) k_fwd_logits64<bf16, true><<<nblk, kThreads, 0, s>>>(a);
+      else k_fwd_logits64<float, true><<<nblk, kThreads, 0, s>>>(a);
+    } else {
+      if (dt) k_fwd_logits<bf16, false, true><<<nblk, kThreads, 0, s>>>(a);
+      else k_fwd_logits<float, false, true><<<nblk, kThreads, 0, s>>>(a);
+    }
   });
 }
 
@@ -1490,13 +1498,21 @@ hipError_t launch_fwd_logits(int dt, const void* hidden, int64_t lda_bytes,
   a.V = V;
   a.Vpad = Vpad;
   a.nk = H / (dt ? Stage<bf16>::kK : Stage<float>::kK);
-  a.mt = cdiv(rows.cap, kBM);
+  // host-known small row counts without the e output take the 64-row tile
+  // (same per-row results, a quarter of the MFMA work per W byte)
+  const bool small = !rows.count && !e && rows.cap <= kRows64Max;
+  a.mt = cdiv(rows.cap, small ? kBM64 : kBM);
   a.nt = cdiv(V, kBN);
   a.partials = partials;
   a.ldp = ldp;
   a.e = e;
   a.lde = lde;
   const int nblk = a.mt * a.nt;
+  if (small)
+    return timed(K_FWD_LOGITS, s, [&] {
+      if (dt) k_fwd_logits64<bf16, false><<<nblk, kThreads, 0, s>>>(a);
+      else k_fwd_logits64<float, false><<<nblk, kThreads, 0, s>>>(a);
+    });
   return timed(K_FWD_LOGITS, s, [&] {
     if (dt) {
       if (e) k_fwd_logits<bf16, true><<<nblk, kThreads, 0, s>>>(a);
