@@ -27,19 +27,31 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA
 HBM_GBS = 8000.0
 GEMM_KERNELS = ("fwd_logits_gemm", "bwd_dh_gemm", "bwd_dw_gemm")
 
-# HBM bytes per launch of the GEMM kernels at the Qwen3-4B tool-use shape,
-# from two rocprofv3 counter runs of this script (FETCH_SIZE x 2.0 and
-# WRITE_SIZE x 1.0, the factors a plain 1 GiB copy reads on the same
-# counters), averaged over one step's chunk launches.  Valid only for the
-# kernel sources they were taken from.  Derivation and commands:
-# profiles/gemm_traffic_qwen3_4b_tool.md.
+# HBM bytes per launch from two rocprofv3 counter runs of this script
+# (FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0, the factors a plain 1 GiB copy
+# reads on the same counters), averaged over the launches of one step: the
+# learner GEMMs at the Qwen3-4B tool-use shape (profiles/
+# gemm_traffic_qwen3_4b_tool.md), the gradient-norm kernel of --mode diag
+# (profiles/run_diagnostics_qwen3_4b_step.md) and the MXFP4 expansion of
+# --mode mx (profiles/mx_dequant_qwen3_4b_head.md).  Valid only for the
+# kernel sources they were taken from.
 COUNTER_TRAFFIC = {
     "workload": "qwen3_4b_tool",
-    "sources_sha256": "2458ee7d0d5e1c09dd47db69d0095d2d853ad398e73ed532645ddbc410c04e9f",
-    "bytes_per_launch": {"fwd_logits_gemm": 30714717981,
-                         "bwd_dh_gemm": 24369720363,
-                         "bwd_dw_gemm": 28226607009},
+    "sources_sha256": "8d840745a9caccbdd39da5e89a7de0415c33a955e0ce39ab7f265c72b6961ca9",
+    "bytes_per_launch": {"fwd_logits_gemm": 30437313498,
+                         "bwd_dh_gemm": 24805986334,
+                         "bwd_dw_gemm": 28439622207,
+                         "grad_norm": 2291971831,
+                         "mx_dequant_mxfp4": 984655022},
 }
+
+
+def counter_traffic(key, workload="qwen3_4b_tool"):
+    """Counter bytes per launch of `key`, or None once the kernels changed."""
+    if (workload != COUNTER_TRAFFIC["workload"]
+            or kernel_sources_sha256() != COUNTER_TRAFFIC["sources_sha256"]):
+        return None
+    return COUNTER_TRAFFIC["bytes_per_launch"].get(key)
 
 
 def kernel_sources_sha256():
@@ -153,6 +165,21 @@ def bench_sample(args, torch, rz, synth, dev):
     kms = {k: v[0] / args.steps for k, v in kt.items() if v[1]}
     log("per-call kernel ms: " + ", ".join(f"{k}={v:.3f}" for k, v in
                                            sorted(kms.items(), key=lambda x: -x[1])))
+    # 2 M H V flops against 2 V H bytes of W: M flops per W byte; below the
+    # chip's balance point (2.5 PFLOP/s over 8 TB/s) W's read bounds the GEMM
+    if M < PEAK_TFLOPS["bf16"] * 1e12 / (HBM_GBS * 1e9):
+        w_gbs = w_bytes / (avg * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "kernel": "fwd_sample_gemm",
+                    "achieved": round(w_gbs, 1), "peak": HBM_GBS, "unit": "GB/s",
+                    "frac": round(w_gbs / HBM_GBS, 4), "traffic": None,
+                    "avg_launch_ms": round(avg, 4),
+                    "mfma_TFLOPs": round(achieved, 2)}
+    else:
+        roofline = {"bound": "mfma", "kernel": "fwd_sample_gemm",
+                    "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"],
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
+                    "traffic": None, "avg_launch_ms": round(avg, 4),
+                    "w_read_TBps": round(w_bytes / (avg * 1e-3) / 1e12, 3)}
     cpu = None
     if not args.no_cpu_baseline:
         import oracle as O
@@ -174,11 +201,7 @@ def bench_sample(args, torch, rz, synth, dev):
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "rollout_draw_qwen3_4b_head", "hidden": H, "vocab": V,
                    "rows": M},
-        "roofline": {"bound": "mfma", "kernel": "fwd_sample_gemm",
-                     "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"],
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
-                     "traffic": None, "avg_launch_ms": round(avg, 4),
-                     "w_read_TBps": round(w_bytes / (avg * 1e-3) / 1e12, 3)},
+        "roofline": roofline,
         "cpu_baseline": cpu,
         "kernel_ms_per_step": {k: round(v, 4) for k, v in kms.items()},
     }
@@ -269,7 +292,7 @@ def bench_diag(args, torch, rz, synth, dev):
         "roofline": {"bound": "hbm", "kernel": "grad_norm",
                      "achieved": round(achieved, 1), "peak": HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_GBS, 4),
-                     "traffic": None,
+                     "traffic": counter_traffic("grad_norm", args.workload),
                      "avg_launch_ms": round(tot_ms / launches, 4),
                      "launches_per_step": launches // args.steps},
         "cpu_baseline": cpu,
@@ -333,7 +356,7 @@ def bench_mx(args, torch, rz, synth, dev):
         "roofline": {"bound": "hbm", "kernel": "mx_dequant",
                      "achieved": round(achieved, 1), "peak": HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_GBS, 4),
-                     "traffic": None, "avg_launch_ms": round(avg, 4),
+                     "traffic": counter_traffic(f"mx_dequant_{fmt}"), "avg_launch_ms": round(avg, 4),
                      "bytes_per_launch": int(nbytes)},
         "cpu_baseline": cpu,
     }
@@ -438,10 +461,7 @@ def main():
     avg_ms = tot_ms / launches
     flop_per_launch = 2.0 * b.H * b.V * nv * args.steps / launches
     achieved = flop_per_launch / (avg_ms * 1e-3) / 1e12
-    traffic = None
-    if (b.name == COUNTER_TRAFFIC["workload"]
-            and kernel_sources_sha256() == COUNTER_TRAFFIC["sources_sha256"]):
-        traffic = COUNTER_TRAFFIC["bytes_per_launch"].get(dom)
+    traffic = counter_traffic(dom, b.name)
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": traffic,
