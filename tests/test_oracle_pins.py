@@ -647,3 +647,105 @@ def test_token_logprobs_mx_is_the_bf16_head_definition():
     z = hidden @ W.T
     want = z[np.arange(n), tok] - np.log(np.exp(z - z.max(1, keepdims=True)).sum(1)) - z.max(1)
     assert np.allclose(lp, want, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------- LoRA on the head
+def test_round_to_bf16_and_f32_against_torch():
+    """Rounding to bfloat16 and float32 agrees with torch's conversions on
+    values where a single rounding is taken (float32 inputs for bf16; float64
+    inputs for f32), ties and subnormals included."""
+    import torch
+    rng = _rng(51)
+    x32 = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32),
+        (rng.standard_normal(2000) * 1e-39).astype(np.float32),     # subnormal
+        np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 2 ** -133,
+                  3 * 2 ** -134, 0.0, -0.0], dtype=np.float32)])  # ties
+    want = torch.from_numpy(x32).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(O.round_to_bf16(x32.astype(np.float64)), want)
+    x64 = np.concatenate([rng.standard_normal(20000), rng.standard_normal(200) * 1e-42])
+    want32 = torch.from_numpy(x64).to(torch.float32).double().numpy()
+    assert np.array_equal(O.round_to_f32(x64), want32)
+
+
+def _lora_problem(seed, r=3):
+    p = _small_problem(seed)
+    rng = _rng(seed + 7)
+    H, V = p["hidden"].shape[1], p["W"].shape[0]
+    p["A"] = 0.3 * rng.standard_normal((r, H))
+    p["B"] = 0.3 * rng.standard_normal((V, r))
+    p["s"] = 0.75
+    return p
+
+
+def test_lora_unrounded_is_the_merged_head():
+    """With an unrounded activation the adapted head is the plain head with
+    W + s B A (the LoRA identity), in logprobs and in the loss."""
+    p = _lora_problem(61)
+    lp, lse = O.token_logprobs_lora(p["hidden"], p["W"], p["A"], p["B"], p["s"],
+                                    p["tokens"], "f32", round_u=False)
+    W_eff = p["W"] + p["s"] * (p["B"] @ p["A"])
+    lp2, lse2 = O.token_logprobs(p["hidden"], W_eff, p["tokens"])
+    assert np.allclose(lp, lp2, rtol=0, atol=1e-12)
+    assert np.allclose(lse, lse2, rtol=0, atol=1e-12)
+    out = O.reinforce_zero_fwd_bwd_lora(p["hidden"], p["W"], p["A"], p["B"], p["s"],
+                                        p["tokens"], p["logmu"], p["mask"], p["cu"],
+                                        p["rewards"], p["group_ids"], "f32", round_u=False)
+    assert abs(out["loss"] - _loss_of(p, p["hidden"], W_eff)) < 1e-12
+    # the hidden-state gradient equals the merged head's
+    ref = O.reinforce_zero_fwd_bwd(p["hidden"], W_eff, p["tokens"], p["logmu"], p["mask"],
+                                   p["cu"], p["rewards"], p["group_ids"])
+    assert np.allclose(out["d_hidden"], ref["d_hidden"], rtol=0, atol=1e-12)
+    # and dL/dA, dL/dB are the chain rule through W_eff = W + s B A
+    assert np.allclose(out["d_lora_A"], p["s"] * p["B"].T @ ref["d_lm_head"], rtol=0, atol=1e-12)
+    assert np.allclose(out["d_lora_B"], p["s"] * ref["d_lm_head"] @ p["A"].T, rtol=0, atol=1e-12)
+
+
+def test_lora_zero_B_is_the_plain_head():
+    p = _lora_problem(62)
+    B0 = np.zeros_like(p["B"])
+    for dtype in ("bf16", "f32"):
+        lp, _ = O.token_logprobs_lora(p["hidden"], p["W"], p["A"], B0, p["s"], p["tokens"], dtype)
+        lp2, _ = O.token_logprobs(p["hidden"], p["W"], p["tokens"])
+        assert np.array_equal(lp, lp2)
+        out = O.reinforce_zero_fwd_bwd_lora(p["hidden"], p["W"], p["A"], B0, p["s"],
+                                            p["tokens"], p["logmu"], p["mask"], p["cu"],
+                                            p["rewards"], p["group_ids"], dtype)
+        assert not out["d_lora_A"].any()
+        ref = O.reinforce_zero_fwd_bwd(p["hidden"], p["W"], p["tokens"], p["logmu"], p["mask"],
+                                       p["cu"], p["rewards"], p["group_ids"])
+        assert np.allclose(out["d_hidden"], ref["d_hidden"], rtol=0, atol=1e-15)
+
+
+def test_lora_activation_rounding():
+    p = _lora_problem(63)
+    u = O.lora_activation(p["hidden"], p["A"], p["s"], "bf16")
+    exact = p["s"] * p["hidden"] @ p["A"].T
+    assert np.all(np.abs(u - exact) <= 2.0 ** -8 * np.abs(exact) + 1e-300)
+    assert np.array_equal(O.round_to_bf16(u), u)         # already bf16 values
+
+
+def test_lora_finite_difference_gradients():
+    """Central differences of the loss (unrounded activation) in A, B and h."""
+    p = _lora_problem(64)
+
+    def loss(hidden, A, B):
+        out = O.reinforce_zero_fwd_bwd_lora(hidden, p["W"], A, B, p["s"], p["tokens"],
+                                            p["logmu"], p["mask"], p["cu"], p["rewards"],
+                                            p["group_ids"], "f32", round_u=False)
+        return out["loss"]
+
+    out = O.reinforce_zero_fwd_bwd_lora(p["hidden"], p["W"], p["A"], p["B"], p["s"],
+                                        p["tokens"], p["logmu"], p["mask"], p["cu"],
+                                        p["rewards"], p["group_ids"], "f32", round_u=False)
+    rng = _rng(65)
+    eps = 1e-6
+    for _ in range(6):
+        dh = rng.standard_normal(p["hidden"].shape)
+        dA = rng.standard_normal(p["A"].shape)
+        dB = rng.standard_normal(p["B"].shape)
+        fd = (loss(p["hidden"] + eps * dh, p["A"] + eps * dA, p["B"] + eps * dB)
+              - loss(p["hidden"] - eps * dh, p["A"] - eps * dA, p["B"] - eps * dB)) / (2 * eps)
+        an = float((out["d_hidden"] * dh).sum() + (out["d_lora_A"] * dA).sum()
+                   + (out["d_lora_B"] * dB).sum())
+        assert abs(fd - an) <= 1e-6 * abs(an) + 1e-9, (fd, an)
