@@ -74,8 +74,13 @@ typedef enum {
   RZ_OP_FWD_BWD = 1,
   RZ_OP_DIAGNOSTICS = 2,
   RZ_OP_SAMPLE = 3,
-  RZ_OP_GRAD_NORMS = 4
+  RZ_OP_GRAD_NORMS = 4,
+  RZ_OP_FWD_BWD_LORA = 5
 } rz_op;
+
+/* LoRA on the head: the largest rank, and the number of columns the
+ * adapter adds to the augmented operands (columns past the rank hold 0). */
+#define RZ_LORA_COLS 64
 
 /* element format of an MX-format LM head (OCP Microscaling Formats v1.0) */
 typedef enum {
@@ -238,6 +243,65 @@ rz_status rz_diagnostics(const float* logpi, const float* logmu,
 rz_status rz_dequantize_head(const uint8_t* codes, const uint8_t* scales,
                              int32_t V, int32_t H, rz_mx_format fmt,
                              void* lm_head, int32_t* err_flag, void* stream);
+
+/*
+ * LoRA adapter on the head ("Zero mismatch, simple async RL", vLLM blog,
+ * Kimi K3.1 section: zero mismatch holds with LoRA adapters on every module
+ * and through LoRA training; LoRA as in Hu et al., 2021).
+ *
+ * The adapted head is z = h W^T + u B^T with u = scale * (h A^T) rounded to
+ * the head's precision (nearest bf16, ties to even, for RZ_DTYPE_BF16; fp32
+ * for RZ_DTYPE_F32): the plain head over the augmented operands
+ * h_aug = [h | u | 0] [n, H + RZ_LORA_COLS] and W_aug = [W | B | 0]
+ * [V, H + RZ_LORA_COLS].  The rollout builds them with the two calls below
+ * (the head once per weight update) and runs rz_token_logprobs /
+ * rz_sample_tokens on them with H + RZ_LORA_COLS as the hidden size; the
+ * learner's rz_reinforce_zero_fwd_bwd_lora builds the same operands with the
+ * same kernels, so rollout records and learner logprobs agree bit for bit.
+ * u is computed by the GEMM tile engine in a fixed K order, so a row's u
+ * does not depend on the batch.
+ *
+ *   lora_A [r, H] dt, lora_B [V, r] dt (device), 1 <= r <= RZ_LORA_COLS,
+ *   scale the adapter's scale (alpha / r); H a multiple of 64 with
+ *   H + RZ_LORA_COLS <= RZ_MAX_HIDDEN.
+ *
+ * rz_lora_augment:    hidden_aug [n_rows, H + RZ_LORA_COLS] dt out.
+ * rz_lora_merge_head: head_aug [V, H + RZ_LORA_COLS] dt out.
+ * Neither takes a workspace.
+ */
+rz_status rz_lora_augment(const void* hidden, const void* lora_A, float scale,
+                          int64_t n_rows, int32_t H, int32_t r, rz_dtype dt,
+                          void* hidden_aug, void* stream);
+rz_status rz_lora_merge_head(const void* lm_head, const void* lora_B,
+                             int32_t V, int32_t H, int32_t r, rz_dtype dt,
+                             void* head_aug, void* stream);
+
+/*
+ * rz_reinforce_zero_fwd_bwd_lora -- the learner step with a LoRA adapter on
+ * a frozen head.  Arguments as rz_reinforce_zero_fwd_bwd, plus lora_A,
+ * lora_B, scale and r as above; outputs:
+ *
+ *   logprobs, loss, diag, adv   as rz_reinforce_zero_fwd_bwd (log pi of the
+ *                               adapted head; bit-identical to
+ *                               rz_token_logprobs on the augmented operands)
+ *   d_hidden  [n_rows, H] fp32  dL/dh through W and through the adapter
+ *   d_lora_A  [r, H] fp32       dL/dA = scale (dL/du)^T h
+ *   d_lora_B  [V, r] fp32       dL/dB = (dL/dz)^T u
+ *
+ * The rounding of u is treated as the identity in the backward pass.  W gets
+ * no gradient and none is computed.  dL/dA sums fixed chunks of 4096 rows in
+ * order.  Workspace: rz_workspace_bytes(RZ_OP_FWD_BWD_LORA, n_rows, n_resp,
+ * H, V, dt) (independent of r).
+ */
+rz_status rz_reinforce_zero_fwd_bwd_lora(
+    const void* hidden, const void* lm_head, const void* lora_A,
+    const void* lora_B, float scale, int32_t r, const int32_t* tokens,
+    const float* logmu, const uint8_t* mask, const int32_t* cu_rows,
+    const float* rewards, const int32_t* group_ids, int64_t n_rows,
+    int32_t n_resp, int32_t H, int32_t V, rz_dtype dt, float* logprobs,
+    float* loss, float* d_hidden, float* d_lora_A, float* d_lora_B,
+    float* diag, float* adv, int32_t* err_flag, void* workspace,
+    size_t workspace_bytes, void* stream);
 
 /*
  * Run-level diagnostics ("Zero mismatch, simple async RL", vLLM blog,

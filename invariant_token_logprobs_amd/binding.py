@@ -19,6 +19,8 @@ RZ_OP_FWD_BWD = 1
 RZ_OP_DIAGNOSTICS = 2
 RZ_OP_SAMPLE = 3
 RZ_OP_GRAD_NORMS = 4
+RZ_OP_FWD_BWD_LORA = 5
+RZ_LORA_COLS = 64
 
 RZ_DEVERR_TOKEN = 1
 RZ_DEVERR_GROUP = 2
@@ -34,7 +36,8 @@ EXPORTS = [
     "rz_workspace_bytes", "rz_status_string", "rz_token_logprobs",
     "rz_reinforce_zero_fwd_bwd", "rz_diagnostics", "rz_sample_tokens",
     "rz_grad_norms", "rz_response_diagnostics", "rz_run_summary",
-    "rz_dequantize_head",
+    "rz_dequantize_head", "rz_lora_augment", "rz_lora_merge_head",
+    "rz_reinforce_zero_fwd_bwd_lora",
     "rz_timing_enable", "rz_timing_num_kernels", "rz_timing_kernel_name",
     "rz_timing_read",
 ]
@@ -88,6 +91,15 @@ def load_library():
     lib.rz_run_summary.argtypes = [vp, vp, vp, i64, i32,
                                    ctypes.POINTER(ctypes.c_double)]
     lib.rz_run_summary.restype = ctypes.c_int
+    f32 = ctypes.c_float
+    lib.rz_lora_augment.argtypes = [vp, vp, f32, i64, i32, i32, ctypes.c_int, vp, vp]
+    lib.rz_lora_augment.restype = ctypes.c_int
+    lib.rz_lora_merge_head.argtypes = [vp, vp, i32, i32, i32, ctypes.c_int, vp, vp]
+    lib.rz_lora_merge_head.restype = ctypes.c_int
+    lib.rz_reinforce_zero_fwd_bwd_lora.argtypes = [
+        vp, vp, vp, vp, f32, i32, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32,
+        ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.rz_reinforce_zero_fwd_bwd_lora.restype = ctypes.c_int
     lib.rz_dequantize_head.argtypes = [vp, vp, i32, i32, ctypes.c_int, vp, vp, vp]
     lib.rz_dequantize_head.restype = ctypes.c_int
     lib.rz_timing_enable.argtypes = [ctypes.c_int]
@@ -307,6 +319,100 @@ def diagnostics(logpi, logmu, mask=None, *, workspace: Optional[Workspace] = Non
     _check(lib.rz_diagnostics(_ptr(logpi), _ptr(logmu), _ptr(mask), n, _ptr(diag),
                               _ptr(ws), nbytes, _stream(stream)), "rz_diagnostics")
     return diag
+
+
+# ------------------------------------------------------- LoRA on the head
+def _lora_shapes(hidden_or_head, lora, name, rank_dim):
+    torch = _torch()
+    _need(lora, name, hidden_or_head.dtype, 2, hidden_or_head.device)
+    r = lora.shape[rank_dim]
+    if not 1 <= r <= RZ_LORA_COLS:
+        raise RzError(f"LoRA rank must be in [1, {RZ_LORA_COLS}], got {r}")
+    return r
+
+
+def lora_augment(hidden, lora_A, scale: float, *, stream=None, out=None):
+    """[h | u | 0] with u = scale * h A^T in the head's precision
+    (rz_lora_augment): [n, H + RZ_LORA_COLS]."""
+    torch = _torch()
+    lib = load_library()
+    dt = _dtype_code(hidden)
+    _need(hidden, "hidden", None, 2)
+    n, H = hidden.shape
+    r = _lora_shapes(hidden, lora_A, "lora_A", 0)
+    if lora_A.shape[1] != H:
+        raise RzError("lora_A must be [r, H]")
+    h_aug = out if out is not None else torch.empty(
+        (n, H + RZ_LORA_COLS), dtype=hidden.dtype, device=hidden.device)
+    _check(lib.rz_lora_augment(_ptr(hidden), _ptr(lora_A), float(scale), n, H, r,
+                               dt, _ptr(h_aug), _stream(stream)), "rz_lora_augment")
+    return h_aug
+
+
+def lora_merge_head(lm_head, lora_B, *, stream=None, out=None):
+    """[W | B | 0] (rz_lora_merge_head): [V, H + RZ_LORA_COLS]."""
+    torch = _torch()
+    lib = load_library()
+    dt = _dtype_code(lm_head)
+    _need(lm_head, "lm_head", None, 2)
+    V, H = lm_head.shape
+    r = _lora_shapes(lm_head, lora_B, "lora_B", 1)
+    if lora_B.shape[0] != V:
+        raise RzError("lora_B must be [V, r]")
+    W_aug = out if out is not None else torch.empty(
+        (V, H + RZ_LORA_COLS), dtype=lm_head.dtype, device=lm_head.device)
+    _check(lib.rz_lora_merge_head(_ptr(lm_head), _ptr(lora_B), V, H, r, dt,
+                                  _ptr(W_aug), _stream(stream)), "rz_lora_merge_head")
+    return W_aug
+
+
+def reinforce_zero_fwd_bwd_lora(hidden, lm_head, lora_A, lora_B, scale: float,
+                                tokens, logmu, mask, cu_rows, rewards, group_ids,
+                                *, err_flag=None,
+                                workspace: Optional[Workspace] = None,
+                                stream=None):
+    """The learner step with a LoRA adapter on a frozen head
+    (rz_reinforce_zero_fwd_bwd_lora).  Returns a dict with logprobs, loss,
+    d_hidden, d_lora_A, d_lora_B, diag and adv."""
+    torch = _torch()
+    lib = load_library()
+    dt = _dtype_code(hidden)
+    _need(hidden, "hidden", None, 2)
+    dev = hidden.device
+    _need(lm_head, "lm_head", hidden.dtype, 2, dev)
+    for t, nm, d in ((tokens, "tokens", torch.int32), (logmu, "logmu", torch.float32),
+                     (mask, "mask", torch.uint8), (cu_rows, "cu_rows", torch.int32),
+                     (rewards, "rewards", torch.float32),
+                     (group_ids, "group_ids", torch.int32)):
+        _need(t, nm, d, 1, dev)
+    N, H = hidden.shape
+    V = lm_head.shape[0]
+    B = rewards.shape[0]
+    r = _lora_shapes(hidden, lora_A, "lora_A", 0)
+    _need(lora_B, "lora_B", hidden.dtype, 2, dev)
+    if (lm_head.shape[1] != H or lora_A.shape[1] != H
+            or tuple(lora_B.shape) != (V, r) or tokens.shape[0] != N
+            or logmu.shape[0] != N or mask.shape[0] != N
+            or cu_rows.shape[0] != B + 1 or group_ids.shape[0] != B):
+        raise RzError("shape mismatch between the fwd_bwd_lora arguments")
+    f32 = torch.float32
+    o = {"logprobs": torch.empty(N, dtype=f32, device=dev),
+         "loss": torch.empty(1, dtype=f32, device=dev),
+         "d_hidden": torch.empty((N, H), dtype=f32, device=dev),
+         "d_lora_A": torch.empty((r, H), dtype=f32, device=dev),
+         "d_lora_B": torch.empty((V, r), dtype=f32, device=dev),
+         "diag": torch.empty(2, dtype=f32, device=dev),
+         "adv": torch.empty(B, dtype=f32, device=dev)}
+    nbytes = workspace_bytes(RZ_OP_FWD_BWD_LORA, N, B, H, V, dt)
+    ws = _workspace(workspace, nbytes, dev)
+    _check(lib.rz_reinforce_zero_fwd_bwd_lora(
+        _ptr(hidden), _ptr(lm_head), _ptr(lora_A), _ptr(lora_B), float(scale), r,
+        _ptr(tokens), _ptr(logmu), _ptr(mask), _ptr(cu_rows), _ptr(rewards),
+        _ptr(group_ids), N, B, H, V, dt, _ptr(o["logprobs"]), _ptr(o["loss"]),
+        _ptr(o["d_hidden"]), _ptr(o["d_lora_A"]), _ptr(o["d_lora_B"]),
+        _ptr(o["diag"]), _ptr(o["adv"]), _ptr(err_flag), _ptr(ws), nbytes,
+        _stream(stream)), "rz_reinforce_zero_fwd_bwd_lora")
+    return o
 
 
 # ------------------------------------------------------------ MX-format head

@@ -119,8 +119,11 @@ struct FbWs {
   int* offsets;
   int* sorted;
 };
+// H: the GEMM width (hidden and head row length); dw_cols: the columns of
+// the head that get a gradient (all H, or a LoRA adapter's window)
 size_t carve_fb(Carver& c, int64_t n, int32_t B, int32_t H, int32_t V,
-                rz_dtype dt, FbWs* w) {
+                rz_dtype dt, FbWs* w, int32_t dw_cols) {
+  if (dw_cols < 0) dw_cols = H;
   const int nt = (int)((V + kVocabTile - 1) / kVocabTile);
   const int64_t Vpad = round_up(V, 64);
   const int C = chunk_rows(n);
@@ -146,7 +149,7 @@ size_t carve_fb(Carver& c, int64_t n, int32_t B, int32_t H, int32_t V,
   t.diag_tmp = c.take<float>(2 * sizeof(float));
   t.diag_part = c.take<char>(diag_partials_bytes(n));
   t.WT = c.take<char>(es * (size_t)H * (size_t)Vpad);
-  t.hT = c.take<char>(es * (size_t)H * (size_t)C);
+  t.hT = c.take<char>(es * (size_t)dw_cols * (size_t)C);
   t.dz = c.take<char>(es * (size_t)C * (size_t)Vpad);
   // dz^T only for fp32 (bf16 dW reads dz through transposing LDS reads)
   t.dzT = dt == RZ_DTYPE_F32 ? c.take<char>(es * (size_t)Vpad * (size_t)C)
@@ -158,6 +161,34 @@ size_t carve_fb(Carver& c, int64_t n, int32_t B, int32_t H, int32_t V,
   if (w) *w = t;
   return c.off;
 }
+
+// ---- LoRA learner layout: augmented operands, dL/dh_aug, dB, dA partials,
+// then the core's own workspace for the augmented width ----
+struct LoraWs {
+  void* h_aug;
+  void* head_aug;
+  float* dh_aug;
+  float* dB;
+  float* part;
+  char* core;
+};
+size_t carve_lora(Carver& c, int64_t n, int32_t B, int32_t H, int32_t V,
+                  rz_dtype dt, LoraWs* w) {
+  const size_t es = esize(dt);
+  const int64_t Ha = (int64_t)H + kLoraCols;
+  LoraWs t;
+  t.h_aug = c.take<char>(es * (size_t)n * (size_t)Ha);
+  t.head_aug = c.take<char>(es * (size_t)V * (size_t)Ha);
+  t.dh_aug = c.take<float>(sizeof(float) * (size_t)n * (size_t)Ha);
+  t.dB = c.take<float>(sizeof(float) * (size_t)V * kLoraCols);
+  t.part = c.take<float>(sizeof(float) * lora_da_partials(n, kLoraCols, H));
+  t.core = c.base ? c.base + c.off : nullptr;
+  Carver cc{t.core};
+  c.off += carve_fb(cc, n, B, (int32_t)Ha, V, dt, nullptr, kLoraCols);
+  if (w) *w = t;
+  return c.off;
+}
+
 
 rz_status ws_check(void* ws, size_t have, size_t need) {
   if (need == 0) return RZ_OK;
@@ -245,12 +276,15 @@ size_t rz_workspace_bytes(rz_op op, int64_t n_rows, int32_t n_resp, int32_t H,
       return n_rows == 0 ? 0 : carve_tlp(c, n_rows, V, nullptr);
     case RZ_OP_FWD_BWD:
       if (!dims_ok(H, V, dt) || n_resp < 1) return 0;
-      return carve_fb(c, n_rows, n_resp, H, V, dt, nullptr);
+      return carve_fb(c, n_rows, n_resp, H, V, dt, nullptr, -1);
     case RZ_OP_DIAGNOSTICS:
       return align_up(diag_partials_bytes(n_rows));
     case RZ_OP_SAMPLE:
       if (!dims_ok(H, V, dt)) return 0;
       return n_rows == 0 ? 0 : carve_smp(c, n_rows, V, nullptr);
+    case RZ_OP_FWD_BWD_LORA:
+      if (!dims_ok(H, V, dt) || n_resp < 1 || H + kLoraCols > RZ_MAX_HIDDEN) return 0;
+      return carve_lora(c, n_rows, n_resp, H, V, dt, nullptr);
     case RZ_OP_GRAD_NORMS:
       if (H <= 0 || H > RZ_MAX_HIDDEN || V <= 0 || V > RZ_MAX_VOCAB) return 0;
       return carve_gn(c, n_rows, H, V, nullptr);
@@ -395,32 +429,23 @@ rz_status rz_diagnostics(const float* logpi, const float* logmu,
   return RZ_OK;
 }
 
-rz_status rz_reinforce_zero_fwd_bwd(
+// The learner step over hidden [n_rows, H] and head [V, H] (H is the GEMM
+// width and the row stride of both; d_hidden is [n_rows, H]); the head's
+// gradient is taken for columns [dw_col0, dw_col0 + dw_cols) only and
+// written as [V, dw_cols].  The workspace is carve_fb(..., dw_cols) and has
+// been checked by the caller.
+static rz_status fwd_bwd_core(
     const void* hidden, const void* lm_head, const int32_t* tokens,
     const float* logmu, const uint8_t* mask, const int32_t* cu_rows,
     const float* rewards, const int32_t* group_ids, int64_t n_rows,
-    int32_t n_resp, int32_t H, int32_t V, rz_dtype dt, float* logprobs,
-    float* loss, float* d_hidden, float* d_lm_head, float* diag, float* adv,
-    int32_t* err_flag, void* workspace, size_t workspace_bytes, void* stream) {
-  if (n_rows < 0 || n_rows > RZ_MAX_ROWS) return RZ_ERR_INVALID_ARG;
-  if (n_resp < 1 || n_resp > (1 << 24)) return RZ_ERR_INVALID_ARG;
-  if (dt != RZ_DTYPE_F32 && dt != RZ_DTYPE_BF16) return RZ_ERR_UNSUPPORTED;
-  if (H <= 0 || V <= 0) return RZ_ERR_INVALID_ARG;
-  if (!dims_ok(H, V, dt)) return RZ_ERR_UNSUPPORTED;
-  if (!lm_head || !cu_rows || !rewards || !group_ids || !loss || !d_lm_head)
-    return RZ_ERR_INVALID_ARG;
-  if (n_rows > 0 && (!hidden || !tokens || !logmu || !mask || !logprobs ||
-                     !d_hidden))
-    return RZ_ERR_INVALID_ARG;
-  Carver meas{nullptr};
-  const size_t need = carve_fb(meas, n_rows, n_resp, H, V, dt, nullptr);
-  rz_status st = ws_check(workspace, workspace_bytes, need);
-  if (st != RZ_OK) return st;
-
+    int32_t n_resp, int32_t H, int32_t V, rz_dtype dt, int32_t dw_col0,
+    int32_t dw_cols, float* logprobs, float* loss, float* d_hidden,
+    float* d_lm_head, float* diag, float* adv, int32_t* err_flag,
+    void* workspace, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   Carver c{reinterpret_cast<char*>(workspace)};
   FbWs w;
-  carve_fb(c, n_rows, n_resp, H, V, dt, &w);
+  carve_fb(c, n_rows, n_resp, H, V, dt, &w, dw_cols);
   const int64_t N = n_rows;
   const int nt = (V + kVocabTile - 1) / kVocabTile;
   const int Vpad = (int)round_up(V, 64);
@@ -457,15 +482,16 @@ rz_status rz_reinforce_zero_fwd_bwd(
                          w.coef, s));
       RZ_TRY(launch_dz_scale(dt, w.dz, Vpad, w.dzT, C, crow, w.partials, N,
                              w.lse_v, w.coef, Vpad, s));
-      RZ_TRY(launch_transpose(dt, K_TRANSPOSE_H, hidden, H, w.idx, crow, C, H,
-                              w.hT, C, s));
+      RZ_TRY(launch_transpose(dt, K_TRANSPOSE_H,
+                              (const char*)hidden + (size_t)dw_col0 * es, H,
+                              w.idx, crow, C, dw_cols, w.hT, C, s));
       RZ_TRY(launch_bwd_dh(dt, w.dz, Vpad, crow, w.WT, Vpad, H, V, Vpad,
                            w.idx, w.tokv, w.coef, lm_head, d_hidden, s));
     }
     const bool kmaj = dt == RZ_DTYPE_BF16;
     RZ_TRY(launch_bwd_dw(dt, kmaj ? w.dz : w.dzT, kmaj ? Vpad : C,
-                         N > 0 ? crow : DevRows{nullptr, 0, 0}, w.hT, C, H, V,
-                         Vpad, d_lm_head, k == 0, s));
+                         N > 0 ? crow : DevRows{nullptr, 0, 0}, w.hT, C,
+                         dw_cols, V, Vpad, d_lm_head, k == 0, s));
   }
   if (N > 0) RZ_TRY(launch_rows_finalize(mask, N, H, logprobs, d_hidden, s));
   // a5: S_i from this call's logprobs, then L
@@ -475,10 +501,41 @@ rz_status rz_reinforce_zero_fwd_bwd(
   RZ_TRY(launch_diagnostics(logprobs, logmu, mask, N, w.diag_part,
                             diag ? diag : w.diag_tmp, s));
   // a9: exact one-hot part of dW
-  RZ_TRY(launch_dw_fix(dt, w.nvalid, N, w.tokv, w.idx, w.coef, hidden, H, V,
-                       w.counts, w.cursor, w.offsets, w.sorted, d_lm_head, s));
+  RZ_TRY(launch_dw_fix(dt, w.nvalid, N, w.tokv, w.idx, w.coef,
+                       (const char*)hidden + (size_t)dw_col0 * es, H, dw_cols,
+                       V, w.counts, w.cursor, w.offsets, w.sorted, d_lm_head,
+                       s));
   return RZ_OK;
 }
+
+rz_status rz_reinforce_zero_fwd_bwd(
+    const void* hidden, const void* lm_head, const int32_t* tokens,
+    const float* logmu, const uint8_t* mask, const int32_t* cu_rows,
+    const float* rewards, const int32_t* group_ids, int64_t n_rows,
+    int32_t n_resp, int32_t H, int32_t V, rz_dtype dt, float* logprobs,
+    float* loss, float* d_hidden, float* d_lm_head, float* diag, float* adv,
+    int32_t* err_flag, void* workspace, size_t workspace_bytes, void* stream) {
+  if (n_rows < 0 || n_rows > RZ_MAX_ROWS) return RZ_ERR_INVALID_ARG;
+  if (n_resp < 1 || n_resp > (1 << 24)) return RZ_ERR_INVALID_ARG;
+  if (dt != RZ_DTYPE_F32 && dt != RZ_DTYPE_BF16) return RZ_ERR_UNSUPPORTED;
+  if (H <= 0 || V <= 0) return RZ_ERR_INVALID_ARG;
+  if (!dims_ok(H, V, dt)) return RZ_ERR_UNSUPPORTED;
+  if (!lm_head || !cu_rows || !rewards || !group_ids || !loss || !d_lm_head)
+    return RZ_ERR_INVALID_ARG;
+  if (n_rows > 0 && (!hidden || !tokens || !logmu || !mask || !logprobs ||
+                     !d_hidden))
+    return RZ_ERR_INVALID_ARG;
+  Carver meas{nullptr};
+  const size_t need = carve_fb(meas, n_rows, n_resp, H, V, dt, nullptr, -1);
+  rz_status st = ws_check(workspace, workspace_bytes, need);
+  if (st != RZ_OK) return st;
+
+  return fwd_bwd_core(hidden, lm_head, tokens, logmu, mask, cu_rows, rewards,
+                      group_ids, n_rows, n_resp, H, V, dt, 0, H, logprobs,
+                      loss, d_hidden, d_lm_head, diag, adv, err_flag,
+                      workspace, stream);
+}
+
 
 rz_status rz_run_summary(const float* d3, const float* kl,
                          const float* grad_norm, int64_t n_steps,
@@ -516,6 +573,83 @@ rz_status rz_run_summary(const float* d3, const float* kl,
   out[4] = median(kl, n_steps - w, n_steps);
   out[5] = out[4] / out[3];
   out[6] = maximum(grad_norm);
+  return RZ_OK;
+}
+
+rz_status rz_lora_augment(const void* hidden, const void* lora_A, float scale,
+                          int64_t n_rows, int32_t H, int32_t r, rz_dtype dt,
+                          void* hidden_aug, void* stream) {
+  if (dt != RZ_DTYPE_F32 && dt != RZ_DTYPE_BF16) return RZ_ERR_UNSUPPORTED;
+  if (n_rows < 0 || n_rows > RZ_MAX_ROWS) return RZ_ERR_INVALID_ARG;
+  if (r < 1 || r > kLoraCols) return RZ_ERR_INVALID_ARG;
+  if (!dims_ok(H, 1, dt) || H + kLoraCols > RZ_MAX_HIDDEN) return RZ_ERR_UNSUPPORTED;
+  if (n_rows == 0) return RZ_OK;
+  if (!hidden || !lora_A || !hidden_aug) return RZ_ERR_INVALID_ARG;
+  RZ_TRY(launch_lora_u(dt, hidden, lora_A, scale, n_rows, H, r, hidden_aug,
+                       reinterpret_cast<hipStream_t>(stream)));
+  return RZ_OK;
+}
+
+rz_status rz_lora_merge_head(const void* lm_head, const void* lora_B, int32_t V,
+                             int32_t H, int32_t r, rz_dtype dt, void* head_aug,
+                             void* stream) {
+  if (dt != RZ_DTYPE_F32 && dt != RZ_DTYPE_BF16) return RZ_ERR_UNSUPPORTED;
+  if (r < 1 || r > kLoraCols) return RZ_ERR_INVALID_ARG;
+  if (!dims_ok(H, V, dt) || H + kLoraCols > RZ_MAX_HIDDEN) return RZ_ERR_UNSUPPORTED;
+  if (!lm_head || !lora_B || !head_aug) return RZ_ERR_INVALID_ARG;
+  RZ_TRY(launch_lora_head(dt, lm_head, lora_B, V, H, r, head_aug,
+                          reinterpret_cast<hipStream_t>(stream)));
+  return RZ_OK;
+}
+
+rz_status rz_reinforce_zero_fwd_bwd_lora(
+    const void* hidden, const void* lm_head, const void* lora_A,
+    const void* lora_B, float scale, int32_t r, const int32_t* tokens,
+    const float* logmu, const uint8_t* mask, const int32_t* cu_rows,
+    const float* rewards, const int32_t* group_ids, int64_t n_rows,
+    int32_t n_resp, int32_t H, int32_t V, rz_dtype dt, float* logprobs,
+    float* loss, float* d_hidden, float* d_lora_A, float* d_lora_B,
+    float* diag, float* adv, int32_t* err_flag, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  if (n_rows < 0 || n_rows > RZ_MAX_ROWS) return RZ_ERR_INVALID_ARG;
+  if (n_resp < 1 || n_resp > (1 << 24)) return RZ_ERR_INVALID_ARG;
+  if (dt != RZ_DTYPE_F32 && dt != RZ_DTYPE_BF16) return RZ_ERR_UNSUPPORTED;
+  if (H <= 0 || V <= 0 || r < 1 || r > kLoraCols) return RZ_ERR_INVALID_ARG;
+  if (!dims_ok(H, V, dt) || H + kLoraCols > RZ_MAX_HIDDEN) return RZ_ERR_UNSUPPORTED;
+  if (!lm_head || !lora_A || !lora_B || !cu_rows || !rewards || !group_ids ||
+      !loss || !d_lora_A || !d_lora_B)
+    return RZ_ERR_INVALID_ARG;
+  if (n_rows > 0 && (!hidden || !tokens || !logmu || !mask || !logprobs ||
+                     !d_hidden))
+    return RZ_ERR_INVALID_ARG;
+  Carver meas{nullptr};
+  const size_t need = carve_lora(meas, n_rows, n_resp, H, V, dt, nullptr);
+  rz_status st = ws_check(workspace, workspace_bytes, need);
+  if (st != RZ_OK) return st;
+  Carver c{reinterpret_cast<char*>(workspace)};
+  LoraWs w;
+  carve_lora(c, n_rows, n_resp, H, V, dt, &w);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int32_t Ha = H + kLoraCols;
+  // [h | u] and [W | B]: the learner then runs on the same kernels as the
+  // rollout's rz_token_logprobs / rz_sample_tokens over these operands
+  if (n_rows > 0)
+    RZ_TRY(launch_lora_u(dt, hidden, lora_A, scale, n_rows, H, r, w.h_aug, s));
+  RZ_TRY(launch_lora_head(dt, lm_head, lora_B, V, H, r, w.head_aug, s));
+  // the step over the augmented operands; the head's gradient only for the
+  // adapter's columns (W is frozen): dL/dB
+  rz_status core = fwd_bwd_core(w.h_aug, w.head_aug, tokens, logmu, mask,
+                                cu_rows, rewards, group_ids, n_rows, n_resp,
+                                Ha, V, dt, H, kLoraCols, logprobs, loss,
+                                w.dh_aug, w.dB, diag, adv, err_flag, w.core,
+                                stream);
+  if (core != RZ_OK) return core;
+  // chain rule through u: dL/dh and dL/dA; dL/dB without the padding
+  RZ_TRY(launch_lora_grads(dt, w.dh_aug, n_rows, H, hidden, lora_A, r, scale,
+                           w.part, d_hidden, d_lora_A, s));
+  RZ_TRY(hipMemcpy2DAsync(d_lora_B, (size_t)r * sizeof(float), w.dB,
+                          kLoraCols * sizeof(float), (size_t)r * sizeof(float),
+                          (size_t)V, hipMemcpyDeviceToDevice, s));
   return RZ_OK;
 }
 

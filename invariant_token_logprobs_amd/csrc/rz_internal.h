@@ -39,6 +39,10 @@ enum KernelId {
   K_GRAD_NORM_FINAL, // run-level: fixed tree over the chunks, sqrt
   K_RESP_DIAG,       // run-level: per-response D3 and KL
   K_MX_DEQUANT,      // MX-format head -> bf16
+  K_LORA_U,          // LoRA: u = s h A^T into the augmented hidden
+  K_LORA_COLS,       // LoRA: B into the augmented head
+  K_LORA_DH,         // LoRA: dL/dh through both paths
+  K_LORA_DA,         // LoRA: dL/dA partials and their ordered sum
   K_NUM_KERNELS
 };
 
@@ -79,6 +83,17 @@ hipError_t launch_draw_merge(const float2* cand, int64_t ldp, int nt, int64_t n,
                              int* tokens, hipStream_t s);
 hipError_t launch_mx_dequant(int fmt, const uint8_t* codes, const uint8_t* scales,
                              int64_t nblk, void* out, int* err, hipStream_t s);
+constexpr int kLoraCols = 64;  // LoRA: largest rank and u block width
+hipError_t launch_lora_u(int dt, const void* hidden, const void* lora_A,
+                         float scale, int64_t n, int H, int r, void* hidden_aug,
+                         hipStream_t s);
+hipError_t launch_lora_head(int dt, const void* lm_head, const void* lora_B,
+                            int V, int H, int r, void* head_aug, hipStream_t s);
+size_t lora_da_partials(int64_t n, int r, int H);
+hipError_t launch_lora_grads(int dt, const float* dh_aug, int64_t n, int H,
+                             const void* hidden, const void* lora_A, int r,
+                             float scale, float* part, float* d_hidden,
+                             float* d_lora_A, hipStream_t s);
 size_t norm_partials(int64_t n);
 hipError_t launch_grad_norm(const float* x, int64_t n, double* partials,
                             float* norm, hipStream_t s);
@@ -133,7 +148,7 @@ hipError_t launch_bwd_dw(int dt, const void* dz, int64_t ld, DevRows krows,
                          float* d_lm_head, int first, hipStream_t s);
 hipError_t launch_dw_fix(int dt, const int* nvalid, int64_t cap,
                          const int* tokv, const int* idx, const float* coef,
-                         const void* hidden, int H, int V, int* counts,
+                         const void* hidden, int64_t ld, int H, int V, int* counts,
                          int* cursor, int* offsets, int* sorted,
                          float* d_lm_head, hipStream_t s);
 

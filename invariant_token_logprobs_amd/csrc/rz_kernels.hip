@@ -1035,6 +1035,160 @@ __global__ __launch_bounds__(256) void k_mx_dequant(const uint8_t* __restrict__ 
 }
 
 // ===================================================================
+// LoRA adapter on the head ("Zero mismatch, simple async RL", vLLM blog,
+// Kimi K3.1 section: zero mismatch with LoRA adapters on every module).
+// z = h W^T + u B^T with u = s h A^T rounded to the head's precision, i.e.
+// the plain head over [h | u] and [W | B]: the adapter runs on the path's
+// own kernels, so the rollout and the learner agree bit for bit.  The
+// augmented width is H + kLoraPad; columns of u past the rank r hold 0.
+// ===================================================================
+constexpr int kLoraPad = 64;     // the largest rank, and the u block width
+static_assert(kLoraPad == kLoraCols, "one LoRA width for kernels and ABI");
+constexpr int kLoraChunk = 4096; // rows per dL/dA partial sum
+
+__device__ __forceinline__ uint16_t bf16_rne(float x) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, x);
+  return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);  // finite x
+}
+__device__ __forceinline__ void store_val(bf16* p, float x) {
+  *reinterpret_cast<uint16_t*>(p) = bf16_rne(x);
+}
+__device__ __forceinline__ void store_val(float* p, float x) { *p = x; }
+
+struct LoraUArgs {
+  GemmOperands op;  // A = hidden rows, B = lora_A rows (N = r)
+  int n, nk, H, r;
+  int64_t ld_aug;   // row stride of the augmented hidden (values)
+  float scale;
+  void* out;        // augmented hidden [n, H + kLoraPad]
+};
+
+// u = s (h A^T) for one 256-row tile on the tile engine (fixed K order: a
+// row's u does not depend on the batch), written as columns H .. H + 63.
+template <typename T>
+__global__ RZ_GEMM_ATTR void k_lora_u(LoraUArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  const int m0 = blockIdx.x * kBM;
+  f32x16 acc[kTM][kTN];
+  gemm_mainloop<T, false>(a.op, a.n, m0, 0, a.nk, acc, lds);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+  T* out = reinterpret_cast<T*>(a.out);
+#pragma unroll
+  for (int mi = 0; mi < kTM; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < kTN; ++ni) {
+      const int j = acc_col(wn, ni, lane);
+      if (j >= kLoraPad) continue;
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int row = m0 + acc_row(wm, mi, rr, lane);
+        if (row < a.n)
+          store_val(out + (int64_t)row * a.ld_aug + a.H + j,
+                    j < a.r ? a.scale * acc[mi][ni][rr] : 0.f);
+      }
+    }
+}
+
+// dst[row, col0 + j] = j < nsrc ? src[row, j] : 0 for j < kLoraPad
+template <typename T>
+__global__ __launch_bounds__(64) void k_lora_cols(T* __restrict__ dst, int64_t ld,
+                                                  int col0, const T* __restrict__ src,
+                                                  int64_t ld_src, int nsrc) {
+  const int64_t row = blockIdx.x;
+  const int j = threadIdx.x;
+  dst[row * ld + col0 + j] = j < nsrc ? src[row * ld_src + j] : T(0.f);
+}
+
+// dL/dh = dL/dh_aug[:, :H] + s (dL/du) A with dL/du = dL/dh_aug[:, H:]:
+// 64 rows per workgroup, A staged 256 columns at a time, 8 rows per thread
+// in registers; the sum over the rank runs in ascending order.
+template <typename T>
+__global__ __launch_bounds__(256) void k_lora_dh(const float* __restrict__ dh_aug,
+                                                 int64_t ld_aug, int H,
+                                                 const T* __restrict__ A, int r,
+                                                 float scale, int64_t n,
+                                                 float* __restrict__ d_hidden) {
+  __shared__ float du[64][kLoraPad];
+  __shared__ float ab[kLoraPad][256];
+  const int64_t r0 = (int64_t)blockIdx.x * 64;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < 64 * kLoraPad; i += 256) {
+    const int t = i / kLoraPad, j = i % kLoraPad;
+    du[t][j] = (r0 + t < n && j < r) ? dh_aug[(r0 + t) * ld_aug + H + j] : 0.f;
+  }
+  for (int hb = 0; hb < H; hb += 256) {
+    const int h = hb + tid;
+    __syncthreads();
+    for (int j = 0; j < kLoraPad; ++j)
+      ab[j][tid] = (j < r && h < H) ? load_f(A + (int64_t)j * H + h) : 0.f;
+    __syncthreads();
+    if (h >= H) continue;
+    for (int t0 = 0; t0 < 64; t0 += 8) {
+      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < kLoraPad; ++j) {
+        const float av = ab[j][tid];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(du[t0 + i][j], av, acc[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int64_t row = r0 + t0 + i;
+        if (row < n)
+          d_hidden[row * H + h] = dh_aug[row * ld_aug + h] + scale * acc[i];
+      }
+    }
+  }
+}
+
+// dL/dA partials: part[c][j][h] = sum over the rows of chunk c (ascending)
+// of (dL/du)[t, j] h[t, h]; one column per thread, the rank in registers,
+// dL/du staged 64 rows at a time.
+template <typename T>
+__global__ __launch_bounds__(256) void k_lora_da_partial(
+    const float* __restrict__ dh_aug, int64_t ld_aug, int H,
+    const T* __restrict__ hidden, int64_t n, int r, float* __restrict__ part) {
+  __shared__ float du[64][kLoraPad];
+  const int c = blockIdx.x;
+  const int h = blockIdx.y * 256 + threadIdx.x;
+  const int64_t t_begin = (int64_t)c * kLoraChunk;
+  const int64_t t_end = t_begin + kLoraChunk < n ? t_begin + kLoraChunk : n;
+  float acc[kLoraPad];
+#pragma unroll
+  for (int j = 0; j < kLoraPad; ++j) acc[j] = 0.f;
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += 64) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < 64 * kLoraPad; i += 256) {
+      const int t = i / kLoraPad, j = i % kLoraPad;
+      du[t][j] = (t0 + t < t_end && j < r) ? dh_aug[(t0 + t) * ld_aug + H + j] : 0.f;
+    }
+    __syncthreads();
+    if (h >= H) continue;
+    const int nt = t_end - t0 < 64 ? (int)(t_end - t0) : 64;
+    for (int t = 0; t < nt; ++t) {
+      const float hv = load_f(hidden + (t0 + t) * H + h);
+#pragma unroll
+      for (int j = 0; j < kLoraPad; ++j) acc[j] = fmaf(du[t][j], hv, acc[j]);
+    }
+  }
+  if (h < H)
+#pragma unroll
+    for (int j = 0; j < kLoraPad; ++j)  // static indices keep acc in registers
+      if (j < r) part[((int64_t)c * r + j) * H + h] = acc[j];
+}
+
+// dL/dA = s * sum of the partials in ascending chunk order
+__global__ __launch_bounds__(256) void k_lora_da_final(const float* __restrict__ part,
+                                                       int nchunk, int r, int H,
+                                                       float scale, float* __restrict__ dA) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)r * H) return;
+  float acc = 0.f;
+  for (int c = 0; c < nchunk; ++c) acc += part[(int64_t)c * r * H + i];
+  dA[i] = scale * acc;
+}
+
+// ===================================================================
 // Transposes feeding the backward GEMMs their K-contiguous operands:
 // out[c, r] = in[row(r), c] for r < rows, and 0 for rows <= r < the row
 // count rounded up to 64 (the last K stage a GEMM reads; never past
@@ -1374,8 +1528,8 @@ __global__ __launch_bounds__(256) void k_dw_fix(const int* offsets,
                                                 const int* sorted,
                                                 const int* idx,
                                                 const float* coef,
-                                                const T* hidden, int H,
-                                                float* dw) {
+                                                const T* hidden, int64_t ld,
+                                                int H, float* dw) {
   const int v = blockIdx.x;
   const int lo = offsets[v], hi = offsets[v + 1];
   if (lo == hi) return;
@@ -1383,7 +1537,7 @@ __global__ __launch_bounds__(256) void k_dw_fix(const int* offsets,
     float acc = 0.f;
     for (int q = lo; q < hi; ++q) {
       const int p = sorted[q];
-      acc += coef[p] * load_f(hidden + (int64_t)idx[p] * H + h);
+      acc += coef[p] * load_f(hidden + (int64_t)idx[p] * ld + h);
     }
     dw[(int64_t)v * H + h] -= acc;
   }
@@ -1416,7 +1570,8 @@ const char* kernel_name(int k) {
       "bwd_dh_gemm", "bwd_dw_gemm", "fill",         "tok_hist",
       "scan",        "tok_scatter", "bucket_sort",  "dw_fix",
       "target_logit", "fwd_sample_gemm", "draw_merge", "grad_norm",
-      "grad_norm_final", "resp_diag", "mx_dequant"};
+      "grad_norm_final", "resp_diag", "mx_dequant", "lora_u", "lora_cols",
+      "lora_dh", "lora_da"};
   return (k >= 0 && k < K_NUM_KERNELS) ? names[k] : "?";
 }
 
@@ -1641,6 +1796,89 @@ hipError_t launch_mx_dequant(int fmt, const uint8_t* codes, const uint8_t* scale
   });
 }
 
+hipError_t launch_lora_u(int dt, const void* hidden, const void* lora_A,
+                         float scale, int64_t n, int H, int r, void* hidden_aug,
+                         hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const int es = dt ? 2 : 4;
+  const int64_t ld_aug = (int64_t)H + kLoraPad;
+  // h into the first H columns
+  hipError_t e = hipMemcpy2DAsync(hidden_aug, (size_t)ld_aug * es, hidden, (size_t)H * es,
+                                  (size_t)H * es, (size_t)n, hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess) return e;
+  LoraUArgs a{};
+  a.op = GemmOperands{(const char*)hidden, (int64_t)H * es, nullptr, 0,
+                      (const char*)lora_A, (int64_t)H * es, r};
+  a.n = (int)n;
+  a.nk = H / (dt ? Stage<bf16>::kK : Stage<float>::kK);
+  a.H = H;
+  a.r = r;
+  a.ld_aug = ld_aug;
+  a.scale = scale;
+  a.out = hidden_aug;
+  return timed(K_LORA_U, s, [&] {
+    if (dt) k_lora_u<bf16><<<cdiv(n, kBM), kThreads, 0, s>>>(a);
+    else k_lora_u<float><<<cdiv(n, kBM), kThreads, 0, s>>>(a);
+  });
+}
+
+hipError_t launch_lora_head(int dt, const void* lm_head, const void* lora_B,
+                            int V, int H, int r, void* head_aug, hipStream_t s) {
+  const int es = dt ? 2 : 4;
+  const int64_t ld_aug = (int64_t)H + kLoraPad;
+  hipError_t e = hipMemcpy2DAsync(head_aug, (size_t)ld_aug * es, lm_head, (size_t)H * es,
+                                  (size_t)H * es, (size_t)V, hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess) return e;
+  return timed(K_LORA_COLS, s, [&] {
+    if (dt)
+      k_lora_cols<bf16><<<V, kLoraPad, 0, s>>>((bf16*)head_aug, ld_aug, H,
+                                               (const bf16*)lora_B, r, r);
+    else
+      k_lora_cols<float><<<V, kLoraPad, 0, s>>>((float*)head_aug, ld_aug, H,
+                                                (const float*)lora_B, r, r);
+  });
+}
+
+size_t lora_da_partials(int64_t n, int r, int H) {
+  return (size_t)cdiv(n > 0 ? n : 1, kLoraChunk) * (size_t)r * (size_t)H;
+}
+
+hipError_t launch_lora_grads(int dt, const float* dh_aug, int64_t n, int H,
+                             const void* hidden, const void* lora_A, int r,
+                             float scale, float* part, float* d_hidden,
+                             float* d_lora_A, hipStream_t s) {
+  const int64_t ld_aug = (int64_t)H + kLoraPad;
+  hipError_t e = hipSuccess;
+  if (n > 0) {
+    e = timed(K_LORA_DH, s, [&] {
+      if (dt)
+        k_lora_dh<bf16><<<cdiv(n, 64), 256, 0, s>>>(dh_aug, ld_aug, H, (const bf16*)lora_A,
+                                                    r, scale, n, d_hidden);
+      else
+        k_lora_dh<float><<<cdiv(n, 64), 256, 0, s>>>(dh_aug, ld_aug, H, (const float*)lora_A,
+                                                     r, scale, n, d_hidden);
+    });
+    if (e != hipSuccess) return e;
+  }
+  const int nchunk = (int)cdiv(n > 0 ? n : 1, kLoraChunk);
+  if (n > 0) {
+    dim3 grid(nchunk, cdiv(H, 256));
+    e = timed(K_LORA_DA, s, [&] {
+      if (dt)
+        k_lora_da_partial<bf16><<<grid, 256, 0, s>>>(dh_aug, ld_aug, H, (const bf16*)hidden,
+                                                     n, r, part);
+      else
+        k_lora_da_partial<float><<<grid, 256, 0, s>>>(dh_aug, ld_aug, H, (const float*)hidden,
+                                                      n, r, part);
+    });
+    if (e != hipSuccess) return e;
+  }
+  return timed(K_LORA_DA, s, [&] {
+    k_lora_da_final<<<cdiv((int64_t)r * H, 256), 256, 0, s>>>(part, n > 0 ? nchunk : 0,
+                                                             r, H, scale, d_lora_A);
+  });
+}
+
 size_t norm_partials(int64_t n) { return (size_t)cdiv(n, kNormChunk); }
 
 hipError_t launch_grad_norm(const float* x, int64_t n, double* partials,
@@ -1763,7 +2001,7 @@ hipError_t launch_bwd_dw(int dt, const void* dz, int64_t ld, DevRows krows,
 
 hipError_t launch_dw_fix(int dt, const int* nvalid, int64_t cap,
                          const int* tokv, const int* idx, const float* coef,
-                         const void* hidden, int H, int V, int* counts,
+                         const void* hidden, int64_t ld, int H, int V, int* counts,
                          int* cursor, int* offsets, int* sorted,
                          float* d_lm_head, hipStream_t s) {
   DevRows rows{nvalid, 0, (int)cap};
@@ -1796,10 +2034,10 @@ hipError_t launch_dw_fix(int dt, const int* nvalid, int64_t cap,
   return timed(K_DW_FIX, s, [&] {
     if (dt)
       k_dw_fix<bf16><<<V, 256, 0, s>>>(offsets, sorted, idx, coef,
-                                       (const bf16*)hidden, H, d_lm_head);
+                                       (const bf16*)hidden, ld, H, d_lm_head);
     else
       k_dw_fix<float><<<V, 256, 0, s>>>(offsets, sorted, idx, coef,
-                                        (const float*)hidden, H, d_lm_head);
+                                        (const float*)hidden, ld, H, d_lm_head);
   });
 }
 

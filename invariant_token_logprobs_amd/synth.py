@@ -259,3 +259,11 @@ def random_mx_head(V: int, H: int, fmt: str, seed: int, scale_code: int = 121):
         raise ValueError(fmt)
     scales = (scale_code + rng.integers(-1, 2, size=(V, H // 32))).astype(np.uint8)
     return codes, scales
+
+
+def random_lora(r: int, H: int, V: int, dtype: str, seed: int, b_scale: float = 0.05):
+    """A LoRA adapter for the head: A [r, H] ~ N(0, 0.02^2) and B [V, r] ~
+    N(0, b_scale^2) (non-zero, unlike a fresh adapter, so the adapter's path
+    carries weight in the tests), in the head's precision."""
+    rng = np.random.default_rng(np.random.PCG64(seed))
+    return _normal(rng, (r, H), 0.02, dtype), _normal(rng, (V, r), b_scale, dtype)

@@ -284,3 +284,27 @@ def test_random_mx_head_is_valid_storage():
         W = O.dequantize_head(codes, scales, fmt)
         assert W.shape == (64, 128) and np.isfinite(W).all()
         assert 0.003 < W.std() < 0.1, (fmt, W.std())
+
+
+def test_lora_argument_errors(lib):
+    f = ctypes.c_float(0.5)
+    def aug(h=P, A=P, n=10, H=64, r=8, dt=BF16, out=P):
+        return lib.rz_lora_augment(h, A, f, n, H, r, dt, out, NULL)
+    assert aug(r=0) == INVALID and aug(r=65) == INVALID
+    assert aug(H=48) == UNSUPPORTED and aug(dt=7) == UNSUPPORTED
+    assert aug(n=-1) == INVALID
+    assert aug(n=0) == OK                               # nothing to do
+    assert aug(h=NULL) == INVALID and aug(out=NULL) == INVALID
+    def merge(W=P, B=P, V=10, H=64, r=8, dt=BF16, out=P):
+        return lib.rz_lora_merge_head(W, B, V, H, r, dt, out, NULL)
+    assert merge(r=0) == INVALID and merge(V=0) == UNSUPPORTED
+    assert merge(B=NULL) == INVALID
+    nb = rz.workspace_bytes(rz.RZ_OP_FWD_BWD_LORA, 10, 2, 64, 10, BF16)
+    assert nb > rz.workspace_bytes(rz.RZ_OP_FWD_BWD, 10, 2, 64, 10, BF16)
+    def fb(r=8, ws=P, wsb=nb, dA=P):
+        return lib.rz_reinforce_zero_fwd_bwd_lora(
+            P, P, P, P, f, r, P, P, P, P, P, P, 10, 2, 64, 10, BF16, P, P, P, dA, P,
+            NULL, NULL, NULL, ws, wsb, NULL)
+    assert fb(r=0) == INVALID and fb(r=65) == INVALID
+    assert fb(dA=NULL) == INVALID
+    assert fb(ws=NULL) == WORKSPACE and fb(wsb=nb - 1) == WORKSPACE
