@@ -2,7 +2,7 @@
 per step on the Qwen3-4B tool-use shape, on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--mode learner|sample|diag|mx]
+                    [--mode learner|sample|diag|mx] [--lora-rank R]
 
 A step is one rz_reinforce_zero_fwd_bwd call over the whole synthetic batch
 (inputs already resident in HBM).  Prints ONE JSON line with the throughput
@@ -23,6 +23,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "tokens/s fused logprob+IS-loss fwd/bwd (Qwen3-4B shape); % MFMA peak"
+METRIC_LORA = ("tokens/s fused logprob+IS-loss fwd/bwd, rank-{r} LoRA on a frozen "
+               "head (Qwen3-4B shape); % MFMA peak")
+LORA_SCALE = 0.5
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA
 HBM_GBS = 8000.0
 GEMM_KERNELS = ("fwd_logits_gemm", "bwd_dh_gemm", "bwd_dw_gemm")
@@ -84,9 +87,10 @@ def behaviour_logprobs(torch, hidden, head, tokens, rows=2048):
     return out
 
 
-def cpu_baseline(b, logmu, max_valid):
+def cpu_baseline(b, logmu, max_valid, lora=None):
     """The float64 oracle, as it stands, on the first responses of the same
-    workload up to `max_valid` valid rows at the full H and V."""
+    workload up to `max_valid` valid rows at the full H and V (with a LoRA
+    adapter (A, B, scale) on the head when `lora` is given)."""
     import oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -103,10 +107,17 @@ def cpu_baseline(b, logmu, max_valid):
     hidden = O.to_f64(b.hidden[:n_keep], b.dtype)
     head = O.to_f64(b.lm_head, b.dtype)
     t0 = time.perf_counter()
-    out = O.reinforce_zero_fwd_bwd(hidden, head, b.tokens[:n_keep],
-                                   logmu[:n_keep].astype(np.float64),
-                                   b.mask[:n_keep], cu_s, b.rewards[:nb],
-                                   b.group_ids[:nb])
+    if lora is None:
+        out = O.reinforce_zero_fwd_bwd(hidden, head, b.tokens[:n_keep],
+                                       logmu[:n_keep].astype(np.float64),
+                                       b.mask[:n_keep], cu_s, b.rewards[:nb],
+                                       b.group_ids[:nb])
+    else:
+        A, B, sc = lora
+        out = O.reinforce_zero_fwd_bwd_lora(
+            hidden, head, O.to_f64(A, b.dtype), O.to_f64(B, b.dtype), sc,
+            b.tokens[:n_keep], logmu[:n_keep].astype(np.float64),
+            b.mask[:n_keep], cu_s, b.rewards[:nb], b.group_ids[:nb], b.dtype)
     dt = time.perf_counter() - t0
     nv = int(np.count_nonzero(b.mask[:n_keep]))
     assert np.isfinite(out["loss"])
@@ -378,6 +389,9 @@ def main():
                          "sample: the rollout-side draw + record at decode size; "
                          "diag: the run-level diagnostics over a step's outputs; "
                          "mx: expanding an MX-format head to bf16")
+    ap.add_argument("--lora-rank", type=int, default=0,
+                    help="learner mode: a LoRA adapter of this rank (1..64) "
+                         "on the frozen head (rz_reinforce_zero_fwd_bwd_lora)")
     ap.add_argument("--mx-format", choices=("mxfp4", "mxfp8"), default="mxfp4",
                     help="element format of the head in --mode mx")
     ap.add_argument("--sample-rows", type=int, default=1024,
@@ -414,7 +428,18 @@ def main():
     isbf = b.dtype == "bf16"
     hidden, head = up(b.hidden, isbf), up(b.lm_head, isbf)
     tokens = up(b.tokens)
-    mu_ref = behaviour_logprobs(torch, hidden, head, tokens)
+    r = args.lora_rank
+    lora = None
+    if r:
+        A_np, B_np = synth.random_lora(r, b.H, b.V, b.dtype, 6001)
+        lora = (A_np, B_np, LORA_SCALE)
+        A_d, B_d = up(A_np, isbf), up(B_np, isbf)
+        # stand-in behaviour policy on the merged head W + s B A (torch fp32)
+        w_eff = head.float() + LORA_SCALE * (B_d.float() @ A_d.float())
+        mu_ref = behaviour_logprobs(torch, hidden, w_eff, tokens)
+        del w_eff
+    else:
+        mu_ref = behaviour_logprobs(torch, hidden, head, tokens)
     logmu = synth.make_logmu(mu_ref.cpu().numpy(), b.sigma, b.noise_seed)
     del mu_ref
     torch.cuda.empty_cache()
@@ -422,7 +447,12 @@ def main():
                 up(b.rewards), up(b.group_ids)]
     ws = rz.Workspace()
     outs = {}
-    step = lambda: rz.reinforce_zero_fwd_bwd(*args_dev, workspace=ws, outputs=outs)
+    if r:
+        def step():
+            outs.update(rz.reinforce_zero_fwd_bwd_lora(
+                hidden, head, A_d, B_d, LORA_SCALE, *args_dev[2:], workspace=ws))
+    else:
+        step = lambda: rz.reinforce_zero_fwd_bwd(*args_dev, workspace=ws, outputs=outs)
 
     for _ in range(args.warmup):
         step()
@@ -450,7 +480,12 @@ def main():
     ms = (te - ts) * 1e3 / args.steps
     nv = b.n_valid
     value = nv * args.steps / (te - ts)
-    flop_alg = 6.0 * b.H * b.V * nv
+    # algorithmic FLOP per valid token: forward, dHidden and dW GEMMs 2HV
+    # each; with an adapter of rank r the first two are 2(H + r)V, the head's
+    # gradient is dB (2rV) and u, dL/dA and the chain rule to h add 6Hr
+    flop_tok = (6.0 * b.H * b.V if not r else
+                4.0 * (b.H + r) * b.V + 2.0 * r * b.V + 6.0 * b.H * r)
+    flop_alg = flop_tok * nv
     peak = PEAK_TFLOPS[b.dtype]
     mfma_frac = flop_alg / (ms * 1e-3) / (peak * 1e12)
 
@@ -459,9 +494,10 @@ def main():
     dom = max(GEMM_KERNELS, key=lambda k: kt[k][0])
     tot_ms, launches = kt[dom]
     avg_ms = tot_ms / launches
-    flop_per_launch = 2.0 * b.H * b.V * nv * args.steps / launches
+    gemm_k = b.H if not r else (b.H + r if dom != "bwd_dw_gemm" else r)
+    flop_per_launch = 2.0 * gemm_k * b.V * nv * args.steps / launches
     achieved = flop_per_launch / (avg_ms * 1e-3) / 1e12
-    traffic = counter_traffic(dom, b.name)
+    traffic = counter_traffic(dom, b.name) if not r else None
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": traffic,
@@ -477,21 +513,23 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the float64 oracle on a bounded sample ...")
-        cpu = cpu_baseline(b, logmu, args.cpu_valid)
+        cpu = cpu_baseline(b, logmu, args.cpu_valid, lora)
 
     line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s",
+        "metric": METRIC if not r else METRIC_LORA.format(r=r),
+        "value": round(value, 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": b.dtype, "data": "synthetic",
         "config": {"workload": b.name, "hidden": b.H, "vocab": b.V,
                    "responses": b.B, "rows": b.N, "valid_tokens": nv,
-                   "masked_frac": round(1 - nv / b.N, 4), "lag_sigma": b.sigma},
+                   "masked_frac": round(1 - nv / b.N, 4), "lag_sigma": b.sigma,
+                   **({"lora_rank": r, "lora_scale": LORA_SCALE} if r else {})},
         "rows_per_s": round(b.N * args.steps / (te - ts), 1),
         "step_ms_median": round(float(np.median(step_ms)), 3),
         "step_ms_min": round(float(np.min(step_ms)), 3),
         "mfma_peak_frac_algorithmic": round(mfma_frac, 4),
-        "executed_flop_per_valid_token": 6.0 * b.H * b.V,
+        "algorithmic_flop_per_valid_token": flop_tok,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernel_ms_per_step": {k: round(v, 3) for k, v in kms.items()},
