@@ -146,22 +146,34 @@ def bench_sample(args, torch, rz, synth, dev):
     --sample-rows live rows at the Qwen3-4B head (H 2560, V 151936, bf16)."""
     H, V, M = 2560, 151936, args.sample_rows
     hid, _ = synth.random_rows(M, H, V, "bf16", 3001)
-    head = synth.random_lm_head(V, H, "bf16", 3002)
     up = lambda x: torch.from_numpy(np.ascontiguousarray(x.view(np.int16))).view(
         torch.bfloat16).to(dev)
-    hidden, W = up(hid), up(head)
+    hidden = up(hid)
     ids = torch.arange(M, dtype=torch.int64, device=dev)
     ws = rz.Workspace()
     seed = 0x5EED
+    fmt = args.head
+    if fmt == "bf16":
+        head = synth.random_lm_head(V, H, "bf16", 3002)
+        W = up(head)
+        w_bytes = 2.0 * V * H
+        draw = lambda: rz.sample_tokens(hidden, W, ids, seed, workspace=ws)
+    else:
+        codes_np, scales_np = synth.random_mx_head(V, H, fmt, 3002)
+        codes = torch.from_numpy(codes_np).to(dev)
+        scales = torch.from_numpy(scales_np).to(dev)
+        w_bytes = float(codes_np.nbytes + scales_np.nbytes)
+        draw = lambda: rz.sample_tokens_mx(hidden, codes, scales, fmt, ids, seed,
+                                           workspace=ws)
     for _ in range(args.warmup):
-        rz.sample_tokens(hidden, W, ids, seed, workspace=ws)
+        draw()
     torch.cuda.synchronize()
     rz.timing_enable(True)
     rz.timing_read(reset=True)
     torch.cuda.synchronize()
     ts = time.perf_counter()
     for _ in range(args.steps):
-        tok, logmu = rz.sample_tokens(hidden, W, ids, seed, workspace=ws)
+        tok, logmu = draw()
     torch.cuda.synchronize()
     te = time.perf_counter()
     kt = rz.timing_read(reset=True)
@@ -171,7 +183,6 @@ def bench_sample(args, torch, rz, synth, dev):
     gemm_ms, launches = kt["fwd_sample_gemm"]
     avg = gemm_ms / launches
     flop = 2.0 * M * H * V
-    w_bytes = 2.0 * V * H
     achieved = flop / (avg * 1e-3) / 1e12
     kms = {k: v[0] / args.steps for k, v in kt.items() if v[1]}
     log("per-call kernel ms: " + ", ".join(f"{k}={v:.3f}" for k, v in
@@ -196,8 +207,10 @@ def bench_sample(args, torch, rz, synth, dev):
         import oracle as O
         n_cpu = 16
         t0 = time.perf_counter()
-        O.sample_tokens(O.to_f64(hid[:n_cpu], "bf16"), O.to_f64(head, "bf16"),
-                        np.arange(n_cpu), seed, row_chunk=n_cpu)
+        W64 = (O.to_f64(head, "bf16") if fmt == "bf16"
+               else O.dequantize_head(codes_np, scales_np, fmt))
+        O.sample_tokens(O.to_f64(hid[:n_cpu], "bf16"), W64, np.arange(n_cpu), seed,
+                        row_chunk=n_cpu)
         dt = time.perf_counter() - t0
         cpu = {"value": n_cpu / dt, "unit": "tokens/s",
                "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
@@ -205,13 +218,14 @@ def bench_sample(args, torch, rz, synth, dev):
                          f"logits + Philox noise + draw + record, {dt:.1f} s "
                          "(includes decoding W to float64)"}
     line = {
-        "metric": "sampled tokens/s (rollout draw + recorded logprob, Qwen3-4B head)",
+        "metric": ("sampled tokens/s (rollout draw + recorded logprob, Qwen3-4B head"
+                   + (")" if fmt == "bf16" else f", {fmt} weights)")),
         "value": round(M * args.steps / (te - ts), 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "rollout_draw_qwen3_4b_head", "hidden": H, "vocab": V,
-                   "rows": M},
+        "config": {"workload": "rollout_draw_qwen3_4b_head" + ("" if fmt == "bf16" else f"_{fmt}"),
+                   "hidden": H, "vocab": V, "rows": M, "head": fmt},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernel_ms_per_step": {k: round(v, 4) for k, v in kms.items()},
@@ -389,6 +403,9 @@ def main():
                          "sample: the rollout-side draw + record at decode size; "
                          "diag: the run-level diagnostics over a step's outputs; "
                          "mx: expanding an MX-format head to bf16")
+    ap.add_argument("--head", choices=("bf16", "mxfp4", "mxfp8"), default="bf16",
+                    help="--mode sample: the head's storage (MX heads run "
+                         "rz_sample_tokens_mx)")
     ap.add_argument("--lora-rank", type=int, default=0,
                     help="learner mode: a LoRA adapter of this rank (1..64) "
                          "on the frozen head (rz_reinforce_zero_fwd_bwd_lora)")

@@ -75,7 +75,9 @@ typedef enum {
   RZ_OP_DIAGNOSTICS = 2,
   RZ_OP_SAMPLE = 3,
   RZ_OP_GRAD_NORMS = 4,
-  RZ_OP_FWD_BWD_LORA = 5
+  RZ_OP_FWD_BWD_LORA = 5,
+  RZ_OP_TOKEN_LOGPROBS_MX = 6,
+  RZ_OP_SAMPLE_MX = 7
 } rz_op;
 
 /* LoRA on the head: the largest rank, and the number of columns the
@@ -243,6 +245,36 @@ rz_status rz_diagnostics(const float* logpi, const float* logmu,
 rz_status rz_dequantize_head(const uint8_t* codes, const uint8_t* scales,
                              int32_t V, int32_t H, rz_mx_format fmt,
                              void* lm_head, int32_t* err_flag, void* stream);
+
+/*
+ * rz_token_logprobs_mx, rz_sample_tokens_mx -- rz_token_logprobs and
+ * rz_sample_tokens on a head stored as MX blocks (codes and scales as in
+ * rz_dequantize_head; 16-byte aligned), with bf16 hidden states.
+ *
+ * Their results are bit-identical to the bf16 calls on
+ * rz_dequantize_head(codes, scales), the expanded head, in every case (same
+ * MFMA operands, same folds).  Up to 128 rows (rz_token_logprobs_mx) or 256
+ * rows (rz_sample_tokens_mx), and with H a multiple of 128, the 64-row tile
+ * reads the codes directly: a quarter (MXFP4) or a half (MXFP8) of the bf16
+ * head's bytes per call, which is what bounds the rollout at decode size.
+ * Otherwise the head is expanded into the workspace first.  Blocks with an
+ * invalid scale give NaN and set RZ_DEVERR_MX_SCALE in err_flag (may be
+ * NULL).  Workspace: rz_workspace_bytes(RZ_OP_TOKEN_LOGPROBS_MX or
+ * RZ_OP_SAMPLE_MX, n_rows, 1, H, V, RZ_DTYPE_BF16).
+ */
+rz_status rz_token_logprobs_mx(const void* hidden, const uint8_t* codes,
+                               const uint8_t* scales, rz_mx_format fmt,
+                               const int32_t* tokens, int64_t n_rows, int32_t H,
+                               int32_t V, float* logprobs, float* lse,
+                               int32_t* err_flag, void* workspace,
+                               size_t workspace_bytes, void* stream);
+rz_status rz_sample_tokens_mx(const void* hidden, const uint8_t* codes,
+                              const uint8_t* scales, rz_mx_format fmt,
+                              const uint64_t* row_ids, int64_t n_rows,
+                              int32_t H, int32_t V, uint64_t seed,
+                              int32_t* tokens, float* logmu, float* lse,
+                              int32_t* err_flag, void* workspace,
+                              size_t workspace_bytes, void* stream);
 
 /*
  * LoRA adapter on the head ("Zero mismatch, simple async RL", vLLM blog,

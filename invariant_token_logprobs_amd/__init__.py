@@ -9,7 +9,7 @@ from .binding import (  # noqa: F401
     EXPORTS, RZ_DEVERR_CU_ROWS, RZ_DEVERR_GROUP, RZ_DEVERR_TOKEN,
     RUN_SUMMARY_KEYS, RZ_DEVERR_MX_SCALE, RZ_LORA_COLS, RZ_MX_FORMATS,
     RZ_OP_FWD_BWD_LORA, RZ_DTYPE_BF16, lora_augment, lora_merge_head,
-    reinforce_zero_fwd_bwd_lora, RZ_DTYPE_F32, RZ_OP_DIAGNOSTICS,
+    reinforce_zero_fwd_bwd_lora, token_logprobs_mx, sample_tokens_mx, RZ_DTYPE_F32, RZ_OP_DIAGNOSTICS,
     RZ_OP_FWD_BWD, RZ_OP_GRAD_NORMS, RZ_OP_SAMPLE, RZ_OP_TOKEN_LOGPROBS,
     RunTracker, RzError, Workspace, dequantize_head, diagnostics, grad_norms,
     library_path,

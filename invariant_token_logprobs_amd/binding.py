@@ -20,6 +20,8 @@ RZ_OP_DIAGNOSTICS = 2
 RZ_OP_SAMPLE = 3
 RZ_OP_GRAD_NORMS = 4
 RZ_OP_FWD_BWD_LORA = 5
+RZ_OP_TOKEN_LOGPROBS_MX = 6
+RZ_OP_SAMPLE_MX = 7
 RZ_LORA_COLS = 64
 
 RZ_DEVERR_TOKEN = 1
@@ -37,7 +39,8 @@ EXPORTS = [
     "rz_reinforce_zero_fwd_bwd", "rz_diagnostics", "rz_sample_tokens",
     "rz_grad_norms", "rz_response_diagnostics", "rz_run_summary",
     "rz_dequantize_head", "rz_lora_augment", "rz_lora_merge_head",
-    "rz_reinforce_zero_fwd_bwd_lora",
+    "rz_reinforce_zero_fwd_bwd_lora", "rz_token_logprobs_mx",
+    "rz_sample_tokens_mx",
     "rz_timing_enable", "rz_timing_num_kernels", "rz_timing_kernel_name",
     "rz_timing_read",
 ]
@@ -100,6 +103,12 @@ def load_library():
         vp, vp, vp, vp, f32, i32, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32,
         ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.rz_reinforce_zero_fwd_bwd_lora.restype = ctypes.c_int
+    lib.rz_token_logprobs_mx.argtypes = [vp, vp, vp, ctypes.c_int, vp, i64, i32, i32,
+                                         vp, vp, vp, vp, sz, vp]
+    lib.rz_token_logprobs_mx.restype = ctypes.c_int
+    lib.rz_sample_tokens_mx.argtypes = [vp, vp, vp, ctypes.c_int, vp, i64, i32, i32,
+                                        ctypes.c_uint64, vp, vp, vp, vp, vp, sz, vp]
+    lib.rz_sample_tokens_mx.restype = ctypes.c_int
     lib.rz_dequantize_head.argtypes = [vp, vp, i32, i32, ctypes.c_int, vp, vp, vp]
     lib.rz_dequantize_head.restype = ctypes.c_int
     lib.rz_timing_enable.argtypes = [ctypes.c_int]
@@ -438,6 +447,73 @@ def dequantize_head(codes, scales, fmt: str, *, err_flag=None, stream=None,
                                   RZ_MX_FORMATS[fmt], _ptr(W), _ptr(err_flag),
                                   _stream(stream)), "rz_dequantize_head")
     return W
+
+
+def _mx_head(codes, scales, fmt, dev):
+    torch = _torch()
+    if fmt not in RZ_MX_FORMATS:
+        raise RzError(f"fmt must be one of {sorted(RZ_MX_FORMATS)}, got {fmt!r}")
+    _need(codes, "codes", torch.uint8, 2, dev)
+    _need(scales, "scales", torch.uint8, 2, dev)
+    V = codes.shape[0]
+    H = codes.shape[1] * (2 if fmt == "mxfp4" else 1)
+    if tuple(scales.shape) != (V, H // 32):
+        raise RzError("scales must be [V, H/32]")
+    return V, H
+
+
+def token_logprobs_mx(hidden, codes, scales, fmt: str, tokens, *,
+                      want_lse: bool = False, err_flag=None,
+                      workspace: Optional[Workspace] = None, stream=None):
+    """log pi on an MX-format head (rz_token_logprobs_mx); bf16 hidden."""
+    torch = _torch()
+    lib = load_library()
+    _need(hidden, "hidden", torch.bfloat16, 2)
+    dev = hidden.device
+    V, H = _mx_head(codes, scales, fmt, dev)
+    _need(tokens, "tokens", torch.int32, 1, dev)
+    N = hidden.shape[0]
+    if hidden.shape[1] != H or tokens.shape[0] != N:
+        raise RzError("shape mismatch between hidden, the MX head and tokens")
+    logprobs = torch.empty(N, dtype=torch.float32, device=dev)
+    lse = torch.empty(N, dtype=torch.float32, device=dev) if want_lse else None
+    nbytes = workspace_bytes(RZ_OP_TOKEN_LOGPROBS_MX, N, 1, H, V, RZ_DTYPE_BF16)
+    ws = _workspace(workspace, nbytes, dev)
+    _check(lib.rz_token_logprobs_mx(_ptr(hidden), _ptr(codes), _ptr(scales),
+                                    RZ_MX_FORMATS[fmt], _ptr(tokens), N, H, V,
+                                    _ptr(logprobs), _ptr(lse), _ptr(err_flag),
+                                    _ptr(ws), nbytes, _stream(stream)),
+           "rz_token_logprobs_mx")
+    return (logprobs, lse) if want_lse else logprobs
+
+
+def sample_tokens_mx(hidden, codes, scales, fmt: str, row_ids, seed: int, *,
+                     want_lse: bool = False, err_flag=None,
+                     workspace: Optional[Workspace] = None, stream=None):
+    """The rollout draw on an MX-format head (rz_sample_tokens_mx)."""
+    torch = _torch()
+    lib = load_library()
+    _need(hidden, "hidden", torch.bfloat16, 2)
+    dev = hidden.device
+    V, H = _mx_head(codes, scales, fmt, dev)
+    _need(row_ids, "row_ids", torch.int64, 1, dev)
+    N = hidden.shape[0]
+    if hidden.shape[1] != H or row_ids.shape[0] != N:
+        raise RzError("shape mismatch between hidden, the MX head and row_ids")
+    if not 0 <= int(seed) < 2 ** 64:
+        raise RzError("seed must be in [0, 2**64)")
+    tokens = torch.empty(N, dtype=torch.int32, device=dev)
+    logmu = torch.empty(N, dtype=torch.float32, device=dev)
+    lse = torch.empty(N, dtype=torch.float32, device=dev) if want_lse else None
+    nbytes = workspace_bytes(RZ_OP_SAMPLE_MX, N, 1, H, V, RZ_DTYPE_BF16)
+    ws = _workspace(workspace, nbytes, dev)
+    _check(lib.rz_sample_tokens_mx(_ptr(hidden), _ptr(codes), _ptr(scales),
+                                   RZ_MX_FORMATS[fmt], _ptr(row_ids), N, H, V,
+                                   ctypes.c_uint64(int(seed)), _ptr(tokens),
+                                   _ptr(logmu), _ptr(lse), _ptr(err_flag),
+                                   _ptr(ws), nbytes, _stream(stream)),
+           "rz_sample_tokens_mx")
+    return (tokens, logmu, lse) if want_lse else (tokens, logmu)
 
 
 # ------------------------------------------------------- run-level diagnostics

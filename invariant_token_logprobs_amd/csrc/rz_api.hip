@@ -89,6 +89,12 @@ size_t carve_gn(Carver& c, int64_t n, int32_t H, int32_t V, GnWs* w) {
   return c.off;
 }
 
+// ---- MX-format head: the 64-row tile reads the codes itself; otherwise the
+// head is expanded to bf16 at the end of the workspace first ----
+bool mx_fused(int64_t n, int32_t H, bool sample) {
+  return n <= mx_rows64_max(sample ? 1 : 0) && H % 128 == 0;
+}
+
 // ---- fwd_bwd layout ----
 struct FbWs {
   int* nvalid;
@@ -282,6 +288,13 @@ size_t rz_workspace_bytes(rz_op op, int64_t n_rows, int32_t n_resp, int32_t H,
     case RZ_OP_SAMPLE:
       if (!dims_ok(H, V, dt)) return 0;
       return n_rows == 0 ? 0 : carve_smp(c, n_rows, V, nullptr);
+    case RZ_OP_TOKEN_LOGPROBS_MX:
+    case RZ_OP_SAMPLE_MX: {
+      if (!dims_ok(H, V, RZ_DTYPE_BF16) || n_rows == 0) return 0;
+      const bool smp = op == RZ_OP_SAMPLE_MX;
+      return (smp ? carve_smp(c, n_rows, V, nullptr) : carve_tlp(c, n_rows, V, nullptr)) +
+             (mx_fused(n_rows, H, smp) ? 0 : align_up(2 * (size_t)V * (size_t)H));
+    }
     case RZ_OP_FWD_BWD_LORA:
       if (!dims_ok(H, V, dt) || n_resp < 1 || H + kLoraCols > RZ_MAX_HIDDEN) return 0;
       return carve_lora(c, n_rows, n_resp, H, V, dt, nullptr);
@@ -573,6 +586,103 @@ rz_status rz_run_summary(const float* d3, const float* kl,
   out[4] = median(kl, n_steps - w, n_steps);
   out[5] = out[4] / out[3];
   out[6] = maximum(grad_norm);
+  return RZ_OK;
+}
+
+static rz_status mx_args_ok(const void* hidden, const uint8_t* codes,
+                            const uint8_t* scales, rz_mx_format fmt,
+                            int64_t n_rows, int32_t H, int32_t V) {
+  if (fmt != RZ_MX_FP4 && fmt != RZ_MX_FP8) return RZ_ERR_UNSUPPORTED;
+  if (n_rows < 0 || n_rows > RZ_MAX_ROWS) return RZ_ERR_INVALID_ARG;
+  if (H <= 0 || V <= 0) return RZ_ERR_INVALID_ARG;
+  if (!dims_ok(H, V, RZ_DTYPE_BF16)) return RZ_ERR_UNSUPPORTED;
+  if (n_rows > 0 && (!hidden || !codes || !scales)) return RZ_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(codes) | reinterpret_cast<uintptr_t>(scales)) & 15)
+    return RZ_ERR_INVALID_ARG;
+  return RZ_OK;
+}
+
+rz_status rz_token_logprobs_mx(const void* hidden, const uint8_t* codes,
+                               const uint8_t* scales, rz_mx_format fmt,
+                               const int32_t* tokens, int64_t n_rows, int32_t H,
+                               int32_t V, float* logprobs, float* lse,
+                               int32_t* err_flag, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  rz_status st = mx_args_ok(hidden, codes, scales, fmt, n_rows, H, V);
+  if (st != RZ_OK) return st;
+  if (n_rows == 0) return RZ_OK;
+  if (!tokens || !logprobs) return RZ_ERR_INVALID_ARG;
+  const bool fused = mx_fused(n_rows, H, false);
+  Carver meas{nullptr};
+  const size_t need = carve_tlp(meas, n_rows, V, nullptr) +
+                      (fused ? 0 : align_up(2 * (size_t)V * (size_t)H));
+  st = ws_check(workspace, workspace_bytes, need);
+  if (st != RZ_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  Carver c{reinterpret_cast<char*>(workspace)};
+  TlpWs w;
+  carve_tlp(c, n_rows, V, &w);
+  const int nt = (V + kVocabTile - 1) / kVocabTile;
+  DevRows rows{nullptr, 0, (int)n_rows};
+  if (fused) {
+    RZ_TRY(launch_fwd_mx(fmt, hidden, n_rows, codes, scales, H, V, tokens,
+                         w.partials, n_rows, w.ztgt, nullptr, 0, nullptr,
+                         err_flag, s));
+  } else {
+    void* Wb = c.take<char>(2 * (size_t)V * (size_t)H);
+    RZ_TRY(launch_mx_dequant(fmt, codes, scales, (int64_t)V * (H / 32), Wb,
+                             err_flag, s));
+    RZ_TRY(launch_fwd_logits(RZ_DTYPE_BF16, hidden, (int64_t)H * 2, nullptr,
+                             rows, Wb, H, V, tokens, w.partials, n_rows,
+                             w.ztgt, nullptr, 0, 0, s));
+  }
+  RZ_TRY(launch_lse_merge(w.partials, n_rows, nt, rows, w.ztgt, tokens, V,
+                          lse, logprobs, nullptr, nullptr, err_flag, s));
+  return RZ_OK;
+}
+
+rz_status rz_sample_tokens_mx(const void* hidden, const uint8_t* codes,
+                              const uint8_t* scales, rz_mx_format fmt,
+                              const uint64_t* row_ids, int64_t n_rows,
+                              int32_t H, int32_t V, uint64_t seed,
+                              int32_t* tokens, float* logmu, float* lse,
+                              int32_t* err_flag, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  rz_status st = mx_args_ok(hidden, codes, scales, fmt, n_rows, H, V);
+  if (st != RZ_OK) return st;
+  if (n_rows == 0) return RZ_OK;
+  if (!row_ids || !tokens || !logmu) return RZ_ERR_INVALID_ARG;
+  const bool fused = mx_fused(n_rows, H, true);
+  Carver meas{nullptr};
+  const size_t need = carve_smp(meas, n_rows, V, nullptr) +
+                      (fused ? 0 : align_up(2 * (size_t)V * (size_t)H));
+  st = ws_check(workspace, workspace_bytes, need);
+  if (st != RZ_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  Carver c{reinterpret_cast<char*>(workspace)};
+  SmpWs w;
+  carve_smp(c, n_rows, V, &w);
+  const int nt = (V + kVocabTile - 1) / kVocabTile;
+  DevRows rows{nullptr, 0, (int)n_rows};
+  if (fused) {
+    RZ_TRY(launch_fwd_mx(fmt, hidden, n_rows, codes, scales, H, V, nullptr,
+                         w.partials, n_rows, nullptr, row_ids, seed, w.cand,
+                         err_flag, s));
+    RZ_TRY(launch_draw_merge(w.cand, n_rows, nt, n_rows, tokens, s));
+    RZ_TRY(launch_target_logit_mx(fmt, hidden, n_rows, codes, scales, H, V,
+                                  tokens, w.ztgt, s));
+  } else {
+    void* Wb = c.take<char>(2 * (size_t)V * (size_t)H);
+    RZ_TRY(launch_mx_dequant(fmt, codes, scales, (int64_t)V * (H / 32), Wb,
+                             err_flag, s));
+    RZ_TRY(launch_fwd_sample(RZ_DTYPE_BF16, hidden, n_rows, Wb, H, V, row_ids,
+                             seed, w.partials, w.cand, n_rows, s));
+    RZ_TRY(launch_draw_merge(w.cand, n_rows, nt, n_rows, tokens, s));
+    RZ_TRY(launch_target_logit(RZ_DTYPE_BF16, hidden, (int64_t)H * 2, nullptr,
+                               rows, Wb, H, V, tokens, w.ztgt, s));
+  }
+  RZ_TRY(launch_lse_merge(w.partials, n_rows, nt, rows, w.ztgt, tokens, V,
+                          lse, logmu, nullptr, nullptr, nullptr, s));
   return RZ_OK;
 }
 

@@ -463,4 +463,217 @@ __device__ __forceinline__ void gemm_mainloop_rows64(const GemmOperands& op, int
   }
 }
 
+// ---- MX-format B operand (the release-precision head) ----
+// gfx950's scaled conversions
+// (v_cvt_scalef32_pk_bf16_fp4 / _fp8: two codes times a float scale to two
+// bf16 values, low nibble / low byte first), which an exhaustive check over
+// every code at every E8M0 scale found exact wherever the result is a bf16
+// number -- the whole valid range, subnormal results included.  The scale
+// 2^s is the float with exponent field s + 127 (2^-127: the subnormal
+// 0x00400000).
+__device__ __forceinline__ float e8m0_scale(int code) {
+  return __builtin_bit_cast(float, code == 0 ? 0x00400000u : (uint32_t)code << 23);
+}
+
+// 8 E2M1 codes (4 bytes, low nibble first) -> 8 bf16 values
+__device__ __forceinline__ u32x4 fp4x8_to_bf16(uint32_t c, float sc) {
+  return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 0)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 1)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 2)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 3))};
+}
+// 8 E4M3 codes (8 bytes, low byte first) -> 8 bf16 values
+__device__ __forceinline__ u32x4 fp8x8_to_bf16(u32x2 c, float sc) {
+  return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, sc, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, sc, true)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, sc, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, sc, true))};
+}
+
+__device__ __forceinline__ bool mx_scale_ok(int fmt, int code) {
+  const int s = code - 127;
+  return code != 255 && (fmt == 0 ? s <= 125 : (s >= -124 && s <= 119));
+}
+
+// The 64-row tile with the head W read from MX storage (codes and E8M0
+// block scales) instead of bf16.  Each fragment of W is made in registers by
+// the scaled conversions above -- exact on every valid block -- so the MFMA
+// operands, and with them every accumulator, equal those of
+// gemm_mainloop_rows64 on the expanded bf16 head.  A stage is 64 A rows
+// (bf16, swizzled as in gemm_mainloop), the stage's 64 K values of the 256 W
+// rows as codes, and one dword of scales per W row (4 blocks: this stage and
+// its even/odd partner); all arrive by LDS DMA in a ring of kRing stages, so
+// kRing - 1 stages stream while one feeds the MFMAs, one barrier per stage.
+// Code rows are 32 (E2M1) or 64 (E4M3) bytes whose 16-byte chunks are XOR
+// swizzled by row bits 3 (E2M1) or 2..3 (E4M3), which keeps the fragment
+// reads bank-conflict free.  Needs H % 128 == 0 (whole scale dwords).
+// A block with an invalid scale gives NaN fragments and sets `bad`.
+template <int kFmt>
+struct MxStage {
+  static constexpr int kCodeRow = kFmt == 0 ? 32 : 64;
+  static constexpr int kCodes = 256 * kCodeRow;
+  static constexpr int kScales = 256 * 4;
+  static constexpr int kBytes = kOperandBytesA64 + kCodes + kScales;
+  // stages in the ring: three (E2M1: 51 KB, three workgroups share a CU, so
+  // the Qwen3-4B head's 594 vocab tiles run in one round; E4M3: 75 KB, two)
+  static constexpr int kRing = 3;
+  static constexpr int kLds = kRing * kBytes;
+  static constexpr int kCodeLoads = kCodes / 4096;      // per wave per stage
+  static constexpr int kLoads = 2 + kCodeLoads + 1;     // A, codes, scales
+};
+
+template <int kFmt>
+__device__ __forceinline__ void gemm_mainloop_rows64_mx(
+    const GemmOperands& op, const uint8_t* wcodes, const uint8_t* wscales,
+    int H, int M, int m0, int n0, int nk, f32x16 (&acc)[1][kTN], char* lds,
+    bool& bad) {
+  using S = MxStage<kFmt>;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wid = tid >> 6;
+  const int wm = wid >> 1, wn = wid & 1, half = lane >> 5;
+#pragma unroll
+  for (int ni = 0; ni < kTN; ++ni)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[0][ni][r] = 0.f;
+  if (nk <= 0) return;
+
+  const int a_off = (wm * 32 + (lane & 31)) * kRowBytes;
+  int c_off[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    c_off[s] = ((2 * s + (lane >> 5)) ^ swz(lane & 31)) << 4;
+  int brow[kTN];
+#pragma unroll
+  for (int ni = 0; ni < kTN; ++ni) brow[ni] = wn * 128 + ni * 32 + (lane & 31);
+
+  typedef __attribute__((address_space(3))) void* lds_ptr_t;
+  const int wu = __builtin_amdgcn_readfirstlane(wid);
+  const int64_t code_ld = kFmt == 0 ? H / 2 : H, scale_ld = H / 32;
+  const char* ga[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = wu * 16 + 8 * i + (lane >> 3);
+    const int c = (lane & 7) ^ swz(r);
+    int m = m0 + r;
+    m = m < M ? m : M - 1;
+    const int64_t prow = op.a_rows ? (int64_t)op.a_rows[op.a_base + m] : op.a_base + m;
+    ga[i] = op.A + prow * op.lda + c * 16;
+  }
+  // code loads: lane l of load i lands at LDS offset 16 l of its 1 KB span,
+  // i.e. physical chunk l % (kCodeRow / 16) of row l / (kCodeRow / 16); it
+  // fetches the logical chunk the swizzle places there
+  // sized 4, the larger count (the host pass rejects capturing an array
+  // whose size depends on the local alias)
+  const char* gc[4] = {nullptr, nullptr, nullptr, nullptr};
+#pragma unroll
+  for (int i = 0; i < S::kCodeLoads; ++i) {
+    constexpr int kChunks = S::kCodeRow / 16;
+    const int r = wu * 64 + i * (64 / S::kCodeLoads) + lane / kChunks;
+    const int phys = lane % kChunks;
+    const int logical = kFmt == 0 ? phys ^ ((r >> 3) & 1) : phys ^ ((r >> 2) & 3);
+    int n = n0 + r;
+    n = n < op.N ? n : op.N - 1;
+    gc[i] = (const char*)wcodes + (int64_t)n * code_ld + logical * 16;
+  }
+  int ns = n0 + wu * 64 + lane;
+  ns = ns < op.N ? ns : op.N - 1;
+  const char* gs = (const char*)wscales + (int64_t)ns * scale_ld;
+
+  constexpr int kStB = MxStage<kFmt>::kBytes, kCL = MxStage<kFmt>::kCodeLoads;
+  constexpr int kCR = MxStage<kFmt>::kCodeRow, kCB = MxStage<kFmt>::kCodes;
+  auto dma = [&](int kt, int buf) {
+    char* st = lds + buf * kStB;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_global_load_lds(ga[i] + (int64_t)kt * kRowBytes,
+                                       (lds_ptr_t)(st + (wu * 16 + 8 * i) * kRowBytes),
+                                       16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < kCL; ++i)
+      __builtin_amdgcn_global_load_lds(
+          gc[i] + (int64_t)kt * kCR,
+          (lds_ptr_t)(st + kOperandBytesA64 + (wu * 64 + i * (64 / kCL)) * kCR),
+          16, 0, 0);
+    __builtin_amdgcn_global_load_lds(gs + (kt >> 1) * 4,
+                                     (lds_ptr_t)(st + kOperandBytesA64 + kCB + wu * 256),
+                                     4, 0, 0);
+  };
+
+#pragma unroll
+  for (int p = 0; p < S::kRing - 1; ++p)
+    if (p < nk) dma(p, p);
+  bool anybad = false;
+  for (int kt = 0; kt < nk; ++kt) {
+    // this wave's loads of stage kt are done when at most those of the
+    // stages after it (up to kRing - 2 of them) are outstanding; the barrier
+    // then makes every wave's visible and retires the reads of stage kt - 1,
+    // whose buffer takes stage kt + kRing - 1
+    const int later = (nk - 1 - kt) < (S::kRing - 2) ? (nk - 1 - kt) : (S::kRing - 2);
+    if constexpr (S::kLoads == 5) {
+      if (later >= 2) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+      else if (later == 1) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+      if (later >= 2) asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
+      else if (later == 1) asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();
+    if (kt + S::kRing - 1 < nk) dma(kt + S::kRing - 1, (kt + S::kRing - 1) % S::kRing);
+    const char* st = lds + (kt % S::kRing) * S::kBytes;
+    const char* sc = st + kOperandBytesA64;
+    const char* ss = sc + S::kCodes;
+    // everything the stage needs from LDS first (one wait), then all 16
+    // fragments of W, then the 16 MFMAs: per accumulator still k = 0, 1, ...
+    uint32_t sw[kTN];
+#pragma unroll
+    for (int ni = 0; ni < kTN; ++ni)
+      sw[ni] = *reinterpret_cast<const uint32_t*>(ss + brow[ni] * 4);
+    u32x4 fa[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      fa[s] = *reinterpret_cast<const u32x4*>(st + a_off + c_off[s]);
+    constexpr int kCh = S::kCodeRow / 16;  // 16-byte chunks per code row
+    u32x4 cw[kTN][kCh];
+#pragma unroll
+    for (int ni = 0; ni < kTN; ++ni)
+#pragma unroll
+      for (int c = 0; c < kCh; ++c) {
+        const int sw_bits = kFmt == 0 ? ((brow[ni] >> 3) & 1) : ((brow[ni] >> 2) & 3);
+        cw[ni][c] = *reinterpret_cast<const u32x4*>(sc + brow[ni] * S::kCodeRow +
+                                                    ((c ^ sw_bits) << 4));
+      }
+    const int sbyte = 2 * (kt & 1);
+    u32x4 fb[4][kTN];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int ni = 0; ni < kTN; ++ni) {
+        const int code = (sw[ni] >> (8 * (sbyte + (s >> 1)))) & 0xFF;
+        const bool ok = mx_scale_ok(kFmt, code);
+        anybad |= !ok;
+        u32x4 v;
+        if constexpr (kFmt == 0) {
+          // K values 16 s + 8 half .. + 7: chunk s / 2, word 2 (s % 2) + half
+          const u32x4 ch = cw[ni][s >> 1];
+          const uint32_t c4 = (s & 1) ? (half ? ch[3] : ch[2]) : (half ? ch[1] : ch[0]);
+          v = fp4x8_to_bf16(c4, e8m0_scale(code));
+        } else {
+          // chunk s, words 2 half and 2 half + 1
+          const u32x4 ch = cw[ni][s];
+          const u32x2 c8 = half ? u32x2{ch[2], ch[3]} : u32x2{ch[0], ch[1]};
+          v = fp8x8_to_bf16(c8, e8m0_scale(code));
+        }
+        fb[s][ni] = ok ? v : u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+      }
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int ni = 0; ni < kTN; ++ni)
+        mfma_step(acc[0][ni], fb[s][ni], fa[s], (const bf16*)nullptr);
+  }
+  __syncthreads();  // the caller may reuse the ring's LDS
+  bad = anybad;
+}
+
 }  // namespace rz

@@ -94,6 +94,16 @@ hipError_t launch_lora_grads(int dt, const float* dh_aug, int64_t n, int H,
                              const void* hidden, const void* lora_A, int r,
                              float scale, float* part, float* d_hidden,
                              float* d_lora_A, hipStream_t s);
+int mx_rows64_max(int sample);
+hipError_t launch_fwd_mx(int fmt, const void* hidden, int64_t n,
+                         const uint8_t* codes, const uint8_t* scales, int H,
+                         int V, const int* row_tokens, float2* partials,
+                         int64_t ldp, float* ztgt, const uint64_t* row_ids,
+                         uint64_t seed, float2* cand, int* err, hipStream_t s);
+hipError_t launch_target_logit_mx(int fmt, const void* hidden, int64_t n,
+                                  const uint8_t* codes, const uint8_t* scales,
+                                  int H, int V, const int* row_tokens, float* ztgt,
+                                  hipStream_t s);
 size_t norm_partials(int64_t n);
 hipError_t launch_grad_norm(const float* x, int64_t n, double* partials,
                             float* norm, hipStream_t s);

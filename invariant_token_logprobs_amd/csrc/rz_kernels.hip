@@ -64,6 +64,10 @@ struct FwdArgs {
   const uint64_t* row_ids;  // sampling call only: the rows' identities
   uint64_t seed;
   float2* cand;           // sampling call only: [nt][ldp] (best z + g, index)
+  const uint8_t* wcodes;  // MX head only: codes and E8M0 scales of W
+  const uint8_t* wscales;
+  int H;                  // MX head only: hidden size
+  int* err;               // MX head only: RZ_DEVERR_MX_SCALE
 };
 
 // Storage type of e = exp(z - m_tile) in (0, 1]: fp16 for bf16 inputs (an
@@ -168,7 +172,9 @@ __device__ __forceinline__ bool draw_better(float s, int v, float bs, int bv) {
 // 64-row tile for small row counts).  Both run the same MFMA per 32 x 32
 // block in the same K order and the same per-row folds below, so a row's
 // statistics and draw are bit-identical whichever tile computes them.
-template <typename T, bool kStoreE, bool kSample, int TM>
+// kWFmt: -1 for a bf16 / fp32 head, 0 / 1 for an MXFP4 / MXFP8 head read
+// by the 64-row tile (the accumulators are those of the expanded head).
+template <typename T, bool kStoreE, bool kSample, int TM, int kWFmt = -1>
 __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
   static_assert(TM == kTM || (TM == 1 && !kStoreE), "64-row tile: no e output");
   constexpr int BM = 64 * TM;  // tile rows
@@ -187,10 +193,16 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
   const int m0 = tc.tm * BM, n0 = tc.tn * kBN;
 
   f32x16 acc[TM][kTN];
-  if constexpr (TM == kTM)
+  if constexpr (TM == kTM) {
     gemm_mainloop<T, true>(a.op, M, m0, n0, a.nk, acc, lds);
-  else
+  } else if constexpr (kWFmt < 0) {
     gemm_mainloop_rows64<T>(a.op, M, m0, n0, a.nk, acc, lds);
+  } else {
+    bool bad = false;
+    gemm_mainloop_rows64_mx<kWFmt>(a.op, a.wcodes, a.wscales, a.H, M, m0, n0,
+                                   a.nk, acc, lds, bad);
+    if (bad && a.err) atomicOr(a.err, 8);
+  }
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
@@ -366,6 +378,16 @@ void k_fwd_logits64(FwdArgs a) {
   fwd_logits_body<T, false, kSample, 1>(a, lds);
 }
 
+// The 64-row tile on an MX-format head (bf16 hidden states); E2M1 is sized
+// for three workgroups per CU (LDS and at most 168 VGPRs), E4M3 for two.
+template <int kFmt, bool kSample>
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(kFmt == 0 ? 3 : 2, kFmt == 0 ? 3 : 2)))
+void k_fwd_logits64_mx(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[MxStage<kFmt>::kLds];
+  fwd_logits_body<bf16, false, kSample, 1, kFmt>(a, lds);
+}
+
 // z[t, a_t] = <hidden[t], W[a_t]> for every listed row: one wave per row,
 // lane l folding 16-byte chunks l, l + 64, ... in ascending order (fp32
 // FMA), then a fixed xor butterfly across the wave.  Per-row work in a fixed
@@ -409,6 +431,55 @@ __global__ __launch_bounds__(256) void k_target_logit(
       const f32x4 wf = __builtin_bit_cast(f32x4, wv);
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc = fmaf(hf[j], wf[j], acc);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  if (lane == 0) ztgt[pos] = acc;
+}
+
+// The target logit on an MX-format head: the same 16-byte chunks (8 values)
+// in the same order and the same FMAs as k_target_logit<bf16>, with W's 8
+// values made from their codes by the exact scaled conversion, so the result
+// equals k_target_logit on the expanded head bit for bit.
+template <int kFmt>
+__global__ __launch_bounds__(256) void k_target_logit_mx(
+    const char* __restrict__ hidden, int64_t lda, DevRows rows,
+    const uint8_t* __restrict__ wcodes, const uint8_t* __restrict__ wscales,
+    int H, int V, const int* __restrict__ row_tokens, float* __restrict__ ztgt) {
+  const RowCount rc = to_rc(rows);
+  const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (p >= rc.get()) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t pos = rc.base + p;
+  const int tok = row_tokens[pos];
+  if (tok < 0 || tok >= V) return;
+  const char* hp = hidden + pos * lda;
+  const uint8_t* cp = wcodes + (int64_t)tok * (kFmt == 0 ? H / 2 : H);
+  const uint8_t* sp = wscales + (int64_t)tok * (H / 32);
+  const int nch = H / 8;
+  float acc = 0.f;
+  for (int c = lane; c < nch; c += 64) {
+    const u32x4 hv = *reinterpret_cast<const u32x4*>(hp + (int64_t)c * 16);
+    const int code = sp[c >> 2];
+    u32x4 wv;
+    if constexpr (kFmt == 0)
+      wv = fp4x8_to_bf16(*reinterpret_cast<const uint32_t*>(cp + (int64_t)c * 4),
+                         e8m0_scale(code));
+    else
+      wv = fp8x8_to_bf16(*reinterpret_cast<const u32x2*>(cp + (int64_t)c * 8),
+                         e8m0_scale(code));
+    if (!mx_scale_ok(kFmt, code))
+      wv = u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+    const u32x4 hi_mask = {0xffff0000u, 0xffff0000u, 0xffff0000u, 0xffff0000u};
+    const f32x4 hl = __builtin_bit_cast(f32x4, hv << 16);
+    const f32x4 wl = __builtin_bit_cast(f32x4, wv << 16);
+    const f32x4 hh = __builtin_bit_cast(f32x4, hv & hi_mask);
+    const f32x4 wh = __builtin_bit_cast(f32x4, wv & hi_mask);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc = fmaf(hl[j], wl[j], acc);
+      acc = fmaf(hh[j], wh[j], acc);
     }
   }
 #pragma unroll
@@ -964,36 +1035,8 @@ __global__ __launch_bounds__(1024) void k_resp_diag(
 // scale range checked per block makes every value of a valid block exactly a
 // bf16 number (normal or subnormal), so nothing is rounded.
 // ===================================================================
-// Valid blocks go through gfx950's scaled conversions
-// (v_cvt_scalef32_pk_bf16_fp4 / _fp8: two codes times a float scale to two
-// bf16 values, low nibble / low byte first), which an exhaustive check over
-// every code at every E8M0 scale found exact wherever the result is a bf16
-// number -- the whole valid range, subnormal results included.  The scale
-// 2^s is the float with exponent field s + 127 (2^-127: the subnormal
-// 0x00400000).
-__device__ __forceinline__ float e8m0_scale(int code) {
-  return __builtin_bit_cast(float, code == 0 ? 0x00400000u : (uint32_t)code << 23);
-}
-
-// 8 E2M1 codes (4 bytes, low nibble first) -> 8 bf16 values
-__device__ __forceinline__ u32x4 fp4x8_to_bf16(uint32_t c, float sc) {
-  return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 0)),
-               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 1)),
-               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 2)),
-               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 3))};
-}
-// 8 E4M3 codes (8 bytes, low byte first) -> 8 bf16 values
-__device__ __forceinline__ u32x4 fp8x8_to_bf16(u32x2 c, float sc) {
-  return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, sc, false)),
-               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, sc, true)),
-               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, sc, false)),
-               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, sc, true))};
-}
-
-__device__ __forceinline__ bool mx_scale_ok(int fmt, int code) {
-  const int s = code - 127;
-  return code != 255 && (fmt == 0 ? s <= 125 : (s >= -124 && s <= 119));
-}
+// Valid blocks go through the scaled conversions of rz_gemm.h
+// (fp4x8_to_bf16 / fp8x8_to_bf16).
 
 // A wave expands 64 consecutive blocks (4 KB of bf16) with every load and
 // store instruction covering one contiguous span: in step j = 0..3, lane l
@@ -1621,6 +1664,75 @@ hipError_t launch_fwd_sample(int dt, const void* hidden, int64_t n,
       if (dt) k_fwd_logits<bf16, false, true><<<nblk, kThreads, 0, s>>>(a);
       else k_fwd_logits<float, false, true><<<nblk, kThreads, 0, s>>>(a);
     }
+  });
+}
+
+// The forward of rz_token_logprobs_mx / rz_sample_tokens_mx on the 64-row
+// tile (host-known rows, n <= mx_rows64_max(sample), H % 128 == 0): the
+// target logits, then the logits GEMM with its statistics (and the draw).
+int mx_rows64_max(int sample) { return sample ? kRows64MaxSample : kRows64MaxLogits; }
+
+hipError_t launch_fwd_mx(int fmt, const void* hidden, int64_t n,
+                         const uint8_t* codes, const uint8_t* scales, int H,
+                         int V, const int* row_tokens, float2* partials,
+                         int64_t ldp, float* ztgt, const uint64_t* row_ids,
+                         uint64_t seed, float2* cand, int* err, hipStream_t s) {
+  FwdArgs a{};
+  a.op = GemmOperands{(const char*)hidden, (int64_t)H * 2, nullptr, 0, nullptr, 0, V};
+  a.rows = DevRows{nullptr, 0, (int)n};
+  a.V = V;
+  a.Vpad = V;
+  a.nk = H / Stage<bf16>::kK;
+  a.mt = cdiv(n, kBM64);
+  a.nt = cdiv(V, kBN);
+  a.partials = partials;
+  a.ldp = ldp;
+  a.row_ids = row_ids;
+  a.seed = seed;
+  a.cand = cand;
+  a.wcodes = codes;
+  a.wscales = scales;
+  a.H = H;
+  a.err = err;
+  const int nblk = a.mt * a.nt;
+  if (!cand) {
+    hipError_t e = timed(K_TARGET_LOGIT, s, [&] {
+      if (fmt == 0)
+        k_target_logit_mx<0><<<cdiv(n, 4), 256, 0, s>>>((const char*)hidden, (int64_t)H * 2,
+                                                         a.rows, codes, scales, H, V,
+                                                         row_tokens, ztgt);
+      else
+        k_target_logit_mx<1><<<cdiv(n, 4), 256, 0, s>>>((const char*)hidden, (int64_t)H * 2,
+                                                         a.rows, codes, scales, H, V,
+                                                         row_tokens, ztgt);
+    });
+    if (e != hipSuccess) return e;
+  }
+  return timed(cand ? K_FWD_SAMPLE : K_FWD_LOGITS, s, [&] {
+    if (cand) {
+      if (fmt == 0) k_fwd_logits64_mx<0, true><<<nblk, kThreads, 0, s>>>(a);
+      else k_fwd_logits64_mx<1, true><<<nblk, kThreads, 0, s>>>(a);
+    } else {
+      if (fmt == 0) k_fwd_logits64_mx<0, false><<<nblk, kThreads, 0, s>>>(a);
+      else k_fwd_logits64_mx<1, false><<<nblk, kThreads, 0, s>>>(a);
+    }
+  });
+}
+
+hipError_t launch_target_logit_mx(int fmt, const void* hidden, int64_t n,
+                                  const uint8_t* codes, const uint8_t* scales,
+                                  int H, int V, const int* row_tokens, float* ztgt,
+                                  hipStream_t s) {
+  const DevRows rows{nullptr, 0, (int)n};
+  return timed(K_TARGET_LOGIT, s, [&] {
+    if (fmt == 0)
+      k_target_logit_mx<0><<<cdiv(n, 4), 256, 0, s>>>((const char*)hidden, (int64_t)H * 2,
+                                                       rows, codes, scales, H, V,
+                                                       row_tokens, ztgt);
+    else
+      k_target_logit_mx<1><<<cdiv(n, 4), 256, 0, s>>>((const char*)hidden, (int64_t)H * 2,
+                                                       rows, codes, scales, H, V,
+                                                       row_tokens, ztgt);
   });
 }
 

@@ -120,3 +120,78 @@ def test_mx_qwen3_4b_head_mxfp4():
     assert_close(host(lp), want, t["rtol"], t["atol"], "qwen3-4b mxfp4 logprobs")
     del W
     torch.cuda.empty_cache()
+
+
+def _same_bits(a, b):
+    a, b = host(a), host(b)
+    return np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
+@pytest.mark.parametrize("n,H", [(1, 256), (64, 256), (200, 256), (300, 256), (40, 192)])
+def test_mx_entry_points_equal_the_expanded_head(fmt, n, H):
+    """rz_token_logprobs_mx / rz_sample_tokens_mx against the bf16 calls on
+    rz_dequantize_head's output, bit for bit: the codes read by the 64-row
+    tile (n <= 128 / 256, H % 128 == 0) and the expansion path (the rest)."""
+    import invariant_token_logprobs_amd as rz
+    torch = torch_mod()
+    V = 1000
+    codes, scales = synth.random_mx_head(V, H, fmt, 51 + n + H)
+    hid, tok = synth.random_rows(n, H, V, "bf16", 52 + n)
+    say("mx entry points", fmt, n, H)
+    cd, sd = vec_to_dev(codes), vec_to_dev(scales)
+    hidden = mat_to_dev(hid, "bf16")
+    W = rz.dequantize_head(cd, sd, fmt)
+    tokens = vec_to_dev(tok)
+    lp, lse = rz.token_logprobs_mx(hidden, cd, sd, fmt, tokens, want_lse=True)
+    lp2, lse2 = rz.token_logprobs(hidden, W, tokens, want_lse=True)
+    ids = vec_to_dev(np.arange(n, dtype=np.int64) * 31 + 7)
+    t1, m1, l1 = rz.sample_tokens_mx(hidden, cd, sd, fmt, ids, 0xFEED, want_lse=True)
+    t2, m2, l2 = rz.sample_tokens(hidden, W, ids, 0xFEED, want_lse=True)
+    torch.cuda.synchronize()
+    assert _same_bits(lp, lp2) and _same_bits(lse, lse2)
+    assert torch.equal(t1, t2) and _same_bits(m1, m2) and _same_bits(l1, l2)
+    # and the record is the learner's logprob of the drawn token (diff 0)
+    assert _same_bits(m1, rz.token_logprobs_mx(hidden, cd, sd, fmt, t1))
+
+
+def test_mx_entry_points_invalid_scale():
+    """A NaN scale code in the head: the same NaNs as the expanded head's,
+    and the device flag."""
+    import invariant_token_logprobs_amd as rz
+    torch = torch_mod()
+    V, H, n = 600, 256, 48
+    codes, scales = synth.random_mx_head(V, H, "mxfp4", 61)
+    scales[5, 2] = 255
+    hid, tok = synth.random_rows(n, H, V, "bf16", 62)
+    cd, sd = vec_to_dev(codes), vec_to_dev(scales)
+    hidden, tokens = mat_to_dev(hid, "bf16"), vec_to_dev(tok)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    lp = rz.token_logprobs_mx(hidden, cd, sd, "mxfp4", tokens, err_flag=err)
+    W = rz.dequantize_head(cd, sd, "mxfp4")
+    lp2 = rz.token_logprobs(hidden, W, tokens)
+    torch.cuda.synchronize()
+    assert int(host(err)[0]) & 8
+    assert np.array_equal(np.isnan(host(lp)), np.isnan(host(lp2)))
+    assert np.isnan(host(lp)).all()          # a NaN logit reaches every lse
+
+
+def test_mx_qwen3_4b_head_fused_decode():
+    """The Qwen3-4B head in MXFP4 at 64 live rows: the fused draw equals the
+    draw on the expanded head bit for bit."""
+    import invariant_token_logprobs_amd as rz
+    torch = torch_mod()
+    V, H, n = 151936, 2560, 64
+    codes, scales = synth.random_mx_head(V, H, "mxfp4", 77)
+    hid, _ = synth.random_rows(n, H, V, "bf16", 81)
+    cd, sd = vec_to_dev(codes), vec_to_dev(scales)
+    hidden = mat_to_dev(hid, "bf16")
+    ids = vec_to_dev(np.arange(n, dtype=np.int64))
+    say("mx qwen3-4b fused decode")
+    t1, m1 = rz.sample_tokens_mx(hidden, cd, sd, "mxfp4", ids, 99)
+    W = rz.dequantize_head(cd, sd, "mxfp4")
+    t2, m2 = rz.sample_tokens(hidden, W, ids, 99)
+    torch.cuda.synchronize()
+    assert torch.equal(t1, t2) and _same_bits(m1, m2)
+    del W
+    torch.cuda.empty_cache()
