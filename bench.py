@@ -40,12 +40,12 @@ GEMM_KERNELS = ("fwd_logits_gemm", "bwd_dh_gemm", "bwd_dw_gemm")
 # kernel sources they were taken from.
 COUNTER_TRAFFIC = {
     "workload": "qwen3_4b_tool",
-    "sources_sha256": "8d840745a9caccbdd39da5e89a7de0415c33a955e0ce39ab7f265c72b6961ca9",
-    "bytes_per_launch": {"fwd_logits_gemm": 30437313498,
-                         "bwd_dh_gemm": 24805986334,
-                         "bwd_dw_gemm": 28439622207,
-                         "grad_norm": 2291971831,
-                         "mx_dequant_mxfp4": 984655022},
+    "sources_sha256": "71386c5cee00d35f1488dcbdb6305a478e8adc78f057ee2f0dcbc892c64487ea",
+    "bytes_per_launch": {"fwd_logits_gemm": 30892543452,
+                         "bwd_dh_gemm": 24631077916,
+                         "bwd_dw_gemm": 28404561312,
+                         "grad_norm": 2291986678,
+                         "mx_dequant_mxfp4": 984655273},
 }
 
 
