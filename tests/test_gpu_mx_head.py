@@ -195,3 +195,35 @@ def test_mx_qwen3_4b_head_fused_decode():
     assert torch.equal(t1, t2) and _same_bits(m1, m2)
     del W
     torch.cuda.empty_cache()
+
+
+def test_release_precision_rollout_learner_diff0():
+    """Zero mismatch at release precision: the rollout draws on the MXFP4
+    Qwen3-4B head with the codes read directly (rz_sample_tokens_mx, 48
+    rows), the learner expands the head once and runs its step on the same
+    rows (rz_reinforce_zero_fwd_bwd): the learner's log pi equals the
+    recorded log mu bit for bit on every row, so w = 1, D3 = KL = 0."""
+    import invariant_token_logprobs_amd as rz
+    torch = torch_mod()
+    V, H, n = 151936, 2560, 48
+    codes, scales = synth.random_mx_head(V, H, "mxfp4", 83)
+    hid, _ = synth.random_rows(n, H, V, "bf16", 84)
+    cd, sd = vec_to_dev(codes), vec_to_dev(scales)
+    hidden = mat_to_dev(hid, "bf16")
+    ids = vec_to_dev(np.arange(n, dtype=np.int64) + 1000)
+    say("release precision: rollout draw")
+    tokens, logmu = rz.sample_tokens_mx(hidden, cd, sd, "mxfp4", ids, 2026)
+    say("release precision: learner step")
+    W = rz.dequantize_head(cd, sd, "mxfp4")
+    dev = "cuda:0"
+    out = rz.reinforce_zero_fwd_bwd(
+        hidden, W, tokens, logmu, torch.ones(n, dtype=torch.uint8, device=dev),
+        torch.tensor([0, 20, 48], dtype=torch.int32, device=dev),
+        torch.tensor([1.0, 0.0], dtype=torch.float32, device=dev),
+        torch.zeros(2, dtype=torch.int32, device=dev))
+    torch.cuda.synchronize()
+    assert _same_bits(out["logprobs"], logmu)
+    d = host(out["diag"])
+    assert d[0] == 0.0 and d[1] == 0.0
+    del W
+    torch.cuda.empty_cache()
