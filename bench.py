@@ -40,7 +40,7 @@ GEMM_KERNELS = ("fwd_logits_gemm", "bwd_dh_gemm", "bwd_dw_gemm")
 # kernel sources they were taken from.
 COUNTER_TRAFFIC = {
     "workload": "qwen3_4b_tool",
-    "sources_sha256": "71386c5cee00d35f1488dcbdb6305a478e8adc78f057ee2f0dcbc892c64487ea",
+    "sources_sha256": "4f7868abc7d7ff71e693acfa133b180389401f0efe954b8c607f776a09101215",
     "bytes_per_launch": {"fwd_logits_gemm": 30892543452,
                          "bwd_dh_gemm": 24631077916,
                          "bwd_dw_gemm": 28404561312,

@@ -96,6 +96,11 @@ typedef enum {
 #define RZ_DEVERR_CU_ROWS 4 /* cu_rows not 0..n_rows monotone: loss/adv NaN   */
 #define RZ_DEVERR_MX_SCALE 8 /* an MX block scale outside the exact range     */
 
+/* Alignment: every array the kernels move in 16-byte pieces -- hidden,
+ * lm_head, d_hidden, d_lm_head, lora_A, the MX codes and scales, and the
+ * gradient-norm inputs -- must start on a 16-byte boundary; an entry point
+ * given one that does not returns RZ_ERR_INVALID_ARG before any HIP call. */
+
 /* Limits checked on the host. */
 #define RZ_MAX_ROWS ((int64_t)1 << 30)
 #define RZ_MAX_VOCAB (1 << 24)

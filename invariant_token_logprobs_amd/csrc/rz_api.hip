@@ -196,6 +196,13 @@ size_t carve_lora(Carver& c, int64_t n, int32_t B, int32_t H, int32_t V,
 }
 
 
+// Arrays the kernels move in 16-byte pieces must start 16-byte aligned.
+bool misaligned(const void* a, const void* b = nullptr, const void* c = nullptr,
+                const void* d = nullptr) {
+  return ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b) |
+           reinterpret_cast<uintptr_t>(c) | reinterpret_cast<uintptr_t>(d)) & 15) != 0;
+}
+
 rz_status ws_check(void* ws, size_t have, size_t need) {
   if (need == 0) return RZ_OK;
   if (!ws || (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0 || have < need)
@@ -374,6 +381,7 @@ rz_status rz_sample_tokens(const void* hidden, const void* lm_head,
   if (n_rows == 0) return RZ_OK;
   if (!hidden || !lm_head || !row_ids || !tokens || !logmu)
     return RZ_ERR_INVALID_ARG;
+  if (misaligned(hidden, lm_head)) return RZ_ERR_INVALID_ARG;
   Carver meas{nullptr};
   const size_t need = carve_smp(meas, n_rows, V, nullptr);
   rz_status st = ws_check(workspace, workspace_bytes, need);
@@ -408,6 +416,7 @@ rz_status rz_token_logprobs(const void* hidden, const void* lm_head,
   if (!dims_ok(H, V, dt)) return RZ_ERR_UNSUPPORTED;
   if (n_rows == 0) return RZ_OK;
   if (!hidden || !lm_head || !tokens || !logprobs) return RZ_ERR_INVALID_ARG;
+  if (misaligned(hidden, lm_head)) return RZ_ERR_INVALID_ARG;
   Carver meas{nullptr};
   const size_t need = carve_tlp(meas, n_rows, V, nullptr);
   rz_status st = ws_check(workspace, workspace_bytes, need);
@@ -538,6 +547,7 @@ rz_status rz_reinforce_zero_fwd_bwd(
   if (n_rows > 0 && (!hidden || !tokens || !logmu || !mask || !logprobs ||
                      !d_hidden))
     return RZ_ERR_INVALID_ARG;
+  if (misaligned(hidden, lm_head, d_hidden, d_lm_head)) return RZ_ERR_INVALID_ARG;
   Carver meas{nullptr};
   const size_t need = carve_fb(meas, n_rows, n_resp, H, V, dt, nullptr, -1);
   rz_status st = ws_check(workspace, workspace_bytes, need);
@@ -597,8 +607,7 @@ static rz_status mx_args_ok(const void* hidden, const uint8_t* codes,
   if (H <= 0 || V <= 0) return RZ_ERR_INVALID_ARG;
   if (!dims_ok(H, V, RZ_DTYPE_BF16)) return RZ_ERR_UNSUPPORTED;
   if (n_rows > 0 && (!hidden || !codes || !scales)) return RZ_ERR_INVALID_ARG;
-  if ((reinterpret_cast<uintptr_t>(codes) | reinterpret_cast<uintptr_t>(scales)) & 15)
-    return RZ_ERR_INVALID_ARG;
+  if (misaligned(codes, scales, hidden)) return RZ_ERR_INVALID_ARG;
   return RZ_OK;
 }
 
@@ -695,6 +704,7 @@ rz_status rz_lora_augment(const void* hidden, const void* lora_A, float scale,
   if (!dims_ok(H, 1, dt) || H + kLoraCols > RZ_MAX_HIDDEN) return RZ_ERR_UNSUPPORTED;
   if (n_rows == 0) return RZ_OK;
   if (!hidden || !lora_A || !hidden_aug) return RZ_ERR_INVALID_ARG;
+  if (misaligned(hidden, lora_A)) return RZ_ERR_INVALID_ARG;
   RZ_TRY(launch_lora_u(dt, hidden, lora_A, scale, n_rows, H, r, hidden_aug,
                        reinterpret_cast<hipStream_t>(stream)));
   return RZ_OK;
@@ -732,6 +742,7 @@ rz_status rz_reinforce_zero_fwd_bwd_lora(
   if (n_rows > 0 && (!hidden || !tokens || !logmu || !mask || !logprobs ||
                      !d_hidden))
     return RZ_ERR_INVALID_ARG;
+  if (misaligned(hidden, lm_head, lora_A, d_hidden)) return RZ_ERR_INVALID_ARG;
   Carver meas{nullptr};
   const size_t need = carve_lora(meas, n_rows, n_resp, H, V, dt, nullptr);
   rz_status st = ws_check(workspace, workspace_bytes, need);

@@ -308,3 +308,18 @@ def test_lora_argument_errors(lib):
     assert fb(r=0) == INVALID and fb(r=65) == INVALID
     assert fb(dA=NULL) == INVALID
     assert fb(ws=NULL) == WORKSPACE and fb(wsb=nb - 1) == WORKSPACE
+
+
+def test_misaligned_arrays_are_rejected(lib):
+    """Arrays read in 16-byte pieces must be 16-byte aligned; a misaligned
+    one is an argument error, caught before any HIP call."""
+    bad = ctypes.c_void_p(0x1002)
+    assert tlp(lib, hidden=bad) == INVALID
+    assert tlp(lib, head=bad) == INVALID
+    ids = P
+    assert lib.rz_sample_tokens(bad, P, ids, 4, 64, 10, BF16, ctypes.c_uint64(1), P, P,
+                                NULL, P, 0, NULL) == INVALID
+    f = ctypes.c_float(0.5)
+    assert lib.rz_lora_augment(bad, P, f, 10, 64, 8, BF16, P, NULL) == INVALID
+    assert lib.rz_token_logprobs_mx(bad, P, P, 0, P, 4, 128, 10, P, NULL, NULL, P, 0,
+                                    NULL) == INVALID
