@@ -488,14 +488,15 @@ __global__ __launch_bounds__(256) void k_target_logit_mx(
 }
 
 // ===================================================================
-// bi_logsoftmax_gather merge: per row, eight lanes fold the vocab-tile
-// partials, lane q the tiles q, q + 8, q + 16, ... in ascending order, with
-// (m, s) <- (m', s e^(m - m') + s_j e^(m_j - m')); the eight pairs are then
-// folded the same way in the order q = 0 .. 7.  lse = m + log s and
-// log pi = z[a_t] - lse.  The fold order depends only on V, never on the
-// number of rows or the row's position.
+// bi_logsoftmax_gather merge: one wave per row.  Lane q folds the vocab-tile
+// partials q, q + 64, q + 128, ... in ascending order with
+// (m, s) <- (m', s e^(m - m') + s_j e^(m_j - m')), m' = max(m, m_j); the
+// 64 lane results then meet in a fixed xor tree (offsets 32, 16, ..., 1),
+// and lane 0's result is used.  lse = m + log s and log pi = z[a_t] - lse.
+// The tree's shape and the tiles each lane folds depend only on V, never on
+// the number of rows or the row's position.
 // ===================================================================
-constexpr int kMergeBatch = 8;  // tile partials loaded ahead per lane
+constexpr int kMergeBatch = 4;  // tile partials loaded ahead per lane
 
 __device__ __forceinline__ void ms_fold(float& m, float& s, float mj,
                                         float sj) {
@@ -504,41 +505,48 @@ __device__ __forceinline__ void ms_fold(float& m, float& s, float mj,
   m = mn;
 }
 
+// fold of two pairs where either may be empty (-inf, 0)
+__device__ __forceinline__ void ms_merge(float& m, float& s, float mj, float sj) {
+  if (mj == kNegInf) return;
+  if (m == kNegInf) {
+    m = mj;
+    s = sj;
+    return;
+  }
+  ms_fold(m, s, mj, sj);
+}
+
 __global__ __launch_bounds__(256) void k_lse_merge(
     const float2* __restrict__ partials, int64_t ldp, int nt, DevRows rows,
     const float* __restrict__ ztgt, const int* __restrict__ row_tokens, int V,
     float* lse_out, float* logpi_out, const int* scatter_idx,
     float* logprobs_rows, int* err) {
   const RowCount rc = to_rc(rows);
-  const int p = blockIdx.x * 32 + (threadIdx.x >> 3);
-  const int q = threadIdx.x & 7;
-  // every lane of a row's group of eight stays to the shuffles
-  const bool live = p < rc.get();
-  const int64_t pos = rc.base + (live ? p : 0);
+  const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int q = threadIdx.x & 63;
+  if (p >= rc.get()) return;  // uniform per wave
+  const int64_t pos = rc.base + p;
   float m = kNegInf, s = 0.f;
-  if (live)
-    for (int t0 = q; t0 < nt; t0 += 8 * kMergeBatch) {
-      // loads issued kMergeBatch at a time, folded in the same order
-      float2 ms[kMergeBatch];
+  for (int t0 = q; t0 < nt; t0 += 64 * kMergeBatch) {
+    // loads issued kMergeBatch at a time, folded in ascending tile order
+    float2 ms[kMergeBatch];
 #pragma unroll
-      for (int j = 0; j < kMergeBatch; ++j) {
-        const int t = t0 + 8 * j;
-        if (t < nt) ms[j] = partials[(int64_t)t * ldp + pos];
-      }
-#pragma unroll
-      for (int j = 0; j < kMergeBatch; ++j)
-        if (t0 + 8 * j < nt) ms_fold(m, s, ms[j].x, ms[j].y);
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const int t = t0 + 64 * j;
+      if (t < nt) ms[j] = partials[(int64_t)t * ldp + pos];
     }
-  float M = kNegInf, S = 0.f;
-  const int g0 = threadIdx.x & ~7;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float mj = __shfl(m, g0 + j, 64);
-    const float sj = __shfl(s, g0 + j, 64);
-    if (mj != kNegInf) ms_fold(M, S, mj, sj);  // lanes with no tile hold (-inf, 0)
+    for (int j = 0; j < kMergeBatch; ++j)
+      if (t0 + 64 * j < nt) ms_merge(m, s, ms[j].x, ms[j].y);
   }
-  if (!live || q != 0) return;
-  const float lse = M + logf(S);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float mj = __shfl_xor(m, o, 64);
+    const float sj = __shfl_xor(s, o, 64);
+    ms_merge(m, s, mj, sj);
+  }
+  if (q != 0) return;
+  const float lse = m + logf(s);
   const int tok = row_tokens[pos];
   float lp;
   if (tok >= 0 && tok < V) {
@@ -552,36 +560,35 @@ __global__ __launch_bounds__(256) void k_lse_merge(
   if (scatter_idx) logprobs_rows[scatter_idx[pos]] = lp;
 }
 
-// The draw's merge: per row, the best (score, index) over the vocab tiles
-// under draw_better's total order (lanes take tiles q, q + 8, ...; any
-// meeting order gives the same winner).
+// The draw's merge: per row (one wave), the best (score, index) over the
+// vocab tiles under draw_better's total order, so any meeting order of
+// lanes and tiles gives the same winner.
 __global__ __launch_bounds__(256) void k_draw_merge(
     const float2* __restrict__ cand, int64_t ldp, int nt, int64_t n,
     int* __restrict__ tokens) {
-  const int64_t p = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
-  const int q = threadIdx.x & 7;
-  const bool live = p < n;
+  const int64_t p = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int q = threadIdx.x & 63;
+  if (p >= n) return;  // uniform per wave
   float bs = -__builtin_inff();
   int bv = 0x7fffffff;
-  if (live)
-    for (int t0 = q; t0 < nt; t0 += 8 * kMergeBatch) {
-      float2 c[kMergeBatch];
+  for (int t0 = q; t0 < nt; t0 += 64 * kMergeBatch) {
+    float2 c[kMergeBatch];
 #pragma unroll
-      for (int j = 0; j < kMergeBatch; ++j) {
-        const int t = t0 + 8 * j;
-        if (t < nt) c[j] = cand[(int64_t)t * ldp + p];
-      }
-#pragma unroll
-      for (int j = 0; j < kMergeBatch; ++j) {
-        const int v = __builtin_bit_cast(int, c[j].y);
-        if (t0 + 8 * j < nt && draw_better(c[j].x, v, bs, bv)) {
-          bs = c[j].x;
-          bv = v;
-        }
-      }
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const int t = t0 + 64 * j;
+      if (t < nt) c[j] = cand[(int64_t)t * ldp + p];
     }
 #pragma unroll
-  for (int o = 4; o >= 1; o >>= 1) {
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const int v = __builtin_bit_cast(int, c[j].y);
+      if (t0 + 64 * j < nt && draw_better(c[j].x, v, bs, bv)) {
+        bs = c[j].x;
+        bv = v;
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
     const float os = __shfl_xor(bs, o, 64);
     const int ov = __shfl_xor(bv, o, 64);
     if (draw_better(os, ov, bs, bv)) {
@@ -589,7 +596,7 @@ __global__ __launch_bounds__(256) void k_draw_merge(
       bv = ov;
     }
   }
-  if (live && q == 0) tokens[p] = bv;
+  if (q == 0) tokens[p] = bv;
 }
 
 // ===================================================================
@@ -1739,7 +1746,7 @@ hipError_t launch_target_logit_mx(int fmt, const void* hidden, int64_t n,
 hipError_t launch_draw_merge(const float2* cand, int64_t ldp, int nt, int64_t n,
                              int* tokens, hipStream_t s) {
   return timed(K_DRAW_MERGE, s, [&] {
-    k_draw_merge<<<cdiv(n, 32), 256, 0, s>>>(cand, ldp, nt, n, tokens);
+    k_draw_merge<<<cdiv(n, 4), 256, 0, s>>>(cand, ldp, nt, n, tokens);
   });
 }
 
@@ -1799,7 +1806,7 @@ hipError_t launch_lse_merge(const float2* partials, int64_t ldp, int nt,
                             float* logpi_out, const int* scatter_idx,
                             float* logprobs_rows, int* err, hipStream_t s) {
   return timed(K_LSE_MERGE, s, [&] {
-    k_lse_merge<<<cdiv(rows.cap, 32), 256, 0, s>>>(
+    k_lse_merge<<<cdiv(rows.cap, 4), 256, 0, s>>>(
         partials, ldp, nt, rows, ztgt, row_tokens, V, lse_out, logpi_out,
         scatter_idx, logprobs_rows, err);
   });
