@@ -180,6 +180,9 @@ def bench_sample(args, torch, rz, synth, dev):
     rz.timing_enable(False)
     ms = (te - ts) * 1e3 / args.steps
     assert bool(torch.isfinite(logmu).all()), "non-finite record"
+    fast = fast_baseline(torch, hidden, W if fmt == "bf16" else
+                         rz.dequantize_head(codes, scales, fmt), args) \
+        if args.fast_baseline else None
     gemm_ms, launches = kt["fwd_sample_gemm"]
     avg = gemm_ms / launches
     flop = 2.0 * M * H * V
@@ -228,9 +231,42 @@ def bench_sample(args, torch, rz, synth, dev):
                    "hidden": H, "vocab": V, "rows": M, "head": fmt},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "fast_baseline": (None if fast is None else
+                          dict(fast, aligned_over_fast=round(ms / fast["ms_per_call"], 3))),
         "kernel_ms_per_step": {k: round(v, 4) for k, v in kms.items()},
     }
     print(json.dumps(line), flush=True)
+
+
+def fast_baseline(torch, hidden, W, args):
+    """The unaligned draw the pages compare against: the vendor GEMM
+    (torch.mm on bf16, hipBLASLt), an fp32 log-softmax and a Gumbel-max draw
+    with torch's own generator -- fast, but neither batch-invariant nor
+    reproducible against the learner.  Timed per call like the aligned path
+    (W^T is made contiguous once, outside the timed region)."""
+    WT = W.t().contiguous()
+    gen = torch.Generator(device=hidden.device)
+    gen.manual_seed(7)
+
+    def call():
+        z = torch.mm(hidden, WT).float()
+        lp = torch.log_softmax(z, dim=-1)
+        u = torch.rand(z.shape, generator=gen, device=z.device)
+        tok = torch.argmax(z - torch.log(-torch.log(u)), dim=-1)
+        return tok, lp.gather(1, tok[:, None])[:, 0]
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    del WT
+    return {"ms_per_call": round(ms, 4),
+            "what": "torch.mm (hipBLASLt, bf16) + fp32 log_softmax + Gumbel-max "
+                    "draw with torch.rand; not batch-invariant"}
 
 
 def bench_diag(args, torch, rz, synth, dev):
@@ -403,6 +439,9 @@ def main():
                          "sample: the rollout-side draw + record at decode size; "
                          "diag: the run-level diagnostics over a step's outputs; "
                          "mx: expanding an MX-format head to bf16")
+    ap.add_argument("--fast-baseline", action="store_true",
+                    help="--mode sample: also time the unaligned vendor path "
+                         "(torch.mm + log_softmax + torch RNG draw)")
     ap.add_argument("--head", choices=("bf16", "mxfp4", "mxfp8"), default="bf16",
                     help="--mode sample: the head's storage (MX heads run "
                          "rz_sample_tokens_mx)")
