@@ -40,12 +40,12 @@ GEMM_KERNELS = ("fwd_logits_gemm", "bwd_dh_gemm", "bwd_dw_gemm")
 # kernel sources they were taken from.
 COUNTER_TRAFFIC = {
     "workload": "qwen3_4b_tool",
-    "sources_sha256": "4f7868abc7d7ff71e693acfa133b180389401f0efe954b8c607f776a09101215",
-    "bytes_per_launch": {"fwd_logits_gemm": 30892543452,
-                         "bwd_dh_gemm": 24631077916,
-                         "bwd_dw_gemm": 28404561312,
-                         "grad_norm": 2291986678,
-                         "mx_dequant_mxfp4": 984655273},
+    "sources_sha256": "3a926103c5c284d3598218208544a4204a1efc3eddb6a3a0f28729dd9afeab2b",
+    "bytes_per_launch": {"fwd_logits_gemm": 29318449799,
+                         "bwd_dh_gemm": 24389700910,
+                         "bwd_dw_gemm": 28227910055,
+                         "grad_norm": 2291983581,
+                         "mx_dequant_mxfp4": 984659649},
 }
 
 
@@ -269,6 +269,47 @@ def fast_baseline(torch, hidden, W, args):
                     "draw with torch.rand; not batch-invariant"}
 
 
+def fast_learner_step(torch, hidden, head, tokens, logmu, mask, cu_rows, rewards,
+                      group_ids, chunk=16384):
+    """The learner step the unaligned way, for comparison: per chunk of
+    valid rows, torch.mm (hipBLASLt, bf16) for the logits, the dHidden and the
+    dW products, fp32 logits and log-softmax, the same unclipped IS loss's
+    dL/dz, and dW accumulated in fp32.  Not batch-invariant; W^T is made
+    contiguous once per step."""
+    dev = hidden.device
+    valid = torch.nonzero(mask, as_tuple=True)[0]
+    B = rewards.shape[0]
+    lengths = (cu_rows[1:] - cu_rows[:-1]).long()
+    resp = torch.repeat_interleave(torch.arange(B, device=dev), lengths)
+    T = torch.zeros(B, device=dev).index_add_(0, resp, mask.float())
+    G = int(group_ids.max().item()) + 1
+    gsum = torch.zeros(G, device=dev).index_add_(0, group_ids.long(), rewards)
+    gcnt = torch.zeros(G, device=dev).index_add_(0, group_ids.long(), torch.ones_like(rewards))
+    A = rewards - (gsum / gcnt)[group_ids.long()]
+    fac = (A / (B * T.clamp(min=1)))[resp]                   # A_i / (B T_i) per row
+    WT = head.t().contiguous()
+    dW = torch.zeros(head.shape, dtype=torch.float32, device=dev)
+    d_hidden = torch.zeros(hidden.shape, dtype=torch.float32, device=dev)
+    loss = torch.zeros((), device=dev)
+    for c0 in range(0, valid.numel(), chunk):
+        rows = valid[c0:c0 + chunk]
+        h = hidden[rows]
+        z = torch.mm(h, WT).float()
+        lp = torch.log_softmax(z, dim=-1)
+        tok = tokens[rows].long()
+        lpt = lp.gather(1, tok[:, None])[:, 0]
+        w = torch.exp(lpt - logmu[rows])
+        coef = fac[rows] * w                                   # dL/dlog pi = -coef
+        loss = loss - (coef).sum()
+        g = torch.exp(lp) * coef[:, None]                      # coef (softmax - onehot)
+        g[torch.arange(rows.numel(), device=dev), tok] -= coef
+        gb = g.to(hidden.dtype)
+        d_hidden[rows] = torch.mm(gb, head).float()
+        dW += torch.mm(gb.t().contiguous(), h).float()
+        del z, lp, g, gb
+    return loss, d_hidden, dW
+
+
 def bench_diag(args, torch, rz, synth, dev):
     """Run-level diagnostics over one learner step's outputs at the step's
     shape: rz_grad_norms over dL/dhidden [N, H] and dL/dW [V, H] (fp32),
@@ -440,8 +481,9 @@ def main():
                          "diag: the run-level diagnostics over a step's outputs; "
                          "mx: expanding an MX-format head to bf16")
     ap.add_argument("--fast-baseline", action="store_true",
-                    help="--mode sample: also time the unaligned vendor path "
-                         "(torch.mm + log_softmax + torch RNG draw)")
+                    help="also time the unaligned vendor path: the draw "
+                         "(--mode sample) or the learner step (torch.mm, fp32 "
+                         "log_softmax)")
     ap.add_argument("--head", choices=("bf16", "mxfp4", "mxfp8"), default="bf16",
                     help="--mode sample: the head's storage (MX heads run "
                          "rz_sample_tokens_mx)")
@@ -566,6 +608,24 @@ def main():
     if args.copy_calibration:
         copy_calibration(torch, dev)
 
+    fast = None
+    if args.fast_baseline and not r:
+        log("timing the unaligned vendor-GEMM learner step ...")
+        fargs = [hidden, head, tokens] + args_dev[3:]
+        floss = float(fast_learner_step(torch, *fargs)[0].item())
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fast_learner_step(torch, *fargs)
+        torch.cuda.synchronize()
+        fms = (time.perf_counter() - t0) * 1e3 / args.steps
+        torch.cuda.empty_cache()
+        fast = {"ms_per_step": round(fms, 2), "aligned_over_fast": round(ms / fms, 3),
+                "loss": floss,
+                "what": "per 16384 valid rows: torch.mm (hipBLASLt, bf16) logits, dHidden "
+                        "and dW, fp32 log_softmax and dL/dz, dW accumulated in fp32; not "
+                        "batch-invariant"}
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the float64 oracle on a bounded sample ...")
@@ -588,6 +648,7 @@ def main():
         "algorithmic_flop_per_valid_token": flop_tok,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "fast_baseline": fast,
         "kernel_ms_per_step": {k: round(v, 3) for k, v in kms.items()},
         "loss": loss,
     }
