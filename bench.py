@@ -494,6 +494,11 @@ def main():
                     help="element format of the head in --mode mx")
     ap.add_argument("--sample-rows", type=int, default=1024,
                     help="live rows of the rollout batch in --mode sample")
+    ap.add_argument("--operand-data", choices=("random", "zero"), default="random",
+                    help="learner mode: 'zero' runs the same step with all-zero "
+                         "hidden states and head (same kernels, launches and "
+                         "addresses; only the values the matrix cores see differ), "
+                         "to show what the data costs in power; not a headline figure")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run one plain 1 GiB device "
                          "copy so a counter run can scale its byte counters")
@@ -525,6 +530,10 @@ def main():
 
     isbf = b.dtype == "bf16"
     hidden, head = up(b.hidden, isbf), up(b.lm_head, isbf)
+    zero_ops = args.operand_data == "zero"
+    if zero_ops:
+        hidden.zero_()
+        head.zero_()
     tokens = up(b.tokens)
     r = args.lora_rank
     lora = None
@@ -636,7 +645,10 @@ def main():
         "value": round(value, 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": b.dtype, "data": "synthetic",
+        "vs_baseline": None, "dtype": b.dtype,
+        "data": ("synthetic" if not zero_ops else
+                 "synthetic, zero-valued hidden states and head (power check, "
+                 "not a headline figure)"),
         "config": {"workload": b.name, "hidden": b.H, "vocab": b.V,
                    "responses": b.B, "rows": b.N, "valid_tokens": nv,
                    "masked_frac": round(1 - nv / b.N, 4), "lag_sigma": b.sigma,
