@@ -124,6 +124,7 @@ struct FbWs {
   int* cursor;
   int* offsets;
   int* sorted;
+  float* dwpart;
 };
 // H: the GEMM width (hidden and head row length); dw_cols: the columns of
 // the head that get a gradient (all H, or a LoRA adapter's window)
@@ -164,6 +165,7 @@ size_t carve_fb(Carver& c, int64_t n, int32_t B, int32_t H, int32_t V,
   t.cursor = c.take<int>(sizeof(int) * (size_t)V);
   t.offsets = c.take<int>(sizeof(int) * ((size_t)V + 1));
   t.sorted = c.take<int>(sizeof(int) * (size_t)n);
+  t.dwpart = c.take<float>(sizeof(float) * (size_t)dw_part_floats(V, dw_cols));
   if (w) *w = t;
   return c.off;
 }
@@ -513,7 +515,7 @@ static rz_status fwd_bwd_core(
     const bool kmaj = dt == RZ_DTYPE_BF16;
     RZ_TRY(launch_bwd_dw(dt, kmaj ? w.dz : w.dzT, kmaj ? Vpad : C,
                          N > 0 ? crow : DevRows{nullptr, 0, 0}, w.hT, C,
-                         dw_cols, V, Vpad, d_lm_head, k == 0, s));
+                         dw_cols, V, Vpad, d_lm_head, k == 0, w.dwpart, s));
   }
   if (N > 0) RZ_TRY(launch_rows_finalize(mask, N, H, logprobs, d_hidden, s));
   // a5: S_i from this call's logprobs, then L

@@ -374,11 +374,17 @@ __device__ __forceinline__ void gemm_mainloop(const GemmOperands& op, int M,
 // per vocab tile) bounds the kernel, not the MFMAs.  Rows of A at or past M
 // (B rows past N) read row M - 1 (N - 1), as in gemm_mainloop.  Leaves the
 // LDS free on return.
-template <typename T>
+//
+// kStages = 1 keeps a single 40 KB stage instead (load, wait, compute, in
+// turn): three workgroups then share a CU, so the 594 vocab tiles of a
+// 151936-word head run in one round, and a workgroup's wait or epilogue
+// overlaps the other two's streams.  Same stages, reads and MFMAs.
+template <typename T, int kStages = 2>
 __device__ __forceinline__ void gemm_mainloop_rows64(const GemmOperands& op, int M,
                                                      int m0, int n0, int nk,
                                                      f32x16 (&acc)[1][kTN],
                                                      char* lds) {
+  static_assert(kStages == 1 || kStages == 2, "one or two stages");
   const int tid = threadIdx.x;
   const int lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
@@ -438,13 +444,22 @@ __device__ __forceinline__ void gemm_mainloop_rows64(const GemmOperands& op, int
                                        16, 0, 0);
   };
 
-  dma(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  if constexpr (kStages == 2) {
+    dma(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    // buffer cur ^ 1 was drained by the barrier that ended stage kt - 1
-    if (kt + 1 < nk) dma(kt + 1, cur ^ 1);
+    const int cur = kStages == 2 ? kt & 1 : 0;
+    if constexpr (kStages == 2) {
+      // buffer cur ^ 1 was drained by the barrier that ended stage kt - 1
+      if (kt + 1 < nk) dma(kt + 1, cur ^ 1);
+    } else {
+      // the one buffer was drained by the barrier that ended stage kt - 1
+      dma(kt, 0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
     const char* sa = lds + cur * kStageBytes64;
     const char* sb = sa + kOperandBytesA64;
 #pragma unroll

@@ -153,9 +153,13 @@ hipError_t launch_bwd_dh(int dt, const void* dz, int64_t ldz, DevRows rows,
                          const void* lm_head, float* d_hidden, hipStream_t s);
 // bf16: dz = dz [C][Vpad] (ld = Vpad), read K-major; fp32: dz = dz^T
 // [Vpad][C] (ld = C)
+// Floats of the dW split workspace (launch_bwd_dw's part) for a head of
+// V rows and H gradient columns.
+int64_t dw_part_floats(int V, int H);
 hipError_t launch_bwd_dw(int dt, const void* dz, int64_t ld, DevRows krows,
                          const void* hT, int64_t ldht, int H, int V, int Vpad,
-                         float* d_lm_head, int first, hipStream_t s);
+                         float* d_lm_head, int first, float* part,
+                         hipStream_t s);
 hipError_t launch_dw_fix(int dt, const int* nvalid, int64_t cap,
                          const int* tokv, const int* idx, const float* coef,
                          const void* hidden, int64_t ld, int H, int V, int* counts,

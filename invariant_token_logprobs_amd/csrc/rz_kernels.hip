@@ -22,7 +22,8 @@ constexpr float kNegInf = -__builtin_inff();
 
 // Row counts up to which the forward runs on the 64-row tile (measured at
 // the Qwen3-4B head: the logits forward gains up to 128 rows, the draw, whose
-// epilogue spreads over four times the workgroups, up to 256).
+// epilogue spreads over four times the workgroups, up to 256).  Up to 64
+// rows (one row block) its single-stage form runs, three workgroups per CU.
 constexpr int kRows64MaxLogits = 128;
 constexpr int kRows64MaxSample = 256;
 
@@ -174,7 +175,8 @@ __device__ __forceinline__ bool draw_better(float s, int v, float bs, int bv) {
 // statistics and draw are bit-identical whichever tile computes them.
 // kWFmt: -1 for a bf16 / fp32 head, 0 / 1 for an MXFP4 / MXFP8 head read
 // by the 64-row tile (the accumulators are those of the expanded head).
-template <typename T, bool kStoreE, bool kSample, int TM, int kWFmt = -1>
+template <typename T, bool kStoreE, bool kSample, int TM, int kWFmt = -1,
+          int kStages64 = 2>
 __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
   static_assert(TM == kTM || (TM == 1 && !kStoreE), "64-row tile: no e output");
   constexpr int BM = 64 * TM;  // tile rows
@@ -196,7 +198,7 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
   if constexpr (TM == kTM) {
     gemm_mainloop<T, true>(a.op, M, m0, n0, a.nk, acc, lds);
   } else if constexpr (kWFmt < 0) {
-    gemm_mainloop_rows64<T>(a.op, M, m0, n0, a.nk, acc, lds);
+    gemm_mainloop_rows64<T, kStages64>(a.op, M, m0, n0, a.nk, acc, lds);
   } else {
     bool bad = false;
     gemm_mainloop_rows64_mx<kWFmt>(a.op, a.wcodes, a.wscales, a.H, M, m0, n0,
@@ -376,6 +378,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_fwd_logits64(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes64];
   fwd_logits_body<T, false, kSample, 1>(a, lds);
+}
+
+// The single-stage 64-row tile for at most 64 rows (one row block): 40 KB of
+// LDS and at most 168 VGPRs, three workgroups per CU (see
+// gemm_mainloop_rows64); same per-row results.
+template <typename T, bool kSample>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void k_fwd_logits64_1s(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[kStageBytes64];
+  fwd_logits_body<T, false, kSample, 1, -1, 1>(a, lds);
 }
 
 // The 64-row tile on an MX-format head (bf16 hidden states); E2M1 is sized
@@ -1315,70 +1327,97 @@ __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ in,
 // kVec 16-byte row pieces and writes them back rescaled; for fp32 it then
 // transposes the block in registers and writes kVec 16-byte column pieces
 // of dz^T.  Eight lanes (bf16) cover one 128-byte line of a dz row; no LDS
-// round trip.
+// round trip.  A bf16 workgroup covers two vocab tiles of 64 rows and issues
+// its e loads before it reads the row scales' inputs, so the two latencies
+// overlap.
 // ===================================================================
 template <typename T>
 __global__ __launch_bounds__(256) void k_dz_scale(
     T* __restrict__ dz, int64_t ldz, T* __restrict__ dzT, int64_t ldzt,
     DevRows rows, const float2* __restrict__ partials, int64_t ldp,
     const float* __restrict__ lse, const float* __restrict__ coef, int Vpad) {
-  typedef typename EStore<T>::type E;
   constexpr int kVec = 16 / (int)sizeof(T);       // 8 (bf16) or 4 (fp32)
   constexpr int kG = 64 / kVec;                   // row blocks per wave
   constexpr int kWaveCols = (64 / kG) * kVec;     // 64 (bf16) or 16 (fp32)
   constexpr int kBlockCols = 4 * kWaveCols;       // within one vocab tile
-  __shared__ float sc[64];
+  constexpr int kSpan = sizeof(T) == 2 ? 2 : 1;   // column blocks per workgroup
+  __shared__ float sc[kSpan][64];
   const RowCount rc = to_rc(rows);
   const int R = rc.get();
-  const int r0 = blockIdx.x * 64;
+  const int r0 = blockIdx.y * 64;
   if (r0 >= ((R + 63) & ~63)) return;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int cblk = blockIdx.y * kBlockCols;
-  const int j = cblk / kBN;
-  // one scale per row of this vocab tile: c_t exp(m_tile(t, j) - lse_t)
-  if (tid < 64) {
-    const int t = r0 + tid;
+  const int tr = (lane % kG) * kVec;             // first row of the block
+  // first column of this wave's piece of column block b (whole waves past
+  // Vpad, a multiple of 64, have nothing to do)
+  auto wave_col = [&](int b) {
+    return (blockIdx.x * kSpan + b) * kBlockCols + wid * kWaveCols;
+  };
+  // bf16: the e pieces are loaded first, so their latency overlaps that of
+  // the scales' inputs below
+  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+  u32x4 x[kSpan][8];
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int b = 0; b < kSpan; ++b) {
+      const int col = wave_col(b) + (lane / kG) * kVec;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int t = r0 + tr + i;
+        if (wave_col(b) < Vpad && t < R)
+          x[b][i] = *reinterpret_cast<const u32x4*>(dz + (int64_t)t * ldz + col);
+      }
+    }
+  }
+  // one scale per row and column block: c_t exp(m_tile(t, j) - lse_t), j the
+  // vocab tile holding the block
+  if (tid < 64 * kSpan) {
+    const int b = tid >> 6, t = r0 + (tid & 63);
+    const int j = ((blockIdx.x * kSpan + b) * kBlockCols) / kBN;
     float v = 0.f;
-    if (t < R) {
+    if (t < R && j * kBN < Vpad) {
       const int64_t pos = rc.base + t;
       v = coef[pos] * exp_approx(partials[(int64_t)j * ldp + pos].x - lse[pos]);
     }
-    sc[tid] = v;
+    sc[b][tid & 63] = v;
   }
   __syncthreads();
-  const int cw = cblk + wid * kWaveCols;
-  if (cw >= Vpad) return;  // Vpad is a multiple of 64: whole waves drop out
-  const int tr = (lane % kG) * kVec;             // first row of the block
-  const int col = cw + (lane / kG) * kVec;       // first column
   if constexpr (sizeof(T) == 2) {
-    uint32_t y[8][4];  // y[i]: row tr + i, columns col .. col + 7 (bf16 pairs)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int t = r0 + tr + i;
-      if (t < R) {
+    for (int b = 0; b < kSpan; ++b) {
+      if (wave_col(b) >= Vpad) continue;
+      const int col = wave_col(b) + (lane / kG) * kVec;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int t = r0 + tr + i;
         T* p = dz + (int64_t)t * ldz + col;
-        typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-        const f16x8 x = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(p));
-        const float f = sc[tr + i];
+        if (t < R) {
+          const f16x8 e = __builtin_bit_cast(f16x8, x[b][i]);
+          const float f = sc[b][tr + i];
+          uint32_t y[4];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t lo = __builtin_bit_cast(uint16_t, (T)(f * (float)x[2 * w]));
-          const uint32_t hi = __builtin_bit_cast(uint16_t, (T)(f * (float)x[2 * w + 1]));
-          y[i][w] = lo | (hi << 16);
+          for (int w = 0; w < 4; ++w) {
+            const uint32_t lo = __builtin_bit_cast(uint16_t, (T)(f * (float)e[2 * w]));
+            const uint32_t hi = __builtin_bit_cast(uint16_t, (T)(f * (float)e[2 * w + 1]));
+            y[w] = lo | (hi << 16);
+          }
+          *reinterpret_cast<u32x4*>(p) = u32x4{y[0], y[1], y[2], y[3]};
+        } else {
+          *reinterpret_cast<u32x4*>(p) = u32x4{0u, 0u, 0u, 0u};
         }
-        *reinterpret_cast<u32x4*>(p) = u32x4{y[i][0], y[i][1], y[i][2], y[i][3]};
-      } else {
-        *reinterpret_cast<u32x4*>(dz + (int64_t)t * ldz + col) = u32x4{0u, 0u, 0u, 0u};
       }
     }
   } else {
+    const int cw = wave_col(0);
+    if (cw >= Vpad) return;
+    const int col = cw + (lane / kG) * kVec;
     f32x4 y[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = r0 + tr + i;
       if (t < R) {
         T* p = dz + (int64_t)t * ldz + col;
-        y[i] = sc[tr + i] * *reinterpret_cast<const f32x4*>(p);
+        y[i] = sc[0][tr + i] * *reinterpret_cast<const f32x4*>(p);
         *reinterpret_cast<f32x4*>(p) = y[i];
       } else {
         y[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1461,23 +1500,22 @@ struct DwArgs {
   GemmOperands op;  // bf16: A = dz [K rows][Vpad], K-major; fp32: A = dz^T
   DevRows krows;
   int V, H, amax, kstage, mt, nt, first;  // amax: A columns (bf16) / rows
+  // The last round of tiles splits K: T = mt nt tiles, of which the tail
+  // (those map_tile numbers T - tail .. T - 1) run as split pieces each,
+  // parked in part and summed in order by k_dw_tail.  tail = 0: no split.
+  int T, tail, split;
+  float* part;
   float* dw;
 };
 
-template <typename T>
-__global__ RZ_GEMM_ATTR void k_bwd_dw(DwArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
-  const int K = to_rc(a.krows).get();
-  const int nk = (K + a.kstage - 1) / a.kstage;
-  if (nk == 0 && !a.first) return;
-  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, a.mt, a.nt);
-  const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
+constexpr int kDwTileFloats = kBM * kBN;  // one parked 256 x 256 fp32 tile
+constexpr int kDwSplitMax = 4;            // pieces per tile of the last round
+constexpr int kDwSplitWGs = 256;          // parked tiles at most
 
-  f32x16 acc[kTM][kTN];
-  // bf16 reads dz itself through transposing LDS reads; fp32 has no such
-  // read and takes the transposed copy dz^T
-  gemm_mainloop<T, false, sizeof(T) == 2>(a.op, a.amax, m0, n0, nk, acc, lds);
-
+// dW (+)= acc for one tile: rows v (vocabulary), columns h (hidden); the
+// first chunk overwrites.
+__device__ __forceinline__ void dw_store(const DwArgs& a, int m0, int n0,
+                                         f32x16 (&acc)[kTM][kTN]) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
 #pragma unroll
@@ -1500,6 +1538,77 @@ __global__ RZ_GEMM_ATTR void k_bwd_dw(DwArgs a) {
         if (v < a.V) a.dw[(int64_t)v * a.H + h] = prev[r] + acc[mi][ni][r];
       }
     }
+}
+
+// Parked tile q: 16-byte chunk c of thread t at part + q kDwTileFloats +
+// 4 (256 c + t), chunk c holding registers 4 (c % 4) .. + 3 of block c / 4.
+__device__ __forceinline__ f32x4* dw_part_chunk(float* part, int q, int c) {
+  return reinterpret_cast<f32x4*>(part + (int64_t)q * kDwTileFloats) + c * 256 +
+         threadIdx.x;
+}
+
+template <typename T>
+__global__ RZ_GEMM_ATTR void k_bwd_dw(DwArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  const int K = to_rc(a.krows).get();
+  const int nk = (K + a.kstage - 1) / a.kstage;
+  if (nk == 0 && !a.first) return;
+  // workgroups past the first T - tail take piece `piece` of a last-round tile
+  const int full = a.T - a.tail;
+  int tb = blockIdx.x, piece = 0, pieces = 1;
+  if (tb >= full) {
+    piece = (tb - full) % a.split;
+    tb = full + (tb - full) / a.split;
+    pieces = a.split;
+  }
+  const TileCoord tc = map_tile(tb, a.T, a.mt, a.nt);
+  const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
+  // the piece's K stages [k0, k1); the operands start at stage k0
+  const int k0 = (int)((int64_t)nk * piece / pieces);
+  const int k1 = (int)((int64_t)nk * (piece + 1) / pieces);
+  GemmOperands op = a.op;
+  const int64_t kr = (int64_t)k0 * a.kstage;  // K rows (tokens) before the piece
+  op.A += sizeof(T) == 2 ? kr * op.lda : kr * (int64_t)sizeof(T);
+  op.B += kr * (int64_t)sizeof(T);
+
+  f32x16 acc[kTM][kTN];
+  // bf16 reads dz itself through transposing LDS reads; fp32 has no such
+  // read and takes the transposed copy dz^T
+  gemm_mainloop<T, false, sizeof(T) == 2>(op, a.amax, m0, n0, k1 - k0, acc, lds);
+  if (pieces > 1) {
+    const int q = (tb - full) * pieces + piece;
+#pragma unroll
+    for (int c = 0; c < 4 * kTM * kTN; ++c) {
+      const f32x16& blk = acc[c / 16][(c / 4) % 4];
+      const int r = 4 * (c % 4);
+      *dw_part_chunk(a.part, q, c) = f32x4{blk[r], blk[r + 1], blk[r + 2], blk[r + 3]};
+    }
+    return;
+  }
+  dw_store(a, m0, n0, acc);
+}
+
+// The last round's tiles: the pieces summed in piece order (a fixed order,
+// so dW stays run-to-run deterministic), then stored like any other tile.
+__global__ __launch_bounds__(256) void k_dw_tail(DwArgs a) {
+  const int K = to_rc(a.krows).get();
+  const int nk = (K + a.kstage - 1) / a.kstage;
+  if (nk == 0 && !a.first) return;
+  const int i = blockIdx.x;
+  const TileCoord tc = map_tile(a.T - a.tail + i, a.T, a.mt, a.nt);
+  f32x16 acc[kTM][kTN];
+#pragma unroll
+  for (int c = 0; c < 4 * kTM * kTN; ++c) {
+    f32x4 v = *dw_part_chunk(a.part, i * a.split, c);
+    for (int p = 1; p < a.split; ++p) v += *dw_part_chunk(a.part, i * a.split + p, c);
+    f32x16& blk = acc[c / 16][(c / 4) % 4];
+    const int r = 4 * (c % 4);
+    blk[r] = v[0];
+    blk[r + 1] = v[1];
+    blk[r + 2] = v[2];
+    blk[r + 3] = v[3];
+  }
+  dw_store(a, tc.tm * kBM, tc.tn * kBN, acc);
 }
 
 // ===================================================================
@@ -1664,7 +1773,10 @@ hipError_t launch_fwd_sample(int dt, const void* hidden, int64_t n,
   a.cand = cand;
   const int nblk = a.mt * a.nt;
   return timed(K_FWD_SAMPLE, s, [&] {
-    if (small) {
+    if (small && n <= kBM64) {
+      if (dt) k_fwd_logits64_1s<bf16, true><<<nblk, kThreads, 0, s>>>(a);
+      else k_fwd_logits64_1s<float, true><<<nblk, kThreads, 0, s>>>(a);
+    } else if (small) {
       if (dt) k_fwd_logits64<bf16, true><<<nblk, kThreads, 0, s>>>(a);
       else k_fwd_logits64<float, true><<<nblk, kThreads, 0, s>>>(a);
     } else {
@@ -1786,8 +1898,13 @@ hipError_t launch_fwd_logits(int dt, const void* hidden, int64_t lda_bytes,
   const int nblk = a.mt * a.nt;
   if (small)
     return timed(K_FWD_LOGITS, s, [&] {
-      if (dt) k_fwd_logits64<bf16, false><<<nblk, kThreads, 0, s>>>(a);
-      else k_fwd_logits64<float, false><<<nblk, kThreads, 0, s>>>(a);
+      if (rows.cap <= kBM64) {
+        if (dt) k_fwd_logits64_1s<bf16, false><<<nblk, kThreads, 0, s>>>(a);
+        else k_fwd_logits64_1s<float, false><<<nblk, kThreads, 0, s>>>(a);
+      } else {
+        if (dt) k_fwd_logits64<bf16, false><<<nblk, kThreads, 0, s>>>(a);
+        else k_fwd_logits64<float, false><<<nblk, kThreads, 0, s>>>(a);
+      }
     });
   return timed(K_FWD_LOGITS, s, [&] {
     if (dt) {
@@ -2046,8 +2163,9 @@ hipError_t launch_dz_scale(int dt, void* dz, int64_t ldz, void* dzT,
                            int64_t ldzt, DevRows rows, const float2* partials,
                            int64_t ldp, const float* lse, const float* coef,
                            int Vpad, hipStream_t s) {
-  // 64 rows x (4 waves x 64 bf16 or 16 fp32 columns) per workgroup
-  dim3 grid(cdiv(rows.cap, 64), cdiv(Vpad, dt ? 256 : 64));
+  // 64 rows x (two column blocks of 4 waves x 64 bf16, or one of 4 x 16
+  // fp32 columns) per workgroup; neighbouring workgroups share rows
+  dim3 grid(cdiv(Vpad, dt ? 512 : 64), cdiv(rows.cap, 64));
   return timed(K_DZ_SCALE, s, [&] {
     if (dt)
       k_dz_scale<bf16><<<grid, 256, 0, s>>>((bf16*)dz, ldz, (bf16*)dzT, ldzt,
@@ -2096,9 +2214,16 @@ hipError_t launch_bwd_dh(int dt, const void* dz, int64_t ldz, DevRows rows,
                                      tokv, coef, lm_head, d_hidden, s);
 }
 
+int64_t dw_part_floats(int V, int H) {
+  const int64_t T = (int64_t)cdiv(V, kBM) * cdiv(H, kBN);
+  const int64_t tiles = T * kDwSplitMax < kDwSplitWGs ? T * kDwSplitMax : kDwSplitWGs;
+  return tiles * kDwTileFloats;
+}
+
 hipError_t launch_bwd_dw(int dt, const void* dz, int64_t ld, DevRows krows,
                          const void* hT, int64_t ldht, int H, int V, int Vpad,
-                         float* d_lm_head, int first, hipStream_t s) {
+                         float* d_lm_head, int first, float* part,
+                         hipStream_t s) {
   const int esz = dt ? 2 : 4;
   DwArgs a;
   a.op = GemmOperands{(const char*)dz, ld * esz, nullptr, 0,
@@ -2112,9 +2237,30 @@ hipError_t launch_bwd_dw(int dt, const void* dz, int64_t ld, DevRows krows,
   a.nt = cdiv(H, kBN);
   a.first = first;
   a.dw = d_lm_head;
+  // One workgroup per CU per round: the last round's tiles (tail) would
+  // leave most CUs idle, so each is split into up to kDwSplitMax pieces
+  // along K (fixed by V, H and the CU count, never by the row count).
+  a.T = a.mt * a.nt;
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) !=
+          hipSuccess ||
+      ncu < 1)
+    ncu = 256;
+  a.tail = a.T - (cdiv(a.T, ncu) - 1) * ncu;
+  a.split = ncu / a.tail;
+  if (a.split > kDwSplitMax) a.split = kDwSplitMax;
+  if (a.tail * a.split > kDwSplitWGs) a.split = kDwSplitWGs / a.tail;
+  if (a.split < 2 || !part) {
+    a.tail = 0;
+    a.split = 1;
+  }
+  a.part = part;
   return timed(K_BWD_DW, s, [&] {
-    if (dt) k_bwd_dw<bf16><<<a.mt * a.nt, kThreads, 0, s>>>(a);
-    else k_bwd_dw<float><<<a.mt * a.nt, kThreads, 0, s>>>(a);
+    const int grid = a.T - a.tail + a.tail * a.split;
+    if (dt) k_bwd_dw<bf16><<<grid, kThreads, 0, s>>>(a);
+    else k_bwd_dw<float><<<grid, kThreads, 0, s>>>(a);
+    if (a.tail) k_dw_tail<<<a.tail, kThreads, 0, s>>>(a);
   });
 }
 
