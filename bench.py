@@ -49,6 +49,25 @@ COUNTER_TRAFFIC = {
 }
 
 
+# Matrix-core busy share (SQ_VALU_MFMA_BUSY_CYCLES over the SIMDs' cycles)
+# and clock (GRBM_GUI_ACTIVE per XCD over the launch time) of the learner
+# GEMMs, from the counter run of profiles/mfma_utilisation_qwen3_4b_tool.md,
+# over the launches that hold rows; same validity rule as COUNTER_TRAFFIC.
+COUNTER_MFMA = {
+    "fwd_logits_gemm": {"mfma_busy": 0.578, "clock_ghz": 1.825},
+    "bwd_dh_gemm": {"mfma_busy": 0.596, "clock_ghz": 1.786},
+    "bwd_dw_gemm": {"mfma_busy": 0.569, "clock_ghz": 1.830},
+}
+
+
+def counter_mfma(key, workload="qwen3_4b_tool"):
+    """Counter busy share and clock of `key`, or None once the kernels changed."""
+    if (workload != COUNTER_TRAFFIC["workload"]
+            or kernel_sources_sha256() != COUNTER_TRAFFIC["sources_sha256"]):
+        return None
+    return COUNTER_MFMA.get(key)
+
+
 def counter_traffic(key, workload="qwen3_4b_tool"):
     """Counter bytes per launch of `key`, or None once the kernels changed."""
     if (workload != COUNTER_TRAFFIC["workload"]
@@ -610,7 +629,8 @@ def main():
                 "traffic": traffic,
                 "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                 "avg_launch_ms": round(avg_ms, 4),
-                "launches_per_step": launches // args.steps}
+                "launches_per_step": launches // args.steps,
+                "counters": counter_mfma(dom, b.name) if not r else None}
     log("per-step kernel ms: " + ", ".join(f"{k}={v:.2f}" for k, v in
                                             sorted(kms.items(), key=lambda x: -x[1])))
 

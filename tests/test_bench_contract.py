@@ -49,3 +49,15 @@ def test_counter_traffic_is_void_for_other_sources(monkeypatch):
     assert bench.counter_traffic("bwd_dw_gemm", workload="tiny") is None
     monkeypatch.setattr(bench, "kernel_sources_sha256", lambda: "0" * 64)
     assert bench.counter_traffic("bwd_dw_gemm") is None
+
+
+def test_counter_mfma_is_void_for_other_sources(monkeypatch):
+    sys.path.insert(0, ROOT)
+    import bench
+    sha = bench.COUNTER_TRAFFIC["sources_sha256"]
+    monkeypatch.setattr(bench, "kernel_sources_sha256", lambda: sha)
+    c = bench.counter_mfma("bwd_dw_gemm")
+    assert 0 < c["mfma_busy"] < 1 and 1.0 < c["clock_ghz"] < 2.5
+    monkeypatch.setattr(bench, "kernel_sources_sha256", lambda: "0" * 64)
+    assert bench.counter_mfma("bwd_dw_gemm") is None
+
