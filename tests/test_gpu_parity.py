@@ -81,6 +81,29 @@ def test_multi_chunk_backward(dtype):
     _case(b, f"multichunk-{dtype}")
 
 
+@pytest.mark.parametrize("n_vtiles", [256, 257, 308, 356])
+def test_dw_last_round_split(n_vtiles):
+    """The dW GEMM runs one 256 x 256 tile per CU per round and splits the
+    tiles of its last round along K, summing the pieces in a fixed order.
+    With H = 64 (one column tile) the tile count is the vocab tile count: on
+    a 256-CU part, 256 fills whole rounds (no split), 257 leaves one tile
+    (four pieces), 308 leaves 52 (four pieces, the count at the Qwen3-4B
+    head) and 356 leaves 100 (two pieces).  Each matches the oracle, and a
+    second call gives the same dW bit for bit."""
+    V = 256 * n_vtiles - 37  # a ragged last vocab tile
+    b = small_batch(N_resp=4, group_size=2, H=64, V=V, lo=60, hi=120,
+                    dtype="bf16", seed=21)
+    what = f"dw-split-{n_vtiles}"
+    say(what, f"N={b.N} V={V} tiles={n_vtiles}")
+    logmu = logmu_from_oracle(b)
+    d = batch_to_dev(b, logmu)
+    out = run_fwd_bwd(d)
+    dw1 = host(out["d_lm_head"]).copy()
+    compare_full(out, oracle_full(b, logmu), b, what)
+    again = run_fwd_bwd(d)
+    assert np.array_equal(host(again["d_lm_head"]), dw1), f"{what}: dW not reproducible"
+
+
 def test_qwen3_4b_truncated_full_parity():
     """The headline tool-use shape at its full H = 2560, V = 151936, on the
     first responses up to 1024 valid rows, every output compared."""
