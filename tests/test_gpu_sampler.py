@@ -85,6 +85,40 @@ def test_sampler_parity_and_diff0(dtype):
     _diff0(hidden, W, tok, logmu, lse, f"sampler-{dtype} diff0")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_small_batches_match_the_large_batch(dtype):
+    """Up to 64 rows the forward runs the single-stage 64-row tile, up to 256
+    rows (draw) or 128 rows (logits) the two-stage 64-row tile, and beyond that
+    the 256-row tile.  The first 1, 37, 64 and 65 rows of a batch, drawn and
+    scored alone, give the same tokens, records and log-sum-exps, bit for bit,
+    as they do inside the whole batch."""
+    import invariant_token_logprobs_amd as rz
+    torch = torch_mod()
+    b = small_batch(N_resp=3, group_size=3, H=256, V=1000, lo=100, hi=140,
+                    dtype=dtype, seed=23)
+    assert b.N > 256
+    say("small batches vs large", dtype, "rows", b.N)
+    hidden = mat_to_dev(b.hidden, dtype)
+    W = mat_to_dev(b.lm_head, dtype)
+    ids = _ids(b.N, 9)
+    tok, logmu, lse = _run(hidden, W, ids, SEED)
+    lp_all, lse_all = rz.token_logprobs(hidden, W, vec_to_dev(b.tokens), want_lse=True)
+    torch.cuda.synchronize()
+    lp_all, lse_all = host(lp_all), host(lse_all)
+    bits = lambda x: np.asarray(x, np.float32).view(np.uint32)
+    for n in (1, 37, 64, 65):
+        what = f"{dtype} first {n} rows"
+        t_n, m_n, l_n = _run(hidden[:n].contiguous(), W, ids[:n], SEED)
+        assert np.array_equal(t_n, tok[:n]), what
+        assert np.array_equal(bits(m_n), bits(logmu[:n])), what
+        assert np.array_equal(bits(l_n), bits(lse[:n])), what
+        lp, ls = rz.token_logprobs(hidden[:n].contiguous(), W, vec_to_dev(b.tokens[:n]),
+                                   want_lse=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(host(lp)), bits(lp_all[:n])), what
+        assert np.array_equal(bits(host(ls)), bits(lse_all[:n])), what
+
+
 def test_sampler_frequencies_follow_softmax():
     """60000 draws from one hidden state over V = 24 (fp32): chi-square of
     the counts against the oracle's float64 softmax, 23 degrees of freedom
