@@ -140,12 +140,33 @@ def cpu_baseline(b, logmu, max_valid, lora=None):
     dt = time.perf_counter() - t0
     nv = int(np.count_nonzero(b.mask[:n_keep]))
     assert np.isfinite(out["loss"])
-    return {"value": nv / dt, "unit": "tokens/s", "cores": blas_threads or cores,
-            "kind": "oracle",
-            "sample": (f"first {nb} responses, {nv} valid of {n_keep} rows of "
-                       f"{b.name} at full H={b.H}, V={b.V}; float64 NumPy "
-                       f"fwd+loss+bwd, {dt:.1f} s on {cores} host cores "
-                       f"(BLAS threads {blas_threads})")}
+    res = {"value": nv / dt, "unit": "tokens/s", "cores": blas_threads or cores,
+           "kind": "oracle",
+           "sample": (f"first {nb} responses, {nv} valid of {n_keep} rows of "
+                      f"{b.name} at full H={b.H}, V={b.V}; float64 NumPy "
+                      f"fwd+loss+bwd, {dt:.1f} s on {cores} host cores "
+                      f"(BLAS threads {blas_threads})")}
+    if lora is None:
+        res["tiny"] = tiny_cpu_baseline()
+    return res
+
+
+def tiny_cpu_baseline():
+    """The float64 oracle on the whole Tiny workload (8 responses, fp32,
+    H=256, V=1024): valid tokens per second of one fwd+loss+bwd pass."""
+    import oracle as O
+    from invariant_token_logprobs_amd import synth
+    t = synth.make_workload("tiny")
+    h64, W64 = O.to_f64(t.hidden, t.dtype), O.to_f64(t.lm_head, t.dtype)
+    logpi, _ = O.token_logprobs(h64, W64, t.tokens)
+    logmu = synth.make_logmu(logpi, t.sigma, t.noise_seed).astype(np.float64)
+    t0 = time.perf_counter()
+    out = O.reinforce_zero_fwd_bwd(h64, W64, t.tokens, logmu, t.mask, t.cu_rows,
+                                   t.rewards, t.group_ids)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(out["loss"])
+    return {"value": round(t.n_valid / dt, 1), "unit": "tokens/s",
+            "sample": f"tiny: all {t.n_valid} valid rows, H={t.H}, V={t.V}, {dt * 1e3:.1f} ms"}
 
 
 def copy_calibration(torch, dev):
