@@ -40,12 +40,12 @@ GEMM_KERNELS = ("fwd_logits_gemm", "bwd_dh_gemm", "bwd_dw_gemm")
 # kernel sources they were taken from.
 COUNTER_TRAFFIC = {
     "workload": "qwen3_4b_tool",
-    "sources_sha256": "64a80fab55ca21185368891fe6eef28c7292ae4bae083af5d755e24636521bc3",
-    "bytes_per_launch": {"fwd_logits_gemm": 30759654408,
-                         "bwd_dh_gemm": 24613009925,
-                         "bwd_dw_gemm": 28945214513 + 47679675,  # + its tail sum
-                         "grad_norm": 2291985128,
-                         "mx_dequant_mxfp4": 984647849},
+    "sources_sha256": "40d14eefe1b1593191759f1fd4547e86b46d062021febfddca07d12821aad47c",
+    "bytes_per_launch": {"fwd_logits_gemm": 29355093970,
+                         "bwd_dh_gemm": 24424364965,
+                         "bwd_dw_gemm": 28876816456 + 47679704,  # + its tail sum
+                         "grad_norm": 2291985991,
+                         "mx_dequant_mxfp4": 984648854},
 }
 
 
@@ -54,9 +54,9 @@ COUNTER_TRAFFIC = {
 # GEMMs, from the counter run of profiles/mfma_utilisation_qwen3_4b_tool.md,
 # over the launches that hold rows; same validity rule as COUNTER_TRAFFIC.
 COUNTER_MFMA = {
-    "fwd_logits_gemm": {"mfma_busy": 0.578, "clock_ghz": 1.825},
-    "bwd_dh_gemm": {"mfma_busy": 0.596, "clock_ghz": 1.786},
-    "bwd_dw_gemm": {"mfma_busy": 0.569, "clock_ghz": 1.830},
+    "fwd_logits_gemm": {"mfma_busy": 0.580, "clock_ghz": 1.842},
+    "bwd_dh_gemm": {"mfma_busy": 0.591, "clock_ghz": 1.812},
+    "bwd_dw_gemm": {"mfma_busy": 0.568, "clock_ghz": 1.854},
 }
 
 

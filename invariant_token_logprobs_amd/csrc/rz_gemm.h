@@ -58,6 +58,10 @@ struct Stage {
   static constexpr int kK = kRowBytes / (int)sizeof(T);  // K values per stage
 };
 
+// Cache-policy operand of a load: the non-temporal hint ("nt" on gfx950),
+// for data each workgroup streams once and no other reads again.
+constexpr int kPolicyNT = 2;
+
 constexpr float kLog2e = 1.4426950408889634f;  // log2(e), for exp via exp2
 
 __device__ __forceinline__ float exp_approx(float x) {
@@ -378,7 +382,10 @@ __device__ __forceinline__ void gemm_mainloop(const GemmOperands& op, int M,
 // kStages = 1 keeps a single 40 KB stage instead (load, wait, compute, in
 // turn): three workgroups then share a CU, so the 594 vocab tiles of a
 // 151936-word head run in one round, and a workgroup's wait or epilogue
-// overlaps the other two's streams.  Same stages, reads and MFMAs.
+// overlaps the other two's streams.  Same stages, reads and MFMAs.  This
+// form runs for one row block only, where every byte of the head is read
+// once per call, so its head loads carry the non-temporal hint (the hidden
+// rows, which every workgroup reads, keep the default policy).
 template <typename T, int kStages = 2>
 __device__ __forceinline__ void gemm_mainloop_rows64(const GemmOperands& op, int M,
                                                      int m0, int n0, int nk,
@@ -441,7 +448,7 @@ __device__ __forceinline__ void gemm_mainloop_rows64(const GemmOperands& op, int
     for (int i = 0; i < 8; ++i)
       __builtin_amdgcn_global_load_lds(gb[i] + k,
                                        (lds_ptr_t)(sb + (wu * 64 + 8 * i) * kRowBytes),
-                                       16, 0, 0);
+                                       16, 0, kStages == 1 ? kPolicyNT : 0);
   };
 
   if constexpr (kStages == 2) {
