@@ -387,6 +387,103 @@ def test_importance_sampling_identities_by_enumeration():
     assert B == len(rewards)
 
 
+# --------------------------------------------------------- score centering
+def _enumeration_batch():
+    mu = np.array([0.5, 0.25, 0.125, 0.125])
+    tokens = np.array([0, 0, 0, 0, 1, 1, 2, 3])       # multiset reproduces mu
+    reward_of = np.array([1.0, 0.0, 0.5, 1.0])
+    z = np.array([0.3, -0.1, 0.7, 0.0])
+    return dict(mu=mu, tokens=tokens, reward_of=reward_of, z=z, W=z[:, None],
+                hidden=np.ones((8, 1)), mask=np.ones(8, dtype=np.uint8),
+                cu=np.arange(9), rewards=reward_of[tokens],
+                groups=np.zeros(8, dtype=np.int64), logmu=np.log(mu[tokens]))
+
+
+def test_score_centering_is_the_sampler_covariance_by_enumeration():
+    """'The full IS correction', block 03: g_SC = Cov_q(A, s), and its gap to
+    the target update is Cov_q(A, s) - Cov_p(A, s).  One group of
+    single-token responses whose tokens reproduce q = mu exactly: the SC
+    update (minus the loss gradient wrt the shared logits, collected in
+    dW[:, 0] with hidden = 1) must equal the covariance written in its
+    two-sided form E_q[(A - E_q A)(s - E_q s)], and the gap to the IS update
+    must equal the difference of the two covariances."""
+    e = _enumeration_batch()
+    sc = O.score_centering_fwd_bwd(e["hidden"], e["W"], e["tokens"], e["mask"],
+                                   e["cu"], e["rewards"], e["groups"], e["logmu"])
+    is_ = O.reinforce_zero_fwd_bwd(e["hidden"], e["W"], e["tokens"], e["logmu"],
+                                   e["mask"], e["cu"], e["rewards"], e["groups"])
+    pi = np.exp(e["z"]) / np.exp(e["z"]).sum()
+    q, R = e["mu"], e["reward_of"]
+    score = np.eye(4) - pi                      # row a: grad_z log pi(a)
+    s_q = (q[:, None] * score).sum(axis=0)      # E_q[s] = q - pi (not 0)
+    cov_q = sum(q[a] * (R[a] - q @ R) * (score[a] - s_q) for a in range(4))
+    cov_p = sum(pi[a] * (R[a] - pi @ R) * score[a] for a in range(4))
+    g_sc = -sc["d_lm_head"][:, 0]
+    g_is = -is_["d_lm_head"][:, 0]
+    assert np.allclose(g_sc, cov_q, rtol=0, atol=1e-15)
+    assert np.allclose(g_sc - g_is, cov_q - cov_p, rtol=0, atol=1e-15)
+    assert np.abs(cov_q - cov_p).max() > 1e-2   # q != p: SC keeps a bias
+    # the drift SC removes: the update with uncentred rewards is
+    # Cov_q(R, s) + E_q[R] E_q[s] (block 02)
+    uncentred = sum(q[a] * R[a] * score[a] for a in range(4))
+    assert np.allclose(uncentred, cov_q + (q @ R) * s_q, rtol=0, atol=1e-15)
+    # the diagnostics of the records are those of the IS call
+    assert sc["d3"] == is_["d3"] and sc["kl"] == is_["kl"]
+
+
+def test_score_centering_surrogate_hand_case():
+    """One group, r = (1, 0): A = (1/2, -1/2); T = (1, 3) with a masked row
+    in between.  L_SC = -1/2 (1/2 lp_1 - 1/2 (lp_3 + lp_4 + lp_5) / 3) with
+    lp = (-1/2, *, -1, -2, -1/4) = -7/48."""
+    logpi = np.array([-0.5, -9.0, -1.0, -2.0, -0.25])
+    mask = np.array([1, 0, 1, 1, 1], dtype=np.uint8)
+    cu = np.array([0, 1, 5])
+    A = O.group_mean_advantages(np.array([1.0, 0.0]), np.array([0, 0]))
+    T = O.valid_token_counts(cu, mask)
+    assert list(T) == [1, 3] and list(A) == [0.5, -0.5]
+    assert abs(O.score_centering_surrogate(logpi, mask, cu, A, T) - _frac("-7/48")) < 1e-16
+
+
+def test_score_centering_finite_difference_gradients():
+    p = _small_problem(31)
+    out = O.score_centering_fwd_bwd(p["hidden"], p["W"], p["tokens"], p["mask"],
+                                    p["cu"], p["rewards"], p["group_ids"])
+    A, T = out["adv"], out["T"]
+
+    def loss(hidden, W):
+        lp, _ = O.token_logprobs(hidden, W, p["tokens"])
+        lp = np.where(p["mask"] != 0, lp, 0.0)
+        return O.score_centering_surrogate(lp, p["mask"], p["cu"], A, T)
+
+    assert loss(p["hidden"], p["W"]) == out["loss"]
+    rng = _rng(131)
+    eps = 1e-6
+    for _ in range(6):
+        dh = rng.standard_normal(p["hidden"].shape)
+        dw = rng.standard_normal(p["W"].shape)
+        fd = (loss(p["hidden"] + eps * dh, p["W"] + eps * dw)
+              - loss(p["hidden"] - eps * dh, p["W"] - eps * dw)) / (2 * eps)
+        an = float((out["d_hidden"] * dh).sum() + (out["d_lm_head"] * dw).sum())
+        assert abs(fd - an) <= 1e-6 * abs(an) + 1e-10
+
+
+def test_score_centering_equals_is_at_unit_weights_and_vanishes_at_equal_rewards():
+    p = _small_problem(32)
+    logpi_all, _ = O.token_logprobs(p["hidden"], p["W"], p["tokens"])
+    at_pi = np.where(p["mask"] != 0, logpi_all, 0.0)
+    is_ = O.reinforce_zero_fwd_bwd(p["hidden"], p["W"], p["tokens"], at_pi,
+                                   p["mask"], p["cu"], p["rewards"], p["group_ids"])
+    sc = O.score_centering_fwd_bwd(p["hidden"], p["W"], p["tokens"], p["mask"],
+                                   p["cu"], p["rewards"], p["group_ids"])
+    for k in ("d_hidden", "d_lm_head"):
+        assert np.allclose(sc[k], is_[k], rtol=1e-13, atol=1e-16)
+    flat = O.score_centering_fwd_bwd(p["hidden"], p["W"], p["tokens"], p["mask"],
+                                     p["cu"], np.full(len(p["rewards"]), 0.7),
+                                     p["group_ids"])
+    assert flat["loss"] == 0.0
+    assert not flat["d_hidden"].any() and not flat["d_lm_head"].any()
+
+
 # ------------------------------------------------------- rollout-side sampler
 # Published known-answer vectors of Philox4x32-10 (Salmon, Moraes, Dror and
 # Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011; the
