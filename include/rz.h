@@ -32,10 +32,11 @@
  * Conventions shared by every entry point:
  *  - All array arguments are DEVICE pointers owned by the caller, row-major
  *    and contiguous.  The library never allocates, frees or synchronises: it
- *    enqueues work on `stream` (a hipStream_t; NULL = the null stream) and
+ *    enqueues work on `stream` (NULL = the null stream) and
  *    outputs are valid once the stream reaches that point.
  *  - Scratch memory is a caller-provided device workspace of at least
- *    rz_workspace_bytes(...) bytes, 256-byte aligned.  Its contents on entry
+ *    rz_workspace_bytes(...) or rz_workspace_bytes_op(...) bytes, 256-byte
+ *    aligned.  Its contents on entry
  *    do not matter and on return are unspecified.
  *  - hidden and lm_head are fp32 (RZ_DTYPE_F32) or bfloat16 (RZ_DTYPE_BF16);
  *    every other floating-point array is fp32.  Arithmetic accumulates in
@@ -47,7 +48,8 @@
  *    may be NULL; bits are OR-ed in, never cleared) and turn the affected
  *    outputs into NaN; the call still completes normally.
  *  - The library keeps no state between calls except the optional kernel
- *    timer (rz_timing_*), which is process-global and not thread-safe.
+ *    timer (rz_timing_*), which is kept per host thread: enabling it on one
+ *    thread times only that thread's calls.
  */
 #ifndef RZ_H_
 #define RZ_H_
@@ -58,6 +60,11 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* The HIP stream handle, declared as the HIP runtime declares it, so that
+ * this header needs no HIP header (repeating an identical typedef is legal
+ * in C11 and C++). */
+typedef struct ihipStream_t* hipStream_t;
 
 typedef enum {
   RZ_OK = 0,
@@ -77,7 +84,8 @@ typedef enum {
   RZ_OP_GRAD_NORMS = 4,
   RZ_OP_FWD_BWD_LORA = 5,
   RZ_OP_TOKEN_LOGPROBS_MX = 6,
-  RZ_OP_SAMPLE_MX = 7
+  RZ_OP_SAMPLE_MX = 7,
+  RZ_OP_SCORE_CENTERING = 8
 } rz_op;
 
 /* LoRA on the head: the largest rank, and the number of columns the
@@ -105,14 +113,23 @@ typedef enum {
 #define RZ_MAX_ROWS ((int64_t)1 << 30)
 #define RZ_MAX_VOCAB (1 << 24)
 #define RZ_MAX_HIDDEN 32768
+#define RZ_MAX_RESPONSES (1 << 24)
 
-/* Bytes of workspace an entry point needs for the given sizes; 0 when the
- * sizes are themselves invalid (the call would return an error anyway).
- * For RZ_OP_DIAGNOSTICS only n_rows is read; for RZ_OP_GRAD_NORMS, n_rows,
- * H and V (dt is ignored).  rz_response_diagnostics and rz_run_summary need
- * no workspace. */
-size_t rz_workspace_bytes(rz_op op, int64_t n_rows, int32_t n_resp, int32_t H,
+/* Bytes of workspace that rz_token_logprobs, rz_reinforce_zero_fwd_bwd and
+ * rz_diagnostics need at these sizes: the largest of the three, so one
+ * buffer serves all of them (n_resp is read by the learner step only; when
+ * it is invalid the learner step's need is left out).  0 when the sizes are
+ * invalid for all three. */
+size_t rz_workspace_bytes(int64_t n_rows, int32_t n_resp, int32_t H,
                           int32_t V, rz_dtype dt);
+
+/* Bytes of workspace one entry point needs (op names it); 0 when the sizes
+ * are themselves invalid (the call would return an error anyway).  For
+ * RZ_OP_DIAGNOSTICS only n_rows is read; for RZ_OP_GRAD_NORMS, n_rows, H and
+ * V (dt is ignored).  rz_response_diagnostics and rz_run_summary need no
+ * workspace. */
+size_t rz_workspace_bytes_op(rz_op op, int64_t n_rows, int32_t n_resp,
+                             int32_t H, int32_t V, rz_dtype dt);
 
 /* Static description of an error code. Never NULL. */
 const char* rz_status_string(rz_status s);
@@ -134,7 +151,7 @@ rz_status rz_token_logprobs(const void* hidden, const void* lm_head,
                             const int32_t* tokens, int64_t n_rows, int32_t H,
                             int32_t V, rz_dtype dt, float* logprobs,
                             float* lse, int32_t* err_flag, void* workspace,
-                            size_t workspace_bytes, void* stream);
+                            size_t workspace_bytes, hipStream_t stream);
 
 /*
  * rz_reinforce_zero_fwd_bwd -- one learner step of the hot path.
@@ -174,7 +191,39 @@ rz_status rz_reinforce_zero_fwd_bwd(
     const float* rewards, const int32_t* group_ids, int64_t n_rows,
     int32_t n_resp, int32_t H, int32_t V, rz_dtype dt, float* logprobs,
     float* loss, float* d_hidden, float* d_lm_head, float* diag, float* adv,
-    int32_t* err_flag, void* workspace, size_t workspace_bytes, void* stream);
+    int32_t* err_flag, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * rz_score_centering_fwd_bwd -- the score-centering (SC) update: the same
+ * learner step without importance weights.
+ *
+ * "REINFORCE Zero" project page, "The full IS correction", blocks 02-03:
+ * sampled under q, the plain update E_q[A s] is the covariance Cov_q(A, s)
+ * plus the drift E_q[A] E_q[s]; SC removes the drift and keeps
+ * g_SC = Cov_q(A, s) = E_q[(A - E_q A) s].  The group-mean advantage A_i is
+ * that centred factor, so the estimate is the unclipped IS loss's gradient
+ * with w replaced by 1 (vLLM blog, section 4 "Results", runs "Score
+ * Centering without IS" as a training arm).  This call computes
+ *     L_SC = -(1/B) sum_i (1/T_i) sum_{valid t in i} A_i log pi_t,
+ *     c_t  = A_i / (B T_i)   (minus dL_SC / d log pi_t),
+ * and dL_SC/dhidden, dL_SC/dW through log pi, on the kernels of
+ * rz_reinforce_zero_fwd_bwd (only c_t and the loss's per-token term
+ * differ).  Arguments and outputs as rz_reinforce_zero_fwd_bwd, except:
+ *   logmu  may be NULL (SC never reads it); then diag must be NULL.  With
+ *          logmu given, diag is {D3, KL} of the rollout records, as in
+ *          rz_reinforce_zero_fwd_bwd.
+ *   loss   L_SC above (its gradient is the SC update, negated).
+ * logprobs are bit-identical to rz_reinforce_zero_fwd_bwd's.  Workspace:
+ * rz_workspace_bytes(n_rows, n_resp, H, V, dt) (RZ_OP_SCORE_CENTERING).
+ */
+rz_status rz_score_centering_fwd_bwd(
+    const void* hidden, const void* lm_head, const int32_t* tokens,
+    const float* logmu, const uint8_t* mask, const int32_t* cu_rows,
+    const float* rewards, const int32_t* group_ids, int64_t n_rows,
+    int32_t n_resp, int32_t H, int32_t V, rz_dtype dt, float* logprobs,
+    float* loss, float* d_hidden, float* d_lm_head, float* diag, float* adv,
+    int32_t* err_flag, void* workspace, size_t workspace_bytes,
+    hipStream_t stream);
 
 /*
  * rz_sample_tokens -- the rollout side: draw each row's token and record
@@ -206,7 +255,7 @@ rz_status rz_sample_tokens(const void* hidden, const void* lm_head,
                            int32_t V, rz_dtype dt, uint64_t seed,
                            int32_t* tokens, float* logmu, float* lse,
                            void* workspace, size_t workspace_bytes,
-                           void* stream);
+                           hipStream_t stream);
 
 /*
  * rz_diagnostics -- D3 and the k1 rollout-to-learner KL.
@@ -221,7 +270,7 @@ rz_status rz_sample_tokens(const void* hidden, const void* lm_head,
 rz_status rz_diagnostics(const float* logpi, const float* logmu,
                          const uint8_t* mask, int64_t n, float* diag,
                          void* workspace, size_t workspace_bytes,
-                         void* stream);
+                         hipStream_t stream);
 
 /*
  * rz_dequantize_head -- an LM head stored at release precision, as MX
@@ -249,7 +298,7 @@ rz_status rz_diagnostics(const float* logpi, const float* logmu,
  */
 rz_status rz_dequantize_head(const uint8_t* codes, const uint8_t* scales,
                              int32_t V, int32_t H, rz_mx_format fmt,
-                             void* lm_head, int32_t* err_flag, void* stream);
+                             void* lm_head, int32_t* err_flag, hipStream_t stream);
 
 /*
  * rz_token_logprobs_mx, rz_sample_tokens_mx -- rz_token_logprobs and
@@ -264,7 +313,7 @@ rz_status rz_dequantize_head(const uint8_t* codes, const uint8_t* scales,
  * head's bytes per call, which is what bounds the rollout at decode size.
  * Otherwise the head is expanded into the workspace first.  Blocks with an
  * invalid scale give NaN and set RZ_DEVERR_MX_SCALE in err_flag (may be
- * NULL).  Workspace: rz_workspace_bytes(RZ_OP_TOKEN_LOGPROBS_MX or
+ * NULL).  Workspace: rz_workspace_bytes_op(RZ_OP_TOKEN_LOGPROBS_MX or
  * RZ_OP_SAMPLE_MX, n_rows, 1, H, V, RZ_DTYPE_BF16).
  */
 rz_status rz_token_logprobs_mx(const void* hidden, const uint8_t* codes,
@@ -272,14 +321,14 @@ rz_status rz_token_logprobs_mx(const void* hidden, const uint8_t* codes,
                                const int32_t* tokens, int64_t n_rows, int32_t H,
                                int32_t V, float* logprobs, float* lse,
                                int32_t* err_flag, void* workspace,
-                               size_t workspace_bytes, void* stream);
+                               size_t workspace_bytes, hipStream_t stream);
 rz_status rz_sample_tokens_mx(const void* hidden, const uint8_t* codes,
                               const uint8_t* scales, rz_mx_format fmt,
                               const uint64_t* row_ids, int64_t n_rows,
                               int32_t H, int32_t V, uint64_t seed,
                               int32_t* tokens, float* logmu, float* lse,
                               int32_t* err_flag, void* workspace,
-                              size_t workspace_bytes, void* stream);
+                              size_t workspace_bytes, hipStream_t stream);
 
 /*
  * LoRA adapter on the head ("Zero mismatch, simple async RL", vLLM blog,
@@ -308,10 +357,10 @@ rz_status rz_sample_tokens_mx(const void* hidden, const uint8_t* codes,
  */
 rz_status rz_lora_augment(const void* hidden, const void* lora_A, float scale,
                           int64_t n_rows, int32_t H, int32_t r, rz_dtype dt,
-                          void* hidden_aug, void* stream);
+                          void* hidden_aug, hipStream_t stream);
 rz_status rz_lora_merge_head(const void* lm_head, const void* lora_B,
                              int32_t V, int32_t H, int32_t r, rz_dtype dt,
-                             void* head_aug, void* stream);
+                             void* head_aug, hipStream_t stream);
 
 /*
  * rz_reinforce_zero_fwd_bwd_lora -- the learner step with a LoRA adapter on
@@ -327,8 +376,8 @@ rz_status rz_lora_merge_head(const void* lm_head, const void* lora_B,
  *
  * The rounding of u is treated as the identity in the backward pass.  W gets
  * no gradient and none is computed.  dL/dA sums fixed chunks of 4096 rows in
- * order.  Workspace: rz_workspace_bytes(RZ_OP_FWD_BWD_LORA, n_rows, n_resp,
- * H, V, dt) (independent of r).
+ * order.  Workspace: rz_workspace_bytes_op(RZ_OP_FWD_BWD_LORA, n_rows,
+ * n_resp, H, V, dt) (independent of r).
  */
 rz_status rz_reinforce_zero_fwd_bwd_lora(
     const void* hidden, const void* lm_head, const void* lora_A,
@@ -338,7 +387,7 @@ rz_status rz_reinforce_zero_fwd_bwd_lora(
     int32_t n_resp, int32_t H, int32_t V, rz_dtype dt, float* logprobs,
     float* loss, float* d_hidden, float* d_lora_A, float* d_lora_B,
     float* diag, float* adv, int32_t* err_flag, void* workspace,
-    size_t workspace_bytes, void* stream);
+    size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Run-level diagnostics ("Zero mismatch, simple async RL", vLLM blog,
@@ -358,11 +407,11 @@ rz_status rz_reinforce_zero_fwd_bwd_lora(
  * Sums of squares are taken in float64 over fixed chunks of 65536 values
  * and then over the chunks in a fixed tree, so the result is a pure
  * function of the inputs and their sizes.  Workspace:
- * rz_workspace_bytes(RZ_OP_GRAD_NORMS, n_rows, 0, H, V, 0).
+ * rz_workspace_bytes_op(RZ_OP_GRAD_NORMS, n_rows, 0, H, V, 0).
  */
 rz_status rz_grad_norms(const float* d_hidden, int64_t n_rows, int32_t H,
                         const float* d_lm_head, int32_t V, float* norms,
-                        void* workspace, size_t workspace_bytes, void* stream);
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * rz_response_diagnostics -- D3 and KL of each response (rz_diagnostics
@@ -383,7 +432,7 @@ rz_status rz_grad_norms(const float* d_hidden, int64_t n_rows, int32_t H,
 rz_status rz_response_diagnostics(const float* logpi, const float* logmu,
                                   const uint8_t* mask, const int32_t* cu_rows,
                                   int64_t n_rows, int32_t n_resp, float* d3,
-                                  float* kl, int32_t* err_flag, void* stream);
+                                  float* kl, int32_t* err_flag, hipStream_t stream);
 
 /*
  * rz_run_summary -- the run-level view over per-step records (host memory,
@@ -413,7 +462,7 @@ rz_status rz_run_summary(const float* d3, const float* kl,
  * time to its kernel's total, and copies totals (milliseconds) and launch
  * counts for kernels 0 .. rz_timing_num_kernels()-1; reset != 0 clears them.
  * Enabling creates the events (host-side driver objects, no device memory);
- * disabling destroys them.  Not thread-safe.
+ * disabling destroys them.  The timer's state is per host thread.
  */
 rz_status rz_timing_enable(int on);
 int rz_timing_num_kernels(void);

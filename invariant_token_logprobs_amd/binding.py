@@ -22,6 +22,7 @@ RZ_OP_GRAD_NORMS = 4
 RZ_OP_FWD_BWD_LORA = 5
 RZ_OP_TOKEN_LOGPROBS_MX = 6
 RZ_OP_SAMPLE_MX = 7
+RZ_OP_SCORE_CENTERING = 8
 RZ_LORA_COLS = 64
 
 RZ_DEVERR_TOKEN = 1
@@ -35,8 +36,9 @@ _STATUS = {0: "RZ_OK", -1: "RZ_ERR_INVALID_ARG", -2: "RZ_ERR_UNSUPPORTED",
            -3: "RZ_ERR_WORKSPACE", -4: "RZ_ERR_HIP"}
 
 EXPORTS = [
-    "rz_workspace_bytes", "rz_status_string", "rz_token_logprobs",
-    "rz_reinforce_zero_fwd_bwd", "rz_diagnostics", "rz_sample_tokens",
+    "rz_workspace_bytes", "rz_workspace_bytes_op", "rz_status_string",
+    "rz_token_logprobs", "rz_reinforce_zero_fwd_bwd", "rz_diagnostics",
+    "rz_score_centering_fwd_bwd", "rz_sample_tokens",
     "rz_grad_norms", "rz_response_diagnostics", "rz_run_summary",
     "rz_dequantize_head", "rz_lora_augment", "rz_lora_merge_head",
     "rz_reinforce_zero_fwd_bwd_lora", "rz_token_logprobs_mx",
@@ -70,8 +72,10 @@ def load_library():
                       "`python -m invariant_token_logprobs_amd.build`")
     lib = ctypes.CDLL(path)
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
-    lib.rz_workspace_bytes.argtypes = [ctypes.c_int, i64, i32, i32, i32, ctypes.c_int]
+    lib.rz_workspace_bytes.argtypes = [i64, i32, i32, i32, ctypes.c_int]
     lib.rz_workspace_bytes.restype = sz
+    lib.rz_workspace_bytes_op.argtypes = [ctypes.c_int, i64, i32, i32, i32, ctypes.c_int]
+    lib.rz_workspace_bytes_op.restype = sz
     lib.rz_status_string.argtypes = [ctypes.c_int]
     lib.rz_status_string.restype = ctypes.c_char_p
     lib.rz_token_logprobs.argtypes = [vp, vp, vp, i64, i32, i32, ctypes.c_int,
@@ -81,6 +85,8 @@ def load_library():
         vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, ctypes.c_int,
         vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.rz_reinforce_zero_fwd_bwd.restype = ctypes.c_int
+    lib.rz_score_centering_fwd_bwd.argtypes = lib.rz_reinforce_zero_fwd_bwd.argtypes
+    lib.rz_score_centering_fwd_bwd.restype = ctypes.c_int
     lib.rz_diagnostics.argtypes = [vp, vp, vp, i64, vp, vp, sz, vp]
     lib.rz_diagnostics.restype = ctypes.c_int
     lib.rz_sample_tokens.argtypes = [vp, vp, vp, i64, i32, i32, ctypes.c_int,
@@ -166,41 +172,64 @@ def _need(t, name, dtype, ndim=None, device=None):
         raise RzError(f"{name} is on {t.device}, expected {device}")
 
 
-def _stream(stream):
+def _stream_obj(stream):
     torch = _torch()
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return ctypes.c_void_p(s.cuda_stream)
+    return stream if stream is not None else torch.cuda.current_stream()
+
+
+def _stream(stream):
+    return ctypes.c_void_p(_stream_obj(stream).cuda_stream)
 
 
 class Workspace:
-    """A grow-only device byte buffer reused across calls on one device."""
+    """A grow-only device byte buffer reused across calls.
+
+    Calls that share one Workspace must not overlap (they would race on its
+    contents): use one per stream.  A larger buffer is allocated on the
+    stream of the call that needs it, so the caching allocator hands the old
+    one out again only in that stream's order."""
 
     def __init__(self, device=None):
         self.device = device
         self.buf = None
 
-    def get(self, nbytes: int, device):
+    def get(self, nbytes: int, device, stream=None):
         torch = _torch()
         if nbytes == 0:
             return None
         if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
+            s = _stream_obj(stream)
+            if self.buf is not None:
+                self.buf.record_stream(s)
             self.buf = None
-            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+            with torch.cuda.stream(s):
+                self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
         return self.buf
 
 
 _default_ws = {}
 
 
-def _workspace(ws: Optional[Workspace], nbytes: int, device):
+def _workspace(ws: Optional[Workspace], nbytes: int, device, stream=None):
+    """The caller's workspace, else the default one of (device, stream)."""
     if ws is None:
-        ws = _default_ws.setdefault(str(device), Workspace())
-    return ws.get(nbytes, device)
+        key = (str(device), int(_stream_obj(stream).cuda_stream))
+        ws = _default_ws.setdefault(key, Workspace())
+    return ws.get(nbytes, device, stream)
 
 
 def workspace_bytes(op: int, n_rows: int, n_resp: int, H: int, V: int,
                     dtype_code: int) -> int:
-    return int(load_library().rz_workspace_bytes(op, n_rows, n_resp, H, V,
+    """Workspace bytes of one entry point (rz_workspace_bytes_op)."""
+    return int(load_library().rz_workspace_bytes_op(op, n_rows, n_resp, H, V,
+                                                    dtype_code))
+
+
+def workspace_bytes_common(n_rows: int, n_resp: int, H: int, V: int,
+                           dtype_code: int) -> int:
+    """Workspace bytes that serve rz_token_logprobs, the learner step and
+    rz_diagnostics at these sizes (rz_workspace_bytes)."""
+    return int(load_library().rz_workspace_bytes(n_rows, n_resp, H, V,
                                                  dtype_code))
 
 
@@ -223,7 +252,7 @@ def token_logprobs(hidden, lm_head, tokens, *, want_lse: bool = False,
     logprobs = out if out is not None else torch.empty(N, dtype=torch.float32, device=dev)
     lse = torch.empty(N, dtype=torch.float32, device=dev) if want_lse else None
     nbytes = workspace_bytes(RZ_OP_TOKEN_LOGPROBS, N, 1, H, V, dt)
-    ws = _workspace(workspace, nbytes, dev)
+    ws = _workspace(workspace, nbytes, dev, stream)
     _check(lib.rz_token_logprobs(_ptr(hidden), _ptr(lm_head), _ptr(tokens), N, H,
                                  V, dt, _ptr(logprobs), _ptr(lse), _ptr(err_flag),
                                  _ptr(ws), nbytes, _stream(stream)),
@@ -255,7 +284,7 @@ def sample_tokens(hidden, lm_head, row_ids, seed: int, *, want_lse: bool = False
     logmu = torch.empty(N, dtype=torch.float32, device=dev)
     lse = torch.empty(N, dtype=torch.float32, device=dev) if want_lse else None
     nbytes = workspace_bytes(RZ_OP_SAMPLE, N, 1, H, V, dt)
-    ws = _workspace(workspace, nbytes, dev)
+    ws = _workspace(workspace, nbytes, dev, stream)
     _check(lib.rz_sample_tokens(_ptr(hidden), _ptr(lm_head), _ptr(row_ids), N, H,
                                 V, dt, ctypes.c_uint64(int(seed)), _ptr(tokens),
                                 _ptr(logmu), _ptr(lse), _ptr(ws), nbytes,
@@ -264,12 +293,8 @@ def sample_tokens(hidden, lm_head, row_ids, seed: int, *, want_lse: bool = False
     return (tokens, logmu, lse) if want_lse else (tokens, logmu)
 
 
-def reinforce_zero_fwd_bwd(hidden, lm_head, tokens, logmu, mask, cu_rows,
-                           rewards, group_ids, *, err_flag=None,
-                           workspace: Optional[Workspace] = None, stream=None,
-                           outputs: Optional[dict] = None):
-    """One learner step (rz_reinforce_zero_fwd_bwd).  Returns a dict with
-    logprobs, loss, d_hidden, d_lm_head, diag (D3, KL) and adv."""
+def _learner_step(fn, op, what, hidden, lm_head, tokens, logmu, mask, cu_rows,
+                  rewards, group_ids, err_flag, workspace, stream, outputs):
     torch = _torch()
     lib = load_library()
     dt = _dtype_code(hidden)
@@ -277,7 +302,8 @@ def reinforce_zero_fwd_bwd(hidden, lm_head, tokens, logmu, mask, cu_rows,
     dev = hidden.device
     _need(lm_head, "lm_head", hidden.dtype, 2, dev)
     _need(tokens, "tokens", torch.int32, 1, dev)
-    _need(logmu, "logmu", torch.float32, 1, dev)
+    if logmu is not None:
+        _need(logmu, "logmu", torch.float32, 1, dev)
     _need(mask, "mask", torch.uint8, 1, dev)
     _need(cu_rows, "cu_rows", torch.int32, 1, dev)
     _need(rewards, "rewards", torch.float32, 1, dev)
@@ -285,10 +311,11 @@ def reinforce_zero_fwd_bwd(hidden, lm_head, tokens, logmu, mask, cu_rows,
     N, H = hidden.shape
     V = lm_head.shape[0]
     B = rewards.shape[0]
-    if (lm_head.shape[1] != H or tokens.shape[0] != N or logmu.shape[0] != N
+    if (lm_head.shape[1] != H or tokens.shape[0] != N
+            or (logmu is not None and logmu.shape[0] != N)
             or mask.shape[0] != N or cu_rows.shape[0] != B + 1
             or group_ids.shape[0] != B):
-        raise RzError("shape mismatch between the fwd_bwd arguments")
+        raise RzError(f"shape mismatch between the {what} arguments")
     o = outputs if outputs is not None else {}
     f32 = torch.float32
     if "logprobs" not in o:
@@ -296,17 +323,44 @@ def reinforce_zero_fwd_bwd(hidden, lm_head, tokens, logmu, mask, cu_rows,
         o["loss"] = torch.empty(1, dtype=f32, device=dev)
         o["d_hidden"] = torch.empty((N, H), dtype=f32, device=dev)
         o["d_lm_head"] = torch.empty((V, H), dtype=f32, device=dev)
-        o["diag"] = torch.empty(2, dtype=f32, device=dev)
+        o["diag"] = torch.empty(2, dtype=f32, device=dev) if logmu is not None else None
         o["adv"] = torch.empty(B, dtype=f32, device=dev)
-    nbytes = workspace_bytes(RZ_OP_FWD_BWD, N, B, H, V, dt)
-    ws = _workspace(workspace, nbytes, dev)
-    _check(lib.rz_reinforce_zero_fwd_bwd(
+    nbytes = workspace_bytes(op, N, B, H, V, dt)
+    ws = _workspace(workspace, nbytes, dev, stream)
+    _check(fn(
         _ptr(hidden), _ptr(lm_head), _ptr(tokens), _ptr(logmu), _ptr(mask),
         _ptr(cu_rows), _ptr(rewards), _ptr(group_ids), N, B, H, V, dt,
         _ptr(o["logprobs"]), _ptr(o["loss"]), _ptr(o["d_hidden"]),
         _ptr(o["d_lm_head"]), _ptr(o["diag"]), _ptr(o["adv"]), _ptr(err_flag),
-        _ptr(ws), nbytes, _stream(stream)), "rz_reinforce_zero_fwd_bwd")
+        _ptr(ws), nbytes, _stream(stream)), what)
     return o
+
+
+def reinforce_zero_fwd_bwd(hidden, lm_head, tokens, logmu, mask, cu_rows,
+                           rewards, group_ids, *, err_flag=None,
+                           workspace: Optional[Workspace] = None, stream=None,
+                           outputs: Optional[dict] = None):
+    """One learner step (rz_reinforce_zero_fwd_bwd).  Returns a dict with
+    logprobs, loss, d_hidden, d_lm_head, diag (D3, KL) and adv."""
+    if logmu is None:
+        raise RzError("logmu is required")
+    return _learner_step(load_library().rz_reinforce_zero_fwd_bwd, RZ_OP_FWD_BWD,
+                         "rz_reinforce_zero_fwd_bwd", hidden, lm_head, tokens,
+                         logmu, mask, cu_rows, rewards, group_ids, err_flag,
+                         workspace, stream, outputs)
+
+
+def score_centering_fwd_bwd(hidden, lm_head, tokens, mask, cu_rows, rewards,
+                            group_ids, *, logmu=None, err_flag=None,
+                            workspace: Optional[Workspace] = None, stream=None,
+                            outputs: Optional[dict] = None):
+    """The score-centering step (rz_score_centering_fwd_bwd): the learner step
+    with w = 1.  Returns logprobs, loss (the SC surrogate), d_hidden,
+    d_lm_head, adv, and diag (D3, KL of the records) when logmu is given."""
+    return _learner_step(load_library().rz_score_centering_fwd_bwd,
+                         RZ_OP_SCORE_CENTERING, "rz_score_centering_fwd_bwd",
+                         hidden, lm_head, tokens, logmu, mask, cu_rows, rewards,
+                         group_ids, err_flag, workspace, stream, outputs)
 
 
 def diagnostics(logpi, logmu, mask=None, *, workspace: Optional[Workspace] = None,
@@ -324,7 +378,7 @@ def diagnostics(logpi, logmu, mask=None, *, workspace: Optional[Workspace] = Non
         raise RzError("shape mismatch between logpi, logmu and mask")
     diag = out if out is not None else torch.empty(2, dtype=torch.float32, device=dev)
     nbytes = workspace_bytes(RZ_OP_DIAGNOSTICS, n, 1, 64, 1, 0)
-    ws = _workspace(workspace, nbytes, dev)
+    ws = _workspace(workspace, nbytes, dev, stream)
     _check(lib.rz_diagnostics(_ptr(logpi), _ptr(logmu), _ptr(mask), n, _ptr(diag),
                               _ptr(ws), nbytes, _stream(stream)), "rz_diagnostics")
     return diag
@@ -413,7 +467,7 @@ def reinforce_zero_fwd_bwd_lora(hidden, lm_head, lora_A, lora_B, scale: float,
          "diag": torch.empty(2, dtype=f32, device=dev),
          "adv": torch.empty(B, dtype=f32, device=dev)}
     nbytes = workspace_bytes(RZ_OP_FWD_BWD_LORA, N, B, H, V, dt)
-    ws = _workspace(workspace, nbytes, dev)
+    ws = _workspace(workspace, nbytes, dev, stream)
     _check(lib.rz_reinforce_zero_fwd_bwd_lora(
         _ptr(hidden), _ptr(lm_head), _ptr(lora_A), _ptr(lora_B), float(scale), r,
         _ptr(tokens), _ptr(logmu), _ptr(mask), _ptr(cu_rows), _ptr(rewards),
@@ -478,7 +532,7 @@ def token_logprobs_mx(hidden, codes, scales, fmt: str, tokens, *,
     logprobs = torch.empty(N, dtype=torch.float32, device=dev)
     lse = torch.empty(N, dtype=torch.float32, device=dev) if want_lse else None
     nbytes = workspace_bytes(RZ_OP_TOKEN_LOGPROBS_MX, N, 1, H, V, RZ_DTYPE_BF16)
-    ws = _workspace(workspace, nbytes, dev)
+    ws = _workspace(workspace, nbytes, dev, stream)
     _check(lib.rz_token_logprobs_mx(_ptr(hidden), _ptr(codes), _ptr(scales),
                                     RZ_MX_FORMATS[fmt], _ptr(tokens), N, H, V,
                                     _ptr(logprobs), _ptr(lse), _ptr(err_flag),
@@ -506,7 +560,7 @@ def sample_tokens_mx(hidden, codes, scales, fmt: str, row_ids, seed: int, *,
     logmu = torch.empty(N, dtype=torch.float32, device=dev)
     lse = torch.empty(N, dtype=torch.float32, device=dev) if want_lse else None
     nbytes = workspace_bytes(RZ_OP_SAMPLE_MX, N, 1, H, V, RZ_DTYPE_BF16)
-    ws = _workspace(workspace, nbytes, dev)
+    ws = _workspace(workspace, nbytes, dev, stream)
     _check(lib.rz_sample_tokens_mx(_ptr(hidden), _ptr(codes), _ptr(scales),
                                    RZ_MX_FORMATS[fmt], _ptr(row_ids), N, H, V,
                                    ctypes.c_uint64(int(seed)), _ptr(tokens),
@@ -532,7 +586,7 @@ def grad_norms(d_hidden, d_lm_head, *, workspace: Optional[Workspace] = None,
         raise RzError("d_hidden and d_lm_head disagree on H")
     norms = out if out is not None else torch.empty(2, dtype=torch.float32, device=dev)
     nbytes = workspace_bytes(RZ_OP_GRAD_NORMS, N, 0, H, V, 0)
-    ws = _workspace(workspace, nbytes, dev)
+    ws = _workspace(workspace, nbytes, dev, stream)
     _check(lib.rz_grad_norms(_ptr(d_hidden), N, H, _ptr(d_lm_head), V,
                              _ptr(norms), _ptr(ws), nbytes, _stream(stream)),
            "rz_grad_norms")

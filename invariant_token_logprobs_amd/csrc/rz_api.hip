@@ -120,10 +120,9 @@ struct FbWs {
   void* hT;
   void* dz;
   void* dzT;
-  int* counts;
-  int* cursor;
-  int* offsets;
-  int* sorted;
+  int* bad_gid;
+  int* sort_ws;
+  float* fix_cont;
   float* dwpart;
 };
 // H: the GEMM width (hidden and head row length); dw_cols: the columns of
@@ -161,10 +160,10 @@ size_t carve_fb(Carver& c, int64_t n, int32_t B, int32_t H, int32_t V,
   // dz^T only for fp32 (bf16 dW reads dz through transposing LDS reads)
   t.dzT = dt == RZ_DTYPE_F32 ? c.take<char>(es * (size_t)Vpad * (size_t)C)
                              : nullptr;
-  t.counts = c.take<int>(sizeof(int) * (size_t)V);
-  t.cursor = c.take<int>(sizeof(int) * (size_t)V);
-  t.offsets = c.take<int>(sizeof(int) * ((size_t)V + 1));
-  t.sorted = c.take<int>(sizeof(int) * (size_t)n);
+  t.bad_gid = c.take<int>(sizeof(int));
+  // one sort buffer serves the group ids (B keys) and then the tokens (n)
+  t.sort_ws = c.take<int>(sizeof(int) * sort_ws_ints(std::max<int64_t>(n, B)));
+  t.fix_cont = c.take<float>(sizeof(float) * (size_t)dw_fix_cont_floats(n, dw_cols));
   t.dwpart = c.take<float>(sizeof(float) * (size_t)dw_part_floats(V, dw_cols));
   if (w) *w = t;
   return c.off;
@@ -231,7 +230,7 @@ struct TimerState {
   int64_t count[K_NUM_KERNELS] = {};
   hipEvent_t cur_a = nullptr;
 };
-TimerState g_timer;
+thread_local TimerState g_timer;
 
 hipEvent_t take_event() {
   if (!g_timer.pool.empty()) {
@@ -281,8 +280,8 @@ const char* rz_status_string(rz_status s) {
   return "unknown status";
 }
 
-size_t rz_workspace_bytes(rz_op op, int64_t n_rows, int32_t n_resp, int32_t H,
-                          int32_t V, rz_dtype dt) {
+size_t rz_workspace_bytes_op(rz_op op, int64_t n_rows, int32_t n_resp,
+                             int32_t H, int32_t V, rz_dtype dt) {
   if (n_rows < 0 || n_rows > RZ_MAX_ROWS) return 0;
   Carver c{nullptr};
   switch (op) {
@@ -290,7 +289,8 @@ size_t rz_workspace_bytes(rz_op op, int64_t n_rows, int32_t n_resp, int32_t H,
       if (!dims_ok(H, V, dt)) return 0;
       return n_rows == 0 ? 0 : carve_tlp(c, n_rows, V, nullptr);
     case RZ_OP_FWD_BWD:
-      if (!dims_ok(H, V, dt) || n_resp < 1) return 0;
+    case RZ_OP_SCORE_CENTERING:
+      if (!dims_ok(H, V, dt) || n_resp < 1 || n_resp > RZ_MAX_RESPONSES) return 0;
       return carve_fb(c, n_rows, n_resp, H, V, dt, nullptr, -1);
     case RZ_OP_DIAGNOSTICS:
       return align_up(diag_partials_bytes(n_rows));
@@ -305,7 +305,9 @@ size_t rz_workspace_bytes(rz_op op, int64_t n_rows, int32_t n_resp, int32_t H,
              (mx_fused(n_rows, H, smp) ? 0 : align_up(2 * (size_t)V * (size_t)H));
     }
     case RZ_OP_FWD_BWD_LORA:
-      if (!dims_ok(H, V, dt) || n_resp < 1 || H + kLoraCols > RZ_MAX_HIDDEN) return 0;
+      if (!dims_ok(H, V, dt) || n_resp < 1 || n_resp > RZ_MAX_RESPONSES ||
+          H + kLoraCols > RZ_MAX_HIDDEN)
+        return 0;
       return carve_lora(c, n_rows, n_resp, H, V, dt, nullptr);
     case RZ_OP_GRAD_NORMS:
       if (H <= 0 || H > RZ_MAX_HIDDEN || V <= 0 || V > RZ_MAX_VOCAB) return 0;
@@ -314,10 +316,18 @@ size_t rz_workspace_bytes(rz_op op, int64_t n_rows, int32_t n_resp, int32_t H,
   return 0;
 }
 
+size_t rz_workspace_bytes(int64_t n_rows, int32_t n_resp, int32_t H, int32_t V,
+                          rz_dtype dt) {
+  const size_t a = rz_workspace_bytes_op(RZ_OP_TOKEN_LOGPROBS, n_rows, 1, H, V, dt);
+  const size_t b = rz_workspace_bytes_op(RZ_OP_FWD_BWD, n_rows, n_resp, H, V, dt);
+  const size_t d = rz_workspace_bytes_op(RZ_OP_DIAGNOSTICS, n_rows, 1, H, V, dt);
+  return std::max(a, std::max(b, d));
+}
+
 rz_status rz_grad_norms(const float* d_hidden, int64_t n_rows, int32_t H,
                         const float* d_lm_head, int32_t V, float* norms,
                         void* workspace, size_t workspace_bytes,
-                        void* stream) {
+                        hipStream_t stream) {
   if (n_rows < 0 || n_rows > RZ_MAX_ROWS) return RZ_ERR_INVALID_ARG;
   if (H <= 0 || H > RZ_MAX_HIDDEN || V <= 0 || V > RZ_MAX_VOCAB)
     return RZ_ERR_INVALID_ARG;
@@ -343,7 +353,7 @@ rz_status rz_grad_norms(const float* d_hidden, int64_t n_rows, int32_t H,
 
 rz_status rz_dequantize_head(const uint8_t* codes, const uint8_t* scales,
                              int32_t V, int32_t H, rz_mx_format fmt,
-                             void* lm_head, int32_t* err_flag, void* stream) {
+                             void* lm_head, int32_t* err_flag, hipStream_t stream) {
   if (fmt != RZ_MX_FP4 && fmt != RZ_MX_FP8) return RZ_ERR_UNSUPPORTED;
   if (V <= 0 || V > RZ_MAX_VOCAB || H <= 0 || H > RZ_MAX_HIDDEN || H % 32)
     return RZ_ERR_INVALID_ARG;
@@ -359,9 +369,9 @@ rz_status rz_dequantize_head(const uint8_t* codes, const uint8_t* scales,
 rz_status rz_response_diagnostics(const float* logpi, const float* logmu,
                                   const uint8_t* mask, const int32_t* cu_rows,
                                   int64_t n_rows, int32_t n_resp, float* d3,
-                                  float* kl, int32_t* err_flag, void* stream) {
+                                  float* kl, int32_t* err_flag, hipStream_t stream) {
   if (n_rows < 0 || n_rows > RZ_MAX_ROWS) return RZ_ERR_INVALID_ARG;
-  if (n_resp < 0 || n_resp > (1 << 24)) return RZ_ERR_INVALID_ARG;
+  if (n_resp < 0 || n_resp > RZ_MAX_RESPONSES) return RZ_ERR_INVALID_ARG;
   if (n_resp == 0) return RZ_OK;
   if (!cu_rows || !d3 || !kl || (n_rows > 0 && (!logpi || !logmu)))
     return RZ_ERR_INVALID_ARG;
@@ -375,7 +385,7 @@ rz_status rz_sample_tokens(const void* hidden, const void* lm_head,
                            int32_t V, rz_dtype dt, uint64_t seed,
                            int32_t* tokens, float* logmu, float* lse,
                            void* workspace, size_t workspace_bytes,
-                           void* stream) {
+                           hipStream_t stream) {
   if (n_rows < 0 || n_rows > RZ_MAX_ROWS) return RZ_ERR_INVALID_ARG;
   if (dt != RZ_DTYPE_F32 && dt != RZ_DTYPE_BF16) return RZ_ERR_UNSUPPORTED;
   if (H <= 0 || V <= 0) return RZ_ERR_INVALID_ARG;
@@ -411,7 +421,7 @@ rz_status rz_token_logprobs(const void* hidden, const void* lm_head,
                             const int32_t* tokens, int64_t n_rows, int32_t H,
                             int32_t V, rz_dtype dt, float* logprobs,
                             float* lse, int32_t* err_flag, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+                            size_t workspace_bytes, hipStream_t stream) {
   if (n_rows < 0 || n_rows > RZ_MAX_ROWS) return RZ_ERR_INVALID_ARG;
   if (dt != RZ_DTYPE_F32 && dt != RZ_DTYPE_BF16) return RZ_ERR_UNSUPPORTED;
   if (H <= 0 || V <= 0) return RZ_ERR_INVALID_ARG;
@@ -441,7 +451,7 @@ rz_status rz_token_logprobs(const void* hidden, const void* lm_head,
 rz_status rz_diagnostics(const float* logpi, const float* logmu,
                          const uint8_t* mask, int64_t n, float* diag,
                          void* workspace, size_t workspace_bytes,
-                         void* stream) {
+                         hipStream_t stream) {
   if (n < 0 || n > RZ_MAX_ROWS) return RZ_ERR_INVALID_ARG;
   if (!diag) return RZ_ERR_INVALID_ARG;
   if (n > 0 && (!logpi || !logmu)) return RZ_ERR_INVALID_ARG;
@@ -463,9 +473,9 @@ static rz_status fwd_bwd_core(
     const float* logmu, const uint8_t* mask, const int32_t* cu_rows,
     const float* rewards, const int32_t* group_ids, int64_t n_rows,
     int32_t n_resp, int32_t H, int32_t V, rz_dtype dt, int32_t dw_col0,
-    int32_t dw_cols, float* logprobs, float* loss, float* d_hidden,
+    int32_t dw_cols, int sc, float* logprobs, float* loss, float* d_hidden,
     float* d_lm_head, float* diag, float* adv, int32_t* err_flag,
-    void* workspace, void* stream) {
+    void* workspace, hipStream_t stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   Carver c{reinterpret_cast<char*>(workspace)};
   FbWs w;
@@ -484,7 +494,7 @@ static rz_status fwd_bwd_core(
   // a5 (inputs only): T_i, group means, A_i and the factors A_i / (B T_i)
   RZ_TRY(launch_advantages(mask, N, cu_rows, rewards, group_ids, n_resp,
                            w.bad_cu, w.T, w.gcnt, w.gsum, w.Ad, w.fcoef, adv,
-                           err_flag, s));
+                           w.bad_gid, w.sort_ws, err_flag, s));
   RZ_TRY(launch_transpose(dt, K_TRANSPOSE_W, lm_head, H, nullptr,
                           DevRows{nullptr, 0, V}, Vpad, H, w.WT, Vpad, s));
   // a1-a4, a7-a9 in chunks of C valid rows (the count lives on the device;
@@ -502,7 +512,7 @@ static rz_status fwd_bwd_core(
       RZ_TRY(launch_lse_merge(w.partials, N, nt, crow, w.ztgt, w.tokv, V,
                               w.lse_v, w.logpi_v, w.idx, logprobs, err_flag,
                               s));
-      RZ_TRY(launch_coef(crow, w.logpi_v, logmu, w.idx, w.respv, w.fcoef,
+      RZ_TRY(launch_coef(crow, w.logpi_v, logmu, w.idx, w.respv, w.fcoef, sc,
                          w.coef, s));
       RZ_TRY(launch_dz_scale(dt, w.dz, Vpad, w.dzT, C, crow, w.partials, N,
                              w.lse_v, w.coef, Vpad, s));
@@ -519,16 +529,41 @@ static rz_status fwd_bwd_core(
   }
   if (N > 0) RZ_TRY(launch_rows_finalize(mask, N, H, logprobs, d_hidden, s));
   // a5: S_i from this call's logprobs, then L
-  RZ_TRY(launch_loss_value(mask, logprobs, logmu, N, cu_rows, n_resp, w.T,
+  RZ_TRY(launch_loss_value(mask, logprobs, logmu, N, cu_rows, n_resp, sc, w.T,
                            w.Ad, w.S, loss, s));
-  // a6: diagnostics over this call's outputs (same kernels as rz_diagnostics)
-  RZ_TRY(launch_diagnostics(logprobs, logmu, mask, N, w.diag_part,
-                            diag ? diag : w.diag_tmp, s));
+  // a6: diagnostics over this call's outputs (same kernels as rz_diagnostics;
+  // score centering without recorded log mu has none)
+  if (logmu || N == 0)
+    RZ_TRY(launch_diagnostics(logprobs, logmu, mask, N, w.diag_part,
+                              diag ? diag : w.diag_tmp, s));
   // a9: exact one-hot part of dW
   RZ_TRY(launch_dw_fix(dt, w.nvalid, N, w.tokv, w.idx, w.coef,
                        (const char*)hidden + (size_t)dw_col0 * es, H, dw_cols,
-                       V, w.counts, w.cursor, w.offsets, w.sorted, d_lm_head,
-                       s));
+                       V, w.sort_ws, w.fix_cont, d_lm_head, s));
+  return RZ_OK;
+}
+
+// Host-side checks shared by the learner entry points (logmu required
+// unless need_logmu is false).
+static rz_status fb_args_ok(const void* hidden, const void* lm_head,
+                            const int32_t* tokens, const float* logmu,
+                            bool need_logmu, const uint8_t* mask,
+                            const int32_t* cu_rows, const float* rewards,
+                            const int32_t* group_ids, int64_t n_rows,
+                            int32_t n_resp, int32_t H, int32_t V, rz_dtype dt,
+                            const float* logprobs, const float* loss,
+                            const float* d_hidden, const float* d_lm_head) {
+  if (n_rows < 0 || n_rows > RZ_MAX_ROWS) return RZ_ERR_INVALID_ARG;
+  if (n_resp < 1 || n_resp > RZ_MAX_RESPONSES) return RZ_ERR_INVALID_ARG;
+  if (dt != RZ_DTYPE_F32 && dt != RZ_DTYPE_BF16) return RZ_ERR_UNSUPPORTED;
+  if (H <= 0 || V <= 0) return RZ_ERR_INVALID_ARG;
+  if (!dims_ok(H, V, dt)) return RZ_ERR_UNSUPPORTED;
+  if (!lm_head || !cu_rows || !rewards || !group_ids || !loss || !d_lm_head)
+    return RZ_ERR_INVALID_ARG;
+  if (n_rows > 0 && (!hidden || !tokens || (need_logmu && !logmu) || !mask ||
+                     !logprobs || !d_hidden))
+    return RZ_ERR_INVALID_ARG;
+  if (misaligned(hidden, lm_head, d_hidden, d_lm_head)) return RZ_ERR_INVALID_ARG;
   return RZ_OK;
 }
 
@@ -538,25 +573,42 @@ rz_status rz_reinforce_zero_fwd_bwd(
     const float* rewards, const int32_t* group_ids, int64_t n_rows,
     int32_t n_resp, int32_t H, int32_t V, rz_dtype dt, float* logprobs,
     float* loss, float* d_hidden, float* d_lm_head, float* diag, float* adv,
-    int32_t* err_flag, void* workspace, size_t workspace_bytes, void* stream) {
-  if (n_rows < 0 || n_rows > RZ_MAX_ROWS) return RZ_ERR_INVALID_ARG;
-  if (n_resp < 1 || n_resp > (1 << 24)) return RZ_ERR_INVALID_ARG;
-  if (dt != RZ_DTYPE_F32 && dt != RZ_DTYPE_BF16) return RZ_ERR_UNSUPPORTED;
-  if (H <= 0 || V <= 0) return RZ_ERR_INVALID_ARG;
-  if (!dims_ok(H, V, dt)) return RZ_ERR_UNSUPPORTED;
-  if (!lm_head || !cu_rows || !rewards || !group_ids || !loss || !d_lm_head)
-    return RZ_ERR_INVALID_ARG;
-  if (n_rows > 0 && (!hidden || !tokens || !logmu || !mask || !logprobs ||
-                     !d_hidden))
-    return RZ_ERR_INVALID_ARG;
-  if (misaligned(hidden, lm_head, d_hidden, d_lm_head)) return RZ_ERR_INVALID_ARG;
+    int32_t* err_flag, void* workspace, size_t workspace_bytes,
+    hipStream_t stream) {
+  rz_status st = fb_args_ok(hidden, lm_head, tokens, logmu, true, mask, cu_rows,
+                            rewards, group_ids, n_rows, n_resp, H, V, dt,
+                            logprobs, loss, d_hidden, d_lm_head);
+  if (st != RZ_OK) return st;
   Carver meas{nullptr};
   const size_t need = carve_fb(meas, n_rows, n_resp, H, V, dt, nullptr, -1);
-  rz_status st = ws_check(workspace, workspace_bytes, need);
+  st = ws_check(workspace, workspace_bytes, need);
   if (st != RZ_OK) return st;
 
   return fwd_bwd_core(hidden, lm_head, tokens, logmu, mask, cu_rows, rewards,
-                      group_ids, n_rows, n_resp, H, V, dt, 0, H, logprobs,
+                      group_ids, n_rows, n_resp, H, V, dt, 0, H, 0, logprobs,
+                      loss, d_hidden, d_lm_head, diag, adv, err_flag,
+                      workspace, stream);
+}
+
+rz_status rz_score_centering_fwd_bwd(
+    const void* hidden, const void* lm_head, const int32_t* tokens,
+    const float* logmu, const uint8_t* mask, const int32_t* cu_rows,
+    const float* rewards, const int32_t* group_ids, int64_t n_rows,
+    int32_t n_resp, int32_t H, int32_t V, rz_dtype dt, float* logprobs,
+    float* loss, float* d_hidden, float* d_lm_head, float* diag, float* adv,
+    int32_t* err_flag, void* workspace, size_t workspace_bytes,
+    hipStream_t stream) {
+  rz_status st = fb_args_ok(hidden, lm_head, tokens, logmu, false, mask,
+                            cu_rows, rewards, group_ids, n_rows, n_resp, H, V,
+                            dt, logprobs, loss, d_hidden, d_lm_head);
+  if (st != RZ_OK) return st;
+  if (diag && !logmu && n_rows > 0) return RZ_ERR_INVALID_ARG;
+  Carver meas{nullptr};
+  const size_t need = carve_fb(meas, n_rows, n_resp, H, V, dt, nullptr, -1);
+  st = ws_check(workspace, workspace_bytes, need);
+  if (st != RZ_OK) return st;
+  return fwd_bwd_core(hidden, lm_head, tokens, logmu, mask, cu_rows, rewards,
+                      group_ids, n_rows, n_resp, H, V, dt, 0, H, 1, logprobs,
                       loss, d_hidden, d_lm_head, diag, adv, err_flag,
                       workspace, stream);
 }
@@ -618,7 +670,7 @@ rz_status rz_token_logprobs_mx(const void* hidden, const uint8_t* codes,
                                const int32_t* tokens, int64_t n_rows, int32_t H,
                                int32_t V, float* logprobs, float* lse,
                                int32_t* err_flag, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+                               size_t workspace_bytes, hipStream_t stream) {
   rz_status st = mx_args_ok(hidden, codes, scales, fmt, n_rows, H, V);
   if (st != RZ_OK) return st;
   if (n_rows == 0) return RZ_OK;
@@ -658,7 +710,7 @@ rz_status rz_sample_tokens_mx(const void* hidden, const uint8_t* codes,
                               int32_t H, int32_t V, uint64_t seed,
                               int32_t* tokens, float* logmu, float* lse,
                               int32_t* err_flag, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+                              size_t workspace_bytes, hipStream_t stream) {
   rz_status st = mx_args_ok(hidden, codes, scales, fmt, n_rows, H, V);
   if (st != RZ_OK) return st;
   if (n_rows == 0) return RZ_OK;
@@ -699,7 +751,7 @@ rz_status rz_sample_tokens_mx(const void* hidden, const uint8_t* codes,
 
 rz_status rz_lora_augment(const void* hidden, const void* lora_A, float scale,
                           int64_t n_rows, int32_t H, int32_t r, rz_dtype dt,
-                          void* hidden_aug, void* stream) {
+                          void* hidden_aug, hipStream_t stream) {
   if (dt != RZ_DTYPE_F32 && dt != RZ_DTYPE_BF16) return RZ_ERR_UNSUPPORTED;
   if (n_rows < 0 || n_rows > RZ_MAX_ROWS) return RZ_ERR_INVALID_ARG;
   if (r < 1 || r > kLoraCols) return RZ_ERR_INVALID_ARG;
@@ -714,7 +766,7 @@ rz_status rz_lora_augment(const void* hidden, const void* lora_A, float scale,
 
 rz_status rz_lora_merge_head(const void* lm_head, const void* lora_B, int32_t V,
                              int32_t H, int32_t r, rz_dtype dt, void* head_aug,
-                             void* stream) {
+                             hipStream_t stream) {
   if (dt != RZ_DTYPE_F32 && dt != RZ_DTYPE_BF16) return RZ_ERR_UNSUPPORTED;
   if (r < 1 || r > kLoraCols) return RZ_ERR_INVALID_ARG;
   if (!dims_ok(H, V, dt) || H + kLoraCols > RZ_MAX_HIDDEN) return RZ_ERR_UNSUPPORTED;
@@ -732,9 +784,9 @@ rz_status rz_reinforce_zero_fwd_bwd_lora(
     int32_t n_resp, int32_t H, int32_t V, rz_dtype dt, float* logprobs,
     float* loss, float* d_hidden, float* d_lora_A, float* d_lora_B,
     float* diag, float* adv, int32_t* err_flag, void* workspace,
-    size_t workspace_bytes, void* stream) {
+    size_t workspace_bytes, hipStream_t stream) {
   if (n_rows < 0 || n_rows > RZ_MAX_ROWS) return RZ_ERR_INVALID_ARG;
-  if (n_resp < 1 || n_resp > (1 << 24)) return RZ_ERR_INVALID_ARG;
+  if (n_resp < 1 || n_resp > RZ_MAX_RESPONSES) return RZ_ERR_INVALID_ARG;
   if (dt != RZ_DTYPE_F32 && dt != RZ_DTYPE_BF16) return RZ_ERR_UNSUPPORTED;
   if (H <= 0 || V <= 0 || r < 1 || r > kLoraCols) return RZ_ERR_INVALID_ARG;
   if (!dims_ok(H, V, dt) || H + kLoraCols > RZ_MAX_HIDDEN) return RZ_ERR_UNSUPPORTED;
@@ -763,7 +815,7 @@ rz_status rz_reinforce_zero_fwd_bwd_lora(
   // adapter's columns (W is frozen): dL/dB
   rz_status core = fwd_bwd_core(w.h_aug, w.head_aug, tokens, logmu, mask,
                                 cu_rows, rewards, group_ids, n_rows, n_resp,
-                                Ha, V, dt, H, kLoraCols, logprobs, loss,
+                                Ha, V, dt, H, kLoraCols, 0, logprobs, loss,
                                 w.dh_aug, w.dB, diag, adv, err_flag, w.core,
                                 stream);
   if (core != RZ_OK) return core;

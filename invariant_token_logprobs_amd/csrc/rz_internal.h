@@ -26,12 +26,11 @@ enum KernelId {
   K_TRANSPOSE_H,
   K_BWD_DH,          // dHidden GEMM
   K_BWD_DW,          // dW GEMM
-  K_FILL,
-  K_TOK_HIST,
-  K_SCAN,
-  K_TOK_SCATTER,
-  K_BUCKET_SORT,
-  K_DW_FIX,
+  K_SORT_HIST,       // stable radix sort by key: digit histograms
+  K_SORT_SCAN,       //   their exclusive scan
+  K_SORT_SCATTER,    //   the stable scatter
+  K_DW_FIX,          // dW one-hot fix-up over pieces of the sorted list
+  K_DW_FIX_SPAN,     //   runs crossing pieces
   K_TARGET_LOGIT,    // z[t, a_t] for the gather
   K_FWD_SAMPLE,      // rollout-side logits GEMM with the draw in the epilogue
   K_DRAW_MERGE,      // per-row best draw over the vocab tiles
@@ -123,18 +122,24 @@ hipError_t launch_mask_compact(const uint8_t* mask, int64_t n,
 hipError_t launch_rows_finalize(const uint8_t* mask, int64_t n, int H,
                                 float* logprobs, float* d_hidden,
                                 hipStream_t s);
+// ints of workspace launch_stable_sort needs for at most cap elements
+size_t sort_ws_ints(int64_t cap);
+hipError_t launch_stable_sort(DevRows rows, int64_t cap, const int* keys,
+                              int kmax, int* ws, const int** skey,
+                              const int** sval, hipStream_t s);
 hipError_t launch_advantages(const uint8_t* mask, int64_t n, const int* cu,
                              const float* rewards, const int* gid, int B,
                              const int* bad_cu, int* T, int* gcnt, double* gsum,
-                             double* Ad, double* fcoef, float* adv, int* err,
-                             hipStream_t s);
+                             double* Ad, double* fcoef, float* adv, int* bad_gid,
+                             int* sort_ws, int* err, hipStream_t s);
+// sc = 1: score centering (S_i sums log pi; c_t = A_i / (B T_i))
 hipError_t launch_loss_value(const uint8_t* mask, const float* logprobs,
                              const float* logmu, int64_t n, const int* cu,
-                             int B, const int* T, const double* Ad, double* S,
-                             float* loss, hipStream_t s);
+                             int B, int sc, const int* T, const double* Ad,
+                             double* S, float* loss, hipStream_t s);
 hipError_t launch_coef(DevRows rows, const float* logpi_v, const float* logmu,
                        const int* idx, const int* respv, const double* fcoef,
-                       float* coef, hipStream_t s);
+                       int sc, float* coef, hipStream_t s);
 size_t diag_partials_bytes(int64_t n);
 hipError_t launch_diagnostics(const float* logpi, const float* logmu,
                               const uint8_t* mask, int64_t n, void* partials,
@@ -160,10 +165,12 @@ hipError_t launch_bwd_dw(int dt, const void* dz, int64_t ld, DevRows krows,
                          const void* hT, int64_t ldht, int H, int V, int Vpad,
                          float* d_lm_head, int first, float* part,
                          hipStream_t s);
+// floats of the parked run sums of launch_dw_fix for at most cap rows
+int64_t dw_fix_cont_floats(int64_t cap, int H);
 hipError_t launch_dw_fix(int dt, const int* nvalid, int64_t cap,
                          const int* tokv, const int* idx, const float* coef,
-                         const void* hidden, int64_t ld, int H, int V, int* counts,
-                         int* cursor, int* offsets, int* sorted,
-                         float* d_lm_head, hipStream_t s);
+                         const void* hidden, int64_t ld, int H, int V,
+                         int* sort_ws, float* cont, float* d_lm_head,
+                         hipStream_t s);
 
 }  // namespace rz

@@ -74,8 +74,14 @@ struct FwdArgs {
 // Storage type of e = exp(z - m_tile) in (0, 1]: fp16 for bf16 inputs (an
 // 11-bit significand at the same two bytes, so that e's rounding adds a
 // quarter of the bf16 rounding the dlogits already carry), fp32 otherwise.
+// The fp16 copy holds e * 2^kEScaleLog2, which keeps every e >= 2^-28 a
+// normal fp16 number (a peaked softmax puts many e far below fp16's smallest
+// normal, 2^-14, where its relative precision is lost) and stays below fp16's
+// largest value at e = 1; the dz rescale undoes the power of two exactly.
 template <typename T> struct EStore { typedef float type; };
 template <> struct EStore<bf16> { typedef _Float16 type; };
+constexpr float kEScale = 16384.f;         // 2^14
+constexpr float kEUnscale = 1.f / 16384.f;  // 2^-14
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 template <bool B> struct BoolC { static constexpr bool value = B; };
 template <int I> struct IntC { static constexpr int value = I; };
@@ -248,8 +254,11 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
       if (m0 + wm * RW + mi * 32 >= M) continue;
       const int R = wm * RW + mi * 32 + l32;
       const bool rvalid = m0 + R < M;
-      // exp(z - m) = 2^(z log2 e - m log2 e): one FMA per element
-      const float nm = -rm[mi] * kLog2e;
+      // exp(z - m) = 2^((z - m) log2 e).  z - m is formed first, so the
+      // maximum's own term is 2^0 = 1 exactly: s_tile >= 1, lse >= m, and
+      // log pi = z[a_t] - lse <= 0 with lse = m exactly on a row whose other
+      // tokens carry less than an ulp of mass.
+      const float mrow = rm[mi];
       float s = 0.f;
 #pragma unroll
       for (int ni = 0; ni < kTN; ++ni)
@@ -259,14 +268,14 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
           float ev[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            ev[j] = __builtin_amdgcn_exp2f(fmaf(acc[mi][ni][4 * q + j], kLog2e, nm));
+            ev[j] = __builtin_amdgcn_exp2f((acc[mi][ni][4 * q + j] - mrow) * kLog2e);
             if constexpr (!kFull) ev[j] = c0 + j < a.V ? ev[j] : 0.f;
             s += ev[j];
           }
           if constexpr (kStoreE) {
             if constexpr (sizeof(T) == 2) {
-              const f16x4 hv = {(_Float16)ev[0], (_Float16)ev[1],
-                                (_Float16)ev[2], (_Float16)ev[3]};
+              const f16x4 hv = {(_Float16)(ev[0] * kEScale), (_Float16)(ev[1] * kEScale),
+                                (_Float16)(ev[2] * kEScale), (_Float16)(ev[3] * kEScale)};
               *reinterpret_cast<u32x2*>(
                   lds + e_stage_off(R, wn * 16 + ni * 4 + q) + half * 8) =
                   __builtin_bit_cast(u32x2, hv);
@@ -400,103 +409,92 @@ void k_fwd_logits64_mx(FwdArgs a) {
   fwd_logits_body<bf16, false, kSample, 1, kFmt>(a, lds);
 }
 
-// z[t, a_t] = <hidden[t], W[a_t]> for every listed row: one wave per row,
-// lane l folding 16-byte chunks l, l + 64, ... in ascending order (fp32
-// FMA), then a fixed xor butterfly across the wave.  Per-row work in a fixed
-// order, so the value does not depend on the batch.  Rows with a token
-// outside [0, V) are skipped (the merge flags them and writes NaN).
-template <typename T>
-__global__ __launch_bounds__(256) void k_target_logit(
+// z[t, a_t] by the logits GEMM's own arithmetic.  One wave takes 32 listed
+// rows and runs the forward tile's MFMA sequence -- the same instruction,
+// the head's fragment as its first operand and the hidden row's as its
+// second (the forward's swapped order), 16-byte fragments of K steps
+// k = 0, 1, 2, ... in order, fp32 accumulators from 0 -- on the 32 x 32
+// block whose first operand rows are the 32 rows' token rows of the head
+// and whose second operand rows are their hidden states.  An output element
+// depends only on its own two operand rows, so the block's diagonal is
+// z[t, a_t] bit for bit as the logits GEMM computes it (in every tile
+// form), and log pi = z[a_t] - lse subtracts two results of one
+// accumulation.  kWFmt >= 0 makes the head's fragments from MX codes by the
+// MX tile's exact conversions.  Rows with a token outside [0, V) run on
+// token 0 and are not stored (the merge flags them).  A row's value does not
+// depend on the other rows of its wave.
+template <typename T, int kWFmt = -1>
+__global__ __launch_bounds__(256) void k_target_mfma(
     const char* __restrict__ hidden, int64_t lda, const int* __restrict__ a_rows,
-    DevRows rows, const char* __restrict__ lm_head, int H, int V,
-    const int* __restrict__ row_tokens, float* __restrict__ ztgt) {
-  const RowCount rc = to_rc(rows);
-  const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (p >= rc.get()) return;
-  const int lane = threadIdx.x & 63;
-  const int64_t pos = rc.base + p;
-  const int tok = row_tokens[pos];
-  if (tok < 0 || tok >= V) return;
-  const int64_t hrow = a_rows ? (int64_t)a_rows[pos] : pos;
-  const char* hp = hidden + hrow * lda;
-  const char* wp = lm_head + (int64_t)tok * H * (int64_t)sizeof(T);
-  const int nch = H * (int)sizeof(T) / 16;
-  float acc = 0.f;
-  for (int c = lane; c < nch; c += 64) {
-    const u32x4 hv = *reinterpret_cast<const u32x4*>(hp + (int64_t)c * 16);
-    const u32x4 wv = *reinterpret_cast<const u32x4*>(wp + (int64_t)c * 16);
-    // whole-vector bit casts only: casting single vector elements is
-    // miscompiled by this toolchain
-    if constexpr (sizeof(T) == 2) {
-      const u32x4 hi_mask = {0xffff0000u, 0xffff0000u, 0xffff0000u, 0xffff0000u};
-      const f32x4 hl = __builtin_bit_cast(f32x4, hv << 16);
-      const f32x4 wl = __builtin_bit_cast(f32x4, wv << 16);
-      const f32x4 hh = __builtin_bit_cast(f32x4, hv & hi_mask);
-      const f32x4 wh = __builtin_bit_cast(f32x4, wv & hi_mask);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc = fmaf(hl[j], wl[j], acc);   // element 2 j
-        acc = fmaf(hh[j], wh[j], acc);   // element 2 j + 1
-      }
-    } else {
-      const f32x4 hf = __builtin_bit_cast(f32x4, hv);
-      const f32x4 wf = __builtin_bit_cast(f32x4, wv);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc = fmaf(hf[j], wf[j], acc);
-    }
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
-  if (lane == 0) ztgt[pos] = acc;
-}
-
-// The target logit on an MX-format head: the same 16-byte chunks (8 values)
-// in the same order and the same FMAs as k_target_logit<bf16>, with W's 8
-// values made from their codes by the exact scaled conversion, so the result
-// equals k_target_logit on the expanded head bit for bit.
-template <int kFmt>
-__global__ __launch_bounds__(256) void k_target_logit_mx(
-    const char* __restrict__ hidden, int64_t lda, DevRows rows,
+    DevRows rows, const char* __restrict__ lm_head,
     const uint8_t* __restrict__ wcodes, const uint8_t* __restrict__ wscales,
     int H, int V, const int* __restrict__ row_tokens, float* __restrict__ ztgt) {
   const RowCount rc = to_rc(rows);
-  const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (p >= rc.get()) return;
+  const int n = rc.get();
+  const int g0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 32;
+  if (g0 >= n) return;  // uniform per wave
   const int lane = threadIdx.x & 63;
+  const int j = lane & 31, half = lane >> 5;
+  int p = g0 + j;
+  const bool live = p < n;
+  p = live ? p : n - 1;
   const int64_t pos = rc.base + p;
-  const int tok = row_tokens[pos];
-  if (tok < 0 || tok >= V) return;
-  const char* hp = hidden + pos * lda;
-  const uint8_t* cp = wcodes + (int64_t)tok * (kFmt == 0 ? H / 2 : H);
-  const uint8_t* sp = wscales + (int64_t)tok * (H / 32);
-  const int nch = H / 8;
-  float acc = 0.f;
-  for (int c = lane; c < nch; c += 64) {
-    const u32x4 hv = *reinterpret_cast<const u32x4*>(hp + (int64_t)c * 16);
-    const int code = sp[c >> 2];
-    u32x4 wv;
-    if constexpr (kFmt == 0)
-      wv = fp4x8_to_bf16(*reinterpret_cast<const uint32_t*>(cp + (int64_t)c * 4),
-                         e8m0_scale(code));
-    else
-      wv = fp8x8_to_bf16(*reinterpret_cast<const u32x2*>(cp + (int64_t)c * 8),
-                         e8m0_scale(code));
-    if (!mx_scale_ok(kFmt, code))
-      wv = u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
-    const u32x4 hi_mask = {0xffff0000u, 0xffff0000u, 0xffff0000u, 0xffff0000u};
-    const f32x4 hl = __builtin_bit_cast(f32x4, hv << 16);
-    const f32x4 wl = __builtin_bit_cast(f32x4, wv << 16);
-    const f32x4 hh = __builtin_bit_cast(f32x4, hv & hi_mask);
-    const f32x4 wh = __builtin_bit_cast(f32x4, wv & hi_mask);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc = fmaf(hl[j], wl[j], acc);
-      acc = fmaf(hh[j], wh[j], acc);
-    }
+  int tok = row_tokens[pos];
+  const bool tok_ok = tok >= 0 && tok < V;
+  tok = tok_ok ? tok : 0;
+  const int64_t hrow = a_rows ? (int64_t)a_rows[pos] : pos;
+  const char* hp = hidden + hrow * lda;
+  const char* wp = lm_head + (int64_t)tok * H * (int64_t)sizeof(T);
+  const uint8_t* cp = nullptr;
+  const uint8_t* sp = nullptr;
+  if constexpr (kWFmt >= 0) {
+    cp = wcodes + (int64_t)tok * (kWFmt == 0 ? H / 2 : H);
+    sp = wscales + (int64_t)tok * (H / 32);
   }
+  // the head's 16-byte fragment (8 values) at chunk c of the row
+  auto wfrag = [&](int c) -> u32x4 {
+    if constexpr (kWFmt < 0) {
+      return *reinterpret_cast<const u32x4*>(wp + (int64_t)c * 16);
+    } else {
+      const int code = sp[c >> 2];
+      u32x4 v;
+      if constexpr (kWFmt == 0)
+        v = fp4x8_to_bf16(*reinterpret_cast<const uint32_t*>(cp + (int64_t)c * 4),
+                          e8m0_scale(code));
+      else
+        v = fp8x8_to_bf16(*reinterpret_cast<const u32x2*>(cp + (int64_t)c * 8),
+                          e8m0_scale(code));
+      return mx_scale_ok(kWFmt, code) ? v
+                                      : u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+    }
+  };
+  f32x16 acc;
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
-  if (lane == 0) ztgt[pos] = acc;
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  // K step s covers 32 bytes of each row; lane half h holds chunk 2 s + h
+  // (bf16: values 16 s + 8 h .. + 7; fp32: 8 s + 4 h .. + 3), as in the tile
+  const int nsteps = H * (int)sizeof(T) / 32;  // a multiple of 4
+  for (int s0 = 0; s0 < nsteps; s0 += 4) {
+    u32x4 fw[4], fh[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = 2 * (s0 + u) + half;
+      fw[u] = wfrag(c);
+      fh[u] = *reinterpret_cast<const u32x4*>(hp + (int64_t)c * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) mfma_step(acc, fw[u], fh[u], (const T*)nullptr);
+  }
+  // lane l holds column j = l % 32 and rows 8 (r / 4) + 4 half + (r % 4):
+  // the diagonal element (j, j) is in the half with 4 half = j & 4, at
+  // register 4 (j / 8) + (j % 4)
+  if (live && tok_ok && ((j >> 2) & 1) == half) {
+    const int rr = 4 * (j >> 3) + (j & 3);
+    float z = acc[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) z = r == rr ? acc[r] : z;
+    ztgt[pos] = z;
+  }
 }
 
 // ===================================================================
@@ -562,7 +560,12 @@ __global__ __launch_bounds__(256) void k_lse_merge(
   const int tok = row_tokens[pos];
   float lp;
   if (tok >= 0 && tok < V) {
+    // The target logit's fp32 dot product and the MFMA sums behind lse
+    // round differently, so on a row where the token takes nearly all the
+    // mass the difference can land a few ulps above 0; a logprob is <= 0.
+    // (NaN stays NaN.)
     lp = ztgt[pos] - lse;
+    lp = lp > 0.f ? 0.f : lp;
   } else {
     lp = __builtin_nanf("");
     if (err) atomicOr(err, 1);
@@ -777,53 +780,62 @@ __global__ __launch_bounds__(256) void k_resp_counts(const uint8_t* mask,
   if (threadIdx.x == 0) T[i] = c;
 }
 
-// Groups and advantages: A_i = r_i - mean of r over the group of i (sums in
-// ascending i, fp64), and the per-response factor A_i / (B T_i) of c_t.
+// Group sums over the responses ordered by group id (stable, so ascending
+// i within a group): the first response of each group's run sums the
+// group's rewards in that order (fp64) and counts them.  Invalid ids sort
+// last (as B), so the last entry tells whether there was one.
+__global__ __launch_bounds__(256) void k_group_sums(int B, const int* skey,
+                                                    const int* sval,
+                                                    const float* rewards,
+                                                    int* gcnt, double* gsum,
+                                                    int* bad_gid) {
+  const int q = blockIdx.x * 256 + threadIdx.x;
+  if (q >= B) return;
+  const int g = skey[q];
+  if (q == B - 1) *bad_gid = g >= B;
+  if (g >= B || (q > 0 && skey[q - 1] == g)) return;
+  int c = 0;
+  double r = 0.0;
+  for (int j = q; j < B && skey[j] == g; ++j) {
+    ++c;
+    r += (double)rewards[sval[j]];
+  }
+  gcnt[g] = c;
+  gsum[g] = r;
+}
+
+// Advantages: A_i = r_i - mean of r over the group of i, and the
+// per-response factor A_i / (B T_i) of c_t (NaN when a group id or cu_rows
+// is invalid).
 __global__ __launch_bounds__(256) void k_advantages(
     const float* rewards, const int* gid, int B, const int* T,
-    const int* bad_cu, int* gcnt, double* gsum, double* Ad, double* fcoef,
-    float* adv, int* err) {
-  __shared__ int bad;
-  const int tid = threadIdx.x;
-  if (tid == 0) bad = *bad_cu;
-  __syncthreads();
-  for (int g = tid; g < B; g += 256) {
-    int c = 0;
-    double r = 0.0;
-    for (int j = 0; j < B; ++j)
-      if (gid[j] == g) {
-        ++c;
-        r += (double)rewards[j];
-      }
-    gcnt[g] = c;
-    gsum[g] = r;
+    const int* bad_cu, const int* bad_gid, const int* gcnt, const double* gsum,
+    double* Ad, double* fcoef, float* adv, int* err) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= B) return;
+  const bool bad = *bad_cu || *bad_gid;
+  double A = __builtin_nan(""), f = __builtin_nan("");
+  if (!bad) {
+    const int g = gid[i];
+    A = (double)rewards[i] - gsum[g] / (double)gcnt[g];
+    f = T[i] > 0 ? A / ((double)B * (double)T[i]) : 0.0;
   }
-  for (int i = tid; i < B; i += 256)
-    if (gid[i] < 0 || gid[i] >= B) atomicOr(&bad, 2);
-  __syncthreads();
-  const double qnan = __builtin_nan("");
-  for (int i = tid; i < B; i += 256) {
-    double A = qnan, f = qnan;
-    if (!bad) {
-      const int g = gid[i];
-      A = (double)rewards[i] - gsum[g] / (double)gcnt[g];
-      f = T[i] > 0 ? A / ((double)B * (double)T[i]) : 0.0;
-    }
-    Ad[i] = A;
-    fcoef[i] = f;
-    if (adv) adv[i] = (float)A;
-  }
-  if (tid == 0 && err && (bad & 2)) atomicOr(err, 2);
+  Ad[i] = A;
+  fcoef[i] = f;
+  if (adv) adv[i] = (float)A;
+  if (i == 0 && err && *bad_gid) atomicOr(err, 2);
 }
 
 // S_i = sum of w_t = exp(log pi_t - log mu_t) over the valid rows of
 // response i (no clipping), fp64, per-thread strided partials then a fixed
-// tree: the order depends only on the response's rows.
+// tree: the order depends only on the response's rows.  Score centering
+// (sc = 1) sums log pi_t instead: its surrogate has w = 1 and the gradient
+// of log pi.
 __global__ __launch_bounds__(256) void k_resp_sums(const uint8_t* mask,
                                                    const float* logprobs,
                                                    const float* logmu,
                                                    int64_t n, const int* cu,
-                                                   double* S) {
+                                                   int sc, double* S) {
   __shared__ double shd[256];
   const int i = blockIdx.x;
   int64_t lo = cu[i], hi = cu[i + 1];
@@ -831,7 +843,8 @@ __global__ __launch_bounds__(256) void k_resp_sums(const uint8_t* mask,
   hi = hi < lo ? lo : (hi > n ? n : hi);
   double s = 0.0;
   for (int64_t t = lo + threadIdx.x; t < hi; t += 256)
-    if (mask[t]) s += (double)expf(logprobs[t] - logmu[t]);
+    if (mask[t])
+      s += sc ? (double)logprobs[t] : (double)expf(logprobs[t] - logmu[t]);
   s = block_sum_d(s, shd);
   if (threadIdx.x == 0) S[i] = s;
 }
@@ -850,18 +863,23 @@ __global__ __launch_bounds__(256) void k_loss_value(const double* Ad,
 }
 
 // c_t = A_i w_t / (B T_i): minus the derivative of L by log pi_t (the
-// gradient flows through the numerator pi_theta only).
+// gradient flows through the numerator pi_theta only).  Score centering
+// (sc = 1): c_t = A_i / (B T_i), the weight replaced by 1.
 __global__ __launch_bounds__(256) void k_coef(DevRows rows,
                                               const float* logpi_v,
                                               const float* logmu,
                                               const int* idx,
                                               const int* respv,
-                                              const double* fcoef,
+                                              const double* fcoef, int sc,
                                               float* coef) {
   const RowCount rc = to_rc(rows);
   const int q = blockIdx.x * 256 + threadIdx.x;
   if (q >= rc.get()) return;
   const int64_t p = rc.base + q;
+  if (sc) {
+    coef[p] = (float)fcoef[respv[p]];
+    return;
+  }
   const float w = expf(logpi_v[p] - logmu[idx[p]]);
   coef[p] = (float)(fcoef[respv[p]] * (double)w);
 }
@@ -1312,7 +1330,7 @@ __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ in,
 
 // ===================================================================
 // Backward, part 1: dlogits.  The forward of the learner call stored
-// e[t, v] = exp(z[t, v] - m_tile(t, j)) (EStore type, in the dz buffer) for
+// e[t, v] = exp(z[t, v] - m_tile(t, j)) (EStore type, times 2^14 for fp16, in the dz buffer) for
 // the vocab tile j holding v; with
 // lse_t known, dz[t, v] = c_t * exp(m_tile(t, j) - lse_t) * e[t, v] is the
 // softmax part of dL/dz (the one-hot part -c_t [v == a_t] is applied exactly
@@ -1397,8 +1415,11 @@ __global__ __launch_bounds__(256) void k_dz_scale(
           uint32_t y[4];
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
-            const uint32_t lo = __builtin_bit_cast(uint16_t, (T)(f * (float)e[2 * w]));
-            const uint32_t hi = __builtin_bit_cast(uint16_t, (T)(f * (float)e[2 * w + 1]));
+            // e was stored times 2^14: unscaled exactly before the product
+            const uint32_t lo = __builtin_bit_cast(
+                uint16_t, (T)(f * ((float)e[2 * w] * kEUnscale)));
+            const uint32_t hi = __builtin_bit_cast(
+                uint16_t, (T)(f * ((float)e[2 * w + 1] * kEUnscale)));
             y[w] = lo | (hi << 16);
           }
           *reinterpret_cast<u32x4*>(p) = u32x4{y[0], y[1], y[2], y[3]};
@@ -1612,30 +1633,55 @@ __global__ __launch_bounds__(256) void k_dw_tail(DwArgs a) {
 }
 
 // ===================================================================
-// dW one-hot fix-up: dW[v, :] -= sum over valid t with a_t = v, in
-// ascending t, of c_t h_t.  Tokens are bucketed by a counting sort whose
-// buckets are then ordered by position, so the sum order is fixed.
+// Stable ordering by an integer key (the dW fix-up's tokens, the group ids
+// of the advantages): an LSD radix sort over 8-bit digits.  Each pass is a
+// per-tile digit histogram, one exclusive scan over (digit, tile) in that
+// order, and a scatter in which each tile places its elements in index
+// order: ranks among equal digits come from wave ballots, then from the
+// waves before, then from the tile's earlier rounds.  Equal keys therefore
+// keep their input order (stability), every pass moves each element once,
+// and the work does not depend on how the keys are distributed (one key on
+// every element costs what distinct keys cost).  All counts are exact
+// integers, so the result is the same in every run.
 // ===================================================================
-__global__ __launch_bounds__(256) void k_fill_i32(int* p, int64_t n, int v) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) p[i] = v;
+constexpr int kSortTile = 2048;  // elements per workgroup per pass (8 rounds)
+
+__device__ __forceinline__ int sort_key_in(const int* keys, int i, int kmax,
+                                           bool clamp) {
+  const int k = keys[i];
+  // keys outside [0, kmax) (bad tokens or group ids) sort last, as kmax
+  return clamp ? ((unsigned)k < (unsigned)kmax ? k : kmax) : k;
 }
 
-__global__ __launch_bounds__(256) void k_tok_hist(DevRows rows,
-                                                  const int* tokv, int V,
-                                                  int* counts) {
-  const int p = blockIdx.x * 256 + threadIdx.x;
-  if (p >= to_rc(rows).get()) return;
-  const int t = tokv[p];
-  if (t >= 0 && t < V) atomicAdd(&counts[t], 1);
+__global__ __launch_bounds__(256) void k_sort_hist(DevRows rows,
+                                                   const int* __restrict__ keys,
+                                                   int kmax, int clamp,
+                                                   int shift, int ntiles,
+                                                   int* __restrict__ ghist) {
+  __shared__ int hist[256];
+  const int tid = threadIdx.x;
+  const int n = to_rc(rows).get();
+  hist[tid] = 0;
+  __syncthreads();
+  const int base = blockIdx.x * kSortTile;
+#pragma unroll
+  for (int r = 0; r < kSortTile / 256; ++r) {
+    const int i = base + r * 256 + tid;
+    if (i < n) atomicAdd(&hist[(sort_key_in(keys, i, kmax, clamp) >> shift) & 255], 1);
+  }
+  __syncthreads();
+  ghist[(int64_t)tid * ntiles + blockIdx.x] = hist[tid];
 }
 
+// Exclusive prefix sum of n counts by one 1024-thread workgroup: each
+// thread sums a contiguous slice, a Hillis-Steele scan over the slice sums,
+// then each thread writes its slice's offsets; offsets[n] = the total.
 __global__ __launch_bounds__(1024) void k_scan_excl(const int* counts, int n,
                                                     int* offsets) {
   __shared__ int sh[1024];
   const int tid = threadIdx.x;
   const int per = (n + 1023) / 1024;
-  const int lo = tid * per, hi = min(n, lo + per);
+  const int lo = min(n, tid * per), hi = min(n, lo + per);
   int sum = 0;
   for (int i = lo; i < hi; ++i) sum += counts[i];
   sh[tid] = sum;
@@ -1654,51 +1700,183 @@ __global__ __launch_bounds__(1024) void k_scan_excl(const int* counts, int n,
   if (tid == 1023) offsets[n] = sh[1023];
 }
 
-__global__ __launch_bounds__(256) void k_tok_scatter(DevRows rows,
-                                                     const int* tokv, int V,
-                                                     const int* offsets,
-                                                     int* cursor,
-                                                     int* sorted) {
-  const int p = blockIdx.x * 256 + threadIdx.x;
-  if (p >= to_rc(rows).get()) return;
-  const int t = tokv[p];
-  if (t < 0 || t >= V) return;
-  sorted[offsets[t] + atomicAdd(&cursor[t], 1)] = p;
-}
-
-__global__ __launch_bounds__(256) void k_bucket_sort(const int* offsets, int V,
-                                                     int* sorted) {
-  const int v = blockIdx.x * 256 + threadIdx.x;
-  if (v >= V) return;
-  const int lo = offsets[v], hi = offsets[v + 1];
-  for (int i = lo + 1; i < hi; ++i) {
-    const int x = sorted[i];
-    int j = i - 1;
-    while (j >= lo && sorted[j] > x) {
-      sorted[j + 1] = sorted[j];
-      --j;
+__global__ __launch_bounds__(256) void k_sort_scatter(
+    DevRows rows, const int* __restrict__ keys_in, const int* __restrict__ vals_in,
+    int kmax, int clamp, int shift, int ntiles, const int* __restrict__ goff,
+    int* __restrict__ keys_out, int* __restrict__ vals_out) {
+  __shared__ int run[256];      // next free slot of each digit in this tile
+  __shared__ int wcnt[4][256];  // this round's count per wave and digit
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int n = to_rc(rows).get();
+  run[tid] = goff[(int64_t)tid * ntiles + blockIdx.x];
+  const uint64_t below = (1ull << lane) - 1ull;  // lanes before this one
+  for (int r = 0; r < kSortTile / 256; ++r) {
+    const int i = blockIdx.x * kSortTile + r * 256 + tid;
+    const bool ok = i < n;
+    int key = 0, val = 0;
+    if (ok) {
+      key = sort_key_in(keys_in, i, kmax, clamp);
+      val = vals_in ? vals_in[i] : i;
     }
-    sorted[j + 1] = x;
+    const int d = (key >> shift) & 255;
+    // lanes of this wave holding the same digit: eight ballots
+    uint64_t peers = __ballot(ok);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const bool bit = (d >> b) & 1;
+      const uint64_t bb = __ballot(bit);
+      peers &= bit ? bb : ~bb;
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) wcnt[w][tid] = 0;
+    __syncthreads();
+    if (ok && (peers & below) == 0) wcnt[wid][d] = __popcll(peers);
+    __syncthreads();
+    if (ok) {
+      int pos = run[d] + __popcll(peers & below);
+      for (int w = 0; w < wid; ++w) pos += wcnt[w][d];
+      keys_out[pos] = key;
+      vals_out[pos] = val;
+    }
+    __syncthreads();
+    run[tid] += wcnt[0][tid] + wcnt[1][tid] + wcnt[2][tid] + wcnt[3][tid];
+    __syncthreads();
   }
 }
 
+// ===================================================================
+// dW one-hot fix-up: dW[v, :] -= sum over valid t with a_t = v of c_t h_t.
+// The valid-row positions, ordered by token (stable, so ascending within a
+// token), are cut into fixed pieces of kFixPiece entries.  A workgroup sums
+// each run of equal tokens in its piece in list order; a run that lies
+// wholly inside the piece updates dW at once, a run continuing from the
+// previous piece is parked (cont_first), and a run that starts in the piece
+// but continues past it is parked too (cont_last).  k_dw_fix_span then adds,
+// for each run that crosses pieces, its parked sums in piece order.  Every
+// token's row of dW is written by one workgroup, each sum has a fixed order
+// that depends only on the sorted list, and no workgroup handles more than
+// a piece of rows (plus, for a run crossing pieces, one parked sum per
+// piece), however often a token occurs.
+// ===================================================================
+constexpr int kFixPiece = 256;  // sorted entries per fix-up workgroup
+constexpr int kFixBatch = 8;    // row chunks loaded ahead per thread
+
 template <typename T>
-__global__ __launch_bounds__(256) void k_dw_fix(const int* offsets,
-                                                const int* sorted,
-                                                const int* idx,
-                                                const float* coef,
-                                                const T* hidden, int64_t ld,
-                                                int H, float* dw) {
-  const int v = blockIdx.x;
-  const int lo = offsets[v], hi = offsets[v + 1];
-  if (lo == hi) return;
-  for (int h = threadIdx.x; h < H; h += 256) {
-    float acc = 0.f;
-    for (int q = lo; q < hi; ++q) {
-      const int p = sorted[q];
-      acc += coef[p] * load_f(hidden + (int64_t)idx[p] * ld + h);
+__global__ __launch_bounds__(256) void k_dw_fix(
+    DevRows rows, const int* __restrict__ skey, const int* __restrict__ sval,
+    const int* __restrict__ idx, const float* __restrict__ coef,
+    const T* __restrict__ hidden, int64_t ld, int H, int V,
+    float* __restrict__ cont_first, float* __restrict__ cont_last,
+    float* __restrict__ dw) {
+  constexpr int kVec = 16 / (int)sizeof(T);  // values per 16-byte chunk
+  __shared__ int sk[kFixPiece];
+  __shared__ int srow[kFixPiece];
+  __shared__ float sc[kFixPiece];
+  const int n = to_rc(rows).get();
+  const int k = blockIdx.x;
+  const int q0 = k * kFixPiece;
+  if (q0 >= n) return;
+  const int cnt = min(n - q0, kFixPiece);
+  const int tid = threadIdx.x;
+  if (tid < cnt) {
+    const int p = sval[q0 + tid];
+    sk[tid] = skey[q0 + tid];
+    srow[tid] = idx[p];
+    sc[tid] = coef[p];
+  }
+  const int prev_key = q0 > 0 ? skey[q0 - 1] : -1;
+  const int next_key = q0 + cnt < n ? skey[q0 + cnt] : -1;
+  __syncthreads();
+  const int nch = H / kVec;
+  for (int c = tid; c < nch; c += 256) {
+    const int col = c * kVec;
+    float acc[kVec];
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) acc[j] = 0.f;
+    int start = 0;
+    for (int j0 = 0; j0 < cnt; j0 += kFixBatch) {
+      // loads of kFixBatch rows first, then the ordered accumulation
+      u32x4 x[kFixBatch];
+#pragma unroll
+      for (int b = 0; b < kFixBatch; ++b)
+        if (j0 + b < cnt)
+          x[b] = *reinterpret_cast<const u32x4*>(hidden + (int64_t)srow[j0 + b] * ld + col);
+#pragma unroll
+      for (int b = 0; b < kFixBatch; ++b) {
+        const int j = j0 + b;
+        if (j >= cnt) break;
+        const float cf = sc[j];
+        if constexpr (sizeof(T) == 2) {
+          const u32x4 hi_mask = {0xffff0000u, 0xffff0000u, 0xffff0000u, 0xffff0000u};
+          const f32x4 lo = __builtin_bit_cast(f32x4, x[b] << 16);
+          const f32x4 hi = __builtin_bit_cast(f32x4, x[b] & hi_mask);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            acc[2 * w] = fmaf(cf, lo[w], acc[2 * w]);
+            acc[2 * w + 1] = fmaf(cf, hi[w], acc[2 * w + 1]);
+          }
+        } else {
+          const f32x4 f = __builtin_bit_cast(f32x4, x[b]);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) acc[w] = fmaf(cf, f[w], acc[w]);
+        }
+        const int v = sk[j];
+        if (j + 1 < cnt && sk[j + 1] == v) continue;  // the run goes on
+        // the run [start, j] of token v ends here (uniform across the block)
+        const bool from_prev = start == 0 && prev_key == v;
+        const bool into_next = j == cnt - 1 && next_key == v;
+        if (v < V) {
+          float* dst;
+          if (from_prev) dst = cont_first + (int64_t)k * H + col;
+          else if (into_next) dst = cont_last + (int64_t)k * H + col;
+          else dst = nullptr;
+          if (dst) {
+#pragma unroll
+            for (int w = 0; w < kVec; w += 4)
+              *reinterpret_cast<f32x4*>(dst + w) =
+                  f32x4{acc[w], acc[w + 1], acc[w + 2], acc[w + 3]};
+          } else {
+            float* o = dw + (int64_t)v * H + col;
+#pragma unroll
+            for (int w = 0; w < kVec; w += 4) {
+              f32x4 y = *reinterpret_cast<const f32x4*>(o + w);
+              y -= f32x4{acc[w], acc[w + 1], acc[w + 2], acc[w + 3]};
+              *reinterpret_cast<f32x4*>(o + w) = y;
+            }
+          }
+        }
+#pragma unroll
+        for (int w = 0; w < kVec; ++w) acc[w] = 0.f;
+        start = j + 1;
+      }
     }
-    dw[(int64_t)v * H + h] -= acc;
+  }
+}
+
+// Runs crossing pieces: the piece where such a run starts adds its parked
+// sums in piece order (its own cont_last, then each following piece's
+// cont_first) and subtracts the total from the token's row of dW.
+__global__ __launch_bounds__(256) void k_dw_fix_span(
+    DevRows rows, const int* __restrict__ skey, int H, int V,
+    const float* __restrict__ cont_first, const float* __restrict__ cont_last,
+    float* __restrict__ dw) {
+  const int n = to_rc(rows).get();
+  const int k = blockIdx.x;
+  const int q0 = k * kFixPiece;
+  if (q0 >= n) return;
+  const int q1 = min(n, q0 + kFixPiece);
+  const int v = skey[q1 - 1];
+  if (v >= V || q1 >= n || skey[q1] != v) return;  // last run ends here
+  // the run began in an earlier piece: that piece owns it
+  if (q0 > 0 && skey[q0] == v && skey[q0 - 1] == v) return;
+  int last = k + 1;  // the last piece the run reaches
+  while ((last + 1) * (int64_t)kFixPiece < n && skey[(last + 1) * kFixPiece] == v) ++last;
+  for (int c = threadIdx.x; c < H / 4; c += 256) {
+    f32x4 s = *reinterpret_cast<const f32x4*>(cont_last + (int64_t)k * H + 4 * c);
+    for (int j = k + 1; j <= last; ++j)
+      s += *reinterpret_cast<const f32x4*>(cont_first + (int64_t)j * H + 4 * c);
+    f32x4* o = reinterpret_cast<f32x4*>(dw + (int64_t)v * H + 4 * c);
+    *o = *o - s;
   }
 }
 
@@ -1726,8 +1904,8 @@ const char* kernel_name(int k) {
       "advantages",  "fwd_logits_gemm", "lse_merge", "rows_finalize",
       "coef",        "dz_scale",    "resp_sums",    "loss_value",
       "diag_partial", "diag_final", "transpose_w",  "transpose_h",
-      "bwd_dh_gemm", "bwd_dw_gemm", "fill",         "tok_hist",
-      "scan",        "tok_scatter", "bucket_sort",  "dw_fix",
+      "bwd_dh_gemm", "bwd_dw_gemm", "sort_hist",    "sort_scan",
+      "sort_scatter", "dw_fix",     "dw_fix_span",
       "target_logit", "fwd_sample_gemm", "draw_merge", "grad_norm",
       "grad_norm_final", "resp_diag", "mx_dequant", "lora_u", "lora_cols",
       "lora_dh", "lora_da"};
@@ -1741,13 +1919,13 @@ hipError_t launch_target_logit(int dt, const void* hidden, int64_t lda_bytes,
                                hipStream_t s) {
   return timed(K_TARGET_LOGIT, s, [&] {
     if (dt)
-      k_target_logit<bf16><<<cdiv(rows.cap, 4), 256, 0, s>>>(
+      k_target_mfma<bf16><<<cdiv(rows.cap, 128), 256, 0, s>>>(
           (const char*)hidden, lda_bytes, a_rows, rows, (const char*)lm_head,
-          H, V, row_tokens, ztgt);
+          nullptr, nullptr, H, V, row_tokens, ztgt);
     else
-      k_target_logit<float><<<cdiv(rows.cap, 4), 256, 0, s>>>(
+      k_target_mfma<float><<<cdiv(rows.cap, 128), 256, 0, s>>>(
           (const char*)hidden, lda_bytes, a_rows, rows, (const char*)lm_head,
-          H, V, row_tokens, ztgt);
+          nullptr, nullptr, H, V, row_tokens, ztgt);
   });
 }
 
@@ -1815,16 +1993,8 @@ hipError_t launch_fwd_mx(int fmt, const void* hidden, int64_t n,
   a.err = err;
   const int nblk = a.mt * a.nt;
   if (!cand) {
-    hipError_t e = timed(K_TARGET_LOGIT, s, [&] {
-      if (fmt == 0)
-        k_target_logit_mx<0><<<cdiv(n, 4), 256, 0, s>>>((const char*)hidden, (int64_t)H * 2,
-                                                         a.rows, codes, scales, H, V,
-                                                         row_tokens, ztgt);
-      else
-        k_target_logit_mx<1><<<cdiv(n, 4), 256, 0, s>>>((const char*)hidden, (int64_t)H * 2,
-                                                         a.rows, codes, scales, H, V,
-                                                         row_tokens, ztgt);
-    });
+    hipError_t e = launch_target_logit_mx(fmt, hidden, n, codes, scales, H, V,
+                                          row_tokens, ztgt, s);
     if (e != hipSuccess) return e;
   }
   return timed(cand ? K_FWD_SAMPLE : K_FWD_LOGITS, s, [&] {
@@ -1845,13 +2015,13 @@ hipError_t launch_target_logit_mx(int fmt, const void* hidden, int64_t n,
   const DevRows rows{nullptr, 0, (int)n};
   return timed(K_TARGET_LOGIT, s, [&] {
     if (fmt == 0)
-      k_target_logit_mx<0><<<cdiv(n, 4), 256, 0, s>>>((const char*)hidden, (int64_t)H * 2,
-                                                       rows, codes, scales, H, V,
-                                                       row_tokens, ztgt);
+      k_target_mfma<bf16, 0><<<cdiv(n, 128), 256, 0, s>>>(
+          (const char*)hidden, (int64_t)H * 2, nullptr, rows, nullptr, codes,
+          scales, H, V, row_tokens, ztgt);
     else
-      k_target_logit_mx<1><<<cdiv(n, 4), 256, 0, s>>>((const char*)hidden, (int64_t)H * 2,
-                                                       rows, codes, scales, H, V,
-                                                       row_tokens, ztgt);
+      k_target_mfma<bf16, 1><<<cdiv(n, 128), 256, 0, s>>>(
+          (const char*)hidden, (int64_t)H * 2, nullptr, rows, nullptr, codes,
+          scales, H, V, row_tokens, ztgt);
   });
 }
 
@@ -1868,16 +2038,8 @@ hipError_t launch_fwd_logits(int dt, const void* hidden, int64_t lda_bytes,
                              const int* row_tokens, float2* partials,
                              int64_t ldp, float* ztgt, void* e, int64_t lde,
                              int Vpad, hipStream_t s) {
-  hipError_t err = timed(K_TARGET_LOGIT, s, [&] {
-    if (dt)
-      k_target_logit<bf16><<<cdiv(rows.cap, 4), 256, 0, s>>>(
-          (const char*)hidden, lda_bytes, a_rows, rows, (const char*)lm_head,
-          H, V, row_tokens, ztgt);
-    else
-      k_target_logit<float><<<cdiv(rows.cap, 4), 256, 0, s>>>(
-          (const char*)hidden, lda_bytes, a_rows, rows, (const char*)lm_head,
-          H, V, row_tokens, ztgt);
-  });
+  hipError_t err = launch_target_logit(dt, hidden, lda_bytes, a_rows, rows,
+                                       lm_head, H, V, row_tokens, ztgt, s);
   if (err != hipSuccess) return err;
   FwdArgs a{};
   a.op = GemmOperands{(const char*)hidden, lda_bytes, a_rows, rows.base,
@@ -1961,27 +2123,85 @@ hipError_t launch_rows_finalize(const uint8_t* mask, int64_t n, int H,
   });
 }
 
+size_t sort_ws_ints(int64_t cap) {
+  const int64_t nt = cap > 0 ? cdiv(cap, kSortTile) : 0;
+  return (size_t)(2 * (256 * nt + 1) + 4 * cap);
+}
+
+// Stable LSD radix sort of the positions 0 .. n-1 (n = rows' count, at most
+// cap) by keys[position] clamped to [0, kmax] (out-of-range keys as kmax):
+// *skey / *sval receive the sorted keys and positions.  ws holds
+// sort_ws_ints(cap) ints.
+hipError_t launch_stable_sort(DevRows rows, int64_t cap, const int* keys,
+                              int kmax, int* ws, const int** skey,
+                              const int** sval, hipStream_t s) {
+  const int ntiles = cap > 0 ? cdiv(cap, kSortTile) : 0;
+  int* ghist = ws;
+  int* goff = ghist + 256 * (int64_t)ntiles + 1;
+  int* buf[4] = {goff + 256 * (int64_t)ntiles + 1, nullptr, nullptr, nullptr};
+  for (int i = 1; i < 4; ++i) buf[i] = buf[i - 1] + cap;
+  int bits = 0;
+  while (bits < 31 && (kmax >> bits) != 0) ++bits;
+  const int passes = bits > 8 ? (bits + 7) / 8 : 1;
+  const int* kin = keys;
+  const int* vin = nullptr;
+  for (int p = 0; p < passes; ++p) {
+    int* kout = buf[(p & 1) * 2];
+    int* vout = buf[(p & 1) * 2 + 1];
+    const int clamp = p == 0;
+    if (ntiles > 0) {
+      hipError_t e = timed(K_SORT_HIST, s, [&] {
+        k_sort_hist<<<ntiles, 256, 0, s>>>(rows, kin, kmax, clamp, 8 * p, ntiles, ghist);
+      });
+      if (e != hipSuccess) return e;
+      e = timed(K_SORT_SCAN, s, [&] {
+        k_scan_excl<<<1, 1024, 0, s>>>(ghist, 256 * ntiles, goff);
+      });
+      if (e != hipSuccess) return e;
+      e = timed(K_SORT_SCATTER, s, [&] {
+        k_sort_scatter<<<ntiles, 256, 0, s>>>(rows, kin, vin, kmax, clamp, 8 * p,
+                                              ntiles, goff, kout, vout);
+      });
+      if (e != hipSuccess) return e;
+    }
+    kin = kout;
+    vin = vout;
+  }
+  *skey = kin;
+  *sval = vin;
+  return hipSuccess;
+}
+
 hipError_t launch_advantages(const uint8_t* mask, int64_t n, const int* cu,
                              const float* rewards, const int* gid, int B,
                              const int* bad_cu, int* T, int* gcnt, double* gsum,
-                             double* Ad, double* fcoef, float* adv, int* err,
-                             hipStream_t s) {
+                             double* Ad, double* fcoef, float* adv, int* bad_gid,
+                             int* sort_ws, int* err, hipStream_t s) {
   hipError_t e = timed(K_RESP_COUNTS, s, [&] {
     k_resp_counts<<<B, 256, 0, s>>>(mask, n, cu, T);
   });
   if (e != hipSuccess) return e;
+  const int* skey = nullptr;
+  const int* sval = nullptr;
+  e = launch_stable_sort(DevRows{nullptr, 0, B}, B, gid, B, sort_ws, &skey, &sval, s);
+  if (e != hipSuccess) return e;
+  e = timed(K_ADVANTAGES, s, [&] {
+    k_group_sums<<<cdiv(B, 256), 256, 0, s>>>(B, skey, sval, rewards, gcnt, gsum,
+                                              bad_gid);
+  });
+  if (e != hipSuccess) return e;
   return timed(K_ADVANTAGES, s, [&] {
-    k_advantages<<<1, 256, 0, s>>>(rewards, gid, B, T, bad_cu, gcnt, gsum, Ad,
-                                   fcoef, adv, err);
+    k_advantages<<<cdiv(B, 256), 256, 0, s>>>(rewards, gid, B, T, bad_cu, bad_gid,
+                                              gcnt, gsum, Ad, fcoef, adv, err);
   });
 }
 
 hipError_t launch_loss_value(const uint8_t* mask, const float* logprobs,
                              const float* logmu, int64_t n, const int* cu,
-                             int B, const int* T, const double* Ad, double* S,
-                             float* loss, hipStream_t s) {
+                             int B, int sc, const int* T, const double* Ad,
+                             double* S, float* loss, hipStream_t s) {
   hipError_t e = timed(K_RESP_SUMS, s, [&] {
-    k_resp_sums<<<B, 256, 0, s>>>(mask, logprobs, logmu, n, cu, S);
+    k_resp_sums<<<B, 256, 0, s>>>(mask, logprobs, logmu, n, cu, sc, S);
   });
   if (e != hipSuccess) return e;
   return timed(K_LOSS_VALUE, s, [&] {
@@ -1991,10 +2211,10 @@ hipError_t launch_loss_value(const uint8_t* mask, const float* logprobs,
 
 hipError_t launch_coef(DevRows rows, const float* logpi_v, const float* logmu,
                        const int* idx, const int* respv, const double* fcoef,
-                       float* coef, hipStream_t s) {
+                       int sc, float* coef, hipStream_t s) {
   return timed(K_COEF, s, [&] {
     k_coef<<<cdiv(rows.cap, 256), 256, 0, s>>>(rows, logpi_v, logmu, idx,
-                                               respv, fcoef, coef);
+                                               respv, fcoef, sc, coef);
   });
 }
 
@@ -2264,45 +2484,38 @@ hipError_t launch_bwd_dw(int dt, const void* dz, int64_t ld, DevRows krows,
   });
 }
 
+int64_t dw_fix_cont_floats(int64_t cap, int H) {
+  return 2 * (int64_t)(cap > 0 ? cdiv(cap, kFixPiece) : 0) * H;
+}
+
 hipError_t launch_dw_fix(int dt, const int* nvalid, int64_t cap,
                          const int* tokv, const int* idx, const float* coef,
-                         const void* hidden, int64_t ld, int H, int V, int* counts,
-                         int* cursor, int* offsets, int* sorted,
-                         float* d_lm_head, hipStream_t s) {
+                         const void* hidden, int64_t ld, int H, int V,
+                         int* sort_ws, float* cont, float* d_lm_head,
+                         hipStream_t s) {
+  if (cap == 0) return hipSuccess;
   DevRows rows{nvalid, 0, (int)cap};
-  hipError_t e = timed(K_FILL, s, [&] {
-    k_fill_i32<<<cdiv(V, 256), 256, 0, s>>>(counts, V, 0);
-    k_fill_i32<<<cdiv(V, 256), 256, 0, s>>>(cursor, V, 0);
-  });
+  const int* skey = nullptr;
+  const int* sval = nullptr;
+  hipError_t e = launch_stable_sort(rows, cap, tokv, V, sort_ws, &skey, &sval, s);
   if (e != hipSuccess) return e;
-  if (cap > 0) {
-    e = timed(K_TOK_HIST, s, [&] {
-      k_tok_hist<<<cdiv(cap, 256), 256, 0, s>>>(rows, tokv, V, counts);
-    });
-    if (e != hipSuccess) return e;
-  }
-  e = timed(K_SCAN, s, [&] {
-    k_scan_excl<<<1, 1024, 0, s>>>(counts, V, offsets);
-  });
-  if (e != hipSuccess) return e;
-  if (cap > 0) {
-    e = timed(K_TOK_SCATTER, s, [&] {
-      k_tok_scatter<<<cdiv(cap, 256), 256, 0, s>>>(rows, tokv, V, offsets,
-                                                   cursor, sorted);
-    });
-    if (e != hipSuccess) return e;
-  }
-  e = timed(K_BUCKET_SORT, s, [&] {
-    k_bucket_sort<<<cdiv(V, 256), 256, 0, s>>>(offsets, V, sorted);
-  });
-  if (e != hipSuccess) return e;
-  return timed(K_DW_FIX, s, [&] {
+  const int npieces = cdiv(cap, kFixPiece);
+  float* cont_first = cont;
+  float* cont_last = cont + (int64_t)npieces * H;
+  e = timed(K_DW_FIX, s, [&] {
     if (dt)
-      k_dw_fix<bf16><<<V, 256, 0, s>>>(offsets, sorted, idx, coef,
-                                       (const bf16*)hidden, ld, H, d_lm_head);
+      k_dw_fix<bf16><<<npieces, 256, 0, s>>>(rows, skey, sval, idx, coef,
+                                             (const bf16*)hidden, ld, H, V,
+                                             cont_first, cont_last, d_lm_head);
     else
-      k_dw_fix<float><<<V, 256, 0, s>>>(offsets, sorted, idx, coef,
-                                        (const float*)hidden, ld, H, d_lm_head);
+      k_dw_fix<float><<<npieces, 256, 0, s>>>(rows, skey, sval, idx, coef,
+                                              (const float*)hidden, ld, H, V,
+                                              cont_first, cont_last, d_lm_head);
+  });
+  if (e != hipSuccess) return e;
+  return timed(K_DW_FIX_SPAN, s, [&] {
+    k_dw_fix_span<<<npieces, 256, 0, s>>>(rows, skey, H, V, cont_first, cont_last,
+                                          d_lm_head);
   });
 }
 

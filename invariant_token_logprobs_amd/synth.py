@@ -18,6 +18,17 @@ the reasoning / tool-use / agentic rollouts the pages describe):
   0.1 at lag 64);
 * seeds: workload k draws its data from seed 1000 + k and its behaviour-logprob
   noise from seed 2000 + k.
+
+Harder inputs for the method's edges (the pages' runs use real policies, whose
+softmax is peaked and whose tokens follow a heavy-tailed law):
+* tokens Zipf-distributed over the vocabulary (zipf_tokens: rank k drawn with
+  probability proportional to k^-s, the ranks assigned to token ids by a
+  seeded permutation);
+* a wider head (random_lm_head's scale; 0.3 at H = 2560 gives logits of
+  standard deviation about 15);
+* hidden rows pulled toward (or away from) their token's head row
+  (aligned_rows), which makes that token nearly certain (or nearly
+  impossible).
 """
 
 from __future__ import annotations
@@ -177,10 +188,12 @@ def workload_layout(name: str):
 
 
 def make_workload(name: str, *, max_responses: Optional[int] = None,
-                  max_valid: Optional[int] = None) -> Batch:
+                  max_valid: Optional[int] = None,
+                  tokens: str = "uniform") -> Batch:
     """Draw the named workload.  Optional caps truncate it (whole responses
     first; the last kept response may be cut) for oracle-sized checks at the
-    full H and V."""
+    full H and V.  tokens = "zipf" replaces the uniform tokens by Zipf(1.1)
+    ones (zipf_tokens, seed 3000 + k); the other arrays are unchanged."""
     wl = WORKLOADS[name]
     rng, lengths, mask, rewards, group_ids = workload_layout(name)
     B = wl.n_resp
@@ -204,10 +217,14 @@ def make_workload(name: str, *, max_responses: Optional[int] = None,
     rewards = rewards[:keep_b].copy()
     group_ids = group_ids[:keep_b].copy()
 
-    tokens = rng.integers(0, wl.V, size=N).astype(np.int32)
+    toks = rng.integers(0, wl.V, size=N).astype(np.int32)
     hidden = _normal(rng, (N, wl.H), 1.0, wl.dtype)
     lm_head = _normal(rng, (wl.V, wl.H), 0.02, wl.dtype)
-    return Batch(name, wl.dtype, wl.H, wl.V, hidden, lm_head, tokens, mask,
+    if tokens == "zipf":
+        toks = zipf_tokens(N, wl.V, 1.1, 3000 + wl.index)
+    elif tokens != "uniform":
+        raise ValueError(f"unknown token law {tokens!r}")
+    return Batch(name, wl.dtype, wl.H, wl.V, hidden, lm_head, toks, mask,
                  cu_rows, rewards, group_ids, wl.sigma, 2000 + wl.index)
 
 
@@ -226,9 +243,36 @@ def random_rows(n: int, H: int, V: int, dtype: str, seed: int):
     return hidden, tokens
 
 
-def random_lm_head(V: int, H: int, dtype: str, seed: int) -> np.ndarray:
+def random_lm_head(V: int, H: int, dtype: str, seed: int,
+                   scale: float = 0.02) -> np.ndarray:
     rng = np.random.default_rng(np.random.PCG64(seed))
-    return _normal(rng, (V, H), 0.02, dtype)
+    return _normal(rng, (V, H), scale, dtype)
+
+
+def zipf_tokens(n: int, V: int, s: float, seed: int) -> np.ndarray:
+    """n tokens whose ranks follow a Zipf law truncated to V: rank k (1-based)
+    with probability k^-s / sum_j j^-s, drawn by inverse transform from
+    PCG64 uniforms; rank k is token perm[k - 1] for a seeded permutation."""
+    rng = np.random.default_rng(np.random.PCG64(seed))
+    w = np.arange(1, V + 1, dtype=np.float64) ** -s
+    cdf = np.cumsum(w)
+    cdf /= cdf[-1]
+    perm = rng.permutation(V)
+    ranks = np.searchsorted(cdf, rng.random(n), side="right")
+    return perm[np.minimum(ranks, V - 1)].astype(np.int32)
+
+
+def aligned_rows(lm_head: np.ndarray, tokens: np.ndarray, dtype: str,
+                 kappa: np.ndarray, seed: int) -> np.ndarray:
+    """Hidden rows kappa_t * W[a_t] + N(0, 1) (rounded to bf16 bits for a
+    bf16 head): kappa_t > 0 pulls row t toward its token's head row, < 0
+    pushes it away, 0 leaves a plain N(0, 1) row."""
+    rng = np.random.default_rng(np.random.PCG64(seed))
+    W = (lm_head.astype(np.uint32) << np.uint32(16)).view(np.float32) \
+        if dtype == "bf16" else np.asarray(lm_head, np.float32)
+    h = rng.standard_normal((len(tokens), W.shape[1]), dtype=np.float32)
+    h += np.asarray(kappa, np.float32)[:, None] * W[np.asarray(tokens)]
+    return round_bf16(h) if dtype == "bf16" else h
 
 
 def random_mx_head(V: int, H: int, fmt: str, seed: int, scale_code: int = 121):

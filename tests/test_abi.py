@@ -69,7 +69,7 @@ def test_token_logprobs_argument_errors(lib):
     assert tlp(lib, tokens=NULL) == INVALID
     assert tlp(lib, out=NULL) == INVALID
     assert tlp(lib, ws=NULL, ws_bytes=1 << 30) == WORKSPACE
-    need = lib.rz_workspace_bytes(0, 4, 1, 64, 10, BF16)
+    need = lib.rz_workspace_bytes_op(0, 4, 1, 64, 10, BF16)
     assert need > 0
     assert tlp(lib, ws_bytes=need - 1) == WORKSPACE
     assert tlp(lib, ws=ctypes.c_void_p(0x1001), ws_bytes=need) == WORKSPACE
@@ -97,7 +97,7 @@ def test_fwd_bwd_argument_errors(lib):
     for name in ("hidden", "head", "tokens", "logmu", "mask", "cu", "rewards",
                  "gid", "logprobs", "loss", "dh", "dw"):
         assert fb(lib, **{name: True}) == INVALID, name
-    need = lib.rz_workspace_bytes(1, 8, 2, 64, 10, F32)
+    need = lib.rz_workspace_bytes_op(1, 8, 2, 64, 10, F32)
     assert need > 0
     assert fb(lib, ws=NULL, ws_bytes=need) == WORKSPACE
     assert fb(lib, ws_bytes=need - 1) == WORKSPACE
@@ -112,7 +112,7 @@ def test_diagnostics_argument_errors(lib):
 
 
 def test_workspace_sizes(lib):
-    ws = lib.rz_workspace_bytes
+    ws = lib.rz_workspace_bytes_op
     assert ws(0, -1, 1, 64, 10, F32) == 0
     assert ws(0, 10, 1, 65, 10, F32) == 0
     assert ws(1, 10, 0, 64, 10, F32) == 0
@@ -125,6 +125,50 @@ def test_workspace_sizes(lib):
         assert ws(op, 12345, 7, 2560, 151936, BF16) % 256 == 0
     # the headline tool-use workload fits comfortably in one MI355X's HBM
     assert ws(1, 295658, 32, 2560, 151936, BF16) < 40 * 2 ** 30
+
+
+def test_common_workspace_query_serves_the_three_calls(lib):
+    """rz_workspace_bytes(n_rows, n_resp, H, V, dt) is one size for
+    rz_token_logprobs, rz_reinforce_zero_fwd_bwd and rz_diagnostics: the
+    largest of their own needs."""
+    ws_op = lib.rz_workspace_bytes_op
+    for (n, B, H, V, dt) in ((1000, 4, 256, 1024, F32), (295658, 32, 2560, 151936, BF16),
+                             (0, 1, 64, 10, BF16), (7, 3, 128, 777, F32)):
+        need = [ws_op(op, n, B, H, V, dt) for op in (0, 1, 2)]
+        assert lib.rz_workspace_bytes(n, B, H, V, dt) == max(need)
+        assert ws_op(rz.RZ_OP_SCORE_CENTERING, n, B, H, V, dt) == need[1]
+    # an invalid n_resp leaves the learner step out, not the other two
+    assert lib.rz_workspace_bytes(100, 0, 64, 10, F32) == max(
+        ws_op(0, 100, 1, 64, 10, F32), ws_op(2, 100, 1, 64, 10, F32))
+    assert lib.rz_workspace_bytes(-1, 1, 64, 10, F32) == 0
+    assert ws_op(1, 10, (1 << 24) + 1, 64, 10, F32) == 0
+
+
+def sc(lib, n=8, B=2, H=64, V=10, dt=F32, ws=P, ws_bytes=0, diag=NULL, **null):
+    args = dict(hidden=P, head=P, tokens=P, logmu=P, mask=P, cu=P, rewards=P,
+                gid=P, logprobs=P, loss=P, dh=P, dw=P)
+    for k in null:
+        args[k] = NULL
+    a = args
+    return lib.rz_score_centering_fwd_bwd(
+        a["hidden"], a["head"], a["tokens"], a["logmu"], a["mask"], a["cu"],
+        a["rewards"], a["gid"], n, B, H, V, dt, a["logprobs"], a["loss"],
+        a["dh"], a["dw"], diag, NULL, NULL, ws, ws_bytes, NULL)
+
+
+def test_score_centering_argument_errors(lib):
+    assert sc(lib, n=-5) == INVALID
+    assert sc(lib, B=0) == INVALID
+    assert sc(lib, H=100) == UNSUPPORTED
+    for name in ("hidden", "head", "tokens", "mask", "cu", "rewards", "gid",
+                 "logprobs", "loss", "dh", "dw"):
+        assert sc(lib, **{name: True}) == INVALID, name
+    need = lib.rz_workspace_bytes_op(rz.RZ_OP_SCORE_CENTERING, 8, 2, 64, 10, F32)
+    # log mu is optional: without it the call gets as far as the workspace
+    # check, but then it cannot report D3 / KL
+    assert sc(lib, logmu=True, ws=NULL, ws_bytes=need) == WORKSPACE
+    assert sc(lib, logmu=True, diag=P, ws_bytes=need) == INVALID
+    assert sc(lib, ws_bytes=need - 1) == WORKSPACE
 
 
 def test_timer_without_gpu_work(lib):
@@ -183,14 +227,14 @@ def test_sample_tokens_argument_errors(lib):
     assert smp(lib, dt=5) == UNSUPPORTED
     for name in ("hidden", "head", "ids", "tokens", "logmu"):
         assert smp(lib, **{name: True}) == INVALID, name
-    need = lib.rz_workspace_bytes(rz.RZ_OP_SAMPLE, 4, 1, 64, 10, BF16)
+    need = lib.rz_workspace_bytes_op(rz.RZ_OP_SAMPLE, 4, 1, 64, 10, BF16)
     assert need > 0 and need % 256 == 0
     assert smp(lib, ws=NULL, ws_bytes=need) == WORKSPACE
     assert smp(lib, ws_bytes=need - 1) == WORKSPACE
     assert smp(lib, n=0) == OK
     # two vocab-tile tables (statistics, draw) and the target logits
     nt = (151936 + 255) // 256
-    big = lib.rz_workspace_bytes(rz.RZ_OP_SAMPLE, 4096, 1, 2560, 151936, BF16)
+    big = lib.rz_workspace_bytes_op(rz.RZ_OP_SAMPLE, 4096, 1, 2560, 151936, BF16)
     assert big >= 2 * 8 * nt * 4096 + 4 * 4096
 
 

@@ -104,15 +104,18 @@ def test_dw_last_round_split(n_vtiles):
     assert np.array_equal(host(again["d_lm_head"]), dw1), f"{what}: dW not reproducible"
 
 
-def test_qwen3_4b_truncated_full_parity():
-    """The headline tool-use shape at its full H = 2560, V = 151936, on the
-    first responses up to 1024 valid rows, every output compared."""
-    b = synth.make_workload("qwen3_4b_tool", max_valid=1024)
-    _case(b, "qwen3-4b-truncated")
+@pytest.mark.parametrize("name", ["qwen3_4b_tool", "r1_distill_1p5b", "qwen3_30b_a3b"])
+def test_truncated_full_parity(name):
+    """Each workload's shape at its full H and V = 151936, on the first
+    responses up to 1024 valid rows, every output compared (the 1.5B head
+    has 6 column tiles of 256, the 30B head 8, the Qwen3-4B head 10, and
+    each its own dW last-round split)."""
+    b = synth.make_workload(name, max_valid=1024)
+    _case(b, f"{name}-truncated")
 
 
 # ----------------------------------------------------------- full sizes
-def _full_size(name, n_sample_rows=512, n_sample_grad=16):
+def _full_size(name, n_sample_rows=4096, n_sample_grad=16):
     torch = torch_mod()
     b = synth.make_workload(name)
     say(f"{name}: N={b.N} B={b.B} valid={b.n_valid}")
@@ -126,7 +129,6 @@ def _full_size(name, n_sample_rows=512, n_sample_grad=16):
     valid = b.mask != 0
     vidx = np.flatnonzero(valid)
     rng = np.random.default_rng(np.random.PCG64(4242))
-    hidden64 = None
 
     # sampled logprobs against the oracle, row by row
     rows = np.sort(rng.choice(vidx, size=min(n_sample_rows, len(vidx)), replace=False))
@@ -134,13 +136,23 @@ def _full_size(name, n_sample_rows=512, n_sample_grad=16):
     h64 = O.to_f64(b.hidden[rows], b.dtype)
     ref_lp, ref_lse = O.token_logprobs(h64, W64, b.tokens[rows])
     lp = host(out["logprobs"])
+    say(f"{name}: {len(rows)} sampled rows checked against the oracle")
     assert_close(lp[rows], ref_lp, t["rtol"], t["atol"], f"{name} sampled logprobs")
     assert np.all(lp[~valid] == 0.0)
+    assert np.all(lp[valid] <= 0.0)
 
-    # advantages and T_i depend only on the inputs
-    A = O.group_mean_advantages(b.rewards, b.group_ids)
-    T = O.valid_token_counts(b.cu_rows, b.mask)
-    assert_close(host(out["adv"]), A, 1e-6, 1e-7, f"{name} adv")
+    # the loss stage of the oracle (w, T, A, loss, D3, KL) fed this call's
+    # own log pi: the GPU's reductions against the plain definition
+    st = O.loss_stage(lp.astype(np.float64), logmu.astype(np.float64), b.mask,
+                      b.cu_rows, b.rewards, b.group_ids)
+    assert_close(host(out["adv"]), st["adv"], 1e-6, 1e-7, f"{name} adv")
+    loss = float(host(out["loss"])[0])
+    # fp32 weights and an fp32 result: a few fp32 roundings of each term
+    scale = float(np.sum(np.abs(st["adv"]) / b.B)) * float(np.max(st["w"][valid]))
+    assert abs(loss - st["loss"]) <= 1e-6 * abs(st["loss"]) + 1e-6 * scale, (loss, st["loss"])
+    diag = host(out["diag"])
+    assert_close(diag, [st["d3"], st["kl"]], 1e-5, 1e-9, f"{name} D3/KL")
+    A, T = st["adv"], st["T"]
 
     # sampled d_hidden rows: c_t from the oracle's own log pi for that row
     grows = rows[:n_sample_grad]
@@ -150,31 +162,24 @@ def _full_size(name, n_sample_rows=512, n_sample_grad=16):
     c = A[resp] * w / (b.B * T[resp])
     dh_ref, _ = O.backward(h64[:n_sample_grad], W64, b.tokens[grows],
                            ref_lse[:n_sample_grad], c)
-    bh, _ = softmax_grad_bounds(h64[:n_sample_grad], W64, ref_lse[:n_sample_grad], c)
+    # c_t of the kernel comes from its own log pi: that difference is
+    # carried into the bound (see gpu_util)
+    bh, _, ch, _ = softmax_grad_bounds(h64[:n_sample_grad], W64, ref_lse[:n_sample_grad], c,
+                                       tokens=b.tokens[grows],
+                                       dlogpi=lp[grows].astype(np.float64) - lp_g)
     dh = host(out["d_hidden"][torch.from_numpy(grows).to(device())])
-    assert_grad_close(dh, dh_ref, b.dtype, f"{name} sampled d_hidden", bh)
+    assert_grad_close(dh, dh_ref, b.dtype, f"{name} sampled d_hidden", bh, ch)
     mrows = np.flatnonzero(~valid)[:64]
     if mrows.size:
         assert not host(out["d_hidden"][torch.from_numpy(mrows).to(device())]).any()
 
     # properties of the whole-batch outputs
-    diag = host(out["diag"])
     diag2 = host(rz.diagnostics(out["logprobs"], d["logmu"], d["mask"]))
     assert np.array_equal(diag, diag2), "fwd_bwd diag != rz_diagnostics"
     nv = len(vidx)
     e_d3 = math.expm1(b.sigma ** 2 / 2)
     assert abs(diag[0] - e_d3) < 6 * b.sigma ** 2 / math.sqrt(2 * nv) + 3 * t["rtol"] * e_d3, (diag, e_d3)
     assert abs(diag[1]) < 6 * b.sigma / math.sqrt(nv), diag
-    # loss is the two-level mean of the weights of the returned logprobs
-    wgpu = np.exp(lp.astype(np.float64) - logmu.astype(np.float64))
-    L = 0.0
-    for i in range(b.B):
-        r = slice(b.cu_rows[i], b.cu_rows[i + 1])
-        if T[i]:
-            L += A[i] * float(np.sum(wgpu[r][valid[r]])) / T[i]
-    L = -L / b.B
-    scale = sum(abs(A[i]) for i in range(b.B)) / b.B * 2
-    assert abs(float(host(out["loss"])[0]) - L) <= 1e-5 * scale, (host(out["loss"]), L)
     # dW: every column sums to zero (sum_v p = 1), and <dW, W> = <dH, h>
     dW = out["d_lm_head"]
     dH = out["d_hidden"]
@@ -193,8 +198,35 @@ def test_qwen3_4b_full_size_sampled():
 
 
 def test_r1_distill_1p5b_full_size_sampled():
-    _full_size("r1_distill_1p5b", n_sample_rows=256, n_sample_grad=8)
+    _full_size("r1_distill_1p5b", n_sample_grad=8)
 
 
 def test_qwen3_30b_full_size_sampled():
-    _full_size("qwen3_30b_a3b", n_sample_rows=256, n_sample_grad=8)
+    _full_size("qwen3_30b_a3b", n_sample_grad=8)
+
+
+def test_qwen3_4b_zipf_tokens_full_size():
+    """The headline workload with Zipf(1.1) tokens (the most frequent token
+    on ~8% of the rows): the one-hot fix-up of dW at full size, checked by
+    dW's column sums and <dW, W> = <dH, h>, and dW reproducible bit for
+    bit."""
+    torch = torch_mod()
+    b = synth.make_workload("qwen3_4b_tool", tokens="zipf")
+    counts = np.bincount(b.tokens[b.mask != 0], minlength=b.V)
+    say(f"qwen3_4b zipf: valid={b.n_valid} top token rows {counts.max()}")
+    d = batch_to_dev(b, np.zeros(b.N, np.float32))
+    mu_ref = behaviour_logprobs_torch(d["hidden"], d["lm_head"], d["tokens"])
+    d["logmu"] = vec_to_dev(synth.make_logmu(host(mu_ref), b.sigma, b.noise_seed))
+    del mu_ref
+    out = run_fwd_bwd(d)
+    dW1 = out["d_lm_head"].clone()
+    colsum = dW1.double().sum(dim=0)
+    colabs = dW1.double().abs().sum(dim=0)
+    assert float((colsum.abs() / colabs.clamp_min(1e-30)).max()) < 1e-3
+    lhs = float((dW1.double() * d["lm_head"].double()).sum())
+    rhs = float((out["d_hidden"].double() * d["hidden"].double()).sum())
+    assert abs(lhs - rhs) <= 2e-3 * max(abs(lhs), abs(rhs)) + 1e-9, (lhs, rhs)
+    again = run_fwd_bwd(d)
+    assert torch.equal(again["d_lm_head"], dW1), "dW not reproducible"
+    del out, again, d, dW1
+    torch.cuda.empty_cache()
