@@ -71,7 +71,9 @@ typedef enum {
   RZ_ERR_INVALID_ARG = -1, /* null required pointer, bad size or count     */
   RZ_ERR_UNSUPPORTED = -2, /* unknown dtype, H not a multiple of 64, ...    */
   RZ_ERR_WORKSPACE = -3,   /* workspace NULL, misaligned or too small      */
-  RZ_ERR_HIP = -4          /* a HIP launch or event call failed            */
+  RZ_ERR_HIP = -4,         /* a HIP launch or event call failed            */
+  RZ_ERR_SCRATCH = -5      /* sizes need more than the static scratch of an
+                              allocation-free entry point                   */
 } rz_status;
 
 typedef enum { RZ_DTYPE_F32 = 0, RZ_DTYPE_BF16 = 1 } rz_dtype;
@@ -256,6 +258,32 @@ rz_status rz_sample_tokens(const void* hidden, const void* lm_head,
                            int32_t* tokens, float* logmu, float* lse,
                            void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
+
+/* Bytes of the static device scratch of rz_sample_tokens_noalloc, per GPU. */
+#define RZ_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * rz_sample_tokens_noalloc -- rz_sample_tokens for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Arguments and outputs as
+ * rz_sample_tokens, without the workspace: the draw's scratch (the
+ * vocab-tile partials, the draw candidates and the target logits;
+ * rz_workspace_bytes_op(RZ_OP_SAMPLE, n_rows, 1, H, V, dt) bytes) lives in
+ * a static device array of RZ_NOALLOC_SCRATCH_BYTES on each GPU, which the
+ * library holds from its first use on that GPU until the process ends.
+ * Sizes that need more return RZ_ERR_SCRATCH before any HIP call (at
+ * V = 151936, more than about 3500 rows).  The call allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine) and its outputs are
+ * those of rz_sample_tokens bit for bit (the same kernels).  Every call on
+ * a GPU uses that GPU's one array: calls that may overlap on one GPU (other
+ * streams, other host threads) race on it and must be serialised by the
+ * caller.  Nothing in the array needs to start at zero.
+ */
+rz_status rz_sample_tokens_noalloc(const void* hidden, const void* lm_head,
+                                   const uint64_t* row_ids, int64_t n_rows,
+                                   int32_t H, int32_t V, rz_dtype dt,
+                                   uint64_t seed, int32_t* tokens, float* logmu,
+                                   float* lse, hipStream_t stream);
 
 /*
  * rz_diagnostics -- D3 and the k1 rollout-to-learner KL.

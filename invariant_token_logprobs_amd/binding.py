@@ -33,12 +33,13 @@ RZ_DEVERR_MX_SCALE = 8
 RZ_MX_FORMATS = {"mxfp4": 0, "mxfp8": 1}
 
 _STATUS = {0: "RZ_OK", -1: "RZ_ERR_INVALID_ARG", -2: "RZ_ERR_UNSUPPORTED",
-           -3: "RZ_ERR_WORKSPACE", -4: "RZ_ERR_HIP"}
+           -3: "RZ_ERR_WORKSPACE", -4: "RZ_ERR_HIP", -5: "RZ_ERR_SCRATCH"}
+RZ_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 EXPORTS = [
     "rz_workspace_bytes", "rz_workspace_bytes_op", "rz_status_string",
     "rz_token_logprobs", "rz_reinforce_zero_fwd_bwd", "rz_diagnostics",
-    "rz_score_centering_fwd_bwd", "rz_sample_tokens",
+    "rz_score_centering_fwd_bwd", "rz_sample_tokens", "rz_sample_tokens_noalloc",
     "rz_grad_norms", "rz_response_diagnostics", "rz_run_summary",
     "rz_dequantize_head", "rz_lora_augment", "rz_lora_merge_head",
     "rz_reinforce_zero_fwd_bwd_lora", "rz_token_logprobs_mx",
@@ -92,6 +93,9 @@ def load_library():
     lib.rz_sample_tokens.argtypes = [vp, vp, vp, i64, i32, i32, ctypes.c_int,
                                      ctypes.c_uint64, vp, vp, vp, vp, sz, vp]
     lib.rz_sample_tokens.restype = ctypes.c_int
+    lib.rz_sample_tokens_noalloc.argtypes = [vp, vp, vp, i64, i32, i32, ctypes.c_int,
+                                             ctypes.c_uint64, vp, vp, vp, vp]
+    lib.rz_sample_tokens_noalloc.restype = ctypes.c_int
     lib.rz_grad_norms.argtypes = [vp, i64, i32, vp, i32, vp, vp, sz, vp]
     lib.rz_grad_norms.restype = ctypes.c_int
     lib.rz_response_diagnostics.argtypes = [vp, vp, vp, vp, i64, i32, vp, vp,
@@ -291,6 +295,39 @@ def sample_tokens(hidden, lm_head, row_ids, seed: int, *, want_lse: bool = False
                                 _stream(stream)),
            "rz_sample_tokens")
     return (tokens, logmu, lse) if want_lse else (tokens, logmu)
+
+
+def sample_tokens_noalloc(hidden, lm_head, row_ids, seed: int, *, out=None,
+                          want_lse: bool = False, stream=None):
+    """rz_sample_tokens_noalloc: the draw with the library's static scratch
+    and no workspace.  out: optional (tokens int32, logmu float32[, lse])
+    tensors to write into, so a caller that must not allocate passes its
+    own.  Returns (tokens, logmu[, lse])."""
+    torch = _torch()
+    lib = load_library()
+    dt = _dtype_code(hidden)
+    _need(hidden, "hidden", None, 2)
+    dev = hidden.device
+    _need(lm_head, "lm_head", hidden.dtype, 2, dev)
+    _need(row_ids, "row_ids", torch.int64, 1, dev)
+    N, H = hidden.shape
+    V = lm_head.shape[0]
+    if lm_head.shape[1] != H or row_ids.shape[0] != N:
+        raise RzError("shape mismatch between hidden, lm_head and row_ids")
+    if not 0 <= int(seed) < 2 ** 64:
+        raise RzError("seed must be in [0, 2**64)")
+    if out is None:
+        out = (torch.empty(N, dtype=torch.int32, device=dev),
+               torch.empty(N, dtype=torch.float32, device=dev),
+               torch.empty(N, dtype=torch.float32, device=dev) if want_lse else None)
+    tokens, logmu = out[0], out[1]
+    lse = out[2] if len(out) > 2 else None
+    _check(lib.rz_sample_tokens_noalloc(_ptr(hidden), _ptr(lm_head), _ptr(row_ids), N,
+                                        H, V, dt, ctypes.c_uint64(int(seed)),
+                                        _ptr(tokens), _ptr(logmu), _ptr(lse),
+                                        _stream(stream)),
+           "rz_sample_tokens_noalloc")
+    return (tokens, logmu, lse) if lse is not None else (tokens, logmu)
 
 
 def _learner_step(fn, op, what, hidden, lm_head, tokens, logmu, mask, cu_rows,

@@ -6,10 +6,14 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "../../include/rz.h"
 #include "rz_internal.h"
+
+// Scratch of rz_sample_tokens_noalloc: RZ_NOALLOC_SCRATCH_BYTES per GPU.
+static __device__ __align__(256) char scratch[RZ_NOALLOC_SCRATCH_BYTES];
 
 namespace rz {
 namespace {
@@ -243,6 +247,32 @@ hipEvent_t take_event() {
   return e;
 }
 
+// ---- the allocation-free draw's scratch (rz_sample_tokens_noalloc) ----
+// `scratch` (file scope, above) is one static device array per GPU, held
+// until the process ends.  In host code its name is a host-side stand-in,
+// never a device address, so the device address is looked up once per
+// device (with that device current) and kept, and only that address is
+// ever handed to kernels.
+constexpr size_t kScratchBytes = (size_t)RZ_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+rz_status scratch_on_current_device(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return RZ_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return RZ_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+      return RZ_ERR_HIP;
+    g_scratch_ptr[dev] = static_cast<char*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return RZ_OK;
+}
+
 }  // namespace
 
 bool Timer::on() { return g_timer.on; }
@@ -276,6 +306,7 @@ const char* rz_status_string(rz_status s) {
     case RZ_ERR_UNSUPPORTED: return "unsupported dtype or size";
     case RZ_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case RZ_ERR_HIP: return "HIP launch or event failure";
+    case RZ_ERR_SCRATCH: return "sizes exceed the static scratch of the allocation-free call";
   }
   return "unknown status";
 }
@@ -380,12 +411,11 @@ rz_status rz_response_diagnostics(const float* logpi, const float* logmu,
   return RZ_OK;
 }
 
-rz_status rz_sample_tokens(const void* hidden, const void* lm_head,
-                           const uint64_t* row_ids, int64_t n_rows, int32_t H,
-                           int32_t V, rz_dtype dt, uint64_t seed,
-                           int32_t* tokens, float* logmu, float* lse,
-                           void* workspace, size_t workspace_bytes,
-                           hipStream_t stream) {
+// Host-side checks of the draw (n_rows = 0 is checked by the caller).
+static rz_status sample_args_ok(const void* hidden, const void* lm_head,
+                                const uint64_t* row_ids, int64_t n_rows,
+                                int32_t H, int32_t V, rz_dtype dt,
+                                const int32_t* tokens, const float* logmu) {
   if (n_rows < 0 || n_rows > RZ_MAX_ROWS) return RZ_ERR_INVALID_ARG;
   if (dt != RZ_DTYPE_F32 && dt != RZ_DTYPE_BF16) return RZ_ERR_UNSUPPORTED;
   if (H <= 0 || V <= 0) return RZ_ERR_INVALID_ARG;
@@ -394,13 +424,16 @@ rz_status rz_sample_tokens(const void* hidden, const void* lm_head,
   if (!hidden || !lm_head || !row_ids || !tokens || !logmu)
     return RZ_ERR_INVALID_ARG;
   if (misaligned(hidden, lm_head)) return RZ_ERR_INVALID_ARG;
-  Carver meas{nullptr};
-  const size_t need = carve_smp(meas, n_rows, V, nullptr);
-  rz_status st = ws_check(workspace, workspace_bytes, need);
-  if (st != RZ_OK) return st;
+  return RZ_OK;
+}
 
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  Carver c{reinterpret_cast<char*>(workspace)};
+// The draw's launch sequence over scratch carved by carve_smp from ws.
+static rz_status sample_core(const void* hidden, const void* lm_head,
+                             const uint64_t* row_ids, int64_t n_rows, int32_t H,
+                             int32_t V, rz_dtype dt, uint64_t seed,
+                             int32_t* tokens, float* logmu, float* lse,
+                             char* ws, hipStream_t s) {
+  Carver c{ws};
   SmpWs w;
   carve_smp(c, n_rows, V, &w);
   const int nt = (V + kVocabTile - 1) / kVocabTile;
@@ -415,6 +448,40 @@ rz_status rz_sample_tokens(const void* hidden, const void* lm_head,
   RZ_TRY(launch_lse_merge(w.partials, n_rows, nt, rows, w.ztgt, tokens, V,
                           lse, logmu, nullptr, nullptr, nullptr, s));
   return RZ_OK;
+}
+
+rz_status rz_sample_tokens(const void* hidden, const void* lm_head,
+                           const uint64_t* row_ids, int64_t n_rows, int32_t H,
+                           int32_t V, rz_dtype dt, uint64_t seed,
+                           int32_t* tokens, float* logmu, float* lse,
+                           void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  rz_status st = sample_args_ok(hidden, lm_head, row_ids, n_rows, H, V, dt,
+                                tokens, logmu);
+  if (st != RZ_OK || n_rows == 0) return st;
+  Carver meas{nullptr};
+  const size_t need = carve_smp(meas, n_rows, V, nullptr);
+  st = ws_check(workspace, workspace_bytes, need);
+  if (st != RZ_OK) return st;
+  return sample_core(hidden, lm_head, row_ids, n_rows, H, V, dt, seed, tokens,
+                     logmu, lse, reinterpret_cast<char*>(workspace), stream);
+}
+
+rz_status rz_sample_tokens_noalloc(const void* hidden, const void* lm_head,
+                                   const uint64_t* row_ids, int64_t n_rows,
+                                   int32_t H, int32_t V, rz_dtype dt,
+                                   uint64_t seed, int32_t* tokens, float* logmu,
+                                   float* lse, hipStream_t stream) {
+  rz_status st = sample_args_ok(hidden, lm_head, row_ids, n_rows, H, V, dt,
+                                tokens, logmu);
+  if (st != RZ_OK || n_rows == 0) return st;
+  Carver meas{nullptr};
+  if (carve_smp(meas, n_rows, V, nullptr) > kScratchBytes) return RZ_ERR_SCRATCH;
+  char* ws = nullptr;
+  st = scratch_on_current_device(&ws);
+  if (st != RZ_OK) return st;
+  return sample_core(hidden, lm_head, row_ids, n_rows, H, V, dt, seed, tokens,
+                     logmu, lse, ws, stream);
 }
 
 rz_status rz_token_logprobs(const void* hidden, const void* lm_head,
