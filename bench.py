@@ -2,7 +2,7 @@
 per step on the Qwen3-4B tool-use shape, on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--mode learner|sample|diag|mx] [--lora-rank R]
+                    [--mode learner|sample|diag|mx|ceiling] [--lora-rank R]
 
 A step is one rz_reinforce_zero_fwd_bwd call over the whole synthetic batch
 (inputs already resident in HBM).  Prints ONE JSON line with the throughput
@@ -443,6 +443,44 @@ def bench_diag(args, torch, rz, synth, dev):
     print(json.dumps(line), flush=True)
 
 
+def bench_ceiling(args, torch, rz, dev):
+    """The matrix cores' own ceiling on this part (rz_calibrate_mfma): the
+    learner GEMMs' MFMA, four waves per CU with a wave's 128 x 128 block of
+    accumulators, no global traffic; operands from registers or from LDS
+    (the GEMM's read volume), random-looking or zero values.  Each variant
+    runs args.warmup untimed launches and args.steps timed ones of about
+    30 ms, back to back on one stream."""
+    ncu = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.empty(ncu * 256, dtype=torch.float32, device=dev)
+    iters = 16384
+    stream = torch.cuda.current_stream()
+    res = {}
+    for lds in (0, 1):
+        for data in (1, 0):
+            key = f"{'lds' if lds else 'registers'}_{'random' if data else 'zero'}"
+            for _ in range(args.warmup):
+                rz.calibrate_mfma(data, lds, ncu, iters, sink)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            flop = 0.0
+            for _ in range(args.steps):
+                flop += rz.calibrate_mfma(data, lds, ncu, iters, sink)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            tf = flop / (ms * 1e-3) / 1e12
+            res[key] = {"TFLOP/s": round(tf, 1), "frac_of_peak": round(tf / PEAK_TFLOPS["bf16"], 4),
+                        "ms_per_launch": round(ms / args.steps, 3)}
+            log(f"{key}: {tf:.1f} TFLOP/s = {tf / PEAK_TFLOPS['bf16']:.3f} of peak "
+                f"({ms / args.steps:.2f} ms per launch)")
+    line = {"metric": "bf16 MFMA ceiling (no global traffic), TFLOP/s",
+            "mode": "ceiling", "unit": "TFLOP/s", "peak": PEAK_TFLOPS["bf16"],
+            "workgroups": ncu, "iters": iters, "steps": args.steps,
+            "warmup": args.warmup, "variants": res}
+    print(json.dumps(line), flush=True)
+
+
 def bench_mx(args, torch, rz, synth, dev):
     """The release-precision head: rz_dequantize_head expanding the Qwen3-4B
     head (V 151936, H 2560) from --mx-format storage to bf16."""
@@ -514,7 +552,7 @@ def main():
     ap.add_argument("--cpu-valid", type=int, default=3072,
                     help="valid rows in the oracle's CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=("learner", "sample", "diag", "mx"),
+    ap.add_argument("--mode", choices=("learner", "sample", "diag", "mx", "ceiling"),
                     default="learner",
                     help="learner: the fused fwd/bwd step (the headline); "
                          "sample: the rollout-side draw + record at decode size; "
@@ -539,6 +577,10 @@ def main():
                          "hidden states and head (same kernels, launches and "
                          "addresses; only the values the matrix cores see differ), "
                          "to show what the data costs in power; not a headline figure")
+    ap.add_argument("--tokens", choices=("uniform", "zipf"), default="uniform",
+                    help="learner mode: the sampled tokens' law (zipf: Zipf(1.1) "
+                         "over the vocabulary, the most frequent token on ~8%% "
+                         "of the rows)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run one plain 1 GiB device "
                          "copy so a counter run can scale its byte counters")
@@ -559,8 +601,10 @@ def main():
         return bench_diag(args, torch, rz, synth, dev)
     if args.mode == "mx":
         return bench_mx(args, torch, rz, synth, dev)
+    if args.mode == "ceiling":
+        return bench_ceiling(args, torch, rz, dev)
     t0 = time.time()
-    b = synth.make_workload(args.workload)
+    b = synth.make_workload(args.workload, tokens=args.tokens)
     log(f"workload {b.name}: N={b.N} B={b.B} valid={b.n_valid} H={b.H} V={b.V} "
         f"({time.time() - t0:.1f}s to draw)")
 
@@ -693,6 +737,7 @@ def main():
         "config": {"workload": b.name, "hidden": b.H, "vocab": b.V,
                    "responses": b.B, "rows": b.N, "valid_tokens": nv,
                    "masked_frac": round(1 - nv / b.N, 4), "lag_sigma": b.sigma,
+                   "tokens": args.tokens,
                    **({"lora_rank": r, "lora_scale": LORA_SCALE} if r else {})},
         "rows_per_s": round(b.N * args.steps / (te - ts), 1),
         "step_ms_median": round(float(np.median(step_ms)), 3),

@@ -497,6 +497,23 @@ int rz_timing_num_kernels(void);
 const char* rz_timing_kernel_name(int k);
 rz_status rz_timing_read(double* total_ms, int64_t* launches, int reset);
 
+/*
+ * Matrix-core ceiling (measurement support, not part of the method).
+ * rz_calibrate_mfma launches n_workgroups workgroups of four waves (one per
+ * SIMD, as the GEMM tile); each wave issues iters x 128 MFMAs of the
+ * learner GEMMs' instruction (v_mfma_f32_32x32x16_bf16, 32768 FLOP each)
+ * into sixteen 32 x 32 accumulators, with operands kept in registers
+ * (from_lds = 0) or read from LDS before every sixteen MFMAs, as the GEMM
+ * reads them (from_lds = 1), and no global memory traffic.  data = 1 gives
+ * the operands random-looking bf16 values, data = 0 all zeros.  FLOP per
+ * launch: n_workgroups x 4 x iters x 128 x 32768.  sink [n_workgroups x 256]
+ * fp32 (device) receives the accumulator sums.  Timed by the caller (HIP
+ * events on `stream`); rocprofv3 counters of the launch give the clock and
+ * the matrix cores' busy share.
+ */
+rz_status rz_calibrate_mfma(int32_t data, int32_t from_lds, int32_t n_workgroups,
+                            int64_t iters, float* sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

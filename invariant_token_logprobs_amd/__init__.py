@@ -12,7 +12,7 @@ from .binding import (  # noqa: F401
     reinforce_zero_fwd_bwd_lora, token_logprobs_mx, sample_tokens_mx, RZ_DTYPE_F32, RZ_OP_DIAGNOSTICS,
     RZ_OP_FWD_BWD, RZ_OP_GRAD_NORMS, RZ_OP_SAMPLE, RZ_OP_TOKEN_LOGPROBS,
     RZ_OP_SCORE_CENTERING, score_centering_fwd_bwd, workspace_bytes_common,
-    sample_tokens_noalloc, RZ_NOALLOC_SCRATCH_BYTES,
+    sample_tokens_noalloc, RZ_NOALLOC_SCRATCH_BYTES, calibrate_mfma,
     RunTracker, RzError, Workspace, dequantize_head, diagnostics, grad_norms,
     library_path,
     load_library, reinforce_zero_fwd_bwd, response_diagnostics, run_summary,

@@ -45,7 +45,7 @@ EXPORTS = [
     "rz_reinforce_zero_fwd_bwd_lora", "rz_token_logprobs_mx",
     "rz_sample_tokens_mx",
     "rz_timing_enable", "rz_timing_num_kernels", "rz_timing_kernel_name",
-    "rz_timing_read",
+    "rz_timing_read", "rz_calibrate_mfma",
 ]
 
 
@@ -130,6 +130,8 @@ def load_library():
     lib.rz_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double),
                                    ctypes.POINTER(ctypes.c_int64), ctypes.c_int]
     lib.rz_timing_read.restype = ctypes.c_int
+    lib.rz_calibrate_mfma.argtypes = [i32, i32, i32, i64, vp, vp]
+    lib.rz_calibrate_mfma.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -733,3 +735,18 @@ def timing_read(reset: bool = True) -> dict:
     _check(lib.rz_timing_read(ms, cnt, 1 if reset else 0), "rz_timing_read")
     return {lib.rz_timing_kernel_name(k).decode(): (ms[k], cnt[k])
             for k in range(n)}
+
+
+def calibrate_mfma(data: bool, from_lds: bool, n_workgroups: int, iters: int,
+                   sink, stream=None):
+    """rz_calibrate_mfma (measurement support): launch the matrix-core
+    ceiling kernel; returns the FLOP it issues."""
+    torch = _torch()
+    _need(sink, "sink", torch.float32, 1)
+    if sink.numel() < n_workgroups * 256:
+        raise RzError("sink must hold n_workgroups * 256 floats")
+    lib = load_library()
+    _check(lib.rz_calibrate_mfma(1 if data else 0, 1 if from_lds else 0,
+                                 n_workgroups, iters, _ptr(sink), _stream(stream)),
+           "rz_calibrate_mfma")
+    return float(n_workgroups) * 4 * iters * 128 * 32768

@@ -21,7 +21,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "librz.so")
-SOURCES = ["rz_kernels.hip", "rz_api.hip"]
+SOURCES = ["rz_kernels.hip", "rz_api.hip", "rz_calib.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

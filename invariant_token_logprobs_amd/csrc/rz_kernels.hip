@@ -358,15 +358,19 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
   }
   if constexpr (kStoreE && sizeof(T) == 2) {
     // 16-byte row chunks: 32 lanes cover one 512-byte tile row.  Columns
-    // >= V hold 0; rows >= M and columns >= Vpad are not stored.
+    // >= V hold 0; rows >= M and columns >= Vpad are not stored.  The e
+    // stream (2 bytes per logit) is read back only by the dz rescale, long
+    // after: non-temporal stores keep it from evicting the operand panels
+    // that the co-resident tiles share in L2.
 #pragma unroll 4
     for (int it = 0; it < 32; ++it) {
       const int idx = it * 256 + tid;
       const int R = idx >> 5, k = idx & 31;
       const int col = n0 + k * 8;
       if (m0 + R < M && col < a.Vpad)
-        *reinterpret_cast<u32x4*>(e + (int64_t)(m0 + R) * a.lde + col) =
-            *reinterpret_cast<const u32x4*>(lds + e_stage_off(R, k));
+        __builtin_nontemporal_store(
+            *reinterpret_cast<const u32x4*>(lds + e_stage_off(R, k)),
+            reinterpret_cast<u32x4*>(e + (int64_t)(m0 + R) * a.lde + col));
     }
   }
 }
@@ -1382,8 +1386,9 @@ __global__ __launch_bounds__(256) void k_dz_scale(
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int t = r0 + tr + i;
-        if (wave_col(b) < Vpad && t < R)
-          x[b][i] = *reinterpret_cast<const u32x4*>(dz + (int64_t)t * ldz + col);
+        if (wave_col(b) < Vpad && t < R)  // read once: non-temporal
+          x[b][i] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4*>(dz + (int64_t)t * ldz + col));
       }
     }
   }
@@ -1422,9 +1427,11 @@ __global__ __launch_bounds__(256) void k_dz_scale(
                 uint16_t, (T)(f * ((float)e[2 * w + 1] * kEUnscale)));
             y[w] = lo | (hi << 16);
           }
-          *reinterpret_cast<u32x4*>(p) = u32x4{y[0], y[1], y[2], y[3]};
+          // dz (10 GB per chunk) reaches the GEMMs from HBM in any case
+          __builtin_nontemporal_store(u32x4{y[0], y[1], y[2], y[3]},
+                                      reinterpret_cast<u32x4*>(p));
         } else {
-          *reinterpret_cast<u32x4*>(p) = u32x4{0u, 0u, 0u, 0u};
+          __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u}, reinterpret_cast<u32x4*>(p));
         }
       }
     }
