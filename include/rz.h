@@ -272,7 +272,7 @@ rz_status rz_sample_tokens(const void* hidden, const void* lm_head,
  * a static device array of RZ_NOALLOC_SCRATCH_BYTES on each GPU, which the
  * library holds from its first use on that GPU until the process ends.
  * Sizes that need more return RZ_ERR_SCRATCH before any HIP call (at
- * V = 151936, more than about 3500 rows).  The call allocates nothing (no
+ * V = 151936, more than about 2800 rows).  The call allocates nothing (no
  * hipMalloc, hipFree or allocating library routine) and its outputs are
  * those of rz_sample_tokens bit for bit (the same kernels).  Every call on
  * a GPU uses that GPU's one array: calls that may overlap on one GPU (other

@@ -67,6 +67,7 @@ size_t carve_tlp(Carver& c, int64_t n, int32_t V, TlpWs* w) {
 struct SmpWs {
   float2* partials;
   float2* cand;
+  float* candz;
   float* ztgt;
 };
 size_t carve_smp(Carver& c, int64_t n, int32_t V, SmpWs* w) {
@@ -74,6 +75,7 @@ size_t carve_smp(Carver& c, int64_t n, int32_t V, SmpWs* w) {
   SmpWs t;
   t.partials = c.take<float2>(sizeof(float2) * (size_t)nt * (size_t)n);
   t.cand = c.take<float2>(sizeof(float2) * (size_t)nt * (size_t)n);
+  t.candz = c.take<float>(sizeof(float) * (size_t)nt * (size_t)n);
   t.ztgt = c.take<float>(sizeof(float) * (size_t)n);
   if (w) *w = t;
   return c.off;
@@ -438,13 +440,12 @@ static rz_status sample_core(const void* hidden, const void* lm_head,
   carve_smp(c, n_rows, V, &w);
   const int nt = (V + kVocabTile - 1) / kVocabTile;
   DevRows rows{nullptr, 0, (int)n_rows};
-  // the logits GEMM with the draw in its epilogue, then the draw's merge
+  // the logits GEMM with the draw in its epilogue (the winning column's
+  // logit comes along), then the draw's merge
   RZ_TRY(launch_fwd_sample(dt, hidden, n_rows, lm_head, H, V, row_ids, seed,
-                           w.partials, w.cand, n_rows, s));
-  RZ_TRY(launch_draw_merge(w.cand, n_rows, nt, n_rows, tokens, s));
-  // the record: rz_token_logprobs' own target and merge kernels
-  RZ_TRY(launch_target_logit(dt, hidden, (int64_t)H * esize(dt), nullptr,
-                             rows, lm_head, H, V, tokens, w.ztgt, s));
+                           w.partials, w.cand, w.candz, n_rows, s));
+  RZ_TRY(launch_draw_merge(w.cand, w.candz, n_rows, nt, n_rows, tokens, w.ztgt, s));
+  // the record: rz_token_logprobs' own merge kernel
   RZ_TRY(launch_lse_merge(w.partials, n_rows, nt, rows, w.ztgt, tokens, V,
                           lse, logmu, nullptr, nullptr, nullptr, s));
   return RZ_OK;
@@ -757,7 +758,7 @@ rz_status rz_token_logprobs_mx(const void* hidden, const uint8_t* codes,
   if (fused) {
     RZ_TRY(launch_fwd_mx(fmt, hidden, n_rows, codes, scales, H, V, tokens,
                          w.partials, n_rows, w.ztgt, nullptr, 0, nullptr,
-                         err_flag, s));
+                         nullptr, err_flag, s));
   } else {
     void* Wb = c.take<char>(2 * (size_t)V * (size_t)H);
     RZ_TRY(launch_mx_dequant(fmt, codes, scales, (int64_t)V * (H / 32), Wb,
@@ -797,20 +798,15 @@ rz_status rz_sample_tokens_mx(const void* hidden, const uint8_t* codes,
   if (fused) {
     RZ_TRY(launch_fwd_mx(fmt, hidden, n_rows, codes, scales, H, V, nullptr,
                          w.partials, n_rows, nullptr, row_ids, seed, w.cand,
-                         err_flag, s));
-    RZ_TRY(launch_draw_merge(w.cand, n_rows, nt, n_rows, tokens, s));
-    RZ_TRY(launch_target_logit_mx(fmt, hidden, n_rows, codes, scales, H, V,
-                                  tokens, w.ztgt, s));
+                         w.candz, err_flag, s));
   } else {
     void* Wb = c.take<char>(2 * (size_t)V * (size_t)H);
     RZ_TRY(launch_mx_dequant(fmt, codes, scales, (int64_t)V * (H / 32), Wb,
                              err_flag, s));
     RZ_TRY(launch_fwd_sample(RZ_DTYPE_BF16, hidden, n_rows, Wb, H, V, row_ids,
-                             seed, w.partials, w.cand, n_rows, s));
-    RZ_TRY(launch_draw_merge(w.cand, n_rows, nt, n_rows, tokens, s));
-    RZ_TRY(launch_target_logit(RZ_DTYPE_BF16, hidden, (int64_t)H * 2, nullptr,
-                               rows, Wb, H, V, tokens, w.ztgt, s));
+                             seed, w.partials, w.cand, w.candz, n_rows, s));
   }
+  RZ_TRY(launch_draw_merge(w.cand, w.candz, n_rows, nt, n_rows, tokens, w.ztgt, s));
   RZ_TRY(launch_lse_merge(w.partials, n_rows, nt, rows, w.ztgt, tokens, V,
                           lse, logmu, nullptr, nullptr, nullptr, s));
   return RZ_OK;

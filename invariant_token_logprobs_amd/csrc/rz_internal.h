@@ -31,7 +31,6 @@ enum KernelId {
   K_SORT_SCATTER,    //   the stable scatter
   K_DW_FIX,          // dW one-hot fix-up over pieces of the sorted list
   K_DW_FIX_SPAN,     //   runs crossing pieces
-  K_TARGET_LOGIT,    // z[t, a_t] for the gather
   K_FWD_SAMPLE,      // rollout-side logits GEMM with the draw in the epilogue
   K_DRAW_MERGE,      // per-row best draw over the vocab tiles
   K_GRAD_NORM,       // run-level: float64 sums of squares per chunk
@@ -68,18 +67,18 @@ hipError_t launch_fwd_logits(int dt, const void* hidden, int64_t lda_bytes,
                              const int* row_tokens, float2* partials,
                              int64_t ldp, float* ztgt, void* e, int64_t lde,
                              int Vpad, hipStream_t s);
-hipError_t launch_target_logit(int dt, const void* hidden, int64_t lda_bytes,
-                               const int* a_rows, DevRows rows,
-                               const void* lm_head, int H, int V,
-                               const int* row_tokens, float* ztgt,
-                               hipStream_t s);
+// The logits GEMM with the draw in its epilogue: per (vocab tile, row) the
+// best (z + g, index) in cand and that column's z in candz.
 hipError_t launch_fwd_sample(int dt, const void* hidden, int64_t n,
                              const void* lm_head, int H, int V,
                              const uint64_t* row_ids, uint64_t seed,
-                             float2* partials, float2* cand, int64_t ldp,
+                             float2* partials, float2* cand, float* candz,
+                             int64_t ldp, hipStream_t s);
+// The draw's winner per row (tokens) and its logit (ztgt, the record's
+// z[a_t]).
+hipError_t launch_draw_merge(const float2* cand, const float* candz, int64_t ldp,
+                             int nt, int64_t n, int* tokens, float* ztgt,
                              hipStream_t s);
-hipError_t launch_draw_merge(const float2* cand, int64_t ldp, int nt, int64_t n,
-                             int* tokens, hipStream_t s);
 hipError_t launch_mx_dequant(int fmt, const uint8_t* codes, const uint8_t* scales,
                              int64_t nblk, void* out, int* err, hipStream_t s);
 constexpr int kLoraCols = 64;  // LoRA: largest rank and u block width
@@ -98,11 +97,8 @@ hipError_t launch_fwd_mx(int fmt, const void* hidden, int64_t n,
                          const uint8_t* codes, const uint8_t* scales, int H,
                          int V, const int* row_tokens, float2* partials,
                          int64_t ldp, float* ztgt, const uint64_t* row_ids,
-                         uint64_t seed, float2* cand, int* err, hipStream_t s);
-hipError_t launch_target_logit_mx(int fmt, const void* hidden, int64_t n,
-                                  const uint8_t* codes, const uint8_t* scales,
-                                  int H, int V, const int* row_tokens, float* ztgt,
-                                  hipStream_t s);
+                         uint64_t seed, float2* cand, float* candz, int* err,
+                         hipStream_t s);
 size_t norm_partials(int64_t n);
 hipError_t launch_grad_norm(const float* x, int64_t n, double* partials,
                             float* norm, hipStream_t s);

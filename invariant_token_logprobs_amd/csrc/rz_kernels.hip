@@ -65,6 +65,9 @@ struct FwdArgs {
   const uint64_t* row_ids;  // sampling call only: the rows' identities
   uint64_t seed;
   float2* cand;           // sampling call only: [nt][ldp] (best z + g, index)
+  float* candz;           // sampling call only: [nt][ldp] the best column's z
+  const int* row_tokens;  // logits calls: a_t by list position (nullable)
+  float* ztgt;            // logits calls: z[t, a_t] by list position
   const uint8_t* wcodes;  // MX head only: codes and E8M0 scales of W
   const uint8_t* wscales;
   int H;                  // MX head only: hidden size
@@ -220,6 +223,28 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
   // column of register r in block ni: cbase + 32 ni + 8 (r / 4) + (r % 4)
   const int cbase = n0 + wn * 128 + 4 * half;
 
+  // The gather: z[t, a_t] straight from the accumulator that holds it, in the
+  // one tile whose columns contain a_t (one lane of the workgroup), so
+  // log pi = z[a_t] - lse subtracts two results of one accumulation.  The
+  // branch is taken by about one row in six hundred per tile.
+  if (a.row_tokens) {
+#pragma unroll
+    for (int mi = 0; mi < TM; ++mi) {
+      const int m = m0 + wm * RW + mi * 32 + l32;
+      const int tok = m < M ? a.row_tokens[rc.base + m] : -1;
+      const int off = tok - cbase;  // this lane's columns: 32 ni + 8 q + j
+      if (tok >= 0 && tok < a.V && off >= 0 && off < 128 && (off & 4) == 0) {
+        const int want = ((off >> 5) << 4) | (((off >> 3) & 3) << 2) | (off & 3);
+        float z = 0.f;
+#pragma unroll
+        for (int ni = 0; ni < kTN; ++ni)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) z = want == ni * 16 + r ? acc[mi][ni][r] : z;
+        a.ztgt[rc.base + m] = z;
+      }
+    }
+  }
+
   // Tile row maxima.  Columns >= V (last vocab tile only) hold a copy of
   // column V - 1 (the main loop reads B rows >= N from row N - 1), which
   // cannot change a maximum, so no mask is needed here.
@@ -300,6 +325,7 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
     // and waves meet does not matter.
     float* wbs = reinterpret_cast<float*>(lds + kEpi + 16 * BM);  // [2][BM]
     int* wbv = reinterpret_cast<int*>(lds + kEpi + 24 * BM);      // [2][BM]
+    float* wbz = reinterpret_cast<float*>(lds + kEpi + 32 * BM);  // [2][BM]
     const uint32_t k0 = (uint32_t)a.seed, k1 = (uint32_t)(a.seed >> 32);
     static_for<0, TM>([&](auto mi_c) {
       constexpr int mi = decltype(mi_c)::value;
@@ -308,6 +334,7 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
       const uint64_t id = m0 + R < M ? a.row_ids[rc.base + m0 + R] : 0;
       float bs = -__builtin_inff();
       int bv = 0x7fffffff;
+      float bz = 0.f;  // the best column's logit: the record's z[a_t]
       static_for<0, kTN * 4>([&](auto nq_c) {
         constexpr int ni = decltype(nq_c)::value / 4, q = decltype(nq_c)::value % 4;
         const int c0 = cbase + ni * 32 + 8 * q;  // multiple of 4
@@ -318,22 +345,27 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
         static_for<0, 4>([&](auto j_c) {
           constexpr int j = decltype(j_c)::value;
           const int v = c0 + j;
-          float sc = acc[mi][ni][4 * q + j] + gumbel_of_bits(x[j]);
+          const float z = acc[mi][ni][4 * q + j];
+          float sc = z + gumbel_of_bits(x[j]);
           sc = v < a.V ? sc : -__builtin_inff();
           const bool take = sc > bs;
           bs = take ? sc : bs;
           bv = take ? v : bv;
+          bz = take ? z : bz;
         });
       });
       const float os = __shfl_xor(bs, 32, 64);
       const int ov = __shfl_xor(bv, 32, 64);
+      const float oz = __shfl_xor(bz, 32, 64);
       if (draw_better(os, ov, bs, bv)) {
         bs = os;
         bv = ov;
+        bz = oz;
       }
       if (half == 0) {
         wbs[wn * BM + R] = bs;
         wbv[wn * BM + R] = bv;
+        wbz[wn * BM + R] = bz;
       }
     });
     __syncthreads();
@@ -341,12 +373,15 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
     if (tid < BM && m < M) {
       float bs = wbs[tid];
       int bv = wbv[tid];
+      float bz = wbz[tid];
       if (draw_better(wbs[BM + tid], wbv[BM + tid], bs, bv)) {
         bs = wbs[BM + tid];
         bv = wbv[BM + tid];
+        bz = wbz[BM + tid];
       }
-      a.cand[(int64_t)tc.tn * a.ldp + rc.base + m] =
-          make_float2(bs, __builtin_bit_cast(float, bv));
+      const int64_t o = (int64_t)tc.tn * a.ldp + rc.base + m;
+      a.cand[o] = make_float2(bs, __builtin_bit_cast(float, bv));
+      a.candz[o] = bz;
     }
   }
   __syncthreads();
@@ -379,7 +414,7 @@ template <typename T, bool kStoreE, bool kSample = false>
 __global__ RZ_GEMM_ATTR void k_fwd_logits(FwdArgs a) {
   // [0, 128 KB): main-loop stages, then (learner call, bf16) the e tile;
   // then the epilogue arrays, [2][256] floats each
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes + (kSample ? 8192 : 4096)];
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes + (kSample ? 10240 : 4096)];
   fwd_logits_body<T, kStoreE, kSample, kTM>(a, lds);
 }
 
@@ -411,94 +446,6 @@ __attribute__((amdgpu_waves_per_eu(kFmt == 0 ? 3 : 2, kFmt == 0 ? 3 : 2)))
 void k_fwd_logits64_mx(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[MxStage<kFmt>::kLds];
   fwd_logits_body<bf16, false, kSample, 1, kFmt>(a, lds);
-}
-
-// z[t, a_t] by the logits GEMM's own arithmetic.  One wave takes 32 listed
-// rows and runs the forward tile's MFMA sequence -- the same instruction,
-// the head's fragment as its first operand and the hidden row's as its
-// second (the forward's swapped order), 16-byte fragments of K steps
-// k = 0, 1, 2, ... in order, fp32 accumulators from 0 -- on the 32 x 32
-// block whose first operand rows are the 32 rows' token rows of the head
-// and whose second operand rows are their hidden states.  An output element
-// depends only on its own two operand rows, so the block's diagonal is
-// z[t, a_t] bit for bit as the logits GEMM computes it (in every tile
-// form), and log pi = z[a_t] - lse subtracts two results of one
-// accumulation.  kWFmt >= 0 makes the head's fragments from MX codes by the
-// MX tile's exact conversions.  Rows with a token outside [0, V) run on
-// token 0 and are not stored (the merge flags them).  A row's value does not
-// depend on the other rows of its wave.
-template <typename T, int kWFmt = -1>
-__global__ __launch_bounds__(256) void k_target_mfma(
-    const char* __restrict__ hidden, int64_t lda, const int* __restrict__ a_rows,
-    DevRows rows, const char* __restrict__ lm_head,
-    const uint8_t* __restrict__ wcodes, const uint8_t* __restrict__ wscales,
-    int H, int V, const int* __restrict__ row_tokens, float* __restrict__ ztgt) {
-  const RowCount rc = to_rc(rows);
-  const int n = rc.get();
-  const int g0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 32;
-  if (g0 >= n) return;  // uniform per wave
-  const int lane = threadIdx.x & 63;
-  const int j = lane & 31, half = lane >> 5;
-  int p = g0 + j;
-  const bool live = p < n;
-  p = live ? p : n - 1;
-  const int64_t pos = rc.base + p;
-  int tok = row_tokens[pos];
-  const bool tok_ok = tok >= 0 && tok < V;
-  tok = tok_ok ? tok : 0;
-  const int64_t hrow = a_rows ? (int64_t)a_rows[pos] : pos;
-  const char* hp = hidden + hrow * lda;
-  const char* wp = lm_head + (int64_t)tok * H * (int64_t)sizeof(T);
-  const uint8_t* cp = nullptr;
-  const uint8_t* sp = nullptr;
-  if constexpr (kWFmt >= 0) {
-    cp = wcodes + (int64_t)tok * (kWFmt == 0 ? H / 2 : H);
-    sp = wscales + (int64_t)tok * (H / 32);
-  }
-  // the head's 16-byte fragment (8 values) at chunk c of the row
-  auto wfrag = [&](int c) -> u32x4 {
-    if constexpr (kWFmt < 0) {
-      return *reinterpret_cast<const u32x4*>(wp + (int64_t)c * 16);
-    } else {
-      const int code = sp[c >> 2];
-      u32x4 v;
-      if constexpr (kWFmt == 0)
-        v = fp4x8_to_bf16(*reinterpret_cast<const uint32_t*>(cp + (int64_t)c * 4),
-                          e8m0_scale(code));
-      else
-        v = fp8x8_to_bf16(*reinterpret_cast<const u32x2*>(cp + (int64_t)c * 8),
-                          e8m0_scale(code));
-      return mx_scale_ok(kWFmt, code) ? v
-                                      : u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
-    }
-  };
-  f32x16 acc;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  // K step s covers 32 bytes of each row; lane half h holds chunk 2 s + h
-  // (bf16: values 16 s + 8 h .. + 7; fp32: 8 s + 4 h .. + 3), as in the tile
-  const int nsteps = H * (int)sizeof(T) / 32;  // a multiple of 4
-  for (int s0 = 0; s0 < nsteps; s0 += 4) {
-    u32x4 fw[4], fh[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int c = 2 * (s0 + u) + half;
-      fw[u] = wfrag(c);
-      fh[u] = *reinterpret_cast<const u32x4*>(hp + (int64_t)c * 16);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) mfma_step(acc, fw[u], fh[u], (const T*)nullptr);
-  }
-  // lane l holds column j = l % 32 and rows 8 (r / 4) + 4 half + (r % 4):
-  // the diagonal element (j, j) is in the half with 4 half = j & 4, at
-  // register 4 (j / 8) + (j % 4)
-  if (live && tok_ok && ((j >> 2) & 1) == half) {
-    const int rr = 4 * (j >> 3) + (j & 3);
-    float z = acc[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) z = r == rr ? acc[r] : z;
-    ztgt[pos] = z;
-  }
 }
 
 // ===================================================================
@@ -581,21 +528,27 @@ __global__ __launch_bounds__(256) void k_lse_merge(
 
 // The draw's merge: per row (one wave), the best (score, index) over the
 // vocab tiles under draw_better's total order, so any meeting order of
-// lanes and tiles gives the same winner.
+// lanes and tiles gives the same winner; the winner's logit comes along as
+// the record's z[a_t].
 __global__ __launch_bounds__(256) void k_draw_merge(
-    const float2* __restrict__ cand, int64_t ldp, int nt, int64_t n,
-    int* __restrict__ tokens) {
+    const float2* __restrict__ cand, const float* __restrict__ candz, int64_t ldp,
+    int nt, int64_t n, int* __restrict__ tokens, float* __restrict__ ztgt) {
   const int64_t p = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int q = threadIdx.x & 63;
   if (p >= n) return;  // uniform per wave
   float bs = -__builtin_inff();
   int bv = 0x7fffffff;
+  float bz = 0.f;
   for (int t0 = q; t0 < nt; t0 += 64 * kMergeBatch) {
     float2 c[kMergeBatch];
+    float cz[kMergeBatch];
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j) {
       const int t = t0 + 64 * j;
-      if (t < nt) c[j] = cand[(int64_t)t * ldp + p];
+      if (t < nt) {
+        c[j] = cand[(int64_t)t * ldp + p];
+        cz[j] = candz[(int64_t)t * ldp + p];
+      }
     }
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j) {
@@ -603,6 +556,7 @@ __global__ __launch_bounds__(256) void k_draw_merge(
       if (t0 + 64 * j < nt && draw_better(c[j].x, v, bs, bv)) {
         bs = c[j].x;
         bv = v;
+        bz = cz[j];
       }
     }
   }
@@ -610,12 +564,17 @@ __global__ __launch_bounds__(256) void k_draw_merge(
   for (int o = 32; o >= 1; o >>= 1) {
     const float os = __shfl_xor(bs, o, 64);
     const int ov = __shfl_xor(bv, o, 64);
+    const float oz = __shfl_xor(bz, o, 64);
     if (draw_better(os, ov, bs, bv)) {
       bs = os;
       bv = ov;
+      bz = oz;
     }
   }
-  if (q == 0) tokens[p] = bv;
+  if (q == 0) {
+    tokens[p] = bv;
+    ztgt[p] = bz;
+  }
 }
 
 // ===================================================================
@@ -1913,34 +1872,17 @@ const char* kernel_name(int k) {
       "diag_partial", "diag_final", "transpose_w",  "transpose_h",
       "bwd_dh_gemm", "bwd_dw_gemm", "sort_hist",    "sort_scan",
       "sort_scatter", "dw_fix",     "dw_fix_span",
-      "target_logit", "fwd_sample_gemm", "draw_merge", "grad_norm",
+      "fwd_sample_gemm", "draw_merge", "grad_norm",
       "grad_norm_final", "resp_diag", "mx_dequant", "lora_u", "lora_cols",
       "lora_dh", "lora_da"};
   return (k >= 0 && k < K_NUM_KERNELS) ? names[k] : "?";
 }
 
-hipError_t launch_target_logit(int dt, const void* hidden, int64_t lda_bytes,
-                               const int* a_rows, DevRows rows,
-                               const void* lm_head, int H, int V,
-                               const int* row_tokens, float* ztgt,
-                               hipStream_t s) {
-  return timed(K_TARGET_LOGIT, s, [&] {
-    if (dt)
-      k_target_mfma<bf16><<<cdiv(rows.cap, 128), 256, 0, s>>>(
-          (const char*)hidden, lda_bytes, a_rows, rows, (const char*)lm_head,
-          nullptr, nullptr, H, V, row_tokens, ztgt);
-    else
-      k_target_mfma<float><<<cdiv(rows.cap, 128), 256, 0, s>>>(
-          (const char*)hidden, lda_bytes, a_rows, rows, (const char*)lm_head,
-          nullptr, nullptr, H, V, row_tokens, ztgt);
-  });
-}
-
 hipError_t launch_fwd_sample(int dt, const void* hidden, int64_t n,
                              const void* lm_head, int H, int V,
                              const uint64_t* row_ids, uint64_t seed,
-                             float2* partials, float2* cand, int64_t ldp,
-                             hipStream_t s) {
+                             float2* partials, float2* cand, float* candz,
+                             int64_t ldp, hipStream_t s) {
   FwdArgs a{};
   a.op = GemmOperands{(const char*)hidden, (int64_t)H * (dt ? 2 : 4), nullptr,
                       0, (const char*)lm_head, (int64_t)H * (dt ? 2 : 4), V};
@@ -1956,6 +1898,7 @@ hipError_t launch_fwd_sample(int dt, const void* hidden, int64_t n,
   a.row_ids = row_ids;
   a.seed = seed;
   a.cand = cand;
+  a.candz = candz;
   const int nblk = a.mt * a.nt;
   return timed(K_FWD_SAMPLE, s, [&] {
     if (small && n <= kBM64) {
@@ -1973,14 +1916,15 @@ hipError_t launch_fwd_sample(int dt, const void* hidden, int64_t n,
 
 // The forward of rz_token_logprobs_mx / rz_sample_tokens_mx on the 64-row
 // tile (host-known rows, n <= mx_rows64_max(sample), H % 128 == 0): the
-// target logits, then the logits GEMM with its statistics (and the draw).
+// logits GEMM with its statistics and the gather (or the draw).
 int mx_rows64_max(int sample) { return sample ? kRows64MaxSample : kRows64MaxLogits; }
 
 hipError_t launch_fwd_mx(int fmt, const void* hidden, int64_t n,
                          const uint8_t* codes, const uint8_t* scales, int H,
                          int V, const int* row_tokens, float2* partials,
                          int64_t ldp, float* ztgt, const uint64_t* row_ids,
-                         uint64_t seed, float2* cand, int* err, hipStream_t s) {
+                         uint64_t seed, float2* cand, float* candz, int* err,
+                         hipStream_t s) {
   FwdArgs a{};
   a.op = GemmOperands{(const char*)hidden, (int64_t)H * 2, nullptr, 0, nullptr, 0, V};
   a.rows = DevRows{nullptr, 0, (int)n};
@@ -1994,16 +1938,14 @@ hipError_t launch_fwd_mx(int fmt, const void* hidden, int64_t n,
   a.row_ids = row_ids;
   a.seed = seed;
   a.cand = cand;
+  a.candz = candz;
+  a.row_tokens = cand ? nullptr : row_tokens;
+  a.ztgt = ztgt;
   a.wcodes = codes;
   a.wscales = scales;
   a.H = H;
   a.err = err;
   const int nblk = a.mt * a.nt;
-  if (!cand) {
-    hipError_t e = launch_target_logit_mx(fmt, hidden, n, codes, scales, H, V,
-                                          row_tokens, ztgt, s);
-    if (e != hipSuccess) return e;
-  }
   return timed(cand ? K_FWD_SAMPLE : K_FWD_LOGITS, s, [&] {
     if (cand) {
       if (fmt == 0) k_fwd_logits64_mx<0, true><<<nblk, kThreads, 0, s>>>(a);
@@ -2015,27 +1957,11 @@ hipError_t launch_fwd_mx(int fmt, const void* hidden, int64_t n,
   });
 }
 
-hipError_t launch_target_logit_mx(int fmt, const void* hidden, int64_t n,
-                                  const uint8_t* codes, const uint8_t* scales,
-                                  int H, int V, const int* row_tokens, float* ztgt,
-                                  hipStream_t s) {
-  const DevRows rows{nullptr, 0, (int)n};
-  return timed(K_TARGET_LOGIT, s, [&] {
-    if (fmt == 0)
-      k_target_mfma<bf16, 0><<<cdiv(n, 128), 256, 0, s>>>(
-          (const char*)hidden, (int64_t)H * 2, nullptr, rows, nullptr, codes,
-          scales, H, V, row_tokens, ztgt);
-    else
-      k_target_mfma<bf16, 1><<<cdiv(n, 128), 256, 0, s>>>(
-          (const char*)hidden, (int64_t)H * 2, nullptr, rows, nullptr, codes,
-          scales, H, V, row_tokens, ztgt);
-  });
-}
-
-hipError_t launch_draw_merge(const float2* cand, int64_t ldp, int nt, int64_t n,
-                             int* tokens, hipStream_t s) {
+hipError_t launch_draw_merge(const float2* cand, const float* candz, int64_t ldp,
+                             int nt, int64_t n, int* tokens, float* ztgt,
+                             hipStream_t s) {
   return timed(K_DRAW_MERGE, s, [&] {
-    k_draw_merge<<<cdiv(n, 4), 256, 0, s>>>(cand, ldp, nt, n, tokens);
+    k_draw_merge<<<cdiv(n, 4), 256, 0, s>>>(cand, candz, ldp, nt, n, tokens, ztgt);
   });
 }
 
@@ -2045,9 +1971,6 @@ hipError_t launch_fwd_logits(int dt, const void* hidden, int64_t lda_bytes,
                              const int* row_tokens, float2* partials,
                              int64_t ldp, float* ztgt, void* e, int64_t lde,
                              int Vpad, hipStream_t s) {
-  hipError_t err = launch_target_logit(dt, hidden, lda_bytes, a_rows, rows,
-                                       lm_head, H, V, row_tokens, ztgt, s);
-  if (err != hipSuccess) return err;
   FwdArgs a{};
   a.op = GemmOperands{(const char*)hidden, lda_bytes, a_rows, rows.base,
                       (const char*)lm_head, (int64_t)H * (dt ? 2 : 4), V};
@@ -2064,6 +1987,8 @@ hipError_t launch_fwd_logits(int dt, const void* hidden, int64_t lda_bytes,
   a.ldp = ldp;
   a.e = e;
   a.lde = lde;
+  a.row_tokens = row_tokens;
+  a.ztgt = ztgt;
   const int nblk = a.mt * a.nt;
   if (small)
     return timed(K_FWD_LOGITS, s, [&] {

@@ -49,11 +49,16 @@ def test_noalloc_draw_matches_the_workspace_draw():
     V, H = synth.QWEN_VOCAB, 2560
     W = torch.from_numpy(synth.random_lm_head(V, H, "bf16", 301).view(np.int16)).view(
         torch.bfloat16).to(dev)
-    hid, _ = synth.random_rows(3000, H, V, "bf16", 302)
+    # the largest row count the static scratch holds at this head
+    per_row = rz.workspace_bytes(rz.RZ_OP_SAMPLE, 1000, 1, H, V, rz.RZ_DTYPE_BF16) / 1000
+    n_max = int(rz.RZ_NOALLOC_SCRATCH_BYTES / per_row) - 8
+    assert rz.workspace_bytes(rz.RZ_OP_SAMPLE, n_max, 1, H, V,
+                              rz.RZ_DTYPE_BF16) <= rz.RZ_NOALLOC_SCRATCH_BYTES
+    hid, _ = synth.random_rows(n_max, H, V, "bf16", 302)
     hidden = torch.from_numpy(hid.view(np.int16)).view(torch.bfloat16).to(dev)
-    ids = torch.arange(10_000, 13_000, dtype=torch.int64, device=dev)
+    ids = torch.arange(10_000, 10_000 + n_max, dtype=torch.int64, device=dev)
     # the largest row count that fits, then fewer rows over the same scratch
-    for n in (3000, 300, 37):
+    for n in (n_max, 300, 37):
         _compare(hidden[:n], W, ids[:n], 77, f"noalloc-bf16-{n}")
     # fp32 head, two calls in a row
     Wf = torch.from_numpy(synth.random_lm_head(1000, 256, "f32", 303)).to(dev)
