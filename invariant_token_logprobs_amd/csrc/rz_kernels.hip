@@ -112,29 +112,28 @@ __device__ __forceinline__ int e_stage_off(int R, int k) {
 // As Easy as 1, 2, 3", SC 2011): ten rounds of two 32 x 32 -> 64-bit
 // products on counter words 0 and 2, the halves and the key XORed into the
 // next counter; the key grows by fixed Weyl increments between rounds.
-__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1,
-                                              uint32_t c2, uint32_t c3,
-                                              uint32_t k0, uint32_t k1) {
-  // kept rolled: fully unrolled at every call site of the draw's epilogue
-  // it stops the enclosing loops from unrolling, and the accumulators they
-  // index would move to scratch memory
+// Four blocks at once (counters c[0..3], one key), the four independent
+// chains interleaved in each round, so one wave per SIMD has four products
+// in flight instead of waiting on each round's product in turn.  The round
+// loop stays rolled: unrolled at the draw's call sites it stops the
+// enclosing loops from unrolling, and the accumulators they index would move
+// to scratch memory.  One 64-bit product gives both halves (v_mad_u64_u32).
+__device__ __forceinline__ void philox4x32_10_x4(u32x4 (&c)[4], uint32_t k0,
+                                                 uint32_t k1) {
 #pragma unroll 1
   for (int r = 0; r < 10; ++r) {
     if (r) {
       k0 += 0x9E3779B9u;
       k1 += 0xBB67AE85u;
     }
-    // one 64-bit product gives both halves (v_mad_u64_u32)
-    const uint64_t p0 = (uint64_t)c0 * 0xD2511F53u;
-    const uint64_t p1 = (uint64_t)c2 * 0xCD9E8D57u;
-    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
-    c0 = n0;
-    c1 = (uint32_t)p1;
-    c2 = n2;
-    c3 = (uint32_t)p0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint64_t p0 = (uint64_t)c[i][0] * 0xD2511F53u;
+      const uint64_t p1 = (uint64_t)c[i][2] * 0xCD9E8D57u;
+      c[i] = u32x4{(uint32_t)(p1 >> 32) ^ c[i][1] ^ k0, (uint32_t)p1,
+                   (uint32_t)(p0 >> 32) ^ c[i][3] ^ k1, (uint32_t)p0};
+    }
   }
-  return u32x4{c0, c1, c2, c3};
 }
 
 constexpr float kLn2 = 0.69314718055994531f;
@@ -335,18 +334,23 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
       float bs = -__builtin_inff();
       int bv = 0x7fffffff;
       float bz = 0.f;  // the best column's logit: the record's z[a_t]
-      static_for<0, kTN * 4>([&](auto nq_c) {
-        constexpr int ni = decltype(nq_c)::value / 4, q = decltype(nq_c)::value % 4;
-        const int c0 = cbase + ni * 32 + 8 * q;  // multiple of 4
-        const u32x4 x = philox4x32_10((uint32_t)c0 >> 2, (uint32_t)id,
-                                      (uint32_t)(id >> 32), 0u, k0, k1);
+      // block ni of the lane: its four runs q = 0..3 of four columns, the
+      // four Philox blocks computed together
+      static_for<0, kTN>([&](auto ni_c) {
+        constexpr int ni = decltype(ni_c)::value;
+        u32x4 x[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          x[q] = u32x4{(uint32_t)(cbase + ni * 32 + 8 * q) >> 2, (uint32_t)id,
+                       (uint32_t)(id >> 32), 0u};
+        philox4x32_10_x4(x, k0, k1);
         // a lane meets its columns in increasing order, so a strict > keeps
         // the smallest index among equal scores (draw_better's order)
-        static_for<0, 4>([&](auto j_c) {
-          constexpr int j = decltype(j_c)::value;
-          const int v = c0 + j;
+        static_for<0, 16>([&](auto qj_c) {
+          constexpr int q = decltype(qj_c)::value / 4, j = decltype(qj_c)::value % 4;
+          const int v = cbase + ni * 32 + 8 * q + j;
           const float z = acc[mi][ni][4 * q + j];
-          float sc = z + gumbel_of_bits(x[j]);
+          float sc = z + gumbel_of_bits(x[q][j]);
           sc = v < a.V ? sc : -__builtin_inff();
           const bool take = sc > bs;
           bs = take ? sc : bs;
