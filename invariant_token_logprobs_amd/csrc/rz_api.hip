@@ -114,6 +114,7 @@ struct FbWs {
   float* lse_v;
   float* logpi_v;
   float* coef;
+  float* coef1;
   int* T;
   double* S;
   int* gcnt;
@@ -152,6 +153,7 @@ size_t carve_fb(Carver& c, int64_t n, int32_t B, int32_t H, int32_t V,
   t.lse_v = c.take<float>(sizeof(float) * (size_t)n);
   t.logpi_v = c.take<float>(sizeof(float) * (size_t)n);
   t.coef = c.take<float>(sizeof(float) * (size_t)n);
+  t.coef1 = c.take<float>(sizeof(float) * (size_t)n);
   t.T = c.take<int>(sizeof(int) * (size_t)B);
   t.S = c.take<double>(sizeof(double) * (size_t)B);
   t.gcnt = c.take<int>(sizeof(int) * (size_t)B);
@@ -581,14 +583,14 @@ static rz_status fwd_bwd_core(
                               w.lse_v, w.logpi_v, w.idx, logprobs, err_flag,
                               s));
       RZ_TRY(launch_coef(crow, w.logpi_v, logmu, w.idx, w.respv, w.fcoef, sc,
-                         w.coef, s));
+                         w.coef, w.coef1, s));
       RZ_TRY(launch_dz_scale(dt, w.dz, Vpad, w.dzT, C, crow, w.partials, N,
-                             w.lse_v, w.coef, Vpad, s));
+                             w.lse_v, w.coef, w.tokv, Vpad, s));
       RZ_TRY(launch_transpose(dt, K_TRANSPOSE_H,
                               (const char*)hidden + (size_t)dw_col0 * es, H,
                               w.idx, crow, C, dw_cols, w.hT, C, s));
       RZ_TRY(launch_bwd_dh(dt, w.dz, Vpad, crow, w.WT, Vpad, H, V, Vpad,
-                           w.idx, w.tokv, w.coef, lm_head, d_hidden, s));
+                           w.idx, w.tokv, w.coef1, lm_head, d_hidden, s));
     }
     const bool kmaj = dt == RZ_DTYPE_BF16;
     RZ_TRY(launch_bwd_dw(dt, kmaj ? w.dz : w.dzT, kmaj ? Vpad : C,
@@ -605,7 +607,7 @@ static rz_status fwd_bwd_core(
     RZ_TRY(launch_diagnostics(logprobs, logmu, mask, N, w.diag_part,
                               diag ? diag : w.diag_tmp, s));
   // a9: exact one-hot part of dW
-  RZ_TRY(launch_dw_fix(dt, w.nvalid, N, w.tokv, w.idx, w.coef,
+  RZ_TRY(launch_dw_fix(dt, w.nvalid, N, w.tokv, w.idx, w.coef1,
                        (const char*)hidden + (size_t)dw_col0 * es, H, dw_cols,
                        V, w.sort_ws, w.fix_cont, d_lm_head, s));
   return RZ_OK;

@@ -133,9 +133,10 @@ hipError_t launch_loss_value(const uint8_t* mask, const float* logprobs,
                              const float* logmu, int64_t n, const int* cu,
                              int B, int sc, const int* T, const double* Ad,
                              double* S, float* loss, hipStream_t s);
+// coef = c_t; coef1 = c_t (1 - p[a_t]), the token column's exact term
 hipError_t launch_coef(DevRows rows, const float* logpi_v, const float* logmu,
                        const int* idx, const int* respv, const double* fcoef,
-                       int sc, float* coef, hipStream_t s);
+                       int sc, float* coef, float* coef1, hipStream_t s);
 size_t diag_partials_bytes(int64_t n);
 hipError_t launch_diagnostics(const float* logpi, const float* logmu,
                               const uint8_t* mask, int64_t n, void* partials,
@@ -147,7 +148,7 @@ hipError_t launch_transpose(int dt, int kid, const void* in, int64_t ld_in,
 hipError_t launch_dz_scale(int dt, void* dz, int64_t ldz, void* dzT,
                            int64_t ldzt, DevRows rows, const float2* partials,
                            int64_t ldp, const float* lse, const float* coef,
-                           int Vpad, hipStream_t s);
+                           const int* tokv, int Vpad, hipStream_t s);
 hipError_t launch_bwd_dh(int dt, const void* dz, int64_t ldz, DevRows rows,
                          const void* WT, int64_t ldwt, int H, int V, int Vpad,
                          const int* idx, const int* tokv, const float* coef,

@@ -831,24 +831,27 @@ __global__ __launch_bounds__(256) void k_loss_value(const double* Ad,
 
 // c_t = A_i w_t / (B T_i): minus the derivative of L by log pi_t (the
 // gradient flows through the numerator pi_theta only).  Score centering
-// (sc = 1): c_t = A_i / (B T_i), the weight replaced by 1.
+// (sc = 1): c_t = A_i / (B T_i), the weight replaced by 1.  Also the whole
+// dL/dz of the row's own token, c_t (p[a_t] - 1) = -c_t expm1(log pi_t),
+// kept in fp32 (coef1 holds its negative): the bf16 dlogits leave that
+// column out, because on a row whose token takes nearly all the mass
+// c_t p[a_t] and c_t cancel to far less than bf16's rounding of either.
 __global__ __launch_bounds__(256) void k_coef(DevRows rows,
                                               const float* logpi_v,
                                               const float* logmu,
                                               const int* idx,
                                               const int* respv,
                                               const double* fcoef, int sc,
-                                              float* coef) {
+                                              float* coef, float* coef1) {
   const RowCount rc = to_rc(rows);
   const int q = blockIdx.x * 256 + threadIdx.x;
   if (q >= rc.get()) return;
   const int64_t p = rc.base + q;
-  if (sc) {
-    coef[p] = (float)fcoef[respv[p]];
-    return;
-  }
-  const float w = expf(logpi_v[p] - logmu[idx[p]]);
-  coef[p] = (float)(fcoef[respv[p]] * (double)w);
+  const float lp = logpi_v[p];
+  const double c = sc ? fcoef[respv[p]]
+                      : fcoef[respv[p]] * (double)expf(lp - logmu[idx[p]]);
+  coef[p] = (float)c;
+  coef1[p] = (float)(-c * expm1((double)lp));
 }
 
 // ===================================================================
@@ -1299,9 +1302,10 @@ __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ in,
 // Backward, part 1: dlogits.  The forward of the learner call stored
 // e[t, v] = exp(z[t, v] - m_tile(t, j)) (EStore type, times 2^14 for fp16, in the dz buffer) for
 // the vocab tile j holding v; with
-// lse_t known, dz[t, v] = c_t * exp(m_tile(t, j) - lse_t) * e[t, v] is the
-// softmax part of dL/dz (the one-hot part -c_t [v == a_t] is applied exactly
-// in fp32 by the dHidden epilogue and the dW fix-up).  The kernel rescales
+// lse_t known, dz[t, v] = c_t * exp(m_tile(t, j) - lse_t) * e[t, v] is
+// dL/dz for v != a_t; the token's own column is left at 0 and its whole
+// dL/dz, c_t (p[a_t] - 1), is applied exactly in fp32 by the dHidden
+// epilogue and the dW fix-up.  The kernel rescales
 // e in place into the token-major dz [C, Vpad], the A operand of dHidden and
 // (bf16, read K-major) of dW.  fp32 has no transposing LDS read, so there
 // the kernel also writes the vocab-major dz^T [Vpad, C] for dW.  Rows from
@@ -1320,13 +1324,15 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_dz_scale(
     T* __restrict__ dz, int64_t ldz, T* __restrict__ dzT, int64_t ldzt,
     DevRows rows, const float2* __restrict__ partials, int64_t ldp,
-    const float* __restrict__ lse, const float* __restrict__ coef, int Vpad) {
+    const float* __restrict__ lse, const float* __restrict__ coef,
+    const int* __restrict__ tokv, int Vpad) {
   constexpr int kVec = 16 / (int)sizeof(T);       // 8 (bf16) or 4 (fp32)
   constexpr int kG = 64 / kVec;                   // row blocks per wave
   constexpr int kWaveCols = (64 / kG) * kVec;     // 64 (bf16) or 16 (fp32)
   constexpr int kBlockCols = 4 * kWaveCols;       // within one vocab tile
   constexpr int kSpan = sizeof(T) == 2 ? 2 : 1;   // column blocks per workgroup
   __shared__ float sc[kSpan][64];
+  __shared__ int stok[64];  // the rows' tokens: their column is left at 0
   const RowCount rc = to_rc(rows);
   const int R = rc.get();
   const int r0 = blockIdx.y * 64;
@@ -1366,6 +1372,7 @@ __global__ __launch_bounds__(256) void k_dz_scale(
       v = coef[pos] * exp_approx(partials[(int64_t)j * ldp + pos].x - lse[pos]);
     }
     sc[b][tid & 63] = v;
+    if (b == 0) stok[tid] = t < R ? tokv[rc.base + t] : -1;
   }
   __syncthreads();
   if constexpr (sizeof(T) == 2) {
@@ -1380,6 +1387,8 @@ __global__ __launch_bounds__(256) void k_dz_scale(
         if (t < R) {
           const f16x8 e = __builtin_bit_cast(f16x8, x[b][i]);
           const float f = sc[b][tr + i];
+          // the row's own token (if among these 8 columns) stays 0
+          const uint32_t own = (uint32_t)(stok[tr + i] - col);
           uint32_t y[4];
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
@@ -1388,7 +1397,7 @@ __global__ __launch_bounds__(256) void k_dz_scale(
                 uint16_t, (T)(f * ((float)e[2 * w] * kEUnscale)));
             const uint32_t hi = __builtin_bit_cast(
                 uint16_t, (T)(f * ((float)e[2 * w + 1] * kEUnscale)));
-            y[w] = lo | (hi << 16);
+            y[w] = (own == 2u * w ? 0u : lo) | ((own == 2u * w + 1 ? 0u : hi) << 16);
           }
           // dz (10 GB per chunk) reaches the GEMMs from HBM in any case
           __builtin_nontemporal_store(u32x4{y[0], y[1], y[2], y[3]},
@@ -1409,6 +1418,9 @@ __global__ __launch_bounds__(256) void k_dz_scale(
       if (t < R) {
         T* p = dz + (int64_t)t * ldz + col;
         y[i] = sc[0][tr + i] * *reinterpret_cast<const f32x4*>(p);
+        const uint32_t own = (uint32_t)(stok[tr + i] - col);  // stays 0
+#pragma unroll
+        for (int w = 0; w < 4; ++w) y[i][w] = own == (uint32_t)w ? 0.f : y[i][w];
         *reinterpret_cast<f32x4*>(p) = y[i];
       } else {
         y[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1422,8 +1434,9 @@ __global__ __launch_bounds__(256) void k_dz_scale(
 }
 
 // ===================================================================
-// Backward, part 2: dHidden = dz W (K = Vpad in fixed order) minus the
-// exact one-hot term c_t W[a_t, :], scattered to the rows' positions.
+// Backward, part 2: dHidden = dz W (K = Vpad in fixed order) plus the token
+// column's exact term c_t (p[a_t] - 1) W[a_t, :] (coef holds its
+// negative), scattered to the rows' positions.
 // ===================================================================
 template <typename T>
 struct DhArgs {
@@ -1715,7 +1728,8 @@ __global__ __launch_bounds__(256) void k_sort_scatter(
 }
 
 // ===================================================================
-// dW one-hot fix-up: dW[v, :] -= sum over valid t with a_t = v of c_t h_t.
+// dW token-column fix-up: dW[v, :] -= sum over valid t with a_t = v of
+// c_t (1 - p[a_t]) h_t (the exact fp32 term of each row's own token).
 // The valid-row positions, ordered by token (stable, so ascending within a
 // token), are cut into fixed pieces of kFixPiece entries.  A workgroup sums
 // each run of equal tokens in its piece in list order; a run that lies
@@ -2147,10 +2161,10 @@ hipError_t launch_loss_value(const uint8_t* mask, const float* logprobs,
 
 hipError_t launch_coef(DevRows rows, const float* logpi_v, const float* logmu,
                        const int* idx, const int* respv, const double* fcoef,
-                       int sc, float* coef, hipStream_t s) {
+                       int sc, float* coef, float* coef1, hipStream_t s) {
   return timed(K_COEF, s, [&] {
     k_coef<<<cdiv(rows.cap, 256), 256, 0, s>>>(rows, logpi_v, logmu, idx,
-                                               respv, fcoef, sc, coef);
+                                               respv, fcoef, sc, coef, coef1);
   });
 }
 
@@ -2318,7 +2332,7 @@ hipError_t launch_transpose(int dt, int kid, const void* in, int64_t ld_in,
 hipError_t launch_dz_scale(int dt, void* dz, int64_t ldz, void* dzT,
                            int64_t ldzt, DevRows rows, const float2* partials,
                            int64_t ldp, const float* lse, const float* coef,
-                           int Vpad, hipStream_t s) {
+                           const int* tokv, int Vpad, hipStream_t s) {
   // 64 rows x (two column blocks of 4 waves x 64 bf16, or one of 4 x 16
   // fp32 columns) per workgroup; neighbouring workgroups share rows
   dim3 grid(cdiv(Vpad, dt ? 512 : 64), cdiv(rows.cap, 64));
@@ -2326,11 +2340,11 @@ hipError_t launch_dz_scale(int dt, void* dz, int64_t ldz, void* dzT,
     if (dt)
       k_dz_scale<bf16><<<grid, 256, 0, s>>>((bf16*)dz, ldz, (bf16*)dzT, ldzt,
                                             rows, partials, ldp, lse, coef,
-                                            Vpad);
+                                            tokv, Vpad);
     else
       k_dz_scale<float><<<grid, 256, 0, s>>>((float*)dz, ldz, (float*)dzT,
                                              ldzt, rows, partials, ldp, lse,
-                                             coef, Vpad);
+                                             coef, tokv, Vpad);
   });
 }
 

@@ -189,14 +189,22 @@ def workload_layout(name: str):
 
 def make_workload(name: str, *, max_responses: Optional[int] = None,
                   max_valid: Optional[int] = None,
+                  max_rows_per_response: Optional[int] = None,
                   tokens: str = "uniform") -> Batch:
-    """Draw the named workload.  Optional caps truncate it (whole responses
-    first; the last kept response may be cut) for oracle-sized checks at the
-    full H and V.  tokens = "zipf" replaces the uniform tokens by Zipf(1.1)
-    ones (zipf_tokens, seed 3000 + k); the other arrays are unchanged."""
+    """Draw the named workload.  Optional caps truncate it for oracle-sized
+    checks at the full H and V: max_rows_per_response keeps the first rows
+    of every response (their mask as drawn), max_responses the first
+    responses, max_valid the rows up to that many valid ones (the last kept
+    response may be cut).  tokens = "zipf" replaces the uniform tokens by
+    Zipf(1.1) ones (zipf_tokens, seed 3000 + k); the other arrays are
+    unchanged."""
     wl = WORKLOADS[name]
     rng, lengths, mask, rewards, group_ids = workload_layout(name)
     B = wl.n_resp
+    if max_rows_per_response is not None:
+        starts = np.concatenate([[0], np.cumsum(lengths)[:-1]])
+        lengths = np.minimum(lengths, max_rows_per_response)
+        mask = np.concatenate([mask[s0:s0 + L] for s0, L in zip(starts, lengths)])
 
     # truncate (by responses, then by valid rows) before drawing the big arrays
     cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)

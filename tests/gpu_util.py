@@ -9,7 +9,8 @@ Tolerances (per element, |gpu - oracle| <= atol + rtol * |oracle|):
   (unit roundoff u = 2^-8; the stored exp(z - m_tile) adds at most 2^-11),
   so the forward-error bound of each element is 2u * (|G_s| |W|)[t, h] for
   dL/dhidden and 2u * (|G_s|^T |h|)[v, h] for dL/dW, G_s = c_t softmax(z_t)
-  (the one-hot part is applied exactly in fp32); per element
+  (the row's own token column, c_t (p[a_t] - 1), is applied exactly in fp32,
+  so this bound is conservative there); per element
   |gpu - oracle| <= 2u * bound + cbound + 1e-6 * max|oracle| + rtol * |oracle|.
   cbound carries the logprob error into the gradients: c_t = A_i w_t / (B T_i)
   is computed from the kernel's own log pi_t, so a logprob off by d_t (the

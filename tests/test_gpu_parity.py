@@ -106,11 +106,15 @@ def test_dw_last_round_split(n_vtiles):
 
 @pytest.mark.parametrize("name", ["qwen3_4b_tool", "r1_distill_1p5b", "qwen3_30b_a3b"])
 def test_truncated_full_parity(name):
-    """Each workload's shape at its full H and V = 151936, on the first
-    responses up to 1024 valid rows, every output compared (the 1.5B head
-    has 6 column tiles of 256, the 30B head 8, the Qwen3-4B head 10, and
-    each its own dW last-round split)."""
-    b = synth.make_workload(name, max_valid=1024)
+    """Each workload's shape at its full H and V = 151936, every output
+    compared, on its first group (8 responses, so the advantages and the
+    gradients are not zero) cut to the first rows of each response (about
+    1000 valid rows).  The 1.5B head has 6 column tiles of 256, the 30B head
+    8, the Qwen3-4B head 10, each with its own dW last-round split."""
+    b = synth.make_workload(name, max_responses=8,
+                            max_rows_per_response=200 if name == "qwen3_4b_tool" else 128)
+    assert b.B == 8 and len(set(b.group_ids.tolist())) == 1
+    assert np.abs(O.group_mean_advantages(b.rewards, b.group_ids)).max() > 0
     _case(b, f"{name}-truncated")
 
 
