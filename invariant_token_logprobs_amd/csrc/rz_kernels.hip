@@ -183,8 +183,10 @@ __device__ __forceinline__ bool draw_better(float s, int v, float bs, int bv) {
 // statistics and draw are bit-identical whichever tile computes them.
 // kWFmt: -1 for a bf16 / fp32 head, 0 / 1 for an MXFP4 / MXFP8 head read
 // by the 64-row tile (the accumulators are those of the expanded head).
+// kTokOff: byte offset in lds of the tile's row tokens for the gather
+// (-1: none; the gather then reads them from global memory).
 template <typename T, bool kStoreE, bool kSample, int TM, int kWFmt = -1,
-          int kStages64 = 2>
+          int kStages64 = 2, int kTokOff = -1>
 __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
   static_assert(TM == kTM || (TM == 1 && !kStoreE), "64-row tile: no e output");
   constexpr int BM = 64 * TM;  // tile rows
@@ -201,6 +203,27 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
   if ((int)blockIdx.x >= mt * a.nt) return;
   const TileCoord tc = map_tile(blockIdx.x, mt * a.nt, mt, a.nt);
   const int m0 = tc.tm * BM, n0 = tc.tn * kBN;
+
+  // The 256-row tile's row tokens for the gather, brought into LDS (stok,
+  // outside the stage buffers) by one 4-byte DMA load per lane before the
+  // main loop: the main loop's stage waits and barriers complete it, so the
+  // epilogue reads them without waiting on global memory.  (The 64-row
+  // forms have no LDS to spare at their occupancy and read them in the
+  // epilogue.)
+  if constexpr (kTokOff >= 0) {
+    if (a.row_tokens) {
+      typedef __attribute__((address_space(3))) void* lds_ptr_t;
+      const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+      // an opaque copy of the thread index: the row computed here must not
+      // be merged with the epilogue's (it would live, spilled, through the
+      // whole main loop)
+      int t = (int)threadIdx.x;
+      asm volatile("" : "+v"(t));
+      const int m = min(m0 + t, M - 1);  // in bounds; rows >= M unused
+      __builtin_amdgcn_global_load_lds(a.row_tokens + rc.base + m,
+                                       (lds_ptr_t)(lds + kTokOff + 256 * w), 4, 0, 0);
+    }
+  }
 
   f32x16 acc[TM][kTN];
   if constexpr (TM == kTM) {
@@ -229,8 +252,14 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
   if (a.row_tokens) {
 #pragma unroll
     for (int mi = 0; mi < TM; ++mi) {
-      const int m = m0 + wm * RW + mi * 32 + l32;
-      const int tok = m < M ? a.row_tokens[rc.base + m] : -1;
+      const int R = wm * RW + mi * 32 + l32;
+      const int m = m0 + R;
+      int tok = -1;
+      if constexpr (kTokOff >= 0) {
+        if (m < M) tok = reinterpret_cast<const int*>(lds + kTokOff)[R];
+      } else {
+        if (m < M) tok = a.row_tokens[rc.base + m];
+      }
       const int off = tok - cbase;  // this lane's columns: 32 ni + 8 q + j
       if (tok >= 0 && tok < a.V && off >= 0 && off < 128 && (off & 4) == 0) {
         const int want = ((off >> 5) << 4) | (((off >> 3) & 3) << 2) | (off & 3);
@@ -417,9 +446,11 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
 template <typename T, bool kStoreE, bool kSample = false>
 __global__ RZ_GEMM_ATTR void k_fwd_logits(FwdArgs a) {
   // [0, 128 KB): main-loop stages, then (learner call, bf16) the e tile;
-  // then the epilogue arrays, [2][256] floats each
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes + (kSample ? 10240 : 4096)];
-  fwd_logits_body<T, kStoreE, kSample, kTM>(a, lds);
+  // then the epilogue arrays, [2][256] floats each; then the row tokens
+  // (the draw gathers nothing: its tokens are drawn later)
+  constexpr int kEpiBytes = kSample ? 10240 : 4096;
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes + kEpiBytes + (kSample ? 0 : 4 * kBM)];
+  fwd_logits_body<T, kStoreE, kSample, kTM, -1, 2, kSample ? -1 : kLdsBytes + kEpiBytes>(a, lds);
 }
 
 // The 64-row tile: 80 KB of LDS and a quarter of the accumulators, so two
