@@ -30,22 +30,23 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA
 HBM_GBS = 8000.0
 GEMM_KERNELS = ("fwd_logits_gemm", "bwd_dh_gemm", "bwd_dw_gemm")
 
-# HBM bytes per launch from two rocprofv3 counter runs of this script
+# Bytes per launch past L2 from two rocprofv3 counter runs of this script
 # (FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0, the factors a plain 1 GiB copy
-# reads on the same counters), averaged over the launches of one step: the
-# learner GEMMs at the Qwen3-4B tool-use shape (profiles/
+# reads on the same counters; FETCH_SIZE counts every L2 miss, including
+# those the memory-side cache serves), averaged over the launches of one
+# step: the learner GEMMs at the Qwen3-4B tool-use shape (profiles/
 # gemm_traffic_qwen3_4b_tool.md), the gradient-norm kernel of --mode diag
 # (profiles/run_diagnostics_qwen3_4b_step.md) and the MXFP4 expansion of
 # --mode mx (profiles/mx_dequant_qwen3_4b_head.md).  Valid only for the
 # kernel sources they were taken from.
 COUNTER_TRAFFIC = {
     "workload": "qwen3_4b_tool",
-    "sources_sha256": "40d14eefe1b1593191759f1fd4547e86b46d062021febfddca07d12821aad47c",
-    "bytes_per_launch": {"fwd_logits_gemm": 29355093970,
-                         "bwd_dh_gemm": 24424364965,
-                         "bwd_dw_gemm": 28876816456 + 47679704,  # + its tail sum
-                         "grad_norm": 2291985991,
-                         "mx_dequant_mxfp4": 984648854},
+    "sources_sha256": "bc3c8695f534647527618160492f0bc41d89217587f96443d443de828f37b15c",
+    "bytes_per_launch": {"fwd_logits_gemm": 26247762392,
+                         "bwd_dh_gemm": 24514813720,
+                         "bwd_dw_gemm": 29188745031 + 47679713,  # + its tail sum
+                         "grad_norm": 2291986450,
+                         "mx_dequant_mxfp4": 984653570},
 }
 
 
@@ -54,9 +55,9 @@ COUNTER_TRAFFIC = {
 # GEMMs, from the counter run of profiles/mfma_utilisation_qwen3_4b_tool.md,
 # over the launches that hold rows; same validity rule as COUNTER_TRAFFIC.
 COUNTER_MFMA = {
-    "fwd_logits_gemm": {"mfma_busy": 0.580, "clock_ghz": 1.842},
-    "bwd_dh_gemm": {"mfma_busy": 0.591, "clock_ghz": 1.812},
-    "bwd_dw_gemm": {"mfma_busy": 0.568, "clock_ghz": 1.854},
+    "fwd_logits_gemm": {"mfma_busy": 0.564, "clock_ghz": 1.921},
+    "bwd_dh_gemm": {"mfma_busy": 0.588, "clock_ghz": 1.838},
+    "bwd_dw_gemm": {"mfma_busy": 0.572, "clock_ghz": 1.864},
 }
 
 
@@ -692,7 +693,7 @@ def main():
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": traffic,
-                "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                "traffic_unit": "bytes per launch past L2 (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                 "avg_launch_ms": round(avg_ms, 4),
                 "launches_per_step": launches // args.steps,
                 "counters": counter_mfma(dom, b.name) if not r else None}
