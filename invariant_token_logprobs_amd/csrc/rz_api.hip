@@ -115,6 +115,11 @@ struct FbWs {
   float* logpi_v;
   float* coef;
   float* coef1;
+  float* eref;    // bf16: the row's e reference r*_t
+  int* eflag;     // bf16: the row's tiles need rebasing
+  float* gsc;     // bf16: g_t = exp(r*_t ln 2 - lse_t)
+  int* fexp_part; // bf16: per-workgroup largest exponent of c_t g_t
+  int* sigma;     // bf16: the chunk's power of two for dW
   int* T;
   double* S;
   int* gcnt;
@@ -154,6 +159,11 @@ size_t carve_fb(Carver& c, int64_t n, int32_t B, int32_t H, int32_t V,
   t.logpi_v = c.take<float>(sizeof(float) * (size_t)n);
   t.coef = c.take<float>(sizeof(float) * (size_t)n);
   t.coef1 = c.take<float>(sizeof(float) * (size_t)n);
+  t.eref = c.take<float>(sizeof(float) * (size_t)n);
+  t.eflag = c.take<int>(sizeof(int) * (size_t)n);
+  t.gsc = c.take<float>(sizeof(float) * (size_t)n);
+  t.fexp_part = c.take<int>(sizeof(int) * (size_t)coef_blocks(C));
+  t.sigma = c.take<int>(sizeof(int));
   t.T = c.take<int>(sizeof(int) * (size_t)B);
   t.S = c.take<double>(sizeof(double) * (size_t)B);
   t.gcnt = c.take<int>(sizeof(int) * (size_t)B);
@@ -164,8 +174,9 @@ size_t carve_fb(Carver& c, int64_t n, int32_t B, int32_t H, int32_t V,
   t.diag_part = c.take<char>(diag_partials_bytes(n));
   t.WT = c.take<char>(es * (size_t)H * (size_t)Vpad);
   t.hT = c.take<char>(es * (size_t)dw_cols * (size_t)C);
+  // bf16: the stored e, the backward GEMMs' A operand; fp32: e, then dz
   t.dz = c.take<char>(es * (size_t)C * (size_t)Vpad);
-  // dz^T only for fp32 (bf16 dW reads dz through transposing LDS reads)
+  // dz^T only for fp32 (bf16 dW reads e through transposing LDS reads)
   t.dzT = dt == RZ_DTYPE_F32 ? c.take<char>(es * (size_t)Vpad * (size_t)C)
                              : nullptr;
   t.bad_gid = c.take<int>(sizeof(int));
@@ -449,7 +460,8 @@ static rz_status sample_core(const void* hidden, const void* lm_head,
   RZ_TRY(launch_draw_merge(w.cand, w.candz, n_rows, nt, n_rows, tokens, w.ztgt, s));
   // the record: rz_token_logprobs' own merge kernel
   RZ_TRY(launch_lse_merge(w.partials, n_rows, nt, rows, w.ztgt, tokens, V,
-                          lse, logmu, nullptr, nullptr, nullptr, s));
+                          lse, logmu, nullptr, nullptr, nullptr, nullptr,
+                          nullptr, s));
   return RZ_OK;
 }
 
@@ -514,7 +526,8 @@ rz_status rz_token_logprobs(const void* hidden, const void* lm_head,
                            lm_head, H, V, tokens, w.partials, n_rows, w.ztgt,
                            nullptr, 0, 0, s));
   RZ_TRY(launch_lse_merge(w.partials, n_rows, nt, rows, w.ztgt, tokens, V,
-                          lse, logprobs, nullptr, nullptr, err_flag, s));
+                          lse, logprobs, nullptr, nullptr, err_flag, nullptr,
+                          nullptr, s));
   return RZ_OK;
 }
 
@@ -566,12 +579,17 @@ static rz_status fwd_bwd_core(
                            w.bad_cu, w.T, w.gcnt, w.gsum, w.Ad, w.fcoef, adv,
                            w.bad_gid, w.sort_ws, err_flag, s));
   RZ_TRY(launch_transpose(dt, K_TRANSPOSE_W, lm_head, H, nullptr,
-                          DevRows{nullptr, 0, V}, Vpad, H, w.WT, Vpad, s));
+                          DevRows{nullptr, 0, V}, Vpad, H, w.WT, Vpad, nullptr,
+                          nullptr, nullptr, s));
   // a1-a4, a7-a9 in chunks of C valid rows (the count lives on the device;
   // chunks past it do no work):
-  //   logits GEMM + log-softmax epilogue, also storing exp(z - m_tile);
-  //   ordered merge -> lse, log pi; c_t; dz = c_t e^(m_tile - lse) exp(...);
+  //   logits GEMM + log-softmax epilogue, also storing e (bf16:
+  //   exp(z - r ln 2), the backward's A operand; fp32: exp(z - m_tile));
+  //   ordered merge -> lse, log pi; c_t;
+  //   bf16: g_t and the chunk's scale, flagged rows rebased, h^T scaled by
+  //   c_t g_t 2^sigma; fp32: dz = c_t e^(m_tile - lse) e and dz^T;
   //   dHidden GEMM; dW GEMM accumulated over chunks in order.
+  const bool b16 = dt == RZ_DTYPE_BF16;
   const int64_t nchunks = N > 0 ? (N + C - 1) / C : 1;
   for (int64_t k = 0; k < nchunks; ++k) {
     DevRows crow{w.nvalid, k * C, C};
@@ -581,21 +599,29 @@ static rz_status fwd_bwd_core(
                                s));
       RZ_TRY(launch_lse_merge(w.partials, N, nt, crow, w.ztgt, w.tokv, V,
                               w.lse_v, w.logpi_v, w.idx, logprobs, err_flag,
-                              s));
+                              b16 ? w.eref : nullptr, w.eflag, s));
       RZ_TRY(launch_coef(crow, w.logpi_v, logmu, w.idx, w.respv, w.fcoef, sc,
-                         w.coef, w.coef1, s));
-      RZ_TRY(launch_dz_scale(dt, w.dz, Vpad, w.dzT, C, crow, w.partials, N,
-                             w.lse_v, w.coef, w.tokv, Vpad, s));
+                         w.coef, w.coef1, w.lse_v, b16 ? w.eref : nullptr,
+                         w.gsc, w.fexp_part, w.sigma, s));
+      if (b16) {
+        RZ_TRY(launch_erebase(w.dz, Vpad, crow, w.partials, N, nt, w.eref,
+                              w.eflag, Vpad, s));
+      } else {
+        RZ_TRY(launch_dz_scale((float*)w.dz, Vpad, (float*)w.dzT, C, crow,
+                               w.partials, N, w.lse_v, w.coef, w.tokv, Vpad, s));
+      }
       RZ_TRY(launch_transpose(dt, K_TRANSPOSE_H,
                               (const char*)hidden + (size_t)dw_col0 * es, H,
-                              w.idx, crow, C, dw_cols, w.hT, C, s));
+                              w.idx, crow, C, dw_cols, w.hT, C,
+                              b16 ? w.coef : nullptr, w.gsc, w.sigma, s));
       RZ_TRY(launch_bwd_dh(dt, w.dz, Vpad, crow, w.WT, Vpad, H, V, Vpad,
-                           w.idx, w.tokv, w.coef1, lm_head, d_hidden, s));
+                           w.idx, w.tokv, w.coef1, b16 ? w.coef : nullptr,
+                           w.gsc, lm_head, d_hidden, s));
     }
-    const bool kmaj = dt == RZ_DTYPE_BF16;
-    RZ_TRY(launch_bwd_dw(dt, kmaj ? w.dz : w.dzT, kmaj ? Vpad : C,
+    RZ_TRY(launch_bwd_dw(dt, b16 ? w.dz : w.dzT, b16 ? Vpad : C,
                          N > 0 ? crow : DevRows{nullptr, 0, 0}, w.hT, C,
-                         dw_cols, V, Vpad, d_lm_head, k == 0, w.dwpart, s));
+                         dw_cols, V, Vpad, d_lm_head, k == 0, w.dwpart,
+                         N > 0 ? w.sigma : nullptr, s));
   }
   if (N > 0) RZ_TRY(launch_rows_finalize(mask, N, H, logprobs, d_hidden, s));
   // a5: S_i from this call's logprobs, then L
@@ -770,7 +796,8 @@ rz_status rz_token_logprobs_mx(const void* hidden, const uint8_t* codes,
                              w.ztgt, nullptr, 0, 0, s));
   }
   RZ_TRY(launch_lse_merge(w.partials, n_rows, nt, rows, w.ztgt, tokens, V,
-                          lse, logprobs, nullptr, nullptr, err_flag, s));
+                          lse, logprobs, nullptr, nullptr, err_flag, nullptr,
+                          nullptr, s));
   return RZ_OK;
 }
 
@@ -810,7 +837,8 @@ rz_status rz_sample_tokens_mx(const void* hidden, const uint8_t* codes,
   }
   RZ_TRY(launch_draw_merge(w.cand, w.candz, n_rows, nt, n_rows, tokens, w.ztgt, s));
   RZ_TRY(launch_lse_merge(w.partials, n_rows, nt, rows, w.ztgt, tokens, V,
-                          lse, logmu, nullptr, nullptr, nullptr, s));
+                          lse, logmu, nullptr, nullptr, nullptr, nullptr,
+                          nullptr, s));
   return RZ_OK;
 }
 

@@ -17,7 +17,9 @@ enum KernelId {
   K_LSE_MERGE,       // bi_logsoftmax_gather merge
   K_ROWS_FINALIZE,
   K_COEF,
-  K_DZ_SCALE,        // dlogits from the forward's stored exp(z - m_tile)
+  K_DZ_SCALE,        // fp32 dlogits from the forward's stored exp(z - m_tile)
+  K_EREBASE,         // bf16 e: rows whose tiles straddle the e window
+  K_CHUNK_SCALE,     // bf16 dW: the chunk's power of two
   K_RESP_SUMS,       // rz_loss: S_i
   K_LOSS_VALUE,      // rz_loss: L
   K_DIAG_PARTIAL,    // rz_diagnostics
@@ -106,11 +108,19 @@ hipError_t launch_resp_diag(const float* logpi, const float* logmu,
                             const uint8_t* mask, const int* cu, int B,
                             int64_t n, float* d3, float* kl, int* err,
                             hipStream_t s);
+// eref / eflag (bf16 learner call, else null): the row's e reference and
+// whether its tiles need k_erebase
 hipError_t launch_lse_merge(const float2* partials, int64_t ldp, int nt,
                             DevRows rows, const float* ztgt,
                             const int* row_tokens, int V, float* lse_out,
                             float* logpi_out, const int* scatter_idx,
-                            float* logprobs_rows, int* err, hipStream_t s);
+                            float* logprobs_rows, int* err, float* eref,
+                            int* eflag, hipStream_t s);
+// bf16 e [rows][lde]: the flagged rows' tiles rebased to the row reference
+hipError_t launch_erebase(void* e, int64_t lde, DevRows rows,
+                          const float2* partials, int64_t ldp, int nt,
+                          const float* eref, const int* eflag, int Vpad,
+                          hipStream_t s);
 hipError_t launch_mask_compact(const uint8_t* mask, int64_t n,
                                const int* tokens, const int* cu, int B,
                                int* blk, int* nvalid, int* bad_cu, int* idx,
@@ -133,35 +143,47 @@ hipError_t launch_loss_value(const uint8_t* mask, const float* logprobs,
                              const float* logmu, int64_t n, const int* cu,
                              int B, int sc, const int* T, const double* Ad,
                              double* S, float* loss, hipStream_t s);
-// coef = c_t; coef1 = c_t (1 - p[a_t]), the token column's exact term
+// coef = c_t; coef1 = c_t (1 - p[a_t]), the token column's exact term.
+// bf16 learner (eref non-null): also gsc = g_t = exp(r*_t ln 2 - lse_t),
+// fexp_part [coef_blocks(rows.cap)] and the chunk's sigma
+int coef_blocks(int cap);
 hipError_t launch_coef(DevRows rows, const float* logpi_v, const float* logmu,
                        const int* idx, const int* respv, const double* fcoef,
-                       int sc, float* coef, float* coef1, hipStream_t s);
+                       int sc, float* coef, float* coef1, const float* lse_v,
+                       const float* eref, float* gsc, int* fexp_part,
+                       int* sigma, hipStream_t s);
 size_t diag_partials_bytes(int64_t n);
 hipError_t launch_diagnostics(const float* logpi, const float* logmu,
                               const uint8_t* mask, int64_t n, void* partials,
                               float* diag, hipStream_t s);
+// rs_c / rs_g / rs_sigma (bf16 only, else null): row r scaled by
+// c_r g_r 2^sigma before the transpose
 hipError_t launch_transpose(int dt, int kid, const void* in, int64_t ld_in,
                             const int* rowmap, DevRows rows, int rows_pad,
                             int cols, void* out, int64_t ld_out,
-                            hipStream_t s);
-hipError_t launch_dz_scale(int dt, void* dz, int64_t ldz, void* dzT,
-                           int64_t ldzt, DevRows rows, const float2* partials,
-                           int64_t ldp, const float* lse, const float* coef,
+                            const float* rs_c, const float* rs_g,
+                            const int* rs_sigma, hipStream_t s);
+// fp32 learner only
+hipError_t launch_dz_scale(float* dz, int64_t ldz, float* dzT, int64_t ldzt,
+                           DevRows rows, const float2* partials, int64_t ldp,
+                           const float* lse, const float* coef,
                            const int* tokv, int Vpad, hipStream_t s);
+// bf16: dz = the stored e, scaled by rcoef (c_t) and rg (g_t) in the
+// epilogue; fp32: dz, rcoef = rg = null
 hipError_t launch_bwd_dh(int dt, const void* dz, int64_t ldz, DevRows rows,
                          const void* WT, int64_t ldwt, int H, int V, int Vpad,
                          const int* idx, const int* tokv, const float* coef,
+                         const float* rcoef, const float* rg,
                          const void* lm_head, float* d_hidden, hipStream_t s);
-// bf16: dz = dz [C][Vpad] (ld = Vpad), read K-major; fp32: dz = dz^T
-// [Vpad][C] (ld = C)
+// bf16: dz = e [C][Vpad] (ld = Vpad), read K-major, hT scaled per row and
+// sigma the chunk's power of two; fp32: dz = dz^T [Vpad][C] (ld = C)
 // Floats of the dW split workspace (launch_bwd_dw's part) for a head of
 // V rows and H gradient columns.
 int64_t dw_part_floats(int V, int H);
 hipError_t launch_bwd_dw(int dt, const void* dz, int64_t ld, DevRows krows,
                          const void* hT, int64_t ldht, int H, int V, int Vpad,
                          float* d_lm_head, int first, float* part,
-                         hipStream_t s);
+                         const int* sigma, hipStream_t s);
 // floats of the parked run sums of launch_dw_fix for at most cap rows
 int64_t dw_fix_cont_floats(int64_t cap, int H);
 hipError_t launch_dw_fix(int dt, const int* nvalid, int64_t cap,

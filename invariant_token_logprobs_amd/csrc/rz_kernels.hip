@@ -19,6 +19,7 @@ namespace rz {
 namespace {
 
 constexpr float kNegInf = -__builtin_inff();
+constexpr int kIntMin = -2147483647 - 1;
 
 // Row counts up to which the forward runs on the 64-row tile (measured at
 // the Qwen3-4B head: the logits forward gains up to 128 rows, the draw, whose
@@ -60,7 +61,7 @@ struct FwdArgs {
   int V, Vpad, nk, mt, nt;
   float2* partials;       // [nt][ldp] by list position
   int64_t ldp;
-  void* e;                // learner call only: exp(z - m_tile) [rows][lde]
+  void* e;                // learner call only: e (see EStore) [rows][lde]
   int64_t lde;
   const uint64_t* row_ids;  // sampling call only: the rows' identities
   uint64_t seed;
@@ -74,18 +75,42 @@ struct FwdArgs {
   int* err;               // MX head only: RZ_DEVERR_MX_SCALE
 };
 
-// Storage type of e = exp(z - m_tile) in (0, 1]: fp16 for bf16 inputs (an
-// 11-bit significand at the same two bytes, so that e's rounding adds a
-// quarter of the bf16 rounding the dlogits already carry), fp32 otherwise.
-// The fp16 copy holds e * 2^kEScaleLog2, which keeps every e >= 2^-28 a
-// normal fp16 number (a peaked softmax puts many e far below fp16's smallest
-// normal, 2^-14, where its relative precision is lost) and stays below fp16's
-// largest value at e = 1; the dz rescale undoes the power of two exactly.
+// What the learner's forward stores for the backward.
+//
+// fp32 inputs: e = exp(z - m_tile) in (0, 1], which the dz rescale turns
+// into dz = c_t exp(m_tile - lse_t) e (and dz^T) once lse is known.
+//
+// bf16 inputs: e = exp(z - r ln 2) rounded to bf16, the backward GEMMs' A
+// operand as it stands.  r is an integer fixed by the tile maximum alone
+// (e_ref2): 0 while m_tile log2 e lies in [-kERefLo2, kERefHi2], else the
+// nearest integer that brings the tile maximum's e back to that window, so
+// e never overflows and a tile's largest terms stay normal.  With r the same
+// over a row's tiles, dz = c_t exp(r ln 2 - lse_t) e: one factor per row,
+// which the dHidden epilogue applies in fp32 and the dW GEMM takes through
+// its other operand (h^T scaled per row).  A row whose tiles straddle the
+// window (a tile maximum past 2^80 or below 2^-32 in e units; no realistic
+// logits do this) has its tiles rebased to the row's own r by exact powers of
+// two (k_erebase).  The row's own token column and the rows past the chunk's
+// count up to the next multiple of 64 (the dW GEMM's last K stage) are 0.
 template <typename T> struct EStore { typedef float type; };
-template <> struct EStore<bf16> { typedef _Float16 type; };
-constexpr float kEScale = 16384.f;         // 2^14
-constexpr float kEUnscale = 1.f / 16384.f;  // 2^-14
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+template <> struct EStore<bf16> { typedef bf16 type; };
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+constexpr float kERefHi2 = 80.f;  // e <= 2^80: V e |W| stays far inside fp32
+constexpr float kERefLo2 = 32.f;  // a tile maximum's e >= 2^-32
+__device__ __forceinline__ float e_ref2(float m) {
+  const float mu = m * kLog2e;
+  return mu > kERefHi2 ? ceilf(mu - kERefHi2)
+                       : (mu < -kERefLo2 ? floorf(mu + kERefLo2) : 0.f);
+}
+// two bf16 values in one word, each times f and rounded to bf16 (nearest
+// even)
+__device__ __forceinline__ uint32_t scale_bf16x2(uint32_t w, float f) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = {__builtin_bit_cast(float, w << 16) * f,
+                   __builtin_bit_cast(float, w & 0xffff0000u) * f};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
 template <bool B> struct BoolC { static constexpr bool value = B; };
 template <int I> struct IntC { static constexpr int value = I; };
 // f(IntC<I>{}) for I = B .. E - 1: indices stay compile-time constants
@@ -165,7 +190,7 @@ __device__ __forceinline__ bool draw_better(float s, int v, float bs, int bv) {
 // bi_lmhead_gemm + the log-softmax statistics of one 256 x 256 logits tile
 // (vocab tile j = tn): per row t, m_tile = max_v z[t, v] and
 // s_tile = sum_v exp(z[t, v] - m_tile), written to partials[j][t]; on the
-// learner call also e = exp(z - m_tile) for the backward.
+// learner call also e for the backward (see EStore).
 //
 // The MFMAs run with swapped operands (see gemm_mainloop), so each lane
 // holds one row t and, per 32 x 32 block, four runs of four consecutive
@@ -294,7 +319,7 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
     rm[mi] = fmaxf(wmax[R], wmax[BM + R]);
   }
 
-  // e = exp(z - m_tile) once per element, 0 for columns >= V; row sums in a
+  // exp(z - m_tile) once per element, 0 for columns >= V; row sums in a
   // fixed order
   typedef typename EStore<T>::type E;
   E* e = reinterpret_cast<E*>(a.e);
@@ -312,6 +337,10 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
       // log pi = z[a_t] - lse <= 0 with lse = m exactly on a row whose other
       // tokens carry less than an ulp of mass.
       const float mrow = rm[mi];
+      // bf16 store: exp(z - r ln 2) = exp(z - m_tile) 2^(m_tile log2 e - r)
+      float esc = 0.f;
+      if constexpr (kStoreE && sizeof(T) == 2)
+        esc = __builtin_amdgcn_exp2f(mrow * kLog2e - e_ref2(mrow));
       float s = 0.f;
 #pragma unroll
       for (int ni = 0; ni < kTN; ++ni)
@@ -327,8 +356,8 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
           }
           if constexpr (kStoreE) {
             if constexpr (sizeof(T) == 2) {
-              const f16x4 hv = {(_Float16)(ev[0] * kEScale), (_Float16)(ev[1] * kEScale),
-                                (_Float16)(ev[2] * kEScale), (_Float16)(ev[3] * kEScale)};
+              const bf16x4 hv = {(bf16)(ev[0] * esc), (bf16)(ev[1] * esc),
+                                 (bf16)(ev[2] * esc), (bf16)(ev[3] * esc)};
               *reinterpret_cast<u32x2*>(
                   lds + e_stage_off(R, wn * 16 + ni * 4 + q) + half * 8) =
                   __builtin_bit_cast(u32x2, hv);
@@ -346,6 +375,23 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
   };
   if (n0 + kBN <= a.V) pass2(BoolC<true>{});
   else pass2(BoolC<false>{});
+  if constexpr (kStoreE && sizeof(T) == 2 && kTokOff >= 0) {
+    // the row's own token column stays 0 in e (its dL/dz is applied exactly
+    // in fp32 elsewhere): the lane that holds it clears its staged value
+    if (a.row_tokens) {
+#pragma unroll
+      for (int mi = 0; mi < TM; ++mi) {
+        const int R = wm * RW + mi * 32 + l32;
+        if (m0 + R >= M) continue;
+        const int tok = reinterpret_cast<const int*>(lds + kTokOff)[R];
+        const int off = tok - cbase;
+        if (tok >= 0 && tok < a.V && off >= 0 && off < 128 && (off & 4) == 0)
+          *reinterpret_cast<uint16_t*>(
+              lds + e_stage_off(R, wn * 16 + (off >> 5) * 4 + ((off >> 3) & 3)) +
+              half * 8 + 2 * (off & 3)) = 0;
+      }
+    }
+  }
   if constexpr (kSample) {
     // The draw: per row, the best z + g over the tile's columns < V (see
     // gumbel_of_bits; counter (v / 4, id_lo, id_hi, 0), key = the seed, word
@@ -426,18 +472,21 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
   }
   if constexpr (kStoreE && sizeof(T) == 2) {
     // 16-byte row chunks: 32 lanes cover one 512-byte tile row.  Columns
-    // >= V hold 0; rows >= M and columns >= Vpad are not stored.  The e
-    // stream (2 bytes per logit) is read back only by the dz rescale, long
-    // after: non-temporal stores keep it from evicting the operand panels
-    // that the co-resident tiles share in L2.
+    // >= V hold 0; rows from M up to the next multiple of 64 (read by the
+    // dW GEMM's last K stage) are stored as 0, rows past that and columns
+    // >= Vpad not at all.  The e stream (2 bytes per logit) is read back by
+    // the backward GEMMs, long after: non-temporal stores keep it from
+    // evicting the operand panels that the co-resident tiles share in L2.
+    const int Mz = (M + 63) & ~63;
 #pragma unroll 4
     for (int it = 0; it < 32; ++it) {
       const int idx = it * 256 + tid;
       const int R = idx >> 5, k = idx & 31;
       const int col = n0 + k * 8;
-      if (m0 + R < M && col < a.Vpad)
+      if (m0 + R < Mz && col < a.Vpad)
         __builtin_nontemporal_store(
-            *reinterpret_cast<const u32x4*>(lds + e_stage_off(R, k)),
+            m0 + R < M ? *reinterpret_cast<const u32x4*>(lds + e_stage_off(R, k))
+                       : u32x4{0u, 0u, 0u, 0u},
             reinterpret_cast<u32x4*>(e + (int64_t)(m0 + R) * a.lde + col));
     }
   }
@@ -512,17 +561,21 @@ __device__ __forceinline__ void ms_merge(float& m, float& s, float mj, float sj)
   ms_fold(m, s, mj, sj);
 }
 
+// Learner call (eref non-null): also the row's e reference r* = e_ref2 of
+// the row maximum, and whether any of its tiles was stored against another
+// (e_ref2 is monotone, so that is exactly when the smallest tile maximum
+// maps elsewhere); k_erebase fixes those rows.
 __global__ __launch_bounds__(256) void k_lse_merge(
     const float2* __restrict__ partials, int64_t ldp, int nt, DevRows rows,
     const float* __restrict__ ztgt, const int* __restrict__ row_tokens, int V,
     float* lse_out, float* logpi_out, const int* scatter_idx,
-    float* logprobs_rows, int* err) {
+    float* logprobs_rows, int* err, float* eref, int* eflag) {
   const RowCount rc = to_rc(rows);
   const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int q = threadIdx.x & 63;
   if (p >= rc.get()) return;  // uniform per wave
   const int64_t pos = rc.base + p;
-  float m = kNegInf, s = 0.f;
+  float m = kNegInf, s = 0.f, mlo = __builtin_inff();
   for (int t0 = q; t0 < nt; t0 += 64 * kMergeBatch) {
     // loads issued kMergeBatch at a time, folded in ascending tile order
     float2 ms[kMergeBatch];
@@ -533,23 +586,27 @@ __global__ __launch_bounds__(256) void k_lse_merge(
     }
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j)
-      if (t0 + 64 * j < nt) ms_merge(m, s, ms[j].x, ms[j].y);
+      if (t0 + 64 * j < nt) {
+        ms_merge(m, s, ms[j].x, ms[j].y);
+        mlo = fminf(mlo, ms[j].x);
+      }
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     const float mj = __shfl_xor(m, o, 64);
     const float sj = __shfl_xor(s, o, 64);
     ms_merge(m, s, mj, sj);
+    if (eref) mlo = fminf(mlo, __shfl_xor(mlo, o, 64));
   }
   if (q != 0) return;
   const float lse = m + logf(s);
   const int tok = row_tokens[pos];
   float lp;
   if (tok >= 0 && tok < V) {
-    // The target logit's fp32 dot product and the MFMA sums behind lse
-    // round differently, so on a row where the token takes nearly all the
-    // mass the difference can land a few ulps above 0; a logprob is <= 0.
-    // (NaN stays NaN.)
+    // z[a_t] is an element of the tile statistics' own accumulators, so
+    // z[a_t] <= m <= lse (the tile holding the maximum adds exp2(0) = 1 to
+    // s) and lp <= 0 already; the clamp keeps that promise for any input
+    // (NaN stays NaN).
     lp = ztgt[pos] - lse;
     lp = lp > 0.f ? 0.f : lp;
   } else {
@@ -559,6 +616,11 @@ __global__ __launch_bounds__(256) void k_lse_merge(
   if (lse_out) lse_out[pos] = lse;
   if (logpi_out) logpi_out[pos] = lp;
   if (scatter_idx) logprobs_rows[scatter_idx[pos]] = lp;
+  if (eref) {
+    const float r = e_ref2(m);
+    eref[pos] = r;
+    eflag[pos] = e_ref2(mlo) != r;
+  }
 }
 
 // The draw's merge: per row (one wave), the best (score, index) over the
@@ -867,22 +929,65 @@ __global__ __launch_bounds__(256) void k_loss_value(const double* Ad,
 // kept in fp32 (coef1 holds its negative): the bf16 dlogits leave that
 // column out, because on a row whose token takes nearly all the mass
 // c_t p[a_t] and c_t cancel to far less than bf16's rounding of either.
+//
+// bf16 learner (eref non-null): also g_t = exp(r*_t ln 2 - lse_t), the
+// factor that turns the stored e into the softmax, and per workgroup the
+// largest binary exponent of a finite nonzero c_t g_t (fexp_part); the
+// chunk's scale 2^sigma (k_chunk_scale) brings the largest to [1/2, 1).
 __global__ __launch_bounds__(256) void k_coef(DevRows rows,
                                               const float* logpi_v,
                                               const float* logmu,
                                               const int* idx,
                                               const int* respv,
                                               const double* fcoef, int sc,
-                                              float* coef, float* coef1) {
+                                              float* coef, float* coef1,
+                                              const float* lse_v,
+                                              const float* eref, float* gsc,
+                                              int* fexp_part) {
   const RowCount rc = to_rc(rows);
   const int q = blockIdx.x * 256 + threadIdx.x;
-  if (q >= rc.get()) return;
-  const int64_t p = rc.base + q;
-  const float lp = logpi_v[p];
-  const double c = sc ? fcoef[respv[p]]
-                      : fcoef[respv[p]] * (double)expf(lp - logmu[idx[p]]);
-  coef[p] = (float)c;
-  coef1[p] = (float)(-c * expm1((double)lp));
+  int ex = kIntMin;
+  if (q < rc.get()) {
+    const int64_t p = rc.base + q;
+    const float lp = logpi_v[p];
+    const double c = sc ? fcoef[respv[p]]
+                        : fcoef[respv[p]] * (double)expf(lp - logmu[idx[p]]);
+    coef[p] = (float)c;
+    coef1[p] = (float)(-c * expm1((double)lp));
+    if (eref) {
+      const float g = (float)exp2((double)eref[p] - (double)lse_v[p] * 1.4426950408889634);
+      gsc[p] = g;
+      const double f = (double)(float)c * (double)g;
+      if (f != 0.0 && isfinite(f)) ex = ilogb(f);
+    }
+  }
+  if (!eref) return;
+  // the workgroup's largest exponent: a fixed tree over exact integers
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) ex = max(ex, __shfl_xor(ex, o, 64));
+  __shared__ int wex[4];
+  if ((threadIdx.x & 63) == 0) wex[threadIdx.x >> 6] = ex;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    fexp_part[blockIdx.x] = max(max(wex[0], wex[1]), max(wex[2], wex[3]));
+}
+
+// sigma = -(1 + the largest exponent of the chunk's c_t g_t), or 0 if none
+// is finite and nonzero: the dW operand h^T carries c_t g_t 2^sigma <= 1 in
+// magnitude and the dW store takes 2^-sigma back (both exact powers of two).
+__global__ __launch_bounds__(256) void k_chunk_scale(const int* fexp_part,
+                                                     int nblk, int* sigma) {
+  int ex = kIntMin;
+  for (int i = threadIdx.x; i < nblk; i += 256) ex = max(ex, fexp_part[i]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) ex = max(ex, __shfl_xor(ex, o, 64));
+  __shared__ int wex[4];
+  if ((threadIdx.x & 63) == 0) wex[threadIdx.x >> 6] = ex;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    ex = max(max(wex[0], wex[1]), max(wex[2], wex[3]));
+    *sigma = ex == kIntMin ? 0 : -(ex + 1);
+  }
 }
 
 // ===================================================================
@@ -1279,13 +1384,20 @@ __global__ __launch_bounds__(256) void k_lora_da_final(const float* __restrict__
 // 16-byte row pieces in, a transpose in registers, kVec 16-byte column
 // pieces out.  Eight lanes (bf16) cover one 128-byte line on either side.
 // rows_pad and cols are multiples of 64.
-template <typename T>
+//
+// Row scale (bf16 only, rs_c non-null): row r is multiplied by
+// c_r g_r 2^sigma (k_coef, k_chunk_scale) and rounded to bf16 once: the dW
+// GEMM's B operand then carries the row's whole softmax factor.
+template <typename T, bool kScale = false>
 __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ in,
                                                    int64_t ld_in,
                                                    const int* rowmap,
                                                    DevRows rows, int rows_pad,
                                                    int cols, T* __restrict__ out,
-                                                   int64_t ld_out) {
+                                                   int64_t ld_out,
+                                                   const float* rs_c,
+                                                   const float* rs_g,
+                                                   const int* rs_sigma) {
   constexpr int kVec = 16 / (int)sizeof(T);       // 8 (bf16) or 4 (fp32)
   constexpr int kG = 64 / kVec;                   // row blocks per wave
   constexpr int kWaveCols = (64 / kG) * kVec;     // 64 (bf16) or 16 (fp32)
@@ -1306,6 +1418,17 @@ __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ in,
     if (r < R) {
       const int64_t pr = rowmap ? (int64_t)rowmap[rc.base + r] : rc.base + r;
       x[i] = *reinterpret_cast<const u32x4*>(in + pr * ld_in + col);
+    }
+  }
+  if constexpr (kScale) {
+    // rows past R hold 0 and stay 0 (their scale is read from row R - 1)
+    const int sg = *rs_sigma;
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) {
+      const int64_t p = rc.base + min(r0 + tr + i, R - 1);
+      const float f = (float)ldexp((double)rs_c[p] * (double)rs_g[p], sg);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) x[i][w] = scale_bf16x2(x[i][w], f);
     }
   }
   if constexpr (sizeof(T) == 2) {
@@ -1330,144 +1453,116 @@ __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ in,
 }
 
 // ===================================================================
-// Backward, part 1: dlogits.  The forward of the learner call stored
-// e[t, v] = exp(z[t, v] - m_tile(t, j)) (EStore type, times 2^14 for fp16, in the dz buffer) for
-// the vocab tile j holding v; with
-// lse_t known, dz[t, v] = c_t * exp(m_tile(t, j) - lse_t) * e[t, v] is
-// dL/dz for v != a_t; the token's own column is left at 0 and its whole
-// dL/dz, c_t (p[a_t] - 1), is applied exactly in fp32 by the dHidden
-// epilogue and the dW fix-up.  The kernel rescales
-// e in place into the token-major dz [C, Vpad], the A operand of dHidden and
-// (bf16, read K-major) of dW.  fp32 has no transposing LDS read, so there
-// the kernel also writes the vocab-major dz^T [Vpad, C] for dW.  Rows from
-// the chunk's count up to the next multiple of 64 (the last K stage of dW)
-// become zero rows of dz (bf16) or zero columns of dz^T (fp32).
+// Backward, part 1: dlogits.
 //
-// Each lane owns a kVec x kVec block (kVec = values per 16 bytes): it reads
-// kVec 16-byte row pieces and writes them back rescaled; for fp32 it then
-// transposes the block in registers and writes kVec 16-byte column pieces
-// of dz^T.  Eight lanes (bf16) cover one 128-byte line of a dz row; no LDS
-// round trip.  A bf16 workgroup covers two vocab tiles of 64 rows and issues
-// its e loads before it reads the row scales' inputs, so the two latencies
-// overlap.
+// fp32 inputs: the forward stored e[t, v] = exp(z[t, v] - m_tile(t, j)) in
+// the dz buffer for the vocab tile j holding v; with lse_t known,
+// dz[t, v] = c_t exp(m_tile(t, j) - lse_t) e[t, v] is dL/dz for v != a_t; the
+// token's own column is left at 0 and its whole dL/dz, c_t (p[a_t] - 1), is
+// applied exactly in fp32 by the dHidden epilogue and the dW fix-up.
+// k_dz_scale rescales e in place into the token-major dz [C, Vpad], the A
+// operand of dHidden, and also writes the vocab-major dz^T [Vpad, C] for
+// dW (fp32 has no transposing LDS read).  Rows from the chunk's count up to
+// the next multiple of 64 (the last K stage of dW) become zero columns of
+// dz^T.  Each lane owns a 4 x 4 block: four 16-byte row pieces in and back
+// rescaled, a transpose in registers, four 16-byte column pieces of dz^T out.
+//
+// bf16 inputs need no pass here: the stored e is already the A operand
+// (see EStore), and the factor c_t exp(r*_t ln 2 - lse_t) rides on the other
+// side of each GEMM.  Only the rows whose tiles straddle the e window are
+// rebased (k_erebase).
 // ===================================================================
-template <typename T>
 __global__ __launch_bounds__(256) void k_dz_scale(
-    T* __restrict__ dz, int64_t ldz, T* __restrict__ dzT, int64_t ldzt,
+    float* __restrict__ dz, int64_t ldz, float* __restrict__ dzT, int64_t ldzt,
     DevRows rows, const float2* __restrict__ partials, int64_t ldp,
     const float* __restrict__ lse, const float* __restrict__ coef,
     const int* __restrict__ tokv, int Vpad) {
-  constexpr int kVec = 16 / (int)sizeof(T);       // 8 (bf16) or 4 (fp32)
-  constexpr int kG = 64 / kVec;                   // row blocks per wave
-  constexpr int kWaveCols = (64 / kG) * kVec;     // 64 (bf16) or 16 (fp32)
-  constexpr int kBlockCols = 4 * kWaveCols;       // within one vocab tile
-  constexpr int kSpan = sizeof(T) == 2 ? 2 : 1;   // column blocks per workgroup
-  __shared__ float sc[kSpan][64];
+  __shared__ float sc[64];
   __shared__ int stok[64];  // the rows' tokens: their column is left at 0
   const RowCount rc = to_rc(rows);
   const int R = rc.get();
   const int r0 = blockIdx.y * 64;
   if (r0 >= ((R + 63) & ~63)) return;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int tr = (lane % kG) * kVec;             // first row of the block
-  // first column of this wave's piece of column block b (whole waves past
-  // Vpad, a multiple of 64, have nothing to do)
-  auto wave_col = [&](int b) {
-    return (blockIdx.x * kSpan + b) * kBlockCols + wid * kWaveCols;
-  };
-  // bf16: the e pieces are loaded first, so their latency overlaps that of
-  // the scales' inputs below
-  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-  u32x4 x[kSpan][8];
-  if constexpr (sizeof(T) == 2) {
-#pragma unroll
-    for (int b = 0; b < kSpan; ++b) {
-      const int col = wave_col(b) + (lane / kG) * kVec;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int t = r0 + tr + i;
-        if (wave_col(b) < Vpad && t < R)  // read once: non-temporal
-          x[b][i] = __builtin_nontemporal_load(
-              reinterpret_cast<const u32x4*>(dz + (int64_t)t * ldz + col));
-      }
-    }
-  }
-  // one scale per row and column block: c_t exp(m_tile(t, j) - lse_t), j the
-  // vocab tile holding the block
-  if (tid < 64 * kSpan) {
-    const int b = tid >> 6, t = r0 + (tid & 63);
-    const int j = ((blockIdx.x * kSpan + b) * kBlockCols) / kBN;
+  const int tr = (lane % 16) * 4;  // first row of the block
+  // one scale per row: c_t exp(m_tile(t, j) - lse_t), j the vocab tile
+  // holding the workgroup's 64 columns
+  if (tid < 64) {
+    const int t = r0 + tid;
+    const int j = (blockIdx.x * 64) / kBN;
     float v = 0.f;
-    if (t < R && j * kBN < Vpad) {
+    if (t < R) {
       const int64_t pos = rc.base + t;
       v = coef[pos] * exp_approx(partials[(int64_t)j * ldp + pos].x - lse[pos]);
     }
-    sc[b][tid & 63] = v;
-    if (b == 0) stok[tid] = t < R ? tokv[rc.base + t] : -1;
+    sc[tid] = v;
+    stok[tid] = t < R ? tokv[rc.base + t] : -1;
   }
   __syncthreads();
-  if constexpr (sizeof(T) == 2) {
+  const int cw = blockIdx.x * 64 + wid * 16;
+  if (cw >= Vpad) return;
+  const int col = cw + (lane / 16) * 4;
+  f32x4 y[4];
 #pragma unroll
-    for (int b = 0; b < kSpan; ++b) {
-      if (wave_col(b) >= Vpad) continue;
-      const int col = wave_col(b) + (lane / kG) * kVec;
+  for (int i = 0; i < 4; ++i) {
+    const int t = r0 + tr + i;
+    if (t < R) {
+      float* p = dz + (int64_t)t * ldz + col;
+      y[i] = sc[tr + i] * *reinterpret_cast<const f32x4*>(p);
+      const uint32_t own = (uint32_t)(stok[tr + i] - col);  // stays 0
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int t = r0 + tr + i;
-        T* p = dz + (int64_t)t * ldz + col;
-        if (t < R) {
-          const f16x8 e = __builtin_bit_cast(f16x8, x[b][i]);
-          const float f = sc[b][tr + i];
-          // the row's own token (if among these 8 columns) stays 0
-          const uint32_t own = (uint32_t)(stok[tr + i] - col);
-          uint32_t y[4];
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            // e was stored times 2^14: unscaled exactly before the product
-            const uint32_t lo = __builtin_bit_cast(
-                uint16_t, (T)(f * ((float)e[2 * w] * kEUnscale)));
-            const uint32_t hi = __builtin_bit_cast(
-                uint16_t, (T)(f * ((float)e[2 * w + 1] * kEUnscale)));
-            y[w] = (own == 2u * w ? 0u : lo) | ((own == 2u * w + 1 ? 0u : hi) << 16);
-          }
-          // dz (10 GB per chunk) reaches the GEMMs from HBM in any case
-          __builtin_nontemporal_store(u32x4{y[0], y[1], y[2], y[3]},
-                                      reinterpret_cast<u32x4*>(p));
-        } else {
-          __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u}, reinterpret_cast<u32x4*>(p));
-        }
-      }
+      for (int w = 0; w < 4; ++w) y[i][w] = own == (uint32_t)w ? 0.f : y[i][w];
+      *reinterpret_cast<f32x4*>(p) = y[i];
+    } else {
+      y[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-  } else {
-    const int cw = wave_col(0);
-    if (cw >= Vpad) return;
-    const int col = cw + (lane / kG) * kVec;
-    f32x4 y[4];
+  }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = r0 + tr + i;
-      if (t < R) {
-        T* p = dz + (int64_t)t * ldz + col;
-        y[i] = sc[0][tr + i] * *reinterpret_cast<const f32x4*>(p);
-        const uint32_t own = (uint32_t)(stok[tr + i] - col);  // stays 0
+  for (int q = 0; q < 4; ++q)
+    *reinterpret_cast<f32x4*>(dzT + (int64_t)(col + q) * ldzt + r0 + tr) =
+        f32x4{y[0][q], y[1][q], y[2][q], y[3][q]};
+}
+
+// bf16 rows whose vocab tiles were stored against different e references
+// (k_lse_merge's flag): each tile j with r_j != r*_t is multiplied by
+// 2^(r_j - r*_t) <= 1, an exact power of two, so those tiles share the row's
+// reference without a second rounding.  One wave per row; the other rows
+// return at once.
+__global__ __launch_bounds__(256) void k_erebase(
+    bf16* __restrict__ e, int64_t lde, DevRows rows,
+    const float2* __restrict__ partials, int64_t ldp, int nt,
+    const float* __restrict__ eref, const int* __restrict__ eflag, int Vpad) {
+  const RowCount rc = to_rc(rows);
+  const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (p >= rc.get()) return;
+  const int64_t pos = rc.base + p;
+  if (!eflag[pos]) return;  // uniform per wave
+  const float rs = eref[pos];
+  const int lane = threadIdx.x & 63;
+  bf16* row = e + (int64_t)p * lde;
+  for (int j = 0; j < nt; ++j) {
+    const float d = e_ref2(partials[(int64_t)j * ldp + pos].x) - rs;
+    if (d == 0.f) continue;  // uniform per wave
+    const int c = j * kBN + lane * 4;
+    if (c >= Vpad) continue;
+    // d <= 0 (e_ref2 is monotone and r* is the row maximum's); far below,
+    // the products flush to 0 (their terms are below 2^-1000 of the row's)
+    const int k = d < -1000.f || d != d ? -1000 : (int)d;
+    u32x2* q = reinterpret_cast<u32x2*>(row + c);
+    bf16x4 v = __builtin_bit_cast(bf16x4, *q);
 #pragma unroll
-        for (int w = 0; w < 4; ++w) y[i][w] = own == (uint32_t)w ? 0.f : y[i][w];
-        *reinterpret_cast<f32x4*>(p) = y[i];
-      } else {
-        y[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<f32x4*>(dzT + (int64_t)(col + q) * ldzt + r0 + tr) =
-          f32x4{y[0][q], y[1][q], y[2][q], y[3][q]};
+    for (int i = 0; i < 4; ++i) v[i] = (bf16)ldexpf((float)v[i], k);
+    *q = __builtin_bit_cast(u32x2, v);
   }
 }
 
 // ===================================================================
 // Backward, part 2: dHidden = dz W (K = Vpad in fixed order) plus the token
 // column's exact term c_t (p[a_t] - 1) W[a_t, :] (coef holds its
-// negative), scattered to the rows' positions.
+// negative), scattered to the rows' positions.  bf16: the A operand is the
+// stored e, and the row's factor is applied here in fp32 as
+// c_t (g_t acc) (two products, so that neither factor's range limits the
+// other's).
 // ===================================================================
 template <typename T>
 struct DhArgs {
@@ -1475,7 +1570,9 @@ struct DhArgs {
   DevRows rows;
   const int* idx;
   const int* tokv;
-  const float* coef;
+  const float* coef;   // the token column's term (negated)
+  const float* rc;     // bf16: c_t; fp32: nullptr (dz is already scaled)
+  const float* rg;     // bf16: g_t
   const T* W;
   int H, V, nk, mt, nt;
   float* dh;
@@ -1501,6 +1598,9 @@ __global__ RZ_GEMM_ATTR void k_bwd_dh(DhArgs<T> a) {
   int* sidx = reinterpret_cast<int*>(lds);
   int* stok = sidx + 256;
   float* scoef = reinterpret_cast<float*>(stok + 256);
+  float* src = scoef + 256;
+  float* srg = src + 256;
+  constexpr bool kScaled = sizeof(T) == 2;  // bf16: A was the stored e
   {
     const int m = m0 + tid;
     const int64_t p = rc.base + m;
@@ -1508,8 +1608,25 @@ __global__ RZ_GEMM_ATTR void k_bwd_dh(DhArgs<T> a) {
     int tk = m < M ? a.tokv[p] : 0;
     stok[tid] = (tk >= 0 && tk < a.V) ? tk : 0;
     scoef[tid] = m < M ? a.coef[p] : 0.f;
+    if constexpr (kScaled) {
+      src[tid] = m < M ? a.rc[p] : 0.f;
+      srg[tid] = m < M ? a.rg[p] : 0.f;
+    }
   }
   __syncthreads();
+  if constexpr (kScaled) {
+    // the rows' factors in place, one row's pair of scales at a time
+#pragma unroll
+    for (int mi = 0; mi < kTM; ++mi)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = acc_row(wm, mi, r, lane);
+        const float c = src[row], g = srg[row];
+#pragma unroll
+        for (int ni = 0; ni < kTN; ++ni) acc[mi][ni][r] = c * (g * acc[mi][ni][r]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  }
 #pragma unroll
   for (int mi = 0; mi < kTM; ++mi)
 #pragma unroll
@@ -1529,11 +1646,15 @@ __global__ RZ_GEMM_ATTR void k_bwd_dh(DhArgs<T> a) {
 
 // ===================================================================
 // Backward, part 3: dW (+)= dz^T h over this chunk's tokens (K in fixed
-// order); chunks are accumulated in order, the first one overwrites.
+// order); chunks are accumulated in order, the first one overwrites.  bf16:
+// A is the stored e (read K-major) and B is h^T with row t scaled by
+// c_t g_t 2^sigma, so the tile holds 2^sigma dW; the store takes 2^-sigma
+// back exactly.
 // ===================================================================
 struct DwArgs {
-  GemmOperands op;  // bf16: A = dz [K rows][Vpad], K-major; fp32: A = dz^T
+  GemmOperands op;  // bf16: A = e [K rows][Vpad], K-major; fp32: A = dz^T
   DevRows krows;
+  const int* sigma;  // bf16: the chunk's power of two; fp32: nullptr
   int V, H, amax, kstage, mt, nt, first;  // amax: A columns (bf16) / rows
   // The last round of tiles splits K: T = mt nt tiles, of which the tail
   // (those map_tile numbers T - tail .. T - 1) run as split pieces each,
@@ -1553,6 +1674,7 @@ __device__ __forceinline__ void dw_store(const DwArgs& a, int m0, int n0,
                                          f32x16 (&acc)[kTM][kTN]) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
+  const int unscale = a.sigma ? -*a.sigma : 0;
 #pragma unroll
   for (int mi = 0; mi < kTM; ++mi)
 #pragma unroll
@@ -1570,7 +1692,8 @@ __device__ __forceinline__ void dw_store(const DwArgs& a, int m0, int n0,
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int v = m0 + acc_row(wm, mi, r, lane);
-        if (v < a.V) a.dw[(int64_t)v * a.H + h] = prev[r] + acc[mi][ni][r];
+        if (v < a.V)
+          a.dw[(int64_t)v * a.H + h] = prev[r] + ldexpf(acc[mi][ni][r], unscale);
       }
     }
 }
@@ -1917,7 +2040,8 @@ const char* kernel_name(int k) {
   static const char* names[K_NUM_KERNELS] = {
       "mask_count",  "mask_scan",   "mask_scatter", "resp_counts",
       "advantages",  "fwd_logits_gemm", "lse_merge", "rows_finalize",
-      "coef",        "dz_scale",    "resp_sums",    "loss_value",
+      "coef",        "dz_scale",    "erebase",      "chunk_scale",
+      "resp_sums",   "loss_value",
       "diag_partial", "diag_final", "transpose_w",  "transpose_h",
       "bwd_dh_gemm", "bwd_dw_gemm", "sort_hist",    "sort_scan",
       "sort_scatter", "dw_fix",     "dw_fix_span",
@@ -2064,11 +2188,22 @@ hipError_t launch_lse_merge(const float2* partials, int64_t ldp, int nt,
                             DevRows rows, const float* ztgt,
                             const int* row_tokens, int V, float* lse_out,
                             float* logpi_out, const int* scatter_idx,
-                            float* logprobs_rows, int* err, hipStream_t s) {
+                            float* logprobs_rows, int* err, float* eref,
+                            int* eflag, hipStream_t s) {
   return timed(K_LSE_MERGE, s, [&] {
     k_lse_merge<<<cdiv(rows.cap, 4), 256, 0, s>>>(
         partials, ldp, nt, rows, ztgt, row_tokens, V, lse_out, logpi_out,
-        scatter_idx, logprobs_rows, err);
+        scatter_idx, logprobs_rows, err, eref, eflag);
+  });
+}
+
+hipError_t launch_erebase(void* e, int64_t lde, DevRows rows,
+                          const float2* partials, int64_t ldp, int nt,
+                          const float* eref, const int* eflag, int Vpad,
+                          hipStream_t s) {
+  return timed(K_EREBASE, s, [&] {
+    k_erebase<<<cdiv(rows.cap, 4), 256, 0, s>>>((bf16*)e, lde, rows, partials,
+                                                 ldp, nt, eref, eflag, Vpad);
   });
 }
 
@@ -2190,12 +2325,21 @@ hipError_t launch_loss_value(const uint8_t* mask, const float* logprobs,
   });
 }
 
+int coef_blocks(int cap) { return cdiv(cap, 256); }
+
 hipError_t launch_coef(DevRows rows, const float* logpi_v, const float* logmu,
                        const int* idx, const int* respv, const double* fcoef,
-                       int sc, float* coef, float* coef1, hipStream_t s) {
-  return timed(K_COEF, s, [&] {
-    k_coef<<<cdiv(rows.cap, 256), 256, 0, s>>>(rows, logpi_v, logmu, idx,
-                                               respv, fcoef, sc, coef, coef1);
+                       int sc, float* coef, float* coef1, const float* lse_v,
+                       const float* eref, float* gsc, int* fexp_part,
+                       int* sigma, hipStream_t s) {
+  const int nblk = coef_blocks(rows.cap);
+  hipError_t e = timed(K_COEF, s, [&] {
+    k_coef<<<nblk, 256, 0, s>>>(rows, logpi_v, logmu, idx, respv, fcoef, sc,
+                                coef, coef1, lse_v, eref, gsc, fexp_part);
+  });
+  if (e != hipSuccess || !eref) return e;
+  return timed(K_CHUNK_SCALE, s, [&] {
+    k_chunk_scale<<<1, 256, 0, s>>>(fexp_part, nblk, sigma);
   });
 }
 
@@ -2345,37 +2489,37 @@ hipError_t launch_resp_diag(const float* logpi, const float* logmu,
 hipError_t launch_transpose(int dt, int kid, const void* in, int64_t ld_in,
                             const int* rowmap, DevRows rows, int rows_pad,
                             int cols, void* out, int64_t ld_out,
-                            hipStream_t s) {
+                            const float* rs_c, const float* rs_g,
+                            const int* rs_sigma, hipStream_t s) {
   // 64 rows x (4 waves x 64 bf16 or 16 fp32 columns) per workgroup
   dim3 grid(cdiv(rows_pad, 64), cdiv(cols, dt ? 256 : 64));
   return timed(kid, s, [&] {
-    if (dt)
+    if (dt && rs_c)
+      k_transpose<bf16, true><<<grid, 256, 0, s>>>((const bf16*)in, ld_in,
+                                                   rowmap, rows, rows_pad, cols,
+                                                   (bf16*)out, ld_out, rs_c,
+                                                   rs_g, rs_sigma);
+    else if (dt)
       k_transpose<bf16><<<grid, 256, 0, s>>>((const bf16*)in, ld_in, rowmap,
                                              rows, rows_pad, cols, (bf16*)out,
-                                             ld_out);
+                                             ld_out, nullptr, nullptr, nullptr);
     else
       k_transpose<float><<<grid, 256, 0, s>>>((const float*)in, ld_in,
                                               rowmap, rows, rows_pad, cols,
-                                              (float*)out, ld_out);
+                                              (float*)out, ld_out, nullptr,
+                                              nullptr, nullptr);
   });
 }
 
-hipError_t launch_dz_scale(int dt, void* dz, int64_t ldz, void* dzT,
-                           int64_t ldzt, DevRows rows, const float2* partials,
-                           int64_t ldp, const float* lse, const float* coef,
+hipError_t launch_dz_scale(float* dz, int64_t ldz, float* dzT, int64_t ldzt,
+                           DevRows rows, const float2* partials, int64_t ldp,
+                           const float* lse, const float* coef,
                            const int* tokv, int Vpad, hipStream_t s) {
-  // 64 rows x (two column blocks of 4 waves x 64 bf16, or one of 4 x 16
-  // fp32 columns) per workgroup; neighbouring workgroups share rows
-  dim3 grid(cdiv(Vpad, dt ? 512 : 64), cdiv(rows.cap, 64));
+  // 64 rows x (4 waves x 16 columns) per workgroup
+  dim3 grid(cdiv(Vpad, 64), cdiv(rows.cap, 64));
   return timed(K_DZ_SCALE, s, [&] {
-    if (dt)
-      k_dz_scale<bf16><<<grid, 256, 0, s>>>((bf16*)dz, ldz, (bf16*)dzT, ldzt,
-                                            rows, partials, ldp, lse, coef,
-                                            tokv, Vpad);
-    else
-      k_dz_scale<float><<<grid, 256, 0, s>>>((float*)dz, ldz, (float*)dzT,
-                                             ldzt, rows, partials, ldp, lse,
-                                             coef, tokv, Vpad);
+    k_dz_scale<<<grid, 256, 0, s>>>(dz, ldz, dzT, ldzt, rows, partials, ldp,
+                                    lse, coef, tokv, Vpad);
   });
 }
 
@@ -2383,7 +2527,8 @@ template <typename T>
 static hipError_t launch_bwd_dh_t(const void* dz, int64_t ldz, DevRows rows,
                                   const void* WT, int64_t ldwt, int H, int V,
                                   int Vpad, const int* idx, const int* tokv,
-                                  const float* coef, const void* lm_head,
+                                  const float* coef, const float* rcoef,
+                                  const float* rg, const void* lm_head,
                                   float* d_hidden, hipStream_t s) {
   DhArgs<T> a;
   a.op = GemmOperands{(const char*)dz, ldz * (int64_t)sizeof(T), nullptr,
@@ -2393,6 +2538,8 @@ static hipError_t launch_bwd_dh_t(const void* dz, int64_t ldz, DevRows rows,
   a.idx = idx;
   a.tokv = tokv;
   a.coef = coef;
+  a.rc = rcoef;
+  a.rg = rg;
   a.W = (const T*)lm_head;
   a.H = H;
   a.V = V;
@@ -2408,11 +2555,13 @@ static hipError_t launch_bwd_dh_t(const void* dz, int64_t ldz, DevRows rows,
 hipError_t launch_bwd_dh(int dt, const void* dz, int64_t ldz, DevRows rows,
                          const void* WT, int64_t ldwt, int H, int V, int Vpad,
                          const int* idx, const int* tokv, const float* coef,
+                         const float* rcoef, const float* rg,
                          const void* lm_head, float* d_hidden, hipStream_t s) {
   return dt ? launch_bwd_dh_t<bf16>(dz, ldz, rows, WT, ldwt, H, V, Vpad, idx,
-                                    tokv, coef, lm_head, d_hidden, s)
+                                    tokv, coef, rcoef, rg, lm_head, d_hidden, s)
             : launch_bwd_dh_t<float>(dz, ldz, rows, WT, ldwt, H, V, Vpad, idx,
-                                     tokv, coef, lm_head, d_hidden, s);
+                                     tokv, coef, nullptr, nullptr, lm_head,
+                                     d_hidden, s);
 }
 
 int64_t dw_part_floats(int V, int H) {
@@ -2424,12 +2573,13 @@ int64_t dw_part_floats(int V, int H) {
 hipError_t launch_bwd_dw(int dt, const void* dz, int64_t ld, DevRows krows,
                          const void* hT, int64_t ldht, int H, int V, int Vpad,
                          float* d_lm_head, int first, float* part,
-                         hipStream_t s) {
+                         const int* sigma, hipStream_t s) {
   const int esz = dt ? 2 : 4;
   DwArgs a;
   a.op = GemmOperands{(const char*)dz, ld * esz, nullptr, 0,
                       (const char*)hT, ldht * esz, H};
   a.krows = krows;
+  a.sigma = dt ? sigma : nullptr;
   a.V = V;
   a.H = H;
   a.amax = dt ? Vpad : V;

@@ -28,7 +28,9 @@ softmax is peaked and whose tokens follow a heavy-tailed law):
   standard deviation about 15);
 * hidden rows pulled toward (or away from) their token's head row
   (aligned_rows), which makes that token nearly certain (or nearly
-  impossible).
+  impossible);
+* logits near two large levels by vocabulary half (two_level_logits), so
+  that a row's vocabulary tiles have maxima tens of nats apart.
 """
 
 from __future__ import annotations
@@ -281,6 +283,21 @@ def aligned_rows(lm_head: np.ndarray, tokens: np.ndarray, dtype: str,
     h = rng.standard_normal((len(tokens), W.shape[1]), dtype=np.float32)
     h += np.asarray(kappa, np.float32)[:, None] * W[np.asarray(tokens)]
     return round_bf16(h) if dtype == "bf16" else h
+
+
+def two_level_logits(n: int, H: int, V: int, levels, beta, seed: int):
+    """Hidden rows and a head whose logits sit near two levels by vocabulary
+    half: head rows W[v] = a_v u + N(0, 0.02^2) with a_v = levels[0] / H for
+    v < V / 2 and levels[1] / H above, hidden rows h_t = beta_t u +
+    N(0, 0.1^2), u ~ N(0, 1)^H, so z[t, v] is about beta_t levels[half(v)]
+    (|u|^2 is about H).  bf16 bit patterns (hidden, head)."""
+    rng = np.random.default_rng(np.random.PCG64(seed))
+    u = rng.standard_normal(H, dtype=np.float32)
+    a = np.where(np.arange(V) < V // 2, levels[0], levels[1]).astype(np.float32) / H
+    W = a[:, None] * u[None, :] + 0.02 * rng.standard_normal((V, H), dtype=np.float32)
+    h = (np.asarray(beta, np.float32)[:, None] * u[None, :]
+         + 0.1 * rng.standard_normal((n, H), dtype=np.float32))
+    return round_bf16(h), round_bf16(W)
 
 
 def random_mx_head(V: int, H: int, fmt: str, seed: int, scale_code: int = 121):

@@ -123,6 +123,27 @@ def _weights_batch(dtype, seed):
     return b
 
 
+def test_rows_across_the_e_window():
+    """bf16 learner: rows whose logits sit near +-60 nats on one half of the
+    vocabulary and +-52 on the other, so that their tiles' maxima fall on
+    both sides of the window the stored e keeps (2^-32 .. 2^80 for a tile's
+    largest term) and the tiles are rebased to the row's reference by exact
+    powers of two; rows near 0 and +-30 nats share one reference as they
+    are.  The lower half still carries about e^-8 of the mass, so the
+    rebased tiles weigh in the gradients.  Every output against the oracle."""
+    H, V = 256, 2048
+    b = small_batch(N_resp=6, group_size=3, H=H, V=V, lo=40, hi=120,
+                    dtype="bf16", masked=0.2, seed=81)
+    beta = np.array([1.0, -1.0, 0.0, 0.5], np.float32)[np.arange(b.N) % 4]
+    b.hidden, b.lm_head = synth.two_level_logits(b.N, H, V, (66.0, 58.0), beta, 82)
+    logmu = logmu_from_oracle(b)
+    out = run_fwd_bwd(batch_to_dev(b, logmu))
+    ref = oracle_full(b, logmu)
+    lse = ref["lse"]
+    say("e-window", f"oracle lse by row kind: {[float(np.median(lse[np.arange(b.N) % 4 == k])) for k in range(4)]}")
+    compare_full(out, ref, b, "e-window")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_huge_finite_weights_full_parity(dtype):
     """log mu = log pi - 30 on some valid rows (w ~ 1.1e13) and + 30 on
