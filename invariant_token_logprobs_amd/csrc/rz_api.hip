@@ -183,7 +183,11 @@ size_t carve_fb(Carver& c, int64_t n, int32_t B, int32_t H, int32_t V,
   // one sort buffer serves the group ids (B keys) and then the tokens (n)
   t.sort_ws = c.take<int>(sizeof(int) * sort_ws_ints(std::max<int64_t>(n, B)));
   t.fix_cont = c.take<float>(sizeof(float) * (size_t)dw_fix_cont_floats(n, dw_cols));
-  t.dwpart = c.take<float>(sizeof(float) * (size_t)dw_part_floats(V, dw_cols));
+  // parked K pieces of the last round: the dHidden GEMM's, then (after it)
+  // the dW GEMM's
+  t.dwpart = c.take<float>(sizeof(float) *
+                           (size_t)std::max(dw_part_floats(V, dw_cols),
+                                            dh_part_floats(C, H)));
   if (w) *w = t;
   return c.off;
 }
@@ -616,7 +620,7 @@ static rz_status fwd_bwd_core(
                               b16 ? w.coef : nullptr, w.gsc, w.sigma, s));
       RZ_TRY(launch_bwd_dh(dt, w.dz, Vpad, crow, w.WT, Vpad, H, V, Vpad,
                            w.idx, w.tokv, w.coef1, b16 ? w.coef : nullptr,
-                           w.gsc, lm_head, d_hidden, s));
+                           w.gsc, lm_head, d_hidden, w.dwpart, s));
     }
     RZ_TRY(launch_bwd_dw(dt, b16 ? w.dz : w.dzT, b16 ? Vpad : C,
                          N > 0 ? crow : DevRows{nullptr, 0, 0}, w.hT, C,

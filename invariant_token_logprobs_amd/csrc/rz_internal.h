@@ -170,11 +170,15 @@ hipError_t launch_dz_scale(float* dz, int64_t ldz, float* dzT, int64_t ldzt,
                            const int* tokv, int Vpad, hipStream_t s);
 // bf16: dz = the stored e, scaled by rcoef (c_t) and rg (g_t) in the
 // epilogue; fp32: dz, rcoef = rg = null
+// part: room for the last round's K pieces, dh_part_floats(rows.cap, H)
+// floats (null: no split)
+int64_t dh_part_floats(int64_t rows, int H);
 hipError_t launch_bwd_dh(int dt, const void* dz, int64_t ldz, DevRows rows,
                          const void* WT, int64_t ldwt, int H, int V, int Vpad,
                          const int* idx, const int* tokv, const float* coef,
                          const float* rcoef, const float* rg,
-                         const void* lm_head, float* d_hidden, hipStream_t s);
+                         const void* lm_head, float* d_hidden, float* part,
+                         hipStream_t s);
 // bf16: dz = e [C][Vpad] (ld = Vpad), read K-major, hT scaled per row and
 // sigma the chunk's power of two; fp32: dz = dz^T [Vpad][C] (ld = C)
 // Floats of the dW split workspace (launch_bwd_dw's part) for a head of

@@ -1557,6 +1557,65 @@ __global__ __launch_bounds__(256) void k_erebase(
 }
 
 // ===================================================================
+// The last round of a GEMM's tiles split along K.  One workgroup per CU per
+// round: when the tiles of the last round leave most CUs idle, each of them
+// runs as up to kSplitMax pieces over consecutive K ranges, parked as raw
+// accumulators and summed in piece order by a second kernel (a fixed order,
+// so the result is the same in every run).  The split depends on the tile
+// count and the CU count only.
+// ===================================================================
+constexpr int kPartTileFloats = kBM * kBN;  // one parked 256 x 256 fp32 tile
+constexpr int kSplitMax = 4;                // pieces per tile of the last round
+constexpr int kSplitWGs = 256;              // parked tiles at most
+
+struct RoundSplit {
+  int tail, split;  // tail: tiles T - tail .. T - 1 run as split pieces each
+};
+__host__ __device__ inline RoundSplit round_split(int T, int ncu) {
+  RoundSplit r{0, 1};
+  if (T <= 0 || ncu < 1) return r;
+  const int tail = T - ((T + ncu - 1) / ncu - 1) * ncu;
+  int split = ncu / tail;
+  if (split > kSplitMax) split = kSplitMax;
+  if (tail * split > kSplitWGs) split = kSplitWGs / tail;
+  if (split >= 2) r = RoundSplit{tail, split};
+  return r;
+}
+
+// Parked tile q: 16-byte chunk c of thread t at part + q kPartTileFloats +
+// 4 (256 c + t), chunk c holding registers 4 (c % 4) .. + 3 of block c / 4.
+__device__ __forceinline__ f32x4* part_chunk(float* part, int q, int c) {
+  return reinterpret_cast<f32x4*>(part + (int64_t)q * kPartTileFloats) + c * 256 +
+         threadIdx.x;
+}
+
+__device__ __forceinline__ void park_tile(float* part, int q,
+                                          const f32x16 (&acc)[kTM][kTN]) {
+#pragma unroll
+  for (int c = 0; c < 4 * kTM * kTN; ++c) {
+    const f32x16& blk = acc[c / 16][(c / 4) % 4];
+    const int r = 4 * (c % 4);
+    *part_chunk(part, q, c) = f32x4{blk[r], blk[r + 1], blk[r + 2], blk[r + 3]};
+  }
+}
+
+// the pieces q0 .. q0 + n - 1 summed in order
+__device__ __forceinline__ void sum_parked(float* part, int q0, int n,
+                                           f32x16 (&acc)[kTM][kTN]) {
+#pragma unroll
+  for (int c = 0; c < 4 * kTM * kTN; ++c) {
+    f32x4 v = *part_chunk(part, q0, c);
+    for (int p = 1; p < n; ++p) v += *part_chunk(part, q0 + p, c);
+    f32x16& blk = acc[c / 16][(c / 4) % 4];
+    const int r = 4 * (c % 4);
+    blk[r] = v[0];
+    blk[r + 1] = v[1];
+    blk[r + 2] = v[2];
+    blk[r + 3] = v[3];
+  }
+}
+
+// ===================================================================
 // Backward, part 2: dHidden = dz W (K = Vpad in fixed order) plus the token
 // column's exact term c_t (p[a_t] - 1) W[a_t, :] (coef holds its
 // negative), scattered to the rows' positions.  bf16: the A operand is the
@@ -1575,24 +1634,17 @@ struct DhArgs {
   const float* rg;     // bf16: g_t
   const T* W;
   int H, V, nk, mt, nt;
+  int ncu;      // compute units: the last round's split (round_split)
+  float* part;  // parked pieces of the last round (null: no split)
   float* dh;
 };
 
+// The epilogue of one dHidden tile: the rows' factors (bf16), the token
+// column's exact term, the scatter to the rows' positions.
 template <typename T>
-__global__ RZ_GEMM_ATTR void k_bwd_dh(DhArgs<T> a) {
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
-  const RowCount rc = to_rc(a.rows);
-  const int M = rc.get();
-  // Only the tiles of the M rows present are numbered (M may be a device
-  // count below the launch bound), so the active tiles spread over all XCDs.
-  const int mt = (M + kBM - 1) / kBM;
-  if ((int)blockIdx.x >= mt * a.nt) return;
-  const TileCoord tc = map_tile(blockIdx.x, mt * a.nt, mt, a.nt);
-  const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
-
-  f32x16 acc[kTM][kTN];
-  gemm_mainloop<T>(a.op, M, m0, n0, a.nk, acc, lds);
-
+__device__ __forceinline__ void dh_epilogue(const DhArgs<T>& a, const RowCount& rc,
+                                            int M, int m0, int n0,
+                                            f32x16 (&acc)[kTM][kTN], char* lds) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
   int* sidx = reinterpret_cast<int*>(lds);
@@ -1644,6 +1696,65 @@ __global__ RZ_GEMM_ATTR void k_bwd_dh(DhArgs<T> a) {
     }
 }
 
+// kPiece = false: the tiles of the M rows present (M may be a device count
+// below the launch bound; only those tiles are numbered, so they spread over
+// all XCDs), except the last round's when it is split (round_split of that
+// tile count); kPiece = true: those tiles' K pieces, parked for k_dh_tail.
+// Workgroups past their share return at once.  The split's whole rounds
+// come first, so running the pieces as a second launch costs one launch.
+template <typename T, bool kPiece>
+__global__ RZ_GEMM_ATTR void k_bwd_dh(DhArgs<T> a) {
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  const RowCount rc = to_rc(a.rows);
+  const int M = rc.get();
+  const int mt = (M + kBM - 1) / kBM;
+  const int ntile = mt * a.nt;
+  const RoundSplit sp = a.part ? round_split(ntile, a.ncu) : RoundSplit{0, 1};
+  const int full = ntile - sp.tail;
+  int tb = blockIdx.x, piece = 0, pieces = 1;
+  if constexpr (kPiece) {
+    if (tb >= sp.tail * sp.split) return;
+    piece = tb % sp.split;
+    tb = full + tb / sp.split;
+    pieces = sp.split;
+  } else {
+    if (tb >= full) return;
+  }
+  const TileCoord tc = map_tile(tb, ntile, mt, a.nt);
+  const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
+  // the piece's K stages [k0, k1); both operands are K-contiguous
+  const int k0 = (int)((int64_t)a.nk * piece / pieces);
+  const int k1 = (int)((int64_t)a.nk * (piece + 1) / pieces);
+  GemmOperands op = a.op;
+  const int64_t kb = (int64_t)k0 * Stage<T>::kK * (int64_t)sizeof(T);
+  op.A += kb;
+  op.B += kb;
+
+  f32x16 acc[kTM][kTN];
+  gemm_mainloop<T>(op, M, m0, n0, k1 - k0, acc, lds);
+  // piece q = (tile - full) split + piece is parked at q, the launch index
+  if constexpr (kPiece) park_tile(a.part, blockIdx.x, acc);
+  else dh_epilogue(a, rc, M, m0, n0, acc, lds);
+}
+
+// The last round's tiles: their pieces summed in piece order, then the same
+// epilogue.  One workgroup per tail tile (kSplitWGs launched at most).
+template <typename T>
+__global__ __launch_bounds__(256) void k_dh_tail(DhArgs<T> a) {
+  __shared__ __attribute__((aligned(16))) char lds[5 * 256 * 4];
+  const RowCount rc = to_rc(a.rows);
+  const int M = rc.get();
+  const int mt = (M + kBM - 1) / kBM;
+  const int ntile = mt * a.nt;
+  const RoundSplit sp = round_split(ntile, a.ncu);
+  const int i = blockIdx.x;
+  if (i >= sp.tail) return;
+  const TileCoord tc = map_tile(ntile - sp.tail + i, ntile, mt, a.nt);
+  f32x16 acc[kTM][kTN];
+  sum_parked(a.part, i * sp.split, sp.split, acc);
+  dh_epilogue(a, rc, M, tc.tm * kBM, tc.tn * kBN, acc, lds);
+}
+
 // ===================================================================
 // Backward, part 3: dW (+)= dz^T h over this chunk's tokens (K in fixed
 // order); chunks are accumulated in order, the first one overwrites.  bf16:
@@ -1664,9 +1775,6 @@ struct DwArgs {
   float* dw;
 };
 
-constexpr int kDwTileFloats = kBM * kBN;  // one parked 256 x 256 fp32 tile
-constexpr int kDwSplitMax = 4;            // pieces per tile of the last round
-constexpr int kDwSplitWGs = 256;          // parked tiles at most
 
 // dW (+)= acc for one tile: rows v (vocabulary), columns h (hidden); the
 // first chunk overwrites.
@@ -1698,12 +1806,6 @@ __device__ __forceinline__ void dw_store(const DwArgs& a, int m0, int n0,
     }
 }
 
-// Parked tile q: 16-byte chunk c of thread t at part + q kDwTileFloats +
-// 4 (256 c + t), chunk c holding registers 4 (c % 4) .. + 3 of block c / 4.
-__device__ __forceinline__ f32x4* dw_part_chunk(float* part, int q, int c) {
-  return reinterpret_cast<f32x4*>(part + (int64_t)q * kDwTileFloats) + c * 256 +
-         threadIdx.x;
-}
 
 template <typename T>
 __global__ RZ_GEMM_ATTR void k_bwd_dw(DwArgs a) {
@@ -1734,13 +1836,7 @@ __global__ RZ_GEMM_ATTR void k_bwd_dw(DwArgs a) {
   // read and takes the transposed copy dz^T
   gemm_mainloop<T, false, sizeof(T) == 2>(op, a.amax, m0, n0, k1 - k0, acc, lds);
   if (pieces > 1) {
-    const int q = (tb - full) * pieces + piece;
-#pragma unroll
-    for (int c = 0; c < 4 * kTM * kTN; ++c) {
-      const f32x16& blk = acc[c / 16][(c / 4) % 4];
-      const int r = 4 * (c % 4);
-      *dw_part_chunk(a.part, q, c) = f32x4{blk[r], blk[r + 1], blk[r + 2], blk[r + 3]};
-    }
+    park_tile(a.part, (tb - full) * pieces + piece, acc);
     return;
   }
   dw_store(a, m0, n0, acc);
@@ -1755,17 +1851,7 @@ __global__ __launch_bounds__(256) void k_dw_tail(DwArgs a) {
   const int i = blockIdx.x;
   const TileCoord tc = map_tile(a.T - a.tail + i, a.T, a.mt, a.nt);
   f32x16 acc[kTM][kTN];
-#pragma unroll
-  for (int c = 0; c < 4 * kTM * kTN; ++c) {
-    f32x4 v = *dw_part_chunk(a.part, i * a.split, c);
-    for (int p = 1; p < a.split; ++p) v += *dw_part_chunk(a.part, i * a.split + p, c);
-    f32x16& blk = acc[c / 16][(c / 4) % 4];
-    const int r = 4 * (c % 4);
-    blk[r] = v[0];
-    blk[r + 1] = v[1];
-    blk[r + 2] = v[2];
-    blk[r + 3] = v[3];
-  }
+  sum_parked(a.part, i * a.split, a.split, acc);
   dw_store(a, tc.tm * kBM, tc.tn * kBN, acc);
 }
 
@@ -2033,6 +2119,17 @@ hipError_t timed(int kid, hipStream_t s, F&& launch) {
 }
 
 inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// compute units of the current device (256 if the runtime cannot say)
+inline int cu_count() {
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) !=
+          hipSuccess ||
+      ncu < 1)
+    ncu = 256;
+  return ncu;
+}
 
 }  // namespace
 
@@ -2529,7 +2626,7 @@ static hipError_t launch_bwd_dh_t(const void* dz, int64_t ldz, DevRows rows,
                                   int Vpad, const int* idx, const int* tokv,
                                   const float* coef, const float* rcoef,
                                   const float* rg, const void* lm_head,
-                                  float* d_hidden, hipStream_t s) {
+                                  float* d_hidden, float* part, hipStream_t s) {
   DhArgs<T> a;
   a.op = GemmOperands{(const char*)dz, ldz * (int64_t)sizeof(T), nullptr,
                       rows.base * 0, (const char*)WT,
@@ -2546,9 +2643,17 @@ static hipError_t launch_bwd_dh_t(const void* dz, int64_t ldz, DevRows rows,
   a.nk = Vpad / Stage<T>::kK;
   a.mt = cdiv(rows.cap, kBM);
   a.nt = cdiv(H, kBN);
+  a.ncu = cu_count();
+  a.part = part;
   a.dh = d_hidden;
   return timed(K_BWD_DH, s, [&] {
-    k_bwd_dh<T><<<a.mt * a.nt, kThreads, 0, s>>>(a);
+    // launch bounds: every tile of rows.cap rows; the pieces and their sums
+    // of at most kSplitWGs parked tiles
+    k_bwd_dh<T, false><<<a.mt * a.nt, kThreads, 0, s>>>(a);
+    if (part) {
+      k_bwd_dh<T, true><<<kSplitWGs, kThreads, 0, s>>>(a);
+      k_dh_tail<T><<<kSplitWGs, kThreads, 0, s>>>(a);
+    }
   });
 }
 
@@ -2556,18 +2661,26 @@ hipError_t launch_bwd_dh(int dt, const void* dz, int64_t ldz, DevRows rows,
                          const void* WT, int64_t ldwt, int H, int V, int Vpad,
                          const int* idx, const int* tokv, const float* coef,
                          const float* rcoef, const float* rg,
-                         const void* lm_head, float* d_hidden, hipStream_t s) {
+                         const void* lm_head, float* d_hidden, float* part,
+                         hipStream_t s) {
   return dt ? launch_bwd_dh_t<bf16>(dz, ldz, rows, WT, ldwt, H, V, Vpad, idx,
-                                    tokv, coef, rcoef, rg, lm_head, d_hidden, s)
+                                    tokv, coef, rcoef, rg, lm_head, d_hidden,
+                                    part, s)
             : launch_bwd_dh_t<float>(dz, ldz, rows, WT, ldwt, H, V, Vpad, idx,
                                      tokv, coef, nullptr, nullptr, lm_head,
-                                     d_hidden, s);
+                                     d_hidden, part, s);
 }
 
 int64_t dw_part_floats(int V, int H) {
   const int64_t T = (int64_t)cdiv(V, kBM) * cdiv(H, kBN);
-  const int64_t tiles = T * kDwSplitMax < kDwSplitWGs ? T * kDwSplitMax : kDwSplitWGs;
-  return tiles * kDwTileFloats;
+  const int64_t tiles = T * kSplitMax < kSplitWGs ? T * kSplitMax : kSplitWGs;
+  return tiles * kPartTileFloats;
+}
+
+int64_t dh_part_floats(int64_t rows, int H) {
+  const int64_t T = (int64_t)cdiv(rows, kBM) * cdiv(H, kBN);
+  const int64_t tiles = T * kSplitMax < kSplitWGs ? T * kSplitMax : kSplitWGs;
+  return tiles * kPartTileFloats;
 }
 
 hipError_t launch_bwd_dw(int dt, const void* dz, int64_t ld, DevRows krows,
@@ -2589,23 +2702,12 @@ hipError_t launch_bwd_dw(int dt, const void* dz, int64_t ld, DevRows krows,
   a.first = first;
   a.dw = d_lm_head;
   // One workgroup per CU per round: the last round's tiles (tail) would
-  // leave most CUs idle, so each is split into up to kDwSplitMax pieces
+  // leave most CUs idle, so each is split into up to kSplitMax pieces
   // along K (fixed by V, H and the CU count, never by the row count).
   a.T = a.mt * a.nt;
-  int dev = 0, ncu = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) !=
-          hipSuccess ||
-      ncu < 1)
-    ncu = 256;
-  a.tail = a.T - (cdiv(a.T, ncu) - 1) * ncu;
-  a.split = ncu / a.tail;
-  if (a.split > kDwSplitMax) a.split = kDwSplitMax;
-  if (a.tail * a.split > kDwSplitWGs) a.split = kDwSplitWGs / a.tail;
-  if (a.split < 2 || !part) {
-    a.tail = 0;
-    a.split = 1;
-  }
+  const RoundSplit rs = part ? round_split(a.T, cu_count()) : RoundSplit{0, 1};
+  a.tail = rs.tail;
+  a.split = rs.split;
   a.part = part;
   return timed(K_BWD_DW, s, [&] {
     const int grid = a.T - a.tail + a.tail * a.split;
