@@ -166,19 +166,17 @@ constexpr float kTwoM32 = 2.3283064365386963e-10f;  // 2^-32
 
 // Gumbel noise g = -ln(-ln u) of u = (x + 1/2) 2^-32.  The largest g come
 // from u near 1, so E = -ln u is taken from w = 1 - u (exact from the
-// integer) there: a short series for small w, else Kahan's form
-// -ln(y) w / (1 - y) with y = 1 - w rounded, which cancels y's rounding.
-// Every lane evaluates all three forms and selects (no divergent branches;
-// the discarded forms may be inf or NaN).
+// integer) there: a short series for w < 1/64, else -ln(y) with y = 1 - w
+// rounded (y's rounding moves E by at most 2^-25 / w <= 2^-19 relative, g by
+// that much absolutely).  Every lane evaluates both forms and selects (no
+// divergent branches).
 __device__ __forceinline__ float gumbel_of_bits(uint32_t x) {
   const bool low = x < 0x80000000u;
   const float u = ((float)x + 0.5f) * kTwoM32;
   const float w = ((float)(~x) + 0.5f) * kTwoM32;  // 1 - u for the upper half
-  const float y = 1.f - w;
-  const float L = -__builtin_amdgcn_logf(low ? u : y) * kLn2;
-  const float kahan = L * (w * __builtin_amdgcn_rcpf(1.f - y));
+  const float L = -__builtin_amdgcn_logf(low ? u : 1.f - w) * kLn2;
   const float series = w * (1.f + w * (0.5f + w * (1.f / 3.f + w * (0.25f + w * 0.2f))));
-  const float E = low ? L : (w < 0.015625f ? series : kahan);
+  const float E = (low || w >= 0.015625f) ? L : series;
   return -__builtin_amdgcn_logf(E) * kLn2;
 }
 
