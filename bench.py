@@ -41,12 +41,13 @@ GEMM_KERNELS = ("fwd_logits_gemm", "bwd_dh_gemm", "bwd_dw_gemm")
 # kernel sources they were taken from.
 COUNTER_TRAFFIC = {
     "workload": "qwen3_4b_tool",
-    "sources_sha256": "bc3c8695f534647527618160492f0bc41d89217587f96443d443de828f37b15c",
-    "bytes_per_launch": {"fwd_logits_gemm": 26247762392,
-                         "bwd_dh_gemm": 24514813720,
-                         "bwd_dw_gemm": 29188745031 + 47679713,  # + its tail sum
-                         "grad_norm": 2291986450,
-                         "mx_dequant_mxfp4": 984653570},
+    "sources_sha256": "30998f853738d4726765a49beda2232ac2c4e5b27be9552c1fe2cb1213676b42",
+    # per timed launch: a GEMM with its last-round K pieces and their sum
+    "bytes_per_launch": {"fwd_logits_gemm": 26346542778,
+                         "bwd_dh_gemm": 24724760019,
+                         "bwd_dw_gemm": 29399131403,
+                         "grad_norm": 2291983682,
+                         "mx_dequant_mxfp4": 984657104},
 }
 
 
@@ -55,9 +56,9 @@ COUNTER_TRAFFIC = {
 # GEMMs, from the counter run of profiles/mfma_utilisation_qwen3_4b_tool.md,
 # over the launches that hold rows; same validity rule as COUNTER_TRAFFIC.
 COUNTER_MFMA = {
-    "fwd_logits_gemm": {"mfma_busy": 0.564, "clock_ghz": 1.921},
-    "bwd_dh_gemm": {"mfma_busy": 0.588, "clock_ghz": 1.838},
-    "bwd_dw_gemm": {"mfma_busy": 0.572, "clock_ghz": 1.864},
+    "fwd_logits_gemm": {"mfma_busy": 0.559, "clock_ghz": 1.901},
+    "bwd_dh_gemm": {"mfma_busy": 0.615, "clock_ghz": 1.806},
+    "bwd_dw_gemm": {"mfma_busy": 0.565, "clock_ghz": 1.861},
 }
 
 
