@@ -260,14 +260,14 @@ rz_status rz_sample_tokens(const void* hidden, const void* lm_head,
                            hipStream_t stream);
 
 /* Bytes of the static device scratch of rz_sample_tokens_noalloc, per GPU. */
-#define RZ_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+#define RZ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 /*
  * rz_sample_tokens_noalloc -- rz_sample_tokens for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving
  * loops, harnesses that forbid allocation.  Arguments and outputs as
  * rz_sample_tokens, without the workspace: the draw's scratch (the
- * vocab-tile partials, the draw candidates and the target logits;
+ * statistics-tile partials and the draw candidates with their logits;
  * rz_workspace_bytes_op(RZ_OP_SAMPLE, n_rows, 1, H, V, dt) bytes) lives in
  * a static device array of RZ_NOALLOC_SCRATCH_BYTES on each GPU, which the
  * library holds from its first use on that GPU until the process ends.

@@ -34,7 +34,7 @@ RZ_MX_FORMATS = {"mxfp4": 0, "mxfp8": 1}
 
 _STATUS = {0: "RZ_OK", -1: "RZ_ERR_INVALID_ARG", -2: "RZ_ERR_UNSUPPORTED",
            -3: "RZ_ERR_WORKSPACE", -4: "RZ_ERR_HIP", -5: "RZ_ERR_SCRATCH"}
-RZ_NOALLOC_SCRATCH_BYTES = 32 << 20
+RZ_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTS = [
     "rz_workspace_bytes", "rz_workspace_bytes_op", "rz_status_string",

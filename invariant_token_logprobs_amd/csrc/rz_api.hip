@@ -20,7 +20,9 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int kChunkRows = 32768;  // backward token chunk (a multiple of 256)
-constexpr int kVocabTile = 256;
+// vocabulary columns per statistics tile: one (m, s) partial, and one draw
+// candidate, per row and tile
+constexpr int kVocabTile = 128;
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -68,7 +70,6 @@ struct SmpWs {
   float2* partials;
   float2* cand;
   float* candz;
-  float* ztgt;
 };
 size_t carve_smp(Carver& c, int64_t n, int32_t V, SmpWs* w) {
   const int nt = (int)((V + kVocabTile - 1) / kVocabTile);
@@ -76,7 +77,6 @@ size_t carve_smp(Carver& c, int64_t n, int32_t V, SmpWs* w) {
   t.partials = c.take<float2>(sizeof(float2) * (size_t)nt * (size_t)n);
   t.cand = c.take<float2>(sizeof(float2) * (size_t)nt * (size_t)n);
   t.candz = c.take<float>(sizeof(float) * (size_t)nt * (size_t)n);
-  t.ztgt = c.take<float>(sizeof(float) * (size_t)n);
   if (w) *w = t;
   return c.off;
 }
@@ -456,16 +456,13 @@ static rz_status sample_core(const void* hidden, const void* lm_head,
   SmpWs w;
   carve_smp(c, n_rows, V, &w);
   const int nt = (V + kVocabTile - 1) / kVocabTile;
-  DevRows rows{nullptr, 0, (int)n_rows};
   // the logits GEMM with the draw in its epilogue (the winning column's
   // logit comes along), then the draw's merge
   RZ_TRY(launch_fwd_sample(dt, hidden, n_rows, lm_head, H, V, row_ids, seed,
                            w.partials, w.cand, w.candz, n_rows, s));
-  RZ_TRY(launch_draw_merge(w.cand, w.candz, n_rows, nt, n_rows, tokens, w.ztgt, s));
-  // the record: rz_token_logprobs' own merge kernel
-  RZ_TRY(launch_lse_merge(w.partials, n_rows, nt, rows, w.ztgt, tokens, V,
-                          lse, logmu, nullptr, nullptr, nullptr, nullptr,
-                          nullptr, s));
+  // the draw's merge and the record (rz_token_logprobs' own lse fold)
+  RZ_TRY(launch_draw_merge(w.cand, w.candz, w.partials, n_rows, nt, n_rows, V,
+                           tokens, logmu, lse, s));
   return RZ_OK;
 }
 
@@ -588,10 +585,10 @@ static rz_status fwd_bwd_core(
   // a1-a4, a7-a9 in chunks of C valid rows (the count lives on the device;
   // chunks past it do no work):
   //   logits GEMM + log-softmax epilogue, also storing e (bf16:
-  //   exp(z - r ln 2), the backward's A operand; fp32: exp(z - m_tile));
+  //   exp(z - r ln 2), the backward's A operand; fp32: exp(z - m_j));
   //   ordered merge -> lse, log pi; c_t;
   //   bf16: g_t and the chunk's scale, flagged rows rebased, h^T scaled by
-  //   c_t g_t 2^sigma; fp32: dz = c_t e^(m_tile - lse) e and dz^T;
+  //   c_t g_t 2^sigma; fp32: dz = c_t e^(m_j - lse) e and dz^T;
   //   dHidden GEMM; dW GEMM accumulated over chunks in order.
   const bool b16 = dt == RZ_DTYPE_BF16;
   const int64_t nchunks = N > 0 ? (N + C - 1) / C : 1;
@@ -827,7 +824,6 @@ rz_status rz_sample_tokens_mx(const void* hidden, const uint8_t* codes,
   SmpWs w;
   carve_smp(c, n_rows, V, &w);
   const int nt = (V + kVocabTile - 1) / kVocabTile;
-  DevRows rows{nullptr, 0, (int)n_rows};
   if (fused) {
     RZ_TRY(launch_fwd_mx(fmt, hidden, n_rows, codes, scales, H, V, nullptr,
                          w.partials, n_rows, nullptr, row_ids, seed, w.cand,
@@ -839,10 +835,8 @@ rz_status rz_sample_tokens_mx(const void* hidden, const uint8_t* codes,
     RZ_TRY(launch_fwd_sample(RZ_DTYPE_BF16, hidden, n_rows, Wb, H, V, row_ids,
                              seed, w.partials, w.cand, w.candz, n_rows, s));
   }
-  RZ_TRY(launch_draw_merge(w.cand, w.candz, n_rows, nt, n_rows, tokens, w.ztgt, s));
-  RZ_TRY(launch_lse_merge(w.partials, n_rows, nt, rows, w.ztgt, tokens, V,
-                          lse, logmu, nullptr, nullptr, nullptr, nullptr,
-                          nullptr, s));
+  RZ_TRY(launch_draw_merge(w.cand, w.candz, w.partials, n_rows, nt, n_rows, V,
+                           tokens, logmu, lse, s));
   return RZ_OK;
 }
 

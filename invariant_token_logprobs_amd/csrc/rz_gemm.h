@@ -375,22 +375,27 @@ __device__ __forceinline__ void gemm_mainloop(const GemmOperands& op, int M,
 // (global_load_lds_dwordx4: two loads for A and eight for B per wave) while
 // stage kt feeds the MFMAs; each stage ends with every wave's loads complete
 // and a barrier.  At these row counts the B stream (the head W, read once
-// per vocab tile) bounds the kernel, not the MFMAs.  Rows of A at or past M
+// per column tile) bounds the kernel, not the MFMAs.  Rows of A at or past M
 // (B rows past N) read row M - 1 (N - 1), as in gemm_mainloop.  Leaves the
 // LDS free on return.
 //
 // kStages = 1 keeps a single 40 KB stage instead (load, wait, compute, in
-// turn): three workgroups then share a CU, so the 594 vocab tiles of a
-// 151936-word head run in one round, and a workgroup's wait or epilogue
-// overlaps the other two's streams.  Same stages, reads and MFMAs.  This
+// turn): three workgroups then share a CU, so the 675 workgroups of a
+// 151936-word head (512 of 256 columns and 163 of 128) run in one round,
+// and a workgroup's wait or epilogue overlaps the other two's streams.  Same stages, reads and MFMAs.  This
 // form runs for one row block only, where every byte of the head is read
 // once per call, so its head loads carry the non-temporal hint (the hidden
 // rows, which every workgroup reads, keep the default policy).
+//
+// one_half = true computes the first 128 columns only (a 64 x 128 tile): the
+// waves of column half 1 load no B rows and issue no MFMAs (their
+// accumulators stay 0), but still take part in the A loads and barriers.
 template <typename T, int kStages = 2>
 __device__ __forceinline__ void gemm_mainloop_rows64(const GemmOperands& op, int M,
                                                      int m0, int n0, int nk,
                                                      f32x16 (&acc)[1][kTN],
-                                                     char* lds) {
+                                                     char* lds,
+                                                     bool one_half = false) {
   static_assert(kStages == 1 || kStages == 2, "one or two stages");
   const int tid = threadIdx.x;
   const int lane = tid & 63, wid = tid >> 6;
@@ -416,6 +421,8 @@ __device__ __forceinline__ void gemm_mainloop_rows64(const GemmOperands& op, int
   // A rows 16 wu + 8 i (i < 2), B rows 64 wu + 8 i (i < 8)
   typedef __attribute__((address_space(3))) void* lds_ptr_t;
   const int wu = __builtin_amdgcn_readfirstlane(wid);
+  const bool mma = !(one_half && (wu & 1));       // column half wn = wu & 1
+  const bool loads_b = !(one_half && wu >= 2);    // B rows 64 wu .. + 63
   const char* ga[2];
   const char* gb[8];
 #pragma unroll
@@ -444,11 +451,13 @@ __device__ __forceinline__ void gemm_mainloop_rows64(const GemmOperands& op, int
       __builtin_amdgcn_global_load_lds(ga[i] + k,
                                        (lds_ptr_t)(sa + (wu * 16 + 8 * i) * kRowBytes),
                                        16, 0, 0);
+    if (loads_b) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_global_load_lds(gb[i] + k,
-                                       (lds_ptr_t)(sb + (wu * 64 + 8 * i) * kRowBytes),
-                                       16, 0, kStages == 1 ? kPolicyNT : 0);
+      for (int i = 0; i < 8; ++i)
+        __builtin_amdgcn_global_load_lds(gb[i] + k,
+                                         (lds_ptr_t)(sb + (wu * 64 + 8 * i) * kRowBytes),
+                                         16, 0, kStages == 1 ? kPolicyNT : 0);
+    }
   };
 
   if constexpr (kStages == 2) {
@@ -469,16 +478,18 @@ __device__ __forceinline__ void gemm_mainloop_rows64(const GemmOperands& op, int
     }
     const char* sa = lds + cur * kStageBytes64;
     const char* sb = sa + kOperandBytesA64;
+    if (mma) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const u32x4 fa = *reinterpret_cast<const u32x4*>(sa + a_off + c_off[s]);
-      u32x4 fb[kTN];
+      for (int s = 0; s < 4; ++s) {
+        const u32x4 fa = *reinterpret_cast<const u32x4*>(sa + a_off + c_off[s]);
+        u32x4 fb[kTN];
 #pragma unroll
-      for (int ni = 0; ni < kTN; ++ni)
-        fb[ni] = *reinterpret_cast<const u32x4*>(sb + b_off[ni] + c_off[s]);
+        for (int ni = 0; ni < kTN; ++ni)
+          fb[ni] = *reinterpret_cast<const u32x4*>(sb + b_off[ni] + c_off[s]);
 #pragma unroll
-      for (int ni = 0; ni < kTN; ++ni)
-        mfma_step(acc[0][ni], fb[ni], fa, (const T*)nullptr);
+        for (int ni = 0; ni < kTN; ++ni)
+          mfma_step(acc[0][ni], fb[ni], fa, (const T*)nullptr);
+      }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -537,7 +548,8 @@ struct MxStage {
   static constexpr int kScales = 256 * 4;
   static constexpr int kBytes = kOperandBytesA64 + kCodes + kScales;
   // stages in the ring: three (E2M1: 51 KB, three workgroups share a CU, so
-  // the Qwen3-4B head's 594 vocab tiles run in one round; E4M3: 75 KB, two)
+  // the Qwen3-4B head's 594 tiles of 256 columns run in one round; E4M3:
+  // 75 KB, two)
   static constexpr int kRing = 3;
   static constexpr int kLds = kRing * kBytes;
   static constexpr int kCodeLoads = kCodes / 4096;      // per wave per stage

@@ -17,7 +17,7 @@ enum KernelId {
   K_LSE_MERGE,       // bi_logsoftmax_gather merge
   K_ROWS_FINALIZE,
   K_COEF,
-  K_DZ_SCALE,        // fp32 dlogits from the forward's stored exp(z - m_tile)
+  K_DZ_SCALE,        // fp32 dlogits from the forward's stored exp(z - m_j)
   K_EREBASE,         // bf16 e: rows whose tiles straddle the e window
   K_CHUNK_SCALE,     // bf16 dW: the chunk's power of two
   K_RESP_SUMS,       // rz_loss: S_i
@@ -34,7 +34,7 @@ enum KernelId {
   K_DW_FIX,          // dW one-hot fix-up over pieces of the sorted list
   K_DW_FIX_SPAN,     //   runs crossing pieces
   K_FWD_SAMPLE,      // rollout-side logits GEMM with the draw in the epilogue
-  K_DRAW_MERGE,      // per-row best draw over the vocab tiles
+  K_DRAW_MERGE,      // per-row best draw over the statistics tiles + the record
   K_GRAD_NORM,       // run-level: float64 sums of squares per chunk
   K_GRAD_NORM_FINAL, // run-level: fixed tree over the chunks, sqrt
   K_RESP_DIAG,       // run-level: per-response D3 and KL
@@ -69,18 +69,19 @@ hipError_t launch_fwd_logits(int dt, const void* hidden, int64_t lda_bytes,
                              const int* row_tokens, float2* partials,
                              int64_t ldp, float* ztgt, void* e, int64_t lde,
                              int Vpad, hipStream_t s);
-// The logits GEMM with the draw in its epilogue: per (vocab tile, row) the
-// best (z + g, index) in cand and that column's z in candz.
+// The logits GEMM with the draw in its epilogue: per (statistics tile, row)
+// the best (z + g, index) in cand and that column's z in candz.
 hipError_t launch_fwd_sample(int dt, const void* hidden, int64_t n,
                              const void* lm_head, int H, int V,
                              const uint64_t* row_ids, uint64_t seed,
                              float2* partials, float2* cand, float* candz,
                              int64_t ldp, hipStream_t s);
-// The draw's winner per row (tokens) and its logit (ztgt, the record's
-// z[a_t]).
-hipError_t launch_draw_merge(const float2* cand, const float* candz, int64_t ldp,
-                             int nt, int64_t n, int* tokens, float* ztgt,
-                             hipStream_t s);
+// The draw's winner per row (tokens) and the record: log mu = z[a_t] - lse
+// (and lse, nullable), lse by k_lse_merge's fold.
+hipError_t launch_draw_merge(const float2* cand, const float* candz,
+                             const float2* partials, int64_t ldp, int nt,
+                             int64_t n, int V, int* tokens, float* logmu,
+                             float* lse, hipStream_t s);
 hipError_t launch_mx_dequant(int fmt, const uint8_t* codes, const uint8_t* scales,
                              int64_t nblk, void* out, int* err, hipStream_t s);
 constexpr int kLoraCols = 64;  // LoRA: largest rank and u block width

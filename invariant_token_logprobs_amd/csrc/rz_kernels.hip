@@ -28,7 +28,7 @@ constexpr int kIntMin = -2147483647 - 1;
 constexpr int kRows64MaxLogits = 128;
 constexpr int kRows64MaxSample = 256;
 
-// Logits of vocabulary columns >= V inside the last vocab tile: finite, so
+// Logits of vocabulary columns >= V inside the last statistics tile: finite, so
 // the row maximum stays finite and no (-inf) - (-inf) can appear.
 constexpr float kMaskedLogit = -1.0e30f;
 
@@ -51,9 +51,10 @@ __device__ __forceinline__ T from_f(float x) {
 // ===================================================================
 // bi_lmhead_gemm (forward): z = h W^T on one 256 x 256 tile, with the
 // log-softmax partials and the sampled-token gather fused in the epilogue.
-// Per (row, vocab tile) it writes m = max_v z and s = sum_v exp(z - m) over
-// the tile's columns (pad columns >= V excluded), and z[a_t] when the row's
-// token falls in the tile.  Nothing of the logits leaves the chip.
+// Per (row, statistics tile of 128 columns) it writes m = max_v z and
+// s = sum_v exp(z - m) over the tile's columns (pad columns >= V excluded),
+// and z[a_t] when the row's token falls in the tile.  Nothing of the logits
+// leaves the chip.
 // ===================================================================
 struct FwdArgs {
   GemmOperands op;
@@ -73,16 +74,18 @@ struct FwdArgs {
   const uint8_t* wscales;
   int H;                  // MX head only: hidden size
   int* err;               // MX head only: RZ_DEVERR_MX_SCALE
+  int nfull;              // single-stage 64-row form: 256-column workgroups
 };
 
 // What the learner's forward stores for the backward.
 //
-// fp32 inputs: e = exp(z - m_tile) in (0, 1], which the dz rescale turns
-// into dz = c_t exp(m_tile - lse_t) e (and dz^T) once lse is known.
+// fp32 inputs: e = exp(z - m_j) in (0, 1], m_j the maximum of the statistics
+// tile j holding the column, which the dz rescale turns into
+// dz = c_t exp(m_j - lse_t) e (and dz^T) once lse is known.
 //
 // bf16 inputs: e = exp(z - r ln 2) rounded to bf16, the backward GEMMs' A
 // operand as it stands.  r is an integer fixed by the tile maximum alone
-// (e_ref2): 0 while m_tile log2 e lies in [-kERefLo2, kERefHi2], else the
+// (e_ref2): 0 while m_j log2 e lies in [-kERefLo2, kERefHi2], else the
 // nearest integer that brings the tile maximum's e back to that window, so
 // e never overflows and a tile's largest terms stay normal.  With r the same
 // over a row's tiles, dz = c_t exp(r ln 2 - lse_t) e: one factor per row,
@@ -140,12 +143,14 @@ __device__ __forceinline__ int e_stage_off(int R, int k) {
 // Four blocks at once (counters c[0..3], one key), the four independent
 // chains interleaved in each round, so one wave per SIMD has four products
 // in flight instead of waiting on each round's product in turn.  The round
-// loop stays rolled: unrolled at the draw's call sites it stops the
-// enclosing loops from unrolling, and the accumulators they index would move
-// to scratch memory.  One 64-bit product gives both halves (v_mad_u64_u32).
+// loop is unrolled by two only: the counters then alternate between two
+// register sets with no copies at the loop's end, while a fully unrolled
+// loop at the draw's call sites stops the enclosing loops from unrolling
+// (the accumulators they index would move to scratch memory).  One 64-bit
+// product gives both halves (v_mad_u64_u32).
 __device__ __forceinline__ void philox4x32_10_x4(u32x4 (&c)[4], uint32_t k0,
                                                  uint32_t k1) {
-#pragma unroll 1
+#pragma unroll 2
   for (int r = 0; r < 10; ++r) {
     if (r) {
       k0 += 0x9E3779B9u;
@@ -163,20 +168,23 @@ __device__ __forceinline__ void philox4x32_10_x4(u32x4 (&c)[4], uint32_t k0,
 
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kTwoM32 = 2.3283064365386963e-10f;  // 2^-32
+constexpr float kTwoM33 = 1.1641532182693481e-10f;  // 2^-33
 
 // Gumbel noise g = -ln(-ln u) of u = (x + 1/2) 2^-32.  The largest g come
-// from u near 1, so E = -ln u is taken from w = 1 - u (exact from the
-// integer) there: a short series for w < 1/64, else -ln(y) with y = 1 - w
-// rounded (y's rounding moves E by at most 2^-25 / w <= 2^-19 relative, g by
-// that much absolutely).  Every lane evaluates both forms and selects (no
-// divergent branches).
+// from u near 1, where E = -ln u ~ w = 1 - u.  There, for x >= 2^32 - 2^26
+// (w < 2^-6), E is a short series in w, which is exact from the integer
+// (w = (~x + 1/2) 2^-32); elsewhere E = -ln of u rounded to fp32, whose
+// rounding (at most 2^-25 near 1) moves E by at most 2^-25 / w <= 2^-19
+// relative and g by that much absolutely.  Every lane evaluates both forms
+// and selects (no divergent branches).
 __device__ __forceinline__ float gumbel_of_bits(uint32_t x) {
-  const bool low = x < 0x80000000u;
-  const float u = ((float)x + 0.5f) * kTwoM32;
-  const float w = ((float)(~x) + 0.5f) * kTwoM32;  // 1 - u for the upper half
-  const float L = -__builtin_amdgcn_logf(low ? u : 1.f - w) * kLn2;
+  // (x + 1/2) 2^-32 as one fma: the scaling by a power of two is exact, so
+  // this rounds once, as (float(x) + 1/2) then * 2^-32 does
+  const float u = __builtin_fmaf((float)x, kTwoM32, kTwoM33);
+  const float w = __builtin_fmaf((float)(~x), kTwoM32, kTwoM33);  // 1 - u
+  const float L = -__builtin_amdgcn_logf(u) * kLn2;
   const float series = w * (1.f + w * (0.5f + w * (1.f / 3.f + w * (0.25f + w * 0.2f))));
-  const float E = (low || w >= 0.015625f) ? L : series;
+  const float E = x < 0xFC000000u ? L : series;
   return -__builtin_amdgcn_logf(E) * kLn2;
 }
 
@@ -185,24 +193,28 @@ __device__ __forceinline__ bool draw_better(float s, int v, float bs, int bv) {
   return s > bs || (s == bs && v < bv);
 }
 
-// bi_lmhead_gemm + the log-softmax statistics of one 256 x 256 logits tile
-// (vocab tile j = tn): per row t, m_tile = max_v z[t, v] and
-// s_tile = sum_v exp(z[t, v] - m_tile), written to partials[j][t]; on the
-// learner call also e for the backward (see EStore).
+// bi_lmhead_gemm + the log-softmax statistics of a logits tile: per row t
+// and statistics tile j (128 vocabulary columns, one wave's column half),
+// m_j = max_v z[t, v] and s_j = sum_v exp(z[t, v] - m_j), written to
+// partials[j][t]; on the learner call also e for the backward (see EStore).
 //
 // The MFMAs run with swapped operands (see gemm_mainloop), so each lane
 // holds one row t and, per 32 x 32 block, four runs of four consecutive
-// vocabulary columns.  Row statistics are then in-lane folds over 64 values
-// per block, one exchange with lane l ^ 32 and one combine of the two
-// column-half waves through LDS, each in a fixed order that depends only on
-// the column, never on the row's position or the batch: the per-row result
-// is the same in every launch (batch invariance).  The maximum is exact in
-// any order, so it is taken first over the whole tile; one exp per element
-// then serves both s_tile and e.
+// vocabulary columns.  A wave owns whole statistics tiles, so row statistics
+// are in-lane folds over the wave's 128 columns and one exchange with lane
+// l ^ 32, in a fixed order that depends only on the column, never on the
+// row's position or the batch: the per-row result is the same in every
+// launch (batch invariance).  The maximum is exact in any order, so it is
+// taken first over the statistics tile; one exp per element then serves
+// both s_j and e.
 //
 // TM = 32-row blocks per wave along M: kTM (the 256-row tile) or 1 (the
-// 64-row tile for small row counts).  Both run the same MFMA per 32 x 32
-// block in the same K order and the same per-row folds below, so a row's
+// 64-row tiles for small row counts).  The single-stage 64-row form
+// (kStages64 = 1, one row block) takes 256 columns in workgroups
+// [0, nfull) and 128 columns (one statistics tile; the column-half-1 waves
+// idle) in the rest, so that the head's columns spread evenly over the CUs
+// (see launch_fwd_logits).  Every form runs the same MFMA per 32 x 32 block
+// in the same K order and the same per-wave folds below, so a row's
 // statistics and draw are bit-identical whichever tile computes them.
 // kWFmt: -1 for a bf16 / fp32 head, 0 / 1 for an MXFP4 / MXFP8 head read
 // by the 64-row tile (the accumulators are those of the expanded head).
@@ -212,20 +224,31 @@ template <typename T, bool kStoreE, bool kSample, int TM, int kWFmt = -1,
           int kStages64 = 2, int kTokOff = -1>
 __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
   static_assert(TM == kTM || (TM == 1 && !kStoreE), "64-row tile: no e output");
-  constexpr int BM = 64 * TM;  // tile rows
-  constexpr int RW = 32 * TM;  // rows per wave
-  // epilogue arrays [2][BM] each: row maxima, row sums and (sampling call)
-  // the best draw and its index; after the e tile (256-row tile) or over
-  // the drained stage buffers (64-row tile)
-  constexpr int kEpi = TM == kTM ? kLdsBytes : 0;
+  constexpr bool kMixed = TM == 1 && kStages64 == 1 && kWFmt < 0;
+  constexpr int BM = 64 * TM;       // tile rows
+  constexpr int RW = 32 * TM;       // rows per wave
   const RowCount rc = to_rc(a.rows);
   const int M = rc.get();
-  // Only the tiles of the M rows present are numbered (M may be a device
-  // count below the launch bound), so the active tiles spread over all XCDs.
-  const int mt = (M + BM - 1) / BM;
-  if ((int)blockIdx.x >= mt * a.nt) return;
-  const TileCoord tc = map_tile(blockIdx.x, mt * a.nt, mt, a.nt);
-  const int m0 = tc.tm * BM, n0 = tc.tn * kBN;
+  int m0, n0;
+  bool one_half = false;  // a 128-column workgroup of the single-stage form
+  if constexpr (kMixed) {
+    // one row block (the host launches this form for at most 64 rows);
+    // a.nt counts the workgroups
+    if (M <= 0 || (int)blockIdx.x >= a.nt) return;
+    const int b = blockIdx.x;
+    one_half = b >= a.nfull;
+    m0 = 0;
+    n0 = one_half ? a.nfull * kBN + (b - a.nfull) * (kBN / 2) : b * kBN;
+  } else {
+    // Only the tiles of the M rows present are numbered (M may be a device
+    // count below the launch bound), so the active tiles spread over all
+    // XCDs.
+    const int mt = (M + BM - 1) / BM;
+    if ((int)blockIdx.x >= mt * a.nt) return;
+    const TileCoord tc = map_tile(blockIdx.x, mt * a.nt, mt, a.nt);
+    m0 = tc.tm * BM;
+    n0 = tc.tn * kBN;
+  }
 
   // The 256-row tile's row tokens for the gather, brought into LDS (stok,
   // outside the stage buffers) by one 4-byte DMA load per lane before the
@@ -252,7 +275,7 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
   if constexpr (TM == kTM) {
     gemm_mainloop<T, true>(a.op, M, m0, n0, a.nk, acc, lds);
   } else if constexpr (kWFmt < 0) {
-    gemm_mainloop_rows64<T, kStages64>(a.op, M, m0, n0, a.nk, acc, lds);
+    gemm_mainloop_rows64<T, kStages64>(a.op, M, m0, n0, a.nk, acc, lds, one_half);
   } else {
     bool bad = false;
     gemm_mainloop_rows64_mx<kWFmt>(a.op, a.wcodes, a.wscales, a.H, M, m0, n0,
@@ -262,9 +285,15 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
+  // the idle waves of a 128-column workgroup are done (no barrier follows
+  // in this form's epilogue)
+  if (one_half && wn) return;
   const int half = lane >> 5, l32 = lane & 31;
-  float* wmax = reinterpret_cast<float*>(lds + kEpi);           // [2][BM]
-  float* wsum = reinterpret_cast<float*>(lds + kEpi + 8 * BM);  // [2][BM]
+  // the wave's statistics tile: columns js * 128 .. + 127; none of them
+  // below V only in the last tile column of a V that is not a multiple of
+  // 256 (uniform across the wave)
+  const int js = (n0 + wn * 128) / 128;
+  const bool wvalid = js * 128 < a.V;
   // column of register r in block ni: cbase + 32 ni + 8 (r / 4) + (r % 4)
   const int cbase = n0 + wn * 128 + 4 * half;
 
@@ -296,9 +325,9 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
     }
   }
 
-  // Tile row maxima.  Columns >= V (last vocab tile only) hold a copy of
-  // column V - 1 (the main loop reads B rows >= N from row N - 1), which
-  // cannot change a maximum, so no mask is needed here.
+  // Statistics-tile row maxima.  Columns >= V (last statistics tile only)
+  // hold a copy of column V - 1 (the main loop reads B rows >= N from row
+  // N - 1), which cannot change a maximum, so no mask is needed here.
   float rm[TM];
 #pragma unroll
   for (int mi = 0; mi < TM; ++mi) {
@@ -307,18 +336,11 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
     for (int ni = 0; ni < kTN; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[mi][ni][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    if (half == 0) wmax[wn * BM + wm * RW + mi * 32 + l32] = mx;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int mi = 0; mi < TM; ++mi) {
-    const int R = wm * RW + mi * 32 + l32;
-    rm[mi] = fmaxf(wmax[R], wmax[BM + R]);
+    rm[mi] = fmaxf(mx, __shfl_xor(mx, 32, 64));
   }
 
-  // exp(z - m_tile) once per element, 0 for columns >= V; row sums in a
-  // fixed order
+  // exp(z - m) once per element, 0 for columns >= V; row sums in a fixed
+  // order; the wave's partials straight to global memory
   typedef typename EStore<T>::type E;
   E* e = reinterpret_cast<E*>(a.e);
   auto pass2 = [&](auto full_c) {
@@ -331,11 +353,11 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
       const int R = wm * RW + mi * 32 + l32;
       const bool rvalid = m0 + R < M;
       // exp(z - m) = 2^((z - m) log2 e).  z - m is formed first, so the
-      // maximum's own term is 2^0 = 1 exactly: s_tile >= 1, lse >= m, and
+      // maximum's own term is 2^0 = 1 exactly: s >= 1, lse >= m, and
       // log pi = z[a_t] - lse <= 0 with lse = m exactly on a row whose other
       // tokens carry less than an ulp of mass.
       const float mrow = rm[mi];
-      // bf16 store: exp(z - r ln 2) = exp(z - m_tile) 2^(m_tile log2 e - r)
+      // bf16 store: exp(z - r ln 2) = exp(z - m) 2^(m log2 e - r)
       float esc = 0.f;
       if constexpr (kStoreE && sizeof(T) == 2)
         esc = __builtin_amdgcn_exp2f(mrow * kLog2e - e_ref2(mrow));
@@ -366,12 +388,13 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
             }
           }
         }
-      // the wave's 128 columns: lower column half first
+      // the wave's 128 columns: lower lane half first
       const float so = __shfl_xor(s, 32, 64);
-      if (half == 0) wsum[wn * BM + R] = s + so;
+      if (half == 0 && rvalid && wvalid)
+        a.partials[(int64_t)js * a.ldp + rc.base + m0 + R] = make_float2(mrow, s + so);
     }
   };
-  if (n0 + kBN <= a.V) pass2(BoolC<true>{});
+  if (n0 + wn * 128 + 128 <= a.V) pass2(BoolC<true>{});
   else pass2(BoolC<false>{});
   if constexpr (kStoreE && sizeof(T) == 2 && kTokOff >= 0) {
     // the row's own token column stays 0 in e (its dL/dz is applied exactly
@@ -391,13 +414,10 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
     }
   }
   if constexpr (kSample) {
-    // The draw: per row, the best z + g over the tile's columns < V (see
-    // gumbel_of_bits; counter (v / 4, id_lo, id_hi, 0), key = the seed, word
-    // v % 4), under draw_better's total order, so the order in which lanes
-    // and waves meet does not matter.
-    float* wbs = reinterpret_cast<float*>(lds + kEpi + 16 * BM);  // [2][BM]
-    int* wbv = reinterpret_cast<int*>(lds + kEpi + 24 * BM);      // [2][BM]
-    float* wbz = reinterpret_cast<float*>(lds + kEpi + 32 * BM);  // [2][BM]
+    // The draw: per row, the best z + g over the statistics tile's columns
+    // < V (see gumbel_of_bits; counter (v / 4, id_lo, id_hi, 0), key =
+    // the seed, word v % 4), under draw_better's total order, so the order
+    // in which lanes meet does not matter; one candidate per statistics tile.
     const uint32_t k0 = (uint32_t)a.seed, k1 = (uint32_t)(a.seed >> 32);
     static_for<0, TM>([&](auto mi_c) {
       constexpr int mi = decltype(mi_c)::value;
@@ -423,9 +443,8 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
           constexpr int q = decltype(qj_c)::value / 4, j = decltype(qj_c)::value % 4;
           const int v = cbase + ni * 32 + 8 * q + j;
           const float z = acc[mi][ni][4 * q + j];
-          float sc = z + gumbel_of_bits(x[q][j]);
-          sc = v < a.V ? sc : -__builtin_inff();
-          const bool take = sc > bs;
+          const float sc = z + gumbel_of_bits(x[q][j]);
+          const bool take = sc > bs && v < a.V;  // columns >= V never win
           bs = take ? sc : bs;
           bv = take ? v : bv;
           bz = take ? z : bz;
@@ -439,36 +458,15 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
         bv = ov;
         bz = oz;
       }
-      if (half == 0) {
-        wbs[wn * BM + R] = bs;
-        wbv[wn * BM + R] = bv;
-        wbz[wn * BM + R] = bz;
+      if (half == 0 && m0 + R < M && wvalid) {
+        const int64_t o = (int64_t)js * a.ldp + rc.base + m0 + R;
+        a.cand[o] = make_float2(bs, __builtin_bit_cast(float, bv));
+        a.candz[o] = bz;
       }
     });
-    __syncthreads();
-    const int m = m0 + tid;
-    if (tid < BM && m < M) {
-      float bs = wbs[tid];
-      int bv = wbv[tid];
-      float bz = wbz[tid];
-      if (draw_better(wbs[BM + tid], wbv[BM + tid], bs, bv)) {
-        bs = wbs[BM + tid];
-        bv = wbv[BM + tid];
-        bz = wbz[BM + tid];
-      }
-      const int64_t o = (int64_t)tc.tn * a.ldp + rc.base + m;
-      a.cand[o] = make_float2(bs, __builtin_bit_cast(float, bv));
-      a.candz[o] = bz;
-    }
-  }
-  __syncthreads();
-  {
-    const int m = m0 + tid;
-    if (tid < BM && m < M)
-      a.partials[(int64_t)tc.tn * a.ldp + rc.base + m] =
-          make_float2(fmaxf(wmax[tid], wmax[BM + tid]), wsum[tid] + wsum[BM + tid]);
   }
   if constexpr (kStoreE && sizeof(T) == 2) {
+    __syncthreads();  // every wave's staged e
     // 16-byte row chunks: 32 lanes cover one 512-byte tile row.  Columns
     // >= V hold 0; rows from M up to the next multiple of 64 (read by the
     // dW GEMM's last K stage) are stored as 0, rows past that and columns
@@ -493,11 +491,10 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
 template <typename T, bool kStoreE, bool kSample = false>
 __global__ RZ_GEMM_ATTR void k_fwd_logits(FwdArgs a) {
   // [0, 128 KB): main-loop stages, then (learner call, bf16) the e tile;
-  // then the epilogue arrays, [2][256] floats each; then the row tokens
-  // (the draw gathers nothing: its tokens are drawn later)
-  constexpr int kEpiBytes = kSample ? 10240 : 4096;
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes + kEpiBytes + (kSample ? 0 : 4 * kBM)];
-  fwd_logits_body<T, kStoreE, kSample, kTM, -1, 2, kSample ? -1 : kLdsBytes + kEpiBytes>(a, lds);
+  // then the row tokens (the draw gathers nothing: its tokens are drawn
+  // later)
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes + (kSample ? 0 : 4 * kBM)];
+  fwd_logits_body<T, kStoreE, kSample, kTM, -1, 2, kSample ? -1 : kLdsBytes>(a, lds);
 }
 
 // The 64-row tile: 80 KB of LDS and a quarter of the accumulators, so two
@@ -512,7 +509,8 @@ void k_fwd_logits64(FwdArgs a) {
 
 // The single-stage 64-row tile for at most 64 rows (one row block): 40 KB of
 // LDS and at most 168 VGPRs, three workgroups per CU (see
-// gemm_mainloop_rows64); same per-row results.
+// gemm_mainloop_rows64); same per-row results.  Workgroups [0, nfull) take
+// 256 columns, the rest 128 (see launch_fwd_logits).
 template <typename T, bool kSample>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void k_fwd_logits64_1s(FwdArgs a) {
@@ -531,15 +529,15 @@ void k_fwd_logits64_mx(FwdArgs a) {
 }
 
 // ===================================================================
-// bi_logsoftmax_gather merge: one wave per row.  Lane q folds the vocab-tile
-// partials q, q + 64, q + 128, ... in ascending order with
+// bi_logsoftmax_gather merge: one wave per row.  Lane q folds the
+// statistics-tile partials q, q + 64, q + 128, ... in ascending order with
 // (m, s) <- (m', s e^(m - m') + s_j e^(m_j - m')), m' = max(m, m_j); the
 // 64 lane results then meet in a fixed xor tree (offsets 32, 16, ..., 1),
 // and lane 0's result is used.  lse = m + log s and log pi = z[a_t] - lse.
 // The tree's shape and the tiles each lane folds depend only on V, never on
 // the number of rows or the row's position.
 // ===================================================================
-constexpr int kMergeBatch = 4;  // tile partials loaded ahead per lane
+constexpr int kMergeBatch = 20;  // tile partials loaded ahead per lane (1280 per wave)
 
 __device__ __forceinline__ void ms_fold(float& m, float& s, float mj,
                                         float sj) {
@@ -559,23 +557,18 @@ __device__ __forceinline__ void ms_merge(float& m, float& s, float mj, float sj)
   ms_fold(m, s, mj, sj);
 }
 
-// Learner call (eref non-null): also the row's e reference r* = e_ref2 of
-// the row maximum, and whether any of its tiles was stored against another
-// (e_ref2 is monotone, so that is exactly when the smallest tile maximum
-// maps elsewhere); k_erebase fixes those rows.
-__global__ __launch_bounds__(256) void k_lse_merge(
-    const float2* __restrict__ partials, int64_t ldp, int nt, DevRows rows,
-    const float* __restrict__ ztgt, const int* __restrict__ row_tokens, int V,
-    float* lse_out, float* logpi_out, const int* scatter_idx,
-    float* logprobs_rows, int* err, float* eref, int* eflag) {
-  const RowCount rc = to_rc(rows);
-  const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
+// One row's log-sum-exp over its statistics tiles, by one wave: lane q
+// folds tiles q, q + 64, ... in ascending order (loads kMergeBatch ahead),
+// then the lanes meet in a fixed butterfly (offsets 32, 16, ..., 1).  The
+// order depends on nt only, never on the row or the batch.  mlo: the
+// smallest tile maximum (learner call only).
+__device__ __forceinline__ float row_lse(const float2* __restrict__ partials,
+                                         int64_t ldp, int nt, int64_t pos,
+                                         bool want_mlo, float* m_out,
+                                         float* mlo_out) {
   const int q = threadIdx.x & 63;
-  if (p >= rc.get()) return;  // uniform per wave
-  const int64_t pos = rc.base + p;
   float m = kNegInf, s = 0.f, mlo = __builtin_inff();
   for (int t0 = q; t0 < nt; t0 += 64 * kMergeBatch) {
-    // loads issued kMergeBatch at a time, folded in ascending tile order
     float2 ms[kMergeBatch];
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j) {
@@ -594,23 +587,46 @@ __global__ __launch_bounds__(256) void k_lse_merge(
     const float mj = __shfl_xor(m, o, 64);
     const float sj = __shfl_xor(s, o, 64);
     ms_merge(m, s, mj, sj);
-    if (eref) mlo = fminf(mlo, __shfl_xor(mlo, o, 64));
+    if (want_mlo) mlo = fminf(mlo, __shfl_xor(mlo, o, 64));
   }
-  if (q != 0) return;
-  const float lse = m + logf(s);
-  const int tok = row_tokens[pos];
-  float lp;
+  *m_out = m;
+  *mlo_out = mlo;
+  return m + logf(s);
+}
+
+// log pi = z[a_t] - lse for a token in range, else NaN (and err bit 1).
+// z[a_t] is an element of the tile statistics' own accumulators, so
+// z[a_t] <= m <= lse (the tile holding the maximum adds exp2(0) = 1 to s)
+// and log pi <= 0 already; the clamp keeps that promise for any input (NaN
+// stays NaN).
+__device__ __forceinline__ float logpi_of(int tok, int V, float z, float lse,
+                                          int* err) {
   if (tok >= 0 && tok < V) {
-    // z[a_t] is an element of the tile statistics' own accumulators, so
-    // z[a_t] <= m <= lse (the tile holding the maximum adds exp2(0) = 1 to
-    // s) and lp <= 0 already; the clamp keeps that promise for any input
-    // (NaN stays NaN).
-    lp = ztgt[pos] - lse;
-    lp = lp > 0.f ? 0.f : lp;
-  } else {
-    lp = __builtin_nanf("");
-    if (err) atomicOr(err, 1);
+    const float lp = z - lse;
+    return lp > 0.f ? 0.f : lp;
   }
+  if (err) atomicOr(err, 1);
+  return __builtin_nanf("");
+}
+
+// Learner call (eref non-null): also the row's e reference r* = e_ref2 of
+// the row maximum, and whether any of its tiles was stored against another
+// (e_ref2 is monotone, so that is exactly when the smallest tile maximum
+// maps elsewhere); k_erebase fixes those rows.
+__global__ __launch_bounds__(256) void k_lse_merge(
+    const float2* __restrict__ partials, int64_t ldp, int nt, DevRows rows,
+    const float* __restrict__ ztgt, const int* __restrict__ row_tokens, int V,
+    float* lse_out, float* logpi_out, const int* scatter_idx,
+    float* logprobs_rows, int* err, float* eref, int* eflag) {
+  const RowCount rc = to_rc(rows);
+  const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (p >= rc.get()) return;  // uniform per wave
+  const int64_t pos = rc.base + p;
+  float m, mlo;
+  const float lse = row_lse(partials, ldp, nt, pos, eref != nullptr, &m, &mlo);
+  if ((threadIdx.x & 63) != 0) return;
+  const int tok = row_tokens[pos];
+  const float lp = logpi_of(tok, V, tok >= 0 && tok < V ? ztgt[pos] : 0.f, lse, err);
   if (lse_out) lse_out[pos] = lse;
   if (logpi_out) logpi_out[pos] = lp;
   if (scatter_idx) logprobs_rows[scatter_idx[pos]] = lp;
@@ -621,13 +637,15 @@ __global__ __launch_bounds__(256) void k_lse_merge(
   }
 }
 
-// The draw's merge: per row (one wave), the best (score, index) over the
-// vocab tiles under draw_better's total order, so any meeting order of
-// lanes and tiles gives the same winner; the winner's logit comes along as
-// the record's z[a_t].
+// The draw's merge and record, per row (one wave): the best (score, index)
+// over the statistics tiles' candidates under draw_better's total order (so
+// any meeting order of lanes and tiles gives the same winner), whose logit
+// comes along as the record's z[a_t]; then the row's lse by row_lse, the
+// fold k_lse_merge takes, and log mu = z[a_t] - lse.
 __global__ __launch_bounds__(256) void k_draw_merge(
-    const float2* __restrict__ cand, const float* __restrict__ candz, int64_t ldp,
-    int nt, int64_t n, int* __restrict__ tokens, float* __restrict__ ztgt) {
+    const float2* __restrict__ cand, const float* __restrict__ candz,
+    const float2* __restrict__ partials, int64_t ldp, int nt, int64_t n, int V,
+    int* __restrict__ tokens, float* __restrict__ logmu, float* __restrict__ lse_out) {
   const int64_t p = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int q = threadIdx.x & 63;
   if (p >= n) return;  // uniform per wave
@@ -666,9 +684,12 @@ __global__ __launch_bounds__(256) void k_draw_merge(
       bz = oz;
     }
   }
+  float m, mlo;
+  const float lse = row_lse(partials, ldp, nt, p, false, &m, &mlo);
   if (q == 0) {
     tokens[p] = bv;
-    ztgt[p] = bz;
+    logmu[p] = logpi_of(bv, V, bz, lse, nullptr);
+    if (lse_out) lse_out[p] = lse;
   }
 }
 
@@ -1453,9 +1474,9 @@ __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ in,
 // ===================================================================
 // Backward, part 1: dlogits.
 //
-// fp32 inputs: the forward stored e[t, v] = exp(z[t, v] - m_tile(t, j)) in
-// the dz buffer for the vocab tile j holding v; with lse_t known,
-// dz[t, v] = c_t exp(m_tile(t, j) - lse_t) e[t, v] is dL/dz for v != a_t; the
+// fp32 inputs: the forward stored e[t, v] = exp(z[t, v] - m_j) in the dz
+// buffer, m_j the maximum of the statistics tile j holding v; with lse_t
+// known, dz[t, v] = c_t exp(m_j - lse_t) e[t, v] is dL/dz for v != a_t; the
 // token's own column is left at 0 and its whole dL/dz, c_t (p[a_t] - 1), is
 // applied exactly in fp32 by the dHidden epilogue and the dW fix-up.
 // k_dz_scale rescales e in place into the token-major dz [C, Vpad], the A
@@ -1483,11 +1504,11 @@ __global__ __launch_bounds__(256) void k_dz_scale(
   if (r0 >= ((R + 63) & ~63)) return;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int tr = (lane % 16) * 4;  // first row of the block
-  // one scale per row: c_t exp(m_tile(t, j) - lse_t), j the vocab tile
-  // holding the workgroup's 64 columns
+  // one scale per row: c_t exp(m_j - lse_t), j the statistics tile (128
+  // columns) holding the workgroup's 64 columns
   if (tid < 64) {
     const int t = r0 + tid;
-    const int j = (blockIdx.x * 64) / kBN;
+    const int j = (blockIdx.x * 64) / 128;
     float v = 0.f;
     if (t < R) {
       const int64_t pos = rc.base + t;
@@ -1521,7 +1542,7 @@ __global__ __launch_bounds__(256) void k_dz_scale(
         f32x4{y[0][q], y[1][q], y[2][q], y[3][q]};
 }
 
-// bf16 rows whose vocab tiles were stored against different e references
+// bf16 rows whose statistics tiles were stored against different e references
 // (k_lse_merge's flag): each tile j with r_j != r*_t is multiplied by
 // 2^(r_j - r*_t) <= 1, an exact power of two, so those tiles share the row's
 // reference without a second rounding.  One wave per row; the other rows
@@ -1538,19 +1559,20 @@ __global__ __launch_bounds__(256) void k_erebase(
   const float rs = eref[pos];
   const int lane = threadIdx.x & 63;
   bf16* row = e + (int64_t)p * lde;
-  for (int j = 0; j < nt; ++j) {
+  for (int j = 0; j < nt; ++j) {  // statistics tiles of 128 columns
     const float d = e_ref2(partials[(int64_t)j * ldp + pos].x) - rs;
     if (d == 0.f) continue;  // uniform per wave
-    const int c = j * kBN + lane * 4;
+    const int c = j * 128 + lane * 2;
     if (c >= Vpad) continue;
     // d <= 0 (e_ref2 is monotone and r* is the row maximum's); far below,
     // the products flush to 0 (their terms are below 2^-1000 of the row's)
     const int k = d < -1000.f || d != d ? -1000 : (int)d;
-    u32x2* q = reinterpret_cast<u32x2*>(row + c);
-    bf16x4 v = __builtin_bit_cast(bf16x4, *q);
+    uint32_t* q = reinterpret_cast<uint32_t*>(row + c);
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 v = __builtin_bit_cast(bf16x2, *q);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = (bf16)ldexpf((float)v[i], k);
-    *q = __builtin_bit_cast(u32x2, v);
+    for (int i = 0; i < 2; ++i) v[i] = (bf16)ldexpf((float)v[i], k);
+    *q = __builtin_bit_cast(uint32_t, v);
   }
 }
 
@@ -2129,6 +2151,25 @@ inline int cu_count() {
   return ncu;
 }
 
+// The workgroups of the single-stage 64-row form (one row block, where each
+// CU streams its share of the head): whole rounds of 256-column workgroups
+// over the CUs, then the statistics tiles left (128 columns each) as
+// 128-column workgroups when there are at most as many as CUs, else as
+// 256-column workgroups: at most one more workgroup per CU either way.  For
+// a 151936-word head on 256 CUs that is 512 workgroups of 256 columns and
+// 163 of 128, so no CU streams more than 640 of the head's columns (594
+// tiles of 256 put 768 on some).
+struct ColSplit {
+  int nfull, nblk;  // 256-column workgroups first, then 128-column ones
+};
+inline ColSplit split_columns(int V) {
+  const int units = cdiv(V, kBN / 2), ncu = cu_count();
+  const int nfull = units / (2 * ncu) * ncu;
+  const int rest = units - 2 * nfull;
+  if (rest > ncu) return {nfull + cdiv(rest, 2), nfull + cdiv(rest, 2)};
+  return {nfull, nfull + rest};
+}
+
 }  // namespace
 
 const char* kernel_name(int k) {
@@ -2159,8 +2200,14 @@ hipError_t launch_fwd_sample(int dt, const void* hidden, int64_t n,
   a.Vpad = V;
   a.nk = H / (dt ? Stage<bf16>::kK : Stage<float>::kK);
   const bool small = n <= kRows64MaxSample;
+  const bool one = small && n <= kBM64;  // the single-stage 64-row tile
   a.mt = cdiv(n, small ? kBM64 : kBM);
   a.nt = cdiv(V, kBN);
+  if (one) {
+    const ColSplit cs = split_columns(V);
+    a.nfull = cs.nfull;
+    a.nt = cs.nblk;
+  }
   a.partials = partials;
   a.ldp = ldp;
   a.row_ids = row_ids;
@@ -2169,7 +2216,7 @@ hipError_t launch_fwd_sample(int dt, const void* hidden, int64_t n,
   a.candz = candz;
   const int nblk = a.mt * a.nt;
   return timed(K_FWD_SAMPLE, s, [&] {
-    if (small && n <= kBM64) {
+    if (one) {
       if (dt) k_fwd_logits64_1s<bf16, true><<<nblk, kThreads, 0, s>>>(a);
       else k_fwd_logits64_1s<float, true><<<nblk, kThreads, 0, s>>>(a);
     } else if (small) {
@@ -2225,11 +2272,13 @@ hipError_t launch_fwd_mx(int fmt, const void* hidden, int64_t n,
   });
 }
 
-hipError_t launch_draw_merge(const float2* cand, const float* candz, int64_t ldp,
-                             int nt, int64_t n, int* tokens, float* ztgt,
-                             hipStream_t s) {
+hipError_t launch_draw_merge(const float2* cand, const float* candz,
+                             const float2* partials, int64_t ldp, int nt,
+                             int64_t n, int V, int* tokens, float* logmu,
+                             float* lse, hipStream_t s) {
   return timed(K_DRAW_MERGE, s, [&] {
-    k_draw_merge<<<cdiv(n, 4), 256, 0, s>>>(cand, candz, ldp, nt, n, tokens, ztgt);
+    k_draw_merge<<<cdiv(n, 4), 256, 0, s>>>(cand, candz, partials, ldp, nt, n, V,
+                                            tokens, logmu, lse);
   });
 }
 
@@ -2249,8 +2298,14 @@ hipError_t launch_fwd_logits(int dt, const void* hidden, int64_t lda_bytes,
   // host-known small row counts without the e output take the 64-row tile
   // (same per-row results, a quarter of the MFMA work per W byte)
   const bool small = !rows.count && !e && rows.cap <= kRows64MaxLogits;
+  const bool one = small && rows.cap <= kBM64;  // the single-stage 64-row tile
   a.mt = cdiv(rows.cap, small ? kBM64 : kBM);
   a.nt = cdiv(V, kBN);
+  if (one) {
+    const ColSplit cs = split_columns(V);
+    a.nfull = cs.nfull;
+    a.nt = cs.nblk;
+  }
   a.partials = partials;
   a.ldp = ldp;
   a.e = e;
@@ -2260,7 +2315,7 @@ hipError_t launch_fwd_logits(int dt, const void* hidden, int64_t lda_bytes,
   const int nblk = a.mt * a.nt;
   if (small)
     return timed(K_FWD_LOGITS, s, [&] {
-      if (rows.cap <= kBM64) {
+      if (one) {
         if (dt) k_fwd_logits64_1s<bf16, false><<<nblk, kThreads, 0, s>>>(a);
         else k_fwd_logits64_1s<float, false><<<nblk, kThreads, 0, s>>>(a);
       } else {
