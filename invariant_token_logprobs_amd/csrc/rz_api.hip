@@ -25,6 +25,18 @@ constexpr int kChunkRows = 32768;  // backward token chunk (a multiple of 256)
 constexpr int kVocabTile = 128;
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+// Layout of the statistics-tile partials and draw candidates: (tile j, row
+// p) at j * lt + p * lr.  Host-known row counts up to 256 keep one row's
+// tiles contiguous (the merge's loads of a row coalesce; the forward stores
+// few of them); larger ones keep one tile's rows contiguous (the forward's
+// stores coalesce).
+struct PartLayout {
+  int64_t lt, lr;
+};
+inline PartLayout part_layout(int64_t n, int nt) {
+  return n <= 256 ? PartLayout{1, nt} : PartLayout{n, 1};
+}
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 inline size_t esize(rz_dtype dt) { return dt == RZ_DTYPE_BF16 ? 2 : 4; }
 
@@ -458,11 +470,12 @@ static rz_status sample_core(const void* hidden, const void* lm_head,
   const int nt = (V + kVocabTile - 1) / kVocabTile;
   // the logits GEMM with the draw in its epilogue (the winning column's
   // logit comes along), then the draw's merge
+  const PartLayout pl = part_layout(n_rows, nt);
   RZ_TRY(launch_fwd_sample(dt, hidden, n_rows, lm_head, H, V, row_ids, seed,
-                           w.partials, w.cand, w.candz, n_rows, s));
+                           w.partials, w.cand, w.candz, pl.lt, pl.lr, s));
   // the draw's merge and the record (rz_token_logprobs' own lse fold)
-  RZ_TRY(launch_draw_merge(w.cand, w.candz, w.partials, n_rows, nt, n_rows, V,
-                           tokens, logmu, lse, s));
+  RZ_TRY(launch_draw_merge(w.cand, w.candz, w.partials, pl.lt, pl.lr, nt,
+                           n_rows, V, tokens, logmu, lse, s));
   return RZ_OK;
 }
 
@@ -523,10 +536,11 @@ rz_status rz_token_logprobs(const void* hidden, const void* lm_head,
   carve_tlp(c, n_rows, V, &w);
   const int nt = (V + kVocabTile - 1) / kVocabTile;
   DevRows rows{nullptr, 0, (int)n_rows};
+  const PartLayout pl = part_layout(n_rows, nt);
   RZ_TRY(launch_fwd_logits(dt, hidden, (int64_t)H * esize(dt), nullptr, rows,
-                           lm_head, H, V, tokens, w.partials, n_rows, w.ztgt,
-                           nullptr, 0, 0, s));
-  RZ_TRY(launch_lse_merge(w.partials, n_rows, nt, rows, w.ztgt, tokens, V,
+                           lm_head, H, V, tokens, w.partials, pl.lt, pl.lr,
+                           w.ztgt, nullptr, 0, 0, s));
+  RZ_TRY(launch_lse_merge(w.partials, pl.lt, pl.lr, nt, rows, w.ztgt, tokens, V,
                           lse, logprobs, nullptr, nullptr, err_flag, nullptr,
                           nullptr, s));
   return RZ_OK;
@@ -596,9 +610,9 @@ static rz_status fwd_bwd_core(
     DevRows crow{w.nvalid, k * C, C};
     if (N > 0) {
       RZ_TRY(launch_fwd_logits(dt, hidden, lda, w.idx, crow, lm_head, H, V,
-                               w.tokv, w.partials, N, w.ztgt, w.dz, Vpad, Vpad,
-                               s));
-      RZ_TRY(launch_lse_merge(w.partials, N, nt, crow, w.ztgt, w.tokv, V,
+                               w.tokv, w.partials, N, 1, w.ztgt, w.dz, Vpad,
+                               Vpad, s));
+      RZ_TRY(launch_lse_merge(w.partials, N, 1, nt, crow, w.ztgt, w.tokv, V,
                               w.lse_v, w.logpi_v, w.idx, logprobs, err_flag,
                               b16 ? w.eref : nullptr, w.eflag, s));
       RZ_TRY(launch_coef(crow, w.logpi_v, logmu, w.idx, w.respv, w.fcoef, sc,
@@ -784,19 +798,20 @@ rz_status rz_token_logprobs_mx(const void* hidden, const uint8_t* codes,
   carve_tlp(c, n_rows, V, &w);
   const int nt = (V + kVocabTile - 1) / kVocabTile;
   DevRows rows{nullptr, 0, (int)n_rows};
+  const PartLayout pl = part_layout(n_rows, nt);
   if (fused) {
     RZ_TRY(launch_fwd_mx(fmt, hidden, n_rows, codes, scales, H, V, tokens,
-                         w.partials, n_rows, w.ztgt, nullptr, 0, nullptr,
+                         w.partials, pl.lt, pl.lr, w.ztgt, nullptr, 0, nullptr,
                          nullptr, err_flag, s));
   } else {
     void* Wb = c.take<char>(2 * (size_t)V * (size_t)H);
     RZ_TRY(launch_mx_dequant(fmt, codes, scales, (int64_t)V * (H / 32), Wb,
                              err_flag, s));
     RZ_TRY(launch_fwd_logits(RZ_DTYPE_BF16, hidden, (int64_t)H * 2, nullptr,
-                             rows, Wb, H, V, tokens, w.partials, n_rows,
+                             rows, Wb, H, V, tokens, w.partials, pl.lt, pl.lr,
                              w.ztgt, nullptr, 0, 0, s));
   }
-  RZ_TRY(launch_lse_merge(w.partials, n_rows, nt, rows, w.ztgt, tokens, V,
+  RZ_TRY(launch_lse_merge(w.partials, pl.lt, pl.lr, nt, rows, w.ztgt, tokens, V,
                           lse, logprobs, nullptr, nullptr, err_flag, nullptr,
                           nullptr, s));
   return RZ_OK;
@@ -824,19 +839,20 @@ rz_status rz_sample_tokens_mx(const void* hidden, const uint8_t* codes,
   SmpWs w;
   carve_smp(c, n_rows, V, &w);
   const int nt = (V + kVocabTile - 1) / kVocabTile;
+  const PartLayout pl = part_layout(n_rows, nt);
   if (fused) {
     RZ_TRY(launch_fwd_mx(fmt, hidden, n_rows, codes, scales, H, V, nullptr,
-                         w.partials, n_rows, nullptr, row_ids, seed, w.cand,
+                         w.partials, pl.lt, pl.lr, nullptr, row_ids, seed, w.cand,
                          w.candz, err_flag, s));
   } else {
     void* Wb = c.take<char>(2 * (size_t)V * (size_t)H);
     RZ_TRY(launch_mx_dequant(fmt, codes, scales, (int64_t)V * (H / 32), Wb,
                              err_flag, s));
     RZ_TRY(launch_fwd_sample(RZ_DTYPE_BF16, hidden, n_rows, Wb, H, V, row_ids,
-                             seed, w.partials, w.cand, w.candz, n_rows, s));
+                             seed, w.partials, w.cand, w.candz, pl.lt, pl.lr, s));
   }
-  RZ_TRY(launch_draw_merge(w.cand, w.candz, w.partials, n_rows, nt, n_rows, V,
-                           tokens, logmu, lse, s));
+  RZ_TRY(launch_draw_merge(w.cand, w.candz, w.partials, pl.lt, pl.lr, nt,
+                           n_rows, V, tokens, logmu, lse, s));
   return RZ_OK;
 }
 

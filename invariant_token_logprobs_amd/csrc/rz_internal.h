@@ -67,20 +67,20 @@ hipError_t launch_fwd_logits(int dt, const void* hidden, int64_t lda_bytes,
                              const int* a_rows, DevRows rows,
                              const void* lm_head, int H, int V,
                              const int* row_tokens, float2* partials,
-                             int64_t ldp, float* ztgt, void* e, int64_t lde,
-                             int Vpad, hipStream_t s);
+                             int64_t ldp, int64_t ldr, float* ztgt, void* e,
+                             int64_t lde, int Vpad, hipStream_t s);
 // The logits GEMM with the draw in its epilogue: per (statistics tile, row)
 // the best (z + g, index) in cand and that column's z in candz.
 hipError_t launch_fwd_sample(int dt, const void* hidden, int64_t n,
                              const void* lm_head, int H, int V,
                              const uint64_t* row_ids, uint64_t seed,
                              float2* partials, float2* cand, float* candz,
-                             int64_t ldp, hipStream_t s);
+                             int64_t ldp, int64_t ldr, hipStream_t s);
 // The draw's winner per row (tokens) and the record: log mu = z[a_t] - lse
 // (and lse, nullable), lse by k_lse_merge's fold.
 hipError_t launch_draw_merge(const float2* cand, const float* candz,
-                             const float2* partials, int64_t ldp, int nt,
-                             int64_t n, int V, int* tokens, float* logmu,
+                             const float2* partials, int64_t ldp, int64_t ldr,
+                             int nt, int64_t n, int V, int* tokens, float* logmu,
                              float* lse, hipStream_t s);
 hipError_t launch_mx_dequant(int fmt, const uint8_t* codes, const uint8_t* scales,
                              int64_t nblk, void* out, int* err, hipStream_t s);
@@ -99,7 +99,7 @@ int mx_rows64_max(int sample);
 hipError_t launch_fwd_mx(int fmt, const void* hidden, int64_t n,
                          const uint8_t* codes, const uint8_t* scales, int H,
                          int V, const int* row_tokens, float2* partials,
-                         int64_t ldp, float* ztgt, const uint64_t* row_ids,
+                         int64_t ldp, int64_t ldr, float* ztgt, const uint64_t* row_ids,
                          uint64_t seed, float2* cand, float* candz, int* err,
                          hipStream_t s);
 size_t norm_partials(int64_t n);
@@ -111,7 +111,7 @@ hipError_t launch_resp_diag(const float* logpi, const float* logmu,
                             hipStream_t s);
 // eref / eflag (bf16 learner call, else null): the row's e reference and
 // whether its tiles need k_erebase
-hipError_t launch_lse_merge(const float2* partials, int64_t ldp, int nt,
+hipError_t launch_lse_merge(const float2* partials, int64_t ldp, int64_t ldr, int nt,
                             DevRows rows, const float* ztgt,
                             const int* row_tokens, int V, float* lse_out,
                             float* logpi_out, const int* scatter_idx,

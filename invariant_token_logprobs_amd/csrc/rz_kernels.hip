@@ -60,14 +60,14 @@ struct FwdArgs {
   GemmOperands op;
   DevRows rows;
   int V, Vpad, nk, mt, nt;
-  float2* partials;       // [nt][ldp] by list position
-  int64_t ldp;
+  float2* partials;       // (tile j, list position p) at j * ldp + p * ldr
+  int64_t ldp, ldr;
   void* e;                // learner call only: e (see EStore) [rows][lde]
   int64_t lde;
   const uint64_t* row_ids;  // sampling call only: the rows' identities
   uint64_t seed;
-  float2* cand;           // sampling call only: [nt][ldp] (best z + g, index)
-  float* candz;           // sampling call only: [nt][ldp] the best column's z
+  float2* cand;           // sampling call only, as partials: (best z + g, index)
+  float* candz;           // sampling call only, as partials: the best column's z
   const int* row_tokens;  // logits calls: a_t by list position (nullable)
   float* ztgt;            // logits calls: z[t, a_t] by list position
   const uint8_t* wcodes;  // MX head only: codes and E8M0 scales of W
@@ -213,7 +213,7 @@ __device__ __forceinline__ bool draw_better(float s, int v, float bs, int bv) {
 // (kStages64 = 1, one row block) takes 256 columns in workgroups
 // [0, nfull) and 128 columns (one statistics tile; the column-half-1 waves
 // idle) in the rest, so that the head's columns spread evenly over the CUs
-// (see launch_fwd_logits).  Every form runs the same MFMA per 32 x 32 block
+// (see split_columns).  Every form runs the same MFMA per 32 x 32 block
 // in the same K order and the same per-wave folds below, so a row's
 // statistics and draw are bit-identical whichever tile computes them.
 // kWFmt: -1 for a bf16 / fp32 head, 0 / 1 for an MXFP4 / MXFP8 head read
@@ -391,7 +391,8 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
       // the wave's 128 columns: lower lane half first
       const float so = __shfl_xor(s, 32, 64);
       if (half == 0 && rvalid && wvalid)
-        a.partials[(int64_t)js * a.ldp + rc.base + m0 + R] = make_float2(mrow, s + so);
+        a.partials[(int64_t)js * a.ldp + (rc.base + m0 + R) * a.ldr] =
+            make_float2(mrow, s + so);
     }
   };
   if (n0 + wn * 128 + 128 <= a.V) pass2(BoolC<true>{});
@@ -459,7 +460,7 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
         bz = oz;
       }
       if (half == 0 && m0 + R < M && wvalid) {
-        const int64_t o = (int64_t)js * a.ldp + rc.base + m0 + R;
+        const int64_t o = (int64_t)js * a.ldp + (rc.base + m0 + R) * a.ldr;
         a.cand[o] = make_float2(bs, __builtin_bit_cast(float, bv));
         a.candz[o] = bz;
       }
@@ -510,7 +511,7 @@ void k_fwd_logits64(FwdArgs a) {
 // The single-stage 64-row tile for at most 64 rows (one row block): 40 KB of
 // LDS and at most 168 VGPRs, three workgroups per CU (see
 // gemm_mainloop_rows64); same per-row results.  Workgroups [0, nfull) take
-// 256 columns, the rest 128 (see launch_fwd_logits).
+// 256 columns, the rest 128 (see split_columns).
 template <typename T, bool kSample>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void k_fwd_logits64_1s(FwdArgs a) {
@@ -563,7 +564,8 @@ __device__ __forceinline__ void ms_merge(float& m, float& s, float mj, float sj)
 // order depends on nt only, never on the row or the batch.  mlo: the
 // smallest tile maximum (learner call only).
 __device__ __forceinline__ float row_lse(const float2* __restrict__ partials,
-                                         int64_t ldp, int nt, int64_t pos,
+                                         int64_t ldp, int64_t ldr, int nt,
+                                         int64_t pos,
                                          bool want_mlo, float* m_out,
                                          float* mlo_out) {
   const int q = threadIdx.x & 63;
@@ -573,7 +575,7 @@ __device__ __forceinline__ float row_lse(const float2* __restrict__ partials,
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j) {
       const int t = t0 + 64 * j;
-      if (t < nt) ms[j] = partials[(int64_t)t * ldp + pos];
+      if (t < nt) ms[j] = partials[(int64_t)t * ldp + pos * ldr];
     }
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j)
@@ -614,7 +616,8 @@ __device__ __forceinline__ float logpi_of(int tok, int V, float z, float lse,
 // (e_ref2 is monotone, so that is exactly when the smallest tile maximum
 // maps elsewhere); k_erebase fixes those rows.
 __global__ __launch_bounds__(256) void k_lse_merge(
-    const float2* __restrict__ partials, int64_t ldp, int nt, DevRows rows,
+    const float2* __restrict__ partials, int64_t ldp, int64_t ldr, int nt,
+    DevRows rows,
     const float* __restrict__ ztgt, const int* __restrict__ row_tokens, int V,
     float* lse_out, float* logpi_out, const int* scatter_idx,
     float* logprobs_rows, int* err, float* eref, int* eflag) {
@@ -623,7 +626,7 @@ __global__ __launch_bounds__(256) void k_lse_merge(
   if (p >= rc.get()) return;  // uniform per wave
   const int64_t pos = rc.base + p;
   float m, mlo;
-  const float lse = row_lse(partials, ldp, nt, pos, eref != nullptr, &m, &mlo);
+  const float lse = row_lse(partials, ldp, ldr, nt, pos, eref != nullptr, &m, &mlo);
   if ((threadIdx.x & 63) != 0) return;
   const int tok = row_tokens[pos];
   const float lp = logpi_of(tok, V, tok >= 0 && tok < V ? ztgt[pos] : 0.f, lse, err);
@@ -644,7 +647,8 @@ __global__ __launch_bounds__(256) void k_lse_merge(
 // fold k_lse_merge takes, and log mu = z[a_t] - lse.
 __global__ __launch_bounds__(256) void k_draw_merge(
     const float2* __restrict__ cand, const float* __restrict__ candz,
-    const float2* __restrict__ partials, int64_t ldp, int nt, int64_t n, int V,
+    const float2* __restrict__ partials, int64_t ldp, int64_t ldr, int nt,
+    int64_t n, int V,
     int* __restrict__ tokens, float* __restrict__ logmu, float* __restrict__ lse_out) {
   const int64_t p = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int q = threadIdx.x & 63;
@@ -659,8 +663,8 @@ __global__ __launch_bounds__(256) void k_draw_merge(
     for (int j = 0; j < kMergeBatch; ++j) {
       const int t = t0 + 64 * j;
       if (t < nt) {
-        c[j] = cand[(int64_t)t * ldp + p];
-        cz[j] = candz[(int64_t)t * ldp + p];
+        c[j] = cand[(int64_t)t * ldp + p * ldr];
+        cz[j] = candz[(int64_t)t * ldp + p * ldr];
       }
     }
 #pragma unroll
@@ -685,7 +689,7 @@ __global__ __launch_bounds__(256) void k_draw_merge(
     }
   }
   float m, mlo;
-  const float lse = row_lse(partials, ldp, nt, p, false, &m, &mlo);
+  const float lse = row_lse(partials, ldp, ldr, nt, p, false, &m, &mlo);
   if (q == 0) {
     tokens[p] = bv;
     logmu[p] = logpi_of(bv, V, bz, lse, nullptr);
@@ -2191,7 +2195,7 @@ hipError_t launch_fwd_sample(int dt, const void* hidden, int64_t n,
                              const void* lm_head, int H, int V,
                              const uint64_t* row_ids, uint64_t seed,
                              float2* partials, float2* cand, float* candz,
-                             int64_t ldp, hipStream_t s) {
+                             int64_t ldp, int64_t ldr, hipStream_t s) {
   FwdArgs a{};
   a.op = GemmOperands{(const char*)hidden, (int64_t)H * (dt ? 2 : 4), nullptr,
                       0, (const char*)lm_head, (int64_t)H * (dt ? 2 : 4), V};
@@ -2210,6 +2214,7 @@ hipError_t launch_fwd_sample(int dt, const void* hidden, int64_t n,
   }
   a.partials = partials;
   a.ldp = ldp;
+  a.ldr = ldr;
   a.row_ids = row_ids;
   a.seed = seed;
   a.cand = cand;
@@ -2237,7 +2242,7 @@ int mx_rows64_max(int sample) { return sample ? kRows64MaxSample : kRows64MaxLog
 hipError_t launch_fwd_mx(int fmt, const void* hidden, int64_t n,
                          const uint8_t* codes, const uint8_t* scales, int H,
                          int V, const int* row_tokens, float2* partials,
-                         int64_t ldp, float* ztgt, const uint64_t* row_ids,
+                         int64_t ldp, int64_t ldr, float* ztgt, const uint64_t* row_ids,
                          uint64_t seed, float2* cand, float* candz, int* err,
                          hipStream_t s) {
   FwdArgs a{};
@@ -2250,6 +2255,7 @@ hipError_t launch_fwd_mx(int fmt, const void* hidden, int64_t n,
   a.nt = cdiv(V, kBN);
   a.partials = partials;
   a.ldp = ldp;
+  a.ldr = ldr;
   a.row_ids = row_ids;
   a.seed = seed;
   a.cand = cand;
@@ -2273,11 +2279,11 @@ hipError_t launch_fwd_mx(int fmt, const void* hidden, int64_t n,
 }
 
 hipError_t launch_draw_merge(const float2* cand, const float* candz,
-                             const float2* partials, int64_t ldp, int nt,
-                             int64_t n, int V, int* tokens, float* logmu,
+                             const float2* partials, int64_t ldp, int64_t ldr,
+                             int nt, int64_t n, int V, int* tokens, float* logmu,
                              float* lse, hipStream_t s) {
   return timed(K_DRAW_MERGE, s, [&] {
-    k_draw_merge<<<cdiv(n, 4), 256, 0, s>>>(cand, candz, partials, ldp, nt, n, V,
+    k_draw_merge<<<cdiv(n, 4), 256, 0, s>>>(cand, candz, partials, ldp, ldr, nt, n, V,
                                             tokens, logmu, lse);
   });
 }
@@ -2286,8 +2292,8 @@ hipError_t launch_fwd_logits(int dt, const void* hidden, int64_t lda_bytes,
                              const int* a_rows, DevRows rows,
                              const void* lm_head, int H, int V,
                              const int* row_tokens, float2* partials,
-                             int64_t ldp, float* ztgt, void* e, int64_t lde,
-                             int Vpad, hipStream_t s) {
+                             int64_t ldp, int64_t ldr, float* ztgt, void* e,
+                             int64_t lde, int Vpad, hipStream_t s) {
   FwdArgs a{};
   a.op = GemmOperands{(const char*)hidden, lda_bytes, a_rows, rows.base,
                       (const char*)lm_head, (int64_t)H * (dt ? 2 : 4), V};
@@ -2308,6 +2314,7 @@ hipError_t launch_fwd_logits(int dt, const void* hidden, int64_t lda_bytes,
   }
   a.partials = partials;
   a.ldp = ldp;
+  a.ldr = ldr;
   a.e = e;
   a.lde = lde;
   a.row_tokens = row_tokens;
@@ -2334,7 +2341,7 @@ hipError_t launch_fwd_logits(int dt, const void* hidden, int64_t lda_bytes,
   });
 }
 
-hipError_t launch_lse_merge(const float2* partials, int64_t ldp, int nt,
+hipError_t launch_lse_merge(const float2* partials, int64_t ldp, int64_t ldr, int nt,
                             DevRows rows, const float* ztgt,
                             const int* row_tokens, int V, float* lse_out,
                             float* logpi_out, const int* scatter_idx,
@@ -2342,7 +2349,7 @@ hipError_t launch_lse_merge(const float2* partials, int64_t ldp, int nt,
                             int* eflag, hipStream_t s) {
   return timed(K_LSE_MERGE, s, [&] {
     k_lse_merge<<<cdiv(rows.cap, 4), 256, 0, s>>>(
-        partials, ldp, nt, rows, ztgt, row_tokens, V, lse_out, logpi_out,
+        partials, ldp, ldr, nt, rows, ztgt, row_tokens, V, lse_out, logpi_out,
         scatter_idx, logprobs_rows, err, eref, eflag);
   });
 }
