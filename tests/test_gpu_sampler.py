@@ -141,6 +141,57 @@ def test_sampler_frequencies_follow_softmax():
     torch.cuda.empty_cache()
 
 
+def _split_vocabs(ncu):
+    """Vocabulary sizes that take each branch of the single-stage 64-row
+    form's column split on a device with ncu CUs: all 128-column workgroups
+    (few statistics tiles), whole rounds of 256-column workgroups plus at most
+    one 128-column workgroup per CU, and whole rounds plus further 256-column
+    workgroups (an odd tile count, V not a multiple of 128)."""
+    return [1000, 128 * (2 * ncu + ncu // 2), 128 * (3 * ncu + 37) - 50, 151936]
+
+
+@pytest.mark.parametrize("which", range(4))
+def test_column_splits_match_the_large_batch(which):
+    """At up to 64 rows the forward takes 256- and 128-column workgroups by
+    the head's width and the CU count; at 300 rows it takes the 256-row tile.
+    For a vocabulary in each branch of that split, the first 64 and 37 rows
+    give the same tokens, records, log-sum-exps and logprobs, bit for bit, as
+    inside the 300-row batch, and four rows match the oracle."""
+    import invariant_token_logprobs_amd as rz
+    torch = torch_mod()
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    V = _split_vocabs(ncu)[which]
+    H, N = 128, 300
+    say("column split", which, "V", V, "CUs", ncu)
+    hb, tok = synth.random_rows(N, H, V, "bf16", 1201 + which)
+    W_np = synth.random_lm_head(V, H, "bf16", 1301 + which, scale=0.3)
+    hidden, W = mat_to_dev(hb, "bf16"), mat_to_dev(W_np, "bf16")
+    ids = _ids(N, 1401 + which)
+    t_all, m_all, l_all = _run(hidden, W, ids, SEED)
+    lp_all, ls_all = rz.token_logprobs(hidden, W, vec_to_dev(tok), want_lse=True)
+    torch.cuda.synchronize()
+    lp_all, ls_all = host(lp_all), host(ls_all)
+    bits = lambda x: np.asarray(x, np.float32).view(np.uint32)
+    for n in (64, 37):
+        what = f"V={V} first {n} rows"
+        t_n, m_n, l_n = _run(hidden[:n].contiguous(), W, ids[:n], SEED)
+        assert np.array_equal(t_n, t_all[:n]), what
+        assert np.array_equal(bits(m_n), bits(m_all[:n])), what
+        assert np.array_equal(bits(l_n), bits(l_all[:n])), what
+        lp, ls = rz.token_logprobs(hidden[:n].contiguous(), W, vec_to_dev(tok[:n]),
+                                   want_lse=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(host(lp)), bits(lp_all[:n])), what
+        assert np.array_equal(bits(host(ls)), bits(ls_all[:n])), what
+    h64, W64 = O.to_f64(hb[:4], "bf16"), O.to_f64(W_np, "bf16")
+    _check_tokens(t_all[:4].astype(np.int64), h64, W64, ids[:4], SEED, f"V={V}")
+    logpi_o, _ = O.token_logprobs(h64, W64, tok[:4])
+    t = TOL["bf16"]
+    assert_close(lp_all[:4], logpi_o, t["rtol"], t["atol"], f"V={V} logprobs")
+    del hidden, W
+    torch.cuda.empty_cache()
+
+
 def test_sampler_batch_invariance_qwen3_4b_head():
     """The same 64 reference rows (fixed ids) drawn inside batches of
     1 .. 1100 rows at random slots, at the Qwen3-4B head shape: tokens,
