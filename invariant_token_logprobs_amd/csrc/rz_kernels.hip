@@ -1309,81 +1309,226 @@ __global__ __launch_bounds__(64) void k_lora_cols(T* __restrict__ dst, int64_t l
   dst[row * ld + col0 + j] = j < nsrc ? src[row * ld_src + j] : T(0.f);
 }
 
+// Marks the values as used, in one empty asm: every load that produces them
+// must be complete before it, and none can be moved under a later select's
+// condition.  A fill's loads all go before it, so they are in flight
+// together instead of one round trip each.
+__device__ __forceinline__ void pin8(float* v) {
+  asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]),
+               "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]));
+}
+__device__ __forceinline__ void pin16(float* v) {
+  asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]),
+               "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]),
+               "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]),
+               "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15]));
+}
+
+// Eight consecutive values of a row of T as floats (16-byte loads; p is
+// 16-byte aligned).
+__device__ __forceinline__ void load8_f(const float* p, float (&v)[8]) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    v[k] = a[k];
+    v[4 + k] = b[k];
+  }
+}
+__device__ __forceinline__ void load8_f(const bf16* p, float (&v)[8]) {
+  const bf16x8 a = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) v[k] = (float)a[k];
+}
+
 // dL/dh = dL/dh_aug[:, :H] + s (dL/du) A with dL/du = dL/dh_aug[:, H:]:
-// 64 rows per workgroup, A staged 256 columns at a time, 8 rows per thread
-// in registers; the sum over the rank runs in ascending order.
+// 64 rows per workgroup, A staged 256 columns at a time; each thread holds
+// an 8 x 8 block of outputs (rows 8 (tid / 32) .., columns 8 (tid % 32) ..)
+// in registers, fed per rank index by two 16-byte LDS reads of dL/du and
+// two of A.  Every output's sum over the rank runs in ascending order.
 template <typename T>
-__global__ __launch_bounds__(256) void k_lora_dh(const float* __restrict__ dh_aug,
-                                                 int64_t ld_aug, int H,
-                                                 const T* __restrict__ A, int r,
-                                                 float scale, int64_t n,
-                                                 float* __restrict__ d_hidden) {
-  __shared__ float du[64][kLoraPad];
-  __shared__ float ab[kLoraPad][256];
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_lora_dh(const float* __restrict__ dh_aug, int64_t ld_aug, int H,
+               const T* __restrict__ A, int r, float scale, int64_t n,
+               float* __restrict__ d_hidden) {
+  // 80 KB of LDS and at most 256 VGPRs: two workgroups per CU
+  __shared__ __attribute__((aligned(16))) float duT[kLoraPad][64];     // [j][row]
+  __shared__ __attribute__((aligned(16))) float ab[kLoraPad][256];     // [j][column]
   const int64_t r0 = (int64_t)blockIdx.x * 64;
   const int tid = threadIdx.x;
-  for (int i = tid; i < 64 * kLoraPad; i += 256) {
-    const int t = i / kLoraPad, j = i % kLoraPad;
-    du[t][j] = (r0 + t < n && j < r) ? dh_aug[(r0 + t) * ld_aug + H + j] : 0.f;
+  // All loads of a fill first, from clamped (in-bounds) addresses; then
+  // pin16 (else the compiler moves each load under its select's condition,
+  // a round trip of its own); then the selects.
+  {
+    constexpr int kN = 64 * kLoraPad / 256;
+    float v[kN];
+#pragma unroll
+    for (int k = 0; k < kN; ++k) {
+      const int i = tid + 256 * k;
+      const int t = i / kLoraPad, j = i % kLoraPad;
+      const int64_t row = r0 + t < n ? r0 + t : n - 1;
+      v[k] = dh_aug[row * ld_aug + H + j];
+    }
+    static_assert(kN == 16, "one pin");
+    pin16(v);
+#pragma unroll
+    for (int k = 0; k < kN; ++k) {
+      const int i = tid + 256 * k;
+      const int t = i / kLoraPad, j = i % kLoraPad;
+      duT[j][t] = (r0 + t < n && j < r) ? v[k] : 0.f;
+    }
   }
+  const int rg = tid >> 5, cg = tid & 31;
   for (int hb = 0; hb < H; hb += 256) {
-    const int h = hb + tid;
     __syncthreads();
-    for (int j = 0; j < kLoraPad; ++j)
-      ab[j][tid] = (j < r && h < H) ? load_f(A + (int64_t)j * H + h) : 0.f;
-    __syncthreads();
-    if (h >= H) continue;
-    for (int t0 = 0; t0 < 64; t0 += 8) {
-      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      for (int j = 0; j < kLoraPad; ++j) {
-        const float av = ab[j][tid];
+    {
+      // A[j, hb + 8 c8 .. + 7] for j = tid / 32 + 8 k, c8 = tid % 32: eight
+      // 16-byte-aligned runs of eight values per thread, as the fill above
+      const int c8 = tid & 31, col = hb + 8 * c8;
+      const int cc = col < H ? col : H - 8;  // H % 64 == 0
+      float v[8][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(du[t0 + i][j], av, acc[i]);
+      for (int k = 0; k < 8; ++k) {
+        const int j = (tid >> 5) + 8 * k;
+        load8_f(A + (int64_t)(j < r ? j : r - 1) * H + cc, v[k]);
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int64_t row = r0 + t0 + i;
-        if (row < n)
-          d_hidden[row * H + h] = dh_aug[row * ld_aug + h] + scale * acc[i];
+      for (int k = 0; k < 8; ++k) pin8(v[k]);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int j = (tid >> 5) + 8 * k;
+        const bool ok = j < r && col < H;
+        *reinterpret_cast<f32x4*>(&ab[j][8 * c8]) =
+            ok ? f32x4{v[k][0], v[k][1], v[k][2], v[k][3]} : f32x4{0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<f32x4*>(&ab[j][8 * c8 + 4]) =
+            ok ? f32x4{v[k][4], v[k][5], v[k][6], v[k][7]} : f32x4{0.f, 0.f, 0.f, 0.f};
       }
+    }
+    __syncthreads();
+    const int h = hb + cg * 8;
+    if (h >= H) continue;  // H % 64 == 0: eight columns are all in or all out
+    float acc[8][8];
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[a][c] = 0.f;
+    for (int j = 0; j < kLoraPad; ++j) {
+      float d[8], w[8];
+      load8_f(&duT[j][rg * 8], d);
+      load8_f(&ab[j][cg * 8], w);
+#pragma unroll
+      for (int a = 0; a < 8; ++a)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[a][c] = fmaf(d[a], w[c], acc[a][c]);
+    }
+    float x[8][8];
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+      const int64_t row = r0 + rg * 8 + a < n ? r0 + rg * 8 + a : n - 1;
+      load8_f(dh_aug + row * ld_aug + h, x[a]);
+    }
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+      const int64_t row = r0 + rg * 8 + a;
+      if (row >= n) continue;
+      float* o = d_hidden + row * H + h;
+      *reinterpret_cast<f32x4*>(o) =
+          f32x4{x[a][0] + scale * acc[a][0], x[a][1] + scale * acc[a][1],
+                x[a][2] + scale * acc[a][2], x[a][3] + scale * acc[a][3]};
+      *reinterpret_cast<f32x4*>(o + 4) =
+          f32x4{x[a][4] + scale * acc[a][4], x[a][5] + scale * acc[a][5],
+                x[a][6] + scale * acc[a][6], x[a][7] + scale * acc[a][7]};
     }
   }
 }
 
 // dL/dA partials: part[c][j][h] = sum over the rows of chunk c (ascending)
-// of (dL/du)[t, j] h[t, h]; one column per thread, the rank in registers,
-// dL/du staged 64 rows at a time.
+// of (dL/du)[t, j] h[t, h].  A workgroup takes one chunk and 256 columns;
+// 64 rows of dL/du and of h are staged in LDS at a time (h as floats, by
+// 16-byte loads) and each thread holds an 8 x 8 block of (j, h) sums.
 template <typename T>
 __global__ __launch_bounds__(256) void k_lora_da_partial(
     const float* __restrict__ dh_aug, int64_t ld_aug, int H,
     const T* __restrict__ hidden, int64_t n, int r, float* __restrict__ part) {
-  __shared__ float du[64][kLoraPad];
+  __shared__ __attribute__((aligned(16))) float du[64][kLoraPad];  // [row][j]
+  __shared__ __attribute__((aligned(16))) float hs[64][256];       // [row][column]
+  constexpr int kV = 8;                                            // values per load
   const int c = blockIdx.x;
-  const int h = blockIdx.y * 256 + threadIdx.x;
+  const int hb = blockIdx.y * 256;
+  const int tid = threadIdx.x;
+  const int jg = tid >> 5, cg = tid & 31;
   const int64_t t_begin = (int64_t)c * kLoraChunk;
   const int64_t t_end = t_begin + kLoraChunk < n ? t_begin + kLoraChunk : n;
-  float acc[kLoraPad];
+  float acc[8][8];
 #pragma unroll
-  for (int j = 0; j < kLoraPad; ++j) acc[j] = 0.f;
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int b = 0; b < 8; ++b) acc[a][b] = 0.f;
   for (int64_t t0 = t_begin; t0 < t_end; t0 += 64) {
     __syncthreads();
-    for (int i = threadIdx.x; i < 64 * kLoraPad; i += 256) {
+    // all loads first, from clamped addresses, then the selects (see the
+    // fills of k_lora_dh)
+    constexpr int kND = 64 * kLoraPad / 256, kNH = 64 * (256 / kV) / 256;
+    float vd[kND], vh[kNH][8];
+#pragma unroll
+    for (int k = 0; k < kND; ++k) {
+      const int i = tid + 256 * k;
       const int t = i / kLoraPad, j = i % kLoraPad;
-      du[t][j] = (t0 + t < t_end && j < r) ? dh_aug[(t0 + t) * ld_aug + H + j] : 0.f;
+      const int64_t row = t0 + t < t_end ? t0 + t : t_end - 1;
+      vd[k] = dh_aug[row * ld_aug + H + j];
+    }
+#pragma unroll
+    for (int k = 0; k < kNH; ++k) {
+      const int i = tid + 256 * k;
+      const int t = i / (256 / kV), col = (i % (256 / kV)) * kV;
+      const int64_t row = t0 + t < t_end ? t0 + t : t_end - 1;
+      const int cc = hb + col < H ? hb + col : H - kV;
+      load8_f(hidden + row * H + cc, vh[k]);
+    }
+    static_assert(kND == 16 && kNH == 8, "the pins below");
+    pin16(vd);
+#pragma unroll
+    for (int k = 0; k < kNH; ++k) pin8(vh[k]);
+#pragma unroll
+    for (int k = 0; k < kND; ++k) {
+      const int i = tid + 256 * k;
+      const int t = i / kLoraPad, j = i % kLoraPad;
+      du[t][j] = (t0 + t < t_end && j < r) ? vd[k] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < kNH; ++k) {
+      const int i = tid + 256 * k;
+      const int t = i / (256 / kV), col = (i % (256 / kV)) * kV;
+      // H % 64 == 0: eight columns are all in or all out
+      const bool ok = t0 + t < t_end && hb + col < H;
+      const float* v = vh[k];
+      *reinterpret_cast<f32x4*>(&hs[t][col]) =
+          ok ? f32x4{v[0], v[1], v[2], v[3]} : f32x4{0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4*>(&hs[t][col + 4]) =
+          ok ? f32x4{v[4], v[5], v[6], v[7]} : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     __syncthreads();
-    if (h >= H) continue;
     const int nt = t_end - t0 < 64 ? (int)(t_end - t0) : 64;
     for (int t = 0; t < nt; ++t) {
-      const float hv = load_f(hidden + (t0 + t) * H + h);
+      float d[8], w[8];
+      load8_f(&du[t][jg * 8], d);
+      load8_f(&hs[t][cg * 8], w);
 #pragma unroll
-      for (int j = 0; j < kLoraPad; ++j) acc[j] = fmaf(du[t][j], hv, acc[j]);
+      for (int a = 0; a < 8; ++a)
+#pragma unroll
+        for (int b = 0; b < 8; ++b) acc[a][b] = fmaf(d[a], w[b], acc[a][b]);
     }
   }
+  const int h = hb + cg * 8;
   if (h < H)
 #pragma unroll
-    for (int j = 0; j < kLoraPad; ++j)  // static indices keep acc in registers
-      if (j < r) part[((int64_t)c * r + j) * H + h] = acc[j];
+    for (int a = 0; a < 8; ++a) {
+      const int j = jg * 8 + a;
+      if (j >= r) continue;
+      float* o = part + ((int64_t)c * r + j) * H + h;
+      *reinterpret_cast<f32x4*>(o) = f32x4{acc[a][0], acc[a][1], acc[a][2], acc[a][3]};
+      *reinterpret_cast<f32x4*>(o + 4) = f32x4{acc[a][4], acc[a][5], acc[a][6], acc[a][7]};
+    }
 }
 
 // dL/dA = s * sum of the partials in ascending chunk order
