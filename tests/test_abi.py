@@ -232,10 +232,11 @@ def test_sample_tokens_argument_errors(lib):
     assert smp(lib, ws=NULL, ws_bytes=need) == WORKSPACE
     assert smp(lib, ws_bytes=need - 1) == WORKSPACE
     assert smp(lib, n=0) == OK
-    # two vocab-tile tables (statistics, draw) and the target logits
-    nt = (151936 + 255) // 256
+    # per (row, 128-column statistics tile): the (m, s) partial, the draw
+    # candidate (score, index) and its logit
+    nt = (151936 + 127) // 128
     big = lib.rz_workspace_bytes_op(rz.RZ_OP_SAMPLE, 4096, 1, 2560, 151936, BF16)
-    assert big >= 2 * 8 * nt * 4096 + 4 * 4096
+    assert big >= (8 + 8 + 4) * nt * 4096
 
 
 # ----------------------------------------------------- run-level diagnostics

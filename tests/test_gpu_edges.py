@@ -89,7 +89,7 @@ def test_peaked_softmax_full_parity(dtype):
 
 def test_peaked_softmax_qwen3_4b_head():
     """The same construction at the full Qwen3-4B head (H = 2560,
-    V = 151936, 594 vocab tiles)."""
+    V = 151936, 1187 statistics tiles of 128 columns)."""
     b = _peaked_batch("bf16", 2560, synth.QWEN_VOCAB, 0.3, 43, N_resp=3, lo=60, hi=100,
                       kappa=0.7)
     say("peaked-qwen3-4b", f"N={b.N} valid={b.n_valid}")
