@@ -170,22 +170,27 @@ constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kTwoM32 = 2.3283064365386963e-10f;  // 2^-32
 constexpr float kTwoM33 = 1.1641532182693481e-10f;  // 2^-33
 
-// Gumbel noise g = -ln(-ln u) of u = (x + 1/2) 2^-32.  The largest g come
-// from u near 1, where E = -ln u ~ w = 1 - u.  There, for x >= 2^32 - 2^26
-// (w < 2^-6), E is a short series in w, which is exact from the integer
-// (w = (~x + 1/2) 2^-32); elsewhere E = -ln of u rounded to fp32, whose
-// rounding (at most 2^-25 near 1) moves E by at most 2^-25 / w <= 2^-19
-// relative and g by that much absolutely.  Every lane evaluates both forms
-// and selects (no divergent branches).
-__device__ __forceinline__ float gumbel_of_bits(uint32_t x) {
+// The draw's score of logit z with Gumbel noise g = -ln(-ln u), u =
+// (x + 1/2) 2^-32, up to one constant: z + g + ln(ln 2) = z - ln(E2) with
+// E2 = -log2 u, so a single log2 forms E2 and the constant ln(ln 2), the
+// same for every column, never changes a comparison.  The largest g come
+// from u near 1, where E2 ~ w / ln 2, w = 1 - u.  There, for
+// x >= 2^32 - 2^26 (w < 2^-6), E2 is a three-term series in w, which is
+// exact from the integer (w = (~x + 1/2) 2^-32) and truncated at w^4 / 4
+// (<= 2^-20 relative); elsewhere E2 = -log2 of u rounded to fp32, whose
+// rounding (at most 2^-25 near 1) moves E2 by at most 2^-25 / w <= 2^-19
+// relative.  Either way the score moves by at most 2^-19.  Every lane
+// evaluates both forms and selects (no divergent branches).
+__device__ __forceinline__ float draw_score(float z, uint32_t x) {
   // (x + 1/2) 2^-32 as one fma: the scaling by a power of two is exact, so
   // this rounds once, as (float(x) + 1/2) then * 2^-32 does
   const float u = __builtin_fmaf((float)x, kTwoM32, kTwoM33);
   const float w = __builtin_fmaf((float)(~x), kTwoM32, kTwoM33);  // 1 - u
-  const float L = -__builtin_amdgcn_logf(u) * kLn2;
-  const float series = w * (1.f + w * (0.5f + w * (1.f / 3.f + w * (0.25f + w * 0.2f))));
-  const float E = x < 0xFC000000u ? L : series;
-  return -__builtin_amdgcn_logf(E) * kLn2;
+  const float L = -__builtin_amdgcn_logf(u);
+  // -log2(1 - w) = (w / ln 2) (1 + w / 2 + w^2 / 3 + ...)
+  const float series = w * (kLog2e + w * (0.5f * kLog2e + w * (kLog2e / 3.f)));
+  const float E2 = x < 0xFC000000u ? L : series;
+  return __builtin_fmaf(__builtin_amdgcn_logf(E2), -kLn2, z);
 }
 
 // (score, index) order of the draw: larger score first, then smaller index
@@ -416,9 +421,9 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
   }
   if constexpr (kSample) {
     // The draw: per row, the best z + g over the statistics tile's columns
-    // < V (see gumbel_of_bits; counter (v / 4, id_lo, id_hi, 0), key =
-    // the seed, word v % 4), under draw_better's total order, so the order
-    // in which lanes meet does not matter; one candidate per statistics tile.
+    // < V (see draw_score; counter (v / 4, id_lo, id_hi, 0), key = the seed,
+    // word v % 4), under draw_better's total order, so the order in which
+    // lanes meet does not matter; one candidate per statistics tile.
     const uint32_t k0 = (uint32_t)a.seed, k1 = (uint32_t)(a.seed >> 32);
     static_for<0, TM>([&](auto mi_c) {
       constexpr int mi = decltype(mi_c)::value;
@@ -426,7 +431,7 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
       const int R = wm * RW + mi * 32 + l32;
       const uint64_t id = m0 + R < M ? a.row_ids[rc.base + m0 + R] : 0;
       float bs = -__builtin_inff();
-      int bv = 0x7fffffff;
+      int bo = -1;     // the best column's offset from cbase (-1: none)
       float bz = 0.f;  // the best column's logit: the record's z[a_t]
       // block ni of the lane: its four runs q = 0..3 of four columns, the
       // four Philox blocks computed together
@@ -439,18 +444,22 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
                        (uint32_t)(id >> 32), 0u};
         philox4x32_10_x4(x, k0, k1);
         // a lane meets its columns in increasing order, so a strict > keeps
-        // the smallest index among equal scores (draw_better's order)
+        // the smallest index among equal scores (draw_better's order); the
+        // winner's column is kept as its offset from cbase, a constant per
+        // register (columns >= V, offset >= lim, never win)
+        const int lim = a.V - cbase;
         static_for<0, 16>([&](auto qj_c) {
           constexpr int q = decltype(qj_c)::value / 4, j = decltype(qj_c)::value % 4;
-          const int v = cbase + ni * 32 + 8 * q + j;
+          constexpr int off = ni * 32 + 8 * q + j;
           const float z = acc[mi][ni][4 * q + j];
-          const float sc = z + gumbel_of_bits(x[q][j]);
-          const bool take = sc > bs && v < a.V;  // columns >= V never win
+          const float sc = draw_score(z, x[q][j]);
+          const bool take = sc > bs && off < lim;
           bs = take ? sc : bs;
-          bv = take ? v : bv;
+          bo = take ? off : bo;
           bz = take ? z : bz;
         });
       });
+      int bv = bo < 0 ? 0x7fffffff : cbase + bo;
       const float os = __shfl_xor(bs, 32, 64);
       const int ov = __shfl_xor(bv, 32, 64);
       const float oz = __shfl_xor(bz, 32, 64);
