@@ -41,13 +41,13 @@ GEMM_KERNELS = ("fwd_logits_gemm", "bwd_dh_gemm", "bwd_dw_gemm")
 # kernel sources they were taken from.
 COUNTER_TRAFFIC = {
     "workload": "qwen3_4b_tool",
-    "sources_sha256": "ab6baccdd872849885f647fc4c26095632a2efbc594625d91743d0780573d314",
+    "sources_sha256": "3a005d242dcb560f182ffb037ac5884b76484de628c8612aca4aa04e0f0210ca",
     # per timed launch: a GEMM with its last-round K pieces and their sum
-    "bytes_per_launch": {"fwd_logits_gemm": 26475154995,
-                         "bwd_dh_gemm": 24712247052,
-                         "bwd_dw_gemm": 29232709344,
-                         "grad_norm": 2291984403,
-                         "mx_dequant_mxfp4": 984655106},
+    "bytes_per_launch": {"fwd_logits_gemm": 27011322287,
+                         "bwd_dh_gemm": 24784281054,
+                         "bwd_dw_gemm": 29184592492,
+                         "grad_norm": 2291984798,
+                         "mx_dequant_mxfp4": 984640510},
 }
 
 
@@ -56,9 +56,9 @@ COUNTER_TRAFFIC = {
 # GEMMs, from the counter run of profiles/mfma_utilisation_qwen3_4b_tool.md,
 # over the launches that hold rows; same validity rule as COUNTER_TRAFFIC.
 COUNTER_MFMA = {
-    "fwd_logits_gemm": {"mfma_busy": 0.567, "clock_ghz": 1.856},
-    "bwd_dh_gemm": {"mfma_busy": 0.602, "clock_ghz": 1.794},
-    "bwd_dw_gemm": {"mfma_busy": 0.573, "clock_ghz": 1.816},
+    "fwd_logits_gemm": {"mfma_busy": 0.562, "clock_ghz": 1.864},
+    "bwd_dh_gemm": {"mfma_busy": 0.613, "clock_ghz": 1.774},
+    "bwd_dw_gemm": {"mfma_busy": 0.569, "clock_ghz": 1.823},
 }
 
 
