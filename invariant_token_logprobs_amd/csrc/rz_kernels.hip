@@ -2197,12 +2197,20 @@ __global__ __launch_bounds__(256) void k_dw_fix(
     for (int j = 0; j < kVec; ++j) acc[j] = 0.f;
     int start = 0;
     for (int j0 = 0; j0 < cnt; j0 += kFixBatch) {
-      // loads of kFixBatch rows first, then the ordered accumulation
+      // loads of kFixBatch rows first, with each row's token row of dW (a
+      // token's run ends in this piece at most once, and nothing else here
+      // writes that row before its run ends), then the ordered accumulation
       u32x4 x[kFixBatch];
+      f32x4 y[kFixBatch][kVec / 4];
 #pragma unroll
       for (int b = 0; b < kFixBatch; ++b)
-        if (j0 + b < cnt)
+        if (j0 + b < cnt) {
           x[b] = *reinterpret_cast<const u32x4*>(hidden + (int64_t)srow[j0 + b] * ld + col);
+          const int v = sk[j0 + b];
+          const float* o = dw + (int64_t)(v < V ? v : 0) * H + col;
+#pragma unroll
+          for (int w = 0; w < kVec / 4; ++w) y[b][w] = *reinterpret_cast<const f32x4*>(o + 4 * w);
+        }
 #pragma unroll
       for (int b = 0; b < kFixBatch; ++b) {
         const int j = j0 + b;
@@ -2240,11 +2248,9 @@ __global__ __launch_bounds__(256) void k_dw_fix(
           } else {
             float* o = dw + (int64_t)v * H + col;
 #pragma unroll
-            for (int w = 0; w < kVec; w += 4) {
-              f32x4 y = *reinterpret_cast<const f32x4*>(o + w);
-              y -= f32x4{acc[w], acc[w + 1], acc[w + 2], acc[w + 3]};
-              *reinterpret_cast<f32x4*>(o + w) = y;
-            }
+            for (int w = 0; w < kVec; w += 4)
+              *reinterpret_cast<f32x4*>(o + w) =
+                  y[b][w / 4] - f32x4{acc[w], acc[w + 1], acc[w + 2], acc[w + 3]};
           }
         }
 #pragma unroll
