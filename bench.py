@@ -41,13 +41,13 @@ GEMM_KERNELS = ("fwd_logits_gemm", "bwd_dh_gemm", "bwd_dw_gemm")
 # kernel sources they were taken from.
 COUNTER_TRAFFIC = {
     "workload": "qwen3_4b_tool",
-    "sources_sha256": "3a005d242dcb560f182ffb037ac5884b76484de628c8612aca4aa04e0f0210ca",
+    "sources_sha256": "87e5155cff577bf7fa0d19bed54cf8ccbb97c20fb1477d12cc61c64a546e4dd5",
     # per timed launch: a GEMM with its last-round K pieces and their sum
-    "bytes_per_launch": {"fwd_logits_gemm": 27011322287,
-                         "bwd_dh_gemm": 24784281054,
-                         "bwd_dw_gemm": 29184592492,
-                         "grad_norm": 2291984798,
-                         "mx_dequant_mxfp4": 984640510},
+    "bytes_per_launch": {"fwd_logits_gemm": 27259645679,
+                         "bwd_dh_gemm": 24643787515,
+                         "bwd_dw_gemm": 28682092348,
+                         "grad_norm": 2291984417,
+                         "mx_dequant_mxfp4": 984637807},
 }
 
 
@@ -56,9 +56,9 @@ COUNTER_TRAFFIC = {
 # GEMMs, from the counter run of profiles/mfma_utilisation_qwen3_4b_tool.md,
 # over the launches that hold rows; same validity rule as COUNTER_TRAFFIC.
 COUNTER_MFMA = {
-    "fwd_logits_gemm": {"mfma_busy": 0.562, "clock_ghz": 1.864},
-    "bwd_dh_gemm": {"mfma_busy": 0.613, "clock_ghz": 1.774},
-    "bwd_dw_gemm": {"mfma_busy": 0.569, "clock_ghz": 1.823},
+    "fwd_logits_gemm": {"mfma_busy": 0.565, "clock_ghz": 1.880},
+    "bwd_dh_gemm": {"mfma_busy": 0.613, "clock_ghz": 1.801},
+    "bwd_dw_gemm": {"mfma_busy": 0.569, "clock_ghz": 1.850},
 }
 
 
