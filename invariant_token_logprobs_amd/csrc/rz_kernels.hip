@@ -201,7 +201,8 @@ __device__ __forceinline__ bool draw_better(float s, int v, float bs, int bv) {
 // bi_lmhead_gemm + the log-softmax statistics of a logits tile: per row t
 // and statistics tile j (128 vocabulary columns, one wave's column half),
 // m_j = max_v z[t, v] and s_j = sum_v exp(z[t, v] - m_j), written to
-// partials[j][t]; on the learner call also e for the backward (see EStore).
+// partials[j ldp + t ldr]; on the learner call also e for the backward (see
+// EStore).
 //
 // The MFMAs run with swapped operands (see gemm_mainloop), so each lane
 // holds one row t and, per 32 x 32 block, four runs of four consecutive
@@ -1777,11 +1778,14 @@ __device__ __forceinline__ void park_tile(float* part, int q,
   }
 }
 
-// the pieces q0 .. q0 + n - 1 summed in order
+// the pieces q0 .. q0 + n - 1 summed in order (only the accumulators of
+// block row mi_only when it is >= 0)
 __device__ __forceinline__ void sum_parked(float* part, int q0, int n,
-                                           f32x16 (&acc)[kTM][kTN]) {
+                                           f32x16 (&acc)[kTM][kTN],
+                                           int mi_only = -1) {
 #pragma unroll
   for (int c = 0; c < 4 * kTM * kTN; ++c) {
+    if (mi_only >= 0 && c / 16 != mi_only) continue;
     f32x4 v = *part_chunk(part, q0, c);
     for (int p = 1; p < n; ++p) v += *part_chunk(part, q0 + p, c);
     f32x16& blk = acc[c / 16][(c / 4) % 4];
@@ -1957,7 +1961,8 @@ struct DwArgs {
 // dW (+)= acc for one tile: rows v (vocabulary), columns h (hidden); the
 // first chunk overwrites.
 __device__ __forceinline__ void dw_store(const DwArgs& a, int m0, int n0,
-                                         f32x16 (&acc)[kTM][kTN]) {
+                                         f32x16 (&acc)[kTM][kTN],
+                                         int mi_only = -1) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
   const int unscale = a.sigma ? -*a.sigma : 0;
@@ -1965,6 +1970,7 @@ __device__ __forceinline__ void dw_store(const DwArgs& a, int m0, int n0,
   for (int mi = 0; mi < kTM; ++mi)
 #pragma unroll
     for (int ni = 0; ni < kTN; ++ni) {
+      if (mi_only >= 0 && mi != mi_only) continue;
       // one 32 x 32 block at a time keeps the in-flight loads bounded
       __builtin_amdgcn_sched_barrier(0);
       const int h = n0 + acc_col(wn, ni, lane);
@@ -2022,15 +2028,17 @@ __global__ RZ_GEMM_ATTR void k_bwd_dw(DwArgs a) {
 
 // The last round's tiles: the pieces summed in piece order (a fixed order,
 // so dW stays run-to-run deterministic), then stored like any other tile.
+// kTM workgroups per last-round tile, one per block row mi of every wave:
+// the same sums and stores, spread over four times the CUs.
 __global__ __launch_bounds__(256) void k_dw_tail(DwArgs a) {
   const int K = to_rc(a.krows).get();
   const int nk = (K + a.kstage - 1) / a.kstage;
   if (nk == 0 && !a.first) return;
-  const int i = blockIdx.x;
+  const int i = blockIdx.x / kTM, mi = blockIdx.x % kTM;
   const TileCoord tc = map_tile(a.T - a.tail + i, a.T, a.mt, a.nt);
   f32x16 acc[kTM][kTN];
-  sum_parked(a.part, i * a.split, a.split, acc);
-  dw_store(a, tc.tm * kBM, tc.tn * kBN, acc);
+  sum_parked(a.part, i * a.split, a.split, acc, mi);
+  dw_store(a, tc.tm * kBM, tc.tn * kBN, acc, mi);
 }
 
 // ===================================================================
@@ -2933,7 +2941,7 @@ hipError_t launch_bwd_dw(int dt, const void* dz, int64_t ld, DevRows krows,
     const int grid = a.T - a.tail + a.tail * a.split;
     if (dt) k_bwd_dw<bf16><<<grid, kThreads, 0, s>>>(a);
     else k_bwd_dw<float><<<grid, kThreads, 0, s>>>(a);
-    if (a.tail) k_dw_tail<<<a.tail, kThreads, 0, s>>>(a);
+    if (a.tail) k_dw_tail<<<a.tail * kTM, kThreads, 0, s>>>(a);
   });
 }
 
