@@ -1826,7 +1826,8 @@ struct DhArgs {
 template <typename T>
 __device__ __forceinline__ void dh_epilogue(const DhArgs<T>& a, const RowCount& rc,
                                             int M, int m0, int n0,
-                                            f32x16 (&acc)[kTM][kTN], char* lds) {
+                                            f32x16 (&acc)[kTM][kTN], char* lds,
+                                            int mi_only = -1) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
   int* sidx = reinterpret_cast<int*>(lds);
@@ -1854,6 +1855,7 @@ __device__ __forceinline__ void dh_epilogue(const DhArgs<T>& a, const RowCount& 
     for (int mi = 0; mi < kTM; ++mi)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
+        if (mi_only >= 0 && mi != mi_only) continue;
         const int row = acc_row(wm, mi, r, lane);
         const float c = src[row], g = srg[row];
 #pragma unroll
@@ -1865,6 +1867,7 @@ __device__ __forceinline__ void dh_epilogue(const DhArgs<T>& a, const RowCount& 
   for (int mi = 0; mi < kTM; ++mi)
 #pragma unroll
     for (int ni = 0; ni < kTN; ++ni) {
+      if (mi_only >= 0 && mi != mi_only) continue;
       const int h = n0 + acc_col(wn, ni, lane);
       if (h >= a.H) continue;
 #pragma unroll
@@ -1920,7 +1923,7 @@ __global__ RZ_GEMM_ATTR void k_bwd_dh(DhArgs<T> a) {
 }
 
 // The last round's tiles: their pieces summed in piece order, then the same
-// epilogue.  One workgroup per tail tile (kSplitWGs launched at most).
+// epilogue.  kTM workgroups per tail tile (kSplitWGs tiles at most).
 template <typename T>
 __global__ __launch_bounds__(256) void k_dh_tail(DhArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char lds[5 * 256 * 4];
@@ -1929,12 +1932,13 @@ __global__ __launch_bounds__(256) void k_dh_tail(DhArgs<T> a) {
   const int mt = (M + kBM - 1) / kBM;
   const int ntile = mt * a.nt;
   const RoundSplit sp = round_split(ntile, a.ncu);
-  const int i = blockIdx.x;
+  // kTM workgroups per tail tile, one per block row mi of every wave
+  const int i = blockIdx.x / kTM, mi = blockIdx.x % kTM;
   if (i >= sp.tail) return;
   const TileCoord tc = map_tile(ntile - sp.tail + i, ntile, mt, a.nt);
   f32x16 acc[kTM][kTN];
-  sum_parked(a.part, i * sp.split, sp.split, acc);
-  dh_epilogue(a, rc, M, tc.tm * kBM, tc.tn * kBN, acc, lds);
+  sum_parked(a.part, i * sp.split, sp.split, acc, mi);
+  dh_epilogue(a, rc, M, tc.tm * kBM, tc.tn * kBN, acc, lds, mi);
 }
 
 // ===================================================================
@@ -2880,7 +2884,7 @@ static hipError_t launch_bwd_dh_t(const void* dz, int64_t ldz, DevRows rows,
     k_bwd_dh<T, false><<<a.mt * a.nt, kThreads, 0, s>>>(a);
     if (part) {
       k_bwd_dh<T, true><<<kSplitWGs, kThreads, 0, s>>>(a);
-      k_dh_tail<T><<<kSplitWGs, kThreads, 0, s>>>(a);
+      k_dh_tail<T><<<kSplitWGs * kTM, kThreads, 0, s>>>(a);
     }
   });
 }
