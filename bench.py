@@ -41,13 +41,13 @@ GEMM_KERNELS = ("fwd_logits_gemm", "bwd_dh_gemm", "bwd_dw_gemm")
 # kernel sources they were taken from.
 COUNTER_TRAFFIC = {
     "workload": "qwen3_4b_tool",
-    "sources_sha256": "87e5155cff577bf7fa0d19bed54cf8ccbb97c20fb1477d12cc61c64a546e4dd5",
+    "sources_sha256": "1193572fd0328b1956705ddca1259e0c957a727e04f2113ef8ed223b8082435e",
     # per timed launch: a GEMM with its last-round K pieces and their sum
-    "bytes_per_launch": {"fwd_logits_gemm": 27259645679,
-                         "bwd_dh_gemm": 24643787515,
-                         "bwd_dw_gemm": 28682092348,
-                         "grad_norm": 2291984417,
-                         "mx_dequant_mxfp4": 984637807},
+    "bytes_per_launch": {"fwd_logits_gemm": 26397848480,
+                         "bwd_dh_gemm": 24663784696,
+                         "bwd_dw_gemm": 29358057179,
+                         "grad_norm": 2291985081,
+                         "mx_dequant_mxfp4": 984655505},
 }
 
 
@@ -56,9 +56,9 @@ COUNTER_TRAFFIC = {
 # GEMMs, from the counter run of profiles/mfma_utilisation_qwen3_4b_tool.md,
 # over the launches that hold rows; same validity rule as COUNTER_TRAFFIC.
 COUNTER_MFMA = {
-    "fwd_logits_gemm": {"mfma_busy": 0.565, "clock_ghz": 1.880},
-    "bwd_dh_gemm": {"mfma_busy": 0.613, "clock_ghz": 1.801},
-    "bwd_dw_gemm": {"mfma_busy": 0.569, "clock_ghz": 1.850},
+    "fwd_logits_gemm": {"mfma_busy": 0.563, "clock_ghz": 1.839},
+    "bwd_dh_gemm": {"mfma_busy": 0.619, "clock_ghz": 1.755},
+    "bwd_dw_gemm": {"mfma_busy": 0.575, "clock_ghz": 1.798},
 }
 
 
