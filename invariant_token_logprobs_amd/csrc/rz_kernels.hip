@@ -435,31 +435,37 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
       int bo = -1;     // the best column's offset from cbase (-1: none)
       float bz = 0.f;  // the best column's logit: the record's z[a_t]
       // block ni of the lane: its four runs q = 0..3 of four columns, the
-      // four Philox blocks computed together
-      static_for<0, kTN>([&](auto ni_c) {
-        constexpr int ni = decltype(ni_c)::value;
-        u32x4 x[4];
+      // four Philox blocks computed together.  A lane meets its columns in
+      // increasing order, so a strict > keeps the smallest index among equal
+      // scores (draw_better's order); the winner's column is kept as its
+      // offset from cbase, a constant per register.  Columns >= V (offset >=
+      // lim, in the last statistics tile only) never win; the other tiles
+      // take a copy of the loop without that test.
+      const int lim = a.V - cbase;
+      auto scan = [&](auto all_c) {
+        constexpr bool kAll = decltype(all_c)::value;  // every column < V
+        static_for<0, kTN>([&](auto ni_c) {
+          constexpr int ni = decltype(ni_c)::value;
+          u32x4 x[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          x[q] = u32x4{(uint32_t)(cbase + ni * 32 + 8 * q) >> 2, (uint32_t)id,
-                       (uint32_t)(id >> 32), 0u};
-        philox4x32_10_x4(x, k0, k1);
-        // a lane meets its columns in increasing order, so a strict > keeps
-        // the smallest index among equal scores (draw_better's order); the
-        // winner's column is kept as its offset from cbase, a constant per
-        // register (columns >= V, offset >= lim, never win)
-        const int lim = a.V - cbase;
-        static_for<0, 16>([&](auto qj_c) {
-          constexpr int q = decltype(qj_c)::value / 4, j = decltype(qj_c)::value % 4;
-          constexpr int off = ni * 32 + 8 * q + j;
-          const float z = acc[mi][ni][4 * q + j];
-          const float sc = draw_score(z, x[q][j]);
-          const bool take = sc > bs && off < lim;
-          bs = take ? sc : bs;
-          bo = take ? off : bo;
-          bz = take ? z : bz;
+          for (int q = 0; q < 4; ++q)
+            x[q] = u32x4{(uint32_t)(cbase + ni * 32 + 8 * q) >> 2, (uint32_t)id,
+                         (uint32_t)(id >> 32), 0u};
+          philox4x32_10_x4(x, k0, k1);
+          static_for<0, 16>([&](auto qj_c) {
+            constexpr int q = decltype(qj_c)::value / 4, j = decltype(qj_c)::value % 4;
+            constexpr int off = ni * 32 + 8 * q + j;
+            const float z = acc[mi][ni][4 * q + j];
+            const float sc = draw_score(z, x[q][j]);
+            const bool take = kAll ? sc > bs : (sc > bs && off < lim);
+            bs = take ? sc : bs;
+            bo = take ? off : bo;
+            bz = take ? z : bz;
+          });
         });
-      });
+      };
+      if (n0 + wn * 128 + 128 <= a.V) scan(BoolC<true>{});
+      else scan(BoolC<false>{});
       int bv = bo < 0 ? 0x7fffffff : cbase + bo;
       const float os = __shfl_xor(bs, 32, 64);
       const int ov = __shfl_xor(bv, 32, 64);
