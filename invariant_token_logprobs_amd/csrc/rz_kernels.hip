@@ -160,8 +160,11 @@ __device__ __forceinline__ void philox4x32_10_x4(u32x4 (&c)[4], uint32_t k0,
     for (int i = 0; i < 4; ++i) {
       const uint64_t p0 = (uint64_t)c[i][0] * 0xD2511F53u;
       const uint64_t p1 = (uint64_t)c[i][2] * 0xCD9E8D57u;
-      c[i] = u32x4{(uint32_t)(p1 >> 32) ^ c[i][1] ^ k0, (uint32_t)p1,
-                   (uint32_t)(p0 >> 32) ^ c[i][3] ^ k1, (uint32_t)p0};
+      // a ^ b ^ c in one v_bitop3_b32 (truth table 0x96)
+      c[i] = u32x4{(uint32_t)__builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c[i][1], k0, 0x96),
+                   (uint32_t)p1,
+                   (uint32_t)__builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c[i][3], k1, 0x96),
+                   (uint32_t)p0};
     }
   }
 }
