@@ -206,7 +206,7 @@ def test_sampler_batch_invariance_qwen3_4b_head():
     W = mat_to_dev(W_np, "bf16")
     ref_ids = _ids(64, 903)
     ref_tok = ref_lmu = ref_lse = None
-    for n in (64, 1, 7, 300, 1100):
+    for n in (64, 1, 7, 300, 1024, 1100):
         if n < 64:
             sel = rng.choice(64, size=n, replace=False)
             hb, ib, slots = ref_h[sel], ref_ids[sel], np.arange(n)
