@@ -41,13 +41,13 @@ GEMM_KERNELS = ("fwd_logits_gemm", "bwd_dh_gemm", "bwd_dw_gemm")
 # kernel sources they were taken from.
 COUNTER_TRAFFIC = {
     "workload": "qwen3_4b_tool",
-    "sources_sha256": "1193572fd0328b1956705ddca1259e0c957a727e04f2113ef8ed223b8082435e",
+    "sources_sha256": "302578bbdc394b62bec27ab218874438635cde533b92d53949c15376d78999b3",
     # per timed launch: a GEMM with its last-round K pieces and their sum
-    "bytes_per_launch": {"fwd_logits_gemm": 26397848480,
-                         "bwd_dh_gemm": 24663784696,
-                         "bwd_dw_gemm": 29358057179,
-                         "grad_norm": 2291985081,
-                         "mx_dequant_mxfp4": 984655505},
+    "bytes_per_launch": {"fwd_logits_gemm": 26561835351,
+                         "bwd_dh_gemm": 24553273455,
+                         "bwd_dw_gemm": 29189319307,
+                         "grad_norm": 2291983996,
+                         "mx_dequant_mxfp4": 984650700},
 }
 
 
@@ -56,9 +56,9 @@ COUNTER_TRAFFIC = {
 # GEMMs, from the counter run of profiles/mfma_utilisation_qwen3_4b_tool.md,
 # over the launches that hold rows; same validity rule as COUNTER_TRAFFIC.
 COUNTER_MFMA = {
-    "fwd_logits_gemm": {"mfma_busy": 0.563, "clock_ghz": 1.839},
-    "bwd_dh_gemm": {"mfma_busy": 0.619, "clock_ghz": 1.755},
-    "bwd_dw_gemm": {"mfma_busy": 0.575, "clock_ghz": 1.798},
+    "fwd_logits_gemm": {"mfma_busy": 0.568, "clock_ghz": 1.847},
+    "bwd_dh_gemm": {"mfma_busy": 0.618, "clock_ghz": 1.756},
+    "bwd_dw_gemm": {"mfma_busy": 0.571, "clock_ghz": 1.820},
 }
 
 
