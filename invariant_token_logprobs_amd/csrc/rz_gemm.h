@@ -366,6 +366,136 @@ __device__ __forceinline__ void gemm_mainloop(const GemmOperands& op, int M,
 #undef RZ_SB
 }
 
+// The 256 x 256 tile on eight waves, two per SIMD: wave w owns rows
+// 64 (w % 4) .. + 63 (two 32-row blocks) of column half w / 4 (four
+// 32-column blocks), so each wave holds half the accumulators of
+// gemm_mainloop's and issues half its MFMAs; while one wave of a SIMD waits
+// on its LDS reads, loads or a barrier, the other can issue.  Same stage
+// layout, swizzle and K steps as gemm_mainloop<T, true>, and each 32 x 32
+// block sees the same MFMA (swapped operands) on the same fragments in the
+// same K order, so its accumulators are bit-identical to that tile's.  Each
+// wave fills 32 rows of each operand per stage (four loads each).  Needs
+// 512 threads.  Leaves the LDS free on return.
+template <typename T>
+__device__ __forceinline__ void gemm_mainloop_w8(const GemmOperands& op, int M,
+                                                 int m0, int n0, int nk,
+                                                 f32x16 (&acc)[2][kTN],
+                                                 char* lds) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wid = tid >> 6;
+  const int wrow = (wid & 3) * 64, wcol = (wid >> 2) * 128;
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < kTN; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+  if (nk <= 0) return;
+
+  int a_off[2], b_off[kTN];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+    a_off[mi] = (wrow + mi * 32 + (lane & 31)) * kRowBytes;
+#pragma unroll
+  for (int ni = 0; ni < kTN; ++ni)
+    b_off[ni] = (wcol + ni * 32 + (lane & 31)) * kRowBytes;
+  int c_off[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    c_off[s] = ((2 * s + (lane >> 5)) ^ swz(lane & 31)) << 4;
+
+  typedef __attribute__((address_space(3))) void* lds_ptr_t;
+  const int wu = __builtin_amdgcn_readfirstlane(wid);
+  const char* ga[4];
+  const char* gb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = wu * 32 + 8 * i + (lane >> 3);
+    const int c = (lane & 7) ^ swz(r);
+    int m = m0 + r;
+    m = m < M ? m : M - 1;
+    const int64_t prow = op.a_rows ? (int64_t)op.a_rows[op.a_base + m]
+                                   : op.a_base + m;
+    ga[i] = op.A + prow * op.lda + c * 16;
+    int n = n0 + r;
+    n = n < op.N ? n : op.N - 1;
+    gb[i] = op.B + (int64_t)n * op.ldb + c * 16;
+  }
+  // load j of a stage: j < 4 fills A rows 32 wu + 8 j .. + 7, j >= 4 the
+  // same rows of B
+  auto dma1 = [&](int kt, int stage, int j) {
+    const int64_t k = (int64_t)kt * kRowBytes;
+    char* st = lds + stage * kStageBytes + (wu * 32 + (j & 3) * 8) * kRowBytes;
+    if (j < 4)
+      __builtin_amdgcn_global_load_lds(ga[j] + k, (lds_ptr_t)st, 16, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds(gb[j - 4] + k,
+                                       (lds_ptr_t)(st + kOperandBytes), 16, 0, 0);
+  };
+  u32x4 fa[2][2], fb[2][kTN];
+  auto lread = [&](int buf, int stage, int s) {
+    const char* sa = lds + stage * kStageBytes;
+    const char* sb = sa + kOperandBytes;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+      fa[buf][mi] = *reinterpret_cast<const u32x4*>(sa + a_off[mi] + c_off[s]);
+#pragma unroll
+    for (int ni = 0; ni < kTN; ++ni)
+      fb[buf][ni] = *reinterpret_cast<const u32x4*>(sb + b_off[ni] + c_off[s]);
+  };
+  // block q = 4 mi + ni of one K step (swapped operands)
+  auto mm1 = [&](int buf, int q) {
+    mfma_step(acc[q / kTN][q % kTN], fb[buf][q % kTN], fa[buf][q / kTN],
+              (const T*)nullptr);
+  };
+  auto mmr = [&](int buf, int lo, int hi) {
+#pragma unroll
+    for (int q = lo; q < hi; ++q) mm1(buf, q);
+  };
+  // gemm_mainloop's schedule with 8 MFMAs per K step and 8 loads per
+  // stage: stage kt + 1's loads 0 .. 3 go out after the barrier that frees
+  // its buffer, 4 .. 7 in the first phase of stage kt.
+#define RZ_SB() __builtin_amdgcn_sched_barrier(0)
+#pragma unroll
+  for (int j = 0; j < 8; ++j) dma1(0, 0, j);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (nk > 1) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dma1(1, 1, j);
+  }
+  lread(0, 0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    const bool nx = kt + 1 < nk, nx2 = kt + 2 < nk;
+    RZ_SB(); mm1(0, 0); RZ_SB(); lread(1, cur, 1); RZ_SB();
+#pragma unroll
+    for (int q = 1; q < 8; ++q) {
+      mm1(0, q);
+      RZ_SB();
+      if (q <= 4 && nx) dma1(kt + 1, cur ^ 1, 3 + q);
+      RZ_SB();
+    }
+    mm1(1, 0); RZ_SB(); lread(0, cur, 2); RZ_SB(); mmr(1, 1, 8); RZ_SB();
+    mm1(0, 0); RZ_SB(); lread(1, cur, 3); RZ_SB(); mmr(0, 1, 8); RZ_SB();
+    mmr(1, 0, 4);
+    RZ_SB();
+    if (nx) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    RZ_SB();
+    if (nx) lread(0, cur ^ 1, 0);
+    RZ_SB();
+#pragma unroll
+    for (int q = 4; q < 8; ++q) {
+      mm1(1, q);
+      RZ_SB();
+      if (nx2) dma1(kt + 2, cur, q - 4);
+      RZ_SB();
+    }
+  }
+#undef RZ_SB
+}
+
 // The 64-row tile for small row counts (the rollout at decode size): each
 // wave owns one 32-row block (wm) and the four 32-column blocks of its column
 // half (wn), and issues each MFMA with swapped operands on fragments taken

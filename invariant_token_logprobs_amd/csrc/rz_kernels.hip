@@ -217,8 +217,11 @@ __device__ __forceinline__ bool draw_better(float s, int v, float bs, int bv) {
 // taken first over the statistics tile; one exp per element then serves
 // both s_j and e.
 //
-// TM = 32-row blocks per wave along M: kTM (the 256-row tile) or 1 (the
-// 64-row tiles for small row counts).  The single-stage 64-row form
+// kW8: the 256-row tile on eight waves (gemm_mainloop_w8; TM = 2 32-row
+// blocks per wave, wave w owning rows 64 (w % 4) .. + 63 of column half
+// w / 4); else the 64-row tiles for small row counts (TM = 1, four waves,
+// wave w owning rows 32 (w / 2) .. + 31 of column half w % 2).  The
+// single-stage 64-row form
 // (kStages64 = 1, one row block) takes 256 columns in workgroups
 // [0, nfull) and 128 columns (one statistics tile; the column-half-1 waves
 // idle) in the rest, so that the head's columns spread evenly over the CUs
@@ -230,11 +233,13 @@ __device__ __forceinline__ bool draw_better(float s, int v, float bs, int bv) {
 // kTokOff: byte offset in lds of the tile's row tokens for the gather
 // (-1: none; the gather then reads them from global memory).
 template <typename T, bool kStoreE, bool kSample, int TM, int kWFmt = -1,
-          int kStages64 = 2, int kTokOff = -1>
+          int kStages64 = 2, int kTokOff = -1, bool kW8 = false>
 __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
-  static_assert(TM == kTM || (TM == 1 && !kStoreE), "64-row tile: no e output");
+  static_assert(kW8 ? TM == 2 : (TM == 1 && !kStoreE),
+                "the 256-row tile: eight waves; the 64-row tiles: no e output");
+  constexpr int NT = kW8 ? 2 * kThreads : kThreads;  // threads per workgroup
   constexpr bool kMixed = TM == 1 && kStages64 == 1 && kWFmt < 0;
-  constexpr int BM = 64 * TM;       // tile rows
+  constexpr int BM = kW8 ? kBM : 64 * TM;  // tile rows
   constexpr int RW = 32 * TM;       // rows per wave
   const RowCount rc = to_rc(a.rows);
   const int M = rc.get();
@@ -260,13 +265,13 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
   }
 
   // The 256-row tile's row tokens for the gather, brought into LDS (stok,
-  // outside the stage buffers) by one 4-byte DMA load per lane before the
-  // main loop: the main loop's stage waits and barriers complete it, so the
-  // epilogue reads them without waiting on global memory.  (The 64-row
-  // forms have no LDS to spare at their occupancy and read them in the
-  // epilogue.)
+  // outside the stage buffers) by one 4-byte DMA load per lane of waves
+  // 0 .. 3 before the main loop: the main loop's stage waits and barriers
+  // complete it, so the epilogue reads them without waiting on global
+  // memory.  (The 64-row forms have no LDS to spare at their occupancy and
+  // read them in the epilogue.)
   if constexpr (kTokOff >= 0) {
-    if (a.row_tokens) {
+    if (a.row_tokens && threadIdx.x < kBM) {
       typedef __attribute__((address_space(3))) void* lds_ptr_t;
       const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
       // an opaque copy of the thread index: the row computed here must not
@@ -281,8 +286,8 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
   }
 
   f32x16 acc[TM][kTN];
-  if constexpr (TM == kTM) {
-    gemm_mainloop<T, true>(a.op, M, m0, n0, a.nk, acc, lds);
+  if constexpr (kW8) {
+    gemm_mainloop_w8<T>(a.op, M, m0, n0, a.nk, acc, lds);
   } else if constexpr (kWFmt < 0) {
     gemm_mainloop_rows64<T, kStages64>(a.op, M, m0, n0, a.nk, acc, lds, one_half);
   } else {
@@ -293,7 +298,8 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
   }
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
+  // rows wm RW .. + RW - 1 and columns wn 128 .. + 127 of the tile
+  const int wm = kW8 ? (wid & 3) : wid >> 1, wn = kW8 ? (wid >> 2) : (wid & 1);
   // the idle waves of a 128-column workgroup are done (no barrier follows
   // in this form's epilogue)
   if (one_half && wn) return;
@@ -495,8 +501,8 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
     // evicting the operand panels that the co-resident tiles share in L2.
     const int Mz = (M + 63) & ~63;
 #pragma unroll 4
-    for (int it = 0; it < 32; ++it) {
-      const int idx = it * 256 + tid;
+    for (int it = 0; it < 8192 / NT; ++it) {
+      const int idx = it * NT + tid;
       const int R = idx >> 5, k = idx & 31;
       const int col = n0 + k * 8;
       if (m0 + R < Mz && col < a.Vpad)
@@ -508,13 +514,15 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
   }
 }
 
+// The 256-row tile: eight waves (2 kThreads threads), two per SIMD.
 template <typename T, bool kStoreE, bool kSample = false>
-__global__ RZ_GEMM_ATTR void k_fwd_logits(FwdArgs a) {
+__global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_fwd_logits(FwdArgs a) {
   // [0, 128 KB): main-loop stages, then (learner call, bf16) the e tile;
   // then the row tokens (the draw gathers nothing: its tokens are drawn
   // later)
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes + (kSample ? 0 : 4 * kBM)];
-  fwd_logits_body<T, kStoreE, kSample, kTM, -1, 2, kSample ? -1 : kLdsBytes>(a, lds);
+  fwd_logits_body<T, kStoreE, kSample, 2, -1, 2, kSample ? -1 : kLdsBytes, true>(a, lds);
 }
 
 // The 64-row tile: 80 KB of LDS and a quarter of the accumulators, so two
@@ -2409,8 +2417,8 @@ hipError_t launch_fwd_sample(int dt, const void* hidden, int64_t n,
       if (dt) k_fwd_logits64<bf16, true><<<nblk, kThreads, 0, s>>>(a);
       else k_fwd_logits64<float, true><<<nblk, kThreads, 0, s>>>(a);
     } else {
-      if (dt) k_fwd_logits<bf16, false, true><<<nblk, kThreads, 0, s>>>(a);
-      else k_fwd_logits<float, false, true><<<nblk, kThreads, 0, s>>>(a);
+      if (dt) k_fwd_logits<bf16, false, true><<<nblk, 2 * kThreads, 0, s>>>(a);
+      else k_fwd_logits<float, false, true><<<nblk, 2 * kThreads, 0, s>>>(a);
     }
   });
 }
@@ -2513,11 +2521,11 @@ hipError_t launch_fwd_logits(int dt, const void* hidden, int64_t lda_bytes,
     });
   return timed(K_FWD_LOGITS, s, [&] {
     if (dt) {
-      if (e) k_fwd_logits<bf16, true><<<nblk, kThreads, 0, s>>>(a);
-      else k_fwd_logits<bf16, false><<<nblk, kThreads, 0, s>>>(a);
+      if (e) k_fwd_logits<bf16, true><<<nblk, 2 * kThreads, 0, s>>>(a);
+      else k_fwd_logits<bf16, false><<<nblk, 2 * kThreads, 0, s>>>(a);
     } else {
-      if (e) k_fwd_logits<float, true><<<nblk, kThreads, 0, s>>>(a);
-      else k_fwd_logits<float, false><<<nblk, kThreads, 0, s>>>(a);
+      if (e) k_fwd_logits<float, true><<<nblk, 2 * kThreads, 0, s>>>(a);
+      else k_fwd_logits<float, false><<<nblk, 2 * kThreads, 0, s>>>(a);
     }
   });
 }
