@@ -128,6 +128,14 @@ __device__ __forceinline__ int acc_row(int wm, int mi, int r, int lane) {
 __device__ __forceinline__ int acc_col(int wn, int ni, int lane) {
   return wn * 128 + ni * 32 + (lane & 31);
 }
+// The same for a wave whose blocks start at tile row wrow and column wcol
+// (gemm_mainloop_w8: wrow = 64 (w % 4), wcol = 128 (w / 4)).
+__device__ __forceinline__ int acc_row8(int wrow, int mi, int r, int lane) {
+  return wrow + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+__device__ __forceinline__ int acc_col8(int wcol, int ni, int lane) {
+  return wcol + ni * 32 + (lane & 31);
+}
 
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
@@ -371,16 +379,18 @@ __device__ __forceinline__ void gemm_mainloop(const GemmOperands& op, int M,
 // 32-column blocks), so each wave holds half the accumulators of
 // gemm_mainloop's and issues half its MFMAs; while one wave of a SIMD waits
 // on its LDS reads, loads or a barrier, the other can issue.  Same stage
-// layout, swizzle and K steps as gemm_mainloop<T, true>, and each 32 x 32
-// block sees the same MFMA (swapped operands) on the same fragments in the
-// same K order, so its accumulators are bit-identical to that tile's.  Each
-// wave fills 32 rows of each operand per stage (four loads each).  Needs
-// 512 threads.  Leaves the LDS free on return.
-template <typename T>
+// layouts, swizzles and K steps as gemm_mainloop<T, kSwap, kTransA>, and
+// each 32 x 32 block sees the same MFMA on the same fragments in the same K
+// order, so its accumulators are bit-identical to that tile's (kSwap and
+// kTransA as there).  Each wave fills 32 rows (K-major A: 8 K-rows) of each
+// operand per stage, four loads each.  Needs 512 threads.  Leaves the LDS
+// free on return.
+template <typename T, bool kSwap = true, bool kTransA = false>
 __device__ __forceinline__ void gemm_mainloop_w8(const GemmOperands& op, int M,
                                                  int m0, int n0, int nk,
                                                  f32x16 (&acc)[2][kTN],
                                                  char* lds) {
+  static_assert(!kTransA || sizeof(T) == 2, "K-major A needs 16-bit values");
   const int tid = threadIdx.x;
   const int lane = tid & 63, wid = tid >> 6;
   const int wrow = (wid & 3) * 64, wcol = (wid >> 2) * 128;
@@ -412,41 +422,86 @@ __device__ __forceinline__ void gemm_mainloop_w8(const GemmOperands& op, int M,
   for (int i = 0; i < 4; ++i) {
     const int r = wu * 32 + 8 * i + (lane >> 3);
     const int c = (lane & 7) ^ swz(r);
-    int m = m0 + r;
-    m = m < M ? m : M - 1;
-    const int64_t prow = op.a_rows ? (int64_t)op.a_rows[op.a_base + m]
-                                   : op.a_base + m;
-    ga[i] = op.A + prow * op.lda + c * 16;
+    if constexpr (kTransA) {
+      // K-rows 2 (4 wu + i) and + 1 of the stage, as in gemm_mainloop
+      const int kr = 2 * (wu * 4 + i) + (lane >> 5);
+      const int lc = (lane & 31) ^ (4 * (kr & 3));
+      int mm = m0 + 8 * lc;
+      mm = mm <= M - 8 ? mm : M - 8;
+      ga[i] = op.A + (int64_t)kr * op.lda + (int64_t)mm * 2;
+    } else {
+      int m = m0 + r;
+      m = m < M ? m : M - 1;
+      const int64_t prow = op.a_rows ? (int64_t)op.a_rows[op.a_base + m]
+                                     : op.a_base + m;
+      ga[i] = op.A + prow * op.lda + c * 16;
+    }
     int n = n0 + r;
     n = n < op.N ? n : op.N - 1;
     gb[i] = op.B + (int64_t)n * op.ldb + c * 16;
   }
-  // load j of a stage: j < 4 fills A rows 32 wu + 8 j .. + 7, j >= 4 the
-  // same rows of B
+  // load j of a stage: j < 4 fills A rows 32 wu + 8 j .. + 7 (K-major:
+  // K-rows 8 wu + 2 j, + 1), j >= 4 the same rows of B
   auto dma1 = [&](int kt, int stage, int j) {
     const int64_t k = (int64_t)kt * kRowBytes;
+    const int64_t ka = kTransA ? (int64_t)kt * 64 * op.lda : k;
     char* st = lds + stage * kStageBytes + (wu * 32 + (j & 3) * 8) * kRowBytes;
     if (j < 4)
-      __builtin_amdgcn_global_load_lds(ga[j] + k, (lds_ptr_t)st, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(ga[j] + ka, (lds_ptr_t)st, 16, 0, 0);
     else
       __builtin_amdgcn_global_load_lds(gb[j - 4] + k,
                                        (lds_ptr_t)(st + kOperandBytes), 16, 0, 0);
   };
+  // K-major A: the transposing reads of gemm_mainloop for this wave's rows
+  int a_tr[2][2];
+  if constexpr (kTransA) {
+    const int g = lane >> 4, q = lane & 15;
+    const int X = 4 * (q >> 2);
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int kq = 8 * (g >> 1) + 4 * r + (q >> 2);
+        const int mloc = wrow + mi * 32 + 16 * (g & 1) + 4 * (q & 3);
+        a_tr[mi][r] = kq * 512 + (((mloc >> 3) ^ X) << 4) + (mloc & 7) * 2;
+      }
+  }
+  typedef __attribute__((address_space(3))) const char* lds_cptr_t;
   u32x4 fa[2][2], fb[2][kTN];
   auto lread = [&](int buf, int stage, int s) {
     const char* sa = lds + stage * kStageBytes;
     const char* sb = sa + kOperandBytes;
+    if constexpr (kTransA) {
+      // by hand, as in gemm_mainloop (the compiler's own form would wait
+      // for every outstanding LDS-DMA load first)
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-      fa[buf][mi] = *reinterpret_cast<const u32x4*>(sa + a_off[mi] + c_off[s]);
+      for (int mi = 0; mi < 2; ++mi) {
+        const uint32_t p0 = (uint32_t)(uintptr_t)(lds_cptr_t)(sa + a_tr[mi][0]);
+        const uint32_t p1 = (uint32_t)(uintptr_t)(lds_cptr_t)(sa + a_tr[mi][1]);
+        u32x2 lo, hi;
+        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                     : "=v"(lo) : "v"(p0), "i"(s * 8192) : "memory");
+        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                     : "=v"(hi) : "v"(p1), "i"(s * 8192) : "memory");
+        fa[buf][mi] = u32x4{lo.x, lo.y, hi.x, hi.y};
+      }
+    } else {
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+        fa[buf][mi] = *reinterpret_cast<const u32x4*>(sa + a_off[mi] + c_off[s]);
+    }
 #pragma unroll
     for (int ni = 0; ni < kTN; ++ni)
       fb[buf][ni] = *reinterpret_cast<const u32x4*>(sb + b_off[ni] + c_off[s]);
   };
-  // block q = 4 mi + ni of one K step (swapped operands)
+  // block q = 4 mi + ni of one K step
   auto mm1 = [&](int buf, int q) {
-    mfma_step(acc[q / kTN][q % kTN], fb[buf][q % kTN], fa[buf][q / kTN],
-              (const T*)nullptr);
+    if constexpr (kSwap)
+      mfma_step(acc[q / kTN][q % kTN], fb[buf][q % kTN], fa[buf][q / kTN],
+                (const T*)nullptr);
+    else
+      mfma_step(acc[q / kTN][q % kTN], fa[buf][q / kTN], fb[buf][q % kTN],
+                (const T*)nullptr);
   };
   auto mmr = [&](int buf, int lo, int hi) {
 #pragma unroll

@@ -13,6 +13,9 @@
 
 #define RZ_GEMM_ATTR \
   __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// the 256 x 256 tile on eight waves (gemm_mainloop_w8), two per SIMD
+#define RZ_GEMM8_ATTR \
+  __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
 namespace rz {
 
@@ -516,8 +519,7 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
 
 // The 256-row tile: eight waves (2 kThreads threads), two per SIMD.
 template <typename T, bool kStoreE, bool kSample = false>
-__global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void k_fwd_logits(FwdArgs a) {
+__global__ RZ_GEMM8_ATTR void k_fwd_logits(FwdArgs a) {
   // [0, 128 KB): main-loop stages, then (learner call, bf16) the e tile;
   // then the row tokens (the draw gathers nothing: its tokens are drawn
   // later)
@@ -1778,17 +1780,18 @@ __host__ __device__ inline RoundSplit round_split(int T, int ncu) {
   return r;
 }
 
-// Parked tile q: 16-byte chunk c of thread t at part + q kPartTileFloats +
-// 4 (256 c + t), chunk c holding registers 4 (c % 4) .. + 3 of block c / 4.
+// Parked tile q (the eight-wave tile, 512 threads): 16-byte chunk c of
+// thread t at part + q kPartTileFloats + 4 (512 c + t), chunk c holding
+// registers 4 (c % 4) .. + 3 of block (c / 16, (c / 4) % 4).
 __device__ __forceinline__ f32x4* part_chunk(float* part, int q, int c) {
-  return reinterpret_cast<f32x4*>(part + (int64_t)q * kPartTileFloats) + c * 256 +
-         threadIdx.x;
+  return reinterpret_cast<f32x4*>(part + (int64_t)q * kPartTileFloats) +
+         c * (2 * kThreads) + threadIdx.x;
 }
 
 __device__ __forceinline__ void park_tile(float* part, int q,
-                                          const f32x16 (&acc)[kTM][kTN]) {
+                                          const f32x16 (&acc)[2][kTN]) {
 #pragma unroll
-  for (int c = 0; c < 4 * kTM * kTN; ++c) {
+  for (int c = 0; c < 4 * 2 * kTN; ++c) {
     const f32x16& blk = acc[c / 16][(c / 4) % 4];
     const int r = 4 * (c % 4);
     *part_chunk(part, q, c) = f32x4{blk[r], blk[r + 1], blk[r + 2], blk[r + 3]};
@@ -1798,10 +1801,10 @@ __device__ __forceinline__ void park_tile(float* part, int q,
 // the pieces q0 .. q0 + n - 1 summed in order (only the accumulators of
 // block row mi_only when it is >= 0)
 __device__ __forceinline__ void sum_parked(float* part, int q0, int n,
-                                           f32x16 (&acc)[kTM][kTN],
+                                           f32x16 (&acc)[2][kTN],
                                            int mi_only = -1) {
 #pragma unroll
-  for (int c = 0; c < 4 * kTM * kTN; ++c) {
+  for (int c = 0; c < 4 * 2 * kTN; ++c) {
     if (mi_only >= 0 && c / 16 != mi_only) continue;
     f32x4 v = *part_chunk(part, q0, c);
     for (int p = 1; p < n; ++p) v += *part_chunk(part, q0 + p, c);
@@ -1838,22 +1841,23 @@ struct DhArgs {
   float* dh;
 };
 
-// The epilogue of one dHidden tile: the rows' factors (bf16), the token
-// column's exact term, the scatter to the rows' positions.
+// The epilogue of one dHidden tile (eight waves, see gemm_mainloop_w8): the
+// rows' factors (bf16), the token column's exact term, the scatter to the
+// rows' positions.
 template <typename T>
 __device__ __forceinline__ void dh_epilogue(const DhArgs<T>& a, const RowCount& rc,
                                             int M, int m0, int n0,
-                                            f32x16 (&acc)[kTM][kTN], char* lds,
+                                            f32x16 (&acc)[2][kTN], char* lds,
                                             int mi_only = -1) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
+  const int wrow = (wid & 3) * 64, wcol = (wid >> 2) * 128;
   int* sidx = reinterpret_cast<int*>(lds);
   int* stok = sidx + 256;
   float* scoef = reinterpret_cast<float*>(stok + 256);
   float* src = scoef + 256;
   float* srg = src + 256;
   constexpr bool kScaled = sizeof(T) == 2;  // bf16: A was the stored e
-  {
+  if (tid < kBM) {  // one tile row per thread of waves 0 .. 3
     const int m = m0 + tid;
     const int64_t p = rc.base + m;
     sidx[tid] = m < M ? a.idx[p] : 0;
@@ -1869,11 +1873,11 @@ __device__ __forceinline__ void dh_epilogue(const DhArgs<T>& a, const RowCount& 
   if constexpr (kScaled) {
     // the rows' factors in place, one row's pair of scales at a time
 #pragma unroll
-    for (int mi = 0; mi < kTM; ++mi)
+    for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         if (mi_only >= 0 && mi != mi_only) continue;
-        const int row = acc_row(wm, mi, r, lane);
+        const int row = acc_row8(wrow, mi, r, lane);
         const float c = src[row], g = srg[row];
 #pragma unroll
         for (int ni = 0; ni < kTN; ++ni) acc[mi][ni][r] = c * (g * acc[mi][ni][r]);
@@ -1881,15 +1885,15 @@ __device__ __forceinline__ void dh_epilogue(const DhArgs<T>& a, const RowCount& 
       }
   }
 #pragma unroll
-  for (int mi = 0; mi < kTM; ++mi)
+  for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
     for (int ni = 0; ni < kTN; ++ni) {
       if (mi_only >= 0 && mi != mi_only) continue;
-      const int h = n0 + acc_col(wn, ni, lane);
+      const int h = n0 + acc_col8(wcol, ni, lane);
       if (h >= a.H) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = acc_row(wm, mi, r, lane);
+        const int row = acc_row8(wrow, mi, r, lane);
         if (m0 + row < M) {
           const float w = load_f(a.W + (int64_t)stok[row] * a.H + h);
           a.dh[(int64_t)sidx[row] * a.H + h] = acc[mi][ni][r] - scoef[row] * w;
@@ -1905,7 +1909,7 @@ __device__ __forceinline__ void dh_epilogue(const DhArgs<T>& a, const RowCount& 
 // Workgroups past their share return at once.  The split's whole rounds
 // come first, so running the pieces as a second launch costs one launch.
 template <typename T, bool kPiece>
-__global__ RZ_GEMM_ATTR void k_bwd_dh(DhArgs<T> a) {
+__global__ RZ_GEMM8_ATTR void k_bwd_dh(DhArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
   const RowCount rc = to_rc(a.rows);
   const int M = rc.get();
@@ -1932,28 +1936,28 @@ __global__ RZ_GEMM_ATTR void k_bwd_dh(DhArgs<T> a) {
   op.A += kb;
   op.B += kb;
 
-  f32x16 acc[kTM][kTN];
-  gemm_mainloop<T>(op, M, m0, n0, k1 - k0, acc, lds);
+  f32x16 acc[2][kTN];
+  gemm_mainloop_w8<T, false>(op, M, m0, n0, k1 - k0, acc, lds);
   // piece q = (tile - full) split + piece is parked at q, the launch index
   if constexpr (kPiece) park_tile(a.part, blockIdx.x, acc);
   else dh_epilogue(a, rc, M, m0, n0, acc, lds);
 }
 
 // The last round's tiles: their pieces summed in piece order, then the same
-// epilogue.  kTM workgroups per tail tile (kSplitWGs tiles at most).
+// epilogue.  Two workgroups of 512 threads per tail tile (kSplitWGs tiles at
+// most), one per block row mi of every wave.
 template <typename T>
-__global__ __launch_bounds__(256) void k_dh_tail(DhArgs<T> a) {
+__global__ __launch_bounds__(512) void k_dh_tail(DhArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char lds[5 * 256 * 4];
   const RowCount rc = to_rc(a.rows);
   const int M = rc.get();
   const int mt = (M + kBM - 1) / kBM;
   const int ntile = mt * a.nt;
   const RoundSplit sp = round_split(ntile, a.ncu);
-  // kTM workgroups per tail tile, one per block row mi of every wave
-  const int i = blockIdx.x / kTM, mi = blockIdx.x % kTM;
+  const int i = blockIdx.x / 2, mi = blockIdx.x % 2;
   if (i >= sp.tail) return;
   const TileCoord tc = map_tile(ntile - sp.tail + i, ntile, mt, a.nt);
-  f32x16 acc[kTM][kTN];
+  f32x16 acc[2][kTN];
   sum_parked(a.part, i * sp.split, sp.split, acc, mi);
   dh_epilogue(a, rc, M, tc.tm * kBM, tc.tn * kBN, acc, lds, mi);
 }
@@ -1979,32 +1983,32 @@ struct DwArgs {
 };
 
 
-// dW (+)= acc for one tile: rows v (vocabulary), columns h (hidden); the
-// first chunk overwrites.
+// dW (+)= acc for one tile (eight waves, see gemm_mainloop_w8): rows v
+// (vocabulary), columns h (hidden); the first chunk overwrites.
 __device__ __forceinline__ void dw_store(const DwArgs& a, int m0, int n0,
-                                         f32x16 (&acc)[kTM][kTN],
+                                         f32x16 (&acc)[2][kTN],
                                          int mi_only = -1) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
+  const int wrow = (wid & 3) * 64, wcol = (wid >> 2) * 128;
   const int unscale = a.sigma ? -*a.sigma : 0;
 #pragma unroll
-  for (int mi = 0; mi < kTM; ++mi)
+  for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
     for (int ni = 0; ni < kTN; ++ni) {
       if (mi_only >= 0 && mi != mi_only) continue;
       // one 32 x 32 block at a time keeps the in-flight loads bounded
       __builtin_amdgcn_sched_barrier(0);
-      const int h = n0 + acc_col(wn, ni, lane);
+      const int h = n0 + acc_col8(wcol, ni, lane);
       if (h >= a.H) continue;
       float prev[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int v = m0 + acc_row(wm, mi, r, lane);
+        const int v = m0 + acc_row8(wrow, mi, r, lane);
         prev[r] = (!a.first && v < a.V) ? a.dw[(int64_t)v * a.H + h] : 0.f;
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int v = m0 + acc_row(wm, mi, r, lane);
+        const int v = m0 + acc_row8(wrow, mi, r, lane);
         if (v < a.V)
           a.dw[(int64_t)v * a.H + h] = prev[r] + ldexpf(acc[mi][ni][r], unscale);
       }
@@ -2013,7 +2017,7 @@ __device__ __forceinline__ void dw_store(const DwArgs& a, int m0, int n0,
 
 
 template <typename T>
-__global__ RZ_GEMM_ATTR void k_bwd_dw(DwArgs a) {
+__global__ RZ_GEMM8_ATTR void k_bwd_dw(DwArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
   const int K = to_rc(a.krows).get();
   const int nk = (K + a.kstage - 1) / a.kstage;
@@ -2036,10 +2040,10 @@ __global__ RZ_GEMM_ATTR void k_bwd_dw(DwArgs a) {
   op.A += sizeof(T) == 2 ? kr * op.lda : kr * (int64_t)sizeof(T);
   op.B += kr * (int64_t)sizeof(T);
 
-  f32x16 acc[kTM][kTN];
+  f32x16 acc[2][kTN];
   // bf16 reads dz itself through transposing LDS reads; fp32 has no such
   // read and takes the transposed copy dz^T
-  gemm_mainloop<T, false, sizeof(T) == 2>(op, a.amax, m0, n0, k1 - k0, acc, lds);
+  gemm_mainloop_w8<T, false, sizeof(T) == 2>(op, a.amax, m0, n0, k1 - k0, acc, lds);
   if (pieces > 1) {
     park_tile(a.part, (tb - full) * pieces + piece, acc);
     return;
@@ -2049,15 +2053,15 @@ __global__ RZ_GEMM_ATTR void k_bwd_dw(DwArgs a) {
 
 // The last round's tiles: the pieces summed in piece order (a fixed order,
 // so dW stays run-to-run deterministic), then stored like any other tile.
-// kTM workgroups per last-round tile, one per block row mi of every wave:
-// the same sums and stores, spread over four times the CUs.
-__global__ __launch_bounds__(256) void k_dw_tail(DwArgs a) {
+// Two workgroups of 512 threads per last-round tile, one per block row mi
+// of every wave: the same sums and stores, spread over twice the CUs.
+__global__ __launch_bounds__(512) void k_dw_tail(DwArgs a) {
   const int K = to_rc(a.krows).get();
   const int nk = (K + a.kstage - 1) / a.kstage;
   if (nk == 0 && !a.first) return;
-  const int i = blockIdx.x / kTM, mi = blockIdx.x % kTM;
+  const int i = blockIdx.x / 2, mi = blockIdx.x % 2;
   const TileCoord tc = map_tile(a.T - a.tail + i, a.T, a.mt, a.nt);
-  f32x16 acc[kTM][kTN];
+  f32x16 acc[2][kTN];
   sum_parked(a.part, i * a.split, a.split, acc, mi);
   dw_store(a, tc.tm * kBM, tc.tn * kBN, acc, mi);
 }
@@ -2898,10 +2902,10 @@ static hipError_t launch_bwd_dh_t(const void* dz, int64_t ldz, DevRows rows,
   return timed(K_BWD_DH, s, [&] {
     // launch bounds: every tile of rows.cap rows; the pieces and their sums
     // of at most kSplitWGs parked tiles
-    k_bwd_dh<T, false><<<a.mt * a.nt, kThreads, 0, s>>>(a);
+    k_bwd_dh<T, false><<<a.mt * a.nt, 2 * kThreads, 0, s>>>(a);
     if (part) {
-      k_bwd_dh<T, true><<<kSplitWGs, kThreads, 0, s>>>(a);
-      k_dh_tail<T><<<kSplitWGs * kTM, kThreads, 0, s>>>(a);
+      k_bwd_dh<T, true><<<kSplitWGs, 2 * kThreads, 0, s>>>(a);
+      k_dh_tail<T><<<kSplitWGs * 2, 2 * kThreads, 0, s>>>(a);
     }
   });
 }
@@ -2960,9 +2964,9 @@ hipError_t launch_bwd_dw(int dt, const void* dz, int64_t ld, DevRows krows,
   a.part = part;
   return timed(K_BWD_DW, s, [&] {
     const int grid = a.T - a.tail + a.tail * a.split;
-    if (dt) k_bwd_dw<bf16><<<grid, kThreads, 0, s>>>(a);
-    else k_bwd_dw<float><<<grid, kThreads, 0, s>>>(a);
-    if (a.tail) k_dw_tail<<<a.tail * kTM, kThreads, 0, s>>>(a);
+    if (dt) k_bwd_dw<bf16><<<grid, 2 * kThreads, 0, s>>>(a);
+    else k_bwd_dw<float><<<grid, 2 * kThreads, 0, s>>>(a);
+    if (a.tail) k_dw_tail<<<a.tail * 2, 2 * kThreads, 0, s>>>(a);
   });
 }
 
