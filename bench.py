@@ -41,13 +41,13 @@ GEMM_KERNELS = ("fwd_logits_gemm", "bwd_dh_gemm", "bwd_dw_gemm")
 # kernel sources they were taken from.
 COUNTER_TRAFFIC = {
     "workload": "qwen3_4b_tool",
-    "sources_sha256": "302578bbdc394b62bec27ab218874438635cde533b92d53949c15376d78999b3",
+    "sources_sha256": "cf896f326802db3bb1547498372a8ef4cac4246d81d662d992b0b3ab58a2a470",
     # per timed launch: a GEMM with its last-round K pieces and their sum
-    "bytes_per_launch": {"fwd_logits_gemm": 26561835351,
-                         "bwd_dh_gemm": 24553273455,
-                         "bwd_dw_gemm": 29189319307,
-                         "grad_norm": 2291983996,
-                         "mx_dequant_mxfp4": 984650700},
+    "bytes_per_launch": {"fwd_logits_gemm": 26061052333,
+                         "bwd_dh_gemm": 24139376391,
+                         "bwd_dw_gemm": 28821889512,
+                         "grad_norm": 2291984084,
+                         "mx_dequant_mxfp4": 984657262},
 }
 
 
@@ -56,9 +56,9 @@ COUNTER_TRAFFIC = {
 # GEMMs, from the counter run of profiles/mfma_utilisation_qwen3_4b_tool.md,
 # over the launches that hold rows; same validity rule as COUNTER_TRAFFIC.
 COUNTER_MFMA = {
-    "fwd_logits_gemm": {"mfma_busy": 0.568, "clock_ghz": 1.847},
-    "bwd_dh_gemm": {"mfma_busy": 0.618, "clock_ghz": 1.756},
-    "bwd_dw_gemm": {"mfma_busy": 0.571, "clock_ghz": 1.820},
+    "fwd_logits_gemm": {"mfma_busy": 0.610, "clock_ghz": 1.781},
+    "bwd_dh_gemm": {"mfma_busy": 0.668, "clock_ghz": 1.689},
+    "bwd_dw_gemm": {"mfma_busy": 0.631, "clock_ghz": 1.738},
 }
 
 
