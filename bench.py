@@ -41,7 +41,7 @@ GEMM_KERNELS = ("fwd_logits_gemm", "bwd_dh_gemm", "bwd_dw_gemm")
 # kernel sources they were taken from.
 COUNTER_TRAFFIC = {
     "workload": "qwen3_4b_tool",
-    "sources_sha256": "cf896f326802db3bb1547498372a8ef4cac4246d81d662d992b0b3ab58a2a470",
+    "sources_sha256": "07a29526954b5bd9724f179d7e3a6022b58b9d888bd8a47a9265c7e036e70121",
     # per timed launch: a GEMM with its last-round K pieces and their sum
     "bytes_per_launch": {"fwd_logits_gemm": 26061052333,
                          "bwd_dh_gemm": 24139376391,
@@ -448,7 +448,7 @@ def bench_diag(args, torch, rz, synth, dev):
 def bench_ceiling(args, torch, rz, dev):
     """The matrix cores' own ceiling on this part (rz_calibrate_mfma): the
     learner GEMMs' MFMA, four waves per CU with a wave's 128 x 128 block of
-    accumulators, no global traffic; operands from registers or from LDS
+    accumulators (the four-wave form of the tile), no global traffic; operands from registers or from LDS
     (the GEMM's read volume), random-looking or zero values.  Each variant
     runs args.warmup untimed launches and args.steps timed ones of about
     30 ms, back to back on one stream."""

@@ -3,11 +3,12 @@
 // (v_mfma_f32_32x32x16_bf16) under its own clock and power management, with
 // no global memory traffic at all.
 //
-// Each workgroup is four waves, one per SIMD, as in the GEMM tile.  A wave
-// keeps sixteen 32 x 32 fp32 accumulators (a 128 x 128 block, as a wave of
-// the 256 x 256 tile does) and eight fragments of each operand; K step s
-// feeds accumulator (mi, ni) with A fragment (s + mi) % 8 and B fragment
-// (s + 3 ni) % 8, so successive MFMAs see new operand values as in a GEMM.
+// Each workgroup is four waves, one per SIMD, as in the four-wave form of
+// the GEMM tile.  A wave keeps sixteen 32 x 32 fp32 accumulators (a 128 x 128
+// block, as a wave of that tile does) and eight fragments of each operand;
+// K step s feeds accumulator (mi, ni) with A fragment (s + mi) % 8 and B
+// fragment (s + 3 ni) % 8, so successive MFMAs see new operand values as in
+// a GEMM.
 // from_lds = 0 keeps the fragments in registers; from_lds = 1 reads the
 // step's four A and four B fragments from LDS before its sixteen MFMAs
 // (the GEMM's LDS read volume per MFMA, without its global loads).

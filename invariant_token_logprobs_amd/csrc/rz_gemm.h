@@ -9,9 +9,12 @@
 // page, section 02 "Remove kernel mismatch").
 //
 // Layout of the work (gfx950, CDNA4):
-//  * 256 threads = 4 wave64s in a 2 x 2 grid, each wave owning a 128 x 128
-//    sub-tile = 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 (fp32 inputs use
-//    v_mfma_f32_32x32x2_f32, four per 16-byte fragment);
+//  * the learner GEMMs and the 256-row forward (gemm_mainloop_w8): 512
+//    threads = 8 wave64s, two per SIMD, wave w owning rows 64 (w % 4) .. + 63
+//    of column half w / 4 = 2 x 4 blocks of v_mfma_f32_32x32x16_bf16 (fp32
+//    inputs use v_mfma_f32_32x32x2_f32, four per 16-byte fragment);
+//    gemm_mainloop is the same tile on 4 wave64s in a 2 x 2 grid, each
+//    owning a 128 x 128 sub-tile = 4 x 4 blocks, one wave per SIMD;
 //  * A and B stages go straight from global memory into LDS
 //    (global_load_lds_dwordx4, no register round trip), double-buffered
 //    (2 x 64 KB), with a 16-byte-chunk XOR swizzle (see swz) so the fragment

@@ -144,8 +144,8 @@ __device__ __forceinline__ int e_stage_off(int R, int k) {
 // products on counter words 0 and 2, the halves and the key XORed into the
 // next counter; the key grows by fixed Weyl increments between rounds.
 // Four blocks at once (counters c[0..3], one key), the four independent
-// chains interleaved in each round, so one wave per SIMD has four products
-// in flight instead of waiting on each round's product in turn.  The round
+// chains interleaved in each round, so each wave has four products in
+// flight instead of waiting on each round's product in turn.  The round
 // loop is unrolled by two only: the counters then alternate between two
 // register sets with no copies at the loop's end, while a fully unrolled
 // loop at the draw's call sites stops the enclosing loops from unrolling
