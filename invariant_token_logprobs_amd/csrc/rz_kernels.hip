@@ -24,12 +24,17 @@ namespace {
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kIntMin = -2147483647 - 1;
 
-// Row counts up to which the forward runs on the 64-row tile (measured at
-// the Qwen3-4B head: the logits forward gains up to 128 rows, the draw, whose
-// epilogue spreads over four times the workgroups, up to 256).  Up to 64
-// rows (one row block) its single-stage form runs, three workgroups per CU.
+// Row counts up to which the forward runs on the 64-row tile, measured at
+// the Qwen3-4B head against the eight-wave 256-row tile: the logits forward
+// gains up to 128 rows, the draw, whose epilogue spreads over four times the
+// workgroups, up to 192 (per call at 96 / 128 / 192 / 256 rows: 0.249 /
+// 0.262 / 0.310 / 0.385 ms against 0.302 / 0.310 / 0.317 / 0.331 ms).  The
+// MX head keeps the 64-row tile up to 256 rows for the draw: past it the
+// head is expanded on every call.  Up to 64 rows (one row block) the
+// single-stage form runs, three workgroups per CU.
 constexpr int kRows64MaxLogits = 128;
-constexpr int kRows64MaxSample = 256;
+constexpr int kRows64MaxSample = 192;
+constexpr int kRows64MaxMxSample = 256;
 
 // Logits of vocabulary columns >= V inside the last statistics tile: finite, so
 // the row maximum stays finite and no (-inf) - (-inf) can appear.
@@ -2430,7 +2435,7 @@ hipError_t launch_fwd_sample(int dt, const void* hidden, int64_t n,
 // The forward of rz_token_logprobs_mx / rz_sample_tokens_mx on the 64-row
 // tile (host-known rows, n <= mx_rows64_max(sample), H % 128 == 0): the
 // logits GEMM with its statistics and the gather (or the draw).
-int mx_rows64_max(int sample) { return sample ? kRows64MaxSample : kRows64MaxLogits; }
+int mx_rows64_max(int sample) { return sample ? kRows64MaxMxSample : kRows64MaxLogits; }
 
 hipError_t launch_fwd_mx(int fmt, const void* hidden, int64_t n,
                          const uint8_t* codes, const uint8_t* scales, int H,

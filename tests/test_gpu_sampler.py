@@ -87,11 +87,11 @@ def test_sampler_parity_and_diff0(dtype):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_small_batches_match_the_large_batch(dtype):
-    """Up to 64 rows the forward runs the single-stage 64-row tile, up to 256
+    """Up to 64 rows the forward runs the single-stage 64-row tile, up to 192
     rows (draw) or 128 rows (logits) the two-stage 64-row tile, and beyond that
     the 256-row tile; up to 256 rows the tile partials are stored row-major,
-    beyond that tile-major.  The first 1, 37, 64, 65, 200 and 256 rows of a
-    batch, drawn and scored alone, give the same tokens, records and
+    beyond that tile-major.  The first 1, 37, 64, 65, 192, 193 and 256 rows
+    of a batch, drawn and scored alone, give the same tokens, records and
     log-sum-exps, bit for bit, as they do inside the whole batch."""
     import invariant_token_logprobs_amd as rz
     torch = torch_mod()
@@ -107,7 +107,7 @@ def test_small_batches_match_the_large_batch(dtype):
     torch.cuda.synchronize()
     lp_all, lse_all = host(lp_all), host(lse_all)
     bits = lambda x: np.asarray(x, np.float32).view(np.uint32)
-    for n in (1, 37, 64, 65, 200, 256):
+    for n in (1, 37, 64, 65, 192, 193, 256):
         what = f"{dtype} first {n} rows"
         t_n, m_n, l_n = _run(hidden[:n].contiguous(), W, ids[:n], SEED)
         assert np.array_equal(t_n, tok[:n]), what
