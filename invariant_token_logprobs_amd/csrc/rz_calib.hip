@@ -3,9 +3,10 @@
 // (v_mfma_f32_32x32x16_bf16) under its own clock and power management, with
 // no global memory traffic at all.
 //
-// Each workgroup is four waves, one per SIMD, as in the four-wave form of
-// the GEMM tile.  A wave keeps sixteen 32 x 32 fp32 accumulators (a 128 x 128
-// block, as a wave of that tile does) and eight fragments of each operand;
+// Each workgroup is four waves, one per SIMD.  A wave keeps sixteen 32 x 32
+// fp32 accumulators (a 128 x 128 block: the four-wave layout of the 256 x 256
+// tile, whose MFMA stream per SIMD equals that of the two waves of the
+// library's eight-wave tile) and eight fragments of each operand;
 // K step s feeds accumulator (mi, ni) with A fragment (s + mi) % 8 and B
 // fragment (s + 3 ni) % 8, so successive MFMAs see new operand values as in
 // a GEMM.

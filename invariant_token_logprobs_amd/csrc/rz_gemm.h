@@ -9,12 +9,12 @@
 // page, section 02 "Remove kernel mismatch").
 //
 // Layout of the work (gfx950, CDNA4):
-//  * the learner GEMMs and the 256-row forward (gemm_mainloop_w8): 512
-//    threads = 8 wave64s, two per SIMD, wave w owning rows 64 (w % 4) .. + 63
-//    of column half w / 4 = 2 x 4 blocks of v_mfma_f32_32x32x16_bf16 (fp32
-//    inputs use v_mfma_f32_32x32x2_f32, four per 16-byte fragment);
-//    gemm_mainloop is the same tile on 4 wave64s in a 2 x 2 grid, each
-//    owning a 128 x 128 sub-tile = 4 x 4 blocks, one wave per SIMD;
+//  * gemm_mainloop: 512 threads = 8 wave64s, two per SIMD, wave w owning
+//    rows 64 (w % 4) .. + 63 of column half w / 4 = 2 x 4 blocks of
+//    v_mfma_f32_32x32x16_bf16 (fp32 inputs use v_mfma_f32_32x32x2_f32, four
+//    per 16-byte fragment); the 64-row tiles for small row counts
+//    (gemm_mainloop_rows64) take the same blocks, fragments and K steps on
+//    four waves;
 //  * A and B stages go straight from global memory into LDS
 //    (global_load_lds_dwordx4, no register round trip), double-buffered
 //    (2 x 64 KB), with a 16-byte-chunk XOR swizzle (see swz) so the fragment
@@ -43,9 +43,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kBM = 256;          // tile rows (M)
 constexpr int kBN = 256;          // tile columns (N)
 constexpr int kRowBytes = 128;    // K bytes per stage row
-constexpr int kThreads = 256;
-constexpr int kTM = 4;            // 32 x 32 blocks per wave along M
-constexpr int kTN = 4;            // ... along N
+constexpr int kThreads = 256;     // the 64-row tiles; the 256 x 256 tile 2 kThreads
+constexpr int kTM = 4;            // 32 x 32 blocks per wave along M (rz_calib's four-wave layout)
+constexpr int kTN = 4;            // ... along N (every layout)
 constexpr int kOperandBytes = kBM * kRowBytes;      // 32 KB
 constexpr int kStageBytes = 2 * kOperandBytes;      // A + B
 constexpr int kLdsBytes = 2 * kStageBytes;          // double buffer, 128 KB
@@ -123,20 +123,14 @@ __device__ __forceinline__ TileCoord map_tile(int bid, int nblk, int mt,
 }
 
 // Position of accumulator register r of block (mi, ni) inside the 256 x 256
-// tile, for v_mfma_*_32x32 output: lane l holds column l % 32 and rows
+// tile, for v_mfma_*_32x32 output (operands not swapped) of a wave whose
+// blocks start at tile row wrow and column wcol (gemm_mainloop: wrow =
+// 64 (w % 4), wcol = 128 (w / 4)): lane l holds column l % 32 and rows
 // 8 * (r / 4) + 4 * (l / 32) + (r % 4) of its 32 x 32 block.
-__device__ __forceinline__ int acc_row(int wm, int mi, int r, int lane) {
-  return wm * 128 + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-}
-__device__ __forceinline__ int acc_col(int wn, int ni, int lane) {
-  return wn * 128 + ni * 32 + (lane & 31);
-}
-// The same for a wave whose blocks start at tile row wrow and column wcol
-// (gemm_mainloop_w8: wrow = 64 (w % 4), wcol = 128 (w / 4)).
-__device__ __forceinline__ int acc_row8(int wrow, int mi, int r, int lane) {
+__device__ __forceinline__ int acc_row(int wrow, int mi, int r, int lane) {
   return wrow + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
-__device__ __forceinline__ int acc_col8(int wcol, int ni, int lane) {
+__device__ __forceinline__ int acc_col(int wcol, int ni, int lane) {
   return wcol + ni * 32 + (lane & 31);
 }
 
@@ -152,10 +146,16 @@ struct GemmOperands {
   int N;                // rows of B (columns of C)
 };
 
-// Accumulate acc over K stages [0, nk) for the tile at (m0, n0).  Rows of A
-// at or past M (and rows of B at or past N) are read from row M-1 (N-1) so
-// every load stays in bounds; their results are discarded by the epilogue.
-// Leaves the LDS free (all waves past the last barrier) on return.
+// Accumulate acc over K stages [0, nk) for the 256 x 256 tile at (m0, n0),
+// on eight waves (512 threads), two per SIMD: wave w owns rows
+// 64 (w % 4) .. + 63 (two 32-row blocks) of column half w / 4 (four
+// 32-column blocks); while one wave of a SIMD waits on its LDS reads, loads
+// or a barrier, the other can issue.  Rows of A at or past M (and rows of B
+// at or past N) are read from row M-1 (N-1) so every load stays in bounds;
+// their results are discarded by the epilogue.  Each 32 x 32 block sees the
+// same MFMA on the same fragments in K order k = 0, 1, 2, ..., whichever
+// wave or tile form computes it.  Leaves the LDS free (all waves past the
+// last barrier) on return.
 //
 // kTransA = true (16-bit values only) takes A stored K-major instead:
 // A[m, k] at A + k * lda + 2 m, i.e. rows of the memory matrix are K and
@@ -168,231 +168,11 @@ struct GemmOperands {
 // lane l then holds row l % 32 of its 32 x 32 block (an A row) and registers
 // r hold columns 8 (r / 4) + 4 (l / 32) + (r % 4), i.e. every lane owns
 // four runs of four consecutive B rows of one A row.
-template <typename T, bool kSwap = false, bool kTransA = false>
+template <typename T, bool kSwap = true, bool kTransA = false>
 __device__ __forceinline__ void gemm_mainloop(const GemmOperands& op, int M,
                                               int m0, int n0, int nk,
-                                              f32x16 (&acc)[kTM][kTN],
+                                              f32x16 (&acc)[2][kTN],
                                               char* lds) {
-  static_assert(!kTransA || sizeof(T) == 2, "K-major A needs 16-bit values");
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wid = tid >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
-
-#pragma unroll
-  for (int mi = 0; mi < kTM; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < kTN; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
-  if (nk <= 0) return;
-
-  // fragment read offsets: row (block base + lane % 32), chunk 2 s + lane / 32
-  int a_off[kTM], b_off[kTN];
-#pragma unroll
-  for (int mi = 0; mi < kTM; ++mi)
-    a_off[mi] = (wm * 128 + mi * 32 + (lane & 31)) * kRowBytes;
-#pragma unroll
-  for (int ni = 0; ni < kTN; ++ni)
-    b_off[ni] = (wn * 128 + ni * 32 + (lane & 31)) * kRowBytes;
-  // 16-byte chunk c of LDS row r lives at chunk c ^ swz(r), swz(r) =
-  // (r & 7) ^ ((r >> 3) & 1): any 8 consecutive rows (a 128-byte bank line)
-  // and the same-parity rows of any 16 (a 256-byte line) get distinct
-  // chunks, so the fragment reads are bank-conflict free.
-  int c_off[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s)
-    c_off[s] = ((2 * s + (lane >> 5)) ^ swz(lane & 31)) << 4;
-
-  // Global -> LDS without a register round trip: global_load_lds_dwordx4
-  // writes lane l's 16 bytes at (LDS base + 16 l).  Wave w fills rows
-  // [64 w, 64 w + 64) of each operand, 8 rows per instruction; lane l lands
-  // in row l / 8 at physical chunk l % 8, so it fetches the logical chunk
-  // (l % 8) ^ swz(row) that the swizzle places there.
-  typedef __attribute__((address_space(3))) void* lds_ptr_t;
-  const int wu = __builtin_amdgcn_readfirstlane(wid);
-  const char* ga[8];
-  const char* gb[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = wu * 64 + 8 * i + (lane >> 3);
-    const int c = (lane & 7) ^ swz(r);
-    int m = m0 + r;
-    m = m < M ? m : M - 1;
-    if constexpr (kTransA) {
-      // K-major A: instruction i of wave wu fills K-rows 2 (8 wu + i) and
-      // 2 (8 wu + i) + 1 of the stage (512 bytes each, lane / 32 picks the
-      // row); lane % 32 is the physical 16-byte chunk, which holds logical
-      // chunk (lane % 32) ^ 4 (row % 4), i.e. columns m0 + 8 chunk .. + 7.
-      // Columns past M - 8 read the last 8 (discarded by the epilogue).
-      const int kr = 2 * (wu * 8 + i) + (lane >> 5);
-      const int lc = (lane & 31) ^ (4 * (kr & 3));
-      int mm = m0 + 8 * lc;
-      mm = mm <= M - 8 ? mm : M - 8;
-      ga[i] = op.A + (int64_t)kr * op.lda + (int64_t)mm * 2;
-    } else {
-      const int64_t prow = op.a_rows ? (int64_t)op.a_rows[op.a_base + m]
-                                     : op.a_base + m;
-      ga[i] = op.A + prow * op.lda + c * 16;
-    }
-    int n = n0 + r;
-    n = n < op.N ? n : op.N - 1;
-    gb[i] = op.B + (int64_t)n * op.ldb + c * 16;
-  }
-  // load j of a stage: j < 8 fills A rows 8 j + [0, 8) of this wave's 64,
-  // j >= 8 the same rows of B
-  auto dma1 = [&](int kt, int stage, int j) {
-    const int64_t k = (int64_t)kt * kRowBytes;
-    // a K-major A stage advances by 64 rows, a K-contiguous one by 128 bytes
-    const int64_t ka = kTransA ? (int64_t)kt * 64 * op.lda : k;
-    char* sa = lds + stage * kStageBytes + wu * 64 * kRowBytes;
-    if (j < 8)
-      __builtin_amdgcn_global_load_lds(ga[j] + ka,
-                                       (lds_ptr_t)(sa + j * 8 * kRowBytes), 16,
-                                       0, 0);
-    else
-      __builtin_amdgcn_global_load_lds(
-          gb[j - 8] + k,
-          (lds_ptr_t)(sa + kOperandBytes + (j - 8) * 8 * kRowBytes), 16, 0, 0);
-  };
-  // K-major A: ds_read_b64_tr_b16 works on groups of 16 lanes; lane q of
-  // a group names 8 bytes (4 values) at K-row q / 4 of a 4-row slab and
-  // columns 4 (q % 4) .. + 3, and lane 4 a + b of the group receives column
-  // 4 a + b of all four rows -- four consecutive K values of one M row, the
-  // MFMA A-operand layout.  Group g of the wave covers the 16 columns
-  // 16 (g % 2) .. of the 32-row block and K-rows 8 (g / 2) + 4 r .. of the
-  // step; two reads (r = 0, 1) make the 8 values of one fragment.  The
-  // XOR of the chunk with 4 (row % 4) puts the 8 rows one read touches in
-  // four different 64-byte bank groups (two rows each, the minimum for
-  // 512 bytes).
-  int a_tr[kTM][2];
-  if constexpr (kTransA) {
-    const int g = lane >> 4, q = lane & 15;
-    const int X = 4 * (q >> 2);
-#pragma unroll
-    for (int mi = 0; mi < kTM; ++mi)
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int kq = 8 * (g >> 1) + 4 * r + (q >> 2);
-        const int mloc = wm * 128 + mi * 32 + 16 * (g & 1) + 4 * (q & 3);
-        a_tr[mi][r] = kq * 512 + (((mloc >> 3) ^ X) << 4) + (mloc & 7) * 2;
-      }
-  }
-  typedef __attribute__((address_space(3))) const char* lds_cptr_t;
-  // fragments of two consecutive 16-byte K steps (register double buffer)
-  u32x4 fa[2][kTM], fb[2][kTN];
-  auto lread = [&](int buf, int stage, int s) {
-    const char* sa = lds + stage * kStageBytes;
-    const char* sb = sa + kOperandBytes;
-    if constexpr (kTransA) {
-      // Issued by hand: the compiler waits for every outstanding LDS-DMA
-      // load (vmcnt(0)) before its own form of this read.  The B reads
-      // below are issued after these ("memory" keeps them there) and LDS
-      // reads retire in order, so the lgkmcnt wait the compiler places
-      // before the first MFMA that uses B also covers these.
-#pragma unroll
-      for (int mi = 0; mi < kTM; ++mi) {
-        const uint32_t p0 = (uint32_t)(uintptr_t)(lds_cptr_t)(sa + a_tr[mi][0]);
-        const uint32_t p1 = (uint32_t)(uintptr_t)(lds_cptr_t)(sa + a_tr[mi][1]);
-        u32x2 lo, hi;
-        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
-                     : "=v"(lo) : "v"(p0), "i"(s * 8192) : "memory");
-        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
-                     : "=v"(hi) : "v"(p1), "i"(s * 8192) : "memory");
-        fa[buf][mi] = u32x4{lo.x, lo.y, hi.x, hi.y};
-      }
-    } else {
-#pragma unroll
-      for (int mi = 0; mi < kTM; ++mi)
-        fa[buf][mi] = *reinterpret_cast<const u32x4*>(sa + a_off[mi] + c_off[s]);
-    }
-#pragma unroll
-    for (int ni = 0; ni < kTN; ++ni)
-      fb[buf][ni] = *reinterpret_cast<const u32x4*>(sb + b_off[ni] + c_off[s]);
-  };
-  // block q = 4 mi + ni of one K step
-  auto mm1 = [&](int buf, int q) {
-    if constexpr (kSwap)
-      mfma_step(acc[q / kTN][q % kTN], fb[buf][q % kTN], fa[buf][q / kTN],
-                (const T*)nullptr);
-    else
-      mfma_step(acc[q / kTN][q % kTN], fa[buf][q / kTN], fb[buf][q % kTN],
-                (const T*)nullptr);
-  };
-  auto mmr = [&](int buf, int lo, int hi) {
-#pragma unroll
-    for (int q = lo; q < hi; ++q) mm1(buf, q);
-  };
-
-  // Schedule: stage kt lives in LDS buffer kt & 1 and is consumed as four
-  // 16-byte K steps s, each a phase of 16 MFMAs on fragments read during
-  // the previous phase.  A phase starts with one MFMA, which needs the
-  // previous phase's reads, and only then issues the next step's reads, so
-  // the LDS wait before it never covers reads that were just issued.
-  // Stage kt + 1's sixteen loads go out one per MFMA: eight right after the
-  // barrier that frees its buffer (among the last eight MFMAs of stage
-  // kt - 1) and eight in the first phase of stage kt; a burst of loads
-  // stalls the in-order wave and drains the MFMA pipe.  Before the barrier
-  // that ends stage kt, each wave waits for its own loads (vmcnt(0)), so the
-  // barrier makes stage kt + 1 complete in LDS and buffer kt & 1 free.
-  // sched_barrier(0) pins this order against the scheduler.  The MFMA
-  // order per accumulator is k = 0, 1, 2, ... exactly as in a plain loop.
-#define RZ_SB() __builtin_amdgcn_sched_barrier(0)
-#pragma unroll
-  for (int j = 0; j < 16; ++j) dma1(0, 0, j);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (nk > 1) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) dma1(1, 1, j);
-  }
-  lread(0, 0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool nx = kt + 1 < nk, nx2 = kt + 2 < nk;
-    RZ_SB(); mm1(0, 0); RZ_SB(); lread(1, cur, 1); RZ_SB();
-#pragma unroll
-    for (int q = 1; q < 16; ++q) {
-      mm1(0, q);
-      RZ_SB();
-      if (q <= 8 && nx) dma1(kt + 1, cur ^ 1, 7 + q);
-      RZ_SB();
-    }
-    mm1(1, 0); RZ_SB(); lread(0, cur, 2); RZ_SB(); mmr(1, 1, 16); RZ_SB();
-    mm1(0, 0); RZ_SB(); lread(1, cur, 3); RZ_SB(); mmr(0, 1, 16); RZ_SB();
-    mmr(1, 0, 8);
-    RZ_SB();
-    if (nx) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    RZ_SB();
-    if (nx) lread(0, cur ^ 1, 0);
-    RZ_SB();
-#pragma unroll
-    for (int q = 8; q < 16; ++q) {
-      mm1(1, q);
-      RZ_SB();
-      if (nx2) dma1(kt + 2, cur, q - 8);
-      RZ_SB();
-    }
-  }
-#undef RZ_SB
-}
-
-// The 256 x 256 tile on eight waves, two per SIMD: wave w owns rows
-// 64 (w % 4) .. + 63 (two 32-row blocks) of column half w / 4 (four
-// 32-column blocks), so each wave holds half the accumulators of
-// gemm_mainloop's and issues half its MFMAs; while one wave of a SIMD waits
-// on its LDS reads, loads or a barrier, the other can issue.  Same stage
-// layouts, swizzles and K steps as gemm_mainloop<T, kSwap, kTransA>, and
-// each 32 x 32 block sees the same MFMA on the same fragments in the same K
-// order, so its accumulators are bit-identical to that tile's (kSwap and
-// kTransA as there).  Each wave fills 32 rows (K-major A: 8 K-rows) of each
-// operand per stage, four loads each.  Needs 512 threads.  Leaves the LDS
-// free on return.
-template <typename T, bool kSwap = true, bool kTransA = false>
-__device__ __forceinline__ void gemm_mainloop_w8(const GemmOperands& op, int M,
-                                                 int m0, int n0, int nk,
-                                                 f32x16 (&acc)[2][kTN],
-                                                 char* lds) {
   static_assert(!kTransA || sizeof(T) == 2, "K-major A needs 16-bit values");
   const int tid = threadIdx.x;
   const int lane = tid & 63, wid = tid >> 6;
@@ -412,11 +192,21 @@ __device__ __forceinline__ void gemm_mainloop_w8(const GemmOperands& op, int M,
 #pragma unroll
   for (int ni = 0; ni < kTN; ++ni)
     b_off[ni] = (wcol + ni * 32 + (lane & 31)) * kRowBytes;
+  // fragment read offsets: row (block base + lane % 32), chunk 2 s + lane / 32.
+  // 16-byte chunk c of LDS row r lives at chunk c ^ swz(r), swz(r) =
+  // (r & 7) ^ ((r >> 3) & 1): any 8 consecutive rows (a 128-byte bank line)
+  // and the same-parity rows of any 16 (a 256-byte line) get distinct
+  // chunks, so the fragment reads are bank-conflict free.
   int c_off[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s)
     c_off[s] = ((2 * s + (lane >> 5)) ^ swz(lane & 31)) << 4;
 
+  // Global -> LDS without a register round trip: global_load_lds_dwordx4
+  // writes lane l's 16 bytes at (LDS base + 16 l).  Wave w fills rows
+  // [32 w, 32 w + 32) of each operand, 8 rows per instruction; lane l lands
+  // in row l / 8 at physical chunk l % 8, so it fetches the logical chunk
+  // (l % 8) ^ swz(row) that the swizzle places there.
   typedef __attribute__((address_space(3))) void* lds_ptr_t;
   const int wu = __builtin_amdgcn_readfirstlane(wid);
   const char* ga[4];
@@ -426,7 +216,11 @@ __device__ __forceinline__ void gemm_mainloop_w8(const GemmOperands& op, int M,
     const int r = wu * 32 + 8 * i + (lane >> 3);
     const int c = (lane & 7) ^ swz(r);
     if constexpr (kTransA) {
-      // K-rows 2 (4 wu + i) and + 1 of the stage, as in gemm_mainloop
+      // K-major A: instruction i of wave wu fills K-rows 2 (4 wu + i) and
+      // 2 (4 wu + i) + 1 of the stage (512 bytes each, lane / 32 picks the
+      // row); lane % 32 is the physical 16-byte chunk, which holds logical
+      // chunk (lane % 32) ^ 4 (row % 4), i.e. columns m0 + 8 chunk .. + 7.
+      // Columns past M - 8 read the last 8 (discarded by the epilogue).
       const int kr = 2 * (wu * 4 + i) + (lane >> 5);
       const int lc = (lane & 31) ^ (4 * (kr & 3));
       int mm = m0 + 8 * lc;
@@ -455,7 +249,16 @@ __device__ __forceinline__ void gemm_mainloop_w8(const GemmOperands& op, int M,
       __builtin_amdgcn_global_load_lds(gb[j - 4] + k,
                                        (lds_ptr_t)(st + kOperandBytes), 16, 0, 0);
   };
-  // K-major A: the transposing reads of gemm_mainloop for this wave's rows
+  // K-major A: ds_read_b64_tr_b16 works on groups of 16 lanes; lane q of
+  // a group names 8 bytes (4 values) at K-row q / 4 of a 4-row slab and
+  // columns 4 (q % 4) .. + 3, and lane 4 a + b of the group receives column
+  // 4 a + b of all four rows -- four consecutive K values of one M row, the
+  // MFMA A-operand layout.  Group g of the wave covers the 16 columns
+  // 16 (g % 2) .. of the 32-row block and K-rows 8 (g / 2) + 4 r .. of the
+  // step; two reads (r = 0, 1) make the 8 values of one fragment.  The
+  // XOR of the chunk with 4 (row % 4) puts the 8 rows one read touches in
+  // four different 64-byte bank groups (two rows each, the minimum for
+  // 512 bytes).
   int a_tr[2][2];
   if constexpr (kTransA) {
     const int g = lane >> 4, q = lane & 15;
@@ -475,8 +278,11 @@ __device__ __forceinline__ void gemm_mainloop_w8(const GemmOperands& op, int M,
     const char* sa = lds + stage * kStageBytes;
     const char* sb = sa + kOperandBytes;
     if constexpr (kTransA) {
-      // by hand, as in gemm_mainloop (the compiler's own form would wait
-      // for every outstanding LDS-DMA load first)
+      // Issued by hand: the compiler waits for every outstanding LDS-DMA
+      // load (vmcnt(0)) before its own form of this read.  The B reads
+      // below are issued after these ("memory" keeps them there) and LDS
+      // reads retire in order, so the lgkmcnt wait the compiler places
+      // before the first MFMA that uses B also covers these.
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi) {
         const uint32_t p0 = (uint32_t)(uintptr_t)(lds_cptr_t)(sa + a_tr[mi][0]);
@@ -510,9 +316,18 @@ __device__ __forceinline__ void gemm_mainloop_w8(const GemmOperands& op, int M,
 #pragma unroll
     for (int q = lo; q < hi; ++q) mm1(buf, q);
   };
-  // gemm_mainloop's schedule with 8 MFMAs per K step and 8 loads per
-  // stage: stage kt + 1's loads 0 .. 3 go out after the barrier that frees
-  // its buffer, 4 .. 7 in the first phase of stage kt.
+  // Schedule: stage kt lives in LDS buffer kt & 1 and is consumed as four
+  // 16-byte K steps s, each a phase of 8 MFMAs per wave on fragments read
+  // during the previous phase.  A phase starts with one MFMA, which needs
+  // the previous phase's reads, and only then issues the next step's reads,
+  // so the LDS wait before it never covers reads that were just issued.
+  // Each wave's eight loads of stage kt + 1 go out one per MFMA: four right
+  // after the barrier that frees its buffer (among the last four MFMAs of
+  // stage kt - 1) and four in the first phase of stage kt; a burst of loads
+  // stalls the in-order wave.  Before the barrier that ends stage kt, each
+  // wave waits for its own loads (vmcnt(0)), so the barrier makes stage
+  // kt + 1 complete in LDS and buffer kt & 1 free.  sched_barrier(0) pins
+  // this order against the scheduler.
 #define RZ_SB() __builtin_amdgcn_sched_barrier(0)
 #pragma unroll
   for (int j = 0; j < 8; ++j) dma1(0, 0, j);

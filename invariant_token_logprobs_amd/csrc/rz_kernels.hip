@@ -11,10 +11,8 @@
 #include "rz_gemm.h"
 #include "rz_internal.h"
 
+// the 256 x 256 tile on eight waves (gemm_mainloop), two per SIMD
 #define RZ_GEMM_ATTR \
-  __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-// the 256 x 256 tile on eight waves (gemm_mainloop_w8), two per SIMD
-#define RZ_GEMM8_ATTR \
   __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
 namespace rz {
@@ -225,7 +223,7 @@ __device__ __forceinline__ bool draw_better(float s, int v, float bs, int bv) {
 // taken first over the statistics tile; one exp per element then serves
 // both s_j and e.
 //
-// kW8: the 256-row tile on eight waves (gemm_mainloop_w8; TM = 2 32-row
+// kW8: the 256-row tile on eight waves (gemm_mainloop; TM = 2 32-row
 // blocks per wave, wave w owning rows 64 (w % 4) .. + 63 of column half
 // w / 4); else the 64-row tiles for small row counts (TM = 1, four waves,
 // wave w owning rows 32 (w / 2) .. + 31 of column half w % 2).  The
@@ -295,7 +293,7 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
 
   f32x16 acc[TM][kTN];
   if constexpr (kW8) {
-    gemm_mainloop_w8<T>(a.op, M, m0, n0, a.nk, acc, lds);
+    gemm_mainloop<T>(a.op, M, m0, n0, a.nk, acc, lds);
   } else if constexpr (kWFmt < 0) {
     gemm_mainloop_rows64<T, kStages64>(a.op, M, m0, n0, a.nk, acc, lds, one_half);
   } else {
@@ -524,7 +522,7 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
 
 // The 256-row tile: eight waves (2 kThreads threads), two per SIMD.
 template <typename T, bool kStoreE, bool kSample = false>
-__global__ RZ_GEMM8_ATTR void k_fwd_logits(FwdArgs a) {
+__global__ RZ_GEMM_ATTR void k_fwd_logits(FwdArgs a) {
   // [0, 128 KB): main-loop stages, then (learner call, bf16) the e tile;
   // then the row tokens (the draw gathers nothing: its tokens are drawn
   // later)
@@ -1312,20 +1310,20 @@ template <typename T>
 __global__ RZ_GEMM_ATTR void k_lora_u(LoraUArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
   const int m0 = blockIdx.x * kBM;
-  f32x16 acc[kTM][kTN];
+  f32x16 acc[2][kTN];
   gemm_mainloop<T, false>(a.op, a.n, m0, 0, a.nk, acc, lds);
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
+  const int wrow = (wid & 3) * 64, wcol = (wid >> 2) * 128;
   T* out = reinterpret_cast<T*>(a.out);
 #pragma unroll
-  for (int mi = 0; mi < kTM; ++mi)
+  for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
     for (int ni = 0; ni < kTN; ++ni) {
-      const int j = acc_col(wn, ni, lane);
+      const int j = acc_col(wcol, ni, lane);
       if (j >= kLoraPad) continue;
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
-        const int row = m0 + acc_row(wm, mi, rr, lane);
+        const int row = m0 + acc_row(wrow, mi, rr, lane);
         if (row < a.n)
           store_val(out + (int64_t)row * a.ld_aug + a.H + j,
                     j < a.r ? a.scale * acc[mi][ni][rr] : 0.f);
@@ -1846,7 +1844,7 @@ struct DhArgs {
   float* dh;
 };
 
-// The epilogue of one dHidden tile (eight waves, see gemm_mainloop_w8): the
+// The epilogue of one dHidden tile (eight waves, see gemm_mainloop): the
 // rows' factors (bf16), the token column's exact term, the scatter to the
 // rows' positions.
 template <typename T>
@@ -1882,7 +1880,7 @@ __device__ __forceinline__ void dh_epilogue(const DhArgs<T>& a, const RowCount& 
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         if (mi_only >= 0 && mi != mi_only) continue;
-        const int row = acc_row8(wrow, mi, r, lane);
+        const int row = acc_row(wrow, mi, r, lane);
         const float c = src[row], g = srg[row];
 #pragma unroll
         for (int ni = 0; ni < kTN; ++ni) acc[mi][ni][r] = c * (g * acc[mi][ni][r]);
@@ -1894,11 +1892,11 @@ __device__ __forceinline__ void dh_epilogue(const DhArgs<T>& a, const RowCount& 
 #pragma unroll
     for (int ni = 0; ni < kTN; ++ni) {
       if (mi_only >= 0 && mi != mi_only) continue;
-      const int h = n0 + acc_col8(wcol, ni, lane);
+      const int h = n0 + acc_col(wcol, ni, lane);
       if (h >= a.H) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = acc_row8(wrow, mi, r, lane);
+        const int row = acc_row(wrow, mi, r, lane);
         if (m0 + row < M) {
           const float w = load_f(a.W + (int64_t)stok[row] * a.H + h);
           a.dh[(int64_t)sidx[row] * a.H + h] = acc[mi][ni][r] - scoef[row] * w;
@@ -1914,7 +1912,7 @@ __device__ __forceinline__ void dh_epilogue(const DhArgs<T>& a, const RowCount& 
 // Workgroups past their share return at once.  The split's whole rounds
 // come first, so running the pieces as a second launch costs one launch.
 template <typename T, bool kPiece>
-__global__ RZ_GEMM8_ATTR void k_bwd_dh(DhArgs<T> a) {
+__global__ RZ_GEMM_ATTR void k_bwd_dh(DhArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
   const RowCount rc = to_rc(a.rows);
   const int M = rc.get();
@@ -1942,7 +1940,7 @@ __global__ RZ_GEMM8_ATTR void k_bwd_dh(DhArgs<T> a) {
   op.B += kb;
 
   f32x16 acc[2][kTN];
-  gemm_mainloop_w8<T, false>(op, M, m0, n0, k1 - k0, acc, lds);
+  gemm_mainloop<T, false>(op, M, m0, n0, k1 - k0, acc, lds);
   // piece q = (tile - full) split + piece is parked at q, the launch index
   if constexpr (kPiece) park_tile(a.part, blockIdx.x, acc);
   else dh_epilogue(a, rc, M, m0, n0, acc, lds);
@@ -1988,7 +1986,7 @@ struct DwArgs {
 };
 
 
-// dW (+)= acc for one tile (eight waves, see gemm_mainloop_w8): rows v
+// dW (+)= acc for one tile (eight waves, see gemm_mainloop): rows v
 // (vocabulary), columns h (hidden); the first chunk overwrites.
 __device__ __forceinline__ void dw_store(const DwArgs& a, int m0, int n0,
                                          f32x16 (&acc)[2][kTN],
@@ -2003,17 +2001,17 @@ __device__ __forceinline__ void dw_store(const DwArgs& a, int m0, int n0,
       if (mi_only >= 0 && mi != mi_only) continue;
       // one 32 x 32 block at a time keeps the in-flight loads bounded
       __builtin_amdgcn_sched_barrier(0);
-      const int h = n0 + acc_col8(wcol, ni, lane);
+      const int h = n0 + acc_col(wcol, ni, lane);
       if (h >= a.H) continue;
       float prev[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int v = m0 + acc_row8(wrow, mi, r, lane);
+        const int v = m0 + acc_row(wrow, mi, r, lane);
         prev[r] = (!a.first && v < a.V) ? a.dw[(int64_t)v * a.H + h] : 0.f;
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int v = m0 + acc_row8(wrow, mi, r, lane);
+        const int v = m0 + acc_row(wrow, mi, r, lane);
         if (v < a.V)
           a.dw[(int64_t)v * a.H + h] = prev[r] + ldexpf(acc[mi][ni][r], unscale);
       }
@@ -2022,7 +2020,7 @@ __device__ __forceinline__ void dw_store(const DwArgs& a, int m0, int n0,
 
 
 template <typename T>
-__global__ RZ_GEMM8_ATTR void k_bwd_dw(DwArgs a) {
+__global__ RZ_GEMM_ATTR void k_bwd_dw(DwArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
   const int K = to_rc(a.krows).get();
   const int nk = (K + a.kstage - 1) / a.kstage;
@@ -2048,7 +2046,7 @@ __global__ RZ_GEMM8_ATTR void k_bwd_dw(DwArgs a) {
   f32x16 acc[2][kTN];
   // bf16 reads dz itself through transposing LDS reads; fp32 has no such
   // read and takes the transposed copy dz^T
-  gemm_mainloop_w8<T, false, sizeof(T) == 2>(op, a.amax, m0, n0, k1 - k0, acc, lds);
+  gemm_mainloop<T, false, sizeof(T) == 2>(op, a.amax, m0, n0, k1 - k0, acc, lds);
   if (pieces > 1) {
     park_tile(a.part, (tb - full) * pieces + piece, acc);
     return;
@@ -2753,8 +2751,8 @@ hipError_t launch_lora_u(int dt, const void* hidden, const void* lora_A,
   a.scale = scale;
   a.out = hidden_aug;
   return timed(K_LORA_U, s, [&] {
-    if (dt) k_lora_u<bf16><<<cdiv(n, kBM), kThreads, 0, s>>>(a);
-    else k_lora_u<float><<<cdiv(n, kBM), kThreads, 0, s>>>(a);
+    if (dt) k_lora_u<bf16><<<cdiv(n, kBM), 2 * kThreads, 0, s>>>(a);
+    else k_lora_u<float><<<cdiv(n, kBM), 2 * kThreads, 0, s>>>(a);
   });
 }
 
