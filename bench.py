@@ -41,13 +41,13 @@ GEMM_KERNELS = ("fwd_logits_gemm", "bwd_dh_gemm", "bwd_dw_gemm")
 # kernel sources they were taken from.
 COUNTER_TRAFFIC = {
     "workload": "qwen3_4b_tool",
-    "sources_sha256": "07a29526954b5bd9724f179d7e3a6022b58b9d888bd8a47a9265c7e036e70121",
+    "sources_sha256": "424a3b0acd6c671f37a9dac0ebf2b43558bcb71d3da34cc27d6d47f5a5b42121",
     # per timed launch: a GEMM with its last-round K pieces and their sum
-    "bytes_per_launch": {"fwd_logits_gemm": 26061052333,
-                         "bwd_dh_gemm": 24139376391,
-                         "bwd_dw_gemm": 28821889512,
-                         "grad_norm": 2291984084,
-                         "mx_dequant_mxfp4": 984657262},
+    "bytes_per_launch": {"fwd_logits_gemm": 26089538514,
+                         "bwd_dh_gemm": 24438252845,
+                         "bwd_dw_gemm": 28877389088,
+                         "grad_norm": 2291985274,
+                         "mx_dequant_mxfp4": 984656843},
 }
 
 
@@ -56,9 +56,9 @@ COUNTER_TRAFFIC = {
 # GEMMs, from the counter run of profiles/mfma_utilisation_qwen3_4b_tool.md,
 # over the launches that hold rows; same validity rule as COUNTER_TRAFFIC.
 COUNTER_MFMA = {
-    "fwd_logits_gemm": {"mfma_busy": 0.610, "clock_ghz": 1.781},
-    "bwd_dh_gemm": {"mfma_busy": 0.668, "clock_ghz": 1.689},
-    "bwd_dw_gemm": {"mfma_busy": 0.631, "clock_ghz": 1.738},
+    "fwd_logits_gemm": {"mfma_busy": 0.608, "clock_ghz": 1.802},
+    "bwd_dh_gemm": {"mfma_busy": 0.671, "clock_ghz": 1.709},
+    "bwd_dw_gemm": {"mfma_busy": 0.634, "clock_ghz": 1.755},
 }
 
 
