@@ -183,6 +183,23 @@ def copy_calibration(torch, dev):
     del x, y
 
 
+def timed_pass(torch, rz, call, steps):
+    """The kernels' own HIP-event times over `steps` more calls, with the
+    library's kernel timer on.  The timer records an event pair around
+    every launch, which costs about 5 us per launch on the stream; the
+    sub-millisecond modes therefore time their calls with it off and take
+    the per-kernel split from this second pass of the same calls."""
+    torch.cuda.synchronize()
+    rz.timing_enable(True)
+    rz.timing_read(reset=True)
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    kt = rz.timing_read(reset=True)
+    rz.timing_enable(False)
+    return kt
+
+
 def bench_sample(args, torch, rz, synth, dev):
     """The rollout-side draw at decode size: rz_sample_tokens on
     --sample-rows live rows at the Qwen3-4B head (H 2560, V 151936, bf16)."""
@@ -210,17 +227,13 @@ def bench_sample(args, torch, rz, synth, dev):
     for _ in range(args.warmup):
         draw()
     torch.cuda.synchronize()
-    rz.timing_enable(True)
-    rz.timing_read(reset=True)
-    torch.cuda.synchronize()
     ts = time.perf_counter()
     for _ in range(args.steps):
         tok, logmu = draw()
     torch.cuda.synchronize()
     te = time.perf_counter()
-    kt = rz.timing_read(reset=True)
-    rz.timing_enable(False)
     ms = (te - ts) * 1e3 / args.steps
+    kt = timed_pass(torch, rz, draw, args.steps)
     assert bool(torch.isfinite(logmu).all()), "non-finite record"
     fast = fast_baseline(torch, hidden, W if fmt == "bf16" else
                          rz.dequantize_head(codes, scales, fmt), args) \
@@ -387,17 +400,13 @@ def bench_diag(args, torch, rz, synth, dev):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    rz.timing_enable(True)
-    rz.timing_read(reset=True)
-    torch.cuda.synchronize()
     ts = time.perf_counter()
     for _ in range(args.steps):
         d3, kl = step()
     torch.cuda.synchronize()
     te = time.perf_counter()
-    kt = rz.timing_read(reset=True)
-    rz.timing_enable(False)
     summary = tracker.summary()
+    kt = timed_pass(torch, rz, step, args.steps)
     assert np.isfinite(summary["grad_norm_max"]), "non-finite norm"
     if args.copy_calibration:
         copy_calibration(torch, dev)
@@ -498,16 +507,12 @@ def bench_mx(args, torch, rz, synth, dev):
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()
-    rz.timing_enable(True)
-    rz.timing_read(reset=True)
-    torch.cuda.synchronize()
     ts = time.perf_counter()
     for _ in range(args.steps):
         run()
     torch.cuda.synchronize()
     te = time.perf_counter()
-    kt = rz.timing_read(reset=True)
-    rz.timing_enable(False)
+    kt = timed_pass(torch, rz, run, args.steps)
     assert int(err.cpu()[0]) == 0, "invalid block scales in the synthetic head"
     tot_ms, launches = kt["mx_dequant"]
     avg = tot_ms / launches
