@@ -500,7 +500,8 @@ rz_status rz_timing_read(double* total_ms, int64_t* launches, int reset);
 /*
  * Matrix-core ceiling (measurement support, not part of the method).
  * rz_calibrate_mfma launches n_workgroups workgroups of four waves (one per
- * SIMD, as the GEMM tile); each wave issues iters x 128 MFMAs of the
+ * SIMD; each SIMD gets the MFMA stream of the GEMM tile's two waves on it,
+ * 128 x 128 accumulators); each wave issues iters x 128 MFMAs of the
  * learner GEMMs' instruction (v_mfma_f32_32x32x16_bf16, 32768 FLOP each)
  * into sixteen 32 x 32 accumulators, with operands kept in registers
  * (from_lds = 0) or read from LDS before every sixteen MFMAs, as the GEMM
