@@ -41,7 +41,7 @@ GEMM_KERNELS = ("fwd_logits_gemm", "bwd_dh_gemm", "bwd_dw_gemm")
 # kernel sources they were taken from.
 COUNTER_TRAFFIC = {
     "workload": "qwen3_4b_tool",
-    "sources_sha256": "424a3b0acd6c671f37a9dac0ebf2b43558bcb71d3da34cc27d6d47f5a5b42121",
+    "sources_sha256": "49b4e62517c4a4581f82f9318e0d9274db04915a611f2057971f3ce4725cb7d7",
     # per timed launch: a GEMM with its last-round K pieces and their sum
     "bytes_per_launch": {"fwd_logits_gemm": 26089538514,
                          "bwd_dh_gemm": 24438252845,

@@ -223,12 +223,11 @@ __device__ __forceinline__ bool draw_better(float s, int v, float bs, int bv) {
 // taken first over the statistics tile; one exp per element then serves
 // both s_j and e.
 //
-// kW8: the 256-row tile on eight waves (gemm_mainloop; TM = 2 32-row
-// blocks per wave, wave w owning rows 64 (w % 4) .. + 63 of column half
-// w / 4); else the 64-row tiles for small row counts (TM = 1, four waves,
-// wave w owning rows 32 (w / 2) .. + 31 of column half w % 2).  The
-// single-stage 64-row form
-// (kStages64 = 1, one row block) takes 256 columns in workgroups
+// TM = 32-row blocks per wave: 2 for the 256-row tile on eight waves
+// (gemm_mainloop; wave w owns rows 64 (w % 4) .. + 63 of column half
+// w / 4), 1 for the 64-row tiles for small row counts (four waves, wave w
+// owning rows 32 (w / 2) .. + 31 of column half w % 2).  The single-stage
+// 64-row form (kStages64 = 1, one row block) takes 256 columns in workgroups
 // [0, nfull) and 128 columns (one statistics tile; the column-half-1 waves
 // idle) in the rest, so that the head's columns spread evenly over the CUs
 // (see split_columns).  Every form runs the same MFMA per 32 x 32 block
@@ -239,10 +238,10 @@ __device__ __forceinline__ bool draw_better(float s, int v, float bs, int bv) {
 // kTokOff: byte offset in lds of the tile's row tokens for the gather
 // (-1: none; the gather then reads them from global memory).
 template <typename T, bool kStoreE, bool kSample, int TM, int kWFmt = -1,
-          int kStages64 = 2, int kTokOff = -1, bool kW8 = false>
+          int kStages64 = 2, int kTokOff = -1>
 __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
-  static_assert(kW8 ? TM == 2 : (TM == 1 && !kStoreE),
-                "the 256-row tile: eight waves; the 64-row tiles: no e output");
+  static_assert(TM == 2 || (TM == 1 && !kStoreE), "64-row tiles: no e output");
+  constexpr bool kW8 = TM == 2;  // the 256-row tile on eight waves
   constexpr int NT = kW8 ? 2 * kThreads : kThreads;  // threads per workgroup
   constexpr bool kMixed = TM == 1 && kStages64 == 1 && kWFmt < 0;
   constexpr int BM = kW8 ? kBM : 64 * TM;  // tile rows
@@ -527,7 +526,7 @@ __global__ RZ_GEMM_ATTR void k_fwd_logits(FwdArgs a) {
   // then the row tokens (the draw gathers nothing: its tokens are drawn
   // later)
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes + (kSample ? 0 : 4 * kBM)];
-  fwd_logits_body<T, kStoreE, kSample, 2, -1, 2, kSample ? -1 : kLdsBytes, true>(a, lds);
+  fwd_logits_body<T, kStoreE, kSample, 2, -1, 2, kSample ? -1 : kLdsBytes>(a, lds);
 }
 
 // The 64-row tile: 80 KB of LDS and a quarter of the accumulators, so two
