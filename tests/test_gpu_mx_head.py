@@ -155,6 +155,38 @@ def test_mx_entry_points_equal_the_expanded_head(fmt, n, H):
     assert _same_bits(m1, rz.token_logprobs_mx(hidden, cd, sd, fmt, t1))
 
 
+@pytest.mark.parametrize("which", range(3))
+def test_mx_column_splits_equal_the_expanded_head(which):
+    """Up to 64 rows an MXFP4 head runs in workgroups of 256 and 128 columns
+    by the head's width and the CU count (all 128-column workgroups; whole
+    rounds of 256-column ones plus at most one 128-column one per CU; whole
+    rounds plus further 256-column ones, V not a multiple of 128).  At 64 and
+    37 rows the logprobs, lse and draws equal the bf16 calls on the expanded
+    head bit for bit."""
+    import invariant_token_logprobs_amd as rz
+    torch = torch_mod()
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    V = [1000, 128 * (2 * ncu + ncu // 2), 128 * (3 * ncu + 37) - 50][which]
+    H = 128
+    codes, scales = synth.random_mx_head(V, H, "mxfp4", 91 + which)
+    cd, sd = vec_to_dev(codes), vec_to_dev(scales)
+    W = rz.dequantize_head(cd, sd, "mxfp4")
+    for n in (64, 37):
+        say("mx column split", which, "V", V, "rows", n)
+        hid, tok = synth.random_rows(n, H, V, "bf16", 93 + n + which)
+        hidden, tokens = mat_to_dev(hid, "bf16"), vec_to_dev(tok)
+        lp, lse = rz.token_logprobs_mx(hidden, cd, sd, "mxfp4", tokens, want_lse=True)
+        lp2, lse2 = rz.token_logprobs(hidden, W, tokens, want_lse=True)
+        ids = vec_to_dev(np.arange(n, dtype=np.int64) * 17 + which)
+        t1, m1, l1 = rz.sample_tokens_mx(hidden, cd, sd, "mxfp4", ids, 0xBEEF, want_lse=True)
+        t2, m2, l2 = rz.sample_tokens(hidden, W, ids, 0xBEEF, want_lse=True)
+        torch.cuda.synchronize()
+        assert _same_bits(lp, lp2) and _same_bits(lse, lse2), (V, n)
+        assert torch.equal(t1, t2) and _same_bits(m1, m2) and _same_bits(l1, l2), (V, n)
+    del W
+    torch.cuda.empty_cache()
+
+
 def test_mx_entry_points_invalid_scale():
     """A NaN scale code in the head: the same NaNs as the expanded head's,
     and the device flag."""
