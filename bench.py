@@ -43,11 +43,11 @@ COUNTER_TRAFFIC = {
     "workload": "qwen3_4b_tool",
     "sources_sha256": "49b4e62517c4a4581f82f9318e0d9274db04915a611f2057971f3ce4725cb7d7",
     # per timed launch: a GEMM with its last-round K pieces and their sum
-    "bytes_per_launch": {"fwd_logits_gemm": 26089538514,
-                         "bwd_dh_gemm": 24438252845,
-                         "bwd_dw_gemm": 28877389088,
-                         "grad_norm": 2291985274,
-                         "mx_dequant_mxfp4": 984656843},
+    "bytes_per_launch": {"fwd_logits_gemm": 26114967732,
+                         "bwd_dh_gemm": 24183321527,
+                         "bwd_dw_gemm": 28357882589,
+                         "grad_norm": 2291954742,
+                         "mx_dequant_mxfp4": 984645866},
 }
 
 
@@ -56,9 +56,9 @@ COUNTER_TRAFFIC = {
 # GEMMs, from the counter run of profiles/mfma_utilisation_qwen3_4b_tool.md,
 # over the launches that hold rows; same validity rule as COUNTER_TRAFFIC.
 COUNTER_MFMA = {
-    "fwd_logits_gemm": {"mfma_busy": 0.608, "clock_ghz": 1.802},
-    "bwd_dh_gemm": {"mfma_busy": 0.671, "clock_ghz": 1.709},
-    "bwd_dw_gemm": {"mfma_busy": 0.634, "clock_ghz": 1.755},
+    "fwd_logits_gemm": {"mfma_busy": 0.611, "clock_ghz": 1.758},
+    "bwd_dh_gemm": {"mfma_busy": 0.656, "clock_ghz": 1.661},
+    "bwd_dw_gemm": {"mfma_busy": 0.628, "clock_ghz": 1.698},
 }
 
 

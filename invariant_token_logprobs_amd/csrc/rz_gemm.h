@@ -544,10 +544,6 @@ __device__ __forceinline__ bool mx_scale_ok(int fmt, int code) {
 // swizzled by row bits 3 (E2M1) or 2..3 (E4M3), which keeps the fragment
 // reads bank-conflict free.  Needs H % 128 == 0 (whole scale dwords).
 // A block with an invalid scale gives NaN fragments and sets `bad`.
-// one_half = true computes the first 128 columns only (a 64 x 128 tile):
-// waves 2 and 3 load no code rows or scales (rows 128 .. 255), the waves of
-// column half 1 build no fragments and issue no MFMAs (their accumulators
-// stay 0); every wave keeps its A loads and the barriers.
 template <int kFmt>
 struct MxStage {
   static constexpr int kCodeRow = kFmt == 0 ? 32 : 64;
@@ -567,7 +563,7 @@ template <int kFmt>
 __device__ __forceinline__ void gemm_mainloop_rows64_mx(
     const GemmOperands& op, const uint8_t* wcodes, const uint8_t* wscales,
     int H, int M, int m0, int n0, int nk, f32x16 (&acc)[1][kTN], char* lds,
-    bool& bad, bool one_half = false) {
+    bool& bad) {
   using S = MxStage<kFmt>;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wid = tid >> 6;
@@ -589,8 +585,6 @@ __device__ __forceinline__ void gemm_mainloop_rows64_mx(
 
   typedef __attribute__((address_space(3))) void* lds_ptr_t;
   const int wu = __builtin_amdgcn_readfirstlane(wid);
-  const bool lite = one_half && wu >= 2;      // A loads only
-  const bool idle = one_half && (wu & 1);     // no fragments, no MFMAs
   const int64_t code_ld = kFmt == 0 ? H / 2 : H, scale_ld = H / 32;
   const char* ga[2];
 #pragma unroll
@@ -631,7 +625,6 @@ __device__ __forceinline__ void gemm_mainloop_rows64_mx(
       __builtin_amdgcn_global_load_lds(ga[i] + (int64_t)kt * kRowBytes,
                                        (lds_ptr_t)(st + (wu * 16 + 8 * i) * kRowBytes),
                                        16, 0, 0);
-    if (lite) return;
 #pragma unroll
     for (int i = 0; i < kCL; ++i)
       __builtin_amdgcn_global_load_lds(
@@ -653,11 +646,7 @@ __device__ __forceinline__ void gemm_mainloop_rows64_mx(
     // then makes every wave's visible and retires the reads of stage kt - 1,
     // whose buffer takes stage kt + kRing - 1
     const int later = (nk - 1 - kt) < (S::kRing - 2) ? (nk - 1 - kt) : (S::kRing - 2);
-    if (lite) {  // two loads per stage
-      if (later >= 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-      else if (later == 1) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    } else if constexpr (S::kLoads == 5) {
+    if constexpr (S::kLoads == 5) {
       if (later >= 2) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
       else if (later == 1) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
       else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -668,7 +657,6 @@ __device__ __forceinline__ void gemm_mainloop_rows64_mx(
     }
     __syncthreads();
     if (kt + S::kRing - 1 < nk) dma(kt + S::kRing - 1, (kt + S::kRing - 1) % S::kRing);
-    if (idle) continue;
     const char* st = lds + (kt % S::kRing) * S::kBytes;
     const char* sc = st + kOperandBytesA64;
     const char* ss = sc + S::kCodes;

@@ -243,7 +243,7 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
   static_assert(TM == 2 || (TM == 1 && !kStoreE), "64-row tiles: no e output");
   constexpr bool kW8 = TM == 2;  // the 256-row tile on eight waves
   constexpr int NT = kW8 ? 2 * kThreads : kThreads;  // threads per workgroup
-  constexpr bool kMixed = TM == 1 && kStages64 == 1;
+  constexpr bool kMixed = TM == 1 && kStages64 == 1 && kWFmt < 0;
   constexpr int BM = kW8 ? kBM : 64 * TM;  // tile rows
   constexpr int RW = 32 * TM;       // rows per wave
   const RowCount rc = to_rc(a.rows);
@@ -298,7 +298,7 @@ __device__ __forceinline__ void fwd_logits_body(const FwdArgs& a, char* lds) {
   } else {
     bool bad = false;
     gemm_mainloop_rows64_mx<kWFmt>(a.op, a.wcodes, a.wscales, a.H, M, m0, n0,
-                                   a.nk, acc, lds, bad, one_half);
+                                   a.nk, acc, lds, bad);
     if (bad && a.err) atomicOr(a.err, 8);
   }
 
@@ -552,15 +552,12 @@ void k_fwd_logits64_1s(FwdArgs a) {
 
 // The 64-row tile on an MX-format head (bf16 hidden states); E2M1 is sized
 // for three workgroups per CU (LDS and at most 168 VGPRs), E4M3 for two.
-// kSplit (E2M1, one row block): workgroups [0, nfull) take 256 columns, the
-// rest 128, as k_fwd_logits64_1s (see split_columns).
-template <int kFmt, bool kSample, bool kSplit = false>
+template <int kFmt, bool kSample>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(kFmt == 0 ? 3 : 2, kFmt == 0 ? 3 : 2)))
 void k_fwd_logits64_mx(FwdArgs a) {
-  static_assert(!kSplit || kFmt == 0, "the column split needs three workgroups per CU");
   __shared__ __attribute__((aligned(16))) char lds[MxStage<kFmt>::kLds];
-  fwd_logits_body<bf16, false, kSample, 1, kFmt, kSplit ? 1 : 2>(a, lds);
+  fwd_logits_body<bf16, false, kSample, 1, kFmt>(a, lds);
 }
 
 // ===================================================================
@@ -2464,22 +2461,13 @@ hipError_t launch_fwd_mx(int fmt, const void* hidden, int64_t n,
   a.wscales = scales;
   a.H = H;
   a.err = err;
-  // E2M1 at one row block: 256- and 128-column workgroups (split_columns)
-  const bool split = fmt == 0 && n <= kBM64;
-  if (split) {
-    const ColSplit cs = split_columns(V);
-    a.nfull = cs.nfull;
-    a.nt = cs.nblk;
-  }
   const int nblk = a.mt * a.nt;
   return timed(cand ? K_FWD_SAMPLE : K_FWD_LOGITS, s, [&] {
     if (cand) {
-      if (split) k_fwd_logits64_mx<0, true, true><<<nblk, kThreads, 0, s>>>(a);
-      else if (fmt == 0) k_fwd_logits64_mx<0, true><<<nblk, kThreads, 0, s>>>(a);
+      if (fmt == 0) k_fwd_logits64_mx<0, true><<<nblk, kThreads, 0, s>>>(a);
       else k_fwd_logits64_mx<1, true><<<nblk, kThreads, 0, s>>>(a);
     } else {
-      if (split) k_fwd_logits64_mx<0, false, true><<<nblk, kThreads, 0, s>>>(a);
-      else if (fmt == 0) k_fwd_logits64_mx<0, false><<<nblk, kThreads, 0, s>>>(a);
+      if (fmt == 0) k_fwd_logits64_mx<0, false><<<nblk, kThreads, 0, s>>>(a);
       else k_fwd_logits64_mx<1, false><<<nblk, kThreads, 0, s>>>(a);
     }
   });

@@ -156,13 +156,13 @@ def test_mx_entry_points_equal_the_expanded_head(fmt, n, H):
 
 
 @pytest.mark.parametrize("which", range(3))
-def test_mx_column_splits_equal_the_expanded_head(which):
-    """Up to 64 rows an MXFP4 head runs in workgroups of 256 and 128 columns
-    by the head's width and the CU count (all 128-column workgroups; whole
-    rounds of 256-column ones plus at most one 128-column one per CU; whole
-    rounds plus further 256-column ones, V not a multiple of 128).  At 64 and
-    37 rows the logprobs, lse and draws equal the bf16 calls on the expanded
-    head bit for bit."""
+def test_mx_head_equals_the_split_bf16_tile(which):
+    """An MXFP4 head at the vocabularies that take each branch of the bf16
+    tile's column split (few statistics tiles; whole rounds of 256-column
+    workgroups plus at most one 128-column one per CU; further 256-column
+    ones, V not a multiple of 128), whose bf16 calls run split while the MX
+    tile runs whole 256-column tiles: at 64 and 37 rows the logprobs, lse and
+    draws equal the bf16 calls on the expanded head bit for bit."""
     import invariant_token_logprobs_amd as rz
     torch = torch_mod()
     ncu = torch.cuda.get_device_properties(0).multi_processor_count
