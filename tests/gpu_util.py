@@ -151,7 +151,8 @@ def softmax_grad_bounds(hidden64, W64, lse, coef, row_chunk=256, tokens=None,
 
 def report_grad_error(got, want, what):
     """Print the worst per-element error of a gradient in units of
-    max|oracle| (the survey's plain 1e-4 max|o| per-element bound)."""
+    max|oracle| (the plain per-element bound of 1e-4 times the output's
+    largest magnitude)."""
     got = np.asarray(got, np.float64)
     want = np.asarray(want, np.float64)
     fin = np.isfinite(want)
