@@ -30,6 +30,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
 
 namespace rz {
 
@@ -329,42 +330,110 @@ __device__ __forceinline__ void gemm_mainloop(const GemmOperands& op, int M,
   // kt + 1 complete in LDS and buffer kt & 1 free.  sched_barrier(0) pins
   // this order against the scheduler.
 #define RZ_SB() __builtin_amdgcn_sched_barrier(0)
-#pragma unroll
-  for (int j = 0; j < 8; ++j) dma1(0, 0, j);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (nk > 1) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dma1(1, 1, j);
+  // Plain operands: a wave's 32-column blocks wholly at or past column N
+  // (uniform per wave; the narrow last column tile of the LoRA-widened
+  // dHidden, the adapter's own 64 columns) issue no MFMA: their
+  // accumulators stay 0 and no epilogue stores them.  The swapped form
+  // keeps every MFMA: the forward's row maxima read every accumulator.
+  int nlive = kTN;
+  if constexpr (!kSwap) {
+    const int left = op.N - n0 - wcol;
+    nlive = left <= 0 ? 0 : (left >= 32 * kTN ? kTN : (left + 31) / 32);
   }
-  lread(0, 0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool nx = kt + 1 < nk, nx2 = kt + 2 < nk;
-    RZ_SB(); mm1(0, 0); RZ_SB(); lread(1, cur, 1); RZ_SB();
+  // (the forward below writes the schedule out itself)
+  auto sched = [&](auto part_c) {
+    constexpr bool kPart = decltype(part_c)::value;
+    auto mmx = [&](int buf, int q) {
+      if constexpr (kPart) {
+        if (q % kTN >= nlive) return;
+      }
+      mm1(buf, q);
+    };
+    auto mmrx = [&](int buf, int lo, int hi) {
 #pragma unroll
-    for (int q = 1; q < 8; ++q) {
-      mm1(0, q);
-      RZ_SB();
-      if (q <= 4 && nx) dma1(kt + 1, cur ^ 1, 3 + q);
-      RZ_SB();
-    }
-    mm1(1, 0); RZ_SB(); lread(0, cur, 2); RZ_SB(); mmr(1, 1, 8); RZ_SB();
-    mm1(0, 0); RZ_SB(); lread(1, cur, 3); RZ_SB(); mmr(0, 1, 8); RZ_SB();
-    mmr(1, 0, 4);
-    RZ_SB();
-    if (nx) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      for (int q = lo; q < hi; ++q) mmx(buf, q);
+    };
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dma1(0, 0, j);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    RZ_SB();
-    if (nx) lread(0, cur ^ 1, 0);
-    RZ_SB();
+    if (nk > 1) {
 #pragma unroll
-    for (int q = 4; q < 8; ++q) {
-      mm1(1, q);
-      RZ_SB();
-      if (nx2) dma1(kt + 2, cur, q - 4);
-      RZ_SB();
+      for (int j = 0; j < 4; ++j) dma1(1, 1, j);
     }
+    lread(0, 0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      const bool nx = kt + 1 < nk, nx2 = kt + 2 < nk;
+      RZ_SB(); mmx(0, 0); RZ_SB(); lread(1, cur, 1); RZ_SB();
+#pragma unroll
+      for (int q = 1; q < 8; ++q) {
+        mmx(0, q);
+        RZ_SB();
+        if (q <= 4 && nx) dma1(kt + 1, cur ^ 1, 3 + q);
+        RZ_SB();
+      }
+      mmx(1, 0); RZ_SB(); lread(0, cur, 2); RZ_SB(); mmrx(1, 1, 8); RZ_SB();
+      mmx(0, 0); RZ_SB(); lread(1, cur, 3); RZ_SB(); mmrx(0, 1, 8); RZ_SB();
+      mmrx(1, 0, 4);
+      RZ_SB();
+      if (nx) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      RZ_SB();
+      if (nx) lread(0, cur ^ 1, 0);
+      RZ_SB();
+#pragma unroll
+      for (int q = 4; q < 8; ++q) {
+        mmx(1, q);
+        RZ_SB();
+        if (nx2) dma1(kt + 2, cur, q - 4);
+        RZ_SB();
+      }
+    }
+  };
+  if constexpr (kSwap) {
+    // the same schedule written out with every MFMA (the forward)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dma1(0, 0, j);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (nk > 1) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dma1(1, 1, j);
+    }
+    lread(0, 0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      const bool nx = kt + 1 < nk, nx2 = kt + 2 < nk;
+      RZ_SB(); mm1(0, 0); RZ_SB(); lread(1, cur, 1); RZ_SB();
+#pragma unroll
+      for (int q = 1; q < 8; ++q) {
+        mm1(0, q);
+        RZ_SB();
+        if (q <= 4 && nx) dma1(kt + 1, cur ^ 1, 3 + q);
+        RZ_SB();
+      }
+      mm1(1, 0); RZ_SB(); lread(0, cur, 2); RZ_SB(); mmr(1, 1, 8); RZ_SB();
+      mm1(0, 0); RZ_SB(); lread(1, cur, 3); RZ_SB(); mmr(0, 1, 8); RZ_SB();
+      mmr(1, 0, 4);
+      RZ_SB();
+      if (nx) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      RZ_SB();
+      if (nx) lread(0, cur ^ 1, 0);
+      RZ_SB();
+#pragma unroll
+      for (int q = 4; q < 8; ++q) {
+        mm1(1, q);
+        RZ_SB();
+        if (nx2) dma1(kt + 2, cur, q - 4);
+        RZ_SB();
+      }
+    }
+  } else if (nlive == kTN) {
+    sched(std::integral_constant<bool, false>{});
+  } else {
+    sched(std::integral_constant<bool, true>{});
   }
 #undef RZ_SB
 }
