@@ -41,13 +41,13 @@ GEMM_KERNELS = ("fwd_logits_gemm", "bwd_dh_gemm", "bwd_dw_gemm")
 # kernel sources they were taken from.
 COUNTER_TRAFFIC = {
     "workload": "qwen3_4b_tool",
-    "sources_sha256": "49b4e62517c4a4581f82f9318e0d9274db04915a611f2057971f3ce4725cb7d7",
+    "sources_sha256": "50de99dde003ec4db27f97eb7aab2075a95d7f1944e6ddd4dfb3375af9d5861b",
     # per timed launch: a GEMM with its last-round K pieces and their sum
-    "bytes_per_launch": {"fwd_logits_gemm": 26114967732,
-                         "bwd_dh_gemm": 24183321527,
-                         "bwd_dw_gemm": 28357882589,
-                         "grad_norm": 2291954742,
-                         "mx_dequant_mxfp4": 984645866},
+    "bytes_per_launch": {"fwd_logits_gemm": 26095798992,
+                         "bwd_dh_gemm": 24031489230,
+                         "bwd_dw_gemm": 27943645919,
+                         "grad_norm": 2291958011,
+                         "mx_dequant_mxfp4": 984643114},
 }
 
 
@@ -56,9 +56,9 @@ COUNTER_TRAFFIC = {
 # GEMMs, from the counter run of profiles/mfma_utilisation_qwen3_4b_tool.md,
 # over the launches that hold rows; same validity rule as COUNTER_TRAFFIC.
 COUNTER_MFMA = {
-    "fwd_logits_gemm": {"mfma_busy": 0.611, "clock_ghz": 1.758},
-    "bwd_dh_gemm": {"mfma_busy": 0.656, "clock_ghz": 1.661},
-    "bwd_dw_gemm": {"mfma_busy": 0.628, "clock_ghz": 1.698},
+    "fwd_logits_gemm": {"mfma_busy": 0.605, "clock_ghz": 1.819},
+    "bwd_dh_gemm": {"mfma_busy": 0.674, "clock_ghz": 1.717},
+    "bwd_dw_gemm": {"mfma_busy": 0.636, "clock_ghz": 1.762},
 }
 
 
